@@ -1,0 +1,236 @@
+"""fp64 CPU oracle for the gated delta rule (test infrastructure only).
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may import this package.  It shares no code with the HIP library in
+``gated_delta_rule_66_amd``: the arithmetic lives in ``gdr_oracle.c`` (plain C,
+fp64, OpenMP over independent (sequence, value-head) units) and this module
+only marshals numpy arrays into it.
+
+Shapes follow the Core API of the "flashqla-linear-attention" page:
+q, k ``[B, T, Hq, K]``; v ``[B, T, Hv, V]``; g, beta ``[B, T, Hv]``;
+states ``[N, Hv, K, V]`` (``[N, Hv, V, K]`` with ``state_v_first``), where N is
+B, or ``len(cu_seqlens) - 1`` for packed variable-length input (B must be 1).
+
+Every function accepts any real numpy dtype and computes in float64.  The
+``heads`` argument restricts the work to some value heads (all sequences); the
+outputs of the other heads are returned as zeros.  That is how the tests and
+the benchmark sample full-size problems.
+
+Pins that tie this oracle to the method, not to itself, are in
+``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, -O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        D = ctypes.c_double
+        lib.oracle_fwd.argtypes = [I64, P, I64, I64, I64, I64, P, P, P, P, P, D, P, P, P, P,
+                                   ctypes.c_int]
+        lib.oracle_bwd.argtypes = [I64, P, I64, I64, I64, I64, P, P, P, P, P, D, P, P, P,
+                                   P, P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_chunked_fwd.argtypes = [I64, P, I64, I64, I64, I64, I64, P, P, P, P, P, D,
+                                           P, P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_chunked_bwd.argtypes = [I64, P, I64, I64, I64, I64, I64, P, P, P, P, P, D,
+                                           P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+        for f in (lib.oracle_fwd, lib.oracle_bwd, lib.oracle_chunked_fwd,
+                  lib.oracle_chunked_bwd):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+class _Problem:
+    """Flattens the API shapes into the oracle's token-major layout."""
+
+    def __init__(self, q, k, v, g, beta, cu_seqlens, heads):
+        q = _f64(q)
+        if q.ndim != 4:
+            raise ValueError("q must be [B, T, Hq, K]")
+        self.B, self.T, self.Hq, self.K = q.shape
+        self.Hv = v.shape[2]
+        self.V = v.shape[3]
+        if cu_seqlens is None:
+            self.N = self.B
+            cu = np.arange(self.B + 1, dtype=np.int64) * self.T
+        else:
+            if self.B != 1:
+                raise ValueError("packed input needs B == 1")
+            cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+            self.N = cu.shape[0] - 1
+            if cu[0] != 0 or cu[-1] != self.T or np.any(np.diff(cu) < 0):
+                raise ValueError("bad cu_seqlens")
+        self.cu = cu
+        self.Ttot = self.B * self.T
+        self.q = q.reshape(self.Ttot, self.Hq, self.K)
+        self.k = _f64(k).reshape(self.Ttot, self.Hq, self.K)
+        self.v = _f64(v).reshape(self.Ttot, self.Hv, self.V)
+        self.g = _f64(g).reshape(self.Ttot, self.Hv)
+        self.beta = _f64(beta).reshape(self.Ttot, self.Hv)
+        if heads is None:
+            self.mask = None
+        else:
+            m = np.zeros((self.N, self.Hv), dtype=np.uint8)
+            m[:, list(heads)] = 1
+            self.mask = np.ascontiguousarray(m.reshape(-1))
+
+    def dims(self):
+        return (self.N, _ptr(self.cu), self.Hq, self.Hv, self.K, self.V)
+
+    def state_in(self, s, state_v_first):
+        if s is None:
+            return None
+        s = _f64(s)
+        if state_v_first:
+            s = np.ascontiguousarray(np.swapaxes(s, -1, -2))
+        if s.shape != (self.N, self.Hv, self.K, self.V):
+            raise ValueError("state must be [N, Hv, K, V] (or [N, Hv, V, K] if v-first)")
+        return s
+
+    @staticmethod
+    def state_out(s, state_v_first):
+        return np.ascontiguousarray(np.swapaxes(s, -1, -2)) if state_v_first else s
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise RuntimeError("%s failed with code %d" % (name, rc))
+
+
+def fwd(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None, state_v_first=False,
+        heads=None, nthreads=0):
+    """Token recurrence.  Returns ``(o [B,T,Hv,V], final_state [N,Hv,K,V])``."""
+    p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
+    h0 = p.state_in(initial_state, state_v_first)
+    o = np.zeros((p.Ttot, p.Hv, p.V))
+    ht = np.zeros((p.N, p.Hv, p.K, p.V))
+    rc = _load().oracle_fwd(*p.dims(), _ptr(p.q), _ptr(p.k), _ptr(p.v), _ptr(p.g),
+                            _ptr(p.beta), float(scale), _ptr(h0), _ptr(o), _ptr(ht),
+                            _ptr(p.mask), int(nthreads))
+    _check(rc, "oracle_fwd")
+    return o.reshape(p.B, p.T, p.Hv, p.V), p.state_out(ht, state_v_first)
+
+
+def bwd(q, k, v, g, beta, scale, do, initial_state=None, dht=None, cu_seqlens=None,
+        state_v_first=False, heads=None, nthreads=0):
+    """Gradients of ``sum(do*o) + sum(dht*final_state)`` by the hand-derived
+    reverse pass of the token recurrence.
+
+    Returns ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is with respect to the raw
+    log-decay g; ``dh0`` is ``None`` when ``initial_state`` is ``None``.
+    """
+    p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
+    h0 = p.state_in(initial_state, state_v_first)
+    dht_ = p.state_in(dht, state_v_first)
+    do_ = _f64(do).reshape(p.Ttot, p.Hv, p.V)
+    dq = np.zeros((p.Ttot, p.Hq, p.K))
+    dk = np.zeros((p.Ttot, p.Hq, p.K))
+    dv = np.zeros((p.Ttot, p.Hv, p.V))
+    db = np.zeros((p.Ttot, p.Hv))
+    dg = np.zeros((p.Ttot, p.Hv))
+    dh0 = np.zeros((p.N, p.Hv, p.K, p.V))
+    rc = _load().oracle_bwd(*p.dims(), _ptr(p.q), _ptr(p.k), _ptr(p.v), _ptr(p.g),
+                            _ptr(p.beta), float(scale), _ptr(h0), _ptr(do_), _ptr(dht_),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0),
+                            _ptr(p.mask), int(nthreads))
+    _check(rc, "oracle_bwd")
+    B, T = p.B, p.T
+    return (dq.reshape(B, T, p.Hq, p.K), dk.reshape(B, T, p.Hq, p.K),
+            dv.reshape(B, T, p.Hv, p.V), db.reshape(B, T, p.Hv), dg.reshape(B, T, p.Hv),
+            None if initial_state is None else p.state_out(dh0, state_v_first))
+
+
+def chunk_offsets(cu, chunk):
+    cu = np.asarray(cu, dtype=np.int64)
+    nc = (np.diff(cu) + chunk - 1) // chunk
+    return np.concatenate([[0], np.cumsum(nc)]).astype(np.int64)
+
+
+def chunked_fwd(q, k, v, g, beta, scale, chunk=64, initial_state=None, cu_seqlens=None,
+                state_v_first=False, heads=None, nthreads=0):
+    """Naive fp64 chunked form.
+
+    Returns ``(g_cum [B,T,Hv], A [B,T,Hv,chunk], o [B,T,Hv,V],
+    h [NCtot,Hv,K,V], final_state [N,Hv,K,V])``; ``h`` holds chunk-start states
+    (``[NCtot,Hv,V,K]`` with ``state_v_first``), row ``r`` of a chunk's ``A`` is
+    stored at token ``chunk_start + r`` and columns past a partial chunk are 0.
+    """
+    p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
+    h0 = p.state_in(initial_state, state_v_first)
+    nct = int(chunk_offsets(p.cu, chunk)[-1])
+    gc = np.zeros((p.Ttot, p.Hv))
+    A = np.zeros((p.Ttot, p.Hv, chunk))
+    o = np.zeros((p.Ttot, p.Hv, p.V))
+    h = np.zeros((max(nct, 1), p.Hv, p.K, p.V))
+    ht = np.zeros((p.N, p.Hv, p.K, p.V))
+    rc = _load().oracle_chunked_fwd(*p.dims(), int(chunk), _ptr(p.q), _ptr(p.k), _ptr(p.v),
+                                    _ptr(p.g), _ptr(p.beta), float(scale), _ptr(h0), _ptr(gc),
+                                    _ptr(A), _ptr(o), _ptr(h), _ptr(ht), _ptr(p.mask),
+                                    int(nthreads))
+    _check(rc, "oracle_chunked_fwd")
+    B, T = p.B, p.T
+    return (gc.reshape(B, T, p.Hv), A.reshape(B, T, p.Hv, chunk),
+            o.reshape(B, T, p.Hv, p.V), p.state_out(h[:nct], state_v_first),
+            p.state_out(ht, state_v_first))
+
+
+def chunked_bwd(q, k, v, g, beta, scale, do, chunk=64, initial_state=None, dht=None,
+                cu_seqlens=None, state_v_first=False, heads=None, nthreads=0):
+    """Reverse pass of the naive chunked form; same outputs as :func:`bwd`."""
+    p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
+    h0 = p.state_in(initial_state, state_v_first)
+    dht_ = p.state_in(dht, state_v_first)
+    do_ = _f64(do).reshape(p.Ttot, p.Hv, p.V)
+    dq = np.zeros((p.Ttot, p.Hq, p.K))
+    dk = np.zeros((p.Ttot, p.Hq, p.K))
+    dv = np.zeros((p.Ttot, p.Hv, p.V))
+    db = np.zeros((p.Ttot, p.Hv))
+    dg = np.zeros((p.Ttot, p.Hv))
+    dh0 = np.zeros((p.N, p.Hv, p.K, p.V))
+    rc = _load().oracle_chunked_bwd(*p.dims(), int(chunk), _ptr(p.q), _ptr(p.k), _ptr(p.v),
+                                    _ptr(p.g), _ptr(p.beta), float(scale), _ptr(h0), _ptr(do_),
+                                    _ptr(dht_), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg),
+                                    _ptr(dh0), _ptr(p.mask), int(nthreads))
+    _check(rc, "oracle_chunked_bwd")
+    B, T = p.B, p.T
+    return (dq.reshape(B, T, p.Hq, p.K), dk.reshape(B, T, p.Hq, p.K),
+            dv.reshape(B, T, p.Hv, p.V), db.reshape(B, T, p.Hv), dg.reshape(B, T, p.Hv),
+            None if initial_state is None else p.state_out(dh0, state_v_first))
