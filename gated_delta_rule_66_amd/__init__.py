@@ -1,0 +1,234 @@
+"""Chunked gated delta rule (GDN chunked prefill) for AMD MI355X.
+
+A thin binding over libgdr.so (``include/gdr.h``).  PyTorch provides device
+memory and the current stream; every step of the computation runs in the HIP
+kernels of the library.  Names and arguments follow the FlashQLA pages
+("flashqla-linear-attention", Core API and Low-Level API; "FlashQLA
+Documentation", forward / backward and the utilities prepare_lens,
+prepare_chunk_indices, prepare_chunk_offsets).
+
+Shapes: q, k ``[B, T, Hq, K]``; v ``[B, T, Hv, V]``; g, beta ``[B, T, Hv]``;
+states ``[N, Hv, K, V]`` (``[N, Hv, V, K]`` with ``state_v_first``), fp32.
+K = V = 128; bf16 or fp16 inputs; Hv a multiple of Hq.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import (GDR_BF16, GDR_FP16, GDR_FP32, GdrError, Problem, check, lib)
+
+__all__ = [
+    "chunk_gated_delta_rule", "chunk_gated_delta_rule_fwd", "chunk_gated_delta_rule_bwd",
+    "prepare_lens", "prepare_chunk_indices", "prepare_chunk_offsets", "GdrError",
+]
+
+CHUNK = 64
+_DT = {torch.bfloat16: GDR_BF16, torch.float16: GDR_FP16, torch.float32: GDR_FP32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _code(dtype):
+    if dtype not in _DT:
+        raise GdrError(4, "unsupported dtype %s" % dtype)
+    return _DT[dtype]
+
+
+class _Call:
+    """Problem descriptor plus the host copy of cu_seqlens it points to."""
+
+    def __init__(self, q, v, g_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first,
+                 cp_segments):
+        B, T, Hq, K = q.shape
+        Hv, V = v.shape[2], v.shape[3]
+        self.cu_host = None
+        self.cu_dev = None
+        if cu_seqlens is not None:
+            self.cu_dev = cu_seqlens.to(device=q.device, dtype=torch.int32).contiguous()
+            if cu_seqlens_cpu is None:
+                cu_seqlens_cpu = cu_seqlens.detach().to("cpu")
+            self.cu_host = cu_seqlens_cpu.to(torch.int32).contiguous()
+            N = self.cu_host.numel() - 1
+        else:
+            N = B
+        if scale is None:
+            scale = K ** -0.5
+        self.p = Problem(B=B, T=T, Hq=Hq, Hv=Hv, K=K, V=V, N=N,
+                         cu_seqlens_dev=None if self.cu_dev is None else self.cu_dev.data_ptr(),
+                         cu_seqlens_host=None if self.cu_host is None else self.cu_host.data_ptr(),
+                         in_dtype=_code(q.dtype), g_dtype=_code(g_dtype), scale=float(scale),
+                         state_v_first=1 if state_v_first else 0, cp_segments=int(cp_segments))
+        self.N, self.Hv, self.K, self.V = N, Hv, K, V
+        self.ref = ctypes.byref(self.p)
+        reason = ctypes.create_string_buffer(256)
+        check(lib.gdr_check_supported(self.ref, reason, 256))
+
+    def state_shape(self, state_v_first):
+        return (self.N, self.Hv, self.V, self.K) if state_v_first else (self.N, self.Hv, self.K, self.V)
+
+    def num_chunks(self):
+        if self.cu_host is None:
+            return self.p.B * ((self.p.T + CHUNK - 1) // CHUNK)
+        n = ctypes.c_int64(0)
+        offs = torch.empty(self.cu_host.numel(), dtype=torch.int32)
+        check(lib.gdr_prepare_chunk_offsets_i32(_ptr(self.cu_host), self.cu_host.numel(), CHUNK,
+                                                _ptr(offs), ctypes.byref(n)))
+        return int(n.value)
+
+
+def _contig(*ts):
+    return [None if t is None else t.contiguous() for t in ts]
+
+
+def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
+                               output_final_state=True, cu_seqlens=None, state_v_first=False,
+                               output_h=False, cp_segments=0, cu_seqlens_cpu=None):
+    """Forward.  Returns ``(g_cum, A, o, h, final_state)``: the chunk-local
+    cumsum of g (fp32), the per-chunk inverse A ``[B,T,Hv,64]``, the output,
+    the chunk-start states (``None`` unless ``output_h``) and the fp32 final
+    state (``None`` unless ``output_final_state``)."""
+    q, k, v, g, beta, initial_state = _contig(q, k, v, g, beta, initial_state)
+    c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments)
+    dev = q.device
+    B, T = q.shape[0], q.shape[1]
+    g_cum = torch.empty(B, T, c.Hv, dtype=torch.float32, device=dev)
+    A = torch.empty(B, T, c.Hv, CHUNK, dtype=q.dtype, device=dev)
+    o = torch.empty(B, T, c.Hv, c.V, dtype=q.dtype, device=dev)
+    h = None
+    if output_h:
+        nc = c.num_chunks()
+        h = torch.empty((nc, c.Hv) + c.state_shape(state_v_first)[2:], dtype=q.dtype, device=dev)
+    ht = torch.empty(c.state_shape(state_v_first), dtype=torch.float32, device=dev) \
+        if output_final_state else None
+    if initial_state is not None:
+        initial_state = initial_state.to(torch.float32).contiguous()
+    ws_bytes = lib.gdr_chunk_fwd_workspace_size(c.ref)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    check(lib.gdr_chunk_fwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(initial_state), _ptr(g_cum), _ptr(A), _ptr(o), _ptr(h), _ptr(ht),
+                            _ptr(ws), ws_bytes, _stream(dev)))
+    return g_cum, A, o, h, ht
+
+
+def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=None,
+                               cu_seqlens=None, state_v_first=False, dg_dtype=None,
+                               cp_segments=0, cu_seqlens_cpu=None):
+    """Backward.  ``g`` is the forward's fp32 ``g_cum`` output.  Returns
+    ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is the gradient with respect to
+    the raw log-decay g (dtype ``dg_dtype``, default the input dtype) and
+    ``dh0`` is ``None`` without an initial state."""
+    q, k, v, g, beta, A, do, dht, initial_state = _contig(q, k, v, g, beta, A, do, dht,
+                                                          initial_state)
+    if g.dtype != torch.float32:
+        raise GdrError(4, "the backward takes the forward's fp32 g_cum as g")
+    dg_dtype = q.dtype if dg_dtype is None else dg_dtype
+    c = _Call(q, v, dg_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments)
+    dev = q.device
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    db = torch.empty_like(beta)
+    dg = torch.empty(g.shape, dtype=dg_dtype, device=dev)
+    dh0 = None
+    if initial_state is not None:
+        initial_state = initial_state.to(torch.float32).contiguous()
+        dh0 = torch.empty(c.state_shape(state_v_first), dtype=torch.float32, device=dev)
+    if dht is not None:
+        dht = dht.to(torch.float32).contiguous()
+    ws_bytes = lib.gdr_chunk_bwd_workspace_size(c.ref)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    check(lib.gdr_chunk_bwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
+                            _ptr(do), _ptr(dht), _ptr(initial_state), _ptr(dq), _ptr(dk), _ptr(dv),
+                            _ptr(db), _ptr(dg), _ptr(dh0), _ptr(ws), ws_bytes, _stream(dev)))
+    return dq, dk, dv, db, dg, dh0
+
+
+class _GatedDeltaRule(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                state_v_first, cp_segments, cu_seqlens_cpu):
+        g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
+            q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+            state_v_first, False, cp_segments, cu_seqlens_cpu)
+        ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, cu_seqlens_cpu)
+        ctx.scale, ctx.svf, ctx.cp, ctx.g_dtype = scale, state_v_first, cp_segments, g.dtype
+        return o, ht
+
+    @staticmethod
+    def backward(ctx, do, dht):
+        q, k, v, g_cum, beta, A, h0, cu, cu_cpu = ctx.saved_tensors
+        dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(
+            q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu, ctx.svf, ctx.g_dtype, ctx.cp,
+            cu_cpu)
+        return dq, dk, dv, dg, db, None, dh0, None, None, None, None, None
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
+                           output_final_state=False, use_qk_l2norm_in_kernel=False,
+                           state_v_first=False, cu_seqlens=None, cp_segments=0,
+                           cu_seqlens_cpu=None, **unsupported):
+    """High-level op with autograd: returns ``(o, final_state)``.
+
+    Options the FLA backend pull request lists as rejected by the FlashQLA
+    verifier (use_gate_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
+    inter-card context parallelism, transpose_state_layout) raise
+    NotImplementedError, as does use_qk_l2norm_in_kernel."""
+    for key, val in unsupported.items():
+        if val:
+            raise NotImplementedError("%s is not supported" % key)
+    if use_qk_l2norm_in_kernel:
+        raise NotImplementedError("use_qk_l2norm_in_kernel is not supported yet")
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    return _GatedDeltaRule.apply(q, k, v, g, beta, scale, initial_state, output_final_state,
+                                 cu_seqlens, state_v_first, cp_segments, cu_seqlens_cpu)
+
+
+# ---- variable-length helpers ------------------------------------------------
+
+def _cu_host(cu_seqlens):
+    cu = cu_seqlens.detach().to("cpu")
+    if cu.dtype == torch.int32:
+        return cu.contiguous(), "i32"
+    return cu.to(torch.int64).contiguous(), "i64"
+
+
+def prepare_lens(cu_seqlens: torch.Tensor) -> torch.Tensor:
+    """Sequence lengths ``cu[i+1] - cu[i]`` (same dtype and device)."""
+    cu, sfx = _cu_host(cu_seqlens)
+    out = torch.empty(max(cu.numel() - 1, 0), dtype=cu.dtype)
+    check(getattr(lib, "gdr_prepare_lens_" + sfx)(_ptr(cu), cu.numel(), _ptr(out)))
+    return out.to(cu_seqlens.device)
+
+
+def prepare_chunk_indices(cu_seqlens: torch.Tensor, chunk_size: int) -> torch.Tensor:
+    """``[num_chunks, 2]``: per chunk, its sequence index and its chunk index
+    inside that sequence."""
+    cu, sfx = _cu_host(cu_seqlens)
+    n = ctypes.c_int64(0)
+    f = getattr(lib, "gdr_prepare_chunk_indices_" + sfx)
+    check(f(_ptr(cu), cu.numel(), int(chunk_size), None, ctypes.byref(n)))
+    out = torch.empty(int(n.value), 2, dtype=cu.dtype)
+    check(f(_ptr(cu), cu.numel(), int(chunk_size), _ptr(out), ctypes.byref(n)))
+    return out.to(cu_seqlens.device)
+
+
+def prepare_chunk_offsets(cu_seqlens: torch.Tensor, chunk_size: int):
+    """``(chunk_offsets, total_chunks)``: offsets has the shape of cu_seqlens;
+    chunk c of sequence n sits at row ``chunk_offsets[n] + c`` of a global
+    per-chunk buffer."""
+    cu, sfx = _cu_host(cu_seqlens)
+    out = torch.empty(cu.numel(), dtype=cu.dtype)
+    total = ctypes.c_int64(0)
+    check(getattr(lib, "gdr_prepare_chunk_offsets_" + sfx)(_ptr(cu), cu.numel(), int(chunk_size),
+                                                           _ptr(out), ctypes.byref(total)))
+    return out.to(cu_seqlens.device), int(total.value)

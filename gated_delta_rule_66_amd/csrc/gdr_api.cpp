@@ -1,0 +1,348 @@
+// gdr_api.cpp -- the C ABI of libgdr: argument validation, launch planning,
+// workspace sizes and the variable-length helpers.  Everything here is host
+// code; validation finishes before the first HIP call, so every rejection can
+// be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "gdr_internal.h"
+
+namespace gdr {
+
+static thread_local char g_last_error[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+static gdr_status fail(gdr_status s, char* reason, size_t len, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  memcpy(g_last_error, buf, sizeof(buf));
+  if (reason && len) {
+    strncpy(reason, buf, len - 1);
+    reason[len - 1] = '\0';
+  }
+  return s;
+}
+
+// Context-parallel plan along T: it depends only on shapes (never on data),
+// so every run of a problem, in either state layout, takes the same path.
+Plan make_plan(const gdr_problem* p) {
+  Plan pl;
+  pl.N = p->N;
+  pl.total_chunks = 0;
+  pl.max_len = 0;
+  pl.nc_dense = 0;
+  if (p->cu_seqlens_host) {
+    for (int n = 0; n < p->N; ++n) {
+      const int64_t L = (int64_t)p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n];
+      pl.total_chunks += (L + kChunk - 1) / kChunk;
+      if (L > pl.max_len) pl.max_len = L;
+    }
+  } else {
+    pl.nc_dense = (p->T + kChunk - 1) / kChunk;
+    pl.total_chunks = (int64_t)pl.nc_dense * p->B;
+    pl.max_len = p->T;
+  }
+  pl.cp = 1;
+  pl.cp_chunks = 0;
+  return pl;
+}
+
+static bool is_half(gdr_dtype d) { return d == GDR_BF16 || d == GDR_FP16; }
+
+static gdr_status validate(const gdr_problem* p, char* reason, size_t len) {
+  if (!p) return fail(GDR_ERR_NULL, reason, len, "problem descriptor is NULL");
+  if (p->K != kDim) return fail(GDR_ERR_HEAD_DIM, reason, len, "requires K=128, got %d", p->K);
+  if (p->V != kDim) return fail(GDR_ERR_HEAD_DIM, reason, len, "requires V=128, got %d", p->V);
+  if (!is_half(p->in_dtype))
+    return fail(GDR_ERR_DTYPE, reason, len,
+                "q/k/v must be bf16 or fp16 (got dtype code %d)", (int)p->in_dtype);
+  if (p->g_dtype != p->in_dtype && p->g_dtype != GDR_FP32)
+    return fail(GDR_ERR_DTYPE, reason, len, "g must have the input dtype or fp32 (got code %d)",
+                (int)p->g_dtype);
+  if (p->B < 1 || p->T < 1 || p->Hq < 1 || p->Hv < 1)
+    return fail(GDR_ERR_SHAPE, reason, len, "sizes must be positive (B=%d T=%d Hq=%d Hv=%d)",
+                p->B, p->T, p->Hq, p->Hv);
+  if (p->Hq > p->Hv || p->Hv % p->Hq != 0)
+    return fail(GDR_ERR_HEADS, reason, len,
+                "value heads must be a multiple of q/k heads (Hq=%d Hv=%d)", p->Hq, p->Hv);
+  if ((int64_t)p->B * p->T * p->Hv * kDim > ((int64_t)1 << 40))
+    return fail(GDR_ERR_SHAPE, reason, len, "problem too large");
+  if (!std::isfinite(p->scale)) return fail(GDR_ERR_ARG, reason, len, "scale must be finite");
+  if (p->state_v_first != 0 && p->state_v_first != 1)
+    return fail(GDR_ERR_ARG, reason, len, "state_v_first must be 0 or 1");
+  if (p->cp_segments < 0) return fail(GDR_ERR_ARG, reason, len, "cp_segments must be >= 0");
+  const bool has_dev = p->cu_seqlens_dev != nullptr, has_host = p->cu_seqlens_host != nullptr;
+  if (has_dev != has_host)
+    return fail(GDR_ERR_VARLEN, reason, len,
+                "cu_seqlens needs both the device and the host copy");
+  if (has_dev) {
+    if (p->B != 1)
+      return fail(GDR_ERR_VARLEN, reason, len, "packed input needs B == 1, got %d", p->B);
+    if (p->N < 1) return fail(GDR_ERR_VARLEN, reason, len, "N must be >= 1 with cu_seqlens");
+    const int32_t* cu = p->cu_seqlens_host;
+    if (cu[0] != 0) return fail(GDR_ERR_VARLEN, reason, len, "cu_seqlens[0] must be 0");
+    for (int n = 0; n < p->N; ++n)
+      if (cu[n + 1] < cu[n])
+        return fail(GDR_ERR_VARLEN, reason, len, "cu_seqlens decreases at %d", n + 1);
+    if (cu[p->N] != p->T)
+      return fail(GDR_ERR_VARLEN, reason, len, "cu_seqlens[N]=%d must equal T=%d", cu[p->N],
+                  p->T);
+  } else if (p->N != p->B) {
+    return fail(GDR_ERR_SHAPE, reason, len, "dense input needs N == B (N=%d B=%d)", p->N, p->B);
+  }
+  return GDR_OK;
+}
+
+static gdr_status check_device_cached() {
+  static std::mutex mu;
+  static int known[64];  // 0 unknown, 1 ok, 2 bad
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    set_error("no HIP device is available");
+    return GDR_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev < 64 && known[dev] == 1) return GDR_OK;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    set_error("hipGetDeviceProperties failed for device %d", dev);
+    return GDR_ERR_DEVICE;
+  }
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) known[dev] = ok ? 1 : 2;
+  if (!ok) {
+    set_error("device %d is %s; this library is built for gfx950 (MI355X)", dev,
+              prop.gcnArchName);
+    return GDR_ERR_DEVICE;
+  }
+  return GDR_OK;
+}
+
+template <typename I>
+static gdr_status check_cu(const I* cu, int64_t n1) {
+  if (!cu) {
+    set_error("cu_seqlens is NULL");
+    return GDR_ERR_NULL;
+  }
+  if (n1 < 1) {
+    set_error("cu_seqlens needs at least one entry");
+    return GDR_ERR_VARLEN;
+  }
+  if (cu[0] != 0) {
+    set_error("cu_seqlens[0] must be 0");
+    return GDR_ERR_VARLEN;
+  }
+  for (int64_t i = 1; i < n1; ++i)
+    if (cu[i] < cu[i - 1]) {
+      set_error("cu_seqlens decreases at %lld", (long long)i);
+      return GDR_ERR_VARLEN;
+    }
+  return GDR_OK;
+}
+
+template <typename I>
+static gdr_status lens_impl(const I* cu, int64_t n1, I* lens) {
+  gdr_status s = check_cu(cu, n1);
+  if (s != GDR_OK) return s;
+  if (!lens && n1 > 1) {
+    set_error("lens is NULL");
+    return GDR_ERR_NULL;
+  }
+  for (int64_t i = 0; i + 1 < n1; ++i) lens[i] = cu[i + 1] - cu[i];
+  return GDR_OK;
+}
+
+template <typename I>
+static gdr_status indices_impl(const I* cu, int64_t n1, int64_t bt, I* out, int64_t* nc) {
+  gdr_status s = check_cu(cu, n1);
+  if (s != GDR_OK) return s;
+  if (bt < 1) {
+    set_error("chunk_size must be >= 1");
+    return GDR_ERR_ARG;
+  }
+  if (!nc) {
+    set_error("num_chunks is NULL");
+    return GDR_ERR_NULL;
+  }
+  int64_t m = 0;
+  for (int64_t i = 0; i + 1 < n1; ++i) {
+    const int64_t c = ((int64_t)cu[i + 1] - cu[i] + bt - 1) / bt;
+    for (int64_t j = 0; j < c; ++j, ++m)
+      if (out) {
+        out[2 * m] = (I)i;
+        out[2 * m + 1] = (I)j;
+      }
+  }
+  *nc = m;
+  return GDR_OK;
+}
+
+template <typename I>
+static gdr_status offsets_impl(const I* cu, int64_t n1, int64_t bt, I* offs, int64_t* total) {
+  gdr_status s = check_cu(cu, n1);
+  if (s != GDR_OK) return s;
+  if (bt < 1) {
+    set_error("chunk_size must be >= 1");
+    return GDR_ERR_ARG;
+  }
+  if (!offs) {
+    set_error("offsets is NULL");
+    return GDR_ERR_NULL;
+  }
+  int64_t acc = 0;
+  offs[0] = 0;
+  for (int64_t i = 0; i + 1 < n1; ++i) {
+    acc += ((int64_t)cu[i + 1] - cu[i] + bt - 1) / bt;
+    offs[i + 1] = (I)acc;
+  }
+  if (total) *total = acc;
+  return GDR_OK;
+}
+
+}  // namespace gdr
+
+using namespace gdr;
+
+extern "C" {
+
+const char* gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_NULL: return "GDR_ERR_NULL";
+    case GDR_ERR_SHAPE: return "GDR_ERR_SHAPE";
+    case GDR_ERR_HEAD_DIM: return "GDR_ERR_HEAD_DIM";
+    case GDR_ERR_DTYPE: return "GDR_ERR_DTYPE";
+    case GDR_ERR_HEADS: return "GDR_ERR_HEADS";
+    case GDR_ERR_VARLEN: return "GDR_ERR_VARLEN";
+    case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE";
+    case GDR_ERR_DEVICE: return "GDR_ERR_DEVICE";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP";
+    case GDR_ERR_ARG: return "GDR_ERR_ARG";
+  }
+  return "GDR_UNKNOWN";
+}
+
+const char* gdr_last_error(void) { return g_last_error; }
+
+gdr_status gdr_check_supported(const gdr_problem* p, char* reason, size_t reason_len) {
+  gdr_status s = validate(p, reason, reason_len);
+  if (s == GDR_OK && reason && reason_len) reason[0] = '\0';
+  return s;
+}
+
+gdr_status gdr_check_device(void) { return check_device_cached(); }
+
+size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
+  if (validate(p, nullptr, 0) != GDR_OK) return 0;
+  return fwd_workspace_bytes(p, make_plan(p));
+}
+
+size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p) {
+  if (validate(p, nullptr, 0) != GDR_OK) return 0;
+  return bwd_workspace_bytes(p, make_plan(p));
+}
+
+gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, const float* initial_state,
+                         float* g_cum, void* A, void* o, void* h, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  if (!q || !k || !v || !g || !beta || !g_cum || !A || !o)
+    return fail(GDR_ERR_NULL, nullptr, 0, "a required forward pointer is NULL");
+  const Plan pl = make_plan(p);
+  const size_t need = fwd_workspace_bytes(p, pl);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDR_ERR_WORKSPACE, nullptr, 0, "forward workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  s = check_device_cached();
+  if (s != GDR_OK) return s;
+  return launch_fwd(p, pl, q, k, v, g, beta, initial_state, g_cum, A, o, h, final_state,
+                    workspace, (hipStream_t)stream);
+}
+
+gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const float* g_cum, const void* beta, const void* A, const void* do_,
+                         const float* dht, const float* initial_state, void* dq, void* dk,
+                         void* dv, void* dbeta, void* dg, float* dh0, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  if (!q || !k || !v || !g_cum || !beta || !A || !do_ || !dq || !dk || !dv || !dbeta || !dg)
+    return fail(GDR_ERR_NULL, nullptr, 0, "a required backward pointer is NULL");
+  if (initial_state && !dh0)
+    return fail(GDR_ERR_NULL, nullptr, 0, "dh0 is required when initial_state is given");
+  const Plan pl = make_plan(p);
+  const size_t need = bwd_workspace_bytes(p, pl);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDR_ERR_WORKSPACE, nullptr, 0, "backward workspace needs %zu bytes, got %zu",
+                need, workspace ? workspace_bytes : (size_t)0);
+  s = check_device_cached();
+  if (s != GDR_OK) return s;
+  return launch_bwd(p, pl, q, k, v, g_cum, beta, A, do_, dht, initial_state, dq, dk, dv, dbeta,
+                    dg, initial_state ? dh0 : nullptr, workspace, (hipStream_t)stream);
+}
+
+gdr_status gdr_prepare_lens_i32(const int32_t* cu, int64_t n1, int32_t* lens) {
+  return lens_impl(cu, n1, lens);
+}
+gdr_status gdr_prepare_lens_i64(const int64_t* cu, int64_t n1, int64_t* lens) {
+  return lens_impl(cu, n1, lens);
+}
+gdr_status gdr_prepare_chunk_indices_i32(const int32_t* cu, int64_t n1, int64_t bt, int32_t* out,
+                                         int64_t* nc) {
+  return indices_impl(cu, n1, bt, out, nc);
+}
+gdr_status gdr_prepare_chunk_indices_i64(const int64_t* cu, int64_t n1, int64_t bt, int64_t* out,
+                                         int64_t* nc) {
+  return indices_impl(cu, n1, bt, out, nc);
+}
+gdr_status gdr_prepare_chunk_offsets_i32(const int32_t* cu, int64_t n1, int64_t bt,
+                                         int32_t* offs, int64_t* total) {
+  return offsets_impl(cu, n1, bt, offs, total);
+}
+gdr_status gdr_prepare_chunk_offsets_i64(const int64_t* cu, int64_t n1, int64_t bt,
+                                         int64_t* offs, int64_t* total) {
+  return offsets_impl(cu, n1, bt, offs, total);
+}
+gdr_status gdr_prepare_chunk_token_starts_i64(const int64_t* cu, int64_t n1, int64_t bt,
+                                              int64_t* out, int64_t* nc) {
+  gdr_status s = check_cu(cu, n1);
+  if (s != GDR_OK) return s;
+  if (bt < 1) {
+    set_error("chunk_size must be >= 1");
+    return GDR_ERR_ARG;
+  }
+  if (!nc) {
+    set_error("num_chunks is NULL");
+    return GDR_ERR_NULL;
+  }
+  int64_t m = 0;
+  for (int64_t i = 0; i + 1 < n1; ++i) {
+    for (int64_t t = cu[i]; t < cu[i + 1]; t += bt, ++m)
+      if (out) {
+        out[2 * m] = t;
+        out[2 * m + 1] = m;
+      }
+  }
+  *nc = m;
+  return GDR_OK;
+}
+
+}  // extern "C"

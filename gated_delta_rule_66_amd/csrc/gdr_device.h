@@ -1,0 +1,199 @@
+// gdr_device.h -- device-side building blocks for the gfx950 kernels.
+//
+// MFMA fragment conventions (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
+//   lane l = 16 * grp + col,  grp = l / 16 in [0, 4),  col = l % 16
+//   A operand (16 x 32): lane holds A[col][k(grp, e)] for e in [0, 8)
+//   B operand (32 x 16): lane holds B[k(grp, e)][col]
+//   D/C (16 x 16 fp32):  lane holds D[4 * grp + e][col] for e in [0, 4)
+// The hardware only needs A and B to agree on the k order, so two orders are
+// used:
+//   contiguous: k = 8 * grp + e
+//   split:      k = 4 * grp + e (e < 4),  16 + 4 * grp + (e - 4) (e >= 4)
+// The split order is exactly how two vertically stacked D tiles sit in a
+// lane, so an fp32 accumulator pair becomes a B operand by a register-local
+// conversion (pack_split) with no data movement.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T>
+struct VT;
+template <>
+struct VT<__bf16> {
+  typedef bf16x8 x8;
+  typedef bf16x4 x4;
+};
+template <>
+struct VT<_Float16> {
+  typedef f16x8 x8;
+  typedef f16x4 x4;
+};
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// fp32 16x16x4: A lane holds A[col][grp] (k = grp), B lane holds B[grp][col].
+__device__ __forceinline__ f32x4 mfma16f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+template <typename T>
+__device__ __forceinline__ float to_f(T x) {
+  return (float)x;
+}
+template <typename T>
+__device__ __forceinline__ T from_f(float x) {
+  return (T)x;  // round to nearest even
+}
+
+// ---- operand fragments read from LDS -------------------------------------
+// `base` points at element (row0, k0) of a row-major matrix with leading
+// dimension ld (elements).  Rows are the 16 A-rows (or B-columns).
+
+// contiguous k order: one 16-byte read
+template <typename T>
+__device__ __forceinline__ typename VT<T>::x8 frag_row(const T* base, int ld) {
+  const int l = lane_id();
+  return *reinterpret_cast<const typename VT<T>::x8*>(base + (l & 15) * ld + 8 * (l >> 4));
+}
+
+// split k order: two 8-byte reads
+template <typename T>
+__device__ __forceinline__ typename VT<T>::x8 frag_row_split(const T* base, int ld) {
+  const int l = lane_id();
+  const T* p = base + (l & 15) * ld + 4 * (l >> 4);
+  typename VT<T>::x4 lo = *reinterpret_cast<const typename VT<T>::x4*>(p);
+  typename VT<T>::x4 hi = *reinterpret_cast<const typename VT<T>::x4*>(p + 16);
+  return typename VT<T>::x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Transposed fragment, split k order: the operand's k index runs down the
+// ROWS of a row-major LDS matrix X[k][m] (m contiguous); `base` points at
+// X[k0][m0].  Lane (grp, col) receives X[k0 + k(grp, e)][m0 + col].  Uses
+// ds_read_b64_tr_b16: inside each 16-lane group, lane j gets element j % 4 of
+// the 8-byte slot addressed by lane 4e + j / 4, for e = 0..3.
+template <typename T>
+__device__ __forceinline__ typename VT<T>::x8 frag_tr_split(const T* base, int ld) {
+  const int l = lane_id();
+  const int grp = l >> 4, j = l & 15;
+  const T* p0 = base + (4 * grp + (j >> 2)) * ld + 4 * (j & 3);
+  const T* p1 = p0 + 16 * ld;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  i16x8 r = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename VT<T>::x8, r);
+}
+
+// Transposed fragment, contiguous k order.
+template <typename T>
+__device__ __forceinline__ typename VT<T>::x8 frag_tr(const T* base, int ld) {
+  const int l = lane_id();
+  const int grp = l >> 4, j = l & 15;
+  const T* p0 = base + (8 * grp + (j >> 2)) * ld + 4 * (j & 3);
+  const T* p1 = p0 + 4 * ld;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  i16x8 r = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename VT<T>::x8, r);
+}
+
+// Two stacked fp32 D tiles (rows 0..15 and 16..31 of a 32-row block) become a
+// split-order B operand (k = the 32 rows).
+template <typename T>
+__device__ __forceinline__ typename VT<T>::x8 pack_split(f32x4 top, f32x4 bot) {
+  return typename VT<T>::x8{from_f<T>(top[0]), from_f<T>(top[1]), from_f<T>(top[2]),
+                            from_f<T>(top[3]), from_f<T>(bot[0]), from_f<T>(bot[1]),
+                            from_f<T>(bot[2]), from_f<T>(bot[3])};
+}
+
+// ---- global <-> LDS tile copies -------------------------------------------
+// Copy `rows` valid rows (the rest zero-filled, up to 64) of a row-major tile
+// of `cols` elements (cols % 8 == 0) whose rows sit `gstride` elements apart
+// in global memory into LDS with leading dimension ld.  16-byte transfers,
+// all threads of the block cooperate.
+template <typename T, int NT>
+__device__ __forceinline__ void tile_to_lds(T* lds, int ld, const T* g, int64_t gstride, int rows,
+                                            int cols) {
+  const int per_row = cols / 8;
+  const int total = 64 * per_row;
+  for (int x = threadIdx.x; x < total; x += NT) {
+    const int r = x / per_row, c8 = (x % per_row) * 8;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (r < rows) val = *reinterpret_cast<const uint4*>(g + r * gstride + c8);
+    *reinterpret_cast<uint4*>(lds + r * ld + c8) = val;
+  }
+}
+
+__device__ __forceinline__ float load_scalar(const void* p, int64_t idx, int dtype) {
+  // dtype: 0 bf16, 1 fp16, 2 fp32
+  if (dtype == 0) return (float)reinterpret_cast<const __bf16*>(p)[idx];
+  if (dtype == 1) return (float)reinterpret_cast<const _Float16*>(p)[idx];
+  return reinterpret_cast<const float*>(p)[idx];
+}
+
+__device__ __forceinline__ void store_scalar(void* p, int64_t idx, int dtype, float v) {
+  if (dtype == 0) reinterpret_cast<__bf16*>(p)[idx] = (__bf16)v;
+  else if (dtype == 1) reinterpret_cast<_Float16*>(p)[idx] = (_Float16)v;
+  else reinterpret_cast<float*>(p)[idx] = v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (fixed combination order).
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (l >= off) x += y;
+  }
+  return x;
+}
+
+// Where a (sequence, chunk) pair starts.  Dense batches: sequence n spans
+// tokens [n*T, n*T + T).  Packed input: cu_seqlens.
+struct SeqInfo {
+  int64_t start, end;
+};
+__device__ __forceinline__ SeqInfo seq_info(const int32_t* cu, int n, int T) {
+  SeqInfo s;
+  if (cu) {
+    s.start = cu[n];
+    s.end = cu[n + 1];
+  } else {
+    s.start = (int64_t)n * T;
+    s.end = s.start + T;
+  }
+  return s;
+}
+
+// Largest n in [0, N) with offs[n] <= c (offs non-decreasing, offs[0] = 0).
+__device__ __forceinline__ int find_seq(const int32_t* offs, int N, int c) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace gdr

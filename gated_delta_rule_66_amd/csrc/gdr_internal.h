@@ -1,0 +1,45 @@
+// gdr_internal.h -- host-side interface between the C ABI and the launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdr.h"
+
+namespace gdr {
+
+constexpr int kChunk = 64;
+constexpr int kDim = 128;
+
+// Launch plan derived from the problem on the host (no device access).
+struct Plan {
+  int N;              // sequences
+  int64_t total_chunks;
+  int nc_dense;       // chunks per sequence for dense batches (0 for packed)
+  int64_t max_len;    // longest sequence
+  int cp;             // context-parallel segments per sequence (1 = off)
+  int64_t cp_chunks;  // chunks per segment when cp > 1
+};
+
+Plan make_plan(const gdr_problem* p);
+
+// Workspace layout helpers: every region is 256-byte aligned.
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t fwd_workspace_bytes(const gdr_problem* p, const Plan& pl);
+size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl);
+
+gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
+                      const void* v, const void* g, const void* beta, const float* h0,
+                      float* gcum, void* A, void* o, void* h, float* ht, void* ws,
+                      hipStream_t st);
+
+gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
+                      const void* v, const float* gcum, const void* beta, const void* A,
+                      const void* dO, const float* dht, const float* h0, void* dq, void* dk,
+                      void* dv, void* dbeta, void* dg, float* dh0, void* ws, hipStream_t st);
+
+void set_error(const char* fmt, ...);
+
+}  // namespace gdr

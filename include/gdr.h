@@ -1,0 +1,179 @@
+/*
+ * gdr.h -- C ABI of libgdr: the chunked gated delta rule (GDN chunked prefill)
+ * forward and backward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation
+ * -------------
+ * FlashQLA pages ("flashqla-linear-attention", Core API; "FlashQLA
+ * Documentation", forward / backward) define the tensors; the recurrence is
+ * the gated delta rule of Gated Delta Networks (Yang, Kautz, Hatamizadeh,
+ * 2024).  For every sequence n and value head h (q/k head hq = h / (Hv/Hq),
+ * grouped value attention), with a K x V fp32 state S:
+ *
+ *     S_t = exp(g_t) S_{t-1} + beta_t k_t (v_t - exp(g_t) S_{t-1}^T k_t)^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * computed chunk by chunk (64 tokens) in the WY form: per chunk, gamma is the
+ * chunk-local inclusive cumsum of g, A = (I + strict_lower(diag(beta) K K^T o
+ * exp(gamma_r - gamma_i)))^{-1} is unit lower triangular, and the state moves
+ * from chunk to chunk by S <- e^{gamma_L} S + K^T diag(e^{gamma_L-gamma})
+ * A (diag(beta) V - diag(beta e^gamma) K S).
+ *
+ * Tensor layouts (row-major, contiguous, tokens of all sequences flattened):
+ *   q, k          [B, T, Hq, K]           in_dtype
+ *   v, o, do, dv  [B, T, Hv, V]           in_dtype
+ *   g, dg         [B, T, Hv]              g_dtype (natural-log decay)
+ *   beta, dbeta   [B, T, Hv]              in_dtype
+ *   g_cum         [B, T, Hv]              fp32: chunk-local inclusive cumsum of g
+ *   A             [B, T, Hv, 64]          in_dtype: row r of a chunk's inverse
+ *                                         at token chunk_start + r; columns past
+ *                                         a partial chunk are 0
+ *   h             [NC, Hv, K, V]          in_dtype: state at the start of each
+ *                                         chunk, chunk c of sequence n at row
+ *                                         chunk_offsets[n] + c
+ *   states        [N, Hv, K, V]           fp32: initial_state, final_state,
+ *                                         dht, dh0
+ * With state_v_first != 0 every state tensor (h included) is [.., V, K]
+ * instead; the results are then bit-identical transposes of the default.
+ * Packed variable-length input (cu_seqlens != NULL) has B == 1 and T the total
+ * token count; N = number of sequences.  K and V must be 128.
+ *
+ * Conventions
+ * -----------
+ * - The caller owns every buffer and the stream.  The library allocates no
+ *   device memory, keeps no pointer after a call returns and never
+ *   synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *   null stream) and buffers must stay alive until the stream reaches it.
+ * - Outputs are overwritten, never accumulated.  Inputs and outputs must not
+ *   alias.  Device pointers must be 16-byte aligned.
+ * - Every argument is validated on the host before any HIP call; a failure
+ *   returns a status (never aborts) and gdr_last_error() describes it.
+ * - Results are deterministic: no floating-point atomics, fixed reduction
+ *   orders, and a context-parallel plan that depends only on shapes.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_ERR_NULL = 1,      /* a required pointer is NULL */
+  GDR_ERR_SHAPE = 2,     /* non-positive or inconsistent sizes */
+  GDR_ERR_HEAD_DIM = 3,  /* K != 128 or V != 128 */
+  GDR_ERR_DTYPE = 4,     /* q/k/v not bf16/fp16, or g not in_dtype/fp32 */
+  GDR_ERR_HEADS = 5,     /* Hq > Hv or Hv % Hq != 0 */
+  GDR_ERR_VARLEN = 6,    /* malformed cu_seqlens */
+  GDR_ERR_WORKSPACE = 7, /* workspace missing or too small */
+  GDR_ERR_DEVICE = 8,    /* no gfx950 device current */
+  GDR_ERR_HIP = 9,       /* a HIP launch failed */
+  GDR_ERR_ARG = 10       /* another bad argument (scale, chunk size, flags) */
+} gdr_status;
+
+typedef enum { GDR_BF16 = 0, GDR_FP16 = 1, GDR_FP32 = 2 } gdr_dtype;
+
+typedef struct {
+  int32_t B, T, Hq, Hv, K, V;
+  int32_t N;                      /* sequences: B, or len(cu_seqlens) - 1 */
+  const int32_t* cu_seqlens_dev;  /* device [N+1] token offsets, or NULL (dense) */
+  const int32_t* cu_seqlens_host; /* host copy of the same; used to plan launches
+                                     without a device-to-host copy; NULL iff the
+                                     device pointer is NULL */
+  gdr_dtype in_dtype;             /* q, k, v, beta, do, o, A, h and their grads */
+  gdr_dtype g_dtype;              /* raw g and dg: in_dtype or GDR_FP32 */
+  float scale;                    /* output scale, usually K^-0.5 */
+  int32_t state_v_first;          /* 0: states [.., K, V]; 1: [.., V, K] */
+  int32_t cp_segments;            /* intra-GPU context parallelism along T:
+                                     0 = automatic plan, 1 = off, s > 1 = split
+                                     every sequence into up to s segments */
+} gdr_problem;
+
+/* Status name ("GDR_ERR_SHAPE", ...). */
+const char* gdr_status_string(gdr_status s);
+
+/* Description of the last failure in the calling thread ("" if none). */
+const char* gdr_last_error(void);
+
+/* Host-only argument check, the analogue of the verifier in the FLA backend
+ * pull request ("[GDN] Add FlashQLA backend dispatch", Changes and review
+ * threads: K != 128, V != 128 and unsupported dtypes are rejected with a
+ * reason).  Writes a NUL-terminated reason into `reason` (may be NULL). */
+gdr_status gdr_check_supported(const gdr_problem* p, char* reason, size_t reason_len);
+
+/* Device check: the current HIP device is a gfx950.  GDR_ERR_DEVICE if not. */
+gdr_status gdr_check_device(void);
+
+/* Bytes of device workspace gdr_chunk_fwd / gdr_chunk_bwd need for `p`
+ * (0 if `p` is invalid).  Depends only on the problem's shapes. */
+size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p);
+size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p);
+
+/* Forward ("flashqla-linear-attention", Low-Level API; "FlashQLA
+ * Documentation", forward pass returning g, A, o, h, final_state).
+ *   in : q, k, v, g, beta; initial_state (nullable, fp32 state layout)
+ *   out: g_cum, A, o (required); h (nullable: chunk-start states);
+ *        final_state (nullable: output_final_state == False)
+ *   workspace: device buffer of gdr_chunk_fwd_workspace_size(p) bytes. */
+gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, const float* initial_state,
+                         float* g_cum, void* A, void* o, void* h, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward ("FlashQLA Documentation", backward pass: takes q, k, v, the g
+ * returned by the forward, beta, A, do, dht, scale, initial_state, cu_seqlens
+ * and returns dq, dk, dv, db, dg, dh0).
+ *   in : q, k, v, g_cum (the forward's fp32 g output), beta, A (forward
+ *        output), do; dht (nullable = zero); initial_state (nullable = zero)
+ *   out: dq, dk (in_dtype, [B,T,Hq,K]); dv; dbeta; dg (g_dtype, gradient with
+ *        respect to the raw g); dh0 (fp32, written iff initial_state != NULL,
+ *        may be NULL otherwise)
+ *   workspace: device buffer of gdr_chunk_bwd_workspace_size(p) bytes. */
+gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const float* g_cum, const void* beta, const void* A, const void* do_,
+                         const float* dht, const float* initial_state, void* dq, void* dk,
+                         void* dv, void* dbeta, void* dg, float* dh0, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Variable-length helpers (host, pure integer, bit-exact), after the
+ * utilities of the "FlashQLA Documentation" page.  `cu` holds n_plus_1
+ * non-decreasing offsets starting at 0.  Each returns GDR_ERR_VARLEN for a
+ * malformed `cu`, GDR_ERR_ARG for chunk_size < 1.
+ *
+ * prepare_lens: lens[i] = cu[i+1] - cu[i]   (n_plus_1 - 1 entries). */
+gdr_status gdr_prepare_lens_i32(const int32_t* cu, int64_t n_plus_1, int32_t* lens);
+gdr_status gdr_prepare_lens_i64(const int64_t* cu, int64_t n_plus_1, int64_t* lens);
+
+/* prepare_chunk_indices: one row per chunk, in sequence order, holding
+ * [sequence index n, chunk index j within sequence n]; the chunk's first
+ * token is cu[n] + j * chunk_size.  `out` ([num_chunks, 2]) may be NULL to
+ * query *num_chunks only. */
+gdr_status gdr_prepare_chunk_indices_i32(const int32_t* cu, int64_t n_plus_1, int64_t chunk_size,
+                                         int32_t* out, int64_t* num_chunks);
+gdr_status gdr_prepare_chunk_indices_i64(const int64_t* cu, int64_t n_plus_1, int64_t chunk_size,
+                                         int64_t* out, int64_t* num_chunks);
+
+/* prepare_chunk_offsets: offsets[0] = 0, offsets[i+1] = offsets[i] +
+ * ceil(lens[i] / chunk_size) (n_plus_1 entries, the shape of cu), and
+ * *total = offsets[n_plus_1 - 1]: the row of chunk c of sequence n in a
+ * global per-chunk buffer such as h is offsets[n] + c. */
+gdr_status gdr_prepare_chunk_offsets_i32(const int32_t* cu, int64_t n_plus_1, int64_t chunk_size,
+                                         int32_t* offsets, int64_t* total);
+gdr_status gdr_prepare_chunk_offsets_i64(const int64_t* cu, int64_t n_plus_1, int64_t chunk_size,
+                                         int64_t* offsets, int64_t* total);
+
+/* The literal reading of the chunk-index description: one row per chunk
+ * holding [first token of the chunk, global chunk id]. */
+gdr_status gdr_prepare_chunk_token_starts_i64(const int64_t* cu, int64_t n_plus_1,
+                                              int64_t chunk_size, int64_t* out,
+                                              int64_t* num_chunks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */
