@@ -37,6 +37,20 @@ static gdr_status fail(gdr_status s, char* reason, size_t len, const char* fmt, 
   return s;
 }
 
+// Estimated critical path (in units of one output-scan chunk step) of the
+// forward scan for a plan with P segments and VB column tiles per wave,
+// assuming one workgroup per CU on 256 CUs.
+static double plan_cost(int64_t units, int64_t maxch, int P, int VB) {
+  const double c_out = (VB == 2) ? 1.6 : 1.0;  // output scan, per chunk
+  const double c_st = (VB == 2) ? 1.0 : 0.6;   // transition scan, per chunk
+  const int64_t nvs0 = 2 / VB, nvs1 = 4 / VB;
+  auto rounds = [](int64_t wg) { return (double)((wg + 255) / 256); };
+  if (P == 1) return rounds(units * nvs0) * (double)maxch * c_out;
+  const int64_t sc = (maxch + P - 1) / P;
+  const int64_t wg1 = units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
+  return rounds(wg1) * sc * c_st + rounds(units * P * nvs0) * sc * c_out + 0.5 * (P - 1);
+}
+
 // Context-parallel plan along T: it depends only on shapes (never on data),
 // so every run of a problem, in either state layout, takes the same path.
 Plan make_plan(const gdr_problem* p) {
@@ -56,8 +70,29 @@ Plan make_plan(const gdr_problem* p) {
     pl.total_chunks = (int64_t)pl.nc_dense * p->B;
     pl.max_len = p->T;
   }
+  const int64_t units = (int64_t)p->N * p->Hv;
+  const int64_t maxch = (pl.max_len + kChunk - 1) / kChunk;
   pl.cp = 1;
-  pl.cp_chunks = 0;
+  pl.vb = 2;
+  double best = 1e300;
+  const int fixed = p->cp_segments;
+  for (int P = 1; P <= 16; P *= 2) {
+    if (fixed > 0 && P != fixed) continue;
+    if (fixed == 0 && P > 1 && maxch < 8 * P) continue;
+    for (int VB = 1; VB <= 2; ++VB) {
+      const double c = plan_cost(units, maxch, P, VB);
+      if (c < best) {
+        best = c;
+        pl.cp = P;
+        pl.vb = VB;
+      }
+    }
+  }
+  if (fixed > 0 && best == 1e300) {  // a segment count that is not a power of two
+    pl.cp = fixed;
+    pl.vb = 1;
+  }
+  if (pl.cp > maxch) pl.cp = maxch > 0 ? (int)maxch : 1;
   return pl;
 }
 

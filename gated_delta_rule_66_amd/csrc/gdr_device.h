@@ -144,6 +144,58 @@ __device__ __forceinline__ void tile_to_lds(T* lds, int ld, const T* g, int64_t 
   }
 }
 
+// Register-staged tile copies, split in two so that the global loads of the
+// next chunk can be in flight while the current chunk computes.  A 64-row
+// tile of COLS elements is NT-thread cooperative; thread t holds 16-byte
+// pieces x = t + i * NT (row x / (COLS/8), column (x % (COLS/8)) * 8).
+template <int COLS, int NT>
+struct TileRegs {
+  static constexpr int PER_ROW = COLS / 8;
+  static constexpr int N = (64 * PER_ROW) / NT;
+  static_assert((64 * PER_ROW) % NT == 0, "tile must split evenly");
+  uint4 r[N];
+};
+
+template <typename T, int COLS, int NT>
+__device__ __forceinline__ void tile_load(TileRegs<COLS, NT>& t, const T* g, int64_t gstride,
+                                          int rows) {
+  constexpr int PR = TileRegs<COLS, NT>::PER_ROW;
+#pragma unroll
+  for (int i = 0; i < TileRegs<COLS, NT>::N; ++i) {
+    const int x = threadIdx.x + i * NT;
+    const int r = x / PR, c8 = (x % PR) * 8;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (r < rows) val = *reinterpret_cast<const uint4*>(g + r * gstride + c8);
+    t.r[i] = val;
+  }
+}
+
+template <typename T, int COLS, int NT>
+__device__ __forceinline__ void tile_store(T* lds, int ld, const TileRegs<COLS, NT>& t) {
+  constexpr int PR = TileRegs<COLS, NT>::PER_ROW;
+#pragma unroll
+  for (int i = 0; i < TileRegs<COLS, NT>::N; ++i) {
+    const int x = threadIdx.x + i * NT;
+    const int r = x / PR, c8 = (x % PR) * 8;
+    *reinterpret_cast<uint4*>(lds + r * ld + c8) = t.r[i];
+  }
+}
+
+// LDS tile rows [0, rows) -> global, 16 bytes per store.
+template <typename T, int COLS, int NT>
+__device__ __forceinline__ void tile_from_lds(T* g, int64_t gstride, const T* lds, int ld,
+                                              int rows) {
+  constexpr int PR = COLS / 8;
+#pragma unroll
+  for (int i = 0; i < (64 * PR) / NT; ++i) {
+    const int x = threadIdx.x + i * NT;
+    const int r = x / PR, c8 = (x % PR) * 8;
+    if (r < rows)
+      *reinterpret_cast<uint4*>(g + r * gstride + c8) =
+          *reinterpret_cast<const uint4*>(lds + r * ld + c8);
+  }
+}
+
 __device__ __forceinline__ float load_scalar(const void* p, int64_t idx, int dtype) {
   // dtype: 0 bf16, 1 fp16, 2 fp32
   if (dtype == 0) return (float)reinterpret_cast<const __bf16*>(p)[idx];

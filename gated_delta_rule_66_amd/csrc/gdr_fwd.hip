@@ -22,6 +22,7 @@
 // S and R, Delta enter the next product as register-local B operands.
 #include "gdr_device.h"
 #include "gdr_internal.h"
+#include "gdr_scan.h"
 
 namespace gdr {
 
@@ -179,268 +180,100 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void fwd_scan_kernel(FwdArgs a) {
-  typedef typename VT<T>::x8 x8;
-  constexpr int LD = 136;
-  constexpr int LDA = 72;
-  __shared__ __align__(16) T Qs[64 * LD];
-  __shared__ __align__(16) T Ks[64 * LD];
-  __shared__ __align__(16) T Vs[64 * LD];
-  __shared__ __align__(16) T As[64 * LDA];
-  __shared__ __align__(16) T Ps[64 * LDA];
-  __shared__ float gam[64], bet[64], eg[64], bex[64], dl[64];
 
-  const int unit = blockIdx.x;
-  const int n = unit / a.Hv, h = unit % a.Hv;
-  const int G = a.Hv / a.Hq, hq = h / G;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
-  const SeqInfo s = seq_info(a.cu, n, a.T);
-  const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
-  const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
-  const int64_t KV = (int64_t)kDim * kDim;
-  const T* q = reinterpret_cast<const T*>(a.q);
-  const T* k = reinterpret_cast<const T*>(a.k);
-  const T* v = reinterpret_cast<const T*>(a.v);
-  const T* A = reinterpret_cast<const T*>(a.A);
-  const T* beta = reinterpret_cast<const T*>(a.beta);
-  T* o = reinterpret_cast<T*>(a.o);
-
-  // state S[key][vcol]: tile (kb, vb) = keys 16kb.., columns 32w + 16vb..
-  f32x4 S[8][2];
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-    for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 16 * kb + 4 * grp + e, vc = 32 * w + 16 * vb + col;
-        float x = 0.f;
-        if (a.h0) x = a.h0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)];
-        S[kb][vb][e] = x;
-      }
-
-  for (int c = 0; c < nch; ++c) {
-    const int64_t t0 = s.start + (int64_t)kChunk * c;
-    const int Cc = (int)min((int64_t)kChunk, s.end - t0);
-    if (a.h) {
-      T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = 16 * kb + 4 * grp + e, vc = 32 * w + 16 * vb + col;
-            hp[a.svf ? vc * kDim + key : key * kDim + vc] = from_f<T>(S[kb][vb][e]);
-          }
-    }
-    __syncthreads();  // the previous chunk is done with LDS
-    tile_to_lds<T, 256>(Qs, LD, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, kDim);
-    tile_to_lds<T, 256>(Ks, LD, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, kDim);
-    tile_to_lds<T, 256>(Vs, LD, v + (t0 * a.Hv + h) * kDim, (int64_t)a.Hv * kDim, Cc, kDim);
-    tile_to_lds<T, 256>(As, LDA, A + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc, kChunk);
-    if (tid < 64) {
-      const int r = min(tid, Cc - 1);  // rows past the end repeat the last gamma
-      gam[tid] = a.gcum[(t0 + r) * a.Hv + h];
-      bet[tid] = (tid < Cc) ? to_f(beta[(t0 + tid) * a.Hv + h]) : 0.f;
-    }
-    __syncthreads();
-    if (tid < 64) {
-      const float gr = gam[tid];
-      eg[tid] = __expf(gr);
-      bex[tid] = bet[tid] * __expf(gr);
-      dl[tid] = __expf(gam[63] - gr);
-    }
-    // P = lower_incl(Q K^T o Gamma), rows 16w .. 16w+15
-    for (int cb = 0; cb < 4; ++cb) {
-      f32x4 acc = zero4();
-      if (cb <= w) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          acc = mfma16(frag_row(Qs + 16 * w * LD + 32 * kk, LD),
-                       frag_row(Ks + 16 * cb * LD + 32 * kk, LD), acc);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
-        float p = 0.f;
-        if (i <= r) p = acc[e] * __expf(gam[r] - gam[i]);
-        Ps[r * LDA + i] = from_f<T>(p);
-      }
-    }
-    __syncthreads();
-    const float eL = __expf(gam[63]);
-
-    // K S and Q S for this wave's 32 columns
-    x8 Sb[4][2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 4; ++kb2)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) Sb[kb2][vb] = pack_split<T>(S[2 * kb2][vb], S[2 * kb2 + 1][vb]);
-    f32x4 ks[4][2], qs[4][2];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) {
-        ks[tb][vb] = zero4();
-        qs[tb][vb] = zero4();
-      }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const x8 fk = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
-        const x8 fq = frag_row_split(Qs + 16 * tb * LD + 32 * kb2, LD);
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
-          ks[tb][vb] = mfma16(fk, Sb[kb2][vb], ks[tb][vb]);
-          qs[tb][vb] = mfma16(fq, Sb[kb2][vb], qs[tb][vb]);
-        }
-      }
-    // R = diag(beta) V - diag(beta e^gamma) K S   (in place in ks)
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + 4 * grp + e, vc = 32 * w + 16 * vb + col;
-          ks[tb][vb][e] = bet[r] * to_f(Vs[r * LD + vc]) - bex[r] * ks[tb][vb][e];
-        }
-    // Delta = A R (A lower triangular: token block kb <= tb / 2)
-    x8 Rb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) Rb[kb][vb] = pack_split<T>(ks[2 * kb][vb], ks[2 * kb + 1][vb]);
-    f32x4 dd[4][2];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb <= tb / 2; ++kb)
-          acc = mfma16(frag_row_split(As + 16 * tb * LDA + 32 * kb, LDA), Rb[kb][vb], acc);
-        dd[tb][vb] = acc;
-      }
-    // O = scale (diag(e^gamma) Q S + P Delta)
-    x8 Db[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) Db[kb][vb] = pack_split<T>(dd[2 * kb][vb], dd[2 * kb + 1][vb]);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb <= tb / 2; ++kb)
-          acc = mfma16(frag_row_split(Ps + 16 * tb * LDA + 32 * kb, LDA), Db[kb][vb], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + 4 * grp + e, vc = 32 * w + 16 * vb + col;
-          if (r < Cc)
-            o[((t0 + r) * a.Hv + h) * kDim + vc] =
-                from_f<T>(a.scale * (eg[r] * qs[tb][vb][e] + acc[e]));
-        }
-      }
-    // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) Delta
-    x8 Eb[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) {
-        f32x4 top = dd[2 * kt][vb], bot = dd[2 * kt + 1][vb];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          top[e] *= dl[32 * kt + 4 * grp + e];
-          bot[e] *= dl[32 * kt + 16 + 4 * grp + e];
-        }
-        Eb[kt][vb] = pack_split<T>(top, bot);
-      }
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) {
-        f32x4 acc = S[kb][vb] * eL;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          acc = mfma16(frag_tr_split(Ks + 32 * kt * LD + 16 * kb, LD), Eb[kt][vb], acc);
-        S[kb][vb] = acc;
-      }
-  }
-
-  if (a.ht) {
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = 16 * kb + 4 * grp + e, vc = 32 * w + 16 * vb + col;
-          a.ht[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = S[kb][vb][e];
-        }
-  }
+size_t cp_workspace_bytes(const Plan& pl, int Hv) {
+  if (pl.cp <= 1) return 0;
+  const size_t units = (size_t)pl.N * Hv;
+  const size_t KV = (size_t)kDim * kDim;
+  return align256(units * pl.cp * 2 * KV * sizeof(float)) +
+         align256(units * pl.cp * KV * sizeof(float));
 }
 
 size_t fwd_workspace_bytes(const gdr_problem* p, const Plan& pl) {
   size_t b = 0;
   if (p->cu_seqlens_dev) b += align256(sizeof(int32_t) * (size_t)(pl.N + 1));
+  b += cp_workspace_bytes(pl, p->Hv);
   return b;
 }
 
-template <typename T>
-static gdr_status launch_fwd_t(const gdr_problem* p, const Plan& pl, FwdArgs a, hipStream_t st) {
-  if (pl.total_chunks > 0) {
-    hipLaunchKernelGGL(fwd_prep_kernel<T>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(256), 0,
-                       st, a);
+template <typename T, int VB>
+static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st) {
+  const unsigned units = (unsigned)(pl.N * a.Hv);
+  if (pl.cp > 1) {
+    ScanArgs a1 = a;
+    a1.P = pl.cp;
+    a1.nvs = 4 / VB;
+    hipLaunchKernelGGL((scan_kernel<T, VB, MODE_AUG>), dim3(units * pl.cp * a1.nvs), dim3(256), 0,
+                       st, a1);
+    hipLaunchKernelGGL(cp_combine_kernel, dim3(units * 8), dim3(256), 0, st, a1);
   }
-  hipLaunchKernelGGL(fwd_scan_kernel<T>, dim3((unsigned)(pl.N * p->Hv)), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_error("kernel launch failed: %s", hipGetErrorString(e));
-    return GDR_ERR_HIP;
-  }
-  return GDR_OK;
+  a.P = pl.cp;
+  a.nvs = 2 / VB;
+  const dim3 grid(units * pl.cp * a.nvs);
+  if (mode == MODE_OUT) hipLaunchKernelGGL((scan_kernel<T, VB, MODE_OUT>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((scan_kernel<T, VB, MODE_STATE>), grid, dim3(256), 0, st, a);
 }
+
+template <typename T>
+void launch_scan(const Plan& pl, ScanArgs a, int mode, hipStream_t st) {
+  if (pl.vb == 2) launch_scan_vb<T, 2>(pl, a, mode, st);
+  else launch_scan_vb<T, 1>(pl, a, mode, st);
+}
+template void launch_scan<__bf16>(const Plan&, ScanArgs, int, hipStream_t);
+template void launch_scan<_Float16>(const Plan&, ScanArgs, int, hipStream_t);
 
 gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const void* g, const void* beta, const float* h0,
                       float* gcum, void* A, void* o, void* h, float* ht, void* ws,
                       hipStream_t st) {
-  FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.g = g;
-  a.beta = beta;
-  a.h0 = h0;
-  a.gcum = gcum;
-  a.A = A;
-  a.o = o;
-  a.h = h;
-  a.ht = ht;
-  a.cu = p->cu_seqlens_dev;
-  a.offs = nullptr;
-  a.N = pl.N;
-  a.T = p->T;
-  a.Hq = p->Hq;
-  a.Hv = p->Hv;
-  a.nc_dense = pl.nc_dense;
-  a.g_dtype = (int)p->g_dtype;
-  a.scale = p->scale;
-  a.svf = p->state_v_first ? 1 : 0;
+  char* wp = reinterpret_cast<char*>(ws);
+  const int32_t* offs = nullptr;
   if (p->cu_seqlens_dev) {
-    int32_t* offs = reinterpret_cast<int32_t*>(ws);
+    int32_t* o32 = reinterpret_cast<int32_t*>(wp);
     hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, st, p->cu_seqlens_dev, pl.N,
-                       offs);
-    a.offs = offs;
+                       o32);
+    offs = o32;
+    wp += align256(sizeof(int32_t) * (size_t)(pl.N + 1));
   }
-  if (p->in_dtype == GDR_BF16) return launch_fwd_t<__bf16>(p, pl, a, st);
-  return launch_fwd_t<_Float16>(p, pl, a, st);
+  FwdArgs fa;
+  fa.q = q; fa.k = k; fa.v = v; fa.g = g; fa.beta = beta; fa.h0 = h0; fa.gcum = gcum;
+  fa.A = A; fa.o = o; fa.h = h; fa.ht = ht;
+  fa.cu = p->cu_seqlens_dev; fa.offs = offs;
+  fa.N = pl.N; fa.T = p->T; fa.Hq = p->Hq; fa.Hv = p->Hv; fa.nc_dense = pl.nc_dense;
+  fa.g_dtype = (int)p->g_dtype; fa.scale = p->scale; fa.svf = p->state_v_first ? 1 : 0;
+
+  ScanArgs sa;
+  sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
+  sa.o = o; sa.h = h; sa.ht = ht;
+  sa.cu = p->cu_seqlens_dev; sa.offs = offs;
+  sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
+  sa.P = 1; sa.nvs = 1;
+  sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf;
+  sa.seg_out = nullptr; sa.seg_start = nullptr;
+  if (pl.cp > 1) {
+    const size_t units = (size_t)pl.N * p->Hv;
+    const size_t KV = (size_t)kDim * kDim;
+    sa.seg_out = reinterpret_cast<float*>(wp);
+    wp += align256(units * pl.cp * 2 * KV * sizeof(float));
+    sa.seg_start = reinterpret_cast<float*>(wp);
+  }
+  if (p->in_dtype == GDR_BF16) {
+    if (pl.total_chunks > 0)
+      hipLaunchKernelGGL(fwd_prep_kernel<__bf16>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(256),
+                         0, st, fa);
+    launch_scan<__bf16>(pl, sa, MODE_OUT, st);
+  } else {
+    if (pl.total_chunks > 0)
+      hipLaunchKernelGGL(fwd_prep_kernel<_Float16>, dim3((unsigned)pl.total_chunks, p->Hv),
+                         dim3(256), 0, st, fa);
+    launch_scan<_Float16>(pl, sa, MODE_OUT, st);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("forward launch failed: %s", hipGetErrorString(e));
+    return GDR_ERR_HIP;
+  }
+  return GDR_OK;
 }
 
 }  // namespace gdr

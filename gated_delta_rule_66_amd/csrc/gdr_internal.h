@@ -19,7 +19,7 @@ struct Plan {
   int nc_dense;       // chunks per sequence for dense batches (0 for packed)
   int64_t max_len;    // longest sequence
   int cp;             // context-parallel segments per sequence (1 = off)
-  int64_t cp_chunks;  // chunks per segment when cp > 1
+  int vb;             // 16-column MFMA tiles per wave in the scans (1 or 2)
 };
 
 Plan make_plan(const gdr_problem* p);
@@ -28,6 +28,7 @@ Plan make_plan(const gdr_problem* p);
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t fwd_workspace_bytes(const gdr_problem* p, const Plan& pl);
+size_t cp_workspace_bytes(const Plan& pl, int Hv);
 size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl);
 
 gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
@@ -39,6 +40,12 @@ gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const
                       const void* v, const float* gcum, const void* beta, const void* A,
                       const void* dO, const float* dht, const float* h0, void* dq, void* dk,
                       void* dv, void* dbeta, void* dg, float* dh0, void* ws, hipStream_t st);
+
+struct ScanArgs;
+// The forward state scan (with the CP passes when pl.cp > 1).  mode 0 writes
+// outputs, mode 2 only the chunk-start states.
+template <typename T>
+void launch_scan(const Plan& pl, ScanArgs a, int mode, hipStream_t st);
 
 void set_error(const char* fmt, ...);
 

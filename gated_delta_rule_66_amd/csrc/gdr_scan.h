@@ -1,0 +1,435 @@
+// gdr_scan.h -- the sequential inter-chunk state recurrence (forward
+// direction) and its intra-GPU context-parallel (CP) split.
+//
+// One workgroup = 4 waves = one (sequence, value head, T-segment, column
+// block).  The state S (K x V fp32) is split by value columns: the columns
+// of S evolve independently, so a workgroup owns CW = 64 * VB of them and
+// wave w owns 16 * VB, kept as MFMA accumulators for the whole segment.
+// Per chunk (gamma = g_cum, L = last valid row):
+//   R     = diag(beta) V - diag(beta e^gamma) (K S)
+//   Delta = A R                                         (WY form)
+//   O     = scale (diag(e^gamma) (Q S) + P Delta),   P = lower_incl(Q K^T o Gamma)
+//   S     = e^{gamma_L} S + K^T (diag(e^{gamma_L - gamma}) Delta)
+// The next chunk's tiles are loaded into registers while the current chunk
+// computes.
+//
+// Intra-GPU context parallelism (the pages' "intra-card CP"; the mechanism is
+// ours): a chunk maps its start state affinely, S' = T_c S + B_c with
+// T_c = e^{gamma_L} I - K~^T A X and B_c = K~^T A Y.  So a segment of chunks
+// maps S_start to S_end = T_seg S_start + B_seg, and (T_seg | B_seg) is the
+// end state of the same recurrence run on the augmented K x 2V state
+// [I | 0] with values [0 | V] (MODE_AUG).  Pass 1 computes the transitions of
+// every segment but the last in parallel, pass 2 (cp_combine_kernel) chains
+// the segment start states, pass 3 reruns each segment from its start state
+// with outputs.  The plan depends only on shapes.
+#pragma once
+
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+enum ScanMode { MODE_OUT = 0, MODE_AUG = 1, MODE_STATE = 2 };
+
+struct ScanArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const float* gcum;
+  const void* A;
+  const float* h0;        // [N, Hv, K, V] (or [.., V, K] when svf), nullable
+  void* o;                // MODE_OUT output
+  void* h;                // chunk-start states (in_dtype), nullable
+  float* ht;              // final state, nullable
+  const float* seg_start; // [units, P, K, V] fp32 segment start states (P > 1)
+  float* seg_out;         // [units, P, K, 2V] fp32 augmented end states (pass 1)
+  const int32_t* cu;
+  const int32_t* offs;
+  int N, T, Hq, Hv;
+  int nc_dense;
+  int P;    // segments per sequence
+  int nvs;  // column blocks per (unit, segment)
+  float scale;
+  int svf;     // layout of h0 / ht / user h
+  int h_svf;   // layout of h (user h follows svf; the backward's own copy is [K][V])
+};
+
+// Chunks [c0, c1) of segment p; the segment holding the last chunk is
+// p_last (0 for an empty sequence).
+struct SegRange {
+  int c0, c1, p_last;
+};
+__device__ __forceinline__ SegRange seg_range(int nch, int P, int p) {
+  SegRange r;
+  const int sc = (nch + P - 1) / P;
+  r.c0 = min(p * sc, nch);
+  r.c1 = min(r.c0 + sc, nch);
+  r.p_last = (nch == 0) ? 0 : (nch - 1) / sc;
+  return r;
+}
+
+template <typename T, int VB, int MODE>
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  typedef typename VT<T>::x8 x8;
+  constexpr int CW = 64 * VB;          // columns per workgroup
+  constexpr int LD = 136;              // q / k tile leading dimension
+  constexpr int LDV = CW + 8;          // v / o tile leading dimension
+  constexpr int LDA = 72;              // A / P tile leading dimension
+  constexpr bool OUT = (MODE == MODE_OUT);
+  constexpr int HS_ELEMS = (128 * (CW + 8) > CW * 136) ? 128 * (CW + 8) : CW * 136;
+  __shared__ __align__(16) T Ks[64 * LD];
+  __shared__ __align__(16) T Qs[OUT ? 64 * LD : 8];
+  __shared__ __align__(16) T Vs[64 * LDV];
+  __shared__ __align__(16) T Os[OUT ? 64 * LDV : 8];
+  __shared__ __align__(16) T As[64 * LDA];
+  __shared__ __align__(16) T Ps[OUT ? 64 * LDA : 8];
+  __shared__ __align__(16) T Hs[MODE == MODE_STATE ? HS_ELEMS : 8];
+  __shared__ float gam[64], bet[64], eg[64], bex[64], dl[64];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  const int vs = blockIdx.x % a.nvs;
+  const int up = blockIdx.x / a.nvs;
+  const int p = up % a.P, unit = up / a.P;
+  const int n = unit / a.Hv, h = unit % a.Hv;
+  const int G = a.Hv / a.Hq, hq = h / G;
+  const SeqInfo s = seq_info(a.cu, n, a.T);
+  const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
+  const SegRange sr = seg_range(nch, a.P, p);
+  const int cb0 = vs * CW;
+  const bool isT = (MODE == MODE_AUG) && cb0 < kDim;  // transition columns
+  if (MODE == MODE_AUG) {
+    if (p >= sr.p_last) return;   // the last segment needs no transition
+    if (p == 0 && isT) return;    // segment 0 starts from h0: its end state suffices
+  } else {
+    if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;  // empty segment
+  }
+  const int vcol0 = (MODE == MODE_AUG) ? (isT ? 0 : cb0 - kDim) : cb0;
+  const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
+  const int64_t KV = (int64_t)kDim * kDim;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* v = reinterpret_cast<const T*>(a.v);
+  const T* Ag = reinterpret_cast<const T*>(a.A);
+  const T* beta = reinterpret_cast<const T*>(a.beta);
+  const int cw0 = 16 * VB * w;  // this wave's first column inside the block
+
+  // ---- initial state ----
+  f32x4 S[8][VB];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e;
+        const int lc = cw0 + 16 * vb + col;  // local column
+        float x = 0.f;
+        if (MODE == MODE_AUG && isT) {
+          x = (key == cb0 + lc) ? 1.f : 0.f;
+        } else if (p == 0) {
+          const int vc = vcol0 + lc;
+          if (a.h0) x = a.h0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)];
+        } else {
+          x = a.seg_start[((int64_t)unit * a.P + p) * KV + key * kDim + vcol0 + lc];
+        }
+        S[kb][vb][e] = x;
+      }
+
+  // ---- register prefetch of one chunk ----
+  TileRegs<128, 256> rq, rk;
+  TileRegs<CW, 256> rv;
+  TileRegs<64, 256> ra;
+  float r_g = 0.f, r_b = 0.f, r_gl = 0.f;
+  auto prefetch = [&](int c) {
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+    if (OUT) tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
+    tile_load<T, 128, 256>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
+    if (!isT) tile_load<T, CW, 256>(rv, v + (t0 * a.Hv + h) * kDim + vcol0, (int64_t)a.Hv * kDim, Cc);
+    tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc);
+    if (tid < 64) {
+      r_g = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
+      r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
+      r_b = (tid < Cc) ? to_f(beta[(t0 + tid) * a.Hv + h]) : 0.f;
+    }
+  };
+
+  int64_t t_prev = 0;
+  int cc_prev = 0;
+  if (sr.c0 < sr.c1) prefetch(sr.c0);
+  for (int c = sr.c0; c < sr.c1; ++c) {
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+    __syncthreads();  // the previous chunk is done with LDS
+    if (OUT && c > sr.c0)
+      tile_from_lds<T, CW, 256>(reinterpret_cast<T*>(a.o) + (t_prev * a.Hv + h) * kDim + cb0,
+                                (int64_t)a.Hv * kDim, Os, LDV, cc_prev);
+    if (OUT) tile_store<T, 128, 256>(Qs, LD, rq);
+    tile_store<T, 128, 256>(Ks, LD, rk);
+    if (!isT) tile_store<T, CW, 256>(Vs, LDV, rv);
+    tile_store<T, 64, 256>(As, LDA, ra);
+    if (tid < 64) {
+      gam[tid] = r_g;
+      bet[tid] = r_b;
+      const float e = __expf(r_g);
+      eg[tid] = e;
+      bex[tid] = r_b * e;
+      dl[tid] = __expf(r_gl - r_g);
+    }
+    __syncthreads();
+    const float eLc = __expf(gam[63]);
+    if (c + 1 < sr.c1) prefetch(c + 1);
+
+    // chunk-start state out: the backward's own copy is staged in LDS for
+    // 16-byte stores; the optional user h of the forward is written directly
+    if (MODE == MODE_STATE && a.h) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = 16 * kb + 4 * grp + e, lc = cw0 + 16 * vb + col;
+            if (a.h_svf) Hs[lc * 136 + key] = from_f<T>(S[kb][vb][e]);
+            else Hs[key * (CW + 8) + lc] = from_f<T>(S[kb][vb][e]);
+          }
+    }
+    if (MODE == MODE_OUT && a.h) {
+      T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
+            hp[a.h_svf ? vc * kDim + key : key * kDim + vc] = from_f<T>(S[kb][vb][e]);
+          }
+    }
+
+    if (OUT) {
+      // P rows 16w .. 16w+15
+      for (int cbk = 0; cbk < 4; ++cbk) {
+        f32x4 acc = zero4();
+        if (cbk <= w) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            acc = mfma16(frag_row(Qs + 16 * w * LD + 32 * kk, LD),
+                         frag_row(Ks + 16 * cbk * LD + 32 * kk, LD), acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * w + 4 * grp + e, i = 16 * cbk + col;
+          float pv = 0.f;
+          if (i <= r) pv = acc[e] * __expf(gam[r] - gam[i]);
+          Ps[r * LDA + i] = from_f<T>(pv);
+        }
+      }
+    }
+    if (OUT || (MODE == MODE_STATE && a.h)) __syncthreads();
+    if (MODE == MODE_STATE && a.h) {
+      T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
+      if (a.h_svf) {
+        // rows = local value columns, 128 keys each
+        for (int x = tid; x < CW * 16; x += 256) {
+          const int r = x >> 4, c8 = (x & 15) * 8;
+          *reinterpret_cast<uint4*>(hp + (int64_t)(cb0 + r) * kDim + c8) =
+              *reinterpret_cast<const uint4*>(Hs + r * 136 + c8);
+        }
+      } else {
+        constexpr int PR = CW / 8;
+        for (int x = tid; x < 128 * PR; x += 256) {
+          const int r = x / PR, c8 = (x % PR) * 8;
+          *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
+              *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
+        }
+      }
+    }
+
+    // K S (and Q S)
+    x8 Sb[4][VB];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) Sb[kb2][vb] = pack_split<T>(S[2 * kb2][vb], S[2 * kb2 + 1][vb]);
+    f32x4 ks[4][VB], qs[4][VB];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        ks[tb][vb] = zero4();
+        qs[tb][vb] = zero4();
+      }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        const x8 fk = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) ks[tb][vb] = mfma16(fk, Sb[kb2][vb], ks[tb][vb]);
+        if (OUT) {
+          const x8 fq = frag_row_split(Qs + 16 * tb * LD + 32 * kb2, LD);
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb) qs[tb][vb] = mfma16(fq, Sb[kb2][vb], qs[tb][vb]);
+        }
+      }
+    // R = diag(beta) V - diag(beta e^gamma) K S
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tb + 4 * grp + e, lc = cw0 + 16 * vb + col;
+          const float vv = isT ? 0.f : bet[r] * to_f(Vs[r * LDV + lc]);
+          ks[tb][vb][e] = vv - bex[r] * ks[tb][vb][e];
+        }
+    // Delta = A R
+    x8 Rb[2][VB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) Rb[kb][vb] = pack_split<T>(ks[2 * kb][vb], ks[2 * kb + 1][vb]);
+    f32x4 dd[4][VB];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      x8 fa[2];
+#pragma unroll
+      for (int kb = 0; kb <= tb / 2; ++kb) fa[kb] = frag_row_split(As + 16 * tb * LDA + 32 * kb, LDA);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb <= tb / 2; ++kb) acc = mfma16(fa[kb], Rb[kb][vb], acc);
+        dd[tb][vb] = acc;
+      }
+    }
+    if (OUT) {
+      x8 Db[2][VB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) Db[kb][vb] = pack_split<T>(dd[2 * kb][vb], dd[2 * kb + 1][vb]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        x8 fp[2];
+#pragma unroll
+        for (int kb = 0; kb <= tb / 2; ++kb) fp[kb] = frag_row_split(Ps + 16 * tb * LDA + 32 * kb, LDA);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb <= tb / 2; ++kb) acc = mfma16(fp[kb], Db[kb][vb], acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tb + 4 * grp + e, lc = cw0 + 16 * vb + col;
+            Os[r * LDV + lc] = from_f<T>(a.scale * (eg[r] * qs[tb][vb][e] + acc[e]));
+          }
+        }
+      }
+    }
+    // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) Delta
+    x8 Eb[2][VB];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 top = dd[2 * kt][vb], bot = dd[2 * kt + 1][vb];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          top[e] *= dl[32 * kt + 4 * grp + e];
+          bot[e] *= dl[32 * kt + 16 + 4 * grp + e];
+        }
+        Eb[kt][vb] = pack_split<T>(top, bot);
+      }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      x8 fk[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) fk[kt] = frag_tr_split(Ks + 32 * kt * LD + 16 * kb, LD);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 acc = S[kb][vb] * eLc;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) acc = mfma16(fk[kt], Eb[kt][vb], acc);
+        S[kb][vb] = acc;
+      }
+    }
+    t_prev = t0;
+    cc_prev = Cc;
+  }
+
+  if (OUT && sr.c1 > sr.c0) {
+    __syncthreads();
+    tile_from_lds<T, CW, 256>(reinterpret_cast<T*>(a.o) + (t_prev * a.Hv + h) * kDim + cb0,
+                              (int64_t)a.Hv * kDim, Os, LDV, cc_prev);
+  }
+  if (MODE == MODE_AUG) {
+    float* so = a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, lc = cw0 + 16 * vb + col;
+          so[key * (2 * kDim) + cb0 + lc] = S[kb][vb][e];
+        }
+  } else if (a.ht && p == sr.p_last) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
+          a.ht[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = S[kb][vb][e];
+        }
+  }
+}
+
+// Pass 2: chain the segment start states of one (unit, 16-column block):
+//   start[1] = B_0 (segment 0 ran from the initial state),
+//   start[p] = T_{p-1} start[p-1] + B_{p-1}, p = 2 .. p_last.
+// fp32 MFMA (16x16x4); wave w owns rows 32w .. 32w+31.
+__global__ __launch_bounds__(256) void cp_combine_kernel(ScanArgs a) {
+  __shared__ float Sp[128 * 17];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  const int unit = blockIdx.x >> 3, cblk = blockIdx.x & 7;
+  const int n = unit / a.Hv;
+  const SeqInfo s = seq_info(a.cu, n, a.T);
+  const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
+  const SegRange sr = seg_range(nch, a.P, 0);
+  const int64_t KV = (int64_t)kDim * kDim;
+  const int c0 = 16 * cblk;
+  for (int p = 1; p <= sr.p_last; ++p) {
+    const float* prev = a.seg_out + ((int64_t)unit * a.P + (p - 1)) * (2 * KV);
+    float* dst = const_cast<float*>(a.seg_start) + ((int64_t)unit * a.P + p) * KV;
+    f32x4 acc[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r0 = 32 * w + 16 * rt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[rt][e] = prev[(r0 + 4 * grp + e) * (2 * kDim) + kDim + c0 + col];
+      if (p > 1) {
+        for (int st = 0; st < 32; ++st) {
+          const float av = prev[(r0 + col) * (2 * kDim) + 4 * st + grp];
+          const float bv = Sp[(4 * st + grp) * 17 + col];
+          acc[rt] = mfma16f32(av, bv, acc[rt]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(r0 + 4 * grp + e) * kDim + c0 + col] = acc[rt][e];
+    }
+    __syncthreads();  // every wave is done reading the previous start state
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Sp[(32 * w + 16 * rt + 4 * grp + e) * 17 + col] = acc[rt][e];
+    __syncthreads();
+  }
+}
+
+}  // namespace gdr
