@@ -1,21 +1,914 @@
-// gdr_bwd.hip -- backward kernels (in progress).
+// gdr_bwd.hip -- backward kernels of the chunked gated delta rule on gfx950.
+//
+// The backward of the FlashQLA pages ("FlashQLA Documentation", backward
+// pass: dq, dk, dv, db, dg, dh0 from q, k, v, g, beta, A, do, dht).  The
+// forward's chunk states are not an input, so they are recomputed.
+//
+//   B1  scan (forward, state mode)   chunk-start states S_c       -> h  (ws)
+//   B2  dh_scan (reverse)            with dSn the gradient of a chunk's end
+//       state:   dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
+//                dS     = e^{gL} dSn + Q^T (scale diag(e^gamma) dO)
+//                         - K^T diag(beta e^gamma) A^T dDelta
+//       stores dSn per chunk (-> dh, ws) and dh0; long sequences are split
+//       along T with the transposed segment transitions (same augmented-
+//       state construction as the forward).
+//   B3-5 grad_kernel, one workgroup per (chunk, value head), from S and dSn:
+//       R = diag(beta) V - diag(beta e^gamma) K S, Delta = A R,
+//       dDelta (as above), dR = A^T dDelta, dA = dDelta R^T,
+//       dM = strict_lower(-A^T dA A^T), dP = scale lower_incl(dO Delta^T),
+//       dq = scale diag(e^gamma) dO S^T + (dP o Gamma) K
+//       dk = (dP o Gamma)^T Q + diag(e^{gL-gamma}) Delta dSn^T
+//            - diag(beta e^gamma) dR S^T + (dM o beta Gamma) K + (..)^T K
+//       dv = diag(beta) dR, dbeta and dgamma by fixed-order row reductions,
+//       dg = reverse chunk-local cumsum of dgamma.
+//   B6  gva_reduce: dq, dk summed over the Hv/Hq value heads of a group.
 #include "gdr_device.h"
 #include "gdr_internal.h"
+#include "gdr_scan.h"
+
+#include <algorithm>
+#include <cstring>
 
 namespace gdr {
 
-size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl) {
-  (void)p;
-  (void)pl;
-  return 0;
+// sum over the 16 lanes of a lane group (same grp)
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+// sum over the 4 lane groups (same col)
+__device__ __forceinline__ float sum4g(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
 }
 
-gdr_status launch_bwd(const gdr_problem*, const Plan&, const void*, const void*, const void*,
-                      const float*, const void*, const void*, const void*, const float*,
-                      const float*, void*, void*, void*, void*, void*, float*, void*,
-                      hipStream_t) {
-  set_error("backward not built yet");
-  return GDR_ERR_ARG;
+// ---------------------------------------------------------------------------
+// B2: reverse recurrence of the state gradient
+// ---------------------------------------------------------------------------
+struct DhArgs {
+  const void* q;
+  const void* k;
+  const void* dO;
+  const void* beta;
+  const float* gcum;
+  const void* A;
+  const float* dht;    // [N, Hv, K, V] (svf aware), nullable
+  void* dh;            // [NC, Hv, K, V] in_dtype: gradient of each chunk's end state
+  float* dh0;          // nullable (svf aware)
+  const float* seg_start;  // [units, P, K, V]: gradient entering each segment's end
+  float* seg_out;          // [units, P, K, 2V]: augmented pass-1 results
+  const int32_t* cu;
+  const int32_t* offs;
+  int N, T, Hq, Hv, nc_dense;
+  int P, nvs;
+  float scale;
+  int svf;
+};
+
+template <typename T, int VB, int MODE>
+__global__ __launch_bounds__(256) void dh_scan_kernel(DhArgs a) {
+  typedef typename VT<T>::x8 x8;
+  constexpr int CW = 64 * VB;
+  constexpr int LD = 136;
+  constexpr int LDV = CW + 8;
+  constexpr int LDA = 72;
+  constexpr bool OUT = (MODE == MODE_OUT);
+  __shared__ __align__(16) T Qs[64 * LD];
+  __shared__ __align__(16) T Ks[64 * LD];
+  __shared__ __align__(16) T Ds[64 * LDV];
+  __shared__ __align__(16) T As[64 * LDA];
+  __shared__ __align__(16) T Ps[64 * LDA];
+  __shared__ __align__(16) T Hs[OUT ? 128 * (CW + 8) : 8];
+  __shared__ float gam[64], eg[64], bex[64], dl[64];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  const int vs = blockIdx.x % a.nvs;
+  const int up = blockIdx.x / a.nvs;
+  const int p = up % a.P, unit = up / a.P;
+  const int n = unit / a.Hv, h = unit % a.Hv;
+  const int G = a.Hv / a.Hq, hq = h / G;
+  const SeqInfo s = seq_info(a.cu, n, a.T);
+  const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
+  const SegRange sr = seg_range(nch, a.P, p);
+  const int cb0 = vs * CW;
+  const bool isT = (MODE == MODE_AUG) && cb0 < kDim;
+  if (MODE == MODE_AUG) {
+    if (p == 0 || p > sr.p_last) return;       // segment 0 needs no transition
+    if (p == sr.p_last && isT) return;         // the last segment starts from dht
+  } else {
+    if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;
+  }
+  const int vcol0 = (MODE == MODE_AUG) ? (isT ? 0 : cb0 - kDim) : cb0;
+  const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
+  const int64_t KV = (int64_t)kDim * kDim;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* dO = reinterpret_cast<const T*>(a.dO);
+  const T* Ag = reinterpret_cast<const T*>(a.A);
+  const T* beta = reinterpret_cast<const T*>(a.beta);
+  const int cw0 = 16 * VB * w;
+
+  f32x4 Gs[8][VB];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, lc = cw0 + 16 * vb + col;
+        float x = 0.f;
+        if (MODE == MODE_AUG && isT) {
+          x = (key == cb0 + lc) ? 1.f : 0.f;
+        } else if (p == sr.p_last) {
+          const int vc = vcol0 + lc;
+          if (a.dht) x = a.dht[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)];
+        } else {
+          x = a.seg_start[((int64_t)unit * a.P + p) * KV + key * kDim + vcol0 + lc];
+        }
+        Gs[kb][vb][e] = x;
+      }
+
+  TileRegs<128, 256> rq, rk;
+  TileRegs<CW, 256> rd;
+  TileRegs<64, 256> ra;
+  float r_g = 0.f, r_gl = 0.f;
+  T r_b = from_f<T>(0.f);
+  auto prefetch = [&](int c) {
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+    tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
+    tile_load<T, 128, 256>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
+    if (!isT) tile_load<T, CW, 256>(rd, dO + (t0 * a.Hv + h) * kDim + vcol0, (int64_t)a.Hv * kDim, Cc);
+    tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc);
+    if (tid < 64) {
+      r_g = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
+      r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
+      r_b = (tid < Cc) ? beta[(t0 + tid) * a.Hv + h] : from_f<T>(0.f);
+    }
+  };
+
+  if (sr.c0 < sr.c1) prefetch(sr.c1 - 1);
+  for (int c = sr.c1 - 1; c >= sr.c0; --c) {
+    __syncthreads();
+    tile_store<T, 128, 256>(Qs, LD, rq);
+    tile_store<T, 128, 256>(Ks, LD, rk);
+    if (!isT) tile_store<T, CW, 256>(Ds, LDV, rd);
+    tile_store<T, 64, 256>(As, LDA, ra);
+    if (tid < 64) {
+      const float e = __expf(r_g);
+      gam[tid] = r_g;
+      eg[tid] = a.scale * e;
+      bex[tid] = to_f(r_b) * e;
+      dl[tid] = __expf(r_gl - r_g);
+    }
+    __syncthreads();
+    const float eL = __expf(gam[63]);
+    if (c - 1 >= sr.c0) prefetch(c - 1);
+
+    if (OUT) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Hs[(16 * kb + 4 * grp + e) * (CW + 8) + cw0 + 16 * vb + col] = from_f<T>(Gs[kb][vb][e]);
+    }
+    // P rows 16w .. 16w+15
+    for (int cbk = 0; cbk < 4; ++cbk) {
+      f32x4 acc = zero4();
+      if (cbk <= w) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc = mfma16(frag_row(Qs + 16 * w * LD + 32 * kk, LD),
+                       frag_row(Ks + 16 * cbk * LD + 32 * kk, LD), acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * grp + e, i = 16 * cbk + col;
+        float pv = 0.f;
+        if (i <= r) pv = acc[e] * __expf(gam[r] - gam[i]);
+        Ps[r * LDA + i] = from_f<T>(pv);
+      }
+    }
+    __syncthreads();
+    if (OUT) {
+      T* hp = reinterpret_cast<T*>(a.dh) + ((choff + c) * a.Hv + h) * KV;
+      constexpr int PR = CW / 8;
+      for (int x = tid; x < 128 * PR; x += 256) {
+        const int r = x / PR, c8 = (x % PR) * 8;
+        *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
+            *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
+      }
+    }
+
+    // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
+    x8 Gb[4][VB];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) Gb[kb2][vb] = pack_split<T>(Gs[2 * kb2][vb], Gs[2 * kb2 + 1][vb]);
+    f32x4 dd[4][VB];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = zero4();
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        const x8 fk = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = mfma16(fk, Gb[kb2][vb], dd[tb][vb]);
+      }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 acc = zero4();
+        if (!isT) {
+#pragma unroll
+          for (int kt = tb / 2; kt < 2; ++kt)
+            acc = mfma16(frag_tr_split(Ps + 32 * kt * LDA + 16 * tb, LDA),
+                         frag_tr_split(Ds + 32 * kt * LDV + cw0 + 16 * vb, LDV), acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tb + 4 * grp + e;
+          dd[tb][vb][e] = dl[r] * dd[tb][vb][e] + a.scale * acc[e];
+        }
+      }
+    // Z = -diag(beta e^gamma) A^T dDelta
+    f32x4 zz[4][VB];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kt = tb / 2; kt < 2; ++kt)
+          acc = mfma16(frag_tr_split(As + 32 * kt * LDA + 16 * tb, LDA),
+                       pack_split<T>(dd[2 * kt][vb], dd[2 * kt + 1][vb]), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= -bex[16 * tb + 4 * grp + e];
+        zz[tb][vb] = acc;
+      }
+    // dS = e^{gL} dSn + K^T Z + Q^T (scale diag(e^gamma) dO)
+    x8 Zb[2][VB], Ob[2][VB];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        Zb[kt][vb] = pack_split<T>(zz[2 * kt][vb], zz[2 * kt + 1][vb]);
+        if (!isT) {
+          x8 f = frag_tr_split(Ds + 32 * kt * LDV + cw0 + 16 * vb, LDV);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 32 * kt + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+            f[e] = from_f<T>(to_f(f[e]) * eg[r]);
+          }
+          Ob[kt][vb] = f;
+        }
+      }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      x8 fk[2], fq[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        fk[kt] = frag_tr_split(Ks + 32 * kt * LD + 16 * kb, LD);
+        if (!isT) fq[kt] = frag_tr_split(Qs + 32 * kt * LD + 16 * kb, LD);
+      }
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 acc = Gs[kb][vb] * eL;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          acc = mfma16(fk[kt], Zb[kt][vb], acc);
+          if (!isT) acc = mfma16(fq[kt], Ob[kt][vb], acc);
+        }
+        Gs[kb][vb] = acc;
+      }
+    }
+  }
+
+  if (MODE == MODE_AUG) {
+    float* so = a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          so[(16 * kb + 4 * grp + e) * (2 * kDim) + cb0 + cw0 + 16 * vb + col] = Gs[kb][vb][e];
+  } else if (p == 0 && a.dh0) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
+          a.dh0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = Gs[kb][vb][e];
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// B3-B5: per-chunk gradients
+// ---------------------------------------------------------------------------
+struct GradArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dO;
+  const void* beta;
+  const float* gcum;
+  const void* A;
+  const void* h;   // [NC, Hv, K, V] chunk-start states
+  const void* dh;  // [NC, Hv, K, V] end-state gradients
+  void* dq;        // in_dtype [T, Hq, K], or fp32 [T, Hv, K] partials when partial
+  void* dk;
+  void* dv;
+  void* dbeta;
+  void* dg;
+  const int32_t* cu;
+  const int32_t* offs;
+  int N, T, Hq, Hv, nc_dense, g_dtype;
+  float scale;
+  int partial;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
+  typedef typename VT<T>::x8 x8;
+  constexpr int LD = 136;  // q, k
+  constexpr int L7 = 72;   // every 64-wide tile
+  __shared__ __align__(16) T Qs[64 * LD];
+  __shared__ __align__(16) T Ks[64 * LD];
+  __shared__ __align__(16) T As[64 * L7];
+  __shared__ __align__(16) T Ps[64 * L7];
+  __shared__ __align__(16) T Ss[128 * L7];   // S[:, half]; later dA, T1
+  __shared__ __align__(16) T Gs_[128 * L7];  // dSn[:, half]; later dP o Gamma, dM o beta Gamma
+  __shared__ __align__(16) T Vs[64 * L7];
+  __shared__ __align__(16) T Os[64 * L7];    // dO[:, half]
+  __shared__ __align__(16) T Rs[64 * L7];
+  __shared__ __align__(16) T Dls[64 * L7];   // Delta
+  __shared__ __align__(16) T DDs[64 * L7];   // dDelta
+  __shared__ __align__(16) T DRs[64 * L7];   // dR
+  __shared__ float gam[64], bet[64], eg[64], bex[64], dl[64];
+  __shared__ float dbv[8][64];       // v . dR partials per (half, wave)
+  __shared__ float colE[4][64];      // column sums of dP o P and dM o M per wave
+  __shared__ float red[256];         // <S, dSn> partials
+  __shared__ float dgam[64];
+  __shared__ float fsum[4][4];       // F partials per (wave, lane group)
+
+  const int c = blockIdx.x, h = blockIdx.y;
+  int n, j;
+  if (a.cu) {
+    n = find_seq(a.offs, a.N, c);
+    j = c - a.offs[n];
+  } else {
+    n = c / a.nc_dense;
+    j = c % a.nc_dense;
+  }
+  const SeqInfo s = seq_info(a.cu, n, a.T);
+  const int64_t t0 = s.start + (int64_t)kChunk * j;
+  const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+  const int G = a.Hv / a.Hq, hq = h / G;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  const int64_t KV = (int64_t)kDim * kDim;
+  const T* hS = reinterpret_cast<const T*>(a.h) + ((int64_t)c * a.Hv + h) * KV;
+  const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)c * a.Hv + h) * KV;
+  const T* vv = reinterpret_cast<const T*>(a.v);
+  const T* dOg = reinterpret_cast<const T*>(a.dO);
+
+  tile_to_lds<T, 256>(Qs, LD, reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim,
+                      (int64_t)a.Hq * kDim, Cc, kDim);
+  tile_to_lds<T, 256>(Ks, LD, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
+                      (int64_t)a.Hq * kDim, Cc, kDim);
+  tile_to_lds<T, 256>(As, L7, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
+                      (int64_t)a.Hv * kChunk, Cc, kChunk);
+  if (tid < 64) {
+    const float gr = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
+    const float gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
+    const float bt = (tid < Cc) ? to_f(reinterpret_cast<const T*>(a.beta)[(t0 + tid) * a.Hv + h]) : 0.f;
+    const float e = __expf(gr);
+    gam[tid] = gr;
+    bet[tid] = bt;
+    eg[tid] = e;
+    bex[tid] = bt * e;
+    dl[tid] = __expf(gl - gr);
+    dgam[tid] = 0.f;
+  }
+  __syncthreads();
+  const float gL = gam[63];
+
+  // P and N = K K^T o Gamma (strict lower), rows 16w .. 16w+15, fp32 in registers
+  f32x4 pv[4], nv[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    f32x4 accq = zero4(), acck = zero4();
+    if (cb <= w) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const x8 fkb = frag_row(Ks + 16 * cb * LD + 32 * kk, LD);
+        accq = mfma16(frag_row(Qs + 16 * w * LD + 32 * kk, LD), fkb, accq);
+        acck = mfma16(frag_row(Ks + 16 * w * LD + 32 * kk, LD), fkb, acck);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
+      const float gm = (i <= r) ? __expf(gam[r] - gam[i]) : 0.f;
+      pv[cb][e] = accq[e] * gm;
+      nv[cb][e] = (i < r) ? acck[e] * gm : 0.f;
+      Ps[r * L7 + i] = from_f<T>(pv[cb][e]);
+    }
+  }
+
+  // accumulators over the value halves
+  f32x4 dA[4], dP[4], dQ1[8], dX[8], dKs[8];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    dA[x] = zero4();
+    dP[x] = zero4();
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    dQ1[x] = zero4();
+    dX[x] = zero4();
+    dKs[x] = zero4();
+  }
+  float sds = 0.f;
+
+  for (int hv = 0; hv < 2; ++hv) {
+    const int v0 = 64 * hv;
+    __syncthreads();  // previous half done with the per-half tiles
+    // S[:, half], dSn[:, half]: 128 rows x 64 columns
+    for (int x = tid; x < 128 * 8; x += 256) {
+      const int r = x >> 3, c8 = (x & 7) * 8;
+      *reinterpret_cast<uint4*>(Ss + r * L7 + c8) =
+          *reinterpret_cast<const uint4*>(hS + (int64_t)r * kDim + v0 + c8);
+      *reinterpret_cast<uint4*>(Gs_ + r * L7 + c8) =
+          *reinterpret_cast<const uint4*>(hG + (int64_t)r * kDim + v0 + c8);
+    }
+    tile_to_lds<T, 256>(Vs, L7, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc, 64);
+    tile_to_lds<T, 256>(Os, L7, dOg + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc, 64);
+    __syncthreads();
+
+    // ---- wave w: value columns cc .. cc+15 of this half ----
+    const int cc = 16 * w;
+    f32x4 R[4], Dl[4], dD[4], dR[4];
+    {
+      f32x4 ks[4], kg[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        ks[tb] = zero4();
+        kg[tb] = zero4();
+      }
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        const x8 fs = frag_tr_split(Ss + 32 * kb2 * L7 + cc, L7);
+        const x8 fg = frag_tr_split(Gs_ + 32 * kb2 * L7 + cc, L7);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const x8 fk = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
+          ks[tb] = mfma16(fk, fs, ks[tb]);
+          kg[tb] = mfma16(fk, fg, kg[tb]);
+        }
+      }
+      // R = diag(beta) V - diag(beta e^gamma) K S
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tb + 4 * grp + e;
+          R[tb][e] = bet[r] * to_f(Vs[r * L7 + cc + col]) - bex[r] * ks[tb][e];
+        }
+      // Delta = A R ; dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
+      const x8 Rb0 = pack_split<T>(R[0], R[1]), Rb1 = pack_split<T>(R[2], R[3]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc = mfma16(frag_row_split(As + 16 * tb * L7, L7), Rb0, zero4());
+        if (tb >= 2) acc = mfma16(frag_row_split(As + 16 * tb * L7 + 32, L7), Rb1, acc);
+        Dl[tb] = acc;
+        f32x4 pt = zero4();
+#pragma unroll
+        for (int kt = tb / 2; kt < 2; ++kt)
+          pt = mfma16(frag_tr_split(Ps + 32 * kt * L7 + 16 * tb, L7),
+                      frag_tr_split(Os + 32 * kt * L7 + cc, L7), pt);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tb + 4 * grp + e;
+          dD[tb][e] = dl[r] * kg[tb][e] + a.scale * pt[e];
+        }
+      }
+      // dR = A^T dDelta
+      const x8 Db0 = pack_split<T>(dD[0], dD[1]), Db1 = pack_split<T>(dD[2], dD[3]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc = mfma16(frag_tr_split(As + 32 * L7 + 16 * tb, L7), Db1, zero4());
+        if (tb < 2) acc = mfma16(frag_tr_split(As + 16 * tb, L7), Db0, acc);
+        dR[tb] = acc;
+      }
+    }
+    // dv, the v . dR part of dbeta, and the tiles for the v-contractions
+    T* dvp = reinterpret_cast<T*>(a.dv);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tb + 4 * grp + e;
+        if (r < Cc) dvp[((t0 + r) * a.Hv + h) * kDim + v0 + cc + col] = from_f<T>(bet[r] * dR[tb][e]);
+        const float pdot = sum16(to_f(Vs[r * L7 + cc + col]) * dR[tb][e]);
+        if (col == 0) dbv[4 * hv + w][r] = pdot;
+        Rs[r * L7 + cc + col] = from_f<T>(R[tb][e]);
+        Dls[r * L7 + cc + col] = from_f<T>(Dl[tb][e]);
+        DDs[r * L7 + cc + col] = from_f<T>(dD[tb][e]);
+        DRs[r * L7 + cc + col] = from_f<T>(dR[tb][e]);
+      }
+    }
+    // <S, dSn> over this half: thread tid sums a fixed slice
+    {
+      float acc = 0.f;
+      for (int x = tid; x < 128 * 64; x += 256) {
+        const int r = x >> 6, cc2 = x & 63;
+        acc += to_f(Ss[r * L7 + cc2]) * to_f(Gs_[r * L7 + cc2]);
+      }
+      sds += acc;
+    }
+    __syncthreads();
+
+    // ---- wave w: rows 16w .. 16w+15, contractions over this half's v ----
+#pragma unroll
+    for (int vk = 0; vk < 2; ++vk) {
+      const x8 fdd = frag_row_split(DDs + 16 * w * L7 + 32 * vk, L7);
+      const x8 fdo = frag_row_split(Os + 16 * w * L7 + 32 * vk, L7);
+      const x8 fdr = frag_row_split(DRs + 16 * w * L7 + 32 * vk, L7);
+      const x8 fdl = frag_row_split(Dls + 16 * w * L7 + 32 * vk, L7);
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        if (ib <= w) {
+          dA[ib] = mfma16(fdd, frag_row_split(Rs + 16 * ib * L7 + 32 * vk, L7), dA[ib]);
+          dP[ib] = mfma16(fdo, frag_row_split(Dls + 16 * ib * L7 + 32 * vk, L7), dP[ib]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const x8 fs = frag_row_split(Ss + 16 * kb * L7 + 32 * vk, L7);
+        dQ1[kb] = mfma16(fdo, fs, dQ1[kb]);
+        dX[kb] = mfma16(fdr, fs, dX[kb]);
+        dKs[kb] = mfma16(fdl, frag_row_split(Gs_ + 16 * kb * L7 + 32 * vk, L7), dKs[kb]);
+      }
+    }
+  }
+  red[tid] = sds;
+  __syncthreads();
+
+  // ---- C x C terms, rows r = 16w + 4grp + e ----
+  T* dAs = Ss;              // bf16 dA (64 x 64)
+  T* T1s = Ss + 64 * L7;    // bf16 A^T dA
+  T* dPG = Gs_;             // bf16 dP o Gamma
+  T* DMs = Gs_ + 64 * L7;   // bf16 dM o beta Gamma
+  float rowacc[4] = {0.f, 0.f, 0.f, 0.f};  // dgamma row terms of this lane's rows
+  float dbacc[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta row terms
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    float cs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
+      const float dpv = (i <= r) ? a.scale * dP[cb][e] : 0.f;
+      const float E = dpv * pv[cb][e];
+      rowacc[e] += E;
+      cs += E;
+      const float gm = (i <= r) ? __expf(gam[r] - gam[i]) : 0.f;
+      dPG[r * L7 + i] = from_f<T>(dpv * gm);
+      dAs[r * L7 + i] = from_f<T>(i <= r ? dA[cb][e] : 0.f);
+    }
+    cs = sum4g(cs);
+    if (grp == 0) colE[w][16 * cb + col] = cs;
+  }
+  __syncthreads();
+  // dgamma -= column sums of dP o P (fixed order over waves)
+  if (tid < 64) {
+    dgam[tid] -= colE[0][tid] + colE[1][tid] + colE[2][tid] + colE[3][tid];
+  }
+  // T1 = A^T dA (rows 16w), and the (dP o Gamma) products
+  f32x4 dQ2[8], dK2[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    dQ2[x] = zero4();
+    dK2[x] = zero4();
+  }
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int mk = 0; mk < 2; ++mk)
+      acc = mfma16(frag_tr_split(As + 32 * mk * L7 + 16 * w, L7),
+                   frag_tr_split(dAs + 32 * mk * L7 + 16 * ib, L7), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) T1s[(16 * w + 4 * grp + e) * L7 + 16 * ib + col] = from_f<T>(acc[e]);
+  }
+#pragma unroll
+  for (int ik = 0; ik < 2; ++ik) {
+    const x8 fa = frag_row_split(dPG + 16 * w * L7 + 32 * ik, L7);
+    const x8 fb = frag_tr_split(dPG + 32 * ik * L7 + 16 * w, L7);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      dQ2[kb] = mfma16(fa, frag_tr_split(Ks + 32 * ik * LD + 16 * kb, LD), dQ2[kb]);
+      dK2[kb] = mfma16(fb, frag_tr_split(Qs + 32 * ik * LD + 16 * kb, LD), dK2[kb]);
+    }
+  }
+  __syncthreads();
+  // dM = strict_lower(-T1 A^T), rows 16w
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int mk = 0; mk < 2; ++mk)
+      acc = mfma16(frag_row_split(T1s + 16 * w * L7 + 32 * mk, L7),
+                   frag_row_split(As + 16 * ib * L7 + 32 * mk, L7), acc);
+    float cs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * grp + e, i = 16 * ib + col;
+      const float dm = (i < r) ? -acc[e] : 0.f;
+      // M = beta_r N, N = (k_r . k_i) Gamma_ri
+      dbacc[e] += dm * nv[ib][e];
+      const float E2 = dm * bet[r] * nv[ib][e];
+      rowacc[e] += E2;
+      cs += E2;
+      const float gm = (i < r) ? __expf(gam[r] - gam[i]) : 0.f;
+      DMs[r * L7 + i] = from_f<T>(dm * bet[r] * gm);
+    }
+    cs = sum4g(cs);
+    if (grp == 0) colE[w][16 * ib + col] = cs;
+  }
+  __syncthreads();
+  if (tid < 64) dgam[tid] -= colE[0][tid] + colE[1][tid] + colE[2][tid] + colE[3][tid];
+  // dK3 = D K + D^T K
+#pragma unroll
+  for (int ik = 0; ik < 2; ++ik) {
+    const x8 fa = frag_row_split(DMs + 16 * w * L7 + 32 * ik, L7);
+    const x8 fb = frag_tr_split(DMs + 32 * ik * L7 + 16 * w, L7);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const x8 fk = frag_tr_split(Ks + 32 * ik * LD + 16 * kb, LD);
+      dK2[kb] = mfma16(fa, fk, dK2[kb]);
+      dK2[kb] = mfma16(fb, fk, dK2[kb]);
+    }
+  }
+
+  // ---- final rows: dq, dk, dbeta, dgamma ----
+  float qsd[4] = {0.f, 0.f, 0.f, 0.f}, kdx[4] = {0.f, 0.f, 0.f, 0.f}, fF[4] = {0.f, 0.f, 0.f, 0.f};
+  float dqv[8][4], dkv[8][4];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * grp + e, key = 16 * kb + col;
+      const float qv = to_f(Qs[r * LD + key]), kv = to_f(Ks[r * LD + key]);
+      const float dxv = -dX[kb][e];  // dX = -dR S^T
+      qsd[e] += qv * dQ1[kb][e];
+      kdx[e] += kv * dxv;
+      fF[e] += kv * dKs[kb][e];
+      dqv[kb][e] = a.scale * eg[r] * dQ1[kb][e] + dQ2[kb][e];
+      dkv[kb][e] = dK2[kb][e] + dl[r] * dKs[kb][e] + bex[r] * dxv;
+    }
+  float Fsum_part = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 16 * w + 4 * grp + e;
+    qsd[e] = sum16(qsd[e]);
+    kdx[e] = sum16(kdx[e]);
+    fF[e] = sum16(fF[e]) * dl[r];
+    rowacc[e] = sum16(rowacc[e]);
+    dbacc[e] = sum16(dbacc[e]);
+    if (r >= Cc) fF[e] = 0.f;
+    Fsum_part += fF[e];  // same value in all 16 lanes of the group
+  }
+  // F summed over every row of the chunk, in a fixed order
+  if (col == 0) fsum[w][grp] = Fsum_part;
+  __syncthreads();
+  if (col == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * grp + e;
+      float dgv = a.scale * eg[r] * qsd[e] + rowacc[e] + bex[r] * kdx[e] - fF[e];
+      if (r == Cc - 1) {
+        float Fs = 0.f;
+        for (int ww = 0; ww < 4; ++ww)
+          for (int gg = 0; gg < 4; ++gg) Fs += fsum[ww][gg];
+        float ss = 0.f;
+        for (int x = 0; x < 256; ++x) ss += red[x];
+        dgv += Fs + __expf(gL) * ss;
+      }
+      dgam[r] += dgv;
+      const float db = dbv[0][r] + dbv[1][r] + dbv[2][r] + dbv[3][r] + dbv[4][r] + dbv[5][r] +
+                       dbv[6][r] + dbv[7][r] + eg[r] * kdx[e] + dbacc[e];
+      if (r < Cc) reinterpret_cast<T*>(a.dbeta)[(t0 + r) * a.Hv + h] = from_f<T>(db);
+    }
+  }
+  // dq, dk rows
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + 4 * grp + e, key = 16 * kb + col;
+      if (r < Cc) {
+        if (a.partial) {
+          reinterpret_cast<float*>(a.dq)[((t0 + r) * a.Hv + h) * kDim + key] = dqv[kb][e];
+          reinterpret_cast<float*>(a.dk)[((t0 + r) * a.Hv + h) * kDim + key] = dkv[kb][e];
+        } else {
+          reinterpret_cast<T*>(a.dq)[((t0 + r) * a.Hq + hq) * kDim + key] = from_f<T>(dqv[kb][e]);
+          reinterpret_cast<T*>(a.dk)[((t0 + r) * a.Hq + hq) * kDim + key] = from_f<T>(dkv[kb][e]);
+        }
+      }
+    }
+  __syncthreads();
+  // dg = reverse cumsum of dgamma over the valid rows (one lane, fixed order)
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int r = Cc - 1; r >= 0; --r) {
+      acc += dgam[r];
+      store_scalar(a.dg, (t0 + r) * a.Hv + h, a.g_dtype, acc);
+    }
+  }
+}
+
+// B6: dq[t, hq] = sum over the group's value heads, in head order
+template <typename T>
+__global__ void gva_reduce_kernel(const float* pq, const float* pk, T* dq, T* dk, int64_t Ttot,
+                                  int Hq, int Hv) {
+  const int G = Hv / Hq;
+  const int64_t total = Ttot * Hq * kDim;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < total;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int key = (int)(x % kDim);
+    const int64_t th = x / kDim;
+    const int hq = (int)(th % Hq);
+    const int64_t t = th / Hq;
+    float sq = 0.f, sk = 0.f;
+    for (int r = 0; r < G; ++r) {
+      const int64_t src = (t * Hv + hq * G + r) * kDim + key;
+      sq += pq[src];
+      sk += pk[src];
+    }
+    dq[x] = from_f<T>(sq);
+    dk[x] = from_f<T>(sk);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct BwdLayout {
+  size_t offs, cp, h, dh, pq, pk, total;
+};
+
+static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
+  BwdLayout L;
+  size_t o = 0;
+  L.offs = o;
+  if (p->cu_seqlens_dev) o += align256(sizeof(int32_t) * (size_t)(pl.N + 1));
+  L.cp = o;
+  o += cp_workspace_bytes(pl, p->Hv);
+  const size_t st = (size_t)pl.total_chunks * p->Hv * kDim * kDim * 2;  // bf16/fp16
+  L.h = o;
+  o += align256(st);
+  L.dh = o;
+  o += align256(st);
+  L.pq = L.pk = o;
+  if (p->Hq != p->Hv) {
+    const size_t part = (size_t)p->B * p->T * p->Hv * kDim * sizeof(float);
+    L.pq = o;
+    o += align256(part);
+    L.pk = o;
+    o += align256(part);
+  }
+  L.total = o;
+  return L;
+}
+
+size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl) { return bwd_layout(p, pl).total; }
+
+template <typename T, int VB>
+static void launch_dh_vb(const Plan& pl, DhArgs a, hipStream_t st) {
+  const unsigned units = (unsigned)(pl.N * a.Hv);
+  if (pl.cp > 1) {
+    DhArgs a1 = a;
+    a1.P = pl.cp;
+    a1.nvs = 4 / VB;
+    hipLaunchKernelGGL((dh_scan_kernel<T, VB, MODE_AUG>), dim3(units * pl.cp * a1.nvs), dim3(256),
+                       0, st, a1);
+    ScanArgs sa;
+    memset(&sa, 0, sizeof(sa));
+    sa.cu = a.cu;
+    sa.T = a.T;
+    sa.Hv = a.Hv;
+    sa.P = pl.cp;
+    sa.seg_out = a.seg_out;
+    sa.seg_start = a.seg_start;
+    sa.reverse = 1;
+    hipLaunchKernelGGL(cp_combine_kernel, dim3(units * 8), dim3(256), 0, st, sa);
+  }
+  a.P = pl.cp;
+  a.nvs = 2 / VB;
+  hipLaunchKernelGGL((dh_scan_kernel<T, VB, MODE_OUT>), dim3(units * pl.cp * a.nvs), dim3(256), 0,
+                     st, a);
+}
+
+template <typename T>
+static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
+                               const void* v, const float* gcum, const void* beta, const void* A,
+                               const void* dO, const float* dht, const float* h0, void* dq,
+                               void* dk, void* dv, void* dbeta, void* dg, float* dh0, char* ws,
+                               hipStream_t st) {
+  const BwdLayout L = bwd_layout(p, pl);
+  const int32_t* offs = nullptr;
+  if (p->cu_seqlens_dev) {
+    int32_t* o32 = reinterpret_cast<int32_t*>(ws + L.offs);
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, st, p->cu_seqlens_dev, pl.N,
+                       o32);
+    offs = o32;
+  }
+  float* cp_out = nullptr;
+  float* cp_start = nullptr;
+  if (pl.cp > 1) {
+    const size_t units = (size_t)pl.N * p->Hv;
+    cp_out = reinterpret_cast<float*>(ws + L.cp);
+    cp_start = reinterpret_cast<float*>(ws + L.cp +
+                                        align256(units * pl.cp * 2 * kDim * kDim * sizeof(float)));
+  }
+  void* hbuf = ws + L.h;
+  void* dhbuf = ws + L.dh;
+  // B1: chunk-start states
+  ScanArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
+  sa.h = hbuf;
+  sa.cu = p->cu_seqlens_dev; sa.offs = offs;
+  sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
+  sa.P = 1; sa.nvs = 1; sa.scale = p->scale; sa.svf = p->state_v_first ? 1 : 0; sa.h_svf = 0;
+  sa.seg_out = cp_out; sa.seg_start = cp_start; sa.reverse = 0;
+  launch_scan<T>(pl, sa, MODE_STATE, st);
+  // B2: state gradients
+  DhArgs da;
+  da.q = q; da.k = k; da.dO = dO; da.beta = beta; da.gcum = gcum; da.A = A; da.dht = dht;
+  da.dh = dhbuf; da.dh0 = dh0; da.seg_start = cp_start; da.seg_out = cp_out;
+  da.cu = p->cu_seqlens_dev; da.offs = offs;
+  da.N = pl.N; da.T = p->T; da.Hq = p->Hq; da.Hv = p->Hv; da.nc_dense = pl.nc_dense;
+  da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf;
+  if (pl.vb == 2) launch_dh_vb<T, 2>(pl, da, st);
+  else launch_dh_vb<T, 1>(pl, da, st);
+  // B3-B5
+  const bool partial = p->Hq != p->Hv;
+  GradArgs ga;
+  ga.q = q; ga.k = k; ga.v = v; ga.dO = dO; ga.beta = beta; ga.gcum = gcum; ga.A = A;
+  ga.h = hbuf; ga.dh = dhbuf;
+  ga.dq = partial ? (void*)(ws + L.pq) : dq;
+  ga.dk = partial ? (void*)(ws + L.pk) : dk;
+  ga.dv = dv; ga.dbeta = dbeta; ga.dg = dg;
+  ga.cu = p->cu_seqlens_dev; ga.offs = offs;
+  ga.N = pl.N; ga.T = p->T; ga.Hq = p->Hq; ga.Hv = p->Hv; ga.nc_dense = pl.nc_dense;
+  ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale; ga.partial = partial ? 1 : 0;
+  if (pl.total_chunks > 0)
+    hipLaunchKernelGGL(grad_kernel<T>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(256), 0, st,
+                       ga);
+  // B6
+  if (partial) {
+    const int64_t Ttot = (int64_t)p->B * p->T;
+    const int64_t total = Ttot * p->Hq * kDim;
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+    hipLaunchKernelGGL(gva_reduce_kernel<T>, dim3(blocks), dim3(256), 0, st,
+                       reinterpret_cast<const float*>(ws + L.pq),
+                       reinterpret_cast<const float*>(ws + L.pk), reinterpret_cast<T*>(dq),
+                       reinterpret_cast<T*>(dk), Ttot, p->Hq, p->Hv);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("backward launch failed: %s", hipGetErrorString(e));
+    return GDR_ERR_HIP;
+  }
+  return GDR_OK;
+}
+
+gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
+                      const void* v, const float* gcum, const void* beta, const void* A,
+                      const void* dO, const float* dht, const float* h0, void* dq, void* dk,
+                      void* dv, void* dbeta, void* dg, float* dh0, void* ws, hipStream_t st) {
+  char* w = reinterpret_cast<char*>(ws);
+  if (p->in_dtype == GDR_BF16)
+    return launch_bwd_t<__bf16>(p, pl, q, k, v, gcum, beta, A, dO, dht, h0, dq, dk, dv, dbeta, dg,
+                                dh0, w, st);
+  return launch_bwd_t<_Float16>(p, pl, q, k, v, gcum, beta, A, dO, dht, h0, dq, dk, dv, dbeta, dg,
+                                dh0, w, st);
 }
 
 }  // namespace gdr

@@ -47,20 +47,6 @@ struct FwdArgs {
   int svf;
 };
 
-// Chunk offsets of packed sequences, computed on the device so that no
-// device-to-host copy is needed: offs[0] = 0, offs[n+1] = offs[n] +
-// ceil(len_n / 64).
-__global__ void chunk_offsets_kernel(const int32_t* cu, int N, int32_t* offs) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    int32_t acc = 0;
-    offs[0] = 0;
-    for (int n = 0; n < N; ++n) {
-      acc += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
-      offs[n + 1] = acc;
-    }
-  }
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   constexpr int LDK = 136;
@@ -250,6 +236,7 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   sa.P = 1; sa.nvs = 1;
   sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf;
   sa.seg_out = nullptr; sa.seg_start = nullptr;
+  sa.reverse = 0;
   if (pl.cp > 1) {
     const size_t units = (size_t)pl.N * p->Hv;
     const size_t KV = (size_t)kDim * kDim;

@@ -31,6 +31,20 @@ namespace gdr {
 
 enum ScanMode { MODE_OUT = 0, MODE_AUG = 1, MODE_STATE = 2 };
 
+// Chunk offsets of packed sequences, computed on the device so that no
+// device-to-host copy is needed: offs[0] = 0, offs[n+1] = offs[n] +
+// ceil(len_n / 64).
+static __global__ void chunk_offsets_kernel(const int32_t* cu, int N, int32_t* offs) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    int32_t acc = 0;
+    offs[0] = 0;
+    for (int n = 0; n < N; ++n) {
+      acc += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+      offs[n + 1] = acc;
+    }
+  }
+}
+
 struct ScanArgs {
   const void* q;
   const void* k;
@@ -53,6 +67,7 @@ struct ScanArgs {
   float scale;
   int svf;     // layout of h0 / ht / user h
   int h_svf;   // layout of h (user h follows svf; the backward's own copy is [K][V])
+  int reverse; // cp_combine_kernel: chain segments backwards (state gradients)
 };
 
 // Chunks [c0, c1) of segment p; the segment holding the last chunk is
@@ -140,7 +155,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   TileRegs<128, 256> rq, rk;
   TileRegs<CW, 256> rv;
   TileRegs<64, 256> ra;
-  float r_g = 0.f, r_b = 0.f, r_gl = 0.f;
+  float r_g = 0.f, r_gl = 0.f;
+  T r_b = from_f<T>(0.f);  // raw bits: converting here would wait for every prefetched load
   auto prefetch = [&](int c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
@@ -151,7 +167,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     if (tid < 64) {
       r_g = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
       r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
-      r_b = (tid < Cc) ? to_f(beta[(t0 + tid) * a.Hv + h]) : 0.f;
+      r_b = (tid < Cc) ? beta[(t0 + tid) * a.Hv + h] : from_f<T>(0.f);
     }
   };
 
@@ -170,11 +186,12 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     if (!isT) tile_store<T, CW, 256>(Vs, LDV, rv);
     tile_store<T, 64, 256>(As, LDA, ra);
     if (tid < 64) {
+      const float bv = to_f(r_b);
       gam[tid] = r_g;
-      bet[tid] = r_b;
+      bet[tid] = bv;
       const float e = __expf(r_g);
       eg[tid] = e;
-      bex[tid] = r_b * e;
+      bex[tid] = bv * e;
       dl[tid] = __expf(r_gl - r_g);
     }
     __syncthreads();
@@ -389,11 +406,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   }
 }
 
-// Pass 2: chain the segment start states of one (unit, 16-column block):
-//   start[1] = B_0 (segment 0 ran from the initial state),
-//   start[p] = T_{p-1} start[p-1] + B_{p-1}, p = 2 .. p_last.
+// Pass 2: chain the segment start states of one (unit, 16-column block).
+// Forward:  start[1] = B_0 (segment 0 ran from the initial state),
+//           start[p] = T_{p-1} start[p-1] + B_{p-1},  p = 2 .. p_last.
+// Reverse (state gradients, segments walked from the end): with G[p] the
+// gradient entering segment p's end, G[p_last-1] = B_{p_last} (the last
+// segment ran from dht), G[p] = T_{p+1} G[p+1] + B_{p+1}, p = p_last-2 .. 0.
 // fp32 MFMA (16x16x4); wave w owns rows 32w .. 32w+31.
-__global__ __launch_bounds__(256) void cp_combine_kernel(ScanArgs a) {
+static __global__ __launch_bounds__(256) void cp_combine_kernel(ScanArgs a) {
   __shared__ float Sp[128 * 17];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const int unit = blockIdx.x >> 3, cblk = blockIdx.x & 7;
@@ -403,8 +423,10 @@ __global__ __launch_bounds__(256) void cp_combine_kernel(ScanArgs a) {
   const SegRange sr = seg_range(nch, a.P, 0);
   const int64_t KV = (int64_t)kDim * kDim;
   const int c0 = 16 * cblk;
-  for (int p = 1; p <= sr.p_last; ++p) {
-    const float* prev = a.seg_out + ((int64_t)unit * a.P + (p - 1)) * (2 * KV);
+  for (int jstep = 1; jstep <= sr.p_last; ++jstep) {
+    const int p = a.reverse ? sr.p_last - jstep : jstep;
+    const int src = a.reverse ? p + 1 : p - 1;
+    const float* prev = a.seg_out + ((int64_t)unit * a.P + src) * (2 * KV);
     float* dst = const_cast<float*>(a.seg_start) + ((int64_t)unit * a.P + p) * KV;
     f32x4 acc[2];
 #pragma unroll
@@ -413,7 +435,7 @@ __global__ __launch_bounds__(256) void cp_combine_kernel(ScanArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         acc[rt][e] = prev[(r0 + 4 * grp + e) * (2 * kDim) + kDim + c0 + col];
-      if (p > 1) {
+      if (jstep > 1) {
         for (int st = 0; st < 32; ++st) {
           const float av = prev[(r0 + col) * (2 * kDim) + 4 * st + grp];
           const float bv = Sp[(4 * st + grp) * 17 + col];

@@ -1,0 +1,122 @@
+"""GPU parity of the backward against the fp64 oracle (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import gdr_synth
+import oracle
+from _util import TOL, np64, ratio, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
+
+
+def gpu_fwd_bwd(d, svf=False, cp=0):
+    import gated_delta_rule_66_amd as gdr
+    dd = to_dev(d)
+    h0, dht = dd["h0"], dd["dht"]
+    if svf:
+        h0 = None if h0 is None else h0.transpose(-1, -2).contiguous()
+        dht = None if dht is None else dht.transpose(-1, -2).contiguous()
+    cu_cpu = d["cu_seqlens"]
+    g_cum, A, o, _, ht = gdr.chunk_gated_delta_rule_fwd(
+        dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"], initial_state=h0,
+        output_final_state=True, cu_seqlens=dd["cu_seqlens"], state_v_first=svf, cp_segments=cp,
+        cu_seqlens_cpu=cu_cpu)
+    grads = gdr.chunk_gated_delta_rule_bwd(
+        dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dht, scale=dd["scale"],
+        initial_state=h0, cu_seqlens=dd["cu_seqlens"], state_v_first=svf, dg_dtype=dd["g"].dtype,
+        cp_segments=cp, cu_seqlens_cpu=cu_cpu)
+    torch.cuda.synchronize()
+    return o, ht, grads
+
+
+def oracle_grads(d):
+    cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].numpy()
+    return oracle.bwd(np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]),
+                      d["scale"], np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]),
+                      cu_seqlens=cu)
+
+
+def P(name, **kw):
+    kw.setdefault("backward", True)
+    return gdr_synth.Problem(name, **kw)
+
+
+CASES = {
+    "dense_state_dht": P("dense", B=2, T=200, Hq=2, Hv=2, init_state=True, dht=True),
+    "no_state": P("nostate", B=1, T=130, Hq=2, Hv=2),
+    "fp16_gva": P("fp16_gva", B=1, T=333, Hq=1, Hv=2, dtype="fp16", init_state=True, dht=True),
+    "varlen": P("varlen", B=1, T=0, Hq=2, Hv=2, init_state=True, dht=True,
+                lens=[70, 1, 64, 129, 250]),
+    "varlen_empty_seq": P("varlen_empty", B=1, T=0, Hq=1, Hv=1, init_state=True, dht=True,
+                          lens=[70, 0, 65]),
+    "one_token": P("one", B=1, T=1, Hq=1, Hv=1, init_state=True, dht=True),
+    "long_slow_decay": P("long", B=1, T=1500, Hq=2, Hv=2, init_state=True, dht=True, g_shift=2.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_matches_oracle(name):
+    d = gdr_synth.make(CASES[name])
+    print("case", name, CASES[name], flush=True)
+    o, ht, g = gpu_fwd_bwd(d, cp=1)
+    ref = oracle_grads(d)
+    for nm, x, r in zip(NAMES, g, ref):
+        if r is None:
+            assert x is None
+            continue
+        rt = ratio(np64(x), r)
+        print(nm, rt, flush=True)
+        assert rt <= TOL, (nm, rt)
+
+
+CP_CASES = [("long_slow_decay", 2), ("long_slow_decay", 4), ("long_slow_decay", 7),
+            ("varlen", 2), ("varlen", 3), ("fp16_gva", 4)]
+
+
+@pytest.mark.parametrize("name,cp", CP_CASES)
+def test_context_parallel_backward_matches_oracle(name, cp):
+    d = gdr_synth.make(CASES[name])
+    print("case", name, "cp", cp, flush=True)
+    o, ht, g = gpu_fwd_bwd(d, cp=cp)
+    ref = oracle_grads(d)
+    for nm, x, r in zip(NAMES, g, ref):
+        rt = ratio(np64(x), r)
+        print(nm, rt, flush=True)
+        assert rt <= TOL, (nm, rt)
+
+
+@pytest.mark.parametrize("cp", [1, 3])
+def test_backward_state_v_first_is_bit_exact(cp):
+    d = gdr_synth.make(CASES["varlen"])
+    _, _, a = gpu_fwd_bwd(d, svf=False, cp=cp)
+    _, _, b = gpu_fwd_bwd(d, svf=True, cp=cp)
+    for x, y in zip(a[:5], b[:5]):
+        assert torch.equal(x, y)
+    assert torch.equal(a[5].transpose(-1, -2), b[5])
+
+
+def test_backward_is_deterministic():
+    d = gdr_synth.make(CASES["fp16_gva"])
+    _, _, a = gpu_fwd_bwd(d)
+    _, _, b = gpu_fwd_bwd(d)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_autograd_end_to_end():
+    import gated_delta_rule_66_amd as gdr
+    d = gdr_synth.make(CASES["dense_state_dht"])
+    dd = to_dev(d)
+    leaves = {k: dd[k].clone().requires_grad_(True) for k in ("q", "k", "v", "g", "beta", "h0")}
+    o, ht = gdr.chunk_gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["g"],
+                                       leaves["beta"], scale=dd["scale"],
+                                       initial_state=leaves["h0"], output_final_state=True)
+    loss = (o.float() * dd["do"].float()).sum() + (ht * dd["dht"]).sum()
+    loss.backward()
+    ref = oracle_grads(d)
+    for nm, key in zip(NAMES, ("q", "k", "v", "beta", "g", "h0")):
+        rt = ratio(np64(leaves[key].grad), ref[NAMES.index(nm)])
+        assert rt <= TOL, (nm, rt)
