@@ -232,3 +232,42 @@ def prepare_chunk_offsets(cu_seqlens: torch.Tensor, chunk_size: int):
     check(getattr(lib, "gdr_prepare_chunk_offsets_" + sfx)(_ptr(cu), cu.numel(), int(chunk_size),
                                                            _ptr(out), ctypes.byref(total)))
     return out.to(cu_seqlens.device), int(total.value)
+
+
+# ---- diagnostics --------------------------------------------------------------
+
+def plan_info(q, v, g_dtype=None, cu_seqlens=None, cu_seqlens_cpu=None, cp_segments=0):
+    """``(cp_segments, wave_tiles)`` the library plans for these shapes."""
+    c = _Call(q, v, q.dtype if g_dtype is None else g_dtype, None, cu_seqlens, cu_seqlens_cpu,
+              False, cp_segments)
+    cp = ctypes.c_int32(0)
+    vt = ctypes.c_int32(0)
+    check(lib.gdr_plan_info(c.ref, ctypes.byref(cp), ctypes.byref(vt)))
+    return int(cp.value), int(vt.value)
+
+
+class KernelTimer:
+    """Brackets every kernel the library launches with HIP events while
+    active; ``read()`` returns ``{name: (total_ms, launches)}``."""
+
+    def __enter__(self):
+        check(lib.gdr_profile_enable(1))
+        return self
+
+    def __exit__(self, *exc):
+        lib.gdr_profile_enable(0)
+        return False
+
+    @staticmethod
+    def read(max_entries=32):
+        stride = 64
+        names = ctypes.create_string_buffer(stride * max_entries)
+        tot = (ctypes.c_double * max_entries)()
+        cnt = (ctypes.c_int * max_entries)()
+        n = lib.gdr_profile_read(names, stride, ctypes.cast(tot, ctypes.c_void_p),
+                                 ctypes.cast(cnt, ctypes.c_void_p), max_entries)
+        out = {}
+        for i in range(n):
+            nm = names.raw[i * stride:(i + 1) * stride].split(b"\0", 1)[0].decode()
+            out[nm] = (float(tot[i]), int(cnt[i]))
+        return out

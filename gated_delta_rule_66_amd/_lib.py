@@ -38,7 +38,8 @@ EXPORTS = [
     "gdr_chunk_bwd", "gdr_prepare_lens_i32", "gdr_prepare_lens_i64",
     "gdr_prepare_chunk_indices_i32", "gdr_prepare_chunk_indices_i64",
     "gdr_prepare_chunk_offsets_i32", "gdr_prepare_chunk_offsets_i64",
-    "gdr_prepare_chunk_token_starts_i64",
+    "gdr_prepare_chunk_token_starts_i64", "gdr_profile_enable", "gdr_profile_read",
+    "gdr_plan_info",
 ]
 
 
@@ -81,6 +82,17 @@ def _declare(lib):
         getattr(lib, name).restype = st
 
 
+def _declare_profile(lib):
+    lib.gdr_profile_enable.argtypes = [ctypes.c_int]
+    lib.gdr_profile_enable.restype = ctypes.c_int
+    lib.gdr_profile_read.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int]
+    lib.gdr_profile_read.restype = ctypes.c_int
+    lib.gdr_plan_info.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int32),
+                                  ctypes.POINTER(ctypes.c_int32)]
+    lib.gdr_plan_info.restype = ctypes.c_int
+
+
 def load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -88,6 +100,7 @@ def load():
             % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     _declare(lib)
+    _declare_profile(lib)
     return lib
 
 

@@ -9,6 +9,8 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <string>
+#include <vector>
 
 #include "gdr_internal.h"
 
@@ -21,6 +23,31 @@ void set_error(const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
+}
+
+// ---- per-kernel timing -----------------------------------------------------
+volatile int g_profiling = 0;
+namespace {
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;
+}  // namespace
+
+void profile_begin(hipStream_t st, const char* name) {
+  ProfRec r;
+  r.name = name;
+  if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
+  (void)hipEventRecord(r.start, st);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back(r);
+}
+
+void profile_end(hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof.empty()) (void)hipEventRecord(g_prof.back().stop, st);
 }
 
 static gdr_status fail(gdr_status s, char* reason, size_t len, const char* fmt, ...) {
@@ -332,6 +359,60 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   if (s != GDR_OK) return s;
   return launch_bwd(p, pl, q, k, v, g_cum, beta, A, do_, dht, initial_state, dq, dk, dv, dbeta,
                     dg, initial_state ? dh0 : nullptr, workspace, (hipStream_t)stream);
+}
+
+gdr_status gdr_plan_info(const gdr_problem* p, int32_t* cp_segments, int32_t* wave_tiles) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  const Plan pl = make_plan(p);
+  if (cp_segments) *cp_segments = pl.cp;
+  if (wave_tiles) *wave_tiles = pl.vb;
+  return GDR_OK;
+}
+
+gdr_status gdr_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  g_profiling = enable ? 1 : 0;
+  return GDR_OK;
+}
+
+int gdr_profile_read(char* names, size_t name_stride, double* total_ms, int* launches,
+                     int max_entries) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<std::string> keys;
+  std::vector<double> tot;
+  std::vector<int> cnt;
+  for (auto& r : g_prof) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess) (void)hipEventElapsedTime(&ms, r.start, r.stop);
+    size_t i = 0;
+    while (i < keys.size() && keys[i] != r.name) ++i;
+    if (i == keys.size()) {
+      keys.push_back(r.name);
+      tot.push_back(0.0);
+      cnt.push_back(0);
+    }
+    tot[i] += ms;
+    cnt[i] += 1;
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  const int n = (int)keys.size() < max_entries ? (int)keys.size() : max_entries;
+  for (int i = 0; i < n; ++i) {
+    if (names && name_stride) {
+      strncpy(names + i * name_stride, keys[i].c_str(), name_stride - 1);
+      names[i * name_stride + name_stride - 1] = '\0';
+    }
+    if (total_ms) total_ms[i] = tot[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return n;
 }
 
 gdr_status gdr_prepare_lens_i32(const int32_t* cu, int64_t n1, int32_t* lens) {

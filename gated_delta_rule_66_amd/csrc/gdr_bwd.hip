@@ -805,8 +805,8 @@ static void launch_dh_vb(const Plan& pl, DhArgs a, hipStream_t st) {
     DhArgs a1 = a;
     a1.P = pl.cp;
     a1.nvs = 4 / VB;
-    hipLaunchKernelGGL((dh_scan_kernel<T, VB, MODE_AUG>), dim3(units * pl.cp * a1.nvs), dim3(256),
-                       0, st, a1);
+    GDR_LAUNCH("dh_scan_aug", (dh_scan_kernel<T, VB, MODE_AUG>), dim3(units * pl.cp * a1.nvs),
+               dim3(256), st, a1);
     ScanArgs sa;
     memset(&sa, 0, sizeof(sa));
     sa.cu = a.cu;
@@ -816,12 +816,12 @@ static void launch_dh_vb(const Plan& pl, DhArgs a, hipStream_t st) {
     sa.seg_out = a.seg_out;
     sa.seg_start = a.seg_start;
     sa.reverse = 1;
-    hipLaunchKernelGGL(cp_combine_kernel, dim3(units * 8), dim3(256), 0, st, sa);
+    GDR_LAUNCH("cp_combine", cp_combine_kernel, dim3(units * 8), dim3(256), st, sa);
   }
   a.P = pl.cp;
   a.nvs = 2 / VB;
-  hipLaunchKernelGGL((dh_scan_kernel<T, VB, MODE_OUT>), dim3(units * pl.cp * a.nvs), dim3(256), 0,
-                     st, a);
+  GDR_LAUNCH("dh_scan_out", (dh_scan_kernel<T, VB, MODE_OUT>), dim3(units * pl.cp * a.nvs),
+             dim3(256), st, a);
 }
 
 template <typename T>
@@ -834,8 +834,8 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   const int32_t* offs = nullptr;
   if (p->cu_seqlens_dev) {
     int32_t* o32 = reinterpret_cast<int32_t*>(ws + L.offs);
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, st, p->cu_seqlens_dev, pl.N,
-                       o32);
+    GDR_LAUNCH("chunk_offsets", chunk_offsets_kernel, dim3(1), dim3(64), st, p->cu_seqlens_dev,
+               pl.N, o32);
     offs = o32;
   }
   float* cp_out = nullptr;
@@ -879,14 +879,13 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   ga.N = pl.N; ga.T = p->T; ga.Hq = p->Hq; ga.Hv = p->Hv; ga.nc_dense = pl.nc_dense;
   ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale; ga.partial = partial ? 1 : 0;
   if (pl.total_chunks > 0)
-    hipLaunchKernelGGL(grad_kernel<T>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(256), 0, st,
-                       ga);
+    GDR_LAUNCH("grad", grad_kernel<T>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(256), st, ga);
   // B6
   if (partial) {
     const int64_t Ttot = (int64_t)p->B * p->T;
     const int64_t total = Ttot * p->Hq * kDim;
     const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
-    hipLaunchKernelGGL(gva_reduce_kernel<T>, dim3(blocks), dim3(256), 0, st,
+    GDR_LAUNCH("gva_reduce", gva_reduce_kernel<T>, dim3(blocks), dim3(256), st,
                        reinterpret_cast<const float*>(ws + L.pq),
                        reinterpret_cast<const float*>(ws + L.pk), reinterpret_cast<T*>(dq),
                        reinterpret_cast<T*>(dk), Ttot, p->Hq, p->Hv);

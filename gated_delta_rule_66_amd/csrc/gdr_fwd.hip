@@ -189,15 +189,15 @@ static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st)
     ScanArgs a1 = a;
     a1.P = pl.cp;
     a1.nvs = 4 / VB;
-    hipLaunchKernelGGL((scan_kernel<T, VB, MODE_AUG>), dim3(units * pl.cp * a1.nvs), dim3(256), 0,
-                       st, a1);
-    hipLaunchKernelGGL(cp_combine_kernel, dim3(units * 8), dim3(256), 0, st, a1);
+    GDR_LAUNCH("scan_aug", (scan_kernel<T, VB, MODE_AUG>), dim3(units * pl.cp * a1.nvs), dim3(256),
+               st, a1);
+    GDR_LAUNCH("cp_combine", cp_combine_kernel, dim3(units * 8), dim3(256), st, a1);
   }
   a.P = pl.cp;
   a.nvs = 2 / VB;
   const dim3 grid(units * pl.cp * a.nvs);
-  if (mode == MODE_OUT) hipLaunchKernelGGL((scan_kernel<T, VB, MODE_OUT>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((scan_kernel<T, VB, MODE_STATE>), grid, dim3(256), 0, st, a);
+  if (mode == MODE_OUT) GDR_LAUNCH("scan_out", (scan_kernel<T, VB, MODE_OUT>), grid, dim3(256), st, a);
+  else GDR_LAUNCH("scan_state", (scan_kernel<T, VB, MODE_STATE>), grid, dim3(256), st, a);
 }
 
 template <typename T>
@@ -216,8 +216,8 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   const int32_t* offs = nullptr;
   if (p->cu_seqlens_dev) {
     int32_t* o32 = reinterpret_cast<int32_t*>(wp);
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, st, p->cu_seqlens_dev, pl.N,
-                       o32);
+    GDR_LAUNCH("chunk_offsets", chunk_offsets_kernel, dim3(1), dim3(64), st, p->cu_seqlens_dev, pl.N,
+               o32);
     offs = o32;
     wp += align256(sizeof(int32_t) * (size_t)(pl.N + 1));
   }
@@ -246,13 +246,13 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   }
   if (p->in_dtype == GDR_BF16) {
     if (pl.total_chunks > 0)
-      hipLaunchKernelGGL(fwd_prep_kernel<__bf16>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(256),
-                         0, st, fa);
+      GDR_LAUNCH("fwd_prep", fwd_prep_kernel<__bf16>, dim3((unsigned)pl.total_chunks, p->Hv),
+                 dim3(256), st, fa);
     launch_scan<__bf16>(pl, sa, MODE_OUT, st);
   } else {
     if (pl.total_chunks > 0)
-      hipLaunchKernelGGL(fwd_prep_kernel<_Float16>, dim3((unsigned)pl.total_chunks, p->Hv),
-                         dim3(256), 0, st, fa);
+      GDR_LAUNCH("fwd_prep", fwd_prep_kernel<_Float16>, dim3((unsigned)pl.total_chunks, p->Hv),
+                 dim3(256), st, fa);
     launch_scan<_Float16>(pl, sa, MODE_OUT, st);
   }
   hipError_t e = hipGetLastError();

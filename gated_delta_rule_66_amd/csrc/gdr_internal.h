@@ -49,4 +49,17 @@ void launch_scan(const Plan& pl, ScanArgs a, int mode, hipStream_t st);
 
 void set_error(const char* fmt, ...);
 
+// Optional per-kernel timing (diagnostics): while enabled, every launch is
+// bracketed by two HIP events recorded on its stream.
+extern volatile int g_profiling;
+void profile_begin(hipStream_t st, const char* name);
+void profile_end(hipStream_t st);
+
+#define GDR_LAUNCH(name, kernel, grid, block, st, ...)      \
+  do {                                                      \
+    if (::gdr::g_profiling) ::gdr::profile_begin(st, name); \
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, __VA_ARGS__); \
+    if (::gdr::g_profiling) ::gdr::profile_end(st);         \
+  } while (0)
+
 }  // namespace gdr

@@ -172,6 +172,25 @@ gdr_status gdr_prepare_chunk_token_starts_i64(const int64_t* cu, int64_t n_plus_
                                               int64_t chunk_size, int64_t* out,
                                               int64_t* num_chunks);
 
+/* The launch plan the library picks for `p` (it depends only on shapes):
+ * *cp_segments = T-segments per sequence (1 = no context parallelism),
+ * *wave_tiles = 16-column state tiles per wave in the scans (1 or 2). */
+gdr_status gdr_plan_info(const gdr_problem* p, int32_t* cp_segments, int32_t* wave_tiles);
+
+/* Kernel timing for benchmarks and diagnostics (not part of the pages' API).
+ * While enabled, every kernel the library launches is bracketed by a pair of
+ * HIP events recorded on its stream.  gdr_profile_enable clears the records
+ * (and creates events lazily afterwards); gdr_profile_read waits for the
+ * recorded events, adds up the elapsed time per kernel name (names such as
+ * "fwd_prep", "scan_out", "scan_aug", "scan_state", "cp_combine",
+ * "dh_scan_out", "dh_scan_aug", "grad", "gva_reduce", "chunk_offsets"),
+ * writes up to max_entries of them (names: NUL-terminated, name_stride bytes
+ * apart; total_ms; launches -- each may be NULL), clears the records and
+ * returns the number of entries written. */
+gdr_status gdr_profile_enable(int enable);
+int gdr_profile_read(char* names, size_t name_stride, double* total_ms, int* launches,
+                     int max_entries);
+
 #ifdef __cplusplus
 }
 #endif
