@@ -1,0 +1,167 @@
+"""The C ABI on the host: exports, argument validation, workspace queries.
+
+Validation finishes before the first HIP call, so every rejection branch runs
+on a machine without a GPU (the analogue of the verifier rejection tests in
+the FLA backend pull request's test plan)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from gated_delta_rule_66_amd import _lib
+from gated_delta_rule_66_amd._lib import GDR_BF16, GDR_FP16, GDR_FP32, Problem, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "gdr.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 17
+    assert sorted(_lib.EXPORTS) == names
+    cdll = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(cdll, n), n
+
+
+def test_status_strings():
+    for code, name in _lib.STATUS.items():
+        assert lib.gdr_status_string(code).decode() == name
+
+
+def good(**kw):
+    base = dict(B=2, T=200, Hq=2, Hv=4, K=128, V=128, N=2, cu_seqlens_dev=None,
+                cu_seqlens_host=None, in_dtype=GDR_BF16, g_dtype=GDR_BF16, scale=0.088,
+                state_v_first=0, cp_segments=0)
+    base.update(kw)
+    return Problem(**base)
+
+
+def check(p):
+    reason = ctypes.create_string_buffer(256)
+    st = lib.gdr_check_supported(ctypes.byref(p), reason, 256)
+    return _lib.STATUS[st], reason.value.decode()
+
+
+def test_acceptance_path():
+    assert check(good()) == ("GDR_OK", "")
+    assert check(good(in_dtype=GDR_FP16, g_dtype=GDR_FP32))[0] == "GDR_OK"
+
+
+HOST_CU = (ctypes.c_int32 * 4)(0, 70, 70, 200)
+HOST_CU_BAD0 = (ctypes.c_int32 * 4)(1, 70, 70, 200)
+HOST_CU_DEC = (ctypes.c_int32 * 4)(0, 70, 60, 200)
+HOST_CU_END = (ctypes.c_int32 * 4)(0, 70, 70, 199)
+FAKE_DEV = 0x1000  # never dereferenced: validation happens on the host copy
+
+
+def varlen(cu, **kw):
+    return good(B=1, N=3, cu_seqlens_dev=FAKE_DEV,
+                cu_seqlens_host=ctypes.cast(cu, ctypes.c_void_p).value, **kw)
+
+
+REJECT = [
+    ("K=64", good(K=64), "GDR_ERR_HEAD_DIM", "requires K=128, got 64"),
+    ("V=64", good(V=64), "GDR_ERR_HEAD_DIM", "requires V=128, got 64"),
+    ("fp32 inputs", good(in_dtype=GDR_FP32, g_dtype=GDR_FP32), "GDR_ERR_DTYPE", "bf16 or fp16"),
+    ("g dtype", good(g_dtype=GDR_FP16), "GDR_ERR_DTYPE", "g must"),
+    ("Hq>Hv", good(Hq=8, Hv=4), "GDR_ERR_HEADS", "multiple"),
+    ("Hv%Hq", good(Hq=3, Hv=4), "GDR_ERR_HEADS", "multiple"),
+    ("T=0", good(T=0), "GDR_ERR_SHAPE", "positive"),
+    ("N!=B", good(N=3), "GDR_ERR_SHAPE", "N == B"),
+    ("scale", good(scale=float("inf")), "GDR_ERR_ARG", "scale"),
+    ("svf", good(state_v_first=2), "GDR_ERR_ARG", "state_v_first"),
+    ("cp", good(cp_segments=-1), "GDR_ERR_ARG", "cp_segments"),
+]
+
+
+@pytest.mark.parametrize("name,p,status,msg", REJECT, ids=[r[0] for r in REJECT])
+def test_rejections(name, p, status, msg):
+    st, reason = check(p)
+    assert st == status
+    assert msg in reason
+    assert msg in lib.gdr_last_error().decode()
+
+
+def test_varlen_rejections():
+    assert check(varlen(HOST_CU, T=200))[0] == "GDR_OK"
+    p = varlen(HOST_CU, T=200)
+    p.B = 2
+    assert check(p)[0] == "GDR_ERR_VARLEN"
+    assert check(varlen(HOST_CU_BAD0, T=200))[0] == "GDR_ERR_VARLEN"
+    assert check(varlen(HOST_CU_DEC, T=200))[0] == "GDR_ERR_VARLEN"
+    assert check(varlen(HOST_CU_END, T=200))[0] == "GDR_ERR_VARLEN"
+    p = varlen(HOST_CU, T=200)
+    p.cu_seqlens_host = None
+    assert check(p)[0] == "GDR_ERR_VARLEN"
+    assert lib.gdr_check_supported(None, None, 0) == 1  # GDR_ERR_NULL
+
+
+def test_workspace_queries():
+    p = good()
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == 0
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(p)) > 0
+    pv = varlen(HOST_CU, T=200)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(pv)) > 0
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(good(K=64))) == 0
+    long = good(B=1, N=1, T=65536, Hq=32, Hv=32)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(long)) > 0  # context-parallel buffers
+
+
+def test_plan_depends_only_on_shapes():
+    cp = ctypes.c_int32()
+    vt = ctypes.c_int32()
+    plans = []
+    for svf in (0, 1):
+        p = good(B=1, N=1, T=65536, Hq=32, Hv=32, state_v_first=svf)
+        assert lib.gdr_plan_info(ctypes.byref(p), ctypes.byref(cp), ctypes.byref(vt)) == 0
+        plans.append((cp.value, vt.value))
+    assert plans[0] == plans[1]
+    assert plans[0][0] > 1  # one long sequence is split along T
+    p = good(B=1, N=1, T=65536, Hq=32, Hv=32, cp_segments=1)
+    lib.gdr_plan_info(ctypes.byref(p), ctypes.byref(cp), ctypes.byref(vt))
+    assert cp.value == 1
+
+
+def test_null_and_workspace_errors_before_any_device_work():
+    p = good()
+    P = ctypes.c_void_p
+    # missing required outputs
+    st = lib.gdr_chunk_fwd(ctypes.byref(p), P(16), P(16), P(16), P(16), P(16), None, None, P(16),
+                           P(16), None, None, None, 0, None)
+    assert _lib.STATUS[st] == "GDR_ERR_NULL"
+    st = lib.gdr_chunk_bwd(ctypes.byref(p), P(16), P(16), P(16), P(16), P(16), P(16), P(16), None,
+                           P(16), P(16), P(16), P(16), P(16), P(16), None, P(16), 1 << 40, None)
+    assert _lib.STATUS[st] == "GDR_ERR_NULL"  # initial_state without dh0
+    pv = varlen(HOST_CU, T=200)
+    st = lib.gdr_chunk_fwd(ctypes.byref(pv), P(16), P(16), P(16), P(16), P(16), None, P(16),
+                           P(16), P(16), None, None, P(16), 1, None)
+    assert _lib.STATUS[st] == "GDR_ERR_WORKSPACE"
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="exercises the no-device path")
+def test_no_device_is_reported():
+    assert _lib.STATUS[lib.gdr_check_device()] == "GDR_ERR_DEVICE"
+    p = good()
+    P = ctypes.c_void_p
+    st = lib.gdr_chunk_fwd(ctypes.byref(p), P(16), P(16), P(16), P(16), P(16), None, P(16), P(16),
+                           P(16), None, None, None, 0, None)
+    assert _lib.STATUS[st] == "GDR_ERR_DEVICE"
+
+
+def test_python_rejects_verifier_options():
+    import gated_delta_rule_66_amd as gdr
+    x = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    g = torch.zeros(1, 4, 1, dtype=torch.bfloat16)
+    for opt in ("use_gate_in_kernel", "use_beta_sigmoid_in_kernel", "allow_neg_eigval",
+                "transpose_state_layout"):
+        with pytest.raises(NotImplementedError):
+            gdr.chunk_gated_delta_rule(x, x, x, g, g, **{opt: True})
