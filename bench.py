@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cp", type=int, default=0,
+                    help="context-parallel segments per sequence (0 = the library's plan)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path runs on a single MI355X and this build "
@@ -182,19 +184,21 @@ def main():
     dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
     cu_cpu = d["cu_seqlens"]
     cp, wave_tiles = gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
-                                   cu_seqlens_cpu=cu_cpu)
+                                   cu_seqlens_cpu=cu_cpu, cp_segments=args.cp)
 
     def fwd():
         return gdr.chunk_gated_delta_rule_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"],
                                               scale=dd["scale"], initial_state=dd["h0"],
                                               output_final_state=True,
-                                              cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=cu_cpu)
+                                              cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=cu_cpu,
+                                              cp_segments=args.cp)
 
     def bwd(g_cum, A):
         return gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
                                               dd["do"], dht=dd["dht"], scale=dd["scale"],
                                               initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
-                                              dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu)
+                                              dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu,
+                                              cp_segments=args.cp)
 
     def step():
         g_cum, A, o, _, ht = fwd()

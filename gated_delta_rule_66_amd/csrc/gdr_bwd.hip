@@ -70,7 +70,7 @@ struct DhArgs {
 };
 
 template <typename T, int VB, int MODE>
-__global__ __launch_bounds__(256) void dh_scan_kernel(DhArgs a) {
+__global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a) {
   typedef typename VT<T>::x8 x8;
   constexpr int CW = 64 * VB;
   constexpr int LD = 136;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void dh_scan_kernel(DhArgs a) {
   __shared__ __align__(16) T As[64 * LDA];
   __shared__ __align__(16) T Ps[64 * LDA];
   __shared__ __align__(16) T Hs[OUT ? 128 * (CW + 8) : 8];
-  __shared__ float gam[64], eg[64], bex[64], dl[64];
+  __shared__ __align__(16) float gam[64], eg[64], bex[64], dl[64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const int vs = blockIdx.x % a.nvs;
@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256) void dh_scan_kernel(DhArgs a) {
     }
   };
 
+  p_zero_tiles<T>(Ps, LDA);
   if (sr.c0 < sr.c1) prefetch(sr.c1 - 1);
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
     __syncthreads();
@@ -178,34 +179,7 @@ __global__ __launch_bounds__(256) void dh_scan_kernel(DhArgs a) {
           for (int e = 0; e < 4; ++e)
             Hs[(16 * kb + 4 * grp + e) * (CW + 8) + cw0 + 16 * vb + col] = from_f<T>(Gs[kb][vb][e]);
     }
-    // P rows 16w .. 16w+15
-    for (int cbk = 0; cbk < 4; ++cbk) {
-      f32x4 acc = zero4();
-      if (cbk <= w) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          acc = mfma16(frag_row(Qs + 16 * w * LD + 32 * kk, LD),
-                       frag_row(Ks + 16 * cbk * LD + 32 * kk, LD), acc);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * grp + e, i = 16 * cbk + col;
-        float pv = 0.f;
-        if (i <= r) pv = acc[e] * __expf(gam[r] - gam[i]);
-        Ps[r * LDA + i] = from_f<T>(pv);
-      }
-    }
-    __syncthreads();
-    if (OUT) {
-      T* hp = reinterpret_cast<T*>(a.dh) + ((choff + c) * a.Hv + h) * KV;
-      constexpr int PR = CW / 8;
-      for (int x = tid; x < 128 * PR; x += 256) {
-        const int r = x / PR, c8 = (x % PR) * 8;
-        *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
-            *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
-      }
-    }
-
+    if (!isT) p_tiles<T>(Qs, Ks, LD, Ps, LDA, gam, w);
     // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
     x8 Gb[4][VB];
 #pragma unroll
@@ -225,6 +199,17 @@ __global__ __launch_bounds__(256) void dh_scan_kernel(DhArgs a) {
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = mfma16(fk, Gb[kb2][vb], dd[tb][vb]);
       }
+    __syncthreads();
+    if (OUT) {
+      T* hp = reinterpret_cast<T*>(a.dh) + ((choff + c) * a.Hv + h) * KV;
+      constexpr int PR = CW / 8;
+      for (int x = tid; x < 128 * PR; x += 256) {
+        const int r = x / PR, c8 = (x % PR) * 8;
+        *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
+            *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
+      }
+    }
+
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -355,14 +340,14 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   __shared__ __align__(16) T Gs_[128 * L7];  // dSn[:, half]; later dP o Gamma, dM o beta Gamma
   __shared__ __align__(16) T Vs[64 * L7];
   __shared__ __align__(16) T Os[64 * L7];    // dO[:, half]
-  __shared__ __align__(16) T Rs[64 * L7];
-  __shared__ __align__(16) T Dls[64 * L7];   // Delta
-  __shared__ __align__(16) T DDs[64 * L7];   // dDelta
-  __shared__ __align__(16) T DRs[64 * L7];   // dR
+  __shared__ __align__(16) T Rs[64 * L7];    // R, transposed: [v][r]
+  __shared__ __align__(16) T Dls[64 * L7];   // Delta, transposed
+  __shared__ __align__(16) T DDs[64 * L7];   // dDelta, transposed
+  __shared__ __align__(16) T DRs[64 * L7];   // dR, transposed
   __shared__ float gam[64], bet[64], eg[64], bex[64], dl[64];
   __shared__ float dbv[8][64];       // v . dR partials per (half, wave)
   __shared__ float colE[4][64];      // column sums of dP o P and dM o M per wave
-  __shared__ float red[256];         // <S, dSn> partials
+  __shared__ float red[4];           // <S, dSn> per wave
   __shared__ float dgam[64];
   __shared__ float fsum[4][4];       // F partials per (wave, lane group)
 
@@ -386,12 +371,20 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   const T* vv = reinterpret_cast<const T*>(a.v);
   const T* dOg = reinterpret_cast<const T*>(a.dO);
 
-  tile_to_lds<T, 256>(Qs, LD, reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim,
-                      (int64_t)a.Hq * kDim, Cc, kDim);
-  tile_to_lds<T, 256>(Ks, LD, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
-                      (int64_t)a.Hq * kDim, Cc, kDim);
-  tile_to_lds<T, 256>(As, L7, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
-                      (int64_t)a.Hv * kChunk, Cc, kChunk);
+  // every global load of a phase is issued before the first LDS store
+  {
+    TileRegs<128, 256> rq, rk;
+    TileRegs<64, 256> ra;
+    tile_load<T, 128, 256>(rq, reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim,
+                           (int64_t)a.Hq * kDim, Cc);
+    tile_load<T, 128, 256>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
+                           (int64_t)a.Hq * kDim, Cc);
+    tile_load<T, 64, 256>(ra, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
+                          (int64_t)a.Hv * kChunk, Cc);
+    tile_store<T, 128, 256>(Qs, LD, rq);
+    tile_store<T, 128, 256>(Ks, LD, rk);
+    tile_store<T, 64, 256>(As, L7, ra);
+  }
   if (tid < 64) {
     const float gr = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
     const float gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
@@ -448,21 +441,30 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   for (int hv = 0; hv < 2; ++hv) {
     const int v0 = 64 * hv;
     __syncthreads();  // previous half done with the per-half tiles
-    // S[:, half], dSn[:, half]: 128 rows x 64 columns
-    for (int x = tid; x < 128 * 8; x += 256) {
-      const int r = x >> 3, c8 = (x & 7) * 8;
-      *reinterpret_cast<uint4*>(Ss + r * L7 + c8) =
-          *reinterpret_cast<const uint4*>(hS + (int64_t)r * kDim + v0 + c8);
-      *reinterpret_cast<uint4*>(Gs_ + r * L7 + c8) =
-          *reinterpret_cast<const uint4*>(hG + (int64_t)r * kDim + v0 + c8);
+    // S[:, half], dSn[:, half] (128 x 64) and V, dO (64 x 64), loads batched
+    {
+      TileRegs<64, 256> s0, s1, g0, g1, rv, ro;
+      tile_load<T, 64, 256>(s0, hS + v0, kDim, 64);
+      tile_load<T, 64, 256>(s1, hS + 64 * kDim + v0, kDim, 64);
+      tile_load<T, 64, 256>(g0, hG + v0, kDim, 64);
+      tile_load<T, 64, 256>(g1, hG + 64 * kDim + v0, kDim, 64);
+      tile_load<T, 64, 256>(rv, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
+      tile_load<T, 64, 256>(ro, dOg + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
+#pragma unroll
+      for (int i = 0; i < TileRegs<64, 256>::N; ++i)
+        sds += dot8<T>(s0.r[i], g0.r[i]) + dot8<T>(s1.r[i], g1.r[i]);
+      tile_store<T, 64, 256>(Ss, L7, s0);
+      tile_store<T, 64, 256>(Ss + 64 * L7, L7, s1);
+      tile_store<T, 64, 256>(Gs_, L7, g0);
+      tile_store<T, 64, 256>(Gs_ + 64 * L7, L7, g1);
+      tile_store<T, 64, 256>(Vs, L7, rv);
+      tile_store<T, 64, 256>(Os, L7, ro);
     }
-    tile_to_lds<T, 256>(Vs, L7, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc, 64);
-    tile_to_lds<T, 256>(Os, L7, dOg + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc, 64);
     __syncthreads();
 
     // ---- wave w: value columns cc .. cc+15 of this half ----
     const int cc = 16 * w;
-    f32x4 R[4], Dl[4], dD[4], dR[4];
+    f32x4 R[4], Dl[4], dD[4], dR[4], vd[4];
     {
       f32x4 ks[4], kg[4];
 #pragma unroll
@@ -483,12 +485,14 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
       }
       // R = diag(beta) V - diag(beta e^gamma) K S
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb) {
+        vd[tb] = frag_d4(Vs, L7, 16 * tb, cc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * tb + 4 * grp + e;
-          R[tb][e] = bet[r] * to_f(Vs[r * L7 + cc + col]) - bex[r] * ks[tb][e];
+          R[tb][e] = bet[r] * vd[tb][e] - bex[r] * ks[tb][e];
         }
+      }
       // Delta = A R ; dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
       const x8 Rb0 = pack_split<T>(R[0], R[1]), Rb1 = pack_split<T>(R[2], R[3]);
 #pragma unroll
@@ -516,45 +520,39 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
         dR[tb] = acc;
       }
     }
-    // dv, the v . dR part of dbeta, and the tiles for the v-contractions
-    T* dvp = reinterpret_cast<T*>(a.dv);
+    // the v . dR part of dbeta; dv into this wave's own columns of Vs (V is
+    // no longer read there); R, Delta, dDelta, dR stored transposed ([v][r])
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * tb + 4 * grp + e;
-        if (r < Cc) dvp[((t0 + r) * a.Hv + h) * kDim + v0 + cc + col] = from_f<T>(bet[r] * dR[tb][e]);
-        const float pdot = sum16(to_f(Vs[r * L7 + cc + col]) * dR[tb][e]);
+        const float pdot = sum16(vd[tb][e] * dR[tb][e]);
         if (col == 0) dbv[4 * hv + w][r] = pdot;
-        Rs[r * L7 + cc + col] = from_f<T>(R[tb][e]);
-        Dls[r * L7 + cc + col] = from_f<T>(Dl[tb][e]);
-        DDs[r * L7 + cc + col] = from_f<T>(dD[tb][e]);
-        DRs[r * L7 + cc + col] = from_f<T>(dR[tb][e]);
+        Vs[r * L7 + cc + col] = from_f<T>(bet[r] * dR[tb][e]);
       }
-    }
-    // <S, dSn> over this half: thread tid sums a fixed slice
-    {
-      float acc = 0.f;
-      for (int x = tid; x < 128 * 64; x += 256) {
-        const int r = x >> 6, cc2 = x & 63;
-        acc += to_f(Ss[r * L7 + cc2]) * to_f(Gs_[r * L7 + cc2]);
-      }
-      sds += acc;
+      store_d4_t<T>(Rs, L7, 16 * tb, cc, R[tb]);
+      store_d4_t<T>(Dls, L7, 16 * tb, cc, Dl[tb]);
+      store_d4_t<T>(DDs, L7, 16 * tb, cc, dD[tb]);
+      store_d4_t<T>(DRs, L7, 16 * tb, cc, dR[tb]);
     }
     __syncthreads();
+    // dv rows of this half: 16-byte stores of the staged tile
+    tile_from_lds<T, 64, 256>(reinterpret_cast<T*>(a.dv) + (t0 * a.Hv + h) * kDim + v0,
+                              (int64_t)a.Hv * kDim, Vs, L7, Cc);
 
     // ---- wave w: rows 16w .. 16w+15, contractions over this half's v ----
 #pragma unroll
     for (int vk = 0; vk < 2; ++vk) {
-      const x8 fdd = frag_row_split(DDs + 16 * w * L7 + 32 * vk, L7);
+      const x8 fdd = frag_tr_split(DDs + 32 * vk * L7 + 16 * w, L7);
       const x8 fdo = frag_row_split(Os + 16 * w * L7 + 32 * vk, L7);
-      const x8 fdr = frag_row_split(DRs + 16 * w * L7 + 32 * vk, L7);
-      const x8 fdl = frag_row_split(Dls + 16 * w * L7 + 32 * vk, L7);
+      const x8 fdr = frag_tr_split(DRs + 32 * vk * L7 + 16 * w, L7);
+      const x8 fdl = frag_tr_split(Dls + 32 * vk * L7 + 16 * w, L7);
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
         if (ib <= w) {
-          dA[ib] = mfma16(fdd, frag_row_split(Rs + 16 * ib * L7 + 32 * vk, L7), dA[ib]);
-          dP[ib] = mfma16(fdo, frag_row_split(Dls + 16 * ib * L7 + 32 * vk, L7), dP[ib]);
+          dA[ib] = mfma16(fdd, frag_tr_split(Rs + 32 * vk * L7 + 16 * ib, L7), dA[ib]);
+          dP[ib] = mfma16(fdo, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), dP[ib]);
         }
       }
 #pragma unroll
@@ -566,9 +564,14 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
       }
     }
   }
-  red[tid] = sds;
+  // <S, dSn>: wave sums in a fixed shuffle order, then the four wave partials
+  {
+    float x = sds;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    if (l == 0) red[w] = x;
+  }
   __syncthreads();
-
   // ---- C x C terms, rows r = 16w + 4grp + e ----
   T* dAs = Ss;              // bf16 dA (64 x 64)
   T* T1s = Ss + 64 * L7;    // bf16 A^T dA
@@ -669,11 +672,12 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   float qsd[4] = {0.f, 0.f, 0.f, 0.f}, kdx[4] = {0.f, 0.f, 0.f, 0.f}, fF[4] = {0.f, 0.f, 0.f, 0.f};
   float dqv[8][4], dkv[8][4];
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
+  for (int kb = 0; kb < 8; ++kb) {
+    const f32x4 qd = frag_d4(Qs, LD, 16 * w, 16 * kb), kd = frag_d4(Ks, LD, 16 * w, 16 * kb);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * grp + e, key = 16 * kb + col;
-      const float qv = to_f(Qs[r * LD + key]), kv = to_f(Ks[r * LD + key]);
+      const int r = 16 * w + 4 * grp + e;
+      const float qv = qd[e], kv = kd[e];
       const float dxv = -dX[kb][e];  // dX = -dR S^T
       qsd[e] += qv * dQ1[kb][e];
       kdx[e] += kv * dxv;
@@ -681,6 +685,7 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
       dqv[kb][e] = a.scale * eg[r] * dQ1[kb][e] + dQ2[kb][e];
       dkv[kb][e] = dK2[kb][e] + dl[r] * dKs[kb][e] + bex[r] * dxv;
     }
+  }
   float Fsum_part = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -705,8 +710,7 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
         float Fs = 0.f;
         for (int ww = 0; ww < 4; ++ww)
           for (int gg = 0; gg < 4; ++gg) Fs += fsum[ww][gg];
-        float ss = 0.f;
-        for (int x = 0; x < 256; ++x) ss += red[x];
+        const float ss = (red[0] + red[1]) + (red[2] + red[3]);
         dgv += Fs + __expf(gL) * ss;
       }
       dgam[r] += dgv;
@@ -716,29 +720,41 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
     }
   }
   // dq, dk rows
+  if (a.partial) {
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * grp + e, key = 16 * kb + col;
-      if (r < Cc) {
-        if (a.partial) {
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * grp + e, key = 16 * kb + col;
+        if (r < Cc) {
           reinterpret_cast<float*>(a.dq)[((t0 + r) * a.Hv + h) * kDim + key] = dqv[kb][e];
           reinterpret_cast<float*>(a.dk)[((t0 + r) * a.Hv + h) * kDim + key] = dkv[kb][e];
-        } else {
-          reinterpret_cast<T*>(a.dq)[((t0 + r) * a.Hq + hq) * kDim + key] = from_f<T>(dqv[kb][e]);
-          reinterpret_cast<T*>(a.dk)[((t0 + r) * a.Hq + hq) * kDim + key] = from_f<T>(dkv[kb][e]);
         }
       }
-    }
+  } else {
+    // staged row-major in the (now free) S / dSn tiles, then 16-byte stores
+    T* dqs = Ss;
+    T* dks = Gs_;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * grp + e, key = 16 * kb + col;
+        dqs[r * LD + key] = from_f<T>(dqv[kb][e]);
+        dks[r * LD + key] = from_f<T>(dkv[kb][e]);
+      }
+    __syncthreads();
+    tile_from_lds<T, 128, 256>(reinterpret_cast<T*>(a.dq) + (t0 * a.Hq + hq) * kDim,
+                               (int64_t)a.Hq * kDim, dqs, LD, Cc);
+    tile_from_lds<T, 128, 256>(reinterpret_cast<T*>(a.dk) + (t0 * a.Hq + hq) * kDim,
+                               (int64_t)a.Hq * kDim, dks, LD, Cc);
+  }
   __syncthreads();
-  // dg = reverse cumsum of dgamma over the valid rows (one lane, fixed order)
-  if (tid == 0) {
-    float acc = 0.f;
-    for (int r = Cc - 1; r >= 0; --r) {
-      acc += dgam[r];
-      store_scalar(a.dg, (t0 + r) * a.Hv + h, a.g_dtype, acc);
-    }
+  // dg = reverse cumsum of dgamma over the valid rows: lane l scans row 63 - l
+  if (w == 0) {
+    const int r = 63 - l;
+    const float x = wave_inclusive_scan(r < Cc ? dgam[r] : 0.f);
+    if (r < Cc) store_scalar(a.dg, (t0 + r) * a.Hv + h, a.g_dtype, x);
   }
 }
 

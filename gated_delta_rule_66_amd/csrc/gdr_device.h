@@ -117,6 +117,42 @@ __device__ __forceinline__ typename VT<T>::x8 frag_tr(const T* base, int ld) {
   return __builtin_bit_cast(typename VT<T>::x8, r);
 }
 
+// Four rows of one column in D-tile order: lane (grp, col) receives
+// X[row0 + 4 grp + e][col0 + col], e = 0..3, from a row-major LDS matrix with
+// one ds_read_b64_tr_b16 (lane j of group grp addresses row row0 + 4 grp + j/4,
+// columns col0 + 4 (j % 4) ..).
+template <typename T>
+__device__ __forceinline__ f32x4 frag_d4(const T* X, int ld, int row0, int col0) {
+  const int l = lane_id();
+  const int grp = l >> 4, j = l & 15;
+  const T* p = X + (row0 + 4 * grp + (j >> 2)) * ld + col0 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const typename VT<T>::x4 v = __builtin_bit_cast(typename VT<T>::x4, r);
+  return f32x4{to_f(v[0]), to_f(v[1]), to_f(v[2]), to_f(v[3])};
+}
+
+// Store a D tile transposed: lane (grp, col) writes its four rows as four
+// consecutive elements of row col0 + col of Xt (Xt[c][r] = X[r][c]).
+template <typename T>
+__device__ __forceinline__ void store_d4_t(T* Xt, int ld, int row0, int col0, f32x4 v) {
+  const int l = lane_id();
+  const int grp = l >> 4, col = l & 15;
+  typename VT<T>::x4 o{from_f<T>(v[0]), from_f<T>(v[1]), from_f<T>(v[2]), from_f<T>(v[3])};
+  *reinterpret_cast<typename VT<T>::x4*>(Xt + (col0 + col) * ld + row0 + 4 * grp) = o;
+}
+
+// dot product of two registers of eight packed 16-bit values, in fp32
+template <typename T>
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+  const typename VT<T>::x8 x = __builtin_bit_cast(typename VT<T>::x8, a);
+  const typename VT<T>::x8 y = __builtin_bit_cast(typename VT<T>::x8, b);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += to_f(x[e]) * to_f(y[e]);
+  return s;
+}
+
 // Two stacked fp32 D tiles (rows 0..15 and 16..31 of a 32-row block) become a
 // split-order B operand (k = the 32 rows).
 template <typename T>
@@ -207,6 +243,50 @@ __device__ __forceinline__ void store_scalar(void* p, int64_t idx, int dtype, fl
   if (dtype == 0) reinterpret_cast<__bf16*>(p)[idx] = (__bf16)v;
   else if (dtype == 1) reinterpret_cast<_Float16*>(p)[idx] = (_Float16)v;
   else reinterpret_cast<float*>(p)[idx] = v;
+}
+
+// P = lower_incl(Q K^T o exp(gamma_r - gamma_i)) for one 64-token chunk,
+// written to LDS in the input dtype.  The ten 16x16 tiles on or below the
+// diagonal are spread over the four waves (3, 3, 2, 2); the two tiles above
+// the diagonal that the triangular products read, (0,1) and (2,3), are zeroed
+// once by p_zero_tiles and never written again.
+template <typename T>
+__device__ __forceinline__ void p_tiles(const T* Qs, const T* Ks, int ldq, T* Ps, int ldp,
+                                        const float* gam, int w) {
+  const int l = lane_id(), grp = l >> 4, col = l & 15;
+  // (row block, column block) per wave and slot; -1 = no tile
+  constexpr int tab[4][3][2] = {{{0, 0}, {2, 0}, {3, 3}},
+                                {{1, 0}, {1, 1}, {3, 0}},
+                                {{2, 1}, {2, 2}, {-1, -1}},
+                                {{3, 1}, {3, 2}, {-1, -1}}};
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int rb = tab[w][t][0], cb = tab[w][t][1];
+    if (rb < 0) break;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc = mfma16(frag_row(Qs + 16 * rb * ldq + 32 * kk, ldq),
+                   frag_row(Ks + 16 * cb * ldq + 32 * kk, ldq), acc);
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
+    const float gi = gam[16 * cb + col];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rb + 4 * grp + e, i = 16 * cb + col;
+      const float pv = (rb != cb || i <= r) ? acc[e] * __expf(gr[e] - gi) : 0.f;
+      Ps[r * ldp + i] = from_f<T>(pv);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void p_zero_tiles(T* Ps, int ldp) {
+  const int tid = threadIdx.x;  // 256 threads, 2 tiles of 256 elements
+  for (int x = tid; x < 512; x += 256) {
+    const int t = x >> 8, e = x & 255;
+    const int r = 16 * (2 * t) + (e >> 4), i = 16 * (2 * t + 1) + (e & 15);
+    Ps[r * ldp + i] = from_f<T>(0.f);
+  }
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (fixed combination order).

@@ -78,8 +78,12 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
     bet[l] = (l < Cc) ? to_f(reinterpret_cast<const T*>(a.beta)[(t0 + l) * a.Hv + h]) : 0.f;
     if (l < Cc) a.gcum[(t0 + l) * a.Hv + h] = gc;
   }
-  tile_to_lds<T, 256>(Ks, LDK, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
-                      (int64_t)a.Hq * kDim, Cc, kDim);
+  {
+    TileRegs<128, 256> rk;
+    tile_load<T, 128, 256>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
+                           (int64_t)a.Hq * kDim, Cc);
+    tile_store<T, 128, 256>(Ks, LDK, rk);
+  }
   __syncthreads();
 
   // M, rows 16w .. 16w+15 (only the blocks on or below the diagonal are nonzero)
@@ -196,7 +200,10 @@ static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st)
   a.P = pl.cp;
   a.nvs = 2 / VB;
   const dim3 grid(units * pl.cp * a.nvs);
-  if (mode == MODE_OUT) GDR_LAUNCH("scan_out", (scan_kernel<T, VB, MODE_OUT>), grid, dim3(256), st, a);
+  if (mode == MODE_OUT && a.h)
+    GDR_LAUNCH("scan_out", (scan_kernel<T, VB, MODE_OUT_H>), grid, dim3(256), st, a);
+  else if (mode == MODE_OUT)
+    GDR_LAUNCH("scan_out", (scan_kernel<T, VB, MODE_OUT>), grid, dim3(256), st, a);
   else GDR_LAUNCH("scan_state", (scan_kernel<T, VB, MODE_STATE>), grid, dim3(256), st, a);
 }
 

@@ -29,7 +29,9 @@
 
 namespace gdr {
 
-enum ScanMode { MODE_OUT = 0, MODE_AUG = 1, MODE_STATE = 2 };
+// MODE_OUT: outputs; MODE_OUT_H: outputs and the chunk-start states h;
+// MODE_AUG: segment transitions; MODE_STATE: chunk-start states only.
+enum ScanMode { MODE_OUT = 0, MODE_AUG = 1, MODE_STATE = 2, MODE_OUT_H = 3 };
 
 // Chunk offsets of packed sequences, computed on the device so that no
 // device-to-host copy is needed: offs[0] = 0, offs[n+1] = offs[n] +
@@ -85,13 +87,14 @@ __device__ __forceinline__ SegRange seg_range(int nch, int P, int p) {
 }
 
 template <typename T, int VB, int MODE>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(256, (VB == 1 && MODE != MODE_OUT_H) ? 2 : 1) void scan_kernel(ScanArgs a) {
   typedef typename VT<T>::x8 x8;
   constexpr int CW = 64 * VB;          // columns per workgroup
   constexpr int LD = 136;              // q / k tile leading dimension
   constexpr int LDV = CW + 8;          // v / o tile leading dimension
   constexpr int LDA = 72;              // A / P tile leading dimension
-  constexpr bool OUT = (MODE == MODE_OUT);
+  constexpr bool OUT = (MODE == MODE_OUT || MODE == MODE_OUT_H);
+  constexpr bool HST = (MODE == MODE_STATE || MODE == MODE_OUT_H);  // stage h in LDS
   constexpr int HS_ELEMS = (128 * (CW + 8) > CW * 136) ? 128 * (CW + 8) : CW * 136;
   __shared__ __align__(16) T Ks[64 * LD];
   __shared__ __align__(16) T Qs[OUT ? 64 * LD : 8];
@@ -99,8 +102,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   __shared__ __align__(16) T Os[OUT ? 64 * LDV : 8];
   __shared__ __align__(16) T As[64 * LDA];
   __shared__ __align__(16) T Ps[OUT ? 64 * LDA : 8];
-  __shared__ __align__(16) T Hs[MODE == MODE_STATE ? HS_ELEMS : 8];
-  __shared__ float gam[64], bet[64], eg[64], bex[64], dl[64];
+  __shared__ __align__(16) T Hs[HST ? HS_ELEMS : 8];
+  __shared__ __align__(16) float gam[64], bet[64], eg[64], bex[64], dl[64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const int vs = blockIdx.x % a.nvs;
@@ -173,6 +176,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
   int64_t t_prev = 0;
   int cc_prev = 0;
+  if (OUT) p_zero_tiles<T>(Ps, LDA);
   if (sr.c0 < sr.c1) prefetch(sr.c0);
   for (int c = sr.c0; c < sr.c1; ++c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
@@ -198,9 +202,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     const float eLc = __expf(gam[63]);
     if (c + 1 < sr.c1) prefetch(c + 1);
 
-    // chunk-start state out: the backward's own copy is staged in LDS for
-    // 16-byte stores; the optional user h of the forward is written directly
-    if (MODE == MODE_STATE && a.h) {
+    // chunk-start state out, staged in LDS for 16-byte stores
+    if (HST) {
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
@@ -212,58 +215,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
             else Hs[key * (CW + 8) + lc] = from_f<T>(S[kb][vb][e]);
           }
     }
-    if (MODE == MODE_OUT && a.h) {
-      T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
-            hp[a.h_svf ? vc * kDim + key : key * kDim + vc] = from_f<T>(S[kb][vb][e]);
-          }
-    }
-
-    if (OUT) {
-      // P rows 16w .. 16w+15
-      for (int cbk = 0; cbk < 4; ++cbk) {
-        f32x4 acc = zero4();
-        if (cbk <= w) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            acc = mfma16(frag_row(Qs + 16 * w * LD + 32 * kk, LD),
-                         frag_row(Ks + 16 * cbk * LD + 32 * kk, LD), acc);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * w + 4 * grp + e, i = 16 * cbk + col;
-          float pv = 0.f;
-          if (i <= r) pv = acc[e] * __expf(gam[r] - gam[i]);
-          Ps[r * LDA + i] = from_f<T>(pv);
-        }
-      }
-    }
-    if (OUT || (MODE == MODE_STATE && a.h)) __syncthreads();
-    if (MODE == MODE_STATE && a.h) {
-      T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
-      if (a.h_svf) {
-        // rows = local value columns, 128 keys each
-        for (int x = tid; x < CW * 16; x += 256) {
-          const int r = x >> 4, c8 = (x & 15) * 8;
-          *reinterpret_cast<uint4*>(hp + (int64_t)(cb0 + r) * kDim + c8) =
-              *reinterpret_cast<const uint4*>(Hs + r * 136 + c8);
-        }
-      } else {
-        constexpr int PR = CW / 8;
-        for (int x = tid; x < 128 * PR; x += 256) {
-          const int r = x / PR, c8 = (x % PR) * 8;
-          *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
-              *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
-        }
-      }
-    }
-
+    if (OUT) p_tiles<T>(Qs, Ks, LD, Ps, LDA, gam, w);
     // K S (and Q S)
     x8 Sb[4][VB];
 #pragma unroll
@@ -322,6 +274,26 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         dd[tb][vb] = acc;
       }
     }
+    if (OUT || HST) __syncthreads();
+    if (HST) {
+      T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
+      if (a.h_svf) {
+        // rows = local value columns, 128 keys each
+        for (int x = tid; x < CW * 16; x += 256) {
+          const int r = x >> 4, c8 = (x & 15) * 8;
+          *reinterpret_cast<uint4*>(hp + (int64_t)(cb0 + r) * kDim + c8) =
+              *reinterpret_cast<const uint4*>(Hs + r * 136 + c8);
+        }
+      } else {
+        constexpr int PR = CW / 8;
+        for (int x = tid; x < 128 * PR; x += 256) {
+          const int r = x / PR, c8 = (x % PR) * 8;
+          *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
+              *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
+        }
+      }
+    }
+
     if (OUT) {
       x8 Db[2][VB];
 #pragma unroll
