@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cp", type=int, default=0,
                     help="context-parallel segments per sequence (0 = the library's plan)")
+    ap.add_argument("--vt", type=int, default=0,
+                    help="16-column state tiles per wave in the scans (0 = the library's plan)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path runs on a single MI355X and this build "
@@ -184,21 +186,22 @@ def main():
     dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
     cu_cpu = d["cu_seqlens"]
     cp, wave_tiles = gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
-                                   cu_seqlens_cpu=cu_cpu, cp_segments=args.cp)
+                                   cu_seqlens_cpu=cu_cpu, cp_segments=args.cp,
+                                   wave_tiles=args.vt)
 
     def fwd():
         return gdr.chunk_gated_delta_rule_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"],
                                               scale=dd["scale"], initial_state=dd["h0"],
                                               output_final_state=True,
                                               cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=cu_cpu,
-                                              cp_segments=args.cp)
+                                              cp_segments=args.cp, wave_tiles=args.vt)
 
     def bwd(g_cum, A):
         return gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
                                               dd["do"], dht=dd["dht"], scale=dd["scale"],
                                               initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
                                               dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu,
-                                              cp_segments=args.cp)
+                                              cp_segments=args.cp, wave_tiles=args.vt)
 
     def step():
         g_cum, A, o, _, ht = fwd()

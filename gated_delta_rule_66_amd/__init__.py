@@ -47,7 +47,7 @@ class _Call:
     """Problem descriptor plus the host copy of cu_seqlens it points to."""
 
     def __init__(self, q, v, g_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first,
-                 cp_segments):
+                 cp_segments, wave_tiles=0):
         B, T, Hq, K = q.shape
         Hv, V = v.shape[2], v.shape[3]
         self.cu_host = None
@@ -66,7 +66,8 @@ class _Call:
                          cu_seqlens_dev=None if self.cu_dev is None else self.cu_dev.data_ptr(),
                          cu_seqlens_host=None if self.cu_host is None else self.cu_host.data_ptr(),
                          in_dtype=_code(q.dtype), g_dtype=_code(g_dtype), scale=float(scale),
-                         state_v_first=1 if state_v_first else 0, cp_segments=int(cp_segments))
+                         state_v_first=1 if state_v_first else 0, cp_segments=int(cp_segments),
+                         wave_tiles=int(wave_tiles))
         self.N, self.Hv, self.K, self.V = N, Hv, K, V
         self.ref = ctypes.byref(self.p)
         reason = ctypes.create_string_buffer(256)
@@ -91,13 +92,15 @@ def _contig(*ts):
 
 def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                output_final_state=True, cu_seqlens=None, state_v_first=False,
-                               output_h=False, cp_segments=0, cu_seqlens_cpu=None):
+                               output_h=False, cp_segments=0, cu_seqlens_cpu=None,
+                               wave_tiles=0):
     """Forward.  Returns ``(g_cum, A, o, h, final_state)``: the chunk-local
     cumsum of g (fp32), the per-chunk inverse A ``[B,T,Hv,64]``, the output,
     the chunk-start states (``None`` unless ``output_h``) and the fp32 final
     state (``None`` unless ``output_final_state``)."""
     q, k, v, g, beta, initial_state = _contig(q, k, v, g, beta, initial_state)
-    c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments)
+    c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
+              wave_tiles)
     dev = q.device
     B, T = q.shape[0], q.shape[1]
     g_cum = torch.empty(B, T, c.Hv, dtype=torch.float32, device=dev)
@@ -121,7 +124,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
 
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=None,
                                cu_seqlens=None, state_v_first=False, dg_dtype=None,
-                               cp_segments=0, cu_seqlens_cpu=None):
+                               cp_segments=0, cu_seqlens_cpu=None, wave_tiles=0):
     """Backward.  ``g`` is the forward's fp32 ``g_cum`` output.  Returns
     ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is the gradient with respect to
     the raw log-decay g (dtype ``dg_dtype``, default the input dtype) and
@@ -131,7 +134,8 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     if g.dtype != torch.float32:
         raise GdrError(4, "the backward takes the forward's fp32 g_cum as g")
     dg_dtype = q.dtype if dg_dtype is None else dg_dtype
-    c = _Call(q, v, dg_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments)
+    c = _Call(q, v, dg_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
+              wave_tiles)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -236,10 +240,11 @@ def prepare_chunk_offsets(cu_seqlens: torch.Tensor, chunk_size: int):
 
 # ---- diagnostics --------------------------------------------------------------
 
-def plan_info(q, v, g_dtype=None, cu_seqlens=None, cu_seqlens_cpu=None, cp_segments=0):
+def plan_info(q, v, g_dtype=None, cu_seqlens=None, cu_seqlens_cpu=None, cp_segments=0,
+              wave_tiles=0):
     """``(cp_segments, wave_tiles)`` the library plans for these shapes."""
     c = _Call(q, v, q.dtype if g_dtype is None else g_dtype, None, cu_seqlens, cu_seqlens_cpu,
-              False, cp_segments)
+              False, cp_segments, wave_tiles)
     cp = ctypes.c_int32(0)
     vt = ctypes.c_int32(0)
     check(lib.gdr_plan_info(c.ref, ctypes.byref(cp), ctypes.byref(vt)))

@@ -28,6 +28,7 @@ class Problem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("state_v_first", ctypes.c_int32),
         ("cp_segments", ctypes.c_int32),
+        ("wave_tiles", ctypes.c_int32),
     ]
 
 

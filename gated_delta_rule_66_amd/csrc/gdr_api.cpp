@@ -64,18 +64,28 @@ static gdr_status fail(gdr_status s, char* reason, size_t len, const char* fmt, 
   return s;
 }
 
-// Estimated critical path (in units of one output-scan chunk step) of the
-// forward scan for a plan with P segments and VB column tiles per wave,
-// assuming one workgroup per CU on 256 CUs.
+// Estimated time of the forward + backward scans for a plan with P segments
+// and VB column tiles per wave, in units of one output-scan chunk step of a
+// workgroup alone on its CU.  Calibrated on MI355X (256 CUs): a CU holds two
+// VB=1 workgroups (each then takes ~1.46x longer per chunk) or one VB=2
+// workgroup (1.5x the VB=1 chunk time for twice the columns); relative chunk
+// costs: output scan 1, state scan 0.6, state-gradient scan 0.85, forward
+// transition pass 0.75, backward transition pass 1.3, one combine step 2.
+static double pass_cost(int64_t wgs, int64_t chunks, double rel, int VB) {
+  const int64_t slots = (VB == 1) ? 512 : 256;
+  double f = (VB == 1) ? 1.0 : 1.5;
+  if (VB == 1 && wgs > 256) f *= 1.46;
+  const double rounds = (double)((wgs + slots - 1) / slots);
+  return (double)chunks * rel * f * (rounds < 1.0 ? 1.0 : rounds);
+}
+
 static double plan_cost(int64_t units, int64_t maxch, int P, int VB) {
-  const double c_out = (VB == 2) ? 1.6 : 1.0;  // output scan, per chunk
-  const double c_st = (VB == 2) ? 1.0 : 0.6;   // transition scan, per chunk
   const int64_t nvs0 = 2 / VB, nvs1 = 4 / VB;
-  auto rounds = [](int64_t wg) { return (double)((wg + 255) / 256); };
-  if (P == 1) return rounds(units * nvs0) * (double)maxch * c_out;
+  if (P == 1) return pass_cost(units * nvs0, maxch, 1.0 + 0.6 + 0.85, VB);
   const int64_t sc = (maxch + P - 1) / P;
-  const int64_t wg1 = units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
-  return rounds(wg1) * sc * c_st + rounds(units * P * nvs0) * sc * c_out + 0.5 * (P - 1);
+  const int64_t wg_aug = units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);  // B part only for one end
+  return 2.0 * pass_cost(wg_aug, sc, 0.75, VB) + pass_cost(wg_aug, sc, 1.3, VB) +
+         pass_cost(units * P * nvs0, sc, 1.0 + 0.6 + 0.85, VB) + 3.0 * 2.0 * (P - 1);
 }
 
 // Context-parallel plan along T: it depends only on shapes (never on data),
@@ -107,6 +117,7 @@ Plan make_plan(const gdr_problem* p) {
     if (fixed > 0 && P != fixed) continue;
     if (fixed == 0 && P > 1 && maxch < 8 * P) continue;
     for (int VB = 1; VB <= 2; ++VB) {
+      if (p->wave_tiles > 0 && VB != p->wave_tiles) continue;
       const double c = plan_cost(units, maxch, P, VB);
       if (c < best) {
         best = c;
@@ -117,7 +128,7 @@ Plan make_plan(const gdr_problem* p) {
   }
   if (fixed > 0 && best == 1e300) {  // a segment count that is not a power of two
     pl.cp = fixed;
-    pl.vb = 1;
+    pl.vb = p->wave_tiles > 0 ? p->wave_tiles : 1;
   }
   if (pl.cp > maxch) pl.cp = maxch > 0 ? (int)maxch : 1;
   return pl;
@@ -147,6 +158,8 @@ static gdr_status validate(const gdr_problem* p, char* reason, size_t len) {
   if (p->state_v_first != 0 && p->state_v_first != 1)
     return fail(GDR_ERR_ARG, reason, len, "state_v_first must be 0 or 1");
   if (p->cp_segments < 0) return fail(GDR_ERR_ARG, reason, len, "cp_segments must be >= 0");
+  if (p->wave_tiles < 0 || p->wave_tiles > 2)
+    return fail(GDR_ERR_ARG, reason, len, "wave_tiles must be 0, 1 or 2");
   const bool has_dev = p->cu_seqlens_dev != nullptr, has_host = p->cu_seqlens_host != nullptr;
   if (has_dev != has_host)
     return fail(GDR_ERR_VARLEN, reason, len,

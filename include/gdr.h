@@ -91,6 +91,8 @@ typedef struct {
   int32_t cp_segments;            /* intra-GPU context parallelism along T:
                                      0 = automatic plan, 1 = off, s > 1 = split
                                      every sequence into up to s segments */
+  int32_t wave_tiles;             /* 16-column state tiles per wave in the scans:
+                                     0 = automatic, 1 or 2 */
 } gdr_problem;
 
 /* Status name ("GDR_ERR_SHAPE", ...). */
