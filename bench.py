@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cp", type=int, default=0,
                     help="context-parallel segments per sequence (0 = the library's plan)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 256 MiB device copy first (counter calibration)")
     ap.add_argument("--vt", type=int, default=0,
                     help="16-column state tiles per wave in the scans (0 = the library's plan)")
     args = ap.parse_args()
@@ -207,6 +209,15 @@ def main():
         g_cum, A, o, _, ht = fwd()
         return bwd(g_cum, A)
 
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        flush = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(2.0)  # 1 GiB
+        torch.cuda.synchronize()
+        del flush
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -86,8 +86,9 @@ __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a)
   __shared__ __align__(16) float gam[64], eg[64], bex[64], dl[64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
-  const int vs = blockIdx.x % a.nvs;
-  const int up = blockIdx.x / a.nvs;
+  const int bid = xcd_block(blockIdx.x, gridDim.x);
+  const int vs = bid % a.nvs;
+  const int up = bid / a.nvs;
   const int p = up % a.P, unit = up / a.P;
   const int n = unit / a.Hv, h = unit % a.Hv;
   const int G = a.Hv / a.Hq, hq = h / G;

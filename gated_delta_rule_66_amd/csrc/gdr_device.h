@@ -300,6 +300,16 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return x;
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
+// Renumber blocks so that consecutive logical blocks -- the column blocks and
+// segments of one (sequence, head) that read the same q, k, A tiles -- run on
+// the same XCD and share its L2.  Identity when the grid is not a multiple
+// of 8.
+__device__ __forceinline__ int xcd_block(int b, int nblocks) {
+  if (nblocks & 7) return b;
+  return (b & 7) * (nblocks >> 3) + (b >> 3);
+}
+
 // Where a (sequence, chunk) pair starts.  Dense batches: sequence n spans
 // tokens [n*T, n*T + T).  Packed input: cu_seqlens.
 struct SeqInfo {
