@@ -192,17 +192,44 @@ struct TileRegs {
   uint4 r[N];
 };
 
+// Raw buffer resource over the bytes [base, base + bytes).  Raw buffer
+// instructions check each access against that range: a load past the end
+// returns zero and a store past the end is dropped, so the ragged last chunk
+// of a sequence needs no per-row branches.  Offsets are 32-bit byte offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t rs, int off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, rs, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t rs, int off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+}
+
+// Rows [0, rows) of the tile load; rows past that read as zero.  Row r of the
+// tile starts r * gstride elements after g (gstride >= COLS).
 template <typename T, int COLS, int NT>
 __device__ __forceinline__ void tile_load(TileRegs<COLS, NT>& t, const T* g, int64_t gstride,
                                           int rows) {
   constexpr int PR = TileRegs<COLS, NT>::PER_ROW;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(g, (int64_t)rows * gstride * (int64_t)sizeof(T));
+  const int gs = (int)gstride * (int)sizeof(T);
 #pragma unroll
   for (int i = 0; i < TileRegs<COLS, NT>::N; ++i) {
     const int x = threadIdx.x + i * NT;
     const int r = x / PR, c8 = (x % PR) * 8;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < rows) val = *reinterpret_cast<const uint4*>(g + r * gstride + c8);
-    t.r[i] = val;
+    t.r[i] = buf_load16(rs, r * gs + c8 * (int)sizeof(T));
   }
 }
 
@@ -217,18 +244,19 @@ __device__ __forceinline__ void tile_store(T* lds, int ld, const TileRegs<COLS, 
   }
 }
 
-// LDS tile rows [0, rows) -> global, 16 bytes per store.
+// LDS tile rows [0, rows) -> global, 16 bytes per store (stores of rows past
+// `rows` fall outside the buffer range and are dropped).
 template <typename T, int COLS, int NT>
 __device__ __forceinline__ void tile_from_lds(T* g, int64_t gstride, const T* lds, int ld,
                                               int rows) {
   constexpr int PR = COLS / 8;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(g, (int64_t)rows * gstride * (int64_t)sizeof(T));
+  const int gs = (int)gstride * (int)sizeof(T);
 #pragma unroll
   for (int i = 0; i < (64 * PR) / NT; ++i) {
     const int x = threadIdx.x + i * NT;
     const int r = x / PR, c8 = (x % PR) * 8;
-    if (r < rows)
-      *reinterpret_cast<uint4*>(g + r * gstride + c8) =
-          *reinterpret_cast<const uint4*>(lds + r * ld + c8);
+    buf_store16(rs, r * gs + c8 * (int)sizeof(T), *reinterpret_cast<const uint4*>(lds + r * ld + c8));
   }
 }
 

@@ -86,22 +86,24 @@ __device__ __forceinline__ SegRange seg_range(int nch, int P, int p) {
   return r;
 }
 
+// Index of the upper-triangular tile (ib, rb), ib <= rb, of P^T in a packed
+// list of ten tiles.
+__host__ __device__ constexpr int tri_idx(int ib, int rb) { return rb * (rb + 1) / 2 + ib; }
+
 template <typename T, int VB, int MODE>
-__global__ __launch_bounds__(256, (VB == 1 && MODE != MODE_OUT_H) ? 2 : 1) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_STATE)) ? 2 : 1) void scan_kernel(ScanArgs a) {
   typedef typename VT<T>::x8 x8;
   constexpr int CW = 64 * VB;          // columns per workgroup
   constexpr int LD = 136;              // q / k tile leading dimension
-  constexpr int LDV = CW + 8;          // v / o tile leading dimension
-  constexpr int LDA = 72;              // A / P tile leading dimension
+  constexpr int LDV = CW + 8;          // v tile leading dimension
+  constexpr int LDA = 72;              // A tile leading dimension
   constexpr bool OUT = (MODE == MODE_OUT || MODE == MODE_OUT_H);
   constexpr bool HST = (MODE == MODE_STATE || MODE == MODE_OUT_H);  // stage h in LDS
   constexpr int HS_ELEMS = (128 * (CW + 8) > CW * 136) ? 128 * (CW + 8) : CW * 136;
   __shared__ __align__(16) T Ks[64 * LD];
   __shared__ __align__(16) T Qs[OUT ? 64 * LD : 8];
   __shared__ __align__(16) T Vs[64 * LDV];
-  __shared__ __align__(16) T Os[OUT ? 64 * LDV : 8];
   __shared__ __align__(16) T As[64 * LDA];
-  __shared__ __align__(16) T Ps[OUT ? 64 * LDA : 8];
   __shared__ __align__(16) T Hs[HST ? HS_ELEMS : 8];
   __shared__ __align__(16) float gam[64], bet[64], eg[64], bex[64], dl[64];
 
@@ -175,17 +177,11 @@ __global__ __launch_bounds__(256, (VB == 1 && MODE != MODE_OUT_H) ? 2 : 1) void 
     }
   };
 
-  int64_t t_prev = 0;
-  int cc_prev = 0;
-  if (OUT) p_zero_tiles<T>(Ps, LDA);
   if (sr.c0 < sr.c1) prefetch(sr.c0);
   for (int c = sr.c0; c < sr.c1; ++c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
     __syncthreads();  // the previous chunk is done with LDS
-    if (OUT && c > sr.c0)
-      tile_from_lds<T, CW, 256>(reinterpret_cast<T*>(a.o) + (t_prev * a.Hv + h) * kDim + cb0,
-                                (int64_t)a.Hv * kDim, Os, LDV, cc_prev);
     if (OUT) tile_store<T, 128, 256>(Qs, LD, rq);
     tile_store<T, 128, 256>(Ks, LD, rk);
     if (!isT) tile_store<T, CW, 256>(Vs, LDV, rv);
@@ -201,7 +197,10 @@ __global__ __launch_bounds__(256, (VB == 1 && MODE != MODE_OUT_H) ? 2 : 1) void 
     }
     __syncthreads();
     const float eLc = __expf(gam[63]);
-    if (c + 1 < sr.c1) prefetch(c + 1);
+    // Output chunks have the longest per-chunk path: their next-chunk loads are
+    // issued after the key pass (below) so their registers do not overlap the
+    // P^T and (Q S)^T accumulators.
+    if (!OUT && c + 1 < sr.c1) prefetch(c + 1);
 
     // chunk-start state out, staged in LDS for 16-byte stores
     if (HST) {
@@ -216,46 +215,86 @@ __global__ __launch_bounds__(256, (VB == 1 && MODE != MODE_OUT_H) ? 2 : 1) void 
             else Hs[key * (CW + 8) + lc] = from_f<T>(S[kb][vb][e]);
           }
     }
-    if (OUT) p_tiles<T>(Qs, Ks, LD, Ps, LDA, gam, w);
-    // K S (and Q S)
+
+    // One pass over the key dimension forms, from the same K and Q fragments:
+    //   K S            (B operand: S, register-local)
+    //   (Q S)^T = S^T Q^T   (A operand: the same S registers; B: Q fragments)
+    //   P^T = K Q^T    (upper-triangular 16x16 tiles (ib <= rb), in registers)
     x8 Sb[4][VB];
 #pragma unroll
     for (int kb2 = 0; kb2 < 4; ++kb2)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) Sb[kb2][vb] = pack_split<T>(S[2 * kb2][vb], S[2 * kb2 + 1][vb]);
-    f32x4 ks[4][VB], qs[4][VB];
+    f32x4 ks[4][VB], qsT[VB][4], pT[10];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         ks[tb][vb] = zero4();
-        qs[tb][vb] = zero4();
+        qsT[vb][tb] = zero4();
       }
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int x = 0; x < 10; ++x) pT[x] = zero4();
+    // The scheduling barrier closes each key block: hoisting the next block's
+    // fragment reads above it would spill at two workgroups per CU.
 #pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const x8 fk = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      x8 fk[4], fq[4];
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb) ks[tb][vb] = mfma16(fk, Sb[kb2][vb], ks[tb][vb]);
-        if (OUT) {
-          const x8 fq = frag_row_split(Qs + 16 * tb * LD + 32 * kb2, LD);
+      for (int tb = 0; tb < 4; ++tb) fk[tb] = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
+      if (OUT) {
 #pragma unroll
-          for (int vb = 0; vb < VB; ++vb) qs[tb][vb] = mfma16(fq, Sb[kb2][vb], qs[tb][vb]);
+        for (int tb = 0; tb < 4; ++tb) fq[tb] = frag_row_split(Qs + 16 * tb * LD + 32 * kb2, LD);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) ks[tb][vb] = mfma16(fk[tb], Sb[kb2][vb], ks[tb][vb]);
+      if (OUT) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb) qsT[vb][rb] = mfma16(Sb[kb2][vb], fq[rb], qsT[vb][rb]);
+#pragma unroll
+          for (int ib = 0; ib <= rb; ++ib) pT[tri_idx(ib, rb)] = mfma16(fk[ib], fq[rb], pT[tri_idx(ib, rb)]);
         }
       }
-    // R = diag(beta) V - diag(beta e^gamma) K S
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + 4 * grp + e, lc = cw0 + 16 * vb + col;
-          const float vv = isT ? 0.f : bet[r] * to_f(Vs[r * LDV + lc]);
-          ks[tb][vb][e] = vv - bex[r] * ks[tb][vb][e];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (OUT && c + 1 < sr.c1) prefetch(c + 1);
+    if (HST) {
+      __syncthreads();  // every wave's part of the staged state is in Hs
+      T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
+      if (a.h_svf) {
+        // rows = local value columns, 128 keys each
+        for (int x = tid; x < CW * 16; x += 256) {
+          const int r = x >> 4, c8 = (x & 15) * 8;
+          *reinterpret_cast<uint4*>(hp + (int64_t)(cb0 + r) * kDim + c8) =
+              *reinterpret_cast<const uint4*>(Hs + r * 136 + c8);
         }
-    // Delta = A R
+      } else {
+        constexpr int PR = CW / 8;
+        for (int x = tid; x < 128 * PR; x += 256) {
+          const int r = x / PR, c8 = (x % PR) * 8;
+          *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
+              *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
+        }
+      }
+    }
+
+    // R = diag(beta) V - diag(beta e^gamma) K S   (in place in ks)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(bet + 16 * tb + 4 * grp);
+      const f32x4 bx = *reinterpret_cast<const f32x4*>(bex + 16 * tb + 4 * grp);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        const f32x4 vd = isT ? zero4() : frag_d4(Vs, LDV, 16 * tb, cw0 + 16 * vb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ks[tb][vb][e] = bt[e] * vd[e] - bx[e] * ks[tb][vb][e];
+      }
+    }
+    // Delta = A R (A lower triangular: token block kb <= tb / 2)
     x8 Rb[2][VB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -275,64 +314,66 @@ __global__ __launch_bounds__(256, (VB == 1 && MODE != MODE_OUT_H) ? 2 : 1) void 
         dd[tb][vb] = acc;
       }
     }
-    if (OUT || HST) __syncthreads();
-    if (HST) {
-      T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
-      if (a.h_svf) {
-        // rows = local value columns, 128 keys each
-        for (int x = tid; x < CW * 16; x += 256) {
-          const int r = x >> 4, c8 = (x & 15) * 8;
-          *reinterpret_cast<uint4*>(hp + (int64_t)(cb0 + r) * kDim + c8) =
-              *reinterpret_cast<const uint4*>(Hs + r * 136 + c8);
-        }
-      } else {
-        constexpr int PR = CW / 8;
-        for (int x = tid; x < 128 * PR; x += 256) {
-          const int r = x / PR, c8 = (x % PR) * 8;
-          *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
-              *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
+    if (OUT) {
+      // P^T[i][r] = (k_i . q_r) e^{gamma_r - gamma_i} for i <= r: tile (ib, rb)
+      // holds rows i = 16 ib + 4 grp + e, column r = 16 rb + col
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const float gr = gam[16 * rb + col];
+#pragma unroll
+        for (int ib = 0; ib <= rb; ++ib) {
+          const f32x4 gi = *reinterpret_cast<const f32x4*>(gam + 16 * ib + 4 * grp);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // masked entries take exp(-inf) = 0: a select on the argument keeps
+            // the exponential unconditional (a conditional one becomes a branch)
+            const bool keep = (ib < rb) || (4 * grp + e <= col);
+            pT[tri_idx(ib, rb)][e] *= __expf(keep ? gr - gi[e] : -INFINITY);
+          }
         }
       }
-    }
-
-    if (OUT) {
+      // O^T = diag-columns(e^gamma) (Q S)^T + Delta^T P^T; the A operand Delta^T
+      // is the Delta accumulators themselves
       x8 Db[2][VB];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) Db[kb][vb] = pack_split<T>(dd[2 * kb][vb], dd[2 * kb + 1][vb]);
+      const int ors_ld = a.Hv * kDim * (int)sizeof(T);
+      const __amdgpu_buffer_rsrc_t ors =
+          buf_rsrc(reinterpret_cast<T*>(a.o) + (t0 * a.Hv + h) * kDim + vcol0, (int64_t)Cc * ors_ld);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        x8 fp[2];
+      for (int rb = 0; rb < 4; ++rb) {
+        const float er = eg[16 * rb + col];
+        x8 pb[2];
 #pragma unroll
-        for (int kb = 0; kb <= tb / 2; ++kb) fp[kb] = frag_row_split(Ps + 16 * tb * LDA + 32 * kb, LDA);
+        for (int kb = 0; kb <= rb / 2; ++kb)
+          pb[kb] = pack_split<T>(pT[tri_idx(2 * kb, rb)],
+                                 (2 * kb + 1 <= rb) ? pT[tri_idx(2 * kb + 1 < 4 ? 2 * kb + 1 : 3, rb)] : zero4());
+        const int r = 16 * rb + col;
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) {
-          f32x4 acc = zero4();
+          f32x4 acc = qsT[vb][rb] * er;
 #pragma unroll
-          for (int kb = 0; kb <= tb / 2; ++kb) acc = mfma16(fp[kb], Db[kb][vb], acc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * tb + 4 * grp + e, lc = cw0 + 16 * vb + col;
-            Os[r * LDV + lc] = from_f<T>(a.scale * (eg[r] * qs[tb][vb][e] + acc[e]));
-          }
+          for (int kb = 0; kb <= rb / 2; ++kb) acc = mfma16(Db[kb][vb], pb[kb], acc);
+          acc *= a.scale;
+          const typename VT<T>::x4 ov{from_f<T>(acc[0]), from_f<T>(acc[1]), from_f<T>(acc[2]),
+                                      from_f<T>(acc[3])};
+          // rows past the chunk's end fall outside the buffer range: dropped
+          buf_store8(ors, r * ors_ld + (cw0 + 16 * vb + 4 * grp) * (int)sizeof(T),
+                     __builtin_bit_cast(u32x2, ov));
         }
       }
     }
     // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) Delta
     x8 Eb[2][VB];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dl + 32 * kt + 4 * grp);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(dl + 32 * kt + 16 + 4 * grp);
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        f32x4 top = dd[2 * kt][vb], bot = dd[2 * kt + 1][vb];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          top[e] *= dl[32 * kt + 4 * grp + e];
-          bot[e] *= dl[32 * kt + 16 + 4 * grp + e];
-        }
-        Eb[kt][vb] = pack_split<T>(top, bot);
-      }
+      for (int vb = 0; vb < VB; ++vb) Eb[kt][vb] = pack_split<T>(dd[2 * kt][vb] * d0, dd[2 * kt + 1][vb] * d1);
+    }
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
       x8 fk[2];
@@ -346,15 +387,8 @@ __global__ __launch_bounds__(256, (VB == 1 && MODE != MODE_OUT_H) ? 2 : 1) void 
         S[kb][vb] = acc;
       }
     }
-    t_prev = t0;
-    cc_prev = Cc;
   }
 
-  if (OUT && sr.c1 > sr.c0) {
-    __syncthreads();
-    tile_from_lds<T, CW, 256>(reinterpret_cast<T*>(a.o) + (t_prev * a.Hv + h) * kDim + cb0,
-                              (int64_t)a.Hv * kDim, Os, LDV, cc_prev);
-  }
   if (MODE == MODE_AUG) {
     float* so = a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
 #pragma unroll
