@@ -31,21 +31,6 @@
 
 namespace gdr {
 
-// sum over the 16 lanes of a lane group (same grp)
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
-  return v;
-}
-// sum over the 4 lane groups (same col)
-__device__ __forceinline__ float sum4g(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
 // ---------------------------------------------------------------------------
 // B2: reverse recurrence of the state gradient
 // ---------------------------------------------------------------------------
@@ -567,9 +552,7 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   }
   // <S, dSn>: wave sums in a fixed shuffle order, then the four wave partials
   {
-    float x = sds;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    const float x = sum4g(sum16(sds));
     if (l == 0) red[w] = x;
   }
   __syncthreads();

@@ -318,6 +318,37 @@ __device__ __forceinline__ void p_zero_tiles(T* Ps, int ldp) {
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (fixed combination order).
+// ---- cross-lane sums on the VALU (no LDS round trips) ----------------------
+// DPP moves within rows of 16 lanes: quad_perm [1,0,3,2] (0xB1) and
+// [2,3,0,1] (0x4E), row_half_mirror (0x141), row_mirror (0x140).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a lane group (lanes with the same l / 16).  Each
+// step adds a lane to its mirror partner, so all 16 lanes end with the
+// bitwise-identical sum.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
+// Sum over the 4 lane groups (lanes with the same l % 16): the gfx950 row
+// swaps exchange 16-lane rows (then 32-lane halves) between two registers,
+// and the sum of the swapped pair is lane l's value plus its partner's.
+__device__ __forceinline__ float sum4g(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = __builtin_bit_cast(float, (int)p16[0]) + __builtin_bit_cast(float, (int)p16[1]);
+  const int y = __builtin_bit_cast(int, v);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __builtin_bit_cast(float, (int)p32[0]) + __builtin_bit_cast(float, (int)p32[1]);
+}
+
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   const int l = lane_id();
 #pragma unroll
