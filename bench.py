@@ -67,6 +67,12 @@ def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True,
         return TH * (512 * r + 256 + 128 + 4 + isz) + NCH * ch + U * st * (int(with_dht) + int(with_h0))
     if name == "dh_scan_aug":
         return frac * TH * (512 * r + 256 + 128 + 4 + isz) + U * (cp - 1) * 2 * st
+    if name == "bwd_scans":  # the state scan and the state-gradient scan in one launch
+        return (kernel_bytes("scan_state", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht) +
+                kernel_bytes("dh_scan_out", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht))
+    if name == "bwd_scan_aug":
+        return (kernel_bytes("scan_aug", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht) +
+                kernel_bytes("dh_scan_aug", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht))
     if name == "cp_combine":
         return U * max(cp - 1, 0) * 3 * st
     if name == "grad":
@@ -187,9 +193,10 @@ def main():
     dev = torch.device("cuda", 0)
     dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
     cu_cpu = d["cu_seqlens"]
-    cp, wave_tiles = gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
-                                   cu_seqlens_cpu=cu_cpu, cp_segments=args.cp,
-                                   wave_tiles=args.vt)
+    plans = {d_: gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
+                               cu_seqlens_cpu=cu_cpu, cp_segments=args.cp, wave_tiles=args.vt,
+                               backward=(d_ == "bwd"))
+             for d_ in ("fwd", "bwd")}
 
     def fwd():
         return gdr.chunk_gated_delta_rule_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"],
@@ -263,7 +270,8 @@ def main():
                             "share": round(tot / max(sum(v[0] for v in kernels.values()), 1e-9), 4)}
     dom = max(kernels, key=lambda n: kernels[n][0])
     avg_s = kernels[dom][0] / kernels[dom][1] * 1e-3
-    nbytes = kernel_bytes(dom, B, T, Hq, Hv, nchunks, N, cp)
+    dom_cp = plans["bwd" if dom.startswith(("bwd", "grad", "gva")) else "fwd"][0]
+    nbytes = kernel_bytes(dom, B, T, Hq, Hv, nchunks, N, dom_cp)
     achieved = nbytes / avg_s / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -284,8 +292,10 @@ def main():
         "dtype": dt,
         "data": "synthetic (seeded; q,k L2-normalised, g=logsigmoid, beta=sigmoid)",
         "config": {"workload": args.workload, "B": B, "T": T, "Hq": Hq, "Hv": Hv, "K": 128,
-                   "V": 128, "chunk": 64, "tokens": tokens, "cp_segments": cp,
-                   "wave_tiles": wave_tiles, "parallelism": "single GPU"},
+                   "V": 128, "chunk": 64, "tokens": tokens,
+                   "cp_segments": {k_: v_[0] for k_, v_ in plans.items()},
+                   "wave_tiles": {k_: v_[1] for k_, v_ in plans.items()},
+                   "parallelism": "single GPU"},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "tflops": round(tflops, 3),

@@ -241,13 +241,14 @@ def prepare_chunk_offsets(cu_seqlens: torch.Tensor, chunk_size: int):
 # ---- diagnostics --------------------------------------------------------------
 
 def plan_info(q, v, g_dtype=None, cu_seqlens=None, cu_seqlens_cpu=None, cp_segments=0,
-              wave_tiles=0):
-    """``(cp_segments, wave_tiles)`` the library plans for these shapes."""
+              wave_tiles=0, backward=False):
+    """``(cp_segments, wave_tiles)`` the library plans for these shapes, for the
+    forward pass or (``backward=True``) the backward pass."""
     c = _Call(q, v, q.dtype if g_dtype is None else g_dtype, None, cu_seqlens, cu_seqlens_cpu,
               False, cp_segments, wave_tiles)
     cp = ctypes.c_int32(0)
     vt = ctypes.c_int32(0)
-    check(lib.gdr_plan_info(c.ref, ctypes.byref(cp), ctypes.byref(vt)))
+    check(lib.gdr_plan_info(c.ref, 1 if backward else 0, ctypes.byref(cp), ctypes.byref(vt)))
     return int(cp.value), int(vt.value)
 
 

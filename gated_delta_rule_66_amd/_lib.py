@@ -89,8 +89,8 @@ def _declare_profile(lib):
     lib.gdr_profile_read.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_int]
     lib.gdr_profile_read.restype = ctypes.c_int
-    lib.gdr_plan_info.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int32),
-                                  ctypes.POINTER(ctypes.c_int32)]
+    lib.gdr_plan_info.argtypes = [ctypes.POINTER(Problem), ctypes.c_int,
+                                  ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.gdr_plan_info.restype = ctypes.c_int
 
 

@@ -64,33 +64,37 @@ static gdr_status fail(gdr_status s, char* reason, size_t len, const char* fmt, 
   return s;
 }
 
-// Estimated time of the forward + backward scans for a plan with P segments
-// and VB column tiles per wave, in units of one output-scan chunk step of a
-// workgroup alone on its CU.  Calibrated on MI355X (256 CUs): a CU holds two
-// VB=1 workgroups (each then takes ~1.46x longer per chunk) or one VB=2
-// workgroup (1.5x the VB=1 chunk time for twice the columns); relative chunk
-// costs: output scan 1, state scan 0.6, state-gradient scan 0.85, forward
-// transition pass 0.75, backward transition pass 1.3, one combine step 2.
-static double pass_cost(int64_t wgs, int64_t chunks, double rel, int VB) {
-  const int64_t slots = (VB == 1) ? 512 : 256;
-  double f = (VB == 1) ? 1.0 : 1.5;
-  if (VB == 1 && wgs > 256) f *= 1.46;
-  const double rounds = (double)((wgs + slots - 1) / slots);
-  return (double)chunks * rel * f * (rounds < 1.0 ? 1.0 : rounds);
+// Estimated scan time of a plan with P segments per sequence and VB 16-column
+// state tiles per wave, in microseconds per chunk step, calibrated on MI355X
+// (256 CUs).  Every pass runs one 4-wave workgroup per CU, except the forward
+// transition pass at VB = 1, which fits two; a pass with more workgroups than
+// slots runs in rounds.  Forward: output pass 4.1 (VB = 1) / 5.5 (VB = 2) per
+// chunk, transition pass 3.0 / 3.2.  Backward (state and state-gradient scans
+// in one launch): 3.7 / 5.8 per chunk, transition pass 4.5 / 5.5.  A combine
+// step costs 11 per scan, and splitting adds two launches (~16).
+static double rounds(int64_t wgs, int64_t slots) {
+  const int64_t r = (wgs + slots - 1) / slots;
+  return r < 1 ? 1.0 : (double)r;
 }
 
-static double plan_cost(int64_t units, int64_t maxch, int P, int VB) {
+static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd) {
   const int64_t nvs0 = 2 / VB, nvs1 = 4 / VB;
-  if (P == 1) return pass_cost(units * nvs0, maxch, 1.0 + 0.6 + 0.85, VB);
+  const int64_t scans = bwd ? 2 : 1;
+  const double out = bwd ? (VB == 1 ? 3.7 : 5.8) : (VB == 1 ? 4.1 : 5.5);
+  if (P == 1) return (double)maxch * out * rounds(scans * units * nvs0, 256);
+  const double aug = bwd ? (VB == 1 ? 4.5 : 5.5) : (VB == 1 ? 3.0 : 3.2);
+  const int64_t aug_slots = (!bwd && VB == 1) ? 512 : 256;
   const int64_t sc = (maxch + P - 1) / P;
-  const int64_t wg_aug = units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);  // B part only for one end
-  return 2.0 * pass_cost(wg_aug, sc, 0.75, VB) + pass_cost(wg_aug, sc, 1.3, VB) +
-         pass_cost(units * P * nvs0, sc, 1.0 + 0.6 + 0.85, VB) + 3.0 * 2.0 * (P - 1);
+  // one end segment needs only its value columns, the inner ones everything
+  const int64_t wg_aug = scans * units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
+  return (double)sc * aug * rounds(wg_aug, aug_slots) + 11.0 * (double)(scans * (P - 1)) + 16.0 +
+         (double)sc * out * rounds(scans * units * P * nvs0, 256);
 }
 
-// Context-parallel plan along T: it depends only on shapes (never on data),
-// so every run of a problem, in either state layout, takes the same path.
-Plan make_plan(const gdr_problem* p) {
+// Context-parallel plan along T for one direction: it depends only on shapes
+// (never on data), so every run of a problem, in either state layout, takes
+// the same path.
+Plan make_plan(const gdr_problem* p, bool bwd) {
   Plan pl;
   pl.N = p->N;
   pl.total_chunks = 0;
@@ -118,7 +122,8 @@ Plan make_plan(const gdr_problem* p) {
     if (fixed == 0 && P > 1 && maxch < 8 * P) continue;
     for (int VB = 1; VB <= 2; ++VB) {
       if (p->wave_tiles > 0 && VB != p->wave_tiles) continue;
-      const double c = plan_cost(units, maxch, P, VB);
+      // a split must win clearly: the model is coarse and splitting adds work
+      const double c = plan_cost(units, maxch, P, VB, bwd) * ((P > 1 && fixed == 0) ? 1.1 : 1.0);
       if (c < best) {
         best = c;
         pl.cp = P;
@@ -325,12 +330,12 @@ gdr_status gdr_check_device(void) { return check_device_cached(); }
 
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
   if (validate(p, nullptr, 0) != GDR_OK) return 0;
-  return fwd_workspace_bytes(p, make_plan(p));
+  return fwd_workspace_bytes(p, make_plan(p, false));
 }
 
 size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p) {
   if (validate(p, nullptr, 0) != GDR_OK) return 0;
-  return bwd_workspace_bytes(p, make_plan(p));
+  return bwd_workspace_bytes(p, make_plan(p, true));
 }
 
 gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -341,7 +346,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   if (s != GDR_OK) return s;
   if (!q || !k || !v || !g || !beta || !g_cum || !A || !o)
     return fail(GDR_ERR_NULL, nullptr, 0, "a required forward pointer is NULL");
-  const Plan pl = make_plan(p);
+  const Plan pl = make_plan(p, false);
   const size_t need = fwd_workspace_bytes(p, pl);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDR_ERR_WORKSPACE, nullptr, 0, "forward workspace needs %zu bytes, got %zu", need,
@@ -363,7 +368,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
     return fail(GDR_ERR_NULL, nullptr, 0, "a required backward pointer is NULL");
   if (initial_state && !dh0)
     return fail(GDR_ERR_NULL, nullptr, 0, "dh0 is required when initial_state is given");
-  const Plan pl = make_plan(p);
+  const Plan pl = make_plan(p, true);
   const size_t need = bwd_workspace_bytes(p, pl);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDR_ERR_WORKSPACE, nullptr, 0, "backward workspace needs %zu bytes, got %zu",
@@ -374,10 +379,11 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
                     dg, initial_state ? dh0 : nullptr, workspace, (hipStream_t)stream);
 }
 
-gdr_status gdr_plan_info(const gdr_problem* p, int32_t* cp_segments, int32_t* wave_tiles) {
+gdr_status gdr_plan_info(const gdr_problem* p, int backward, int32_t* cp_segments,
+                         int32_t* wave_tiles) {
   gdr_status s = validate(p, nullptr, 0);
   if (s != GDR_OK) return s;
-  const Plan pl = make_plan(p);
+  const Plan pl = make_plan(p, backward != 0);
   if (cp_segments) *cp_segments = pl.cp;
   if (wave_tiles) *wave_tiles = pl.vb;
   return GDR_OK;

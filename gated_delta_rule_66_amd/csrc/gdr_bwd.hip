@@ -42,7 +42,7 @@ struct DhArgs {
   const float* gcum;
   const void* A;
   const float* dht;    // [N, Hv, K, V] (svf aware), nullable
-  void* dh;            // [NC, Hv, K, V] in_dtype: gradient of each chunk's end state
+  void* dh;            // [NC, Hv, V, K] in_dtype (value-major): gradient of each chunk's end state
   float* dh0;          // nullable (svf aware)
   const float* seg_start;  // [units, P, K, V]: gradient entering each segment's end
   float* seg_out;          // [units, P, K, 2V]: augmented pass-1 results
@@ -55,7 +55,7 @@ struct DhArgs {
 };
 
 template <typename T, int VB, int MODE>
-__global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a) {
+__device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
   typedef typename VT<T>::x8 x8;
   constexpr int CW = 64 * VB;
   constexpr int LD = 136;
@@ -66,12 +66,9 @@ __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a)
   __shared__ __align__(16) T Ks[64 * LD];
   __shared__ __align__(16) T Ds[64 * LDV];
   __shared__ __align__(16) T As[64 * LDA];
-  __shared__ __align__(16) T Ps[64 * LDA];
-  __shared__ __align__(16) T Hs[OUT ? 128 * (CW + 8) : 8];
   __shared__ __align__(16) float gam[64], eg[64], bex[64], dl[64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
-  const int bid = xcd_block(blockIdx.x, gridDim.x);
   const int vs = bid % a.nvs;
   const int up = bid / a.nvs;
   const int p = up % a.P, unit = up / a.P;
@@ -126,7 +123,7 @@ __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a)
   auto prefetch = [&](int c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
-    tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
+    if (!isT) tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
     tile_load<T, 128, 256>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
     if (!isT) tile_load<T, CW, 256>(rd, dO + (t0 * a.Hv + h) * kDim + vcol0, (int64_t)a.Hv * kDim, Cc);
     tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc);
@@ -137,11 +134,10 @@ __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a)
     }
   };
 
-  p_zero_tiles<T>(Ps, LDA);
   if (sr.c0 < sr.c1) prefetch(sr.c1 - 1);
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
     __syncthreads();
-    tile_store<T, 128, 256>(Qs, LD, rq);
+    if (!isT) tile_store<T, 128, 256>(Qs, LD, rq);
     tile_store<T, 128, 256>(Ks, LD, rk);
     if (!isT) tile_store<T, CW, 256>(Ds, LDV, rd);
     tile_store<T, 64, 256>(As, LDA, ra);
@@ -154,65 +150,99 @@ __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a)
     }
     __syncthreads();
     const float eL = __expf(gam[63]);
-    if (c - 1 >= sr.c0) prefetch(c - 1);
 
+    // gradient of this chunk's end state out, value-major ([V][K]): a lane's
+    // four consecutive keys of one value column are 8 contiguous bytes
     if (OUT) {
+      const __amdgpu_buffer_rsrc_t hrs =
+          buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            Hs[(16 * kb + 4 * grp + e) * (CW + 8) + cw0 + 16 * vb + col] = from_f<T>(Gs[kb][vb][e]);
+        for (int vb = 0; vb < VB; ++vb) {
+          const int vc = cb0 + cw0 + 16 * vb + col;
+          const typename VT<T>::x4 hv{from_f<T>(Gs[kb][vb][0]), from_f<T>(Gs[kb][vb][1]),
+                                      from_f<T>(Gs[kb][vb][2]), from_f<T>(Gs[kb][vb][3])};
+          buf_store8(hrs, (vc * kDim + 16 * kb + 4 * grp) * (int)sizeof(T), __builtin_bit_cast(u32x2, hv));
+        }
     }
-    if (!isT) p_tiles<T>(Qs, Ks, LD, Ps, LDA, gam, w);
-    // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
+
+    // One pass over the key dimension forms K dSn and the lower tiles of
+    // P = Q K^T (tile (rb, ib), ib <= rb: rows r = 16 rb + 4 grp + e, column
+    // i = 16 ib + col) from the same K fragments.
     x8 Gb[4][VB];
 #pragma unroll
     for (int kb2 = 0; kb2 < 4; ++kb2)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) Gb[kb2][vb] = pack_split<T>(Gs[2 * kb2][vb], Gs[2 * kb2 + 1][vb]);
-    f32x4 dd[4][VB];
+    f32x4 dd[4][VB], pt[10];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = zero4();
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int x = 0; x < 10; ++x) pt[x] = zero4();
 #pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const x8 fk = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      x8 fk[4], fq[4];
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = mfma16(fk, Gb[kb2][vb], dd[tb][vb]);
+      for (int tb = 0; tb < 4; ++tb) fk[tb] = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
+      if (!isT) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) fq[tb] = frag_row_split(Qs + 16 * tb * LD + 32 * kb2, LD);
       }
-    __syncthreads();
-    if (OUT) {
-      T* hp = reinterpret_cast<T*>(a.dh) + ((choff + c) * a.Hv + h) * KV;
-      constexpr int PR = CW / 8;
-      for (int x = tid; x < 128 * PR; x += 256) {
-        const int r = x / PR, c8 = (x % PR) * 8;
-        *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
-            *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = mfma16(fk[tb], Gb[kb2][vb], dd[tb][vb]);
+      if (!isT) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int ib = 0; ib <= rb; ++ib) pt[tri_idx(ib, rb)] = mfma16(fq[rb], fk[ib], pt[tri_idx(ib, rb)]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (c - 1 >= sr.c0) prefetch(c - 1);
+
+    // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO.  Two stacked D tiles
+    // of P (rows r) form the A operand of P^T with k = r.
+    if (!isT) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
+#pragma unroll
+        for (int ib = 0; ib <= rb; ++ib) {
+          const float gi = gam[16 * ib + col];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // masked entries take exp(-inf) = 0 (unconditional exponential)
+            const bool keep = (ib < rb) || (col <= 4 * grp + e);
+            pt[tri_idx(ib, rb)][e] *= __expf(keep ? gr[e] - gi : -INFINITY);
+          }
+        }
       }
     }
-
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < 4; ++tb) {
+      x8 pa[2];
+#pragma unroll
+      for (int kt = tb / 2; kt < 2; ++kt)
+        pa[kt] = pack_split<T>((2 * kt >= tb) ? pt[tri_idx(tb, 2 * kt < 4 ? 2 * kt : 3)] : zero4(),
+                               pt[tri_idx(tb, 2 * kt + 1)]);
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         f32x4 acc = zero4();
         if (!isT) {
 #pragma unroll
           for (int kt = tb / 2; kt < 2; ++kt)
-            acc = mfma16(frag_tr_split(Ps + 32 * kt * LDA + 16 * tb, LDA),
-                         frag_tr_split(Ds + 32 * kt * LDV + cw0 + 16 * vb, LDV), acc);
+            acc = mfma16(pa[kt], frag_tr_split(Ds + 32 * kt * LDV + cw0 + 16 * vb, LDV), acc);
         }
+        const f32x4 dlr = *reinterpret_cast<const f32x4*>(dl + 16 * tb + 4 * grp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + 4 * grp + e;
-          dd[tb][vb][e] = dl[r] * dd[tb][vb][e] + a.scale * acc[e];
-        }
+        for (int e = 0; e < 4; ++e) dd[tb][vb][e] = dlr[e] * dd[tb][vb][e] + a.scale * acc[e];
       }
+    }
     // Z = -diag(beta e^gamma) A^T dDelta
     f32x4 zz[4][VB];
 #pragma unroll
@@ -224,8 +254,9 @@ __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a)
         for (int kt = tb / 2; kt < 2; ++kt)
           acc = mfma16(frag_tr_split(As + 32 * kt * LDA + 16 * tb, LDA),
                        pack_split<T>(dd[2 * kt][vb], dd[2 * kt + 1][vb]), acc);
+        const f32x4 bx = *reinterpret_cast<const f32x4*>(bex + 16 * tb + 4 * grp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] *= -bex[16 * tb + 4 * grp + e];
+        for (int e = 0; e < 4; ++e) acc[e] *= -bx[e];
         zz[tb][vb] = acc;
       }
     // dS = e^{gL} dSn + K^T Z + Q^T (scale diag(e^gamma) dO)
@@ -288,6 +319,16 @@ __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_scan_kernel(DhArgs a)
   }
 }
 
+// The state scan (B1) and the state-gradient scan (B2) are independent (B2
+// needs no chunk states), so one launch runs both: blocks [0, n1) take B1,
+// the rest B2.  Each pass alone fills only part of the chip when there are
+// few (sequence, head) units.
+template <typename T, int VB, int MS, int MD>
+__global__ __launch_bounds__(256, 1) void bwd_scans_kernel(ScanArgs sa, DhArgs da, int n1) {
+  if ((int)blockIdx.x < n1) scan_body<T, VB, MS>(sa, xcd_block(blockIdx.x, n1));
+  else dh_body<T, VB, MD>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
+}
+
 // ---------------------------------------------------------------------------
 // B3-B5: per-chunk gradients
 // ---------------------------------------------------------------------------
@@ -299,8 +340,8 @@ struct GradArgs {
   const void* beta;
   const float* gcum;
   const void* A;
-  const void* h;   // [NC, Hv, K, V] chunk-start states
-  const void* dh;  // [NC, Hv, K, V] end-state gradients
+  const void* h;   // [NC, Hv, V, K] chunk-start states (value-major)
+  const void* dh;  // [NC, Hv, V, K] end-state gradients (value-major)
   void* dq;        // in_dtype [T, Hq, K], or fp32 [T, Hv, K] partials when partial
   void* dk;
   void* dv;
@@ -322,8 +363,8 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   __shared__ __align__(16) T Ks[64 * LD];
   __shared__ __align__(16) T As[64 * L7];
   __shared__ __align__(16) T Ps[64 * L7];
-  __shared__ __align__(16) T Ss[128 * L7];   // S[:, half]; later dA, T1
-  __shared__ __align__(16) T Gs_[128 * L7];  // dSn[:, half]; later dP o Gamma, dM o beta Gamma
+  __shared__ __align__(16) T Ss[128 * L7];   // S[:, half]^T ([v][k], ld LD); later dA, T1
+  __shared__ __align__(16) T Gs_[128 * L7];  // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma
   __shared__ __align__(16) T Vs[64 * L7];
   __shared__ __align__(16) T Os[64 * L7];    // dO[:, half]
   __shared__ __align__(16) T Rs[64 * L7];    // R, transposed: [v][r]
@@ -427,22 +468,19 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   for (int hv = 0; hv < 2; ++hv) {
     const int v0 = 64 * hv;
     __syncthreads();  // previous half done with the per-half tiles
-    // S[:, half], dSn[:, half] (128 x 64) and V, dO (64 x 64), loads batched
+    // S[:, half]^T, dSn[:, half]^T (value-major: 64 x 128) and V, dO (64 x 64),
+    // loads batched
     {
-      TileRegs<64, 256> s0, s1, g0, g1, rv, ro;
-      tile_load<T, 64, 256>(s0, hS + v0, kDim, 64);
-      tile_load<T, 64, 256>(s1, hS + 64 * kDim + v0, kDim, 64);
-      tile_load<T, 64, 256>(g0, hG + v0, kDim, 64);
-      tile_load<T, 64, 256>(g1, hG + 64 * kDim + v0, kDim, 64);
+      TileRegs<128, 256> rs, rg;
+      TileRegs<64, 256> rv, ro;
+      tile_load<T, 128, 256>(rs, hS + v0 * kDim, kDim, 64);
+      tile_load<T, 128, 256>(rg, hG + v0 * kDim, kDim, 64);
       tile_load<T, 64, 256>(rv, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
       tile_load<T, 64, 256>(ro, dOg + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
 #pragma unroll
-      for (int i = 0; i < TileRegs<64, 256>::N; ++i)
-        sds += dot8<T>(s0.r[i], g0.r[i]) + dot8<T>(s1.r[i], g1.r[i]);
-      tile_store<T, 64, 256>(Ss, L7, s0);
-      tile_store<T, 64, 256>(Ss + 64 * L7, L7, s1);
-      tile_store<T, 64, 256>(Gs_, L7, g0);
-      tile_store<T, 64, 256>(Gs_ + 64 * L7, L7, g1);
+      for (int i = 0; i < TileRegs<128, 256>::N; ++i) sds += dot8<T>(rs.r[i], rg.r[i]);
+      tile_store<T, 128, 256>(Ss, LD, rs);
+      tile_store<T, 128, 256>(Gs_, LD, rg);
       tile_store<T, 64, 256>(Vs, L7, rv);
       tile_store<T, 64, 256>(Os, L7, ro);
     }
@@ -460,8 +498,8 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
       }
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const x8 fs = frag_tr_split(Ss + 32 * kb2 * L7 + cc, L7);
-        const x8 fg = frag_tr_split(Gs_ + 32 * kb2 * L7 + cc, L7);
+        const x8 fs = frag_row_split(Ss + cc * LD + 32 * kb2, LD);
+        const x8 fg = frag_row_split(Gs_ + cc * LD + 32 * kb2, LD);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
           const x8 fk = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
@@ -543,10 +581,10 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
       }
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const x8 fs = frag_row_split(Ss + 16 * kb * L7 + 32 * vk, L7);
+        const x8 fs = frag_tr_split(Ss + 32 * vk * LD + 16 * kb, LD);
         dQ1[kb] = mfma16(fdo, fs, dQ1[kb]);
         dX[kb] = mfma16(fdr, fs, dX[kb]);
-        dKs[kb] = mfma16(fdl, frag_row_split(Gs_ + 16 * kb * L7 + 32 * vk, L7), dKs[kb]);
+        dKs[kb] = mfma16(fdl, frag_tr_split(Gs_ + 32 * vk * LD + 16 * kb, LD), dKs[kb]);
       }
     }
   }
@@ -769,7 +807,7 @@ __global__ void gva_reduce_kernel(const float* pq, const float* pk, T* dq, T* dk
 // host side
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-  size_t offs, cp, h, dh, pq, pk, total;
+  size_t offs, cp, cp2, h, dh, pq, pk, total;
 };
 
 static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
@@ -777,7 +815,10 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
   size_t o = 0;
   L.offs = o;
   if (p->cu_seqlens_dev) o += align256(sizeof(int32_t) * (size_t)(pl.N + 1));
+  // the two scans run in one launch: each has its own CP buffers
   L.cp = o;
+  o += cp_workspace_bytes(pl, p->Hv);
+  L.cp2 = o;
   o += cp_workspace_bytes(pl, p->Hv);
   const size_t st = (size_t)pl.total_chunks * p->Hv * kDim * kDim * 2;  // bf16/fp16
   L.h = o;
@@ -798,30 +839,37 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
 
 size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl) { return bwd_layout(p, pl).total; }
 
+// B1 and B2 together: with CP, both augmented passes in one launch, the two
+// chains (forward for B1, reverse for B2), then both output passes in one
+// launch.
 template <typename T, int VB>
-static void launch_dh_vb(const Plan& pl, DhArgs a, hipStream_t st) {
-  const unsigned units = (unsigned)(pl.N * a.Hv);
+static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t st) {
+  const unsigned units = (unsigned)(pl.N * sa.Hv);
   if (pl.cp > 1) {
-    DhArgs a1 = a;
-    a1.P = pl.cp;
-    a1.nvs = 4 / VB;
-    GDR_LAUNCH("dh_scan_aug", (dh_scan_kernel<T, VB, MODE_AUG>), dim3(units * pl.cp * a1.nvs),
-               dim3(256), st, a1);
-    ScanArgs sa;
-    memset(&sa, 0, sizeof(sa));
-    sa.cu = a.cu;
-    sa.T = a.T;
-    sa.Hv = a.Hv;
-    sa.P = pl.cp;
-    sa.seg_out = a.seg_out;
-    sa.seg_start = a.seg_start;
-    sa.reverse = 1;
-    GDR_LAUNCH("cp_combine", cp_combine_kernel, dim3(units * 8), dim3(256), st, sa);
+    ScanArgs s1 = sa;
+    DhArgs d1 = da;
+    s1.P = d1.P = pl.cp;
+    s1.nvs = d1.nvs = 4 / VB;
+    const unsigned n1 = units * pl.cp * s1.nvs;
+    GDR_LAUNCH("bwd_scan_aug", (bwd_scans_kernel<T, VB, MODE_AUG, MODE_AUG>), dim3(2 * n1),
+               dim3(256), st, s1, d1, (int)n1);
+    GDR_LAUNCH("cp_combine", cp_combine_kernel, dim3(units * 8), dim3(256), st, s1);
+    ScanArgs r;
+    memset(&r, 0, sizeof(r));
+    r.cu = da.cu;
+    r.T = da.T;
+    r.Hv = da.Hv;
+    r.P = pl.cp;
+    r.seg_out = da.seg_out;
+    r.seg_start = da.seg_start;
+    r.reverse = 1;
+    GDR_LAUNCH("cp_combine", cp_combine_kernel, dim3(units * 8), dim3(256), st, r);
   }
-  a.P = pl.cp;
-  a.nvs = 2 / VB;
-  GDR_LAUNCH("dh_scan_out", (dh_scan_kernel<T, VB, MODE_OUT>), dim3(units * pl.cp * a.nvs),
-             dim3(256), st, a);
+  sa.P = da.P = pl.cp;
+  sa.nvs = da.nvs = 2 / VB;
+  const unsigned n1 = units * pl.cp * sa.nvs;
+  GDR_LAUNCH("bwd_scans", (bwd_scans_kernel<T, VB, MODE_STATE, MODE_OUT>), dim3(2 * n1), dim3(256),
+             st, sa, da, (int)n1);
 }
 
 template <typename T>
@@ -840,33 +888,36 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   }
   float* cp_out = nullptr;
   float* cp_start = nullptr;
+  float* cp2_out = nullptr;
+  float* cp2_start = nullptr;
   if (pl.cp > 1) {
     const size_t units = (size_t)pl.N * p->Hv;
+    const size_t so = align256(units * pl.cp * 2 * kDim * kDim * sizeof(float));
     cp_out = reinterpret_cast<float*>(ws + L.cp);
-    cp_start = reinterpret_cast<float*>(ws + L.cp +
-                                        align256(units * pl.cp * 2 * kDim * kDim * sizeof(float)));
+    cp_start = reinterpret_cast<float*>(ws + L.cp + so);
+    cp2_out = reinterpret_cast<float*>(ws + L.cp2);
+    cp2_start = reinterpret_cast<float*>(ws + L.cp2 + so);
   }
   void* hbuf = ws + L.h;
   void* dhbuf = ws + L.dh;
-  // B1: chunk-start states
+  // B1: chunk-start states (value-major)
   ScanArgs sa;
   memset(&sa, 0, sizeof(sa));
   sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
   sa.h = hbuf;
   sa.cu = p->cu_seqlens_dev; sa.offs = offs;
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
-  sa.P = 1; sa.nvs = 1; sa.scale = p->scale; sa.svf = p->state_v_first ? 1 : 0; sa.h_svf = 0;
+  sa.P = 1; sa.nvs = 1; sa.scale = p->scale; sa.svf = p->state_v_first ? 1 : 0; sa.h_svf = 1;
   sa.seg_out = cp_out; sa.seg_start = cp_start; sa.reverse = 0;
-  launch_scan<T>(pl, sa, MODE_STATE, st);
-  // B2: state gradients
+  // B2: state gradients (value-major)
   DhArgs da;
   da.q = q; da.k = k; da.dO = dO; da.beta = beta; da.gcum = gcum; da.A = A; da.dht = dht;
-  da.dh = dhbuf; da.dh0 = dh0; da.seg_start = cp_start; da.seg_out = cp_out;
+  da.dh = dhbuf; da.dh0 = dh0; da.seg_start = cp2_start; da.seg_out = cp2_out;
   da.cu = p->cu_seqlens_dev; da.offs = offs;
   da.N = pl.N; da.T = p->T; da.Hq = p->Hq; da.Hv = p->Hv; da.nc_dense = pl.nc_dense;
   da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf;
-  if (pl.vb == 2) launch_dh_vb<T, 2>(pl, da, st);
-  else launch_dh_vb<T, 1>(pl, da, st);
+  if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, st);
+  else launch_bwd_scans<T, 1>(pl, sa, da, st);
   // B3-B5
   const bool partial = p->Hq != p->Hv;
   GradArgs ga;

@@ -22,7 +22,7 @@ struct Plan {
   int vb;             // 16-column MFMA tiles per wave in the scans (1 or 2)
 };
 
-Plan make_plan(const gdr_problem* p);
+Plan make_plan(const gdr_problem* p, bool bwd);
 
 // Workspace layout helpers: every region is 256-byte aligned.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

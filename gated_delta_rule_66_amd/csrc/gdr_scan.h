@@ -68,7 +68,7 @@ struct ScanArgs {
   int nvs;  // column blocks per (unit, segment)
   float scale;
   int svf;     // layout of h0 / ht / user h
-  int h_svf;   // layout of h (user h follows svf; the backward's own copy is [K][V])
+  int h_svf;   // layout of h: the user's h follows svf; MODE_STATE always writes [V][K]
   int reverse; // cp_combine_kernel: chain segments backwards (state gradients)
 };
 
@@ -90,25 +90,27 @@ __device__ __forceinline__ SegRange seg_range(int nch, int P, int p) {
 // list of ten tiles.
 __host__ __device__ constexpr int tri_idx(int ib, int rb) { return rb * (rb + 1) / 2 + ib; }
 
+// One workgroup's share of a scan pass; bid is the (XCD-renumbered) block
+// index within the pass.  A device function so that two independent passes
+// can share one launch (the backward's state and state-gradient scans).
 template <typename T, int VB, int MODE>
-__global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_STATE)) ? 2 : 1) void scan_kernel(ScanArgs a) {
+__device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
   typedef typename VT<T>::x8 x8;
   constexpr int CW = 64 * VB;          // columns per workgroup
   constexpr int LD = 136;              // q / k tile leading dimension
   constexpr int LDV = CW + 8;          // v tile leading dimension
   constexpr int LDA = 72;              // A tile leading dimension
   constexpr bool OUT = (MODE == MODE_OUT || MODE == MODE_OUT_H);
-  constexpr bool HST = (MODE == MODE_STATE || MODE == MODE_OUT_H);  // stage h in LDS
-  constexpr int HS_ELEMS = (128 * (CW + 8) > CW * 136) ? 128 * (CW + 8) : CW * 136;
+  constexpr bool HOUT = (MODE == MODE_STATE || MODE == MODE_OUT_H);  // writes h
+  constexpr bool HST = (MODE == MODE_OUT_H);  // may stage h in LDS (key-major h)
   __shared__ __align__(16) T Ks[64 * LD];
   __shared__ __align__(16) T Qs[OUT ? 64 * LD : 8];
   __shared__ __align__(16) T Vs[64 * LDV];
   __shared__ __align__(16) T As[64 * LDA];
-  __shared__ __align__(16) T Hs[HST ? HS_ELEMS : 8];
+  __shared__ __align__(16) T Hs[HST ? 128 * (CW + 8) : 8];
   __shared__ __align__(16) float gam[64], bet[64], eg[64], bex[64], dl[64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
-  const int bid = xcd_block(blockIdx.x, gridDim.x);
   const int vs = bid % a.nvs;
   const int up = bid / a.nvs;
   const int p = up % a.P, unit = up / a.P;
@@ -202,18 +204,33 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
     // P^T and (Q S)^T accumulators.
     if (!OUT && c + 1 < sr.c1) prefetch(c + 1);
 
-    // chunk-start state out, staged in LDS for 16-byte stores
-    if (HST) {
+    // chunk-start state out.  Value-major ([V][K]): a lane's four consecutive
+    // keys of one value column are 8 contiguous bytes, stored straight from
+    // registers.  Key-major ([K][V]): staged in LDS for 16-byte row stores.
+    if (HOUT) {
+      if (MODE == MODE_STATE || a.h_svf) {
+        const __amdgpu_buffer_rsrc_t hrs =
+            buf_rsrc(reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = 16 * kb + 4 * grp + e, lc = cw0 + 16 * vb + col;
-            if (a.h_svf) Hs[lc * 136 + key] = from_f<T>(S[kb][vb][e]);
-            else Hs[key * (CW + 8) + lc] = from_f<T>(S[kb][vb][e]);
+          for (int vb = 0; vb < VB; ++vb) {
+            const int vc = cb0 + cw0 + 16 * vb + col;
+            const typename VT<T>::x4 hv{from_f<T>(S[kb][vb][0]), from_f<T>(S[kb][vb][1]),
+                                        from_f<T>(S[kb][vb][2]), from_f<T>(S[kb][vb][3])};
+            buf_store8(hrs, (vc * kDim + 16 * kb + 4 * grp) * (int)sizeof(T), __builtin_bit_cast(u32x2, hv));
           }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int key = 16 * kb + 4 * grp + e, lc = cw0 + 16 * vb + col;
+              Hs[key * (CW + 8) + lc] = from_f<T>(S[kb][vb][e]);
+            }
+      }
     }
 
     // One pass over the key dimension forms, from the same K and Q fragments:
@@ -262,23 +279,14 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
       __builtin_amdgcn_sched_barrier(0);
     }
     if (OUT && c + 1 < sr.c1) prefetch(c + 1);
-    if (HST) {
+    if (HST && !a.h_svf) {
       __syncthreads();  // every wave's part of the staged state is in Hs
       T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
-      if (a.h_svf) {
-        // rows = local value columns, 128 keys each
-        for (int x = tid; x < CW * 16; x += 256) {
-          const int r = x >> 4, c8 = (x & 15) * 8;
-          *reinterpret_cast<uint4*>(hp + (int64_t)(cb0 + r) * kDim + c8) =
-              *reinterpret_cast<const uint4*>(Hs + r * 136 + c8);
-        }
-      } else {
-        constexpr int PR = CW / 8;
-        for (int x = tid; x < 128 * PR; x += 256) {
-          const int r = x / PR, c8 = (x % PR) * 8;
-          *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
-              *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
-        }
+      constexpr int PR = CW / 8;
+      for (int x = tid; x < 128 * PR; x += 256) {
+        const int r = x / PR, c8 = (x % PR) * 8;
+        *reinterpret_cast<uint4*>(hp + (int64_t)r * kDim + cb0 + c8) =
+            *reinterpret_cast<const uint4*>(Hs + r * (CW + 8) + c8);
       }
     }
 
@@ -411,6 +419,11 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
           a.ht[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = S[kb][vb][e];
         }
   }
+}
+
+template <typename T, int VB, int MODE>
+__global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_STATE)) ? 2 : 1) void scan_kernel(ScanArgs a) {
+  scan_body<T, VB, MODE>(a, xcd_block(blockIdx.x, gridDim.x));
 }
 
 // Pass 2: chain the segment start states of one (unit, 16-column block).

@@ -174,10 +174,13 @@ gdr_status gdr_prepare_chunk_token_starts_i64(const int64_t* cu, int64_t n_plus_
                                               int64_t chunk_size, int64_t* out,
                                               int64_t* num_chunks);
 
-/* The launch plan the library picks for `p` (it depends only on shapes):
+/* The launch plan the library picks for `p` in one direction (backward != 0:
+ * gdr_chunk_bwd, else gdr_chunk_fwd); it depends only on shapes:
  * *cp_segments = T-segments per sequence (1 = no context parallelism),
- * *wave_tiles = 16-column state tiles per wave in the scans (1 or 2). */
-gdr_status gdr_plan_info(const gdr_problem* p, int32_t* cp_segments, int32_t* wave_tiles);
+ * *wave_tiles = 16-column state tiles per wave in the scans (1 or 2).
+ * A nonzero cp_segments / wave_tiles in `p` fixes that choice for both. */
+gdr_status gdr_plan_info(const gdr_problem* p, int backward, int32_t* cp_segments,
+                         int32_t* wave_tiles);
 
 /* Kernel timing for benchmarks and diagnostics (not part of the pages' API).
  * While enabled, every kernel the library launches is bracketed by a pair of

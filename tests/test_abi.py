@@ -117,19 +117,25 @@ def test_workspace_queries():
     assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(long)) > 0  # context-parallel buffers
 
 
-def test_plan_depends_only_on_shapes():
+def plan(p, backward):
     cp = ctypes.c_int32()
     vt = ctypes.c_int32()
-    plans = []
-    for svf in (0, 1):
-        p = good(B=1, N=1, T=65536, Hq=32, Hv=32, state_v_first=svf)
-        assert lib.gdr_plan_info(ctypes.byref(p), ctypes.byref(cp), ctypes.byref(vt)) == 0
-        plans.append((cp.value, vt.value))
-    assert plans[0] == plans[1]
-    assert plans[0][0] > 1  # one long sequence is split along T
-    p = good(B=1, N=1, T=65536, Hq=32, Hv=32, cp_segments=1)
-    lib.gdr_plan_info(ctypes.byref(p), ctypes.byref(cp), ctypes.byref(vt))
-    assert cp.value == 1
+    assert lib.gdr_plan_info(ctypes.byref(p), backward, ctypes.byref(cp), ctypes.byref(vt)) == 0
+    return cp.value, vt.value
+
+
+def test_plan_depends_only_on_shapes():
+    for bwd in (0, 1):
+        plans = [plan(good(B=1, N=1, T=65536, Hq=32, Hv=32, state_v_first=svf), bwd)
+                 for svf in (0, 1)]
+        assert plans[0] == plans[1]
+        assert plans[0][1] in (1, 2)
+    assert plan(good(B=1, N=1, T=65536, Hq=32, Hv=32), 0)[0] > 1  # one long sequence split along T
+    for bwd in (0, 1):
+        assert plan(good(B=1, N=1, T=65536, Hq=32, Hv=32, cp_segments=1), bwd)[0] == 1
+        assert plan(good(B=1, N=1, T=65536, Hq=32, Hv=32, cp_segments=4, wave_tiles=2), bwd) == (4, 2)
+    # short sequences are never split
+    assert plan(good(B=2, N=2, T=256, Hq=32, Hv=32), 0)[0] == 1
 
 
 def test_null_and_workspace_errors_before_any_device_work():
