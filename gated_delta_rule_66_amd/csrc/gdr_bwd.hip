@@ -354,29 +354,37 @@ struct GradArgs {
   int partial;
 };
 
+// Eight waves: wave w works on row / column block wr = w % 4 and takes one
+// side of every phase (hi = w / 4): hi = 0 the forward-side chain (K S, R,
+// Delta, dA, dP, dQ1 = dO S^T and everything of dq), hi = 1 the gradient side
+// (K dSn, dDelta, dR, dX = -dR S^T, dKs = Delta dSn^T, dM and everything of
+// dk).  The two sides of a phase are independent, so two waves share each
+// SIMD and hide each other's latencies.
 template <typename T>
-__global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
+__global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   typedef typename VT<T>::x8 x8;
-  constexpr int LD = 136;  // q, k
+  constexpr int LD = 136;  // q, k, and the value-major S / dSn halves
   constexpr int L7 = 72;   // every 64-wide tile
   __shared__ __align__(16) T Qs[64 * LD];
   __shared__ __align__(16) T Ks[64 * LD];
   __shared__ __align__(16) T As[64 * L7];
   __shared__ __align__(16) T Ps[64 * L7];
-  __shared__ __align__(16) T Ss[128 * L7];   // S[:, half]^T ([v][k], ld LD); later dA, T1
-  __shared__ __align__(16) T Gs_[128 * L7];  // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma
+  __shared__ __align__(16) T Ss[128 * L7];   // S[:, half]^T ([v][k], ld LD); later dA, T1, dq
+  __shared__ __align__(16) T Gs_[128 * L7];  // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma, dk
   __shared__ __align__(16) T Vs[64 * L7];
   __shared__ __align__(16) T Os[64 * L7];    // dO[:, half]
   __shared__ __align__(16) T Rs[64 * L7];    // R, transposed: [v][r]
   __shared__ __align__(16) T Dls[64 * L7];   // Delta, transposed
   __shared__ __align__(16) T DDs[64 * L7];   // dDelta, transposed
   __shared__ __align__(16) T DRs[64 * L7];   // dR, transposed
+  __shared__ __align__(16) T DVs[64 * L7];   // dv of the half, row-major
   __shared__ float gam[64], bet[64], eg[64], bex[64], dl[64];
-  __shared__ float dbv[8][64];       // v . dR partials per (half, wave)
-  __shared__ float colE[4][64];      // column sums of dP o P and dM o M per wave
-  __shared__ float red[4];           // <S, dSn> per wave
+  __shared__ float dbv[8][64];       // v . dR partials per (half, column block)
+  __shared__ float colE[4][64];      // column sums of dP o P and dM o M per row block
+  __shared__ float red[8];           // <S, dSn> per wave
   __shared__ float dgam[64];
-  __shared__ float fsum[4][4];       // F partials per (wave, lane group)
+  __shared__ float fsum[4][4];       // F partials per (row block, lane group)
+  __shared__ float rowq[64];         // dgamma row terms of the dq side
 
   const int c = blockIdx.x, h = blockIdx.y;
   int n, j;
@@ -392,25 +400,48 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   const int Cc = (int)min((int64_t)kChunk, s.end - t0);
   const int G = a.Hv / a.Hq, hq = h / G;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  const int wr = w & 3;
+  const bool hi = w >= 4;
   const int64_t KV = (int64_t)kDim * kDim;
   const T* hS = reinterpret_cast<const T*>(a.h) + ((int64_t)c * a.Hv + h) * KV;
   const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)c * a.Hv + h) * KV;
   const T* vv = reinterpret_cast<const T*>(a.v);
   const T* dOg = reinterpret_cast<const T*>(a.dO);
 
-  // every global load of a phase is issued before the first LDS store
+  // the value-half tiles: S^T, dSn^T (value-major rows v0 .. v0+63) and
+  // V, dO (columns v0 .. v0+63); half 1 is prefetched while half 0 computes
+  TileRegs<128, 512> rs, rg;
+  TileRegs<64, 512> rv, ro;
+  auto load_half = [&](int v0) {
+    tile_load<T, 128, 512>(rs, hS + v0 * kDim, kDim, 64);
+    tile_load<T, 128, 512>(rg, hG + v0 * kDim, kDim, 64);
+    tile_load<T, 64, 512>(rv, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
+    tile_load<T, 64, 512>(ro, dOg + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
+  };
+  float sds = 0.f;
+  auto store_half = [&]() {
+#pragma unroll
+    for (int i = 0; i < TileRegs<128, 512>::N; ++i) sds += dot8<T>(rs.r[i], rg.r[i]);
+    tile_store<T, 128, 512>(Ss, LD, rs);
+    tile_store<T, 128, 512>(Gs_, LD, rg);
+    tile_store<T, 64, 512>(Vs, L7, rv);
+    tile_store<T, 64, 512>(Os, L7, ro);
+  };
+  // every load of the first phase is issued before the first LDS store
   {
-    TileRegs<128, 256> rq, rk;
-    TileRegs<64, 256> ra;
-    tile_load<T, 128, 256>(rq, reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim,
+    TileRegs<128, 512> rq, rk;
+    TileRegs<64, 512> ra;
+    tile_load<T, 128, 512>(rq, reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim,
                            (int64_t)a.Hq * kDim, Cc);
-    tile_load<T, 128, 256>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
+    tile_load<T, 128, 512>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
                            (int64_t)a.Hq * kDim, Cc);
-    tile_load<T, 64, 256>(ra, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
+    tile_load<T, 64, 512>(ra, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
                           (int64_t)a.Hv * kChunk, Cc);
-    tile_store<T, 128, 256>(Qs, LD, rq);
-    tile_store<T, 128, 256>(Ks, LD, rk);
-    tile_store<T, 64, 256>(As, L7, ra);
+    load_half(0);
+    tile_store<T, 128, 512>(Qs, LD, rq);
+    tile_store<T, 128, 512>(Ks, LD, rk);
+    tile_store<T, 64, 512>(As, L7, ra);
+    store_half();
   }
   if (tid < 64) {
     const float gr = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
@@ -427,351 +458,375 @@ __global__ __launch_bounds__(256) void grad_kernel(GradArgs a) {
   __syncthreads();
   const float gL = gam[63];
 
-  // P and N = K K^T o Gamma (strict lower), rows 16w .. 16w+15, fp32 in registers
-  f32x4 pv[4], nv[4];
+  // rows 16 wr .. 16 wr + 15 of P = lower_incl(Q K^T o Gamma) (side 0, also
+  // written to Ps) or N = strict_lower(K K^T o Gamma) (side 1), fp32
+  f32x4 pn[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
-    f32x4 accq = zero4(), acck = zero4();
-    if (cb <= w) {
+    f32x4 acc = zero4();
+    if (cb <= wr) {
+      const T* rows = (hi ? Ks : Qs) + 16 * wr * LD;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const x8 fkb = frag_row(Ks + 16 * cb * LD + 32 * kk, LD);
-        accq = mfma16(frag_row(Qs + 16 * w * LD + 32 * kk, LD), fkb, accq);
-        acck = mfma16(frag_row(Ks + 16 * w * LD + 32 * kk, LD), fkb, acck);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        acc = mfma16(frag_row(rows + 32 * kk, LD), frag_row(Ks + 16 * cb * LD + 32 * kk, LD), acc);
     }
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * wr + 4 * grp);
+    const float gi = gam[16 * cb + col];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
-      const float gm = (i <= r) ? __expf(gam[r] - gam[i]) : 0.f;
-      pv[cb][e] = accq[e] * gm;
-      nv[cb][e] = (i < r) ? acck[e] * gm : 0.f;
-      Ps[r * L7 + i] = from_f<T>(pv[cb][e]);
+      const int r = 16 * wr + 4 * grp + e, i = 16 * cb + col;
+      const bool keep = hi ? (i < r) : (i <= r);
+      pn[cb][e] = acc[e] * __expf(keep ? gr[e] - gi : -INFINITY);
+      if (!hi) Ps[r * L7 + i] = from_f<T>(pn[cb][e]);
     }
   }
 
-  // accumulators over the value halves
-  f32x4 dA[4], dP[4], dQ1[8], dX[8], dKs[8];
+  // accumulators over the value halves: side 0 accA = dA, accB = dP,
+  // acc1 = dQ1; side 1 acc1 = dX, acc2 = dKs
+  f32x4 accA[4], accB[4], acc1[8], acc2[8];
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    dA[x] = zero4();
-    dP[x] = zero4();
+    accA[x] = zero4();
+    accB[x] = zero4();
   }
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
-    dQ1[x] = zero4();
-    dX[x] = zero4();
-    dKs[x] = zero4();
+    acc1[x] = zero4();
+    acc2[x] = zero4();
   }
-  float sds = 0.f;
-
   for (int hv = 0; hv < 2; ++hv) {
     const int v0 = 64 * hv;
-    __syncthreads();  // previous half done with the per-half tiles
-    // S[:, half]^T, dSn[:, half]^T (value-major: 64 x 128) and V, dO (64 x 64),
-    // loads batched
-    {
-      TileRegs<128, 256> rs, rg;
-      TileRegs<64, 256> rv, ro;
-      tile_load<T, 128, 256>(rs, hS + v0 * kDim, kDim, 64);
-      tile_load<T, 128, 256>(rg, hG + v0 * kDim, kDim, 64);
-      tile_load<T, 64, 256>(rv, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
-      tile_load<T, 64, 256>(ro, dOg + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
-#pragma unroll
-      for (int i = 0; i < TileRegs<128, 256>::N; ++i) sds += dot8<T>(rs.r[i], rg.r[i]);
-      tile_store<T, 128, 256>(Ss, LD, rs);
-      tile_store<T, 128, 256>(Gs_, LD, rg);
-      tile_store<T, 64, 256>(Vs, L7, rv);
-      tile_store<T, 64, 256>(Os, L7, ro);
+    if (hv > 0) {
+      __syncthreads();  // every wave is done with the previous half's tiles
+      store_half();
+      __syncthreads();
+    } else {
+      load_half(64);  // in flight during half 0
     }
-    __syncthreads();
 
-    // ---- wave w: value columns cc .. cc+15 of this half ----
-    const int cc = 16 * w;
-    f32x4 R[4], Dl[4], dD[4], dR[4], vd[4];
-    {
-      f32x4 ks[4], kg[4];
+    // ---- value columns cc .. cc+15 of this half ----
+    const int cc = 16 * wr;
+    if (!hi) {
+      // R = diag(beta) V - diag(beta e^gamma) K S ; Delta = A R
+      f32x4 ks[4];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        ks[tb] = zero4();
-        kg[tb] = zero4();
-      }
+      for (int tb = 0; tb < 4; ++tb) ks[tb] = zero4();
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) {
         const x8 fs = frag_row_split(Ss + cc * LD + 32 * kb2, LD);
-        const x8 fg = frag_row_split(Gs_ + cc * LD + 32 * kb2, LD);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const x8 fk = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
-          ks[tb] = mfma16(fk, fs, ks[tb]);
-          kg[tb] = mfma16(fk, fg, kg[tb]);
-        }
+        for (int tb = 0; tb < 4; ++tb)
+          ks[tb] = mfma16(frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD), fs, ks[tb]);
       }
-      // R = diag(beta) V - diag(beta e^gamma) K S
+      f32x4 R[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        vd[tb] = frag_d4(Vs, L7, 16 * tb, cc);
+        const f32x4 vd = frag_d4(Vs, L7, 16 * tb, cc);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(bet + 16 * tb + 4 * grp);
+        const f32x4 bx = *reinterpret_cast<const f32x4*>(bex + 16 * tb + 4 * grp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + 4 * grp + e;
-          R[tb][e] = bet[r] * vd[tb][e] - bex[r] * ks[tb][e];
-        }
+        for (int e = 0; e < 4; ++e) R[tb][e] = bt[e] * vd[e] - bx[e] * ks[tb][e];
       }
-      // Delta = A R ; dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
       const x8 Rb0 = pack_split<T>(R[0], R[1]), Rb1 = pack_split<T>(R[2], R[3]);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         f32x4 acc = mfma16(frag_row_split(As + 16 * tb * L7, L7), Rb0, zero4());
         if (tb >= 2) acc = mfma16(frag_row_split(As + 16 * tb * L7 + 32, L7), Rb1, acc);
-        Dl[tb] = acc;
+        store_d4_t<T>(Rs, L7, 16 * tb, cc, R[tb]);
+        store_d4_t<T>(Dls, L7, 16 * tb, cc, acc);
+      }
+    } else {
+      // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO ; dR = A^T dDelta
+      f32x4 kg[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) kg[tb] = zero4();
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        const x8 fg = frag_row_split(Gs_ + cc * LD + 32 * kb2, LD);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          kg[tb] = mfma16(frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD), fg, kg[tb]);
+      }
+      f32x4 dD[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
         f32x4 pt = zero4();
 #pragma unroll
         for (int kt = tb / 2; kt < 2; ++kt)
           pt = mfma16(frag_tr_split(Ps + 32 * kt * L7 + 16 * tb, L7),
                       frag_tr_split(Os + 32 * kt * L7 + cc, L7), pt);
+        const f32x4 dlr = *reinterpret_cast<const f32x4*>(dl + 16 * tb + 4 * grp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + 4 * grp + e;
-          dD[tb][e] = dl[r] * kg[tb][e] + a.scale * pt[e];
-        }
+        for (int e = 0; e < 4; ++e) dD[tb][e] = dlr[e] * kg[tb][e] + a.scale * pt[e];
       }
-      // dR = A^T dDelta
       const x8 Db0 = pack_split<T>(dD[0], dD[1]), Db1 = pack_split<T>(dD[2], dD[3]);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = mfma16(frag_tr_split(As + 32 * L7 + 16 * tb, L7), Db1, zero4());
-        if (tb < 2) acc = mfma16(frag_tr_split(As + 16 * tb, L7), Db0, acc);
-        dR[tb] = acc;
-      }
-    }
-    // the v . dR part of dbeta; dv into this wave's own columns of Vs (V is
-    // no longer read there); R, Delta, dDelta, dR stored transposed ([v][r])
+        f32x4 dR = mfma16(frag_tr_split(As + 32 * L7 + 16 * tb, L7), Db1, zero4());
+        if (tb < 2) dR = mfma16(frag_tr_split(As + 16 * tb, L7), Db0, dR);
+        // the v . dR part of dbeta, and dv = diag(beta) dR
+        const f32x4 vd = frag_d4(Vs, L7, 16 * tb, cc);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(bet + 16 * tb + 4 * grp);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * tb + 4 * grp + e;
-        const float pdot = sum16(vd[tb][e] * dR[tb][e]);
-        if (col == 0) dbv[4 * hv + w][r] = pdot;
-        Vs[r * L7 + cc + col] = from_f<T>(bet[r] * dR[tb][e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tb + 4 * grp + e;
+          const float pdot = sum16(vd[e] * dR[e]);
+          if (col == 0) dbv[4 * hv + wr][r] = pdot;
+          DVs[r * L7 + cc + col] = from_f<T>(bt[e] * dR[e]);
+        }
+        store_d4_t<T>(DDs, L7, 16 * tb, cc, dD[tb]);
+        store_d4_t<T>(DRs, L7, 16 * tb, cc, dR);
       }
-      store_d4_t<T>(Rs, L7, 16 * tb, cc, R[tb]);
-      store_d4_t<T>(Dls, L7, 16 * tb, cc, Dl[tb]);
-      store_d4_t<T>(DDs, L7, 16 * tb, cc, dD[tb]);
-      store_d4_t<T>(DRs, L7, 16 * tb, cc, dR[tb]);
     }
     __syncthreads();
-    // dv rows of this half: 16-byte stores of the staged tile
-    tile_from_lds<T, 64, 256>(reinterpret_cast<T*>(a.dv) + (t0 * a.Hv + h) * kDim + v0,
-                              (int64_t)a.Hv * kDim, Vs, L7, Cc);
+    tile_from_lds<T, 64, 512>(reinterpret_cast<T*>(a.dv) + (t0 * a.Hv + h) * kDim + v0,
+                              (int64_t)a.Hv * kDim, DVs, L7, Cc);
 
-    // ---- wave w: rows 16w .. 16w+15, contractions over this half's v ----
+    // ---- rows 16 wr .. 16 wr + 15, contractions over this half's v ----
 #pragma unroll
     for (int vk = 0; vk < 2; ++vk) {
-      const x8 fdd = frag_tr_split(DDs + 32 * vk * L7 + 16 * w, L7);
-      const x8 fdo = frag_row_split(Os + 16 * w * L7 + 32 * vk, L7);
-      const x8 fdr = frag_tr_split(DRs + 32 * vk * L7 + 16 * w, L7);
-      const x8 fdl = frag_tr_split(Dls + 32 * vk * L7 + 16 * w, L7);
+      if (!hi) {
+        const x8 fdd = frag_tr_split(DDs + 32 * vk * L7 + 16 * wr, L7);
+        const x8 fdo = frag_row_split(Os + 16 * wr * L7 + 32 * vk, L7);
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        if (ib <= w) {
-          dA[ib] = mfma16(fdd, frag_tr_split(Rs + 32 * vk * L7 + 16 * ib, L7), dA[ib]);
-          dP[ib] = mfma16(fdo, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), dP[ib]);
+        for (int ib = 0; ib < 4; ++ib) {
+          if (ib <= wr) {
+            accA[ib] = mfma16(fdd, frag_tr_split(Rs + 32 * vk * L7 + 16 * ib, L7), accA[ib]);
+            accB[ib] = mfma16(fdo, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), accB[ib]);
+          }
         }
-      }
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const x8 fs = frag_tr_split(Ss + 32 * vk * LD + 16 * kb, LD);
-        dQ1[kb] = mfma16(fdo, fs, dQ1[kb]);
-        dX[kb] = mfma16(fdr, fs, dX[kb]);
-        dKs[kb] = mfma16(fdl, frag_tr_split(Gs_ + 32 * vk * LD + 16 * kb, LD), dKs[kb]);
+        for (int kb = 0; kb < 8; ++kb)
+          acc1[kb] = mfma16(fdo, frag_tr_split(Ss + 32 * vk * LD + 16 * kb, LD), acc1[kb]);
+      } else {
+        const x8 fdr = frag_tr_split(DRs + 32 * vk * L7 + 16 * wr, L7);
+        const x8 fdl = frag_tr_split(Dls + 32 * vk * L7 + 16 * wr, L7);
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          acc1[kb] = mfma16(fdr, frag_tr_split(Ss + 32 * vk * LD + 16 * kb, LD), acc1[kb]);
+          acc2[kb] = mfma16(fdl, frag_tr_split(Gs_ + 32 * vk * LD + 16 * kb, LD), acc2[kb]);
+        }
       }
     }
   }
-  // <S, dSn>: wave sums in a fixed shuffle order, then the four wave partials
+  // <S, dSn>: wave sums, then the eight wave partials in a fixed order
   {
     const float x = sum4g(sum16(sds));
     if (l == 0) red[w] = x;
   }
   __syncthreads();
-  // ---- C x C terms, rows r = 16w + 4grp + e ----
+
+  // ---- C x C terms, rows r = 16 wr + 4 grp + e ----
   T* dAs = Ss;              // bf16 dA (64 x 64)
   T* T1s = Ss + 64 * L7;    // bf16 A^T dA
   T* dPG = Gs_;             // bf16 dP o Gamma
   T* DMs = Gs_ + 64 * L7;   // bf16 dM o beta Gamma
-  float rowacc[4] = {0.f, 0.f, 0.f, 0.f};  // dgamma row terms of this lane's rows
-  float dbacc[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta row terms
+  float rowacc[4] = {0.f, 0.f, 0.f, 0.f};  // dgamma row terms (E on side 0, E2 on side 1)
+  float dbacc[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta row terms (side 1)
+  if (!hi) {
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * wr + 4 * grp);
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    float cs = 0.f;
+    for (int cb = 0; cb < 4; ++cb) {
+      float cs = 0.f;
+      const float gi = gam[16 * cb + col];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
-      const float dpv = (i <= r) ? a.scale * dP[cb][e] : 0.f;
-      const float E = dpv * pv[cb][e];
-      rowacc[e] += E;
-      cs += E;
-      const float gm = (i <= r) ? __expf(gam[r] - gam[i]) : 0.f;
-      dPG[r * L7 + i] = from_f<T>(dpv * gm);
-      dAs[r * L7 + i] = from_f<T>(i <= r ? dA[cb][e] : 0.f);
-    }
-    cs = sum4g(cs);
-    if (grp == 0) colE[w][16 * cb + col] = cs;
-  }
-  __syncthreads();
-  // dgamma -= column sums of dP o P (fixed order over waves)
-  if (tid < 64) {
-    dgam[tid] -= colE[0][tid] + colE[1][tid] + colE[2][tid] + colE[3][tid];
-  }
-  // T1 = A^T dA (rows 16w), and the (dP o Gamma) products
-  f32x4 dQ2[8], dK2[8];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    dQ2[x] = zero4();
-    dK2[x] = zero4();
-  }
-#pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
-      acc = mfma16(frag_tr_split(As + 32 * mk * L7 + 16 * w, L7),
-                   frag_tr_split(dAs + 32 * mk * L7 + 16 * ib, L7), acc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) T1s[(16 * w + 4 * grp + e) * L7 + 16 * ib + col] = from_f<T>(acc[e]);
-  }
-#pragma unroll
-  for (int ik = 0; ik < 2; ++ik) {
-    const x8 fa = frag_row_split(dPG + 16 * w * L7 + 32 * ik, L7);
-    const x8 fb = frag_tr_split(dPG + 32 * ik * L7 + 16 * w, L7);
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      dQ2[kb] = mfma16(fa, frag_tr_split(Ks + 32 * ik * LD + 16 * kb, LD), dQ2[kb]);
-      dK2[kb] = mfma16(fb, frag_tr_split(Qs + 32 * ik * LD + 16 * kb, LD), dK2[kb]);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wr + 4 * grp + e, i = 16 * cb + col;
+        const bool keep = i <= r;
+        const float dpv = keep ? a.scale * accB[cb][e] : 0.f;
+        const float E = dpv * pn[cb][e];
+        rowacc[e] += E;
+        cs += E;
+        dPG[r * L7 + i] = from_f<T>(dpv * __expf(keep ? gr[e] - gi : -INFINITY));
+        dAs[r * L7 + i] = from_f<T>(keep ? accA[cb][e] : 0.f);
+      }
+      cs = sum4g(cs);
+      if (grp == 0) colE[wr][16 * cb + col] = cs;
     }
   }
   __syncthreads();
-  // dM = strict_lower(-T1 A^T), rows 16w
+  // dgamma -= column sums of dP o P (fixed order over row blocks)
+  if (tid < 64) dgam[tid] -= colE[0][tid] + colE[1][tid] + colE[2][tid] + colE[3][tid];
+  // side 0: T1 = A^T dA (rows 16 wr) and dQ2 = (dP o Gamma) K;
+  // side 1: dK2 = (dP o Gamma)^T Q
+  f32x4 acc3[8];
 #pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    f32x4 acc = zero4();
+  for (int x = 0; x < 8; ++x) acc3[x] = zero4();
+  if (!hi) {
 #pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
-      acc = mfma16(frag_row_split(T1s + 16 * w * L7 + 32 * mk, L7),
-                   frag_row_split(As + 16 * ib * L7 + 32 * mk, L7), acc);
-    float cs = 0.f;
+    for (int ib = 0; ib < 4; ++ib) {
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * grp + e, i = 16 * ib + col;
-      const float dm = (i < r) ? -acc[e] : 0.f;
-      // M = beta_r N, N = (k_r . k_i) Gamma_ri
-      dbacc[e] += dm * nv[ib][e];
-      const float E2 = dm * bet[r] * nv[ib][e];
-      rowacc[e] += E2;
-      cs += E2;
-      const float gm = (i < r) ? __expf(gam[r] - gam[i]) : 0.f;
-      DMs[r * L7 + i] = from_f<T>(dm * bet[r] * gm);
+      for (int mk = 0; mk < 2; ++mk)
+        acc = mfma16(frag_tr_split(As + 32 * mk * L7 + 16 * wr, L7),
+                     frag_tr_split(dAs + 32 * mk * L7 + 16 * ib, L7), acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) T1s[(16 * wr + 4 * grp + e) * L7 + 16 * ib + col] = from_f<T>(acc[e]);
     }
-    cs = sum4g(cs);
-    if (grp == 0) colE[w][16 * ib + col] = cs;
+#pragma unroll
+    for (int ik = 0; ik < 2; ++ik) {
+      const x8 fa = frag_row_split(dPG + 16 * wr * L7 + 32 * ik, L7);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        acc3[kb] = mfma16(fa, frag_tr_split(Ks + 32 * ik * LD + 16 * kb, LD), acc3[kb]);
+    }
+  } else {
+#pragma unroll
+    for (int ik = 0; ik < 2; ++ik) {
+      const x8 fb = frag_tr_split(dPG + 32 * ik * L7 + 16 * wr, L7);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        acc3[kb] = mfma16(fb, frag_tr_split(Qs + 32 * ik * LD + 16 * kb, LD), acc3[kb]);
+    }
+  }
+  __syncthreads();
+  // side 1: dM = strict_lower(-T1 A^T), rows 16 wr
+  if (hi) {
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * wr + 4 * grp);
+    const f32x4 br = *reinterpret_cast<const f32x4*>(bet + 16 * wr + 4 * grp);
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk)
+        acc = mfma16(frag_row_split(T1s + 16 * wr * L7 + 32 * mk, L7),
+                     frag_row_split(As + 16 * ib * L7 + 32 * mk, L7), acc);
+      float cs = 0.f;
+      const float gi = gam[16 * ib + col];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wr + 4 * grp + e, i = 16 * ib + col;
+        const bool keep = i < r;
+        const float dm = keep ? -acc[e] : 0.f;
+        // M = beta_r N, N = (k_r . k_i) Gamma_ri
+        dbacc[e] += dm * pn[ib][e];
+        const float E2 = dm * br[e] * pn[ib][e];
+        rowacc[e] += E2;
+        cs += E2;
+        DMs[r * L7 + i] = from_f<T>(dm * br[e] * __expf(keep ? gr[e] - gi : -INFINITY));
+      }
+      cs = sum4g(cs);
+      if (grp == 0) colE[wr][16 * ib + col] = cs;
+    }
   }
   __syncthreads();
   if (tid < 64) dgam[tid] -= colE[0][tid] + colE[1][tid] + colE[2][tid] + colE[3][tid];
-  // dK3 = D K + D^T K
+
+  // ---- final rows ----
+  float rs1[4] = {0.f, 0.f, 0.f, 0.f}, rs2[4] = {0.f, 0.f, 0.f, 0.f};
+  float dxv[8][4];
+  if (hi) {
+    // dK3 = D K + D^T K with D = dM o beta Gamma
 #pragma unroll
-  for (int ik = 0; ik < 2; ++ik) {
-    const x8 fa = frag_row_split(DMs + 16 * w * L7 + 32 * ik, L7);
-    const x8 fb = frag_tr_split(DMs + 32 * ik * L7 + 16 * w, L7);
+    for (int ik = 0; ik < 2; ++ik) {
+      const x8 fa = frag_row_split(DMs + 16 * wr * L7 + 32 * ik, L7);
+      const x8 fb = frag_tr_split(DMs + 32 * ik * L7 + 16 * wr, L7);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const x8 fk = frag_tr_split(Ks + 32 * ik * LD + 16 * kb, LD);
+        acc3[kb] = mfma16(fa, fk, acc3[kb]);
+        acc3[kb] = mfma16(fb, fk, acc3[kb]);
+      }
+    }
+    // dk = dK2 + dK3 + diag(e^{gL-gamma}) dKs + diag(beta e^gamma) dX, with
+    // dX = -dR S^T; row sums k . dX (rs1) and k . dKs (rs2)
+    const f32x4 dlr = *reinterpret_cast<const f32x4*>(dl + 16 * wr + 4 * grp);
+    const f32x4 bxr = *reinterpret_cast<const f32x4*>(bex + 16 * wr + 4 * grp);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const x8 fk = frag_tr_split(Ks + 32 * ik * LD + 16 * kb, LD);
-      dK2[kb] = mfma16(fa, fk, dK2[kb]);
-      dK2[kb] = mfma16(fb, fk, dK2[kb]);
+      const f32x4 kd = frag_d4(Ks, LD, 16 * wr, 16 * kb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dx = -acc1[kb][e];
+        rs1[e] += kd[e] * dx;
+        rs2[e] += kd[e] * acc2[kb][e];
+        dxv[kb][e] = acc3[kb][e] + dlr[e] * acc2[kb][e] + bxr[e] * dx;
+      }
+    }
+  } else {
+    // dq = scale diag(e^gamma) dQ1 + dQ2; row sums q . dQ1 (rs1)
+    const f32x4 er = *reinterpret_cast<const f32x4*>(eg + 16 * wr + 4 * grp);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const f32x4 qd = frag_d4(Qs, LD, 16 * wr, 16 * kb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rs1[e] += qd[e] * acc1[kb][e];
+        dxv[kb][e] = a.scale * er[e] * acc1[kb][e] + acc3[kb][e];
+      }
     }
   }
-
-  // ---- final rows: dq, dk, dbeta, dgamma ----
-  float qsd[4] = {0.f, 0.f, 0.f, 0.f}, kdx[4] = {0.f, 0.f, 0.f, 0.f}, fF[4] = {0.f, 0.f, 0.f, 0.f};
-  float dqv[8][4], dkv[8][4];
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    const f32x4 qd = frag_d4(Qs, LD, 16 * w, 16 * kb), kd = frag_d4(Ks, LD, 16 * w, 16 * kb);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * grp + e;
-      const float qv = qd[e], kv = kd[e];
-      const float dxv = -dX[kb][e];  // dX = -dR S^T
-      qsd[e] += qv * dQ1[kb][e];
-      kdx[e] += kv * dxv;
-      fF[e] += kv * dKs[kb][e];
-      dqv[kb][e] = a.scale * eg[r] * dQ1[kb][e] + dQ2[kb][e];
-      dkv[kb][e] = dK2[kb][e] + dl[r] * dKs[kb][e] + bex[r] * dxv;
-    }
-  }
-  float Fsum_part = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int r = 16 * w + 4 * grp + e;
-    qsd[e] = sum16(qsd[e]);
-    kdx[e] = sum16(kdx[e]);
-    fF[e] = sum16(fF[e]) * dl[r];
+    rs1[e] = sum16(rs1[e]);
+    rs2[e] = sum16(rs2[e]);
     rowacc[e] = sum16(rowacc[e]);
     dbacc[e] = sum16(dbacc[e]);
-    if (r >= Cc) fF[e] = 0.f;
-    Fsum_part += fF[e];  // same value in all 16 lanes of the group
   }
-  // F summed over every row of the chunk, in a fixed order
-  if (col == 0) fsum[w][grp] = Fsum_part;
-  __syncthreads();
-  if (col == 0) {
+  float Fsum_part = 0.f;
+  if (!hi) {
+    if (col == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wr + 4 * grp + e;
+        rowq[r] = a.scale * eg[r] * rs1[e] + rowacc[e];
+      }
+    }
+  } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * grp + e;
-      float dgv = a.scale * eg[r] * qsd[e] + rowacc[e] + bex[r] * kdx[e] - fF[e];
+      const int r = 16 * wr + 4 * grp + e;
+      rs2[e] = (r < Cc) ? rs2[e] * dl[r] : 0.f;  // F_r
+      Fsum_part += rs2[e];
+    }
+    if (col == 0) fsum[wr][grp] = Fsum_part;
+  }
+  // dq (side 0) / dk (side 1) rows: fp32 partials straight from registers, or
+  // staged row-major in the free S / dSn tiles for 16-byte stores
+  if (a.partial) {
+    float* dst = reinterpret_cast<float*>(hi ? a.dk : a.dq);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wr + 4 * grp + e, key = 16 * kb + col;
+        if (r < Cc) dst[((t0 + r) * a.Hv + h) * kDim + key] = dxv[kb][e];
+      }
+  }
+  __syncthreads();  // every wave is done with DMs, T1s, dAs; rowq and fsum are in
+  if (!a.partial) {
+    T* stage = hi ? Gs_ : Ss;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        stage[(16 * wr + 4 * grp + e) * LD + 16 * kb + col] = from_f<T>(dxv[kb][e]);
+  }
+  if (hi && col == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * wr + 4 * grp + e;
+      float dgv = rowq[r] + rowacc[e] + bex[r] * rs1[e] - rs2[e];
       if (r == Cc - 1) {
         float Fs = 0.f;
         for (int ww = 0; ww < 4; ++ww)
           for (int gg = 0; gg < 4; ++gg) Fs += fsum[ww][gg];
-        const float ss = (red[0] + red[1]) + (red[2] + red[3]);
+        const float ss = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
         dgv += Fs + __expf(gL) * ss;
       }
       dgam[r] += dgv;
       const float db = dbv[0][r] + dbv[1][r] + dbv[2][r] + dbv[3][r] + dbv[4][r] + dbv[5][r] +
-                       dbv[6][r] + dbv[7][r] + eg[r] * kdx[e] + dbacc[e];
+                       dbv[6][r] + dbv[7][r] + eg[r] * rs1[e] + dbacc[e];
       if (r < Cc) reinterpret_cast<T*>(a.dbeta)[(t0 + r) * a.Hv + h] = from_f<T>(db);
     }
   }
-  // dq, dk rows
-  if (a.partial) {
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * grp + e, key = 16 * kb + col;
-        if (r < Cc) {
-          reinterpret_cast<float*>(a.dq)[((t0 + r) * a.Hv + h) * kDim + key] = dqv[kb][e];
-          reinterpret_cast<float*>(a.dk)[((t0 + r) * a.Hv + h) * kDim + key] = dkv[kb][e];
-        }
-      }
-  } else {
-    // staged row-major in the (now free) S / dSn tiles, then 16-byte stores
-    T* dqs = Ss;
-    T* dks = Gs_;
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + 4 * grp + e, key = 16 * kb + col;
-        dqs[r * LD + key] = from_f<T>(dqv[kb][e]);
-        dks[r * LD + key] = from_f<T>(dkv[kb][e]);
-      }
-    __syncthreads();
-    tile_from_lds<T, 128, 256>(reinterpret_cast<T*>(a.dq) + (t0 * a.Hq + hq) * kDim,
-                               (int64_t)a.Hq * kDim, dqs, LD, Cc);
-    tile_from_lds<T, 128, 256>(reinterpret_cast<T*>(a.dk) + (t0 * a.Hq + hq) * kDim,
-                               (int64_t)a.Hq * kDim, dks, LD, Cc);
-  }
   __syncthreads();
+  if (!a.partial) {
+    tile_from_lds<T, 128, 512>(reinterpret_cast<T*>(a.dq) + (t0 * a.Hq + hq) * kDim,
+                               (int64_t)a.Hq * kDim, Ss, LD, Cc);
+    tile_from_lds<T, 128, 512>(reinterpret_cast<T*>(a.dk) + (t0 * a.Hq + hq) * kDim,
+                               (int64_t)a.Hq * kDim, Gs_, LD, Cc);
+  }
   // dg = reverse cumsum of dgamma over the valid rows: lane l scans row 63 - l
   if (w == 0) {
     const int r = 63 - l;
@@ -930,7 +985,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   ga.N = pl.N; ga.T = p->T; ga.Hq = p->Hq; ga.Hv = p->Hv; ga.nc_dense = pl.nc_dense;
   ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale; ga.partial = partial ? 1 : 0;
   if (pl.total_chunks > 0)
-    GDR_LAUNCH("grad", grad_kernel<T>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(256), st, ga);
+    GDR_LAUNCH("grad", grad_kernel<T>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(512), st, ga);
   // B6
   if (partial) {
     const int64_t Ttot = (int64_t)p->B * p->T;
