@@ -134,6 +134,9 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
     }
   };
 
+  // the initial state has arrived before the loop (else the loop-entry merge
+  // makes the first use of Gs wait for the prefetch as well)
+  __builtin_amdgcn_s_waitcnt(0);
   if (sr.c0 < sr.c1) prefetch(sr.c1 - 1);
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
     __syncthreads();

@@ -282,15 +282,20 @@ template <typename T>
 __device__ __forceinline__ void p_tiles(const T* Qs, const T* Ks, int ldq, T* Ps, int ldp,
                                         const float* gam, int w) {
   const int l = lane_id(), grp = l >> 4, col = l & 15;
-  // (row block, column block) per wave and slot; -1 = no tile
-  constexpr int tab[4][3][2] = {{{0, 0}, {2, 0}, {3, 3}},
-                                {{1, 0}, {1, 1}, {3, 0}},
-                                {{2, 1}, {2, 2}, {-1, -1}},
-                                {{3, 1}, {3, 2}, {-1, -1}}};
+  // (row block, column block) per wave and slot, 4 bits each (rb * 4 + cb),
+  // 16 bits per wave: w0 (0,0) (2,0) (3,3); w1 (1,0) (1,1) (3,0);
+  // w2 (2,1) (2,2); w3 (3,1) (3,2).  Decoded with scalar shifts of a
+  // wave-uniform index (a table in memory would cost a load per chunk).
+  constexpr uint64_t code = 0x0000ull | (0x8ull << 4) | (0xFull << 8) |
+                            ((0x4ull | (0x5ull << 4) | (0xCull << 8)) << 16) |
+                            ((0x9ull | (0xAull << 4)) << 32) |
+                            ((0xDull | (0xEull << 4)) << 48);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
-    const int rb = tab[w][t][0], cb = tab[w][t][1];
-    if (rb < 0) break;
+    if (t == 2 && wu >= 2) break;
+    const int x = (int)((code >> (16 * wu + 4 * t)) & 15);
+    const int rb = x >> 2, cb = x & 3;
     f32x4 acc = zero4();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -301,7 +306,8 @@ __device__ __forceinline__ void p_tiles(const T* Qs, const T* Ks, int ldq, T* Ps
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * rb + 4 * grp + e, i = 16 * cb + col;
-      const float pv = (rb != cb || i <= r) ? acc[e] * __expf(gr[e] - gi) : 0.f;
+      // masked entries take exp(-inf) = 0 (an unconditional exponential)
+      const float pv = acc[e] * __expf((rb != cb || i <= r) ? gr[e] - gi : -INFINITY);
       Ps[r * ldp + i] = from_f<T>(pv);
     }
   }
@@ -309,15 +315,14 @@ __device__ __forceinline__ void p_tiles(const T* Qs, const T* Ks, int ldq, T* Ps
 
 template <typename T>
 __device__ __forceinline__ void p_zero_tiles(T* Ps, int ldp) {
-  const int tid = threadIdx.x;  // 256 threads, 2 tiles of 256 elements
-  for (int x = tid; x < 512; x += 256) {
+  const int tid = threadIdx.x;  // 2 tiles of 256 elements, any block size
+  for (int x = tid; x < 512; x += blockDim.x) {
     const int t = x >> 8, e = x & 255;
     const int r = 16 * (2 * t) + (e >> 4), i = 16 * (2 * t + 1) + (e & 15);
     Ps[r * ldp + i] = from_f<T>(0.f);
   }
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (fixed combination order).
 // ---- cross-lane sums on the VALU (no LDS round trips) ----------------------
 // DPP moves within rows of 16 lanes: quad_perm [1,0,3,2] (0xB1) and
 // [2,3,0,1] (0x4E), row_half_mirror (0x141), row_mirror (0x140).
@@ -349,6 +354,7 @@ __device__ __forceinline__ float sum4g(float v) {
   return __builtin_bit_cast(float, (int)p32[0]) + __builtin_bit_cast(float, (int)p32[1]);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (fixed combination order).
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   const int l = lane_id();
 #pragma unroll

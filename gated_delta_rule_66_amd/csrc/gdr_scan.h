@@ -179,6 +179,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
     }
   };
 
+  __builtin_amdgcn_s_waitcnt(0);  // the initial state is in (see scan_out_kernel)
   if (sr.c0 < sr.c1) prefetch(sr.c0);
   for (int c = sr.c0; c < sr.c1; ++c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
@@ -424,6 +425,220 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
 template <typename T, int VB, int MODE>
 __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_STATE)) ? 2 : 1) void scan_kernel(ScanArgs a) {
   scan_body<T, VB, MODE>(a, xcd_block(blockIdx.x, gridDim.x));
+}
+
+// Forward output pass with specialized waves (one 64-column block per
+// workgroup, 8 waves).  Waves 0-3 run the state chain of chunk c -- K S, R,
+// Delta, the state update -- and the P tiles of chunk c; waves 4-7 form the
+// output of chunk c-1 from what the state waves left in LDS: the chunk-start
+// state and Delta as MFMA operand registers (copied lane for lane), and P.
+// The output work is thus off the state chain's critical path, and two waves
+// share each SIMD.  Chunk tiles are double-buffered where both roles read
+// them (q, k, P, e^gamma, the operand copies).
+template <typename T>
+__global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
+  typedef typename VT<T>::x8 x8;
+  constexpr int LD = 136;   // q / k tile leading dimension
+  constexpr int LDV = 72;   // v tile (64 columns)
+  constexpr int LDA = 72;   // A and P tiles
+  __shared__ __align__(16) T Qs[2][64 * LD];
+  __shared__ __align__(16) T Ks[2][64 * LD];
+  __shared__ __align__(16) T Vs[64 * LDV];
+  __shared__ __align__(16) T As[64 * LDA];
+  __shared__ __align__(16) T Ps[2][64 * LDA];
+  __shared__ __align__(16) x8 Xs[2][4][4][64];  // S_c operands: [buf][column block][k block][lane]
+  __shared__ __align__(16) x8 Xd[2][4][2][64];  // Delta_c operands
+  __shared__ __align__(16) float gam[64], bet[64], bex[64], dl[64], eg[2][64];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  const bool outw = w >= 4;
+  const int wq = w & 3;  // the wave's 16-column block (both roles)
+  const int bid = xcd_block(blockIdx.x, gridDim.x);
+  const int vs = bid & 1;
+  const int up = bid >> 1;
+  const int p = up % a.P, unit = up / a.P;
+  const int n = unit / a.Hv, h = unit % a.Hv;
+  const int G = a.Hv / a.Hq, hq = h / G;
+  const SeqInfo s = seq_info(a.cu, n, a.T);
+  const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
+  const SegRange sr = seg_range(nch, a.P, p);
+  if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;  // empty segment
+  const int cb0 = 64 * vs;
+  const int cw0 = 16 * wq;
+  const int64_t KV = (int64_t)kDim * kDim;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* v = reinterpret_cast<const T*>(a.v);
+  const T* Ag = reinterpret_cast<const T*>(a.A);
+  const T* beta = reinterpret_cast<const T*>(a.beta);
+
+  // state waves: initial state
+  f32x4 S[8];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
+      float x = 0.f;
+      if (!outw) {
+        if (p == 0) {
+          if (a.h0) x = a.h0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)];
+        } else {
+          x = a.seg_start[((int64_t)unit * a.P + p) * KV + key * kDim + vc];
+        }
+      }
+      S[kb][e] = x;
+    }
+
+  // register prefetch of one chunk, spread over all 512 threads
+  TileRegs<128, 512> rq, rk;
+  TileRegs<64, 512> rv, ra;
+  float r_g = 0.f, r_gl = 0.f;
+  T r_b = from_f<T>(0.f);
+  auto prefetch = [&](int c) {
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+    tile_load<T, 128, 512>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
+    tile_load<T, 128, 512>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
+    tile_load<T, 64, 512>(rv, v + (t0 * a.Hv + h) * kDim + cb0, (int64_t)a.Hv * kDim, Cc);
+    tile_load<T, 64, 512>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc);
+    if (tid < 64) {
+      r_g = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
+      r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
+      r_b = (tid < Cc) ? beta[(t0 + tid) * a.Hv + h] : from_f<T>(0.f);
+    }
+  };
+
+  // The initial state has arrived before the loop starts: otherwise the
+  // compiler, merging the loop entry with the back edge, waits for every
+  // outstanding load (the prefetch included) before the first use of S.
+  __builtin_amdgcn_s_waitcnt(0);
+  p_zero_tiles<T>(Ps[0], LDA);
+  p_zero_tiles<T>(Ps[1], LDA);
+  if (sr.c0 < sr.c1) prefetch(sr.c0);
+  // iteration it: state chain of chunk it (it < c1), output of chunk it-1
+  // (it > c0); the last iteration only drains the output
+  for (int it = sr.c0; it <= sr.c1; ++it) {
+    const int b = it & 1;
+    __syncthreads();  // iteration it-1 is done with every buffer rewritten here
+    if (it < sr.c1) {
+      tile_store<T, 128, 512>(Qs[b], LD, rq);
+      tile_store<T, 128, 512>(Ks[b], LD, rk);
+      tile_store<T, 64, 512>(Vs, LDV, rv);
+      tile_store<T, 64, 512>(As, LDA, ra);
+      if (tid < 64) {
+        const float bv = to_f(r_b);
+        const float e = __expf(r_g);
+        gam[tid] = r_g;
+        bet[tid] = bv;
+        eg[b][tid] = e;
+        bex[tid] = bv * e;
+        dl[tid] = __expf(r_gl - r_g);
+      }
+    }
+    __syncthreads();
+    if (it + 1 < sr.c1) prefetch(it + 1);
+
+    if (!outw) {
+      if (it < sr.c1) {
+        const float eLc = __expf(gam[63]);
+        x8 Sb[4];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2) {
+          Sb[kb2] = pack_split<T>(S[2 * kb2], S[2 * kb2 + 1]);
+          Xs[b][wq][kb2][l] = Sb[kb2];
+        }
+        // K S
+        f32x4 ks[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) ks[tb] = zero4();
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+            ks[tb] = mfma16(frag_row_split(Ks[b] + 16 * tb * LD + 32 * kb2, LD), Sb[kb2], ks[tb]);
+        // R = diag(beta) V - diag(beta e^gamma) K S
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(bet + 16 * tb + 4 * grp);
+          const f32x4 bx = *reinterpret_cast<const f32x4*>(bex + 16 * tb + 4 * grp);
+          const f32x4 vd = frag_d4(Vs, LDV, 16 * tb, cw0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ks[tb][e] = bt[e] * vd[e] - bx[e] * ks[tb][e];
+        }
+        // Delta = A R
+        const x8 Rb0 = pack_split<T>(ks[0], ks[1]), Rb1 = pack_split<T>(ks[2], ks[3]);
+        f32x4 dd[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          f32x4 acc = mfma16(frag_row_split(As + 16 * tb * LDA, LDA), Rb0, zero4());
+          if (tb >= 2) acc = mfma16(frag_row_split(As + 16 * tb * LDA + 32, LDA), Rb1, acc);
+          dd[tb] = acc;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Xd[b][wq][kb][l] = pack_split<T>(dd[2 * kb], dd[2 * kb + 1]);
+        // P of this chunk for the output waves (tiles spread over the four state waves)
+        p_tiles<T>(Qs[b], Ks[b], LD, Ps[b], LDA, gam, wq);
+        // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) Delta
+        x8 Eb[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(dl + 32 * kt + 4 * grp);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(dl + 32 * kt + 16 + 4 * grp);
+          Eb[kt] = pack_split<T>(dd[2 * kt] * d0, dd[2 * kt + 1] * d1);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          f32x4 acc = S[kb] * eLc;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) acc = mfma16(frag_tr_split(Ks[b] + 32 * kt * LD + 16 * kb, LD), Eb[kt], acc);
+          S[kb] = acc;
+        }
+      }
+    } else if (it > sr.c0) {
+      // output of chunk c = it - 1:
+      //   O^T = (Q S)^T diag(e^gamma) + Delta^T P^T, times scale
+      const int c = it - 1, bo = c & 1;
+      const int64_t t0 = s.start + (int64_t)kChunk * c;
+      const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+      f32x4 qsT[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) qsT[rb] = zero4();
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        const x8 sb = Xs[bo][wq][kb2][l];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          qsT[rb] = mfma16(sb, frag_row_split(Qs[bo] + 16 * rb * LD + 32 * kb2, LD), qsT[rb]);
+      }
+      const x8 Db0 = Xd[bo][wq][0][l], Db1 = Xd[bo][wq][1][l];
+      const int ld_o = a.Hv * kDim * (int)sizeof(T);
+      const __amdgpu_buffer_rsrc_t ors =
+          buf_rsrc(reinterpret_cast<T*>(a.o) + (t0 * a.Hv + h) * kDim + cb0, (int64_t)Cc * ld_o);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4 acc = qsT[rb] * eg[bo][16 * rb + col];
+        acc = mfma16(Db0, frag_row_split(Ps[bo] + 16 * rb * LDA, LDA), acc);
+        if (rb >= 2) acc = mfma16(Db1, frag_row_split(Ps[bo] + 16 * rb * LDA + 32, LDA), acc);
+        acc *= a.scale;
+        const typename VT<T>::x4 ov{from_f<T>(acc[0]), from_f<T>(acc[1]), from_f<T>(acc[2]),
+                                    from_f<T>(acc[3])};
+        // rows past the chunk's end fall outside the buffer range: dropped
+        buf_store8(ors, (16 * rb + col) * ld_o + (cw0 + 4 * grp) * (int)sizeof(T),
+                   __builtin_bit_cast(u32x2, ov));
+      }
+    }
+  }
+
+  if (!outw && a.ht && p == sr.p_last) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
+        a.ht[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = S[kb][e];
+      }
+  }
 }
 
 // Pass 2: chain the segment start states of one (unit, 16-column block).
