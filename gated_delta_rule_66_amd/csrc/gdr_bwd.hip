@@ -95,25 +95,32 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
   const T* beta = reinterpret_cast<const T*>(a.beta);
   const int cw0 = 16 * VB * w;
 
+  // gradient entering the segment's end: dht (last segment) or the chained
+  // value; every load is issued before the first is used (null reads zeros)
   f32x4 Gs[8][VB];
+  if (MODE == MODE_AUG && isT) {
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
+      for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 16 * kb + 4 * grp + e, lc = cw0 + 16 * vb + col;
-        float x = 0.f;
-        if (MODE == MODE_AUG && isT) {
-          x = (key == cb0 + lc) ? 1.f : 0.f;
-        } else if (p == sr.p_last) {
-          const int vc = vcol0 + lc;
-          if (a.dht) x = a.dht[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)];
-        } else {
-          x = a.seg_start[((int64_t)unit * a.P + p) * KV + key * kDim + vcol0 + lc];
+        for (int e = 0; e < 4; ++e)
+          Gs[kb][vb][e] = (16 * kb + 4 * grp + e == cb0 + cw0 + 16 * vb + col) ? 1.f : 0.f;
+  } else {
+    const float* src = (p == sr.p_last) ? (a.dht ? a.dht + unit * KV : nullptr)
+                                        : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+    const bool vf = (p == sr.p_last) && a.svf;
+    const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
+          Gs[kb][vb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
         }
-        Gs[kb][vb][e] = x;
-      }
+  }
 
   TileRegs<128, 256> rq, rk;
   TileRegs<CW, 256> rd;

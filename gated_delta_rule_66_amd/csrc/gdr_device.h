@@ -209,6 +209,10 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, int off) 
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t rs, int off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, rs, off, 0, 0);
 }
@@ -219,26 +223,28 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t rs, int off, u
 
 // Rows [0, rows) of the tile load; rows past that read as zero.  Row r of the
 // tile starts r * gstride elements after g (gstride >= COLS).
+// `t0` is the calling thread's index among the NT cooperating threads.
 template <typename T, int COLS, int NT>
 __device__ __forceinline__ void tile_load(TileRegs<COLS, NT>& t, const T* g, int64_t gstride,
-                                          int rows) {
+                                          int rows, int t0 = threadIdx.x) {
   constexpr int PR = TileRegs<COLS, NT>::PER_ROW;
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc(g, (int64_t)rows * gstride * (int64_t)sizeof(T));
   const int gs = (int)gstride * (int)sizeof(T);
 #pragma unroll
   for (int i = 0; i < TileRegs<COLS, NT>::N; ++i) {
-    const int x = threadIdx.x + i * NT;
+    const int x = t0 + i * NT;
     const int r = x / PR, c8 = (x % PR) * 8;
     t.r[i] = buf_load16(rs, r * gs + c8 * (int)sizeof(T));
   }
 }
 
 template <typename T, int COLS, int NT>
-__device__ __forceinline__ void tile_store(T* lds, int ld, const TileRegs<COLS, NT>& t) {
+__device__ __forceinline__ void tile_store(T* lds, int ld, const TileRegs<COLS, NT>& t,
+                                           int t0 = threadIdx.x) {
   constexpr int PR = TileRegs<COLS, NT>::PER_ROW;
 #pragma unroll
   for (int i = 0; i < TileRegs<COLS, NT>::N; ++i) {
-    const int x = threadIdx.x + i * NT;
+    const int x = t0 + i * NT;
     const int r = x / PR, c8 = (x % PR) * 8;
     *reinterpret_cast<uint4*>(lds + r * ld + c8) = t.r[i];
   }

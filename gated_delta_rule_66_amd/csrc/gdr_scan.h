@@ -429,9 +429,10 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
 
 // Forward output pass with specialized waves (one 64-column block per
 // workgroup, 8 waves).  Waves 0-3 run the state chain of chunk c -- K S, R,
-// Delta, the state update -- and the P tiles of chunk c; waves 4-7 form the
-// output of chunk c-1 from what the state waves left in LDS: the chunk-start
-// state and Delta as MFMA operand registers (copied lane for lane), and P.
+// Delta, the state update; waves 4-7 form the output of chunk c-1 from what
+// the state waves left in LDS (the chunk-start state and Delta as MFMA
+// operand registers, copied lane for lane) and the P tiles they computed
+// themselves one iteration earlier, then the P tiles of chunk c.
 // The output work is thus off the state chain's critical path, and two waves
 // share each SIMD.  Chunk tiles are double-buffered where both roles read
 // them (q, k, P, e^gamma, the operand copies).
@@ -490,22 +491,25 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
       S[kb][e] = x;
     }
 
-  // register prefetch of one chunk, spread over all 512 threads
-  TileRegs<128, 512> rq, rk;
-  TileRegs<64, 512> rv, ra;
+  // register prefetch of one chunk by the output waves (256 threads): the
+  // vector-memory issue of a chunk's tiles takes hundreds of cycles, which
+  // the state chain does not wait for
+  const int otid = tid - 256;
+  TileRegs<128, 256> rq, rk;
+  TileRegs<64, 256> rv, ra;
   float r_g = 0.f, r_gl = 0.f;
   T r_b = from_f<T>(0.f);
   auto prefetch = [&](int c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
-    tile_load<T, 128, 512>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
-    tile_load<T, 128, 512>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc);
-    tile_load<T, 64, 512>(rv, v + (t0 * a.Hv + h) * kDim + cb0, (int64_t)a.Hv * kDim, Cc);
-    tile_load<T, 64, 512>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc);
-    if (tid < 64) {
-      r_g = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
+    tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
+    tile_load<T, 128, 256>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
+    tile_load<T, 64, 256>(rv, v + (t0 * a.Hv + h) * kDim + cb0, (int64_t)a.Hv * kDim, Cc, otid);
+    tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc, otid);
+    if (otid < 64) {
+      r_g = a.gcum[(t0 + min(otid, Cc - 1)) * a.Hv + h];
       r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
-      r_b = (tid < Cc) ? beta[(t0 + tid) * a.Hv + h] : from_f<T>(0.f);
+      r_b = (otid < Cc) ? beta[(t0 + otid) * a.Hv + h] : from_f<T>(0.f);
     }
   };
 
@@ -515,29 +519,29 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   p_zero_tiles<T>(Ps[0], LDA);
   p_zero_tiles<T>(Ps[1], LDA);
-  if (sr.c0 < sr.c1) prefetch(sr.c0);
+  if (outw && sr.c0 < sr.c1) prefetch(sr.c0);
   // iteration it: state chain of chunk it (it < c1), output of chunk it-1
   // (it > c0); the last iteration only drains the output
   for (int it = sr.c0; it <= sr.c1; ++it) {
     const int b = it & 1;
     __syncthreads();  // iteration it-1 is done with every buffer rewritten here
-    if (it < sr.c1) {
-      tile_store<T, 128, 512>(Qs[b], LD, rq);
-      tile_store<T, 128, 512>(Ks[b], LD, rk);
-      tile_store<T, 64, 512>(Vs, LDV, rv);
-      tile_store<T, 64, 512>(As, LDA, ra);
-      if (tid < 64) {
+    if (outw && it < sr.c1) {
+      tile_store<T, 128, 256>(Qs[b], LD, rq, otid);
+      tile_store<T, 128, 256>(Ks[b], LD, rk, otid);
+      tile_store<T, 64, 256>(Vs, LDV, rv, otid);
+      tile_store<T, 64, 256>(As, LDA, ra, otid);
+      if (otid < 64) {
         const float bv = to_f(r_b);
         const float e = __expf(r_g);
-        gam[tid] = r_g;
-        bet[tid] = bv;
-        eg[b][tid] = e;
-        bex[tid] = bv * e;
-        dl[tid] = __expf(r_gl - r_g);
+        gam[otid] = r_g;
+        bet[otid] = bv;
+        eg[b][otid] = e;
+        bex[otid] = bv * e;
+        dl[otid] = __expf(r_gl - r_g);
       }
     }
     __syncthreads();
-    if (it + 1 < sr.c1) prefetch(it + 1);
+    if (outw && it + 1 < sr.c1) prefetch(it + 1);
 
     if (!outw) {
       if (it < sr.c1) {
@@ -577,8 +581,6 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) Xd[b][wq][kb][l] = pack_split<T>(dd[2 * kb], dd[2 * kb + 1]);
-        // P of this chunk for the output waves (tiles spread over the four state waves)
-        p_tiles<T>(Qs[b], Ks[b], LD, Ps[b], LDA, gam, wq);
         // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) Delta
         x8 Eb[2];
 #pragma unroll
@@ -595,7 +597,8 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
           S[kb] = acc;
         }
       }
-    } else if (it > sr.c0) {
+    } else {
+      if (it > sr.c0) {
       // output of chunk c = it - 1:
       //   O^T = (Q S)^T diag(e^gamma) + Delta^T P^T, times scale
       const int c = it - 1, bo = c & 1;
@@ -627,6 +630,9 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
         buf_store8(ors, (16 * rb + col) * ld_o + (cw0 + 4 * grp) * (int)sizeof(T),
                    __builtin_bit_cast(u32x2, ov));
       }
+      }
+      // P of chunk it for the next iteration (tiles spread over the four waves)
+      if (it < sr.c1) p_tiles<T>(Qs[b], Ks[b], LD, Ps[b], LDA, gam, wq);
     }
   }
 
