@@ -137,27 +137,32 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
   const T* beta = reinterpret_cast<const T*>(a.beta);
   const int cw0 = 16 * VB * w;  // this wave's first column inside the block
 
-  // ---- initial state ----
+  // ---- initial state: h0 (segment 0) or the chained segment start; every
+  // load is issued before the first is used (a null source reads zeros) ----
   f32x4 S[8][VB];
+  if (MODE == MODE_AUG && isT) {
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
+      for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 16 * kb + 4 * grp + e;
-        const int lc = cw0 + 16 * vb + col;  // local column
-        float x = 0.f;
-        if (MODE == MODE_AUG && isT) {
-          x = (key == cb0 + lc) ? 1.f : 0.f;
-        } else if (p == 0) {
-          const int vc = vcol0 + lc;
-          if (a.h0) x = a.h0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)];
-        } else {
-          x = a.seg_start[((int64_t)unit * a.P + p) * KV + key * kDim + vcol0 + lc];
+        for (int e = 0; e < 4; ++e)
+          S[kb][vb][e] = (16 * kb + 4 * grp + e == cb0 + cw0 + 16 * vb + col) ? 1.f : 0.f;
+  } else {
+    const float* src = (p == 0) ? (a.h0 ? a.h0 + unit * KV : nullptr)
+                                : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+    const bool vf = (p == 0) && a.svf;
+    const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
+          S[kb][vb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
         }
-        S[kb][vb][e] = x;
-      }
+  }
 
   // ---- register prefetch of one chunk ----
   TileRegs<128, 256> rq, rk;
@@ -473,23 +478,23 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
   const T* Ag = reinterpret_cast<const T*>(a.A);
   const T* beta = reinterpret_cast<const T*>(a.beta);
 
-  // state waves: initial state
+  // initial state, every load issued before the first is used (a null source
+  // reads zeros); the source is block-uniform, so the output waves load it
+  // too (and never use it)
   f32x4 S[8];
+  {
+    const float* src = (p == 0) ? (a.h0 ? a.h0 + unit * KV : nullptr)
+                                : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+    const bool vf = (p == 0) && a.svf;
+    const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
-      float x = 0.f;
-      if (!outw) {
-        if (p == 0) {
-          if (a.h0) x = a.h0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)];
-        } else {
-          x = a.seg_start[((int64_t)unit * a.P + p) * KV + key * kDim + vc];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
+        S[kb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
       }
-      S[kb][e] = x;
-    }
+  }
 
   // register prefetch of one chunk by the output waves (256 threads): the
   // vector-memory issue of a chunk's tiles takes hundreds of cycles, which
