@@ -98,9 +98,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
-      float m = 0.f;
-      if (i < r) m = bet[r] * __expf(gam[r] - gam[i]) * acc[e];
-      Mf[r * LDM + i] = m;
+      // masked entries take exp(-inf) = 0 (an unconditional exponential)
+      Mf[r * LDM + i] = bet[r] * __expf(i < r ? gam[r] - gam[i] : -INFINITY) * acc[e];
     }
   }
   // blocks above the diagonal of the inverse are zero
