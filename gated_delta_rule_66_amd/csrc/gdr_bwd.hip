@@ -329,6 +329,301 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
   }
 }
 
+// B2 output pass (one 64-column block, 8 waves): waves 4-7 issue every
+// chunk load and tile store, waves 0-3 run the chain of dh_body unchanged, so
+// the vector-memory issue is off the chain.
+template <typename T>
+__device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
+  constexpr int VB = 1, MODE = MODE_OUT;
+  typedef typename VT<T>::x8 x8;
+  constexpr int CW = 64 * VB;
+  constexpr int LD = 136;
+  constexpr int LDV = CW + 8;
+  constexpr int LDA = 72;
+  constexpr bool OUT = (MODE == MODE_OUT);
+  __shared__ __align__(16) T Qs[64 * LD];
+  __shared__ __align__(16) T Ks[64 * LD];
+  __shared__ __align__(16) T Ds[64 * LDV];
+  __shared__ __align__(16) T As[64 * LDA];
+  __shared__ __align__(16) float gam[64], eg[64], bex[64], dl[64];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  const bool helper = w >= 4;
+  const int otid = tid - 256;  // index among the helper threads
+  const int vs = bid % a.nvs;
+  const int up = bid / a.nvs;
+  const int p = up % a.P, unit = up / a.P;
+  const int n = unit / a.Hv, h = unit % a.Hv;
+  const int G = a.Hv / a.Hq, hq = h / G;
+  const SeqInfo s = seq_info(a.cu, n, a.T);
+  const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
+  const SegRange sr = seg_range(nch, a.P, p);
+  const int cb0 = vs * CW;
+  const bool isT = (MODE == MODE_AUG) && cb0 < kDim;
+  if (MODE == MODE_AUG) {
+    if (p == 0 || p > sr.p_last) return;       // segment 0 needs no transition
+    if (p == sr.p_last && isT) return;         // the last segment starts from dht
+  } else {
+    if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;
+  }
+  const int vcol0 = (MODE == MODE_AUG) ? (isT ? 0 : cb0 - kDim) : cb0;
+  const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
+  const int64_t KV = (int64_t)kDim * kDim;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* dO = reinterpret_cast<const T*>(a.dO);
+  const T* Ag = reinterpret_cast<const T*>(a.A);
+  const T* beta = reinterpret_cast<const T*>(a.beta);
+  const int cw0 = 16 * VB * (w & 3);
+
+  // gradient entering the segment's end: dht (last segment) or the chained
+  // value; every load is issued before the first is used (null reads zeros)
+  f32x4 Gs[8][VB];
+  if (MODE == MODE_AUG && isT) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Gs[kb][vb][e] = (16 * kb + 4 * grp + e == cb0 + cw0 + 16 * vb + col) ? 1.f : 0.f;
+  } else {
+    const float* src = (p == sr.p_last) ? (a.dht ? a.dht + unit * KV : nullptr)
+                                        : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+    const bool vf = (p == sr.p_last) && a.svf;
+    const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
+          Gs[kb][vb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
+        }
+  }
+
+  TileRegs<128, 256> rq, rk;
+  TileRegs<CW, 256> rd;
+  TileRegs<64, 256> ra;
+  float r_g = 0.f, r_gl = 0.f;
+  T r_b = from_f<T>(0.f);
+  auto prefetch = [&](int c) {
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+    tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
+    tile_load<T, 128, 256>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
+    tile_load<T, CW, 256>(rd, dO + (t0 * a.Hv + h) * kDim + vcol0, (int64_t)a.Hv * kDim, Cc, otid);
+    tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc, otid);
+    if (otid < 64) {
+      r_g = a.gcum[(t0 + min(otid, Cc - 1)) * a.Hv + h];
+      r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
+      r_b = (otid < Cc) ? beta[(t0 + otid) * a.Hv + h] : from_f<T>(0.f);
+    }
+  };
+
+  // the initial state has arrived before the loop (else the loop-entry merge
+  // makes the first use of Gs wait for the prefetch as well)
+  __builtin_amdgcn_s_waitcnt(0);
+  if (helper && sr.c0 < sr.c1) prefetch(sr.c1 - 1);
+  for (int c = sr.c1 - 1; c >= sr.c0; --c) {
+    __syncthreads();
+    if (helper) {
+      tile_store<T, 128, 256>(Qs, LD, rq, otid);
+      tile_store<T, 128, 256>(Ks, LD, rk, otid);
+      tile_store<T, CW, 256>(Ds, LDV, rd, otid);
+      tile_store<T, 64, 256>(As, LDA, ra, otid);
+      if (otid < 64) {
+        const float e = __expf(r_g);
+        gam[otid] = r_g;
+        eg[otid] = a.scale * e;
+        bex[otid] = to_f(r_b) * e;
+        dl[otid] = __expf(r_gl - r_g);
+      }
+    }
+    __syncthreads();
+    if (helper) {
+      if (c - 1 >= sr.c0) prefetch(c - 1);
+      continue;
+    }
+    const float eL = __expf(gam[63]);
+
+    // gradient of this chunk's end state out, value-major ([V][K]): a lane's
+    // four consecutive keys of one value column are 8 contiguous bytes
+    if (OUT) {
+      const __amdgpu_buffer_rsrc_t hrs =
+          buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          const int vc = cb0 + cw0 + 16 * vb + col;
+          const typename VT<T>::x4 hv{from_f<T>(Gs[kb][vb][0]), from_f<T>(Gs[kb][vb][1]),
+                                      from_f<T>(Gs[kb][vb][2]), from_f<T>(Gs[kb][vb][3])};
+          buf_store8(hrs, (vc * kDim + 16 * kb + 4 * grp) * (int)sizeof(T), __builtin_bit_cast(u32x2, hv));
+        }
+    }
+
+    // One pass over the key dimension forms K dSn and the lower tiles of
+    // P = Q K^T (tile (rb, ib), ib <= rb: rows r = 16 rb + 4 grp + e, column
+    // i = 16 ib + col) from the same K fragments.
+    x8 Gb[4][VB];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) Gb[kb2][vb] = pack_split<T>(Gs[2 * kb2][vb], Gs[2 * kb2 + 1][vb]);
+    f32x4 dd[4][VB], pt[10];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = zero4();
+#pragma unroll
+    for (int x = 0; x < 10; ++x) pt[x] = zero4();
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      x8 fk[4], fq[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) fk[tb] = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
+      if (!isT) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) fq[tb] = frag_row_split(Qs + 16 * tb * LD + 32 * kb2, LD);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = mfma16(fk[tb], Gb[kb2][vb], dd[tb][vb]);
+      if (!isT) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int ib = 0; ib <= rb; ++ib) pt[tri_idx(ib, rb)] = mfma16(fq[rb], fk[ib], pt[tri_idx(ib, rb)]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO.  Two stacked D tiles
+    // of P (rows r) form the A operand of P^T with k = r.
+    if (!isT) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
+#pragma unroll
+        for (int ib = 0; ib <= rb; ++ib) {
+          const float gi = gam[16 * ib + col];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // masked entries take exp(-inf) = 0 (unconditional exponential)
+            const bool keep = (ib < rb) || (col <= 4 * grp + e);
+            pt[tri_idx(ib, rb)][e] *= __expf(keep ? gr[e] - gi : -INFINITY);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      x8 pa[2];
+#pragma unroll
+      for (int kt = tb / 2; kt < 2; ++kt)
+        pa[kt] = pack_split<T>((2 * kt >= tb) ? pt[tri_idx(tb, 2 * kt < 4 ? 2 * kt : 3)] : zero4(),
+                               pt[tri_idx(tb, 2 * kt + 1)]);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 acc = zero4();
+        if (!isT) {
+#pragma unroll
+          for (int kt = tb / 2; kt < 2; ++kt)
+            acc = mfma16(pa[kt], frag_tr_split(Ds + 32 * kt * LDV + cw0 + 16 * vb, LDV), acc);
+        }
+        const f32x4 dlr = *reinterpret_cast<const f32x4*>(dl + 16 * tb + 4 * grp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dd[tb][vb][e] = dlr[e] * dd[tb][vb][e] + a.scale * acc[e];
+      }
+    }
+    // Z = -diag(beta e^gamma) A^T dDelta
+    f32x4 zz[4][VB];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kt = tb / 2; kt < 2; ++kt)
+          acc = mfma16(frag_tr_split(As + 32 * kt * LDA + 16 * tb, LDA),
+                       pack_split<T>(dd[2 * kt][vb], dd[2 * kt + 1][vb]), acc);
+        const f32x4 bx = *reinterpret_cast<const f32x4*>(bex + 16 * tb + 4 * grp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= -bx[e];
+        zz[tb][vb] = acc;
+      }
+    // dS = e^{gL} dSn + K^T Z + Q^T (scale diag(e^gamma) dO)
+    x8 Zb[2][VB], Ob[2][VB];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        Zb[kt][vb] = pack_split<T>(zz[2 * kt][vb], zz[2 * kt + 1][vb]);
+        if (!isT) {
+          x8 f = frag_tr_split(Ds + 32 * kt * LDV + cw0 + 16 * vb, LDV);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 32 * kt + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+            f[e] = from_f<T>(to_f(f[e]) * eg[r]);
+          }
+          Ob[kt][vb] = f;
+        }
+      }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      x8 fk[2], fq[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        fk[kt] = frag_tr_split(Ks + 32 * kt * LD + 16 * kb, LD);
+        if (!isT) fq[kt] = frag_tr_split(Qs + 32 * kt * LD + 16 * kb, LD);
+      }
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        f32x4 acc = Gs[kb][vb] * eL;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          acc = mfma16(fk[kt], Zb[kt][vb], acc);
+          if (!isT) acc = mfma16(fq[kt], Ob[kt][vb], acc);
+        }
+        Gs[kb][vb] = acc;
+      }
+    }
+  }
+
+  if (helper) return;
+  if (MODE == MODE_AUG) {
+    float* so = a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          so[(16 * kb + 4 * grp + e) * (2 * kDim) + cb0 + cw0 + 16 * vb + col] = Gs[kb][vb][e];
+  } else if (p == 0 && a.dh0) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
+          a.dh0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = Gs[kb][vb][e];
+        }
+  }
+}
+
+// The output passes of B1 and B2 with load-helper waves (VB = 1), in one
+// launch of 8-wave workgroups: blocks [0, n1) take B1.
+template <typename T>
+__global__ __launch_bounds__(512) void bwd_scans_lh_kernel(ScanArgs sa, DhArgs da, int n1) {
+  if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE>(sa, xcd_block(blockIdx.x, n1));
+  else dh_lh_body<T>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
+}
+
 // The state scan (B1) and the state-gradient scan (B2) are independent (B2
 // needs no chunk states), so one launch runs both: blocks [0, n1) take B1,
 // the rest B2.  Each pass alone fills only part of the chip when there are
@@ -933,8 +1228,11 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t
   sa.P = da.P = pl.cp;
   sa.nvs = da.nvs = 2 / VB;
   const unsigned n1 = units * pl.cp * sa.nvs;
-  GDR_LAUNCH("bwd_scans", (bwd_scans_kernel<T, VB, MODE_STATE, MODE_OUT>), dim3(2 * n1), dim3(256),
-             st, sa, da, (int)n1);
+  if (VB == 1)
+    GDR_LAUNCH("bwd_scans", bwd_scans_lh_kernel<T>, dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+  else
+    GDR_LAUNCH("bwd_scans", (bwd_scans_kernel<T, VB, MODE_STATE, MODE_OUT>), dim3(2 * n1),
+               dim3(256), st, sa, da, (int)n1);
 }
 
 template <typename T>

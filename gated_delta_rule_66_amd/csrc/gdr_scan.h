@@ -441,25 +441,30 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
 // The output work is thus off the state chain's critical path, and two waves
 // share each SIMD.  Chunk tiles are double-buffered where both roles read
 // them (q, k, P, e^gamma, the operand copies).
-template <typename T>
-__global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
+//
+// MODE_STATE (the backward's chunk-start states) uses the same split with
+// waves 4-7 only loading and storing the chunk tiles, and the state waves
+// writing h (value-major) straight from registers.
+template <typename T, int MODE>
+__device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   typedef typename VT<T>::x8 x8;
+  constexpr bool OUT = (MODE == MODE_OUT);
+  constexpr int NB = OUT ? 2 : 1;  // buffers of the tiles both roles read
   constexpr int LD = 136;   // q / k tile leading dimension
   constexpr int LDV = 72;   // v tile (64 columns)
   constexpr int LDA = 72;   // A and P tiles
-  __shared__ __align__(16) T Qs[2][64 * LD];
-  __shared__ __align__(16) T Ks[2][64 * LD];
+  __shared__ __align__(16) T Qs[NB][OUT ? 64 * LD : 8];
+  __shared__ __align__(16) T Ks[NB][64 * LD];
   __shared__ __align__(16) T Vs[64 * LDV];
   __shared__ __align__(16) T As[64 * LDA];
-  __shared__ __align__(16) T Ps[2][64 * LDA];
-  __shared__ __align__(16) x8 Xs[2][4][4][64];  // S_c operands: [buf][column block][k block][lane]
-  __shared__ __align__(16) x8 Xd[2][4][2][64];  // Delta_c operands
+  __shared__ __align__(16) T Ps[NB][OUT ? 64 * LDA : 8];
+  __shared__ __align__(16) x8 Xs[NB][4][4][OUT ? 64 : 1];  // S_c operands: [buf][column block][k block][lane]
+  __shared__ __align__(16) x8 Xd[NB][4][2][OUT ? 64 : 1];  // Delta_c operands
   __shared__ __align__(16) float gam[64], bet[64], bex[64], dl[64], eg[2][64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const bool outw = w >= 4;
   const int wq = w & 3;  // the wave's 16-column block (both roles)
-  const int bid = xcd_block(blockIdx.x, gridDim.x);
   const int vs = bid & 1;
   const int up = bid >> 1;
   const int p = up % a.P, unit = up / a.P;
@@ -472,6 +477,7 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
   const int cb0 = 64 * vs;
   const int cw0 = 16 * wq;
   const int64_t KV = (int64_t)kDim * kDim;
+  const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
   const T* q = reinterpret_cast<const T*>(a.q);
   const T* k = reinterpret_cast<const T*>(a.k);
   const T* v = reinterpret_cast<const T*>(a.v);
@@ -507,7 +513,7 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
   auto prefetch = [&](int c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
-    tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
+    if (OUT) tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
     tile_load<T, 128, 256>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
     tile_load<T, 64, 256>(rv, v + (t0 * a.Hv + h) * kDim + cb0, (int64_t)a.Hv * kDim, Cc, otid);
     tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc, otid);
@@ -522,16 +528,18 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
   // compiler, merging the loop entry with the back edge, waits for every
   // outstanding load (the prefetch included) before the first use of S.
   __builtin_amdgcn_s_waitcnt(0);
-  p_zero_tiles<T>(Ps[0], LDA);
-  p_zero_tiles<T>(Ps[1], LDA);
+  if (OUT) {
+    p_zero_tiles<T>(Ps[0], LDA);
+    p_zero_tiles<T>(Ps[NB - 1], LDA);
+  }
   if (outw && sr.c0 < sr.c1) prefetch(sr.c0);
   // iteration it: state chain of chunk it (it < c1), output of chunk it-1
   // (it > c0); the last iteration only drains the output
-  for (int it = sr.c0; it <= sr.c1; ++it) {
-    const int b = it & 1;
+  for (int it = sr.c0; it < sr.c1 + (OUT ? 1 : 0); ++it) {
+    const int b = OUT ? (it & 1) : 0;
     __syncthreads();  // iteration it-1 is done with every buffer rewritten here
     if (outw && it < sr.c1) {
-      tile_store<T, 128, 256>(Qs[b], LD, rq, otid);
+      if (OUT) tile_store<T, 128, 256>(Qs[b], LD, rq, otid);
       tile_store<T, 128, 256>(Ks[b], LD, rk, otid);
       tile_store<T, 64, 256>(Vs, LDV, rv, otid);
       tile_store<T, 64, 256>(As, LDA, ra, otid);
@@ -555,7 +563,20 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 4; ++kb2) {
           Sb[kb2] = pack_split<T>(S[2 * kb2], S[2 * kb2 + 1]);
-          Xs[b][wq][kb2][l] = Sb[kb2];
+          if (OUT) Xs[b][wq][kb2][l] = Sb[kb2];
+        }
+        if (MODE == MODE_STATE) {
+          // chunk-start state out, value-major: a lane's four consecutive keys
+          // of one value column are 8 contiguous bytes
+          const __amdgpu_buffer_rsrc_t hrs = buf_rsrc(
+              reinterpret_cast<T*>(a.h) + ((choff + it) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
+          const int vc = cb0 + cw0 + col;
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            const typename VT<T>::x4 hv{from_f<T>(S[kb][0]), from_f<T>(S[kb][1]), from_f<T>(S[kb][2]),
+                                        from_f<T>(S[kb][3])};
+            buf_store8(hrs, (vc * kDim + 16 * kb + 4 * grp) * (int)sizeof(T), __builtin_bit_cast(u32x2, hv));
+          }
         }
         // K S
         f32x4 ks[4];
@@ -584,8 +605,10 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
           if (tb >= 2) acc = mfma16(frag_row_split(As + 16 * tb * LDA + 32, LDA), Rb1, acc);
           dd[tb] = acc;
         }
+        if (OUT) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) Xd[b][wq][kb][l] = pack_split<T>(dd[2 * kb], dd[2 * kb + 1]);
+          for (int kb = 0; kb < 2; ++kb) Xd[b][wq][kb][l] = pack_split<T>(dd[2 * kb], dd[2 * kb + 1]);
+        }
         // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) Delta
         x8 Eb[2];
 #pragma unroll
@@ -602,7 +625,7 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
           S[kb] = acc;
         }
       }
-    } else {
+    } else if (OUT) {
       if (it > sr.c0) {
       // output of chunk c = it - 1:
       //   O^T = (Q S)^T diag(e^gamma) + Delta^T P^T, times scale
@@ -641,7 +664,7 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
     }
   }
 
-  if (!outw && a.ht && p == sr.p_last) {
+  if (OUT && !outw && a.ht && p == sr.p_last) {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
@@ -650,6 +673,11 @@ __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
         a.ht[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = S[kb][e];
       }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
+  scan_spec_body<T, MODE_OUT>(a, xcd_block(blockIdx.x, gridDim.x));
 }
 
 // Pass 2: chain the segment start states of one (unit, 16-column block).
