@@ -346,6 +346,9 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   __shared__ __align__(16) T Ds[64 * LDV];
   __shared__ __align__(16) T As[64 * LDA];
   __shared__ __align__(16) float gam[64], eg[64], bex[64], dl[64];
+  // dSn of the chain's chunk as bf16 operand registers ([buf][column block]
+  // [k block][lane]); the helpers store it one iteration later
+  __shared__ __align__(16) x8 Hx[2][4][4][64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const bool helper = w >= 4;
@@ -422,6 +425,24 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
     }
   };
 
+  // gradient of chunk cc's end state out, value-major ([V][K]), from the
+  // operand copy the chain left in Hx: element e < 4 of k block kb2 is key
+  // 32 kb2 + 4 grp + e, element e >= 4 key 32 kb2 + 16 + 4 grp + e - 4, so
+  // each half is 8 contiguous bytes of one value column
+  auto store_dh = [&](int cc) {
+    const int wq = w & 3;
+    const __amdgpu_buffer_rsrc_t hrs =
+        buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + cc) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
+    const int vc = cb0 + 16 * wq + col;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      const x8 g = Hx[cc & 1][wq][kb2][l];
+      const u32x4 u = __builtin_bit_cast(u32x4, g);
+      buf_store8(hrs, (vc * kDim + 32 * kb2 + 4 * grp) * (int)sizeof(T), u32x2{u[0], u[1]});
+      buf_store8(hrs, (vc * kDim + 32 * kb2 + 16 + 4 * grp) * (int)sizeof(T), u32x2{u[2], u[3]});
+    }
+  };
+
   // the initial state has arrived before the loop (else the loop-entry merge
   // makes the first use of Gs wait for the prefetch as well)
   __builtin_amdgcn_s_waitcnt(0);
@@ -444,34 +465,20 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
     __syncthreads();
     if (helper) {
       if (c - 1 >= sr.c0) prefetch(c - 1);
+      if (c + 1 < sr.c1) store_dh(c + 1);
       continue;
     }
     const float eL = __expf(gam[63]);
-
-    // gradient of this chunk's end state out, value-major ([V][K]): a lane's
-    // four consecutive keys of one value column are 8 contiguous bytes
-    if (OUT) {
-      const __amdgpu_buffer_rsrc_t hrs =
-          buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int vb = 0; vb < VB; ++vb) {
-          const int vc = cb0 + cw0 + 16 * vb + col;
-          const typename VT<T>::x4 hv{from_f<T>(Gs[kb][vb][0]), from_f<T>(Gs[kb][vb][1]),
-                                      from_f<T>(Gs[kb][vb][2]), from_f<T>(Gs[kb][vb][3])};
-          buf_store8(hrs, (vc * kDim + 16 * kb + 4 * grp) * (int)sizeof(T), __builtin_bit_cast(u32x2, hv));
-        }
-    }
 
     // One pass over the key dimension forms K dSn and the lower tiles of
     // P = Q K^T (tile (rb, ib), ib <= rb: rows r = 16 rb + 4 grp + e, column
     // i = 16 ib + col) from the same K fragments.
     x8 Gb[4][VB];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 4; ++kb2)
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb) Gb[kb2][vb] = pack_split<T>(Gs[2 * kb2][vb], Gs[2 * kb2 + 1][vb]);
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      Gb[kb2][0] = pack_split<T>(Gs[2 * kb2][0], Gs[2 * kb2 + 1][0]);
+      Hx[c & 1][w][kb2][l] = Gb[kb2][0];  // this chunk's dSn, stored by the helpers
+    }
     f32x4 dd[4][VB], pt[10];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -593,7 +600,12 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
     }
   }
 
-  if (helper) return;
+  // the dSn of the last chunk walked (c0)
+  __syncthreads();
+  if (helper) {
+    if (sr.c0 < sr.c1) store_dh(sr.c0);
+    return;
+  }
   if (MODE == MODE_AUG) {
     float* so = a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
 #pragma unroll
