@@ -65,30 +65,48 @@ static gdr_status fail(gdr_status s, char* reason, size_t len, const char* fmt, 
 }
 
 // Estimated scan time of a plan with P segments per sequence and VB 16-column
-// state tiles per wave, in microseconds per chunk step, calibrated on MI355X
-// (256 CUs).  Every pass runs one 4-wave workgroup per CU, except the forward
-// transition pass at VB = 1, which fits two; a pass with more workgroups than
-// slots runs in rounds.  Forward: output pass 4.1 (VB = 1) / 5.5 (VB = 2) per
-// chunk, transition pass 3.0 / 3.2.  Backward (state and state-gradient scans
-// in one launch): 3.7 / 5.8 per chunk, transition pass 4.5 / 5.5.  A combine
-// step costs 11 per scan, and splitting adds two launches (~16).
+// state tiles per wave, in microseconds, calibrated on MI355X (256 CUs; one
+// workgroup per CU in every pass but the forward transition pass at VB = 1,
+// which fits two; a pass with more workgroups than slots runs in rounds).
+// Per chunk step of one workgroup:
+//   forward output pass 3.1 (VB = 1, wave-specialized) / 5.0 (VB = 2),
+//   forward transition pass 2.7 / 3.0,
+//   backward output pass (state and state-gradient scans in one launch):
+//     state scan 2.4 / 5.5 and state-gradient scan 3.3 / 5.5; the launch
+//     takes the longer of its total work spread over the CUs and one
+//     state-gradient chain,
+//   backward transition pass 4.5 / 4.2,
+// one combine step 10 per scan, and 16 for the two extra launches of a split.
 static double rounds(int64_t wgs, int64_t slots) {
   const int64_t r = (wgs + slots - 1) / slots;
   return r < 1 ? 1.0 : (double)r;
 }
 
+static double bwd_out_cost(int64_t wgs_per_scan, int64_t chunks, int VB) {
+  const double c1 = VB == 1 ? 2.4 : 5.5, c2 = VB == 1 ? 3.3 : 5.5;
+  const double spread = (double)wgs_per_scan * (double)chunks * (c1 + c2) / 256.0;
+  const double chain = (double)chunks * c2;
+  return spread > chain ? spread : chain;
+}
+
 static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd) {
   const int64_t nvs0 = 2 / VB, nvs1 = 4 / VB;
-  const int64_t scans = bwd ? 2 : 1;
-  const double out = bwd ? (VB == 1 ? 3.7 : 5.8) : (VB == 1 ? 4.1 : 5.5);
-  if (P == 1) return (double)maxch * out * rounds(scans * units * nvs0, 256);
-  const double aug = bwd ? (VB == 1 ? 4.5 : 5.5) : (VB == 1 ? 3.0 : 3.2);
-  const int64_t aug_slots = (!bwd && VB == 1) ? 512 : 256;
+  if (!bwd) {
+    const double out = VB == 1 ? 3.1 : 5.0;
+    if (P == 1) return (double)maxch * out * rounds(units * nvs0, 256);
+    const int64_t sc = (maxch + P - 1) / P;
+    // one end segment needs only its value columns, the inner ones everything
+    const int64_t wg_aug = units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
+    const double aug = VB == 1 ? 2.7 : 3.0;
+    return (double)sc * aug * rounds(wg_aug, VB == 1 ? 512 : 256) + 10.0 * (double)(P - 1) + 16.0 +
+           (double)sc * out * rounds(units * P * nvs0, 256);
+  }
+  if (P == 1) return bwd_out_cost(units * nvs0, maxch, VB);
   const int64_t sc = (maxch + P - 1) / P;
-  // one end segment needs only its value columns, the inner ones everything
-  const int64_t wg_aug = scans * units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
-  return (double)sc * aug * rounds(wg_aug, aug_slots) + 11.0 * (double)(scans * (P - 1)) + 16.0 +
-         (double)sc * out * rounds(scans * units * P * nvs0, 256);
+  const int64_t wg_aug = 2 * units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
+  const double aug = VB == 1 ? 4.5 : 4.2;
+  return (double)sc * aug * rounds(wg_aug, 256) + 20.0 * (double)(P - 1) + 16.0 +
+         bwd_out_cost(units * P * nvs0, sc, VB);
 }
 
 // Context-parallel plan along T for one direction: it depends only on shapes
