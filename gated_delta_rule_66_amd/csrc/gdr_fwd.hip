@@ -71,19 +71,19 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   const int G = a.Hv / a.Hq, hq = h / G;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
 
+  // the k tile's loads are issued first; the gate loads and scan overlap them
+  TileRegs<128, 256> rk;
+  tile_load<T, 128, 256>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
+                         (int64_t)a.Hq * kDim, Cc);
   if (w == 0) {
     const float gv = (l < Cc) ? load_scalar(a.g, (t0 + l) * a.Hv + h, a.g_dtype) : 0.f;
+    const float bv = (l < Cc) ? to_f(reinterpret_cast<const T*>(a.beta)[(t0 + l) * a.Hv + h]) : 0.f;
     const float gc = wave_inclusive_scan(gv);
     gam[l] = gc;
-    bet[l] = (l < Cc) ? to_f(reinterpret_cast<const T*>(a.beta)[(t0 + l) * a.Hv + h]) : 0.f;
+    bet[l] = bv;
     if (l < Cc) a.gcum[(t0 + l) * a.Hv + h] = gc;
   }
-  {
-    TileRegs<128, 256> rk;
-    tile_load<T, 128, 256>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
-                           (int64_t)a.Hq * kDim, Cc);
-    tile_store<T, 128, 256>(Ks, LDK, rk);
-  }
+  tile_store<T, 128, 256>(Ks, LDK, rk);
   __syncthreads();
 
   // M, rows 16w .. 16w+15 (only the blocks on or below the diagonal are nonzero)
@@ -102,11 +102,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
       Mf[r * LDM + i] = bet[r] * __expf(i < r ? gam[r] - gam[i] : -INFINITY) * acc[e];
     }
   }
-  // blocks above the diagonal of the inverse are zero
-  for (int x = tid; x < 64 * 64; x += 256) {
-    const int r = x >> 6, cc = x & 63;
-    if ((cc >> 4) > (r >> 4)) Ai[r * LDM + cc] = 0.f;
-  }
+  // (the blocks of the inverse above the diagonal are never read)
   __syncthreads();
 
   // diagonal 16x16 blocks: forward substitution, lane l < 16 owns column l
