@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
 
 
-def gpu_fwd_bwd(d, svf=False, cp=0):
+def gpu_fwd_bwd(d, svf=False, cp=0, vt=0):
     import gated_delta_rule_66_amd as gdr
     dd = to_dev(d)
     h0, dht = dd["h0"], dd["dht"]
@@ -23,11 +23,11 @@ def gpu_fwd_bwd(d, svf=False, cp=0):
     g_cum, A, o, _, ht = gdr.chunk_gated_delta_rule_fwd(
         dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"], initial_state=h0,
         output_final_state=True, cu_seqlens=dd["cu_seqlens"], state_v_first=svf, cp_segments=cp,
-        cu_seqlens_cpu=cu_cpu)
+        cu_seqlens_cpu=cu_cpu, wave_tiles=vt)
     grads = gdr.chunk_gated_delta_rule_bwd(
         dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dht, scale=dd["scale"],
         initial_state=h0, cu_seqlens=dd["cu_seqlens"], state_v_first=svf, dg_dtype=dd["g"].dtype,
-        cp_segments=cp, cu_seqlens_cpu=cu_cpu)
+        cp_segments=cp, cu_seqlens_cpu=cu_cpu, wave_tiles=vt)
     torch.cuda.synchronize()
     return o, ht, grads
 
@@ -120,3 +120,18 @@ def test_autograd_end_to_end():
     for nm, key in zip(NAMES, ("q", "k", "v", "beta", "g", "h0")):
         rt = ratio(np64(leaves[key].grad), ref[NAMES.index(nm)])
         assert rt <= TOL, (nm, rt)
+
+
+@pytest.mark.parametrize("name", ["dense_state_dht", "fp16_gva", "varlen_empty_seq"])
+@pytest.mark.parametrize("vt,cp", [(1, 1), (2, 1), (1, 3), (2, 3)])
+def test_backward_scan_variants(name, vt, cp):
+    """One and two 16-column tiles per wave, unsplit and in three segments."""
+    d = gdr_synth.make(CASES[name])
+    print("case", name, "wave_tiles", vt, "cp", cp, flush=True)
+    o, ht, g = gpu_fwd_bwd(d, cp=cp, vt=vt)
+    ref = oracle_grads(d)
+    for n, x, r in zip(NAMES, g, ref):
+        if r is None:
+            assert x is None
+            continue
+        assert ratio(np64(x), r) <= TOL, n

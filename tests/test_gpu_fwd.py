@@ -10,7 +10,7 @@ from _util import TOL, np64, ratio, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu_fwd(d, svf=False, output_h=True, cp=0):
+def run_gpu_fwd(d, svf=False, output_h=True, cp=0, vt=0):
     import gated_delta_rule_66_amd as gdr
     dd = to_dev(d)
     h0 = dd["h0"]
@@ -20,7 +20,7 @@ def run_gpu_fwd(d, svf=False, output_h=True, cp=0):
                                          scale=dd["scale"], initial_state=h0,
                                          output_final_state=True, cu_seqlens=dd["cu_seqlens"],
                                          state_v_first=svf, output_h=output_h, cp_segments=cp,
-                                         cu_seqlens_cpu=d["cu_seqlens"])
+                                         cu_seqlens_cpu=d["cu_seqlens"], wave_tiles=vt)
     torch.cuda.synchronize()
     return out
 
@@ -108,3 +108,24 @@ def test_context_parallel_forward_matches_oracle(name, cp):
     # the plan depends only on shapes: state_v_first stays bit-exact under CP
     b = run_gpu_fwd(d, svf=True, cp=cp)
     assert torch.equal(o, b[2]) and torch.equal(ht.transpose(-1, -2), b[4])
+
+
+# Every scan variant on the small cases: without h (the wave-specialized output
+# kernel at one 16-column tile per wave), with h, and two tiles per wave, each
+# unsplit and split into three segments.
+VARIANTS = [(oh, vt, cp) for oh in (False, True) for vt in (1, 2) for cp in (1, 3)]
+
+
+@pytest.mark.parametrize("name", ["dense_ragged_state", "fp16_gva", "varlen"])
+@pytest.mark.parametrize("output_h,vt,cp", VARIANTS)
+def test_forward_scan_variants(name, output_h, vt, cp):
+    d = gdr_synth.make(CASES[name])
+    print("case", name, "output_h", output_h, "wave_tiles", vt, "cp", cp, flush=True)
+    g_cum, A, o, h, ht = run_gpu_fwd(d, output_h=output_h, cp=cp, vt=vt)
+    gc_r, A_r, o_r, h_r, ht_r = oracle_chunked(d)
+    assert ratio(np64(o), o_r) <= TOL
+    assert ratio(np64(ht), ht_r) <= TOL
+    if output_h:
+        assert ratio(np64(h), h_r) <= TOL
+    else:
+        assert h is None
