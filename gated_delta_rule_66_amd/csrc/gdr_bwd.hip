@@ -340,7 +340,6 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   constexpr int LD = 136;
   constexpr int LDV = CW + 8;
   constexpr int LDA = 72;
-  constexpr bool OUT = (MODE == MODE_OUT);
   __shared__ __align__(16) T Qs[64 * LD];
   __shared__ __align__(16) T Ks[64 * LD];
   __shared__ __align__(16) T Ds[64 * LDV];

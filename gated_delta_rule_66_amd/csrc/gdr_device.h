@@ -180,6 +180,54 @@ __device__ __forceinline__ void tile_to_lds(T* lds, int ld, const T* g, int64_t 
   }
 }
 
+// ---- staggered 64 x 128 tiles -----------------------------------------------
+// Rows of a 64 x 128 tile of 16-bit values are contiguous (256 bytes) but
+// start at staggered offsets: row r begins 16 * U(r) bytes past 256 * r, with
+// U(r) = 2 (r % 4) + 8 q + (q >= 2) + 32 (r / 16), q = (r / 4) % 4.  U grows
+// with r, so rows never overlap.  Modulo the 256-byte bank width the
+// 16-byte shifts of rows 0..15 are all different (operand rows read at one
+// column hit distinct banks) and four consecutive rows are shifted by 32
+// bytes each, so the 4 row x 32 byte reads of the transposing load cover all
+// banks once; with a uniform 272-byte stride those reads collide two ways.
+__device__ __forceinline__ int qk_row(int r) {
+  const int q = (r >> 2) & 3;
+  return 128 * r + 8 * (2 * (r & 3) + 8 * q + (q >> 1) + 32 * (r >> 4));
+}
+constexpr int QK_TILE = 128 * 64 + 8 * 128;  // elements, >= qk_row(63) + 128
+
+// Operand rows r0 + (lane % 16) (r0 a multiple of 16), split k order (k0 a
+// multiple of 32).
+template <typename T>
+__device__ __forceinline__ typename VT<T>::x8 frag_row_split_q(const T* X, int r0, int k0) {
+  const int l = lane_id();
+  const T* p = X + qk_row(l & 15) + (r0 >> 4) * qk_row(16) + k0 + 4 * (l >> 4);
+  typedef typename VT<T>::x4 x4;
+  const x4 lo = *reinterpret_cast<const x4*>(p);
+  const x4 hi = *reinterpret_cast<const x4*>(p + 16);
+  return typename VT<T>::x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Operand rows r0 + (lane % 16), contiguous k order (8 elements from
+// k0 + 8 * (lane / 16)).
+template <typename T>
+__device__ __forceinline__ typename VT<T>::x8 frag_row_q(const T* X, int r0, int k0) {
+  const int l = lane_id();
+  const T* p = X + qk_row(l & 15) + (r0 >> 4) * qk_row(16) + k0 + 8 * (l >> 4);
+  return *reinterpret_cast<const typename VT<T>::x8*>(p);
+}
+
+// Transposed operand (split k order): k runs down rows k0 .. k0 + 31 of the
+// tile (k0 a multiple of 32), the operand's columns are m0 .. m0 + 15.
+template <typename T>
+__device__ __forceinline__ typename VT<T>::x8 frag_tr_split_q(const T* X, int k0, int m0) {
+  const int l = lane_id(), j = l & 15;
+  const T* p = X + qk_row(4 * (l >> 4) + (j >> 2)) + (k0 >> 4) * qk_row(16) + m0 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + qk_row(16)));
+  return __builtin_bit_cast(typename VT<T>::x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
 // Register-staged tile copies, split in two so that the global loads of the
 // next chunk can be in flight while the current chunk computes.  A 64-row
 // tile of COLS elements is NT-thread cooperative; thread t holds 16-byte
@@ -250,6 +298,17 @@ __device__ __forceinline__ void tile_store(T* lds, int ld, const TileRegs<COLS, 
   }
 }
 
+// Store a 64 x 128 register tile into a staggered LDS tile (qk_row).
+template <typename T, int NT>
+__device__ __forceinline__ void tile_store_q(T* lds, const TileRegs<128, NT>& t,
+                                             int t0 = threadIdx.x) {
+#pragma unroll
+  for (int i = 0; i < TileRegs<128, NT>::N; ++i) {
+    const int x = t0 + i * NT;
+    *reinterpret_cast<uint4*>(lds + qk_row(x >> 4) + 8 * (x & 15)) = t.r[i];
+  }
+}
+
 // LDS tile rows [0, rows) -> global, 16 bytes per store (stores of rows past
 // `rows` fall outside the buffer range and are dropped).
 template <typename T, int COLS, int NT>
@@ -283,8 +342,9 @@ __device__ __forceinline__ void store_scalar(void* p, int64_t idx, int dtype, fl
 // written to LDS in the input dtype.  The ten 16x16 tiles on or below the
 // diagonal are spread over the four waves (3, 3, 2, 2); the two tiles above
 // the diagonal that the triangular products read, (0,1) and (2,3), are zeroed
-// once by p_zero_tiles and never written again.
-template <typename T>
+// once by p_zero_tiles and never written again.  With STAG the q and k
+// tiles are staggered (qk_row) and ldq is not used.
+template <typename T, bool STAG = false>
 __device__ __forceinline__ void p_tiles(const T* Qs, const T* Ks, int ldq, T* Ps, int ldp,
                                         const float* gam, int w) {
   const int l = lane_id(), grp = l >> 4, col = l & 15;
@@ -304,9 +364,13 @@ __device__ __forceinline__ void p_tiles(const T* Qs, const T* Ks, int ldq, T* Ps
     const int rb = x >> 2, cb = x & 3;
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = mfma16(frag_row(Qs + 16 * rb * ldq + 32 * kk, ldq),
-                   frag_row(Ks + 16 * cb * ldq + 32 * kk, ldq), acc);
+    for (int kk = 0; kk < 4; ++kk) {
+      if (STAG)
+        acc = mfma16(frag_row_q(Qs, 16 * rb, 32 * kk), frag_row_q(Ks, 16 * cb, 32 * kk), acc);
+      else
+        acc = mfma16(frag_row(Qs + 16 * rb * ldq + 32 * kk, ldq),
+                     frag_row(Ks + 16 * cb * ldq + 32 * kk, ldq), acc);
+    }
     const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
     const float gi = gam[16 * cb + col];
 #pragma unroll

@@ -450,11 +450,10 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   typedef typename VT<T>::x8 x8;
   constexpr bool OUT = (MODE == MODE_OUT);
   constexpr int NB = OUT ? 2 : 1;  // buffers of the tiles both roles read
-  constexpr int LD = 136;   // q / k tile leading dimension
   constexpr int LDV = 72;   // v tile (64 columns)
   constexpr int LDA = 72;   // A and P tiles
-  __shared__ __align__(16) T Qs[NB][OUT ? 64 * LD : 8];
-  __shared__ __align__(16) T Ks[NB][64 * LD];
+  __shared__ __align__(16) T Qs[NB][OUT ? QK_TILE : 8];  // staggered rows (qk_row)
+  __shared__ __align__(16) T Ks[NB][QK_TILE];
   __shared__ __align__(16) T Vs[64 * LDV];
   __shared__ __align__(16) T As[64 * LDA];
   __shared__ __align__(16) T Ps[NB][OUT ? 64 * LDA : 8];
@@ -539,8 +538,8 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
     const int b = OUT ? (it & 1) : 0;
     __syncthreads();  // iteration it-1 is done with every buffer rewritten here
     if (outw && it < sr.c1) {
-      if (OUT) tile_store<T, 128, 256>(Qs[b], LD, rq, otid);
-      tile_store<T, 128, 256>(Ks[b], LD, rk, otid);
+      if (OUT) tile_store_q<T, 256>(Qs[b], rq, otid);
+      tile_store_q<T, 256>(Ks[b], rk, otid);
       tile_store<T, 64, 256>(Vs, LDV, rv, otid);
       tile_store<T, 64, 256>(As, LDA, ra, otid);
       if (otid < 64) {
@@ -586,7 +585,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
         for (int kb2 = 0; kb2 < 4; ++kb2)
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb)
-            ks[tb] = mfma16(frag_row_split(Ks[b] + 16 * tb * LD + 32 * kb2, LD), Sb[kb2], ks[tb]);
+            ks[tb] = mfma16(frag_row_split_q(Ks[b], 16 * tb, 32 * kb2), Sb[kb2], ks[tb]);
         // R = diag(beta) V - diag(beta e^gamma) K S
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -621,7 +620,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
         for (int kb = 0; kb < 8; ++kb) {
           f32x4 acc = S[kb] * eLc;
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) acc = mfma16(frag_tr_split(Ks[b] + 32 * kt * LD + 16 * kb, LD), Eb[kt], acc);
+          for (int kt = 0; kt < 2; ++kt) acc = mfma16(frag_tr_split_q(Ks[b], 32 * kt, 16 * kb), Eb[kt], acc);
           S[kb] = acc;
         }
       }
@@ -640,7 +639,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
         const x8 sb = Xs[bo][wq][kb2][l];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-          qsT[rb] = mfma16(sb, frag_row_split(Qs[bo] + 16 * rb * LD + 32 * kb2, LD), qsT[rb]);
+          qsT[rb] = mfma16(sb, frag_row_split_q(Qs[bo], 16 * rb, 32 * kb2), qsT[rb]);
       }
       const x8 Db0 = Xd[bo][wq][0][l], Db1 = Xd[bo][wq][1][l];
       const int ld_o = a.Hv * kDim * (int)sizeof(T);
@@ -660,7 +659,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
       }
       }
       // P of chunk it for the next iteration (tiles spread over the four waves)
-      if (it < sr.c1) p_tiles<T>(Qs[b], Ks[b], LD, Ps[b], LDA, gam, wq);
+      if (it < sr.c1) p_tiles<T, true>(Qs[b], Ks[b], 128, Ps[b], LDA, gam, wq);
     }
   }
 
