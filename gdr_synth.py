@@ -9,7 +9,8 @@ packed lengths (variable-length problems only) -> q -> k -> v -> g -> beta ->
 initial state -> do -> dht.
 
 * q, k ~ N(0, 1) in fp32, L2-normalised over the head dimension per
-  (token, head), then rounded to the input dtype.
+  (token, head), then rounded to the input dtype.  Problems that ask the
+  kernel to normalise (``qk_l2norm``) keep the raw N(0, 1) rows instead.
 * v ~ N(0, 1); g = logsigmoid(N(shift, 1)) (a natural-log decay <= 0;
   ``shift = 2`` gives the slow-decay long-context workload);
   beta = sigmoid(N(0, 1)); all rounded to the input dtype (round to nearest
@@ -45,6 +46,7 @@ class Problem:
     backward: bool = False
     dht: bool = False
     g_shift: float = 0.0
+    qk_l2norm: bool = False              # raw q, k rows; the kernel normalises them
     seed: int = 0
     extra: dict = field(default_factory=dict)
 
@@ -88,9 +90,13 @@ def make(prob: Problem, lengths_from=None) -> dict:
         cu[1:] = torch.cumsum(torch.tensor(prob.lens, dtype=torch.int64), 0).to(torch.int32)
     B, T, Hq, Hv, K, V = prob.B, prob.T, prob.Hq, prob.Hv, prob.K, prob.V
     q = torch.randn(B, T, Hq, K, generator=gen)
-    q = F.normalize(q, p=2.0, dim=-1).to(dt)
+    if not prob.qk_l2norm:
+        q = F.normalize(q, p=2.0, dim=-1)
+    q = q.to(dt)
     k = torch.randn(B, T, Hq, K, generator=gen)
-    k = F.normalize(k, p=2.0, dim=-1).to(dt)
+    if not prob.qk_l2norm:
+        k = F.normalize(k, p=2.0, dim=-1)
+    k = k.to(dt)
     v = torch.randn(B, T, Hv, V, generator=gen).to(dt)
     g = F.logsigmoid(torch.randn(B, T, Hv, generator=gen) + prob.g_shift).to(dt)
     beta = torch.sigmoid(torch.randn(B, T, Hv, generator=gen)).to(dt)
@@ -99,7 +105,7 @@ def make(prob: Problem, lengths_from=None) -> dict:
     do = torch.randn(B, T, Hv, V, generator=gen).to(dt) if prob.backward else None
     dht = (0.1 * torch.randn(N, Hv, K, V, generator=gen)) if (prob.backward and prob.dht) else None
     return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, do=do, dht=dht, cu_seqlens=cu,
-                scale=K ** -0.5)
+                scale=K ** -0.5, qk_l2norm=prob.qk_l2norm)
 
 
 # The five workloads.  Sizes are those of the pages' API example

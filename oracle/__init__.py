@@ -130,14 +130,47 @@ class _Problem:
         return np.ascontiguousarray(np.swapaxes(s, -1, -2)) if state_v_first else s
 
 
+# ---- q / k L2 normalisation ------------------------------------------------
+# The FLA backend pull request ("[GDN] Add FlashQLA backend dispatch", the
+# dispatch's argument list) passes a `use_qk_l2norm_in_kernel` flag through
+# to the fused kernel; the pages give no formula.  Reading: q and k are scaled
+# per (token, head) to unit Euclidean length over the head dimension before
+# the recurrence, y = x / sqrt(sum(x^2) + eps), eps = 1e-6 (eps only keeps an
+# all-zero row finite), and the gradient flows back through that map.
+QK_L2NORM_EPS = 1e-6
+
+
+def l2norm(x):
+    """y = x / sqrt(|x|^2 + eps) over the last axis, in fp64."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + QK_L2NORM_EPS)
+
+
+def l2norm_bwd(x, dy):
+    """Chain rule through y = x / n, n = sqrt(|x|^2 + eps).
+
+    dy_i/dx_j = (delta_ij - y_i y_j) / n, so dx = (dy - y (y . dy)) / n.
+    """
+    x = _f64(x)
+    dy = _f64(dy)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + QK_L2NORM_EPS)
+    y = x / n
+    return (dy - y * np.sum(y * dy, axis=-1, keepdims=True)) / n
+
+
 def _check(rc, name):
     if rc != 0:
         raise RuntimeError("%s failed with code %d" % (name, rc))
 
 
 def fwd(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None, state_v_first=False,
-        heads=None, nthreads=0):
-    """Token recurrence.  Returns ``(o [B,T,Hv,V], final_state [N,Hv,K,V])``."""
+        heads=None, nthreads=0, use_qk_l2norm=False):
+    """Token recurrence.  Returns ``(o [B,T,Hv,V], final_state [N,Hv,K,V])``.
+
+    With ``use_qk_l2norm`` the recurrence runs on ``l2norm(q)``, ``l2norm(k)``.
+    """
+    if use_qk_l2norm:
+        q, k = l2norm(q), l2norm(k)
     p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
     h0 = p.state_in(initial_state, state_v_first)
     o = np.zeros((p.Ttot, p.Hv, p.V))
@@ -150,13 +183,19 @@ def fwd(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None, state_v_fi
 
 
 def bwd(q, k, v, g, beta, scale, do, initial_state=None, dht=None, cu_seqlens=None,
-        state_v_first=False, heads=None, nthreads=0):
+        state_v_first=False, heads=None, nthreads=0, use_qk_l2norm=False):
     """Gradients of ``sum(do*o) + sum(dht*final_state)`` by the hand-derived
     reverse pass of the token recurrence.
 
     Returns ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is with respect to the raw
-    log-decay g; ``dh0`` is ``None`` when ``initial_state`` is ``None``.
+    log-decay g; ``dh0`` is ``None`` when ``initial_state`` is ``None``.  With
+    ``use_qk_l2norm`` dq and dk are with respect to the raw q and k.
     """
+    if use_qk_l2norm:
+        raw = (q, k)
+        grads = bwd(l2norm(q), l2norm(k), v, g, beta, scale, do, initial_state, dht, cu_seqlens,
+                    state_v_first, heads, nthreads)
+        return (l2norm_bwd(raw[0], grads[0]), l2norm_bwd(raw[1], grads[1])) + tuple(grads[2:])
     p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
     h0 = p.state_in(initial_state, state_v_first)
     dht_ = p.state_in(dht, state_v_first)
@@ -185,14 +224,17 @@ def chunk_offsets(cu, chunk):
 
 
 def chunked_fwd(q, k, v, g, beta, scale, chunk=64, initial_state=None, cu_seqlens=None,
-                state_v_first=False, heads=None, nthreads=0):
+                state_v_first=False, heads=None, nthreads=0, use_qk_l2norm=False):
     """Naive fp64 chunked form.
 
     Returns ``(g_cum [B,T,Hv], A [B,T,Hv,chunk], o [B,T,Hv,V],
     h [NCtot,Hv,K,V], final_state [N,Hv,K,V])``; ``h`` holds chunk-start states
     (``[NCtot,Hv,V,K]`` with ``state_v_first``), row ``r`` of a chunk's ``A`` is
     stored at token ``chunk_start + r`` and columns past a partial chunk are 0.
+    ``use_qk_l2norm`` as in :func:`fwd`.
     """
+    if use_qk_l2norm:
+        q, k = l2norm(q), l2norm(k)
     p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
     h0 = p.state_in(initial_state, state_v_first)
     nct = int(chunk_offsets(p.cu, chunk)[-1])
@@ -213,8 +255,14 @@ def chunked_fwd(q, k, v, g, beta, scale, chunk=64, initial_state=None, cu_seqlen
 
 
 def chunked_bwd(q, k, v, g, beta, scale, do, chunk=64, initial_state=None, dht=None,
-                cu_seqlens=None, state_v_first=False, heads=None, nthreads=0):
+                cu_seqlens=None, state_v_first=False, heads=None, nthreads=0,
+                use_qk_l2norm=False):
     """Reverse pass of the naive chunked form; same outputs as :func:`bwd`."""
+    if use_qk_l2norm:
+        raw = (q, k)
+        grads = chunked_bwd(l2norm(q), l2norm(k), v, g, beta, scale, do, chunk, initial_state,
+                            dht, cu_seqlens, state_v_first, heads, nthreads)
+        return (l2norm_bwd(raw[0], grads[0]), l2norm_bwd(raw[1], grads[1])) + tuple(grads[2:])
     p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
     h0 = p.state_in(initial_state, state_v_first)
     dht_ = p.state_in(dht, state_v_first)

@@ -323,3 +323,119 @@ def test_heads_mask_samples_units():
     np.testing.assert_array_equal(o[:, :, 2:], o2[:, :, 2:])
     assert np.all(o2[:, :, :2] == 0)
     np.testing.assert_array_equal(ht[:, 2:], ht2[:, 2:])
+
+
+# ---- use_qk_l2norm: the recurrence on per-(token, head) unit-length q and k ----
+
+def _raw_qk(d, rng):
+    """Rows of q and k with lengths spread over [1.5, 6] (not unit length)."""
+    for name in ("q", "k"):
+        x = d[name]
+        x /= np.linalg.norm(x, axis=-1, keepdims=True)
+        x *= rng.uniform(1.5, 6.0, size=x.shape[:-1] + (1,))
+    return d
+
+
+def test_l2norm_backward_matches_finite_differences():
+    """dq and dk through the normalisation (and every other gradient) against
+    central differences of the normalised forward."""
+    rng = np.random.default_rng(11)
+    d = _raw_qk(rand_problem(1, 0, 1, 2, 3, 4, rng, varlen=[3, 4]), rng)
+    scale = 0.7
+    o, ht = oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale,
+                       initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+                       use_qk_l2norm=True)
+    do = rng.normal(size=o.shape)
+    dht = rng.normal(size=ht.shape)
+
+    def L():
+        o, ht = oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale,
+                           initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+                           use_qk_l2norm=True)
+        return float(np.sum(o * do) + np.sum(ht * dht))
+
+    grads = oracle.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, do,
+                       initial_state=d["initial_state"], dht=dht, cu_seqlens=d["cu_seqlens"],
+                       use_qk_l2norm=True)
+    eps = 1e-6
+    for gi, name in enumerate(["q", "k", "v", "beta", "g", "initial_state"]):
+        x = d[name]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            orig = x[idx]
+            x[idx] = orig + eps
+            lp = L()
+            x[idx] = orig - eps
+            lm = L()
+            x[idx] = orig
+            fd[idx] = (lp - lm) / (2 * eps)
+        scl = max(1.0, np.abs(fd).max())
+        assert np.abs(fd - grads[gi]).max() <= 1e-7 * scl, (name, np.abs(fd - grads[gi]).max())
+
+
+def test_l2norm_scale_invariance():
+    """Scaling rows of q and k by positive factors leaves the normalised
+    recurrence unchanged (up to eps / |x|^2 < 1e-6) and divides dq, dk by the
+    factors; without the option the output changes."""
+    rng = np.random.default_rng(12)
+    d = _raw_qk(rand_problem(2, 6, 2, 4, 8, 5, rng), rng)
+    scale = 0.5
+    cq = rng.uniform(1.0, 4.0, size=d["q"].shape[:-1] + (1,))
+    ck = rng.uniform(1.0, 4.0, size=d["k"].shape[:-1] + (1,))
+    args = (d["v"], d["g"], d["beta"], scale)
+    o1, h1 = oracle.fwd(d["q"], d["k"], *args, initial_state=d["initial_state"], use_qk_l2norm=True)
+    o2, h2 = oracle.fwd(cq * d["q"], ck * d["k"], *args, initial_state=d["initial_state"],
+                        use_qk_l2norm=True)
+    assert np.abs(o1 - o2).max() <= 1e-6 * np.abs(o1).max()
+    assert np.abs(h1 - h2).max() <= 1e-6 * np.abs(h1).max()
+    o3, _ = oracle.fwd(cq * d["q"], ck * d["k"], *args, initial_state=d["initial_state"])
+    assert np.abs(o1 - o3).max() > 1e-2 * np.abs(o1).max()
+    do = rng.normal(size=o1.shape)
+    g1 = oracle.bwd(d["q"], d["k"], *args, do, initial_state=d["initial_state"], use_qk_l2norm=True)
+    g2 = oracle.bwd(cq * d["q"], ck * d["k"], *args, do, initial_state=d["initial_state"],
+                    use_qk_l2norm=True)
+    assert np.abs(g1[0] - cq * g2[0]).max() <= 1e-6 * np.abs(g1[0]).max()
+    assert np.abs(g1[1] - ck * g2[1]).max() <= 1e-6 * np.abs(g1[1]).max()
+    for i in (2, 3, 4):
+        assert np.abs(g1[i] - g2[i]).max() <= 1e-6 * np.abs(g1[i]).max()
+
+
+def test_l2norm_on_unit_rows_is_the_plain_recurrence():
+    """Unit-length rows: the option changes nothing beyond the 1e-6 eps, in
+    either direction (dq, dk lose only their component along q, k)."""
+    rng = np.random.default_rng(13)
+    d = rand_problem(1, 7, 1, 2, 6, 3, rng)
+    d["q"] /= np.linalg.norm(d["q"], axis=-1, keepdims=True)
+    scale = 0.9
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], scale)
+    o1, h1 = oracle.fwd(*args, initial_state=d["initial_state"], use_qk_l2norm=True)
+    o0, h0 = oracle.fwd(*args, initial_state=d["initial_state"])
+    assert np.abs(o1 - o0).max() <= 2e-6 * np.abs(o0).max()
+    assert np.abs(h1 - h0).max() <= 2e-6 * np.abs(h0).max()
+    do = rng.normal(size=o0.shape)
+    g1 = oracle.bwd(*args, do, initial_state=d["initial_state"], use_qk_l2norm=True)
+    g0 = oracle.bwd(*args, do, initial_state=d["initial_state"])
+    for x, i in ((d["q"], 0), (d["k"], 1)):
+        proj = g0[i] - x * np.sum(x * g0[i], axis=-1, keepdims=True)
+        assert np.abs(g1[i] - proj).max() <= 2e-6 * np.abs(g0[i]).max()
+    for i in (2, 3, 4, 5):
+        assert np.abs(g1[i] - g0[i]).max() <= 2e-6 * np.abs(g0[i]).max()
+
+
+def test_l2norm_gradient_is_orthogonal_to_the_input():
+    """The loss does not change along q or k, so dq . q = dk . k = 0 per row
+    (up to the eps term, relative size eps / |x|^2)."""
+    rng = np.random.default_rng(14)
+    d = _raw_qk(rand_problem(1, 9, 2, 2, 8, 4, rng), rng)
+    o, _ = oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], 0.4,
+                      initial_state=d["initial_state"], use_qk_l2norm=True)
+    do = rng.normal(size=o.shape)
+    gr = oracle.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], 0.4, do,
+                    initial_state=d["initial_state"], use_qk_l2norm=True)
+    for x, dx in ((d["q"], gr[0]), (d["k"], gr[1])):
+        dots = np.abs(np.sum(x * dx, axis=-1))
+        scl = np.linalg.norm(x, axis=-1) * np.linalg.norm(dx, axis=-1)
+        assert np.all(dots <= 1e-6 * scl + 1e-300)
+        assert np.all(np.linalg.norm(dx, axis=-1) > 0)
