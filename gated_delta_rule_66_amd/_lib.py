@@ -29,6 +29,7 @@ class Problem(ctypes.Structure):
         ("state_v_first", ctypes.c_int32),
         ("cp_segments", ctypes.c_int32),
         ("wave_tiles", ctypes.c_int32),
+        ("use_qk_l2norm", ctypes.c_int32),
     ]
 
 

@@ -183,6 +183,8 @@ static gdr_status validate(const gdr_problem* p, char* reason, size_t len) {
   if (p->cp_segments < 0) return fail(GDR_ERR_ARG, reason, len, "cp_segments must be >= 0");
   if (p->wave_tiles < 0 || p->wave_tiles > 2)
     return fail(GDR_ERR_ARG, reason, len, "wave_tiles must be 0, 1 or 2");
+  if (p->use_qk_l2norm != 0 && p->use_qk_l2norm != 1)
+    return fail(GDR_ERR_ARG, reason, len, "use_qk_l2norm must be 0 or 1");
   const bool has_dev = p->cu_seqlens_dev != nullptr, has_host = p->cu_seqlens_host != nullptr;
   if (has_dev != has_host)
     return fail(GDR_ERR_VARLEN, reason, len,

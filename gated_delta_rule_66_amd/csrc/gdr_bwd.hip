@@ -52,6 +52,7 @@ struct DhArgs {
   int P, nvs;
   float scale;
   int svf;
+  int qk_norm;  // q, k rows scaled to unit length before use
 };
 
 template <typename T, int VB, int MODE>
@@ -146,6 +147,10 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
   __builtin_amdgcn_s_waitcnt(0);
   if (sr.c0 < sr.c1) prefetch(sr.c1 - 1);
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
+    if (a.qk_norm) {
+      if (!isT) l2norm_rows<T, 256>(rq, nullptr);
+      l2norm_rows<T, 256>(rk, nullptr);
+    }
     __syncthreads();
     if (!isT) tile_store<T, 128, 256>(Qs, LD, rq);
     tile_store<T, 128, 256>(Ks, LD, rk);
@@ -449,6 +454,10 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
     __syncthreads();
     if (helper) {
+      if (a.qk_norm) {
+        l2norm_rows<T, 256>(rq, nullptr, otid);
+        l2norm_rows<T, 256>(rk, nullptr, otid);
+      }
       tile_store<T, 128, 256>(Qs, LD, rq, otid);
       tile_store<T, 128, 256>(Ks, LD, rk, otid);
       tile_store<T, CW, 256>(Ds, LDV, rd, otid);
@@ -668,6 +677,7 @@ struct GradArgs {
   int N, T, Hq, Hv, nc_dense, g_dtype;
   float scale;
   int partial;
+  int qk_norm;  // q, k rows scaled to unit length before use
 };
 
 // Eight waves: wave w works on row / column block wr = w % 4 and takes one
@@ -701,6 +711,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   __shared__ float dgam[64];
   __shared__ float fsum[4][4];       // F partials per (row block, lane group)
   __shared__ float rowq[64];         // dgamma row terms of the dq side
+  __shared__ float xinv[2][64];      // 1 / |q|, 1 / |k| per row (q / k normalisation)
 
   const int c = blockIdx.x, h = blockIdx.y;
   int n, j;
@@ -754,6 +765,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     tile_load<T, 64, 512>(ra, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
                           (int64_t)a.Hv * kChunk, Cc);
     load_half(0);
+    if (a.qk_norm) {
+      l2norm_rows<T, 512>(rq, xinv[0]);
+      l2norm_rows<T, 512>(rk, xinv[1]);
+    }
     tile_store<T, 128, 512>(Qs, LD, rq);
     tile_store<T, 128, 512>(Ks, LD, rk);
     tile_store<T, 64, 512>(As, L7, ra);
@@ -1072,6 +1087,29 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       }
     }
   }
+  // With q / k normalisation dxv is the gradient with respect to the unit
+  // rows x^ (q^ on side 0, k^ on side 1); the raw rows' gradient is
+  // (dxv - x^ (x^ . dxv)) / |x|.  With value-head partials (Hq < Hv) the
+  // group sum comes first, so that step runs in gva_reduce_kernel.
+  if (a.qk_norm && !a.partial) {
+    const T* X = hi ? Ks : Qs;
+    float dot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const f32x4 xd = frag_d4(X, LD, 16 * wr, 16 * kb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot[e] += xd[e] * dxv[kb][e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dot[e] = sum16(dot[e]);
+    const f32x4 ri = *reinterpret_cast<const f32x4*>(xinv[hi ? 1 : 0] + 16 * wr + 4 * grp);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const f32x4 xd = frag_d4(X, LD, 16 * wr, 16 * kb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dxv[kb][e] = ri[e] * (dxv[kb][e] - xd[e] * dot[e]);
+    }
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     rs1[e] = sum16(rs1[e]);
@@ -1151,26 +1189,63 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   }
 }
 
-// B6: dq[t, hq] = sum over the group's value heads, in head order
+// B6: dq[t, hq] = sum over the group's value heads, in head order, and the
+// same for dk.  Sixteen consecutive lanes take one (token, q head) row, eight
+// keys each.  With q / k normalisation the sum is the gradient with respect
+// to the unit row x^ = x / |x| (|x| = sqrt(sum x^2 + eps), recomputed from the
+// raw row in fp32) and the raw row's gradient is (d - x^ (x^ . d)) / |x|.
 template <typename T>
-__global__ void gva_reduce_kernel(const float* pq, const float* pk, T* dq, T* dk, int64_t Ttot,
-                                  int Hq, int Hv) {
+__device__ __forceinline__ void gva_row_out(const float* part, const T* x, T* out, int64_t t,
+                                            int hq, int Hq, int Hv, int key0, int qk_norm) {
   const int G = Hv / Hq;
-  const int64_t total = Ttot * Hq * kDim;
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < total;
-       x += (int64_t)gridDim.x * blockDim.x) {
-    const int key = (int)(x % kDim);
-    const int64_t th = x / kDim;
-    const int hq = (int)(th % Hq);
-    const int64_t t = th / Hq;
-    float sq = 0.f, sk = 0.f;
-    for (int r = 0; r < G; ++r) {
-      const int64_t src = (t * Hv + hq * G + r) * kDim + key;
-      sq += pq[src];
-      sk += pk[src];
+  float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < G; ++r) {
+    const float* src = part + (t * Hv + (int64_t)hq * G + r) * kDim + key0;
+    const float4 lo = *reinterpret_cast<const float4*>(src);
+    const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+    d[0] += lo.x; d[1] += lo.y; d[2] += lo.z; d[3] += lo.w;
+    d[4] += hi.x; d[5] += hi.y; d[6] += hi.z; d[7] += hi.w;
+  }
+  const int64_t row = (t * Hq + hq) * kDim + key0;
+  if (qk_norm) {
+    const typename VT<T>::x8 xv = *reinterpret_cast<const typename VT<T>::x8*>(x + row);
+    float f[8], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f[e] = to_f(xv[e]);
+      ss += f[e] * f[e];
     }
-    dq[x] = from_f<T>(sq);
-    dk[x] = from_f<T>(sk);
+    const float ri = rsqrtf(sum16(ss) + kQKNormEps);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f[e] *= ri;
+      dot += f[e] * d[e];
+    }
+    dot = sum16(dot);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = ri * (d[e] - f[e] * dot);
+  }
+  typename VT<T>::x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = from_f<T>(d[e]);
+  *reinterpret_cast<typename VT<T>::x8*>(out + row) = o;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gva_reduce_kernel(const float* pq, const float* pk,
+                                                         const T* q, const T* k, T* dq, T* dk,
+                                                         int64_t Ttot, int Hq, int Hv,
+                                                         int qk_norm) {
+  const int64_t rows = Ttot * Hq;
+  const int key0 = 8 * (threadIdx.x & 15);
+  // the 16 lanes of a row share the loop bounds, so the row sums stay whole
+  for (int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4; row < rows;
+       row += ((int64_t)gridDim.x * blockDim.x) >> 4) {
+    const int hq = (int)(row % Hq);
+    const int64_t t = row / Hq;
+    gva_row_out<T>(pq, q, dq, t, hq, Hq, Hv, key0, qk_norm);
+    gva_row_out<T>(pk, k, dk, t, hq, Hq, Hv, key0, qk_norm);
   }
 }
 
@@ -1282,6 +1357,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   sa.cu = p->cu_seqlens_dev; sa.offs = offs;
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1; sa.scale = p->scale; sa.svf = p->state_v_first ? 1 : 0; sa.h_svf = 1;
+  sa.qk_norm = p->use_qk_l2norm ? 1 : 0;
   sa.seg_out = cp_out; sa.seg_start = cp_start; sa.reverse = 0;
   // B2: state gradients (value-major)
   DhArgs da;
@@ -1289,7 +1365,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   da.dh = dhbuf; da.dh0 = dh0; da.seg_start = cp2_start; da.seg_out = cp2_out;
   da.cu = p->cu_seqlens_dev; da.offs = offs;
   da.N = pl.N; da.T = p->T; da.Hq = p->Hq; da.Hv = p->Hv; da.nc_dense = pl.nc_dense;
-  da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf;
+  da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf; da.qk_norm = sa.qk_norm;
   if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, st);
   else launch_bwd_scans<T, 1>(pl, sa, da, st);
   // B3-B5
@@ -1303,17 +1379,19 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   ga.cu = p->cu_seqlens_dev; ga.offs = offs;
   ga.N = pl.N; ga.T = p->T; ga.Hq = p->Hq; ga.Hv = p->Hv; ga.nc_dense = pl.nc_dense;
   ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale; ga.partial = partial ? 1 : 0;
+  ga.qk_norm = sa.qk_norm;
   if (pl.total_chunks > 0)
     GDR_LAUNCH("grad", grad_kernel<T>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(512), st, ga);
   // B6
   if (partial) {
     const int64_t Ttot = (int64_t)p->B * p->T;
-    const int64_t total = Ttot * p->Hq * kDim;
-    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+    const int64_t threads = Ttot * p->Hq * 16;  // 16 lanes per (token, q head) row
+    const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 8192);
     GDR_LAUNCH("gva_reduce", gva_reduce_kernel<T>, dim3(blocks), dim3(256), st,
-                       reinterpret_cast<const float*>(ws + L.pq),
-                       reinterpret_cast<const float*>(ws + L.pk), reinterpret_cast<T*>(dq),
-                       reinterpret_cast<T*>(dk), Ttot, p->Hq, p->Hv);
+               reinterpret_cast<const float*>(ws + L.pq), reinterpret_cast<const float*>(ws + L.pk),
+               reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k),
+               reinterpret_cast<T*>(dq), reinterpret_cast<T*>(dk), Ttot, p->Hq, p->Hv,
+               ga.qk_norm);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

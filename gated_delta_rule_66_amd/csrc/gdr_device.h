@@ -424,6 +424,40 @@ __device__ __forceinline__ float sum4g(float v) {
   return __builtin_bit_cast(float, (int)p32[0]) + __builtin_bit_cast(float, (int)p32[1]);
 }
 
+// ---- q / k L2 normalisation ------------------------------------------------
+// The use_qk_l2norm_in_kernel option that the FLA backend pull request's
+// dispatch passes through: q and k rows (one per token and head) are scaled
+// to unit length over K, x / sqrt(sum x^2 + eps), in fp32 and rounded back
+// to the input type before any product reads them.
+constexpr float kQKNormEps = 1e-6f;
+
+// Normalises every row of a 64 x 128 register tile in place.  Thread x holds
+// 8 elements of row x / 16 and the 16 threads of a row are 16 aligned
+// consecutive lanes, so the row's sum of squares is one 16-lane DPP sum
+// (fixed order).  With `rinv`, 1 / sqrt(sum x^2 + eps) of row r goes to
+// rinv[r].  Rows past the chunk end load as zeros and stay zero.
+template <typename T, int NT>
+__device__ __forceinline__ void l2norm_rows(TileRegs<128, NT>& t, float* rinv,
+                                            int t0 = threadIdx.x) {
+#pragma unroll
+  for (int i = 0; i < TileRegs<128, NT>::N; ++i) {
+    typename VT<T>::x8 x = __builtin_bit_cast(typename VT<T>::x8, t.r[i]);
+    float f[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f[e] = to_f(x[e]);
+      ss += f[e] * f[e];
+    }
+    const float ri = rsqrtf(sum16(ss) + kQKNormEps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = from_f<T>(f[e] * ri);
+    t.r[i] = __builtin_bit_cast(uint4, x);
+    const int xr = t0 + i * NT;
+    if (rinv != nullptr && (xr & 15) == 0) rinv[xr >> 4] = ri;
+  }
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (fixed combination order).
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   const int l = lane_id();

@@ -45,6 +45,7 @@ struct FwdArgs {
   int g_dtype;
   float scale;
   int svf;
+  int qk_norm;  // q, k rows scaled to unit length before use
 };
 
 template <typename T>
@@ -83,6 +84,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
     bet[l] = bv;
     if (l < Cc) a.gcum[(t0 + l) * a.Hv + h] = gc;
   }
+  if (a.qk_norm) l2norm_rows<T, 256>(rk, nullptr);
   tile_store<T, 128, 256>(Ks, LDK, rk);
   __syncthreads();
 
@@ -231,6 +233,7 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   fa.cu = p->cu_seqlens_dev; fa.offs = offs;
   fa.N = pl.N; fa.T = p->T; fa.Hq = p->Hq; fa.Hv = p->Hv; fa.nc_dense = pl.nc_dense;
   fa.g_dtype = (int)p->g_dtype; fa.scale = p->scale; fa.svf = p->state_v_first ? 1 : 0;
+  fa.qk_norm = p->use_qk_l2norm ? 1 : 0;
 
   ScanArgs sa;
   sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
@@ -238,7 +241,7 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   sa.cu = p->cu_seqlens_dev; sa.offs = offs;
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1;
-  sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf;
+  sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf; sa.qk_norm = fa.qk_norm;
   sa.seg_out = nullptr; sa.seg_start = nullptr;
   sa.reverse = 0;
   if (pl.cp > 1) {

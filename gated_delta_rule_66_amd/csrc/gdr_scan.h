@@ -70,6 +70,7 @@ struct ScanArgs {
   int svf;     // layout of h0 / ht / user h
   int h_svf;   // layout of h: the user's h follows svf; MODE_STATE always writes [V][K]
   int reverse; // cp_combine_kernel: chain segments backwards (state gradients)
+  int qk_norm; // q, k rows scaled to unit length before use
 };
 
 // Chunks [c0, c1) of segment p; the segment holding the last chunk is
@@ -189,6 +190,10 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
   for (int c = sr.c0; c < sr.c1; ++c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+    if (a.qk_norm) {
+      if (OUT) l2norm_rows<T, 256>(rq, nullptr);
+      l2norm_rows<T, 256>(rk, nullptr);
+    }
     __syncthreads();  // the previous chunk is done with LDS
     if (OUT) tile_store<T, 128, 256>(Qs, LD, rq);
     tile_store<T, 128, 256>(Ks, LD, rk);
@@ -538,6 +543,10 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
     const int b = OUT ? (it & 1) : 0;
     __syncthreads();  // iteration it-1 is done with every buffer rewritten here
     if (outw && it < sr.c1) {
+      if (a.qk_norm) {
+        if (OUT) l2norm_rows<T, 256>(rq, nullptr, otid);
+        l2norm_rows<T, 256>(rk, nullptr, otid);
+      }
       if (OUT) tile_store_q<T, 256>(Qs[b], rq, otid);
       tile_store_q<T, 256>(Ks[b], rk, otid);
       tile_store<T, 64, 256>(Vs, LDV, rv, otid);

@@ -93,6 +93,15 @@ typedef struct {
                                      every sequence into up to s segments */
   int32_t wave_tiles;             /* 16-column state tiles per wave in the scans:
                                      0 = automatic, 1 or 2 */
+  int32_t use_qk_l2norm;          /* 1: every kernel scales q and k per (token,
+                                     head) to unit length over K before use,
+                                     x / sqrt(sum x^2 + 1e-6) in fp32, and the
+                                     backward's dq, dk are with respect to the
+                                     raw q, k; 0: q and k are used as given.
+                                     The option the FLA backend pull request
+                                     ("[GDN] Add FlashQLA backend dispatch",
+                                     the dispatch's argument list) passes as
+                                     use_qk_l2norm_in_kernel. */
 } gdr_problem;
 
 /* Status name ("GDR_ERR_SHAPE", ...). */

@@ -40,7 +40,7 @@ def test_status_strings():
 def good(**kw):
     base = dict(B=2, T=200, Hq=2, Hv=4, K=128, V=128, N=2, cu_seqlens_dev=None,
                 cu_seqlens_host=None, in_dtype=GDR_BF16, g_dtype=GDR_BF16, scale=0.088,
-                state_v_first=0, cp_segments=0, wave_tiles=0)
+                state_v_first=0, cp_segments=0, wave_tiles=0, use_qk_l2norm=0)
     base.update(kw)
     return Problem(**base)
 
@@ -54,6 +54,7 @@ def check(p):
 def test_acceptance_path():
     assert check(good()) == ("GDR_OK", "")
     assert check(good(in_dtype=GDR_FP16, g_dtype=GDR_FP32))[0] == "GDR_OK"
+    assert check(good(use_qk_l2norm=1))[0] == "GDR_OK"
 
 
 HOST_CU = (ctypes.c_int32 * 4)(0, 70, 70, 200)
@@ -81,6 +82,7 @@ REJECT = [
     ("svf", good(state_v_first=2), "GDR_ERR_ARG", "state_v_first"),
     ("cp", good(cp_segments=-1), "GDR_ERR_ARG", "cp_segments"),
     ("wave_tiles", good(wave_tiles=3), "GDR_ERR_ARG", "wave_tiles"),
+    ("qk_l2norm", good(use_qk_l2norm=2), "GDR_ERR_ARG", "use_qk_l2norm"),
 ]
 
 
