@@ -41,7 +41,8 @@ WORKLOADS = {
 DEFAULT = "fwd_bwd_B2_T4096_H32_bf16"
 
 
-def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True, with_dht=True):
+def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True, with_dht=True,
+                 qk_norm=False):
     """Algorithmic HBM bytes of one launch of a library kernel: every operand
     read once and every result written once (the minimum any schedule of that
     kernel must move).  Per (token, value head) terms with r = Hq / Hv:
@@ -80,7 +81,8 @@ def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True,
         return TH * (512 * r + 256 + 256 + 128 + 4 + isz + dqk + 256 + isz + gsz) + NCH * 2 * ch
     if name == "gva_reduce":
         G = Hv // Hq
-        return B * T * Hq * 128 * (2 * 4 * G + 2 * isz)
+        # fp32 partials in, dq / dk out; with q / k normalisation the raw rows too
+        return B * T * Hq * 128 * (2 * 4 * G + 2 * isz + (2 * isz if qk_norm else 0))
     if name == "chunk_offsets":
         return 8 * (N + 1)
     return None
@@ -114,7 +116,7 @@ def measured_traffic(kernel, workload, launches_bytes):
     return (k["fetch_kib"] * t["fetch_factor"] + k["write_kib"] * t["write_factor"]) * 1024.0
 
 
-def cpu_baseline(d, prob, nthreads_cap=16, max_units=32):
+def cpu_baseline(d, prob, nthreads_cap=16, max_units=32, qk_norm=False):
     """The fp64 oracle, as it stands, on a bounded sample of the workload."""
     import numpy as np
     import oracle
@@ -147,9 +149,10 @@ def cpu_baseline(d, prob, nthreads_cap=16, max_units=32):
     units = nh * nseq
     threads = max(1, min(nthreads_cap, avail, units))
     t0 = time.perf_counter()
-    oracle.fwd(q, k, v, g, beta, d["scale"], initial_state=h0, cu_seqlens=cun, nthreads=threads)
+    oracle.fwd(q, k, v, g, beta, d["scale"], initial_state=h0, cu_seqlens=cun, nthreads=threads,
+               use_qk_l2norm=qk_norm)
     oracle.bwd(q, k, v, g, beta, d["scale"], do, initial_state=h0, dht=dht, cu_seqlens=cun,
-               nthreads=threads)
+               nthreads=threads, use_qk_l2norm=qk_norm)
     dt = time.perf_counter() - t0
     total_units = (B if cu is None else nseq) * Hv
     frac = units / float(total_units)
@@ -175,6 +178,8 @@ def main():
                     help="run one plain 256 MiB device copy first (counter calibration)")
     ap.add_argument("--vt", type=int, default=0,
                     help="16-column state tiles per wave in the scans (0 = the library's plan)")
+    ap.add_argument("--qk-l2norm", action="store_true",
+                    help="raw q / k rows, normalised inside the kernels (use_qk_l2norm_in_kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path runs on a single MI355X and this build "
@@ -187,7 +192,8 @@ def main():
 
     B, T, Hq, Hv, dt, g_shift, varlen = WORKLOADS[args.workload]
     prob = gdr_synth.Problem(args.workload, B=B, T=T, Hq=Hq, Hv=Hv, dtype=dt, init_state=True,
-                             backward=True, dht=True, g_shift=g_shift)
+                             backward=True, dht=True, g_shift=g_shift, qk_l2norm=args.qk_l2norm)
+    qkn = args.qk_l2norm
     d = gdr_synth.make(prob, lengths_from=varlen)
     B, T = prob.B, prob.T
     dev = torch.device("cuda", 0)
@@ -203,14 +209,16 @@ def main():
                                               scale=dd["scale"], initial_state=dd["h0"],
                                               output_final_state=True,
                                               cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=cu_cpu,
-                                              cp_segments=args.cp, wave_tiles=args.vt)
+                                              cp_segments=args.cp, wave_tiles=args.vt,
+                                              use_qk_l2norm_in_kernel=qkn)
 
     def bwd(g_cum, A):
         return gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
                                               dd["do"], dht=dd["dht"], scale=dd["scale"],
                                               initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
                                               dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu,
-                                              cp_segments=args.cp, wave_tiles=args.vt)
+                                              cp_segments=args.cp, wave_tiles=args.vt,
+                                              use_qk_l2norm_in_kernel=qkn)
 
     def step():
         g_cum, A, o, _, ht = fwd()
@@ -271,11 +279,12 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n][0])
     avg_s = kernels[dom][0] / kernels[dom][1] * 1e-3
     dom_cp = plans["bwd" if dom.startswith(("bwd", "grad", "gva")) else "fwd"][0]
-    nbytes = kernel_bytes(dom, B, T, Hq, Hv, nchunks, N, dom_cp)
+    nbytes = kernel_bytes(dom, B, T, Hq, Hv, nchunks, N, dom_cp, qk_norm=qkn)
     achieved = nbytes / avg_s / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, args.workload, nbytes),
+                "traffic": measured_traffic(dom, args.workload + ("+qk_l2norm" if qkn else ""),
+                                            nbytes),
                 "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2)}
 
     out = {
@@ -290,12 +299,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dt,
-        "data": "synthetic (seeded; q,k L2-normalised, g=logsigmoid, beta=sigmoid)",
+        "data": ("synthetic (seeded; raw N(0,1) q,k normalised in-kernel, g=logsigmoid, "
+                 "beta=sigmoid)" if qkn else
+                 "synthetic (seeded; q,k L2-normalised, g=logsigmoid, beta=sigmoid)"),
         "config": {"workload": args.workload, "B": B, "T": T, "Hq": Hq, "Hv": Hv, "K": 128,
                    "V": 128, "chunk": 64, "tokens": tokens,
                    "cp_segments": {k_: v_[0] for k_, v_ in plans.items()},
                    "wave_tiles": {k_: v_[1] for k_, v_ in plans.items()},
-                   "parallelism": "single GPU"},
+                   "qk_l2norm_in_kernel": qkn, "parallelism": "single GPU"},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "tflops": round(tflops, 3),
@@ -305,7 +316,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(d, (B, T, Hq, Hv))
+        out["cpu_baseline"] = cpu_baseline(d, (B, T, Hq, Hv), qk_norm=qkn)
     print(json.dumps(out), flush=True)
 
 

@@ -337,7 +337,7 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
 // B2 output pass (one 64-column block, 8 waves): waves 4-7 issue every
 // chunk load and tile store, waves 0-3 run the chain of dh_body unchanged, so
 // the vector-memory issue is off the chain.
-template <typename T>
+template <typename T, bool QKN>
 __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   constexpr int VB = 1, MODE = MODE_OUT;
   typedef typename VT<T>::x8 x8;
@@ -454,7 +454,7 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
     __syncthreads();
     if (helper) {
-      if (a.qk_norm) {
+      if (QKN) {
         l2norm_rows<T, 256>(rq, nullptr, otid);
         l2norm_rows<T, 256>(rk, nullptr, otid);
       }
@@ -638,10 +638,10 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
 
 // The output passes of B1 and B2 with load-helper waves (VB = 1), in one
 // launch of 8-wave workgroups: blocks [0, n1) take B1.
-template <typename T>
+template <typename T, bool QKN>
 __global__ __launch_bounds__(512) void bwd_scans_lh_kernel(ScanArgs sa, DhArgs da, int n1) {
-  if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE>(sa, xcd_block(blockIdx.x, n1));
-  else dh_lh_body<T>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
+  if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE, QKN>(sa, xcd_block(blockIdx.x, n1));
+  else dh_lh_body<T, QKN>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
 }
 
 // The state scan (B1) and the state-gradient scan (B2) are independent (B2
@@ -686,7 +686,7 @@ struct GradArgs {
 // (K dSn, dDelta, dR, dX = -dR S^T, dKs = Delta dSn^T, dM and everything of
 // dk).  The two sides of a phase are independent, so two waves share each
 // SIMD and hide each other's latencies.
-template <typename T>
+template <typename T, bool QKN>
 __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   typedef typename VT<T>::x8 x8;
   constexpr int LD = 136;  // q, k, and the value-major S / dSn halves
@@ -765,7 +765,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     tile_load<T, 64, 512>(ra, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
                           (int64_t)a.Hv * kChunk, Cc);
     load_half(0);
-    if (a.qk_norm) {
+    if (QKN) {
       l2norm_rows<T, 512>(rq, xinv[0]);
       l2norm_rows<T, 512>(rk, xinv[1]);
     }
@@ -1091,7 +1091,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   // rows x^ (q^ on side 0, k^ on side 1); the raw rows' gradient is
   // (dxv - x^ (x^ . dxv)) / |x|.  With value-head partials (Hq < Hv) the
   // group sum comes first, so that step runs in gva_reduce_kernel.
-  if (a.qk_norm && !a.partial) {
+  if (QKN && !a.partial) {
     const T* X = hi ? Ks : Qs;
     float dot[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1315,7 +1315,12 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t
   sa.nvs = da.nvs = 2 / VB;
   const unsigned n1 = units * pl.cp * sa.nvs;
   if (VB == 1)
-    GDR_LAUNCH("bwd_scans", bwd_scans_lh_kernel<T>, dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+    if (sa.qk_norm)
+      GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, true>), dim3(2 * n1), dim3(512), st, sa, da,
+                 (int)n1);
+    else
+      GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, false>), dim3(2 * n1), dim3(512), st, sa, da,
+                 (int)n1);
   else
     GDR_LAUNCH("bwd_scans", (bwd_scans_kernel<T, VB, MODE_STATE, MODE_OUT>), dim3(2 * n1),
                dim3(256), st, sa, da, (int)n1);
@@ -1380,8 +1385,12 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   ga.N = pl.N; ga.T = p->T; ga.Hq = p->Hq; ga.Hv = p->Hv; ga.nc_dense = pl.nc_dense;
   ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale; ga.partial = partial ? 1 : 0;
   ga.qk_norm = sa.qk_norm;
-  if (pl.total_chunks > 0)
-    GDR_LAUNCH("grad", grad_kernel<T>, dim3((unsigned)pl.total_chunks, p->Hv), dim3(512), st, ga);
+  if (pl.total_chunks > 0 && ga.qk_norm)
+    GDR_LAUNCH("grad", (grad_kernel<T, true>), dim3((unsigned)pl.total_chunks, p->Hv), dim3(512),
+               st, ga);
+  else if (pl.total_chunks > 0)
+    GDR_LAUNCH("grad", (grad_kernel<T, false>), dim3((unsigned)pl.total_chunks, p->Hv), dim3(512),
+               st, ga);
   // B6
   if (partial) {
     const int64_t Ttot = (int64_t)p->B * p->T;

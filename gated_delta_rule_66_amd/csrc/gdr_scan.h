@@ -449,8 +449,10 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
 //
 // MODE_STATE (the backward's chunk-start states) uses the same split with
 // waves 4-7 only loading and storing the chunk tiles, and the state waves
-// writing h (value-major) straight from registers.
-template <typename T, int MODE>
+// writing h (value-major) straight from registers.  QKN: q / k rows are
+// normalised to unit length after their loads (a template flag, so the
+// default path carries none of that code).
+template <typename T, int MODE, bool QKN>
 __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   typedef typename VT<T>::x8 x8;
   constexpr bool OUT = (MODE == MODE_OUT);
@@ -543,7 +545,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
     const int b = OUT ? (it & 1) : 0;
     __syncthreads();  // iteration it-1 is done with every buffer rewritten here
     if (outw && it < sr.c1) {
-      if (a.qk_norm) {
+      if (QKN) {
         if (OUT) l2norm_rows<T, 256>(rq, nullptr, otid);
         l2norm_rows<T, 256>(rk, nullptr, otid);
       }
@@ -683,9 +685,9 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   }
 }
 
-template <typename T>
+template <typename T, bool QKN>
 __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
-  scan_spec_body<T, MODE_OUT>(a, xcd_block(blockIdx.x, gridDim.x));
+  scan_spec_body<T, MODE_OUT, QKN>(a, xcd_block(blockIdx.x, gridDim.x));
 }
 
 // Pass 2: chain the segment start states of one (unit, 16-column block).
