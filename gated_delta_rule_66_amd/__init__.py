@@ -22,7 +22,8 @@ from ._lib import (GDR_BF16, GDR_FP16, GDR_FP32, GdrError, Problem, check, lib)
 
 __all__ = [
     "chunk_gated_delta_rule", "chunk_gated_delta_rule_fwd", "chunk_gated_delta_rule_bwd",
-    "prepare_lens", "prepare_chunk_indices", "prepare_chunk_offsets", "GdrError",
+    "fused_recurrent_gated_delta_rule", "prepare_lens", "prepare_chunk_indices",
+    "prepare_chunk_offsets", "GdrError",
 ]
 
 CHUNK = 64
@@ -203,6 +204,39 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     return _GatedDeltaRule.apply(q, k, v, g, beta, scale, initial_state, output_final_state,
                                  cu_seqlens, state_v_first, cp_segments, cu_seqlens_cpu,
                                  bool(use_qk_l2norm_in_kernel))
+
+
+def fused_recurrent_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
+                                     output_final_state=True, cu_seqlens=None,
+                                     state_v_first=False, use_qk_l2norm_in_kernel=False,
+                                     inplace_final_state=False, cu_seqlens_cpu=None):
+    """Forward one token at a time (decode steps, a few speculative tokens,
+    a prefill continued from a cached state).  Same inputs and outputs as
+    :func:`chunk_gated_delta_rule` without autograd: returns ``(o,
+    final_state)``; ``g`` is the raw log decay.  With ``inplace_final_state``
+    the fp32 ``initial_state`` tensor is updated in place and returned as the
+    final state."""
+    q, k, v, g, beta = _contig(q, k, v, g, beta)
+    c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, 1, 0,
+              use_qk_l2norm_in_kernel)
+    dev = q.device
+    B, T = q.shape[0], q.shape[1]
+    o = torch.empty(B, T, c.Hv, c.V, dtype=q.dtype, device=dev)
+    if inplace_final_state:
+        if (initial_state is None or initial_state.dtype != torch.float32
+                or not initial_state.is_contiguous()
+                or tuple(initial_state.shape) != c.state_shape(state_v_first)):
+            raise GdrError(10, "inplace_final_state needs a contiguous fp32 initial_state of "
+                               "shape %s" % (c.state_shape(state_v_first),))
+        ht = initial_state
+    else:
+        if initial_state is not None:
+            initial_state = initial_state.to(torch.float32).contiguous()
+        ht = torch.empty(c.state_shape(state_v_first), dtype=torch.float32, device=dev) \
+            if output_final_state else None
+    check(lib.gdr_recurrent_fwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(initial_state), _ptr(o), _ptr(ht), _stream(dev)))
+    return o, ht
 
 
 # ---- variable-length helpers ------------------------------------------------

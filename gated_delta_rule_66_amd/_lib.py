@@ -41,7 +41,7 @@ EXPORTS = [
     "gdr_prepare_chunk_indices_i32", "gdr_prepare_chunk_indices_i64",
     "gdr_prepare_chunk_offsets_i32", "gdr_prepare_chunk_offsets_i64",
     "gdr_prepare_chunk_token_starts_i64", "gdr_profile_enable", "gdr_profile_read",
-    "gdr_plan_info",
+    "gdr_plan_info", "gdr_recurrent_fwd",
 ]
 
 
@@ -74,6 +74,8 @@ def _declare(lib):
     lib.gdr_chunk_fwd.restype = st
     lib.gdr_chunk_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_chunk_bwd.restype = st
+    lib.gdr_recurrent_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P]
+    lib.gdr_recurrent_fwd.restype = st
     for name in ("gdr_prepare_lens_i32", "gdr_prepare_lens_i64"):
         getattr(lib, name).argtypes = [P, I64, P]
         getattr(lib, name).restype = st

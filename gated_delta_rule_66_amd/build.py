@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdr.so")
-SOURCES = ["gdr_api.cpp", "gdr_fwd.hip", "gdr_bwd.hip"]
+SOURCES = ["gdr_api.cpp", "gdr_fwd.hip", "gdr_bwd.hip", "gdr_recurrent.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

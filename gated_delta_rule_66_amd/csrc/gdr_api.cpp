@@ -399,6 +399,18 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
                     dg, initial_state ? dh0 : nullptr, workspace, (hipStream_t)stream);
 }
 
+gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                             const void* g, const void* beta, const float* initial_state,
+                             void* o, float* final_state, void* stream) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  if (!q || !k || !v || !g || !beta || !o)
+    return fail(GDR_ERR_NULL, nullptr, 0, "a required recurrent-forward pointer is NULL");
+  s = check_device_cached();
+  if (s != GDR_OK) return s;
+  return launch_recurrent(p, q, k, v, g, beta, initial_state, o, final_state, (hipStream_t)stream);
+}
+
 gdr_status gdr_plan_info(const gdr_problem* p, int backward, int32_t* cp_segments,
                          int32_t* wave_tiles) {
   gdr_status s = validate(p, nullptr, 0);

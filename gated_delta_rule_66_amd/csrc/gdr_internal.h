@@ -41,6 +41,11 @@ gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const
                       const void* dO, const float* dht, const float* h0, void* dq, void* dk,
                       void* dv, void* dbeta, void* dg, float* dh0, void* ws, hipStream_t st);
 
+// Token-by-token recurrence (decode and other short inputs), no workspace.
+gdr_status launch_recurrent(const gdr_problem* p, const void* q, const void* k, const void* v,
+                            const void* g, const void* beta, const float* h0, void* o,
+                            float* ht, hipStream_t st);
+
 struct ScanArgs;
 // The forward state scan (with the CP passes when pl.cp > 1).  mode 0 writes
 // outputs, mode 2 only the chunk-start states.

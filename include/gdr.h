@@ -150,6 +150,27 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
                          void* dv, void* dbeta, void* dg, float* dh0, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Token-by-token forward for short inputs: decode steps, a few speculative
+ * tokens, or a prefill continued from a cached state (the "state-cached
+ * continuation" the "flashqla-linear-attention" page lists among its
+ * topics).  The same o and final_state as gdr_chunk_fwd, from the same
+ * recurrence, but one token at a time with the fp32 state of each
+ * (sequence, value head) held on chip: the state is read once and written
+ * once, so a step costs about two state transfers (128 KiB per head).
+ *   in : q, k [B,T,Hq,K]; v [B,T,Hv,V]; g (raw log decay, g_dtype) and beta
+ *        [B,T,Hv]; initial_state fp32 [N,Hv,K,V] ([N,Hv,V,K] with
+ *        state_v_first), nullable = zeros
+ *   out: o [B,T,Hv,V] in in_dtype; final_state fp32, same layout as
+ *        initial_state, nullable.  final_state may be the same buffer as
+ *        initial_state (the state is updated in place); no other argument
+ *        may alias another.
+ * Honours cu_seqlens, state_v_first, scale and use_qk_l2norm.  Needs no
+ * workspace.  Costs grow linearly with T; past a few chunks gdr_chunk_fwd is
+ * faster.  Errors as gdr_chunk_fwd (validation on the host first). */
+gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                             const void* g, const void* beta, const float* initial_state,
+                             void* o, float* final_state, void* stream);
+
 /* Variable-length helpers (host, pure integer, bit-exact), after the
  * utilities of the "FlashQLA Documentation" page.  `cu` holds n_plus_1
  * non-decreasing offsets starting at 0.  Each returns GDR_ERR_VARLEN for a

@@ -154,6 +154,13 @@ def test_null_and_workspace_errors_before_any_device_work():
     st = lib.gdr_chunk_fwd(ctypes.byref(pv), P(16), P(16), P(16), P(16), P(16), None, P(16),
                            P(16), P(16), None, None, P(16), 1, None)
     assert _lib.STATUS[st] == "GDR_ERR_WORKSPACE"
+    # the token-by-token forward: o is required, the states are optional
+    st = lib.gdr_recurrent_fwd(ctypes.byref(p), P(16), P(16), P(16), P(16), P(16), None, None,
+                               None, None)
+    assert _lib.STATUS[st] == "GDR_ERR_NULL"
+    st = lib.gdr_recurrent_fwd(ctypes.byref(good(K=64)), P(16), P(16), P(16), P(16), P(16), None,
+                               P(16), None, None)
+    assert _lib.STATUS[st] == "GDR_ERR_HEAD_DIM"
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="exercises the no-device path")
@@ -163,6 +170,9 @@ def test_no_device_is_reported():
     P = ctypes.c_void_p
     st = lib.gdr_chunk_fwd(ctypes.byref(p), P(16), P(16), P(16), P(16), P(16), None, P(16), P(16),
                            P(16), None, None, None, 0, None)
+    assert _lib.STATUS[st] == "GDR_ERR_DEVICE"
+    st = lib.gdr_recurrent_fwd(ctypes.byref(p), P(16), P(16), P(16), P(16), P(16), None, P(16),
+                               None, None)
     assert _lib.STATUS[st] == "GDR_ERR_DEVICE"
 
 
