@@ -39,6 +39,8 @@ WORKLOADS = {
     "fwd_bwd_B1_T65536_H32_bf16": (1, 65536, 32, 32, "bf16", 2.0, None),
 }
 DEFAULT = "fwd_bwd_B2_T4096_H32_bf16"
+# token-by-token forward: (B sequences, Hv = Hq heads, tokens per step, dtype)
+DECODE_WORKLOADS = {"decode_B256_H32_bf16": (256, 32, 1, "bf16")}
 
 
 def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True, with_dht=True,
@@ -170,7 +172,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cp", type=int, default=0,
                     help="context-parallel segments per sequence (0 = the library's plan)")
@@ -190,6 +192,8 @@ def main():
     import gdr_synth
     import gated_delta_rule_66_amd as gdr
 
+    if args.workload in DECODE_WORKLOADS:
+        return bench_decode(args)
     B, T, Hq, Hv, dt, g_shift, varlen = WORKLOADS[args.workload]
     prob = gdr_synth.Problem(args.workload, B=B, T=T, Hq=Hq, Hv=Hv, dtype=dt, init_state=True,
                              backward=True, dht=True, g_shift=g_shift, qk_l2norm=args.qk_l2norm)
@@ -317,6 +321,76 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(d, (B, T, Hq, Hv), qk_norm=qkn)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args):
+    """Decode steps of the token-by-token forward: every sequence advances by
+    one token per step, its fp32 state updated in place.  The kernel moves
+    each state in and out once (2 x 64 KiB per (sequence, head)) plus the
+    token's q, k, v, g, beta and o, so it is HBM-bound."""
+    import torch
+    import gdr_synth
+    import gated_delta_rule_66_amd as gdr
+
+    B, H, T, dt = DECODE_WORKLOADS[args.workload]
+    prob = gdr_synth.Problem(args.workload, B=B, T=T, Hq=H, Hv=H, dtype=dt, init_state=True,
+                             qk_l2norm=args.qk_l2norm)
+    d = gdr_synth.make(prob)
+    dev = torch.device("cuda", 0)
+    dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    state = dd["h0"].clone()
+
+    def step():
+        return gdr.fused_recurrent_gated_delta_rule(
+            dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
+            initial_state=state, inplace_final_state=True,
+            use_qk_l2norm_in_kernel=args.qk_l2norm)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with gdr.KernelTimer() as timer:
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        kernels = timer.read()
+    ms = e0.elapsed_time(e1) / args.steps
+    tot, cnt = kernels["recurrent"]
+    avg_s = tot / cnt * 1e-3
+    isz = 2
+    units = B * H
+    nbytes = units * (2 * 128 * 128 * 4 + T * (3 * 128 * isz + 2 * isz + 128 * isz))
+    achieved = nbytes / avg_s / 1e9
+    out = {
+        "metric": "GDN decode (token-by-token forward) Mtokens/s at H=32,K=V=128 bf16",
+        "value": round(B * T / (ms * 1e-3) / 1e6, 4),
+        "unit": "Mtokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded; fp32 states updated in place)",
+        "config": {"workload": args.workload, "B": B, "T_per_step": T, "Hq": H, "Hv": H,
+                   "K": 128, "V": 128, "qk_l2norm_in_kernel": args.qk_l2norm,
+                   "parallelism": "single GPU"},
+        "kernels": {"recurrent": {"avg_us": round(avg_s * 1e6, 2), "launches": cnt}},
+        "roofline": {"bound": "hbm", "kernel": "recurrent", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(nbytes),
+                     "avg_launch_us": round(avg_s * 1e6, 2)},
+        "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
 
 
