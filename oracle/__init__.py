@@ -158,19 +158,54 @@ def l2norm_bwd(x, dy):
     return (dy - y * np.sum(y * dy, axis=-1, keepdims=True)) / n
 
 
+# ---- beta options -----------------------------------------------------------
+# The same pull request lists `use_beta_sigmoid_in_kernel` and
+# `allow_neg_eigval` among the options the FlashQLA verifier rejects, by name
+# only.  Readings: with the sigmoid option the beta input is a logit and the
+# recurrence uses sigmoid(beta); with negative eigenvalues allowed the
+# recurrence uses 2 beta, so that the transition I - beta k k^T (unit k) can
+# have the eigenvalue 1 - beta in (-1, 1) (the range extension of Grazzi et
+# al., "Unlocking State-Tracking in Linear RNNs Through Negative
+# Eigenvalues", 2024).  Both together: 2 sigmoid(beta).
+
+
+def beta_map(beta, beta_sigmoid=False, neg_eigval=False):
+    """The beta the recurrence uses, from the beta input, in fp64."""
+    b = _f64(beta)
+    if beta_sigmoid:
+        b = 1.0 / (1.0 + np.exp(-b))
+    if neg_eigval:
+        b = 2.0 * b
+    return b
+
+
+def beta_map_bwd(beta, dbeta_used, beta_sigmoid=False, neg_eigval=False):
+    """Chain rule through :func:`beta_map`: d(sigmoid)/dx = s (1 - s)."""
+    d = _f64(dbeta_used)
+    if neg_eigval:
+        d = 2.0 * d
+    if beta_sigmoid:
+        s = 1.0 / (1.0 + np.exp(-_f64(beta)))
+        d = d * s * (1.0 - s)
+    return d
+
+
 def _check(rc, name):
     if rc != 0:
         raise RuntimeError("%s failed with code %d" % (name, rc))
 
 
 def fwd(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None, state_v_first=False,
-        heads=None, nthreads=0, use_qk_l2norm=False):
+        heads=None, nthreads=0, use_qk_l2norm=False, beta_sigmoid=False, neg_eigval=False):
     """Token recurrence.  Returns ``(o [B,T,Hv,V], final_state [N,Hv,K,V])``.
 
-    With ``use_qk_l2norm`` the recurrence runs on ``l2norm(q)``, ``l2norm(k)``.
+    With ``use_qk_l2norm`` the recurrence runs on ``l2norm(q)``, ``l2norm(k)``;
+    with ``beta_sigmoid`` / ``neg_eigval`` on ``beta_map(beta, ...)``.
     """
     if use_qk_l2norm:
         q, k = l2norm(q), l2norm(k)
+    if beta_sigmoid or neg_eigval:
+        beta = beta_map(beta, beta_sigmoid, neg_eigval)
     p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
     h0 = p.state_in(initial_state, state_v_first)
     o = np.zeros((p.Ttot, p.Hv, p.V))
@@ -183,14 +218,20 @@ def fwd(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None, state_v_fi
 
 
 def bwd(q, k, v, g, beta, scale, do, initial_state=None, dht=None, cu_seqlens=None,
-        state_v_first=False, heads=None, nthreads=0, use_qk_l2norm=False):
+        state_v_first=False, heads=None, nthreads=0, use_qk_l2norm=False, beta_sigmoid=False,
+        neg_eigval=False):
     """Gradients of ``sum(do*o) + sum(dht*final_state)`` by the hand-derived
     reverse pass of the token recurrence.
 
     Returns ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is with respect to the raw
     log-decay g; ``dh0`` is ``None`` when ``initial_state`` is ``None``.  With
-    ``use_qk_l2norm`` dq and dk are with respect to the raw q and k.
+    ``use_qk_l2norm`` dq and dk are with respect to the raw q and k, with the
+    beta options dbeta with respect to the beta input.
     """
+    if beta_sigmoid or neg_eigval:
+        grads = bwd(q, k, v, g, beta_map(beta, beta_sigmoid, neg_eigval), scale, do,
+                    initial_state, dht, cu_seqlens, state_v_first, heads, nthreads, use_qk_l2norm)
+        return grads[:3] + (beta_map_bwd(beta, grads[3], beta_sigmoid, neg_eigval),) + grads[4:]
     if use_qk_l2norm:
         raw = (q, k)
         grads = bwd(l2norm(q), l2norm(k), v, g, beta, scale, do, initial_state, dht, cu_seqlens,
@@ -224,17 +265,20 @@ def chunk_offsets(cu, chunk):
 
 
 def chunked_fwd(q, k, v, g, beta, scale, chunk=64, initial_state=None, cu_seqlens=None,
-                state_v_first=False, heads=None, nthreads=0, use_qk_l2norm=False):
+                state_v_first=False, heads=None, nthreads=0, use_qk_l2norm=False,
+                beta_sigmoid=False, neg_eigval=False):
     """Naive fp64 chunked form.
 
     Returns ``(g_cum [B,T,Hv], A [B,T,Hv,chunk], o [B,T,Hv,V],
     h [NCtot,Hv,K,V], final_state [N,Hv,K,V])``; ``h`` holds chunk-start states
     (``[NCtot,Hv,V,K]`` with ``state_v_first``), row ``r`` of a chunk's ``A`` is
     stored at token ``chunk_start + r`` and columns past a partial chunk are 0.
-    ``use_qk_l2norm`` as in :func:`fwd`.
+    The options as in :func:`fwd`.
     """
     if use_qk_l2norm:
         q, k = l2norm(q), l2norm(k)
+    if beta_sigmoid or neg_eigval:
+        beta = beta_map(beta, beta_sigmoid, neg_eigval)
     p = _Problem(q, k, v, g, beta, cu_seqlens, heads)
     h0 = p.state_in(initial_state, state_v_first)
     nct = int(chunk_offsets(p.cu, chunk)[-1])
@@ -256,8 +300,13 @@ def chunked_fwd(q, k, v, g, beta, scale, chunk=64, initial_state=None, cu_seqlen
 
 def chunked_bwd(q, k, v, g, beta, scale, do, chunk=64, initial_state=None, dht=None,
                 cu_seqlens=None, state_v_first=False, heads=None, nthreads=0,
-                use_qk_l2norm=False):
+                use_qk_l2norm=False, beta_sigmoid=False, neg_eigval=False):
     """Reverse pass of the naive chunked form; same outputs as :func:`bwd`."""
+    if beta_sigmoid or neg_eigval:
+        grads = chunked_bwd(q, k, v, g, beta_map(beta, beta_sigmoid, neg_eigval), scale, do,
+                            chunk, initial_state, dht, cu_seqlens, state_v_first, heads, nthreads,
+                            use_qk_l2norm)
+        return grads[:3] + (beta_map_bwd(beta, grads[3], beta_sigmoid, neg_eigval),) + grads[4:]
     if use_qk_l2norm:
         raw = (q, k)
         grads = chunked_bwd(l2norm(q), l2norm(k), v, g, beta, scale, do, chunk, initial_state,

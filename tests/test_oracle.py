@@ -439,3 +439,90 @@ def test_l2norm_gradient_is_orthogonal_to_the_input():
         scl = np.linalg.norm(x, axis=-1) * np.linalg.norm(dx, axis=-1)
         assert np.all(dots <= 1e-6 * scl + 1e-300)
         assert np.all(np.linalg.norm(dx, axis=-1) > 0)
+
+
+# ---- beta options: sigmoid(beta) and 2 beta (negative eigenvalues allowed) ----
+
+@pytest.mark.parametrize("sig,neg", [(True, False), (False, True), (True, True)])
+def test_beta_options_backward_matches_finite_differences(sig, neg):
+    rng = np.random.default_rng(21)
+    d = rand_problem(1, 0, 1, 2, 3, 4, rng, varlen=[4, 3])
+    d["beta"] = rng.normal(size=d["beta"].shape) if sig else d["beta"]  # logits when sig
+    scale = 0.8
+    opts = dict(beta_sigmoid=sig, neg_eigval=neg)
+
+    def fwd():
+        return oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale,
+                          initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"], **opts)
+
+    o, ht = fwd()
+    do = rng.normal(size=o.shape)
+    dht = rng.normal(size=ht.shape)
+
+    def L():
+        o, ht = fwd()
+        return float(np.sum(o * do) + np.sum(ht * dht))
+
+    grads = oracle.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, do,
+                       initial_state=d["initial_state"], dht=dht, cu_seqlens=d["cu_seqlens"],
+                       **opts)
+    eps = 1e-6
+    for gi, name in enumerate(["q", "k", "v", "beta", "g", "initial_state"]):
+        x = d[name]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            orig = x[idx]
+            x[idx] = orig + eps
+            lp = L()
+            x[idx] = orig - eps
+            lm = L()
+            x[idx] = orig
+            fd[idx] = (lp - lm) / (2 * eps)
+        scl = max(1.0, np.abs(fd).max())
+        assert np.abs(fd - grads[gi]).max() <= 1e-7 * scl, (name, np.abs(fd - grads[gi]).max())
+
+
+def test_neg_eigval_unit_beta_is_a_householder_reflection():
+    """2 beta = 2, g = 0, v = 0 and unit k: the transition is I - 2 k k^T, a
+    reflection, so the state's component along k flips sign and the same
+    token applied twice restores the state exactly (up to rounding)."""
+    rng = np.random.default_rng(22)
+    K, V = 6, 4
+    k1 = rng.normal(size=K)
+    k1 /= np.linalg.norm(k1)
+    k = np.tile(k1, (1, 2, 1, 1))                  # the same key twice, [1, 2, 1, K]
+    q = rng.normal(size=(1, 2, 1, K))
+    v = np.zeros((1, 2, 1, V))
+    g = np.zeros((1, 2, 1))
+    beta = np.ones((1, 2, 1))
+    S0 = rng.normal(size=(1, 1, K, V))
+    _, S1 = oracle.fwd(q[:, :1], k[:, :1], v[:, :1], g[:, :1], beta[:, :1], 1.0,
+                       initial_state=S0, neg_eigval=True)
+    np.testing.assert_allclose(k1 @ S1[0, 0], -(k1 @ S0[0, 0]), rtol=1e-12, atol=1e-12)
+    P = np.eye(K) - np.outer(k1, k1)
+    np.testing.assert_allclose(P @ S1[0, 0], P @ S0[0, 0], rtol=1e-12, atol=1e-12)
+    _, S2 = oracle.fwd(q, k, v, g, beta, 1.0, initial_state=S0, neg_eigval=True)
+    np.testing.assert_allclose(S2, S0, rtol=1e-12, atol=1e-12)
+    # without the option the same token is a projection: applied twice = once
+    _, P1 = oracle.fwd(q[:, :1], k[:, :1], v[:, :1], g[:, :1], beta[:, :1], 1.0, initial_state=S0)
+    _, P2 = oracle.fwd(q, k, v, g, beta, 1.0, initial_state=S0)
+    np.testing.assert_allclose(P2, P1, rtol=1e-12, atol=1e-12)
+
+
+def test_beta_sigmoid_limits():
+    """Logit 0 with negative eigenvalues gives beta = 1 (exact overwrite: a
+    read with the written unit key returns v); a very negative logit gives
+    beta -> 0, leaving only the decay."""
+    rng = np.random.default_rng(23)
+    d = rand_problem(1, 8, 2, 2, 5, 3, rng)
+    zero = np.zeros_like(d["beta"])
+    o, _ = oracle.fwd(d["k"], d["k"], d["v"], d["g"], zero, 1.0, initial_state=d["initial_state"],
+                      beta_sigmoid=True, neg_eigval=True)
+    np.testing.assert_allclose(o, d["v"], rtol=1e-11, atol=1e-12)
+    o, ht = oracle.fwd(d["q"], d["k"], d["v"], d["g"], zero - 80.0, 0.5,
+                       initial_state=d["initial_state"], beta_sigmoid=True)
+    Gc = np.cumsum(d["g"], axis=1)
+    o_ref = 0.5 * np.exp(Gc)[..., None] * np.einsum("bhkv,bthk->bthv", d["initial_state"], d["q"])
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
