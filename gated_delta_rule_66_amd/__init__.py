@@ -48,7 +48,8 @@ class _Call:
     """Problem descriptor plus the host copy of cu_seqlens it points to."""
 
     def __init__(self, q, v, g_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first,
-                 cp_segments, wave_tiles=0, use_qk_l2norm=False):
+                 cp_segments, wave_tiles=0, use_qk_l2norm=False, beta_sigmoid=False,
+                 neg_eigval=False):
         B, T, Hq, K = q.shape
         Hv, V = v.shape[2], v.shape[3]
         self.cu_host = None
@@ -68,7 +69,9 @@ class _Call:
                          cu_seqlens_host=None if self.cu_host is None else self.cu_host.data_ptr(),
                          in_dtype=_code(q.dtype), g_dtype=_code(g_dtype), scale=float(scale),
                          state_v_first=1 if state_v_first else 0, cp_segments=int(cp_segments),
-                         wave_tiles=int(wave_tiles), use_qk_l2norm=1 if use_qk_l2norm else 0)
+                         wave_tiles=int(wave_tiles), use_qk_l2norm=1 if use_qk_l2norm else 0,
+                         beta_sigmoid=1 if beta_sigmoid else 0,
+                         neg_eigval=1 if neg_eigval else 0)
         self.N, self.Hv, self.K, self.V = N, Hv, K, V
         self.ref = ctypes.byref(self.p)
         reason = ctypes.create_string_buffer(256)
@@ -94,16 +97,19 @@ def _contig(*ts):
 def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                output_final_state=True, cu_seqlens=None, state_v_first=False,
                                output_h=False, cp_segments=0, cu_seqlens_cpu=None,
-                               wave_tiles=0, use_qk_l2norm_in_kernel=False):
+                               wave_tiles=0, use_qk_l2norm_in_kernel=False,
+                               use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
     """Forward.  Returns ``(g_cum, A, o, h, final_state)``: the chunk-local
     cumsum of g (fp32), the per-chunk inverse A ``[B,T,Hv,64]``, the output,
     the chunk-start states (``None`` unless ``output_h``) and the fp32 final
     state (``None`` unless ``output_final_state``).  With
     ``use_qk_l2norm_in_kernel`` the kernels scale q and k per (token, head)
-    to unit length, ``x / sqrt(sum x^2 + 1e-6)``, before use."""
+    to unit length, ``x / sqrt(sum x^2 + 1e-6)``, before use.  With
+    ``use_beta_sigmoid_in_kernel`` beta is a logit and the recurrence uses
+    ``sigmoid(beta)``; with ``allow_neg_eigval`` it uses twice that."""
     q, k, v, g, beta, initial_state = _contig(q, k, v, g, beta, initial_state)
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
-              wave_tiles, use_qk_l2norm_in_kernel)
+              wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval)
     dev = q.device
     B, T = q.shape[0], q.shape[1]
     g_cum = torch.empty(B, T, c.Hv, dtype=torch.float32, device=dev)
@@ -128,20 +134,22 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=None,
                                cu_seqlens=None, state_v_first=False, dg_dtype=None,
                                cp_segments=0, cu_seqlens_cpu=None, wave_tiles=0,
-                               use_qk_l2norm_in_kernel=False):
+                               use_qk_l2norm_in_kernel=False, use_beta_sigmoid_in_kernel=False,
+                               allow_neg_eigval=False):
     """Backward.  ``g`` is the forward's fp32 ``g_cum`` output.  Returns
     ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is the gradient with respect to
     the raw log-decay g (dtype ``dg_dtype``, default the input dtype) and
     ``dh0`` is ``None`` without an initial state.  With
     ``use_qk_l2norm_in_kernel`` (as in the forward that produced ``A``), q and
-    k are the raw rows and dq, dk are with respect to them."""
+    k are the raw rows and dq, dk are with respect to them; with the beta
+    options dbeta is with respect to the beta input."""
     q, k, v, g, beta, A, do, dht, initial_state = _contig(q, k, v, g, beta, A, do, dht,
                                                           initial_state)
     if g.dtype != torch.float32:
         raise GdrError(4, "the backward takes the forward's fp32 g_cum as g")
     dg_dtype = q.dtype if dg_dtype is None else dg_dtype
     c = _Call(q, v, dg_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
-              wave_tiles, use_qk_l2norm_in_kernel)
+              wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -165,14 +173,16 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
 class _GatedDeltaRule(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
-                state_v_first, cp_segments, cu_seqlens_cpu, use_qk_l2norm):
+                state_v_first, cp_segments, cu_seqlens_cpu, use_qk_l2norm, beta_sigmoid,
+                neg_eigval):
         g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
             q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
             state_v_first, False, cp_segments, cu_seqlens_cpu,
-            use_qk_l2norm_in_kernel=use_qk_l2norm)
+            use_qk_l2norm_in_kernel=use_qk_l2norm, use_beta_sigmoid_in_kernel=beta_sigmoid,
+            allow_neg_eigval=neg_eigval)
         ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, cu_seqlens_cpu)
         ctx.scale, ctx.svf, ctx.cp, ctx.g_dtype = scale, state_v_first, cp_segments, g.dtype
-        ctx.qk_norm = use_qk_l2norm
+        ctx.qk_norm, ctx.beta_sigmoid, ctx.neg_eigval = use_qk_l2norm, beta_sigmoid, neg_eigval
         return o, ht
 
     @staticmethod
@@ -180,22 +190,24 @@ class _GatedDeltaRule(torch.autograd.Function):
         q, k, v, g_cum, beta, A, h0, cu, cu_cpu = ctx.saved_tensors
         dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(
             q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu, ctx.svf, ctx.g_dtype, ctx.cp,
-            cu_cpu, use_qk_l2norm_in_kernel=ctx.qk_norm)
-        return dq, dk, dv, dg, db, None, dh0, None, None, None, None, None, None
+            cu_cpu, use_qk_l2norm_in_kernel=ctx.qk_norm,
+            use_beta_sigmoid_in_kernel=ctx.beta_sigmoid, allow_neg_eigval=ctx.neg_eigval)
+        return dq, dk, dv, dg, db, None, dh0, None, None, None, None, None, None, None, None
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                            output_final_state=False, use_qk_l2norm_in_kernel=False,
                            state_v_first=False, cu_seqlens=None, cp_segments=0,
-                           cu_seqlens_cpu=None, **unsupported):
+                           cu_seqlens_cpu=None, use_beta_sigmoid_in_kernel=False,
+                           allow_neg_eigval=False, **unsupported):
     """High-level op with autograd: returns ``(o, final_state)``.
 
     ``use_qk_l2norm_in_kernel`` scales q and k per (token, head) to unit
-    length inside the kernels (and carries the gradient back to the raw q, k).
-    Options the FLA backend pull request lists as rejected by the FlashQLA
-    verifier (use_gate_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
-    inter-card context parallelism, transpose_state_layout) raise
-    NotImplementedError."""
+    length inside the kernels (and carries the gradient back to the raw q, k);
+    ``use_beta_sigmoid_in_kernel`` takes beta as a logit (sigmoid in the
+    kernels) and ``allow_neg_eigval`` doubles beta.  use_gate_in_kernel (its
+    gate parameters are not part of this interface), inter-card context
+    parallelism and transpose_state_layout raise NotImplementedError."""
     for key, val in unsupported.items():
         if val:
             raise NotImplementedError("%s is not supported" % key)
@@ -203,13 +215,15 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
         scale = q.shape[-1] ** -0.5
     return _GatedDeltaRule.apply(q, k, v, g, beta, scale, initial_state, output_final_state,
                                  cu_seqlens, state_v_first, cp_segments, cu_seqlens_cpu,
-                                 bool(use_qk_l2norm_in_kernel))
+                                 bool(use_qk_l2norm_in_kernel), bool(use_beta_sigmoid_in_kernel),
+                                 bool(allow_neg_eigval))
 
 
 def fused_recurrent_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                                      output_final_state=True, cu_seqlens=None,
                                      state_v_first=False, use_qk_l2norm_in_kernel=False,
-                                     inplace_final_state=False, cu_seqlens_cpu=None):
+                                     inplace_final_state=False, cu_seqlens_cpu=None,
+                                     use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
     """Forward one token at a time (decode steps, a few speculative tokens,
     a prefill continued from a cached state).  Same inputs and outputs as
     :func:`chunk_gated_delta_rule` without autograd: returns ``(o,
@@ -218,7 +232,7 @@ def fused_recurrent_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state
     final state."""
     q, k, v, g, beta = _contig(q, k, v, g, beta)
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, 1, 0,
-              use_qk_l2norm_in_kernel)
+              use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval)
     dev = q.device
     B, T = q.shape[0], q.shape[1]
     o = torch.empty(B, T, c.Hv, c.V, dtype=q.dtype, device=dev)

@@ -30,6 +30,8 @@ class Problem(ctypes.Structure):
         ("cp_segments", ctypes.c_int32),
         ("wave_tiles", ctypes.c_int32),
         ("use_qk_l2norm", ctypes.c_int32),
+        ("beta_sigmoid", ctypes.c_int32),
+        ("neg_eigval", ctypes.c_int32),
     ]
 
 

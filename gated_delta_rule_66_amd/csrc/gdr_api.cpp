@@ -185,6 +185,10 @@ static gdr_status validate(const gdr_problem* p, char* reason, size_t len) {
     return fail(GDR_ERR_ARG, reason, len, "wave_tiles must be 0, 1 or 2");
   if (p->use_qk_l2norm != 0 && p->use_qk_l2norm != 1)
     return fail(GDR_ERR_ARG, reason, len, "use_qk_l2norm must be 0 or 1");
+  if (p->beta_sigmoid != 0 && p->beta_sigmoid != 1)
+    return fail(GDR_ERR_ARG, reason, len, "beta_sigmoid must be 0 or 1");
+  if (p->neg_eigval != 0 && p->neg_eigval != 1)
+    return fail(GDR_ERR_ARG, reason, len, "neg_eigval must be 0 or 1");
   const bool has_dev = p->cu_seqlens_dev != nullptr, has_host = p->cu_seqlens_host != nullptr;
   if (has_dev != has_host)
     return fail(GDR_ERR_VARLEN, reason, len,

@@ -52,7 +52,8 @@ struct DhArgs {
   int P, nvs;
   float scale;
   int svf;
-  int qk_norm;  // q, k rows scaled to unit length before use
+  int qk_norm;    // q, k rows scaled to unit length before use
+  int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
 };
 
 template <typename T, int VB, int MODE>
@@ -128,6 +129,7 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
   TileRegs<64, 256> ra;
   float r_g = 0.f, r_gl = 0.f;
   T r_b = from_f<T>(0.f);
+  bool r_ok = false;  // the row is inside the chunk
   auto prefetch = [&](int c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
@@ -139,6 +141,7 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
       r_g = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
       r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
       r_b = (tid < Cc) ? beta[(t0 + tid) * a.Hv + h] : from_f<T>(0.f);
+      r_ok = tid < Cc;
     }
   };
 
@@ -160,7 +163,7 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
       const float e = __expf(r_g);
       gam[tid] = r_g;
       eg[tid] = a.scale * e;
-      bex[tid] = to_f(r_b) * e;
+      bex[tid] = (r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f) * e;
       dl[tid] = __expf(r_gl - r_g);
     }
     __syncthreads();
@@ -415,6 +418,7 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   TileRegs<64, 256> ra;
   float r_g = 0.f, r_gl = 0.f;
   T r_b = from_f<T>(0.f);
+  bool r_ok = false;  // the row is inside the chunk
   auto prefetch = [&](int c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
@@ -426,6 +430,7 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
       r_g = a.gcum[(t0 + min(otid, Cc - 1)) * a.Hv + h];
       r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
       r_b = (otid < Cc) ? beta[(t0 + otid) * a.Hv + h] : from_f<T>(0.f);
+      r_ok = otid < Cc;
     }
   };
 
@@ -466,7 +471,7 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
         const float e = __expf(r_g);
         gam[otid] = r_g;
         eg[otid] = a.scale * e;
-        bex[otid] = to_f(r_b) * e;
+        bex[otid] = (r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f) * e;
         dl[otid] = __expf(r_gl - r_g);
       }
     }
@@ -677,7 +682,8 @@ struct GradArgs {
   int N, T, Hq, Hv, nc_dense, g_dtype;
   float scale;
   int partial;
-  int qk_norm;  // q, k rows scaled to unit length before use
+  int qk_norm;    // q, k rows scaled to unit length before use
+  int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
 };
 
 // Eight waves: wave w works on row / column block wr = w % 4 and takes one
@@ -711,6 +717,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   __shared__ float dgam[64];
   __shared__ float fsum[4][4];       // F partials per (row block, lane group)
   __shared__ float rowq[64];         // dgamma row terms of the dq side
+  __shared__ float dbf[64];          // d beta / d (beta input) per row
   __shared__ float xinv[2][64];      // 1 / |q|, 1 / |k| per row (q / k normalisation)
 
   const int c = blockIdx.x, h = blockIdx.y;
@@ -777,10 +784,12 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   if (tid < 64) {
     const float gr = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
     const float gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
-    const float bt = (tid < Cc) ? to_f(reinterpret_cast<const T*>(a.beta)[(t0 + tid) * a.Hv + h]) : 0.f;
+    const float bx = to_f(reinterpret_cast<const T*>(a.beta)[(t0 + min(tid, Cc - 1)) * a.Hv + h]);
+    const float bt = (tid < Cc) ? beta_used(bx, a.beta_mode) : 0.f;
     const float e = __expf(gr);
     gam[tid] = gr;
     bet[tid] = bt;
+    dbf[tid] = beta_used_grad(bx, a.beta_mode);
     eg[tid] = e;
     bex[tid] = bt * e;
     dl[tid] = __expf(gl - gr);
@@ -1171,7 +1180,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       dgam[r] += dgv;
       const float db = dbv[0][r] + dbv[1][r] + dbv[2][r] + dbv[3][r] + dbv[4][r] + dbv[5][r] +
                        dbv[6][r] + dbv[7][r] + eg[r] * rs1[e] + dbacc[e];
-      if (r < Cc) reinterpret_cast<T*>(a.dbeta)[(t0 + r) * a.Hv + h] = from_f<T>(db);
+      if (r < Cc) reinterpret_cast<T*>(a.dbeta)[(t0 + r) * a.Hv + h] = from_f<T>(db * dbf[r]);
     }
   }
   __syncthreads();
@@ -1363,6 +1372,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1; sa.scale = p->scale; sa.svf = p->state_v_first ? 1 : 0; sa.h_svf = 1;
   sa.qk_norm = p->use_qk_l2norm ? 1 : 0;
+  sa.beta_mode = (p->beta_sigmoid ? 1 : 0) | (p->neg_eigval ? 2 : 0);
   sa.seg_out = cp_out; sa.seg_start = cp_start; sa.reverse = 0;
   // B2: state gradients (value-major)
   DhArgs da;
@@ -1371,6 +1381,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   da.cu = p->cu_seqlens_dev; da.offs = offs;
   da.N = pl.N; da.T = p->T; da.Hq = p->Hq; da.Hv = p->Hv; da.nc_dense = pl.nc_dense;
   da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf; da.qk_norm = sa.qk_norm;
+  da.beta_mode = sa.beta_mode;
   if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, st);
   else launch_bwd_scans<T, 1>(pl, sa, da, st);
   // B3-B5
@@ -1385,6 +1396,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   ga.N = pl.N; ga.T = p->T; ga.Hq = p->Hq; ga.Hv = p->Hv; ga.nc_dense = pl.nc_dense;
   ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale; ga.partial = partial ? 1 : 0;
   ga.qk_norm = sa.qk_norm;
+  ga.beta_mode = sa.beta_mode;
   if (pl.total_chunks > 0 && ga.qk_norm)
     GDR_LAUNCH("grad", (grad_kernel<T, true>), dim3((unsigned)pl.total_chunks, p->Hv), dim3(512),
                st, ga);

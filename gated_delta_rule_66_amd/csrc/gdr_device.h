@@ -458,6 +458,25 @@ __device__ __forceinline__ void l2norm_rows(TileRegs<128, NT>& t, float* rinv,
   }
 }
 
+// ---- beta options ------------------------------------------------------------
+// The beta the recurrence uses, from the beta input x, for the two options the
+// FLA backend pull request's verifier names: bit 0 of `mode`
+// (use_beta_sigmoid_in_kernel) takes the sigmoid of a logit, bit 1
+// (allow_neg_eigval) doubles it, so that I - beta k k^T can have a negative
+// eigenvalue.  beta_used_grad is its derivative d beta / dx.
+__device__ __forceinline__ float beta_used(float x, int mode) {
+  const float b = (mode & 1) ? 1.f / (1.f + __expf(-x)) : x;
+  return (mode & 2) ? 2.f * b : b;
+}
+__device__ __forceinline__ float beta_used_grad(float x, int mode) {
+  float d = 1.f;
+  if (mode & 1) {
+    const float s = 1.f / (1.f + __expf(-x));
+    d = s * (1.f - s);
+  }
+  return (mode & 2) ? 2.f * d : d;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (fixed combination order).
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   const int l = lane_id();

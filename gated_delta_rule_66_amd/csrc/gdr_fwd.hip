@@ -45,7 +45,8 @@ struct FwdArgs {
   int g_dtype;
   float scale;
   int svf;
-  int qk_norm;  // q, k rows scaled to unit length before use
+  int qk_norm;    // q, k rows scaled to unit length before use
+  int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
 };
 
 template <typename T>
@@ -78,7 +79,9 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
                          (int64_t)a.Hq * kDim, Cc);
   if (w == 0) {
     const float gv = (l < Cc) ? load_scalar(a.g, (t0 + l) * a.Hv + h, a.g_dtype) : 0.f;
-    const float bv = (l < Cc) ? to_f(reinterpret_cast<const T*>(a.beta)[(t0 + l) * a.Hv + h]) : 0.f;
+    const float bv =
+        (l < Cc) ? beta_used(to_f(reinterpret_cast<const T*>(a.beta)[(t0 + l) * a.Hv + h]), a.beta_mode)
+                 : 0.f;
     const float gc = wave_inclusive_scan(gv);
     gam[l] = gc;
     bet[l] = bv;
@@ -236,6 +239,7 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   fa.N = pl.N; fa.T = p->T; fa.Hq = p->Hq; fa.Hv = p->Hv; fa.nc_dense = pl.nc_dense;
   fa.g_dtype = (int)p->g_dtype; fa.scale = p->scale; fa.svf = p->state_v_first ? 1 : 0;
   fa.qk_norm = p->use_qk_l2norm ? 1 : 0;
+  fa.beta_mode = (p->beta_sigmoid ? 1 : 0) | (p->neg_eigval ? 2 : 0);
 
   ScanArgs sa;
   sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
@@ -244,6 +248,7 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1;
   sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf; sa.qk_norm = fa.qk_norm;
+  sa.beta_mode = fa.beta_mode;
   sa.seg_out = nullptr; sa.seg_start = nullptr;
   sa.reverse = 0;
   if (pl.cp > 1) {

@@ -29,6 +29,7 @@ struct RecArgs {
   void* o;
   const int32_t* cu;  // device cu_seqlens, or null for dense batches
   int N, T, Hq, Hv, g_dtype, qk_norm;
+  int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
   float scale;
 };
 
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
     }
     if (tid < 128) rv = to_f(vg[(t * a.Hv + h) * 128 + tid]);
     rg = load_scalar(a.g, t * a.Hv + h, a.g_dtype);
-    rb = to_f(bg[t * a.Hv + h]);
+    rb = beta_used(to_f(bg[t * a.Hv + h]), a.beta_mode);
   };
   if (t_begin < t_end) load_token(t_begin);
 
@@ -204,6 +205,7 @@ gdr_status launch_recurrent(const gdr_problem* p, const void* q, const void* k, 
   a.N = p->N; a.T = p->T; a.Hq = p->Hq; a.Hv = p->Hv;
   a.g_dtype = (int)p->g_dtype;
   a.qk_norm = p->use_qk_l2norm ? 1 : 0;
+  a.beta_mode = (p->beta_sigmoid ? 1 : 0) | (p->neg_eigval ? 2 : 0);
   a.scale = p->scale;
   if ((int64_t)p->N * p->Hv == 0) return GDR_OK;
   const dim3 grid((unsigned)((int64_t)p->N * p->Hv));

@@ -71,6 +71,7 @@ struct ScanArgs {
   int h_svf;   // layout of h: the user's h follows svf; MODE_STATE always writes [V][K]
   int reverse; // cp_combine_kernel: chain segments backwards (state gradients)
   int qk_norm; // q, k rows scaled to unit length before use
+  int beta_mode; // bit 0 sigmoid of a beta logit, bit 1 twice beta
 };
 
 // Chunks [c0, c1) of segment p; the segment holding the last chunk is
@@ -200,7 +201,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
     if (!isT) tile_store<T, CW, 256>(Vs, LDV, rv);
     tile_store<T, 64, 256>(As, LDA, ra);
     if (tid < 64) {
-      const float bv = to_f(r_b);
+      const float bv = tid < Cc ? beta_used(to_f(r_b), a.beta_mode) : 0.f;
       gam[tid] = r_g;
       bet[tid] = bv;
       const float e = __expf(r_g);
@@ -516,6 +517,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   TileRegs<64, 256> rv, ra;
   float r_g = 0.f, r_gl = 0.f;
   T r_b = from_f<T>(0.f);
+  bool r_ok = false;  // the row is inside the chunk
   auto prefetch = [&](int c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
@@ -527,6 +529,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
       r_g = a.gcum[(t0 + min(otid, Cc - 1)) * a.Hv + h];
       r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
       r_b = (otid < Cc) ? beta[(t0 + otid) * a.Hv + h] : from_f<T>(0.f);
+      r_ok = otid < Cc;
     }
   };
 
@@ -554,7 +557,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
       tile_store<T, 64, 256>(Vs, LDV, rv, otid);
       tile_store<T, 64, 256>(As, LDA, ra, otid);
       if (otid < 64) {
-        const float bv = to_f(r_b);
+        const float bv = r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f;
         const float e = __expf(r_g);
         gam[otid] = r_g;
         bet[otid] = bv;

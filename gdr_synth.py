@@ -13,7 +13,8 @@ initial state -> do -> dht.
   kernel to normalise (``qk_l2norm``) keep the raw N(0, 1) rows instead.
 * v ~ N(0, 1); g = logsigmoid(N(shift, 1)) (a natural-log decay <= 0;
   ``shift = 2`` gives the slow-decay long-context workload);
-  beta = sigmoid(N(0, 1)); all rounded to the input dtype (round to nearest
+  beta = sigmoid(N(0, 1)) (the logit N(0, 1) itself for problems whose kernel
+  takes the sigmoid); all rounded to the input dtype (round to nearest
   even), the way bf16 / fp16 inputs reach a kernel.
 * initial state and dht = 0.1 * N(0, 1), kept in fp32 (std 0.1).
 * do ~ N(0, 1) in the input dtype.
@@ -47,6 +48,7 @@ class Problem:
     dht: bool = False
     g_shift: float = 0.0
     qk_l2norm: bool = False              # raw q, k rows; the kernel normalises them
+    beta_logit: bool = False             # beta drawn as the logit N(0, 1) (sigmoid in-kernel)
     seed: int = 0
     extra: dict = field(default_factory=dict)
 
@@ -99,7 +101,8 @@ def make(prob: Problem, lengths_from=None) -> dict:
     k = k.to(dt)
     v = torch.randn(B, T, Hv, V, generator=gen).to(dt)
     g = F.logsigmoid(torch.randn(B, T, Hv, generator=gen) + prob.g_shift).to(dt)
-    beta = torch.sigmoid(torch.randn(B, T, Hv, generator=gen)).to(dt)
+    beta = torch.randn(B, T, Hv, generator=gen)
+    beta = (beta if prob.beta_logit else torch.sigmoid(beta)).to(dt)
     N = prob.N
     h0 = (0.1 * torch.randn(N, Hv, K, V, generator=gen)) if prob.init_state else None
     do = torch.randn(B, T, Hv, V, generator=gen).to(dt) if prob.backward else None

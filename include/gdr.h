@@ -102,6 +102,16 @@ typedef struct {
                                      ("[GDN] Add FlashQLA backend dispatch",
                                      the dispatch's argument list) passes as
                                      use_qk_l2norm_in_kernel. */
+  int32_t beta_sigmoid;           /* 1: the beta input is a logit and the
+                                     recurrence uses sigmoid(beta); dbeta is with
+                                     respect to the logit (the PR page's
+                                     use_beta_sigmoid_in_kernel) */
+  int32_t neg_eigval;             /* 1: the recurrence uses 2 beta (after the
+                                     sigmoid when both are set), so the
+                                     transition I - beta k k^T may have a
+                                     negative eigenvalue; dbeta is with respect
+                                     to the input (the PR page's
+                                     allow_neg_eigval) */
 } gdr_problem;
 
 /* Status name ("GDR_ERR_SHAPE", ...). */

@@ -40,7 +40,8 @@ def test_status_strings():
 def good(**kw):
     base = dict(B=2, T=200, Hq=2, Hv=4, K=128, V=128, N=2, cu_seqlens_dev=None,
                 cu_seqlens_host=None, in_dtype=GDR_BF16, g_dtype=GDR_BF16, scale=0.088,
-                state_v_first=0, cp_segments=0, wave_tiles=0, use_qk_l2norm=0)
+                state_v_first=0, cp_segments=0, wave_tiles=0, use_qk_l2norm=0,
+                beta_sigmoid=0, neg_eigval=0)
     base.update(kw)
     return Problem(**base)
 
@@ -83,6 +84,8 @@ REJECT = [
     ("cp", good(cp_segments=-1), "GDR_ERR_ARG", "cp_segments"),
     ("wave_tiles", good(wave_tiles=3), "GDR_ERR_ARG", "wave_tiles"),
     ("qk_l2norm", good(use_qk_l2norm=2), "GDR_ERR_ARG", "use_qk_l2norm"),
+    ("beta_sigmoid", good(beta_sigmoid=2), "GDR_ERR_ARG", "beta_sigmoid"),
+    ("neg_eigval", good(neg_eigval=-1), "GDR_ERR_ARG", "neg_eigval"),
 ]
 
 
@@ -180,7 +183,6 @@ def test_python_rejects_verifier_options():
     import gated_delta_rule_66_amd as gdr
     x = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
     g = torch.zeros(1, 4, 1, dtype=torch.bfloat16)
-    for opt in ("use_gate_in_kernel", "use_beta_sigmoid_in_kernel", "allow_neg_eigval",
-                "transpose_state_layout"):
+    for opt in ("use_gate_in_kernel", "transpose_state_layout"):
         with pytest.raises(NotImplementedError):
             gdr.chunk_gated_delta_rule(x, x, x, g, g, **{opt: True})
