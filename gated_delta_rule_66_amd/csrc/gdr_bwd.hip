@@ -340,7 +340,7 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
 // B2 output pass (one 64-column block, 8 waves): waves 4-7 issue every
 // chunk load and tile store, waves 0-3 run the chain of dh_body unchanged, so
 // the vector-memory issue is off the chain.
-template <typename T, bool QKN>
+template <typename T, int OPT>
 __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   constexpr int VB = 1, MODE = MODE_OUT;
   typedef typename VT<T>::x8 x8;
@@ -459,7 +459,7 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
     __syncthreads();
     if (helper) {
-      if (QKN) {
+      if (OPT & 1) {
         l2norm_rows<T, 256>(rq, nullptr, otid);
         l2norm_rows<T, 256>(rk, nullptr, otid);
       }
@@ -471,7 +471,7 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
         const float e = __expf(r_g);
         gam[otid] = r_g;
         eg[otid] = a.scale * e;
-        bex[otid] = (r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f) * e;
+        bex[otid] = ((OPT & 2) ? (r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f) : to_f(r_b)) * e;
         dl[otid] = __expf(r_gl - r_g);
       }
     }
@@ -643,10 +643,10 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
 
 // The output passes of B1 and B2 with load-helper waves (VB = 1), in one
 // launch of 8-wave workgroups: blocks [0, n1) take B1.
-template <typename T, bool QKN>
+template <typename T, int OPT>
 __global__ __launch_bounds__(512) void bwd_scans_lh_kernel(ScanArgs sa, DhArgs da, int n1) {
-  if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE, QKN>(sa, xcd_block(blockIdx.x, n1));
-  else dh_lh_body<T, QKN>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
+  if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE, OPT>(sa, xcd_block(blockIdx.x, n1));
+  else dh_lh_body<T, OPT>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
 }
 
 // The state scan (B1) and the state-gradient scan (B2) are independent (B2
@@ -1324,12 +1324,19 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t
   sa.nvs = da.nvs = 2 / VB;
   const unsigned n1 = units * pl.cp * sa.nvs;
   if (VB == 1)
-    if (sa.qk_norm)
-      GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, true>), dim3(2 * n1), dim3(512), st, sa, da,
-                 (int)n1);
-    else
-      GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, false>), dim3(2 * n1), dim3(512), st, sa, da,
-                 (int)n1);
+    switch ((sa.qk_norm ? 1 : 0) | (sa.beta_mode ? 2 : 0)) {
+      case 0:
+        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 0>), dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+        break;
+      case 1:
+        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 1>), dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+        break;
+      case 2:
+        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 2>), dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+        break;
+      default:
+        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 3>), dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+    }
   else
     GDR_LAUNCH("bwd_scans", (bwd_scans_kernel<T, VB, MODE_STATE, MODE_OUT>), dim3(2 * n1),
                dim3(256), st, sa, da, (int)n1);

@@ -202,10 +202,14 @@ static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st)
   const dim3 grid(units * pl.cp * a.nvs);
   if (mode == MODE_OUT && a.h)
     GDR_LAUNCH("scan_out", (scan_kernel<T, VB, MODE_OUT_H>), grid, dim3(256), st, a);
-  else if (mode == MODE_OUT && VB == 1 && a.qk_norm)
-    GDR_LAUNCH("scan_out", (scan_out_kernel<T, true>), grid, dim3(512), st, a);
-  else if (mode == MODE_OUT && VB == 1)
-    GDR_LAUNCH("scan_out", (scan_out_kernel<T, false>), grid, dim3(512), st, a);
+  else if (mode == MODE_OUT && VB == 1) {
+    switch ((a.qk_norm ? 1 : 0) | (a.beta_mode ? 2 : 0)) {
+      case 0: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 0>), grid, dim3(512), st, a); break;
+      case 1: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 1>), grid, dim3(512), st, a); break;
+      case 2: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 2>), grid, dim3(512), st, a); break;
+      default: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 3>), grid, dim3(512), st, a);
+    }
+  }
   else if (mode == MODE_OUT)
     GDR_LAUNCH("scan_out", (scan_kernel<T, VB, MODE_OUT>), grid, dim3(256), st, a);
   else GDR_LAUNCH("scan_state", (scan_kernel<T, VB, MODE_STATE>), grid, dim3(256), st, a);

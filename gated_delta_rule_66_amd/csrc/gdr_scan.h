@@ -450,10 +450,10 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
 //
 // MODE_STATE (the backward's chunk-start states) uses the same split with
 // waves 4-7 only loading and storing the chunk tiles, and the state waves
-// writing h (value-major) straight from registers.  QKN: q / k rows are
-// normalised to unit length after their loads (a template flag, so the
-// default path carries none of that code).
-template <typename T, int MODE, bool QKN>
+// writing h (value-major) straight from registers.  OPT (template flags, so
+// the default path carries none of their code): bit 0 normalises the q / k
+// rows after their loads, bit 1 maps beta through the runtime beta options.
+template <typename T, int MODE, int OPT>
 __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   typedef typename VT<T>::x8 x8;
   constexpr bool OUT = (MODE == MODE_OUT);
@@ -548,7 +548,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
     const int b = OUT ? (it & 1) : 0;
     __syncthreads();  // iteration it-1 is done with every buffer rewritten here
     if (outw && it < sr.c1) {
-      if (QKN) {
+      if (OPT & 1) {
         if (OUT) l2norm_rows<T, 256>(rq, nullptr, otid);
         l2norm_rows<T, 256>(rk, nullptr, otid);
       }
@@ -557,7 +557,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
       tile_store<T, 64, 256>(Vs, LDV, rv, otid);
       tile_store<T, 64, 256>(As, LDA, ra, otid);
       if (otid < 64) {
-        const float bv = r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f;
+        const float bv = (OPT & 2) ? (r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f) : to_f(r_b);
         const float e = __expf(r_g);
         gam[otid] = r_g;
         bet[otid] = bv;
@@ -688,9 +688,9 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   }
 }
 
-template <typename T, bool QKN>
+template <typename T, int OPT>
 __global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
-  scan_spec_body<T, MODE_OUT, QKN>(a, xcd_block(blockIdx.x, gridDim.x));
+  scan_spec_body<T, MODE_OUT, OPT>(a, xcd_block(blockIdx.x, gridDim.x));
 }
 
 // Pass 2: chain the segment start states of one (unit, 16-column block).
