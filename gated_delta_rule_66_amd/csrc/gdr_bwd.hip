@@ -695,14 +695,14 @@ struct GradArgs {
 template <typename T, bool QKN>
 __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   typedef typename VT<T>::x8 x8;
-  constexpr int LD = 136;  // q, k, and the value-major S / dSn halves
+  constexpr int LD = 136;  // row stride of the dq / dk staging in Ss / Gs_
   constexpr int L7 = 72;   // every 64-wide tile
-  __shared__ __align__(16) T Qs[64 * LD];
-  __shared__ __align__(16) T Ks[64 * LD];
+  __shared__ __align__(16) T Qs[QK_TILE];  // q, k, S^T, dSn^T: staggered rows (qk_row)
+  __shared__ __align__(16) T Ks[QK_TILE];
   __shared__ __align__(16) T As[64 * L7];
   __shared__ __align__(16) T Ps[64 * L7];
-  __shared__ __align__(16) T Ss[128 * L7];   // S[:, half]^T ([v][k], ld LD); later dA, T1, dq
-  __shared__ __align__(16) T Gs_[128 * L7];  // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma, dk
+  __shared__ __align__(16) T Ss[QK_TILE];    // S[:, half]^T ([v][k]); later dA, T1, dq (ld LD)
+  __shared__ __align__(16) T Gs_[QK_TILE];   // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma, dk
   __shared__ __align__(16) T Vs[64 * L7];
   __shared__ __align__(16) T Os[64 * L7];    // dO[:, half]
   __shared__ __align__(16) T Rs[64 * L7];    // R, transposed: [v][r]
@@ -756,8 +756,8 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   auto store_half = [&]() {
 #pragma unroll
     for (int i = 0; i < TileRegs<128, 512>::N; ++i) sds += dot8<T>(rs.r[i], rg.r[i]);
-    tile_store<T, 128, 512>(Ss, LD, rs);
-    tile_store<T, 128, 512>(Gs_, LD, rg);
+    tile_store_q<T, 512>(Ss, rs);
+    tile_store_q<T, 512>(Gs_, rg);
     tile_store<T, 64, 512>(Vs, L7, rv);
     tile_store<T, 64, 512>(Os, L7, ro);
   };
@@ -776,8 +776,8 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       l2norm_rows<T, 512>(rq, xinv[0]);
       l2norm_rows<T, 512>(rk, xinv[1]);
     }
-    tile_store<T, 128, 512>(Qs, LD, rq);
-    tile_store<T, 128, 512>(Ks, LD, rk);
+    tile_store_q<T, 512>(Qs, rq);
+    tile_store_q<T, 512>(Ks, rk);
     tile_store<T, 64, 512>(As, L7, ra);
     store_half();
   }
@@ -805,10 +805,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   for (int cb = 0; cb < 4; ++cb) {
     f32x4 acc = zero4();
     if (cb <= wr) {
-      const T* rows = (hi ? Ks : Qs) + 16 * wr * LD;
+      const T* rows = hi ? Ks : Qs;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = mfma16(frag_row(rows + 32 * kk, LD), frag_row(Ks + 16 * cb * LD + 32 * kk, LD), acc);
+        acc = mfma16(frag_row_q(rows, 16 * wr, 32 * kk), frag_row_q(Ks, 16 * cb, 32 * kk), acc);
     }
     const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * wr + 4 * grp);
     const float gi = gam[16 * cb + col];
@@ -853,10 +853,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       for (int tb = 0; tb < 4; ++tb) ks[tb] = zero4();
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const x8 fs = frag_row_split(Ss + cc * LD + 32 * kb2, LD);
+        const x8 fs = frag_row_split_q(Ss, cc, 32 * kb2);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
-          ks[tb] = mfma16(frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD), fs, ks[tb]);
+          ks[tb] = mfma16(frag_row_split_q(Ks, 16 * tb, 32 * kb2), fs, ks[tb]);
       }
       f32x4 R[4];
 #pragma unroll
@@ -882,10 +882,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       for (int tb = 0; tb < 4; ++tb) kg[tb] = zero4();
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const x8 fg = frag_row_split(Gs_ + cc * LD + 32 * kb2, LD);
+        const x8 fg = frag_row_split_q(Gs_, cc, 32 * kb2);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
-          kg[tb] = mfma16(frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD), fg, kg[tb]);
+          kg[tb] = mfma16(frag_row_split_q(Ks, 16 * tb, 32 * kb2), fg, kg[tb]);
       }
       f32x4 dD[4];
 #pragma unroll
@@ -937,14 +937,14 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
         }
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
-          acc1[kb] = mfma16(fdo, frag_tr_split(Ss + 32 * vk * LD + 16 * kb, LD), acc1[kb]);
+          acc1[kb] = mfma16(fdo, frag_tr_split_q(Ss, 32 * vk, 16 * kb), acc1[kb]);
       } else {
         const x8 fdr = frag_tr_split(DRs + 32 * vk * L7 + 16 * wr, L7);
         const x8 fdl = frag_tr_split(Dls + 32 * vk * L7 + 16 * wr, L7);
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-          acc1[kb] = mfma16(fdr, frag_tr_split(Ss + 32 * vk * LD + 16 * kb, LD), acc1[kb]);
-          acc2[kb] = mfma16(fdl, frag_tr_split(Gs_ + 32 * vk * LD + 16 * kb, LD), acc2[kb]);
+          acc1[kb] = mfma16(fdr, frag_tr_split_q(Ss, 32 * vk, 16 * kb), acc1[kb]);
+          acc2[kb] = mfma16(fdl, frag_tr_split_q(Gs_, 32 * vk, 16 * kb), acc2[kb]);
         }
       }
     }
@@ -1008,7 +1008,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       const x8 fa = frag_row_split(dPG + 16 * wr * L7 + 32 * ik, L7);
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb)
-        acc3[kb] = mfma16(fa, frag_tr_split(Ks + 32 * ik * LD + 16 * kb, LD), acc3[kb]);
+        acc3[kb] = mfma16(fa, frag_tr_split_q(Ks, 32 * ik, 16 * kb), acc3[kb]);
     }
   } else {
 #pragma unroll
@@ -1016,7 +1016,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       const x8 fb = frag_tr_split(dPG + 32 * ik * L7 + 16 * wr, L7);
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb)
-        acc3[kb] = mfma16(fb, frag_tr_split(Qs + 32 * ik * LD + 16 * kb, LD), acc3[kb]);
+        acc3[kb] = mfma16(fb, frag_tr_split_q(Qs, 32 * ik, 16 * kb), acc3[kb]);
     }
   }
   __syncthreads();
@@ -1063,7 +1063,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       const x8 fb = frag_tr_split(DMs + 32 * ik * L7 + 16 * wr, L7);
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const x8 fk = frag_tr_split(Ks + 32 * ik * LD + 16 * kb, LD);
+        const x8 fk = frag_tr_split_q(Ks, 32 * ik, 16 * kb);
         acc3[kb] = mfma16(fa, fk, acc3[kb]);
         acc3[kb] = mfma16(fb, fk, acc3[kb]);
       }
@@ -1074,7 +1074,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     const f32x4 bxr = *reinterpret_cast<const f32x4*>(bex + 16 * wr + 4 * grp);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const f32x4 kd = frag_d4(Ks, LD, 16 * wr, 16 * kb);
+      const f32x4 kd = frag_d4_q(Ks, 16 * wr, 16 * kb);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float dx = -acc1[kb][e];
@@ -1088,7 +1088,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     const f32x4 er = *reinterpret_cast<const f32x4*>(eg + 16 * wr + 4 * grp);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const f32x4 qd = frag_d4(Qs, LD, 16 * wr, 16 * kb);
+      const f32x4 qd = frag_d4_q(Qs, 16 * wr, 16 * kb);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         rs1[e] += qd[e] * acc1[kb][e];
@@ -1105,7 +1105,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     float dot[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const f32x4 xd = frag_d4(X, LD, 16 * wr, 16 * kb);
+      const f32x4 xd = frag_d4_q(X, 16 * wr, 16 * kb);
 #pragma unroll
       for (int e = 0; e < 4; ++e) dot[e] += xd[e] * dxv[kb][e];
     }
@@ -1114,7 +1114,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     const f32x4 ri = *reinterpret_cast<const f32x4*>(xinv[hi ? 1 : 0] + 16 * wr + 4 * grp);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const f32x4 xd = frag_d4(X, LD, 16 * wr, 16 * kb);
+      const f32x4 xd = frag_d4_q(X, 16 * wr, 16 * kb);
 #pragma unroll
       for (int e = 0; e < 4; ++e) dxv[kb][e] = ri[e] * (dxv[kb][e] - xd[e] * dot[e]);
     }

@@ -228,6 +228,18 @@ __device__ __forceinline__ typename VT<T>::x8 frag_tr_split_q(const T* X, int k0
   return __builtin_bit_cast(typename VT<T>::x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
+// frag_d4 on a staggered tile (row0 a multiple of 16).
+template <typename T>
+__device__ __forceinline__ f32x4 frag_d4_q(const T* X, int row0, int col0) {
+  const int l = lane_id();
+  const int grp = l >> 4, j = l & 15;
+  const T* p = X + qk_row(4 * grp + (j >> 2)) + (row0 >> 4) * qk_row(16) + col0 + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const typename VT<T>::x4 v = __builtin_bit_cast(typename VT<T>::x4, r);
+  return f32x4{to_f(v[0]), to_f(v[1]), to_f(v[2]), to_f(v[3])};
+}
+
 // Register-staged tile copies, split in two so that the global loads of the
 // next chunk can be in flight while the current chunk computes.  A 64-row
 // tile of COLS elements is NT-thread cooperative; thread t holds 16-byte
