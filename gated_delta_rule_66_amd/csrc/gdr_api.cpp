@@ -69,7 +69,9 @@ static gdr_status fail(gdr_status s, char* reason, size_t len, const char* fmt, 
 // workgroup per CU in every pass but the forward transition pass at VB = 1,
 // which fits two; a pass with more workgroups than slots runs in rounds).
 // Per chunk step of one workgroup:
-//   forward output pass 3.1 (VB = 1, wave-specialized) / 5.0 (VB = 2),
+//   forward output pass 3.1 (VB = 1, wave-specialized; 2.55 in the
+//   32-column form used when 64-column workgroups would fill at most 128
+//   CUs) / 5.0 (VB = 2),
 //   forward transition pass 2.7 / 3.0,
 //   backward output pass (state and state-gradient scans in one launch):
 //     state scan 2.4 / 5.5 and state-gradient scan 3.3 / 5.5; the launch
@@ -92,7 +94,8 @@ static double bwd_out_cost(int64_t wgs_per_scan, int64_t chunks, int VB) {
 static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd) {
   const int64_t nvs0 = 2 / VB, nvs1 = 4 / VB;
   if (!bwd) {
-    const double out = VB == 1 ? 3.1 : 5.0;
+    const bool narrow = VB == 1 && units * P * 2 <= 128;
+    const double out = VB == 1 ? (narrow ? 2.55 : 3.1) : 5.0;
     if (P == 1) return (double)maxch * out * rounds(units * nvs0, 256);
     const int64_t sc = (maxch + P - 1) / P;
     // one end segment needs only its value columns, the inner ones everything

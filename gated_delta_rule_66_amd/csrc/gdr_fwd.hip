@@ -200,14 +200,27 @@ static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st)
   a.P = pl.cp;
   a.nvs = 2 / VB;
   const dim3 grid(units * pl.cp * a.nvs);
+  // With 64-column workgroups filling at most half of the 256 CUs, the
+  // output pass splits the value columns in four (two state waves each), so
+  // the idle CUs take half of every workgroup's output work.
+  const bool narrow = units * pl.cp * 2 <= 128;
   if (mode == MODE_OUT && a.h)
     GDR_LAUNCH("scan_out", (scan_kernel<T, VB, MODE_OUT_H>), grid, dim3(256), st, a);
-  else if (mode == MODE_OUT && VB == 1) {
+  else if (mode == MODE_OUT && VB == 1 && narrow) {
+    a.nvs = 4;
+    const dim3 g4(units * pl.cp * 4);
     switch ((a.qk_norm ? 1 : 0) | (a.beta_mode ? 2 : 0)) {
-      case 0: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 0>), grid, dim3(512), st, a); break;
-      case 1: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 1>), grid, dim3(512), st, a); break;
-      case 2: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 2>), grid, dim3(512), st, a); break;
-      default: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 3>), grid, dim3(512), st, a);
+      case 0: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 0, 2>), g4, dim3(384), st, a); break;
+      case 1: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 1, 2>), g4, dim3(384), st, a); break;
+      case 2: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 2, 2>), g4, dim3(384), st, a); break;
+      default: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 3, 2>), g4, dim3(384), st, a);
+    }
+  } else if (mode == MODE_OUT && VB == 1) {
+    switch ((a.qk_norm ? 1 : 0) | (a.beta_mode ? 2 : 0)) {
+      case 0: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 0, 4>), grid, dim3(512), st, a); break;
+      case 1: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 1, 4>), grid, dim3(512), st, a); break;
+      case 2: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 2, 4>), grid, dim3(512), st, a); break;
+      default: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 3, 4>), grid, dim3(512), st, a);
     }
   }
   else if (mode == MODE_OUT)

@@ -453,27 +453,31 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
 // writing h (value-major) straight from registers.  OPT (template flags, so
 // the default path carries none of their code): bit 0 normalises the q / k
 // rows after their loads, bit 1 maps beta through the runtime beta options.
-template <typename T, int MODE, int OPT>
+template <typename T, int MODE, int OPT, int NCW = 4>
 __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   typedef typename VT<T>::x8 x8;
   constexpr bool OUT = (MODE == MODE_OUT);
+  static_assert(NCW == 4 || (NCW == 2 && OUT), "two state waves only for the output pass");
+  constexpr int CW = 16 * NCW;     // value columns per workgroup
+  constexpr int NVS = 128 / CW;    // column blocks per (unit, segment)
   constexpr int NB = OUT ? 2 : 1;  // buffers of the tiles both roles read
-  constexpr int LDV = 72;   // v tile (64 columns)
+  constexpr int LDV = CW + 8;      // v tile
   constexpr int LDA = 72;   // A and P tiles
   __shared__ __align__(16) T Qs[NB][OUT ? QK_TILE : 8];  // staggered rows (qk_row)
   __shared__ __align__(16) T Ks[NB][QK_TILE];
   __shared__ __align__(16) T Vs[64 * LDV];
   __shared__ __align__(16) T As[64 * LDA];
   __shared__ __align__(16) T Ps[NB][OUT ? 64 * LDA : 8];
-  __shared__ __align__(16) x8 Xs[NB][4][4][OUT ? 64 : 1];  // S_c operands: [buf][column block][k block][lane]
-  __shared__ __align__(16) x8 Xd[NB][4][2][OUT ? 64 : 1];  // Delta_c operands
+  __shared__ __align__(16) x8 Xs[NB][NCW][4][OUT ? 64 : 1];  // S_c operands: [buf][column block][k block][lane]
+  __shared__ __align__(16) x8 Xd[NB][NCW][2][OUT ? 64 : 1];  // Delta_c operands
   __shared__ __align__(16) float gam[64], bet[64], bex[64], dl[64], eg[2][64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
-  const bool outw = w >= 4;
-  const int wq = w & 3;  // the wave's 16-column block (both roles)
-  const int vs = bid & 1;
-  const int up = bid >> 1;
+  const bool outw = w >= NCW;
+  // state waves: their 16-column block; output waves: their index 0..3
+  const int wq = NCW == 4 ? (w & 3) : (outw ? w - NCW : w);
+  const int vs = bid % NVS;
+  const int up = bid / NVS;
   const int p = up % a.P, unit = up / a.P;
   const int n = unit / a.Hv, h = unit % a.Hv;
   const int G = a.Hv / a.Hq, hq = h / G;
@@ -481,8 +485,8 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
   const SegRange sr = seg_range(nch, a.P, p);
   if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;  // empty segment
-  const int cb0 = 64 * vs;
-  const int cw0 = 16 * wq;
+  const int cb0 = CW * vs;
+  const int cw0 = (NCW == 4 || !outw) ? 16 * wq : 0;
   const int64_t KV = (int64_t)kDim * kDim;
   const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
   const T* q = reinterpret_cast<const T*>(a.q);
@@ -512,9 +516,10 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   // register prefetch of one chunk by the output waves (256 threads): the
   // vector-memory issue of a chunk's tiles takes hundreds of cycles, which
   // the state chain does not wait for
-  const int otid = tid - 256;
+  const int otid = tid - 64 * NCW;
   TileRegs<128, 256> rq, rk;
-  TileRegs<64, 256> rv, ra;
+  TileRegs<CW, 256> rv;
+  TileRegs<64, 256> ra;
   float r_g = 0.f, r_gl = 0.f;
   T r_b = from_f<T>(0.f);
   bool r_ok = false;  // the row is inside the chunk
@@ -523,7 +528,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
     const int Cc = (int)min((int64_t)kChunk, s.end - t0);
     if (OUT) tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
     tile_load<T, 128, 256>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
-    tile_load<T, 64, 256>(rv, v + (t0 * a.Hv + h) * kDim + cb0, (int64_t)a.Hv * kDim, Cc, otid);
+    tile_load<T, CW, 256>(rv, v + (t0 * a.Hv + h) * kDim + cb0, (int64_t)a.Hv * kDim, Cc, otid);
     tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc, otid);
     if (otid < 64) {
       r_g = a.gcum[(t0 + min(otid, Cc - 1)) * a.Hv + h];
@@ -554,7 +559,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
       }
       if (OUT) tile_store_q<T, 256>(Qs[b], rq, otid);
       tile_store_q<T, 256>(Ks[b], rk, otid);
-      tile_store<T, 64, 256>(Vs, LDV, rv, otid);
+      tile_store<T, CW, 256>(Vs, LDV, rv, otid);
       tile_store<T, 64, 256>(As, LDA, ra, otid);
       if (otid < 64) {
         const float bv = (OPT & 2) ? (r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f) : to_f(r_b);
@@ -642,33 +647,36 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
       if (it > sr.c0) {
       // output of chunk c = it - 1:
       //   O^T = (Q S)^T diag(e^gamma) + Delta^T P^T, times scale
+      // for column block cbk, row blocks rb0 .. rb0 + NCW - 1
       const int c = it - 1, bo = c & 1;
+      const int cbk = wq % NCW, rb0 = (wq / NCW) * NCW;
       const int64_t t0 = s.start + (int64_t)kChunk * c;
       const int Cc = (int)min((int64_t)kChunk, s.end - t0);
-      f32x4 qsT[4];
+      f32x4 qsT[NCW];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) qsT[rb] = zero4();
+      for (int i = 0; i < NCW; ++i) qsT[i] = zero4();
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const x8 sb = Xs[bo][wq][kb2][l];
+        const x8 sb = Xs[bo][cbk][kb2][l];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          qsT[rb] = mfma16(sb, frag_row_split_q(Qs[bo], 16 * rb, 32 * kb2), qsT[rb]);
+        for (int i = 0; i < NCW; ++i)
+          qsT[i] = mfma16(sb, frag_row_split_q(Qs[bo], 16 * (rb0 + i), 32 * kb2), qsT[i]);
       }
-      const x8 Db0 = Xd[bo][wq][0][l], Db1 = Xd[bo][wq][1][l];
+      const x8 Db0 = Xd[bo][cbk][0][l], Db1 = Xd[bo][cbk][1][l];
       const int ld_o = a.Hv * kDim * (int)sizeof(T);
       const __amdgpu_buffer_rsrc_t ors =
           buf_rsrc(reinterpret_cast<T*>(a.o) + (t0 * a.Hv + h) * kDim + cb0, (int64_t)Cc * ld_o);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        f32x4 acc = qsT[rb] * eg[bo][16 * rb + col];
+      for (int i = 0; i < NCW; ++i) {
+        const int rb = rb0 + i;
+        f32x4 acc = qsT[i] * eg[bo][16 * rb + col];
         acc = mfma16(Db0, frag_row_split(Ps[bo] + 16 * rb * LDA, LDA), acc);
         if (rb >= 2) acc = mfma16(Db1, frag_row_split(Ps[bo] + 16 * rb * LDA + 32, LDA), acc);
         acc *= a.scale;
         const typename VT<T>::x4 ov{from_f<T>(acc[0]), from_f<T>(acc[1]), from_f<T>(acc[2]),
                                     from_f<T>(acc[3])};
         // rows past the chunk's end fall outside the buffer range: dropped
-        buf_store8(ors, (16 * rb + col) * ld_o + (cw0 + 4 * grp) * (int)sizeof(T),
+        buf_store8(ors, (16 * rb + col) * ld_o + (16 * cbk + 4 * grp) * (int)sizeof(T),
                    __builtin_bit_cast(u32x2, ov));
       }
       }
@@ -688,9 +696,9 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   }
 }
 
-template <typename T, int OPT>
-__global__ __launch_bounds__(512) void scan_out_kernel(ScanArgs a) {
-  scan_spec_body<T, MODE_OUT, OPT>(a, xcd_block(blockIdx.x, gridDim.x));
+template <typename T, int OPT, int NCW>
+__global__ __launch_bounds__(64 * (NCW + 4)) void scan_out_kernel(ScanArgs a) {
+  scan_spec_body<T, MODE_OUT, OPT, NCW>(a, xcd_block(blockIdx.x, gridDim.x));
 }
 
 // Pass 2: chain the segment start states of one (unit, 16-column block).
