@@ -190,18 +190,71 @@ def beta_map_bwd(beta, dbeta_used, beta_sigmoid=False, neg_eigval=False):
     return d
 
 
+# ---- gate activation ---------------------------------------------------------
+# The same pull request lists `use_gate_in_kernel` among the verifier's
+# rejections, by name only.  Reading: the g input is then the gate's raw,
+# per-token input x, and the log decay is the Mamba-2 discretisation that
+# Gated DeltaNet layers use for their decay (Dao and Gu, "Transformers are
+# SSMs", 2024; Yang et al., "Gated Delta Networks", 2024), with per-head
+# parameters A_log and dt_bias:
+#     g = -exp(A_log[h]) * softplus(x + dt_bias[h]),  softplus(z) = log(1 + e^z)
+# so g < 0 and the decay exp(g) lies in (0, 1).
+
+
+def softplus(z):
+    """log(1 + e^z) in fp64, written so that neither tail overflows."""
+    z = _f64(z)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def _gate_params(x, A_log, dt_bias):
+    x = _f64(x)
+    Hv = x.shape[-1]
+    a = _f64(A_log).reshape(Hv)
+    b = np.zeros(Hv) if dt_bias is None else _f64(dt_bias).reshape(Hv)
+    return x, a, b
+
+
+def gate_map(x, A_log, dt_bias=None):
+    """The log decay g [.., Hv] from the gate input x [.., Hv] (fp64)."""
+    x, a, b = _gate_params(x, A_log, dt_bias)
+    return -np.exp(a) * softplus(x + b)
+
+
+def gate_map_bwd(x, A_log, dt_bias, dg):
+    """Chain rule through :func:`gate_map` for the gradient dg of the log decay.
+
+    dg/dx = dg/d dt_bias = -exp(A_log) sigmoid(x + dt_bias) and
+    dg/dA_log = g, so the per-head parameter gradients are sums over every
+    token.  Returns ``(dx, dA_log [Hv], ddt_bias [Hv])``.
+    """
+    x, a, b = _gate_params(x, A_log, dt_bias)
+    dg = _f64(dg)
+    z = x + b
+    sig = 1.0 / (1.0 + np.exp(-z))
+    dx = dg * (-np.exp(a) * sig)
+    g = -np.exp(a) * softplus(z)
+    red = tuple(range(dg.ndim - 1))
+    return dx, np.sum(dg * g, axis=red), np.sum(dx, axis=red)
+
+
 def _check(rc, name):
     if rc != 0:
         raise RuntimeError("%s failed with code %d" % (name, rc))
 
 
 def fwd(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None, state_v_first=False,
-        heads=None, nthreads=0, use_qk_l2norm=False, beta_sigmoid=False, neg_eigval=False):
+        heads=None, nthreads=0, use_qk_l2norm=False, beta_sigmoid=False, neg_eigval=False,
+        gate=None):
     """Token recurrence.  Returns ``(o [B,T,Hv,V], final_state [N,Hv,K,V])``.
 
     With ``use_qk_l2norm`` the recurrence runs on ``l2norm(q)``, ``l2norm(k)``;
-    with ``beta_sigmoid`` / ``neg_eigval`` on ``beta_map(beta, ...)``.
+    with ``beta_sigmoid`` / ``neg_eigval`` on ``beta_map(beta, ...)``; with
+    ``gate = (A_log, dt_bias)`` g is the gate input and the recurrence runs on
+    ``gate_map(g, A_log, dt_bias)``.
     """
+    if gate is not None:
+        g = gate_map(g, *gate)
     if use_qk_l2norm:
         q, k = l2norm(q), l2norm(k)
     if beta_sigmoid or neg_eigval:
@@ -219,15 +272,22 @@ def fwd(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None, state_v_fi
 
 def bwd(q, k, v, g, beta, scale, do, initial_state=None, dht=None, cu_seqlens=None,
         state_v_first=False, heads=None, nthreads=0, use_qk_l2norm=False, beta_sigmoid=False,
-        neg_eigval=False):
+        neg_eigval=False, gate=None):
     """Gradients of ``sum(do*o) + sum(dht*final_state)`` by the hand-derived
     reverse pass of the token recurrence.
 
     Returns ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is with respect to the raw
     log-decay g; ``dh0`` is ``None`` when ``initial_state`` is ``None``.  With
     ``use_qk_l2norm`` dq and dk are with respect to the raw q and k, with the
-    beta options dbeta with respect to the beta input.
+    beta options dbeta with respect to the beta input.  With ``gate =
+    (A_log, dt_bias)`` dg is with respect to the gate input and two more
+    entries follow: ``dA_log [Hv]`` and ``ddt_bias [Hv]``.
     """
+    if gate is not None:
+        grads = bwd(q, k, v, gate_map(g, *gate), beta, scale, do, initial_state, dht, cu_seqlens,
+                    state_v_first, heads, nthreads, use_qk_l2norm, beta_sigmoid, neg_eigval)
+        dx, da, db = gate_map_bwd(g, gate[0], gate[1], grads[4])
+        return grads[:4] + (dx, grads[5], da, db)
     if beta_sigmoid or neg_eigval:
         grads = bwd(q, k, v, g, beta_map(beta, beta_sigmoid, neg_eigval), scale, do,
                     initial_state, dht, cu_seqlens, state_v_first, heads, nthreads, use_qk_l2norm)
@@ -266,7 +326,7 @@ def chunk_offsets(cu, chunk):
 
 def chunked_fwd(q, k, v, g, beta, scale, chunk=64, initial_state=None, cu_seqlens=None,
                 state_v_first=False, heads=None, nthreads=0, use_qk_l2norm=False,
-                beta_sigmoid=False, neg_eigval=False):
+                beta_sigmoid=False, neg_eigval=False, gate=None):
     """Naive fp64 chunked form.
 
     Returns ``(g_cum [B,T,Hv], A [B,T,Hv,chunk], o [B,T,Hv,V],
@@ -275,6 +335,8 @@ def chunked_fwd(q, k, v, g, beta, scale, chunk=64, initial_state=None, cu_seqlen
     stored at token ``chunk_start + r`` and columns past a partial chunk are 0.
     The options as in :func:`fwd`.
     """
+    if gate is not None:
+        g = gate_map(g, *gate)
     if use_qk_l2norm:
         q, k = l2norm(q), l2norm(k)
     if beta_sigmoid or neg_eigval:
@@ -300,8 +362,14 @@ def chunked_fwd(q, k, v, g, beta, scale, chunk=64, initial_state=None, cu_seqlen
 
 def chunked_bwd(q, k, v, g, beta, scale, do, chunk=64, initial_state=None, dht=None,
                 cu_seqlens=None, state_v_first=False, heads=None, nthreads=0,
-                use_qk_l2norm=False, beta_sigmoid=False, neg_eigval=False):
+                use_qk_l2norm=False, beta_sigmoid=False, neg_eigval=False, gate=None):
     """Reverse pass of the naive chunked form; same outputs as :func:`bwd`."""
+    if gate is not None:
+        grads = chunked_bwd(q, k, v, gate_map(g, *gate), beta, scale, do, chunk, initial_state,
+                            dht, cu_seqlens, state_v_first, heads, nthreads, use_qk_l2norm,
+                            beta_sigmoid, neg_eigval)
+        dx, da, db = gate_map_bwd(g, gate[0], gate[1], grads[4])
+        return grads[:4] + (dx, grads[5], da, db)
     if beta_sigmoid or neg_eigval:
         grads = chunked_bwd(q, k, v, g, beta_map(beta, beta_sigmoid, neg_eigval), scale, do,
                             chunk, initial_state, dht, cu_seqlens, state_v_first, heads, nthreads,

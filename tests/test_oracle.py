@@ -526,3 +526,94 @@ def test_beta_sigmoid_limits():
     Gc = np.cumsum(d["g"], axis=1)
     o_ref = 0.5 * np.exp(Gc)[..., None] * np.einsum("bhkv,bthk->bthv", d["initial_state"], d["q"])
     np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+
+
+# ---- gate activation: g = -exp(A_log) softplus(x + dt_bias) ----
+
+def test_softplus_matches_library_routines():
+    """The oracle's softplus against numpy's log-add-exp and torch's softplus
+    (without its linear cut-off) over both tails and the middle."""
+    import torch
+    z = np.concatenate([np.linspace(-60.0, 60.0, 241), [-745.0, -1e-8, 0.0, 1e-8, 700.0]])
+    sp = oracle.softplus(z)
+    np.testing.assert_allclose(sp, np.logaddexp(0.0, z), rtol=1e-14, atol=0.0)
+    ref = torch.nn.functional.softplus(torch.tensor(z, dtype=torch.float64), beta=1.0,
+                                       threshold=1e4).numpy()
+    np.testing.assert_allclose(sp, ref, rtol=1e-14, atol=0.0)
+    assert np.all(sp >= 0.0)
+
+
+def test_gate_closed_forms():
+    """At x + dt_bias = 0 the log decay is -exp(A_log) ln 2; for large inputs
+    softplus(z) -> z, for very negative ones -> e^z; every decay lies in (0, 1]
+    and falls as x grows."""
+    A_log = np.array([0.0, np.log(2.0), np.log(16.0)])
+    dt_bias = np.array([0.0, -0.5, 3.0])
+    x = -dt_bias[None, :] * np.ones((1, 3))
+    np.testing.assert_allclose(oracle.gate_map(x, A_log, dt_bias),
+                               -np.exp(A_log)[None, :] * np.log(2.0), rtol=1e-15)
+    big = np.full((1, 3), 50.0) - dt_bias
+    np.testing.assert_allclose(oracle.gate_map(big, A_log, dt_bias), -np.exp(A_log)[None, :] * 50.0,
+                               rtol=1e-15)
+    small = np.full((1, 3), -50.0) - dt_bias
+    np.testing.assert_allclose(oracle.gate_map(small, A_log, dt_bias),
+                               -np.exp(A_log)[None, :] * np.exp(-50.0), rtol=1e-14)
+    xs = np.linspace(-20, 20, 81)[:, None] * np.ones((1, 3))
+    g = oracle.gate_map(xs, A_log, dt_bias)
+    assert np.all(g < 0.0) and np.all(np.diff(g, axis=0) < 0.0)
+    # no dt_bias means a zero bias
+    np.testing.assert_array_equal(oracle.gate_map(xs, A_log), oracle.gate_map(xs, A_log, np.zeros(3)))
+
+
+@pytest.mark.parametrize("chunked", [False, True])
+def test_gate_backward_matches_finite_differences(chunked):
+    """Central differences of the loss with respect to every gate input x and
+    both per-head parameters (and every other input), through the token
+    recurrence and through the naive chunked form (chunk 2, ragged)."""
+    rng = np.random.default_rng(31)
+    d = rand_problem(1, 0, 1, 2, 3, 4, rng, varlen=[4, 3])
+    d["g"] = rng.normal(size=d["g"].shape)              # raw gate inputs
+    d["A_log"] = np.log(rng.uniform(1.0, 4.0, size=2))
+    d["dt_bias"] = rng.normal(size=2)
+    scale = 0.7
+
+    def fwd():
+        gate = (d["A_log"], d["dt_bias"])
+        if chunked:
+            r = oracle.chunked_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, chunk=2,
+                                   initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+                                   gate=gate)
+            return r[2], r[4]
+        return oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale,
+                          initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"], gate=gate)
+
+    o, ht = fwd()
+    do = rng.normal(size=o.shape)
+    dht = rng.normal(size=ht.shape)
+
+    def L():
+        o, ht = fwd()
+        return float(np.sum(o * do) + np.sum(ht * dht))
+
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], scale, do)
+    kw = dict(initial_state=d["initial_state"], dht=dht, cu_seqlens=d["cu_seqlens"],
+              gate=(d["A_log"], d["dt_bias"]))
+    grads = oracle.chunked_bwd(*args, chunk=2, **kw) if chunked else oracle.bwd(*args, **kw)
+    assert len(grads) == 8
+    eps = 1e-6
+    names = ["q", "k", "v", "beta", "g", "initial_state", "A_log", "dt_bias"]
+    for gi, name in enumerate(names):
+        x = d[name]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            orig = x[idx]
+            x[idx] = orig + eps
+            lp = L()
+            x[idx] = orig - eps
+            lm = L()
+            x[idx] = orig
+            fd[idx] = (lp - lm) / (2 * eps)
+        scl = max(1.0, np.abs(fd).max())
+        assert np.abs(fd - grads[gi]).max() <= 1e-7 * scl, (name, np.abs(fd - grads[gi]).max())
