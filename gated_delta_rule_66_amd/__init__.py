@@ -49,9 +49,21 @@ class _Call:
 
     def __init__(self, q, v, g_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first,
                  cp_segments, wave_tiles=0, use_qk_l2norm=False, beta_sigmoid=False,
-                 neg_eigval=False):
+                 neg_eigval=False, gate=None):
         B, T, Hq, K = q.shape
         Hv, V = v.shape[2], v.shape[3]
+        # gate = (A_log, dt_bias or None): fp32 [Hv] device copies the problem points to
+        self.gate = None
+        if gate is not None:
+            A_log, dt_bias = gate
+            if A_log is None:
+                raise GdrError(1, "use_gate_in_kernel needs A_log")
+            self.gate = tuple(None if t is None else
+                              t.detach().to(device=q.device, dtype=torch.float32).reshape(-1)
+                              .contiguous() for t in (A_log, dt_bias))
+            for t in self.gate:
+                if t is not None and t.numel() != Hv:
+                    raise GdrError(2, "A_log and dt_bias need Hv=%d entries" % Hv)
         self.cu_host = None
         self.cu_dev = None
         if cu_seqlens is not None:
@@ -71,7 +83,11 @@ class _Call:
                          state_v_first=1 if state_v_first else 0, cp_segments=int(cp_segments),
                          wave_tiles=int(wave_tiles), use_qk_l2norm=1 if use_qk_l2norm else 0,
                          beta_sigmoid=1 if beta_sigmoid else 0,
-                         neg_eigval=1 if neg_eigval else 0)
+                         neg_eigval=1 if neg_eigval else 0,
+                         use_gate=0 if self.gate is None else 1,
+                         gate_A_log=None if self.gate is None else self.gate[0].data_ptr(),
+                         gate_dt_bias=None if self.gate is None or self.gate[1] is None
+                         else self.gate[1].data_ptr())
         self.N, self.Hv, self.K, self.V = N, Hv, K, V
         self.ref = ctypes.byref(self.p)
         reason = ctypes.create_string_buffer(256)
@@ -94,11 +110,25 @@ def _contig(*ts):
     return [None if t is None else t.contiguous() for t in ts]
 
 
+def _workspace(nbytes, dev, workspace):
+    """The caller's workspace (a device uint8 tensor of at least nbytes), or a
+    new one."""
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if (workspace.device != dev or workspace.dtype != torch.uint8
+            or not workspace.is_contiguous() or workspace.numel() < nbytes):
+        raise GdrError(7, "workspace must be a contiguous uint8 tensor of at least %d bytes on %s"
+                       % (nbytes, dev))
+    return workspace
+
+
 def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                output_final_state=True, cu_seqlens=None, state_v_first=False,
                                output_h=False, cp_segments=0, cu_seqlens_cpu=None,
                                wave_tiles=0, use_qk_l2norm_in_kernel=False,
-                               use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
+                               use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False,
+                               use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                               workspace=None):
     """Forward.  Returns ``(g_cum, A, o, h, final_state)``: the chunk-local
     cumsum of g (fp32), the per-chunk inverse A ``[B,T,Hv,64]``, the output,
     the chunk-start states (``None`` unless ``output_h``) and the fp32 final
@@ -106,10 +136,17 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     ``use_qk_l2norm_in_kernel`` the kernels scale q and k per (token, head)
     to unit length, ``x / sqrt(sum x^2 + 1e-6)``, before use.  With
     ``use_beta_sigmoid_in_kernel`` beta is a logit and the recurrence uses
-    ``sigmoid(beta)``; with ``allow_neg_eigval`` it uses twice that."""
+    ``sigmoid(beta)``; with ``allow_neg_eigval`` it uses twice that.  With
+    ``use_gate_in_kernel`` g is the gate's raw input x and the log decay is
+    ``-exp(A_log[h]) * softplus(x + dt_bias[h])`` (A_log, dt_bias: ``[Hv]``;
+    dt_bias may be None); g_cum is the cumsum of that log decay.  ``workspace``
+    (optional): a device uint8 tensor of at least
+    ``gdr_chunk_fwd_workspace_size`` bytes to use instead of a new one; its
+    contents need no initialisation."""
     q, k, v, g, beta, initial_state = _contig(q, k, v, g, beta, initial_state)
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
-              wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval)
+              wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
+              (A_log, dt_bias) if use_gate_in_kernel else None)
     dev = q.device
     B, T = q.shape[0], q.shape[1]
     g_cum = torch.empty(B, T, c.Hv, dtype=torch.float32, device=dev)
@@ -124,7 +161,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     if initial_state is not None:
         initial_state = initial_state.to(torch.float32).contiguous()
     ws_bytes = lib.gdr_chunk_fwd_workspace_size(c.ref)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = _workspace(ws_bytes, dev, workspace)
     check(lib.gdr_chunk_fwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             _ptr(initial_state), _ptr(g_cum), _ptr(A), _ptr(o), _ptr(h), _ptr(ht),
                             _ptr(ws), ws_bytes, _stream(dev)))
@@ -135,21 +172,33 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
                                cu_seqlens=None, state_v_first=False, dg_dtype=None,
                                cp_segments=0, cu_seqlens_cpu=None, wave_tiles=0,
                                use_qk_l2norm_in_kernel=False, use_beta_sigmoid_in_kernel=False,
-                               allow_neg_eigval=False):
+                               allow_neg_eigval=False, use_gate_in_kernel=False, A_log=None,
+                               dt_bias=None, g_input=None, workspace=None):
     """Backward.  ``g`` is the forward's fp32 ``g_cum`` output.  Returns
     ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is the gradient with respect to
     the raw log-decay g (dtype ``dg_dtype``, default the input dtype) and
     ``dh0`` is ``None`` without an initial state.  With
     ``use_qk_l2norm_in_kernel`` (as in the forward that produced ``A``), q and
     k are the raw rows and dq, dk are with respect to them; with the beta
-    options dbeta is with respect to the beta input."""
-    q, k, v, g, beta, A, do, dht, initial_state = _contig(q, k, v, g, beta, A, do, dht,
-                                                          initial_state)
+    options dbeta is with respect to the beta input.  With
+    ``use_gate_in_kernel`` ``g_input`` is the gate input the forward took,
+    ``dg`` is with respect to it (dtype ``dg_dtype``, default g_input's) and
+    two more entries follow: the fp32 gradients of ``A_log`` and ``dt_bias``
+    (``[Hv]``).  ``workspace`` as in the forward, of at least
+    ``gdr_chunk_bwd_workspace_size`` bytes."""
+    q, k, v, g, beta, A, do, dht, initial_state, g_input = _contig(
+        q, k, v, g, beta, A, do, dht, initial_state, g_input)
     if g.dtype != torch.float32:
         raise GdrError(4, "the backward takes the forward's fp32 g_cum as g")
-    dg_dtype = q.dtype if dg_dtype is None else dg_dtype
+    if use_gate_in_kernel and g_input is None:
+        raise GdrError(1, "use_gate_in_kernel needs the gate input (g_input)")
+    if dg_dtype is None:
+        dg_dtype = g_input.dtype if use_gate_in_kernel else q.dtype
+    if use_gate_in_kernel and g_input.dtype != dg_dtype:
+        g_input = g_input.to(dg_dtype).contiguous()
     c = _Call(q, v, dg_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
-              wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval)
+              wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
+              (A_log, dt_bias) if use_gate_in_kernel else None)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -163,7 +212,16 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     if dht is not None:
         dht = dht.to(torch.float32).contiguous()
     ws_bytes = lib.gdr_chunk_bwd_workspace_size(c.ref)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = _workspace(ws_bytes, dev, workspace)
+    if use_gate_in_kernel:
+        dA_log = torch.empty(c.Hv, dtype=torch.float32, device=dev)
+        ddt_bias = torch.empty(c.Hv, dtype=torch.float32, device=dev)
+        check(lib.gdr_chunk_bwd_gate(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_input),
+                                     _ptr(beta), _ptr(A), _ptr(do), _ptr(dht),
+                                     _ptr(initial_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db),
+                                     _ptr(dg), _ptr(dh0), _ptr(dA_log), _ptr(ddt_bias), _ptr(ws),
+                                     ws_bytes, _stream(dev)))
+        return dq, dk, dv, db, dg, dh0, dA_log, ddt_bias
     check(lib.gdr_chunk_bwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
                             _ptr(do), _ptr(dht), _ptr(initial_state), _ptr(dq), _ptr(dk), _ptr(dv),
                             _ptr(db), _ptr(dg), _ptr(dh0), _ptr(ws), ws_bytes, _stream(dev)))
@@ -174,40 +232,53 @@ class _GatedDeltaRule(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
                 state_v_first, cp_segments, cu_seqlens_cpu, use_qk_l2norm, beta_sigmoid,
-                neg_eigval):
+                neg_eigval, use_gate, A_log, dt_bias):
         g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
             q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
             state_v_first, False, cp_segments, cu_seqlens_cpu,
             use_qk_l2norm_in_kernel=use_qk_l2norm, use_beta_sigmoid_in_kernel=beta_sigmoid,
-            allow_neg_eigval=neg_eigval)
-        ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, cu_seqlens_cpu)
+            allow_neg_eigval=neg_eigval, use_gate_in_kernel=use_gate, A_log=A_log,
+            dt_bias=dt_bias)
+        ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, cu_seqlens_cpu,
+                              g if use_gate else None, A_log, dt_bias)
         ctx.scale, ctx.svf, ctx.cp, ctx.g_dtype = scale, state_v_first, cp_segments, g.dtype
         ctx.qk_norm, ctx.beta_sigmoid, ctx.neg_eigval = use_qk_l2norm, beta_sigmoid, neg_eigval
+        ctx.use_gate = use_gate
         return o, ht
 
     @staticmethod
     def backward(ctx, do, dht):
-        q, k, v, g_cum, beta, A, h0, cu, cu_cpu = ctx.saved_tensors
-        dq, dk, dv, db, dg, dh0 = chunk_gated_delta_rule_bwd(
+        q, k, v, g_cum, beta, A, h0, cu, cu_cpu, g_in, A_log, dt_bias = ctx.saved_tensors
+        grads = chunk_gated_delta_rule_bwd(
             q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu, ctx.svf, ctx.g_dtype, ctx.cp,
             cu_cpu, use_qk_l2norm_in_kernel=ctx.qk_norm,
-            use_beta_sigmoid_in_kernel=ctx.beta_sigmoid, allow_neg_eigval=ctx.neg_eigval)
-        return dq, dk, dv, dg, db, None, dh0, None, None, None, None, None, None, None, None
+            use_beta_sigmoid_in_kernel=ctx.beta_sigmoid, allow_neg_eigval=ctx.neg_eigval,
+            use_gate_in_kernel=ctx.use_gate, A_log=A_log, dt_bias=dt_bias, g_input=g_in)
+        dq, dk, dv, db, dg, dh0 = grads[:6]
+        dA = ddt = None
+        if ctx.use_gate:
+            dA = grads[6].to(A_log.dtype)
+            ddt = None if dt_bias is None else grads[7].to(dt_bias.dtype)
+        return (dq, dk, dv, dg, db, None, dh0, None, None, None, None, None, None, None, None,
+                None, dA, ddt)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                            output_final_state=False, use_qk_l2norm_in_kernel=False,
                            state_v_first=False, cu_seqlens=None, cp_segments=0,
                            cu_seqlens_cpu=None, use_beta_sigmoid_in_kernel=False,
-                           allow_neg_eigval=False, **unsupported):
+                           allow_neg_eigval=False, use_gate_in_kernel=False, A_log=None,
+                           dt_bias=None, **unsupported):
     """High-level op with autograd: returns ``(o, final_state)``.
 
     ``use_qk_l2norm_in_kernel`` scales q and k per (token, head) to unit
     length inside the kernels (and carries the gradient back to the raw q, k);
     ``use_beta_sigmoid_in_kernel`` takes beta as a logit (sigmoid in the
-    kernels) and ``allow_neg_eigval`` doubles beta.  use_gate_in_kernel (its
-    gate parameters are not part of this interface), inter-card context
-    parallelism and transpose_state_layout raise NotImplementedError."""
+    kernels) and ``allow_neg_eigval`` doubles beta.  ``use_gate_in_kernel``
+    takes g as the gate's raw input, with the log decay
+    ``-exp(A_log) * softplus(g + dt_bias)`` per value head (gradients flow to
+    g, A_log and dt_bias).  Inter-card context parallelism and
+    transpose_state_layout raise NotImplementedError."""
     for key, val in unsupported.items():
         if val:
             raise NotImplementedError("%s is not supported" % key)
@@ -216,23 +287,28 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     return _GatedDeltaRule.apply(q, k, v, g, beta, scale, initial_state, output_final_state,
                                  cu_seqlens, state_v_first, cp_segments, cu_seqlens_cpu,
                                  bool(use_qk_l2norm_in_kernel), bool(use_beta_sigmoid_in_kernel),
-                                 bool(allow_neg_eigval))
+                                 bool(allow_neg_eigval), bool(use_gate_in_kernel),
+                                 A_log if use_gate_in_kernel else None,
+                                 dt_bias if use_gate_in_kernel else None)
 
 
 def fused_recurrent_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                                      output_final_state=True, cu_seqlens=None,
                                      state_v_first=False, use_qk_l2norm_in_kernel=False,
                                      inplace_final_state=False, cu_seqlens_cpu=None,
-                                     use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False):
+                                     use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False,
+                                     use_gate_in_kernel=False, A_log=None, dt_bias=None):
     """Forward one token at a time (decode steps, a few speculative tokens,
     a prefill continued from a cached state).  Same inputs and outputs as
     :func:`chunk_gated_delta_rule` without autograd: returns ``(o,
-    final_state)``; ``g`` is the raw log decay.  With ``inplace_final_state``
-    the fp32 ``initial_state`` tensor is updated in place and returned as the
-    final state."""
+    final_state)``; ``g`` is the raw log decay (the gate input with
+    ``use_gate_in_kernel``).  With ``inplace_final_state`` the fp32
+    ``initial_state`` tensor is updated in place and returned as the final
+    state."""
     q, k, v, g, beta = _contig(q, k, v, g, beta)
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, 1, 0,
-              use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval)
+              use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
+              (A_log, dt_bias) if use_gate_in_kernel else None)
     dev = q.device
     B, T = q.shape[0], q.shape[1]
     o = torch.empty(B, T, c.Hv, c.V, dtype=q.dtype, device=dev)

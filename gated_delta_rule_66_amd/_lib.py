@@ -32,6 +32,9 @@ class Problem(ctypes.Structure):
         ("use_qk_l2norm", ctypes.c_int32),
         ("beta_sigmoid", ctypes.c_int32),
         ("neg_eigval", ctypes.c_int32),
+        ("use_gate", ctypes.c_int32),
+        ("gate_A_log", ctypes.c_void_p),
+        ("gate_dt_bias", ctypes.c_void_p),
     ]
 
 
@@ -43,7 +46,7 @@ EXPORTS = [
     "gdr_prepare_chunk_indices_i32", "gdr_prepare_chunk_indices_i64",
     "gdr_prepare_chunk_offsets_i32", "gdr_prepare_chunk_offsets_i64",
     "gdr_prepare_chunk_token_starts_i64", "gdr_profile_enable", "gdr_profile_read",
-    "gdr_plan_info", "gdr_recurrent_fwd",
+    "gdr_plan_info", "gdr_recurrent_fwd", "gdr_chunk_bwd_gate",
 ]
 
 
@@ -76,6 +79,9 @@ def _declare(lib):
     lib.gdr_chunk_fwd.restype = st
     lib.gdr_chunk_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_chunk_bwd.restype = st
+    lib.gdr_chunk_bwd_gate.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                       P, S, P]
+    lib.gdr_chunk_bwd_gate.restype = st
     lib.gdr_recurrent_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P]
     lib.gdr_recurrent_fwd.restype = st
     for name in ("gdr_prepare_lens_i32", "gdr_prepare_lens_i64"):

@@ -192,6 +192,12 @@ static gdr_status validate(const gdr_problem* p, char* reason, size_t len) {
     return fail(GDR_ERR_ARG, reason, len, "beta_sigmoid must be 0 or 1");
   if (p->neg_eigval != 0 && p->neg_eigval != 1)
     return fail(GDR_ERR_ARG, reason, len, "neg_eigval must be 0 or 1");
+  if (p->use_gate != 0 && p->use_gate != 1)
+    return fail(GDR_ERR_ARG, reason, len, "use_gate must be 0 or 1");
+  if (p->use_gate && !p->gate_A_log)
+    return fail(GDR_ERR_NULL, reason, len, "use_gate needs gate_A_log");
+  if (!p->use_gate && (p->gate_A_log || p->gate_dt_bias))
+    return fail(GDR_ERR_ARG, reason, len, "gate parameters are given but use_gate is 0");
   const bool has_dev = p->cu_seqlens_dev != nullptr, has_host = p->cu_seqlens_host != nullptr;
   if (has_dev != has_host)
     return fail(GDR_ERR_VARLEN, reason, len,
@@ -384,13 +390,12 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
                     workspace, (hipStream_t)stream);
 }
 
-gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
-                         const float* g_cum, const void* beta, const void* A, const void* do_,
-                         const float* dht, const float* initial_state, void* dq, void* dk,
-                         void* dv, void* dbeta, void* dg, float* dh0, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  gdr_status s = validate(p, nullptr, 0);
-  if (s != GDR_OK) return s;
+static gdr_status chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                            const float* g_cum, const void* graw, const void* beta, const void* A,
+                            const void* do_, const float* dht, const float* initial_state,
+                            void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
+                            float* dA_log, float* ddt_bias, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !g_cum || !beta || !A || !do_ || !dq || !dk || !dv || !dbeta || !dg)
     return fail(GDR_ERR_NULL, nullptr, 0, "a required backward pointer is NULL");
   if (initial_state && !dh0)
@@ -400,10 +405,40 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDR_ERR_WORKSPACE, nullptr, 0, "backward workspace needs %zu bytes, got %zu",
                 need, workspace ? workspace_bytes : (size_t)0);
-  s = check_device_cached();
+  const gdr_status s = check_device_cached();
   if (s != GDR_OK) return s;
-  return launch_bwd(p, pl, q, k, v, g_cum, beta, A, do_, dht, initial_state, dq, dk, dv, dbeta,
-                    dg, initial_state ? dh0 : nullptr, workspace, (hipStream_t)stream);
+  return launch_bwd(p, pl, q, k, v, g_cum, graw, beta, A, do_, dht, initial_state, dq, dk, dv,
+                    dbeta, dg, initial_state ? dh0 : nullptr, dA_log, ddt_bias, workspace,
+                    (hipStream_t)stream);
+}
+
+gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const float* g_cum, const void* beta, const void* A, const void* do_,
+                         const float* dht, const float* initial_state, void* dq, void* dk,
+                         void* dv, void* dbeta, void* dg, float* dh0, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  if (p->use_gate)
+    return fail(GDR_ERR_ARG, nullptr, 0,
+                "use_gate needs the gate input: call gdr_chunk_bwd_gate");
+  return chunk_bwd(p, q, k, v, g_cum, nullptr, beta, A, do_, dht, initial_state, dq, dk, dv,
+                   dbeta, dg, dh0, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k, const void* v,
+                              const float* g_cum, const void* g, const void* beta, const void* A,
+                              const void* do_, const float* dht, const float* initial_state,
+                              void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
+                              float* dA_log, float* ddt_bias, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  if (!p->use_gate)
+    return fail(GDR_ERR_ARG, nullptr, 0, "gdr_chunk_bwd_gate needs use_gate == 1");
+  if (!g) return fail(GDR_ERR_NULL, nullptr, 0, "the gate input g is NULL");
+  return chunk_bwd(p, q, k, v, g_cum, g, beta, A, do_, dht, initial_state, dq, dk, dv, dbeta,
+                   dg, dh0, dA_log, ddt_bias, workspace, workspace_bytes, stream);
 }
 
 gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,

@@ -20,7 +20,9 @@
 //       dk = (dP o Gamma)^T Q + diag(e^{gL-gamma}) Delta dSn^T
 //            - diag(beta e^gamma) dR S^T + (dM o beta Gamma) K + (..)^T K
 //       dv = diag(beta) dR, dbeta and dgamma by fixed-order row reductions,
-//       dg = reverse chunk-local cumsum of dgamma.
+//       dg = reverse chunk-local cumsum of dgamma (times the gate's slope when
+//       g is a gate input, with per-chunk shares of the gate parameters'
+//       gradients, summed per head by gate_param_grad_kernel).
 //   B6  gva_reduce: dq, dk summed over the Hv/Hq value heads of a group.
 #include "gdr_device.h"
 #include "gdr_internal.h"
@@ -109,8 +111,11 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
         for (int e = 0; e < 4; ++e)
           Gs[kb][vb][e] = (16 * kb + 4 * grp + e == cb0 + cw0 + 16 * vb + col) ? 1.f : 0.f;
   } else {
+    // the value columns of an inner segment's transition start from zero
+    // (their end state is b_seg); the gradient entering it comes from pass 2
     const float* src = (p == sr.p_last) ? (a.dht ? a.dht + unit * KV : nullptr)
-                                        : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+                       : (MODE == MODE_AUG) ? nullptr
+                                            : a.seg_start + ((int64_t)unit * a.P + p) * KV;
     const bool vf = (p == sr.p_last) && a.svf;
     const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
 #pragma unroll
@@ -398,8 +403,11 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
         for (int e = 0; e < 4; ++e)
           Gs[kb][vb][e] = (16 * kb + 4 * grp + e == cb0 + cw0 + 16 * vb + col) ? 1.f : 0.f;
   } else {
+    // the value columns of an inner segment's transition start from zero
+    // (their end state is b_seg); the gradient entering it comes from pass 2
     const float* src = (p == sr.p_last) ? (a.dht ? a.dht + unit * KV : nullptr)
-                                        : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+                       : (MODE == MODE_AUG) ? nullptr
+                                            : a.seg_start + ((int64_t)unit * a.P + p) * KV;
     const bool vf = (p == sr.p_last) && a.svf;
     const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
 #pragma unroll
@@ -684,6 +692,13 @@ struct GradArgs {
   int partial;
   int qk_norm;    // q, k rows scaled to unit length before use
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
+  // the gate (use_gate): g is the gate input graw, dg is with respect to it,
+  // and each workgroup leaves its chunk's shares of the parameter gradients
+  // (sum of dlogdecay * logdecay, sum of dg) in gpart[(c * Hv + h) * 2 + {0, 1}]
+  const void* graw;
+  const float* gate_A_log;  // non-null iff the gate is on
+  const float* gate_dt_bias;
+  float* gpart;
 };
 
 // Eight waves: wave w works on row / column block wr = w % 4 and takes one
@@ -1193,8 +1208,51 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   // dg = reverse cumsum of dgamma over the valid rows: lane l scans row 63 - l
   if (w == 0) {
     const int r = 63 - l;
-    const float x = wave_inclusive_scan(r < Cc ? dgam[r] : 0.f);
+    float x = wave_inclusive_scan(r < Cc ? dgam[r] : 0.f);
+    if (a.gate_A_log) {
+      // x is the gradient of the row's log decay; the gate input's gradient is
+      // x times the gate's slope, and the chunk's shares of d A_log and
+      // d dt_bias are the sums of x * logdecay and of that gradient
+      const float ga = a.gate_A_log[h], gb = a.gate_dt_bias ? a.gate_dt_bias[h] : 0.f;
+      const float xin = r < Cc ? load_scalar(a.graw, (t0 + r) * a.Hv + h, a.g_dtype) : 0.f;
+      const float pa = r < Cc ? x * gate_log_decay(xin, ga, gb) : 0.f;
+      x = r < Cc ? x * gate_log_decay_grad(xin, ga, gb) : 0.f;
+      const float sa = sum4g(sum16(pa)), sb = sum4g(sum16(x));
+      if (l == 0) {
+        a.gpart[((int64_t)c * a.Hv + h) * 2] = sa;
+        a.gpart[((int64_t)c * a.Hv + h) * 2 + 1] = sb;
+      }
+    }
     if (r < Cc) store_scalar(a.dg, (t0 + r) * a.Hv + h, a.g_dtype, x);
+  }
+}
+
+// d A_log[h] and d dt_bias[h]: the per-chunk shares summed over every chunk of
+// every sequence.  One workgroup per head; thread t adds chunks t, t + 256,
+// ... in order, then a fixed pairwise tree combines the 256 partial sums.
+__global__ __launch_bounds__(256) void gate_param_grad_kernel(const float* gpart, int64_t nchunks,
+                                                              int Hv, float* dA_log,
+                                                              float* ddt_bias) {
+  __shared__ float ra[256], rb[256];
+  const int h = blockIdx.x, t = threadIdx.x;
+  float sa = 0.f, sb = 0.f;
+  for (int64_t c = t; c < nchunks; c += 256) {
+    sa += gpart[(c * Hv + h) * 2];
+    sb += gpart[(c * Hv + h) * 2 + 1];
+  }
+  ra[t] = sa;
+  rb[t] = sb;
+  __syncthreads();
+  for (int half = 128; half > 0; half >>= 1) {
+    if (t < half) {
+      ra[t] += ra[t + half];
+      rb[t] += rb[t + half];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    if (dA_log) dA_log[h] = ra[0];
+    if (ddt_bias) ddt_bias[h] = rb[0];
   }
 }
 
@@ -1262,7 +1320,7 @@ __global__ __launch_bounds__(256) void gva_reduce_kernel(const float* pq, const 
 // host side
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-  size_t offs, cp, cp2, h, dh, pq, pk, total;
+  size_t offs, cp, cp2, h, dh, pq, pk, gpart, total;
 };
 
 static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
@@ -1288,6 +1346,8 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
     L.pk = o;
     o += align256(part);
   }
+  L.gpart = o;
+  if (p->use_gate) o += align256((size_t)pl.total_chunks * p->Hv * 2 * sizeof(float));
   L.total = o;
   return L;
 }
@@ -1344,9 +1404,10 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t
 
 template <typename T>
 static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
-                               const void* v, const float* gcum, const void* beta, const void* A,
-                               const void* dO, const float* dht, const float* h0, void* dq,
-                               void* dk, void* dv, void* dbeta, void* dg, float* dh0, char* ws,
+                               const void* v, const float* gcum, const void* graw,
+                               const void* beta, const void* A, const void* dO, const float* dht,
+                               const float* h0, void* dq, void* dk, void* dv, void* dbeta,
+                               void* dg, float* dh0, float* dA_log, float* ddt_bias, char* ws,
                                hipStream_t st) {
   const BwdLayout L = bwd_layout(p, pl);
   const int32_t* offs = nullptr;
@@ -1404,12 +1465,20 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale; ga.partial = partial ? 1 : 0;
   ga.qk_norm = sa.qk_norm;
   ga.beta_mode = sa.beta_mode;
+  const bool gate = p->use_gate != 0;
+  ga.graw = gate ? graw : nullptr;
+  ga.gate_A_log = gate ? p->gate_A_log : nullptr;
+  ga.gate_dt_bias = gate ? p->gate_dt_bias : nullptr;
+  ga.gpart = gate ? reinterpret_cast<float*>(ws + L.gpart) : nullptr;
   if (pl.total_chunks > 0 && ga.qk_norm)
     GDR_LAUNCH("grad", (grad_kernel<T, true>), dim3((unsigned)pl.total_chunks, p->Hv), dim3(512),
                st, ga);
   else if (pl.total_chunks > 0)
     GDR_LAUNCH("grad", (grad_kernel<T, false>), dim3((unsigned)pl.total_chunks, p->Hv), dim3(512),
                st, ga);
+  if (gate && (dA_log || ddt_bias))
+    GDR_LAUNCH("gate_param_grad", gate_param_grad_kernel, dim3((unsigned)p->Hv), dim3(256), st,
+               ga.gpart, (int64_t)pl.total_chunks, p->Hv, dA_log, ddt_bias);
   // B6
   if (partial) {
     const int64_t Ttot = (int64_t)p->B * p->T;
@@ -1430,15 +1499,16 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
 }
 
 gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
-                      const void* v, const float* gcum, const void* beta, const void* A,
-                      const void* dO, const float* dht, const float* h0, void* dq, void* dk,
-                      void* dv, void* dbeta, void* dg, float* dh0, void* ws, hipStream_t st) {
+                      const void* v, const float* gcum, const void* graw, const void* beta,
+                      const void* A, const void* dO, const float* dht, const float* h0, void* dq,
+                      void* dk, void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
+                      float* ddt_bias, void* ws, hipStream_t st) {
   char* w = reinterpret_cast<char*>(ws);
   if (p->in_dtype == GDR_BF16)
-    return launch_bwd_t<__bf16>(p, pl, q, k, v, gcum, beta, A, dO, dht, h0, dq, dk, dv, dbeta, dg,
-                                dh0, w, st);
-  return launch_bwd_t<_Float16>(p, pl, q, k, v, gcum, beta, A, dO, dht, h0, dq, dk, dv, dbeta, dg,
-                                dh0, w, st);
+    return launch_bwd_t<__bf16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, dq, dk, dv,
+                                dbeta, dg, dh0, dA_log, ddt_bias, w, st);
+  return launch_bwd_t<_Float16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, dq, dk, dv,
+                                dbeta, dg, dh0, dA_log, ddt_bias, w, st);
 }
 
 }  // namespace gdr

@@ -489,6 +489,21 @@ __device__ __forceinline__ float beta_used_grad(float x, int mode) {
   return (mode & 2) ? 2.f * d : d;
 }
 
+// The gate activation (use_gate): the log decay from the gate input x and the
+// head's parameters, g = -e^{A_log} softplus(x + dt_bias), the decay of the
+// Mamba-2 discretisation that Gated DeltaNet layers use.  softplus(z) =
+// max(z, 0) + log1p(e^{-|z|}) keeps both tails finite; d g / d x =
+// -e^{A_log} sigmoid(x + dt_bias).
+__device__ __forceinline__ float gate_softplus(float z) {
+  return fmaxf(z, 0.f) + log1pf(__expf(-fabsf(z)));
+}
+__device__ __forceinline__ float gate_log_decay(float x, float a_log, float bias) {
+  return -__expf(a_log) * gate_softplus(x + bias);
+}
+__device__ __forceinline__ float gate_log_decay_grad(float x, float a_log, float bias) {
+  return -__expf(a_log) / (1.f + __expf(-(x + bias)));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (fixed combination order).
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   const int l = lane_id();

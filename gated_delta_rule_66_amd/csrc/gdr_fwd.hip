@@ -47,6 +47,8 @@ struct FwdArgs {
   int svf;
   int qk_norm;    // q, k rows scaled to unit length before use
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
+  const float* gate_A_log;    // non-null: g is the gate input (gate_log_decay)
+  const float* gate_dt_bias;  // nullable
 };
 
 template <typename T>
@@ -78,7 +80,9 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   tile_load<T, 128, 256>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
                          (int64_t)a.Hq * kDim, Cc);
   if (w == 0) {
-    const float gv = (l < Cc) ? load_scalar(a.g, (t0 + l) * a.Hv + h, a.g_dtype) : 0.f;
+    float gv = (l < Cc) ? load_scalar(a.g, (t0 + l) * a.Hv + h, a.g_dtype) : 0.f;
+    if (a.gate_A_log && l < Cc)
+      gv = gate_log_decay(gv, a.gate_A_log[h], a.gate_dt_bias ? a.gate_dt_bias[h] : 0.f);
     const float bv =
         (l < Cc) ? beta_used(to_f(reinterpret_cast<const T*>(a.beta)[(t0 + l) * a.Hv + h]), a.beta_mode)
                  : 0.f;
@@ -257,6 +261,8 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   fa.g_dtype = (int)p->g_dtype; fa.scale = p->scale; fa.svf = p->state_v_first ? 1 : 0;
   fa.qk_norm = p->use_qk_l2norm ? 1 : 0;
   fa.beta_mode = (p->beta_sigmoid ? 1 : 0) | (p->neg_eigval ? 2 : 0);
+  fa.gate_A_log = p->use_gate ? p->gate_A_log : nullptr;
+  fa.gate_dt_bias = p->use_gate ? p->gate_dt_bias : nullptr;
 
   ScanArgs sa;
   sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;

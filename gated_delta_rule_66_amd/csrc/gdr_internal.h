@@ -36,10 +36,12 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
                       float* gcum, void* A, void* o, void* h, float* ht, void* ws,
                       hipStream_t st);
 
+// graw: the gate input (use_gate only, else NULL); dA_log, ddt_bias nullable.
 gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
-                      const void* v, const float* gcum, const void* beta, const void* A,
-                      const void* dO, const float* dht, const float* h0, void* dq, void* dk,
-                      void* dv, void* dbeta, void* dg, float* dh0, void* ws, hipStream_t st);
+                      const void* v, const float* gcum, const void* graw, const void* beta,
+                      const void* A, const void* dO, const float* dht, const float* h0, void* dq,
+                      void* dk, void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
+                      float* ddt_bias, void* ws, hipStream_t st);
 
 // Token-by-token recurrence (decode and other short inputs), no workspace.
 gdr_status launch_recurrent(const gdr_problem* p, const void* q, const void* k, const void* v,

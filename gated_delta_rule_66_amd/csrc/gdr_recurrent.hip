@@ -8,7 +8,7 @@
 // fp32 state in registers, 64 values per thread, reads it once and writes it
 // once (in place when final_state == initial_state).  Per token, with the
 // state S before the token:
-//   a = e^g;  s_k = S^T k;  s_q = S^T q
+//   a = e^g (g from the gate input when the gate is on);  s_k = S^T k;  s_q = S^T q
 //   u = beta (v - a s_k)
 //   o = scale (a s_q + (k . q) u)       (= scale S_new^T q, expanded)
 //   S <- a S + k u^T
@@ -31,6 +31,8 @@ struct RecArgs {
   int N, T, Hq, Hv, g_dtype, qk_norm;
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
   float scale;
+  const float* gate_A_log;    // non-null: g is the gate input (gate_log_decay)
+  const float* gate_dt_bias;  // nullable
 };
 
 // Thread t owns 16 four-wide pieces of the state.  SVF = 0 (state [K][V]):
@@ -50,6 +52,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
   const int G = a.Hv / a.Hq, hq = h / G;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int lo = tid & 31, hi = tid >> 5;  // piece index within / across half waves
+  const float gate_a = a.gate_A_log ? a.gate_A_log[h] : 0.f;
+  const float gate_b = a.gate_dt_bias ? a.gate_dt_bias[h] : 0.f;
   int64_t t_begin, t_end;
   if (a.cu) {
     t_begin = a.cu[n];
@@ -87,6 +91,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecArgs a) {
     }
     if (tid < 128) rv = to_f(vg[(t * a.Hv + h) * 128 + tid]);
     rg = load_scalar(a.g, t * a.Hv + h, a.g_dtype);
+    if (a.gate_A_log) rg = gate_log_decay(rg, gate_a, gate_b);
     rb = beta_used(to_f(bg[t * a.Hv + h]), a.beta_mode);
   };
   if (t_begin < t_end) load_token(t_begin);
@@ -207,6 +212,8 @@ gdr_status launch_recurrent(const gdr_problem* p, const void* q, const void* k, 
   a.qk_norm = p->use_qk_l2norm ? 1 : 0;
   a.beta_mode = (p->beta_sigmoid ? 1 : 0) | (p->neg_eigval ? 2 : 0);
   a.scale = p->scale;
+  a.gate_A_log = p->use_gate ? p->gate_A_log : nullptr;
+  a.gate_dt_bias = p->use_gate ? p->gate_dt_bias : nullptr;
   if ((int64_t)p->N * p->Hv == 0) return GDR_OK;
   const dim3 grid((unsigned)((int64_t)p->N * p->Hv));
   const bool svf = p->state_v_first != 0;

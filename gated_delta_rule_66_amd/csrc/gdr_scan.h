@@ -151,8 +151,11 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
         for (int e = 0; e < 4; ++e)
           S[kb][vb][e] = (16 * kb + 4 * grp + e == cb0 + cw0 + 16 * vb + col) ? 1.f : 0.f;
   } else {
+    // the value columns of an inner segment's transition start from zero
+    // (their end state is B_seg); its start state is not known before pass 2
     const float* src = (p == 0) ? (a.h0 ? a.h0 + unit * KV : nullptr)
-                                : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+                       : (MODE == MODE_AUG) ? nullptr
+                                            : a.seg_start + ((int64_t)unit * a.P + p) * KV;
     const bool vf = (p == 0) && a.svf;
     const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
 #pragma unroll

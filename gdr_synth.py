@@ -20,6 +20,11 @@ initial state -> do -> dht.
 * do ~ N(0, 1) in the input dtype.
 * packed lengths: uniform integers in [lo, hi], redrawn while a multiple of 64,
   so that every sequence ends in a ragged chunk.
+* problems with the in-kernel gate (``gate``) keep g as the raw gate input
+  N(shift, 1) (no logsigmoid) and draw, after everything else, the per-head
+  parameters A_log = log U(1, 16) and dt_bias ~ U(-6.9, -2.3) in fp32 (the
+  ranges of a Mamba-2 style initialisation: decay rates 1..16 and step sizes
+  of about 0.001..0.1).
 """
 from __future__ import annotations
 
@@ -49,6 +54,7 @@ class Problem:
     g_shift: float = 0.0
     qk_l2norm: bool = False              # raw q, k rows; the kernel normalises them
     beta_logit: bool = False             # beta drawn as the logit N(0, 1) (sigmoid in-kernel)
+    gate: bool = False                   # g is the raw gate input; A_log, dt_bias drawn
     seed: int = 0
     extra: dict = field(default_factory=dict)
 
@@ -100,15 +106,20 @@ def make(prob: Problem, lengths_from=None) -> dict:
         k = F.normalize(k, p=2.0, dim=-1)
     k = k.to(dt)
     v = torch.randn(B, T, Hv, V, generator=gen).to(dt)
-    g = F.logsigmoid(torch.randn(B, T, Hv, generator=gen) + prob.g_shift).to(dt)
+    g = torch.randn(B, T, Hv, generator=gen) + prob.g_shift
+    g = (g if prob.gate else F.logsigmoid(g)).to(dt)
     beta = torch.randn(B, T, Hv, generator=gen)
     beta = (beta if prob.beta_logit else torch.sigmoid(beta)).to(dt)
     N = prob.N
     h0 = (0.1 * torch.randn(N, Hv, K, V, generator=gen)) if prob.init_state else None
     do = torch.randn(B, T, Hv, V, generator=gen).to(dt) if prob.backward else None
     dht = (0.1 * torch.randn(N, Hv, K, V, generator=gen)) if (prob.backward and prob.dht) else None
+    A_log = dt_bias = None
+    if prob.gate:
+        A_log = torch.log(1.0 + 15.0 * torch.rand(Hv, generator=gen))
+        dt_bias = -6.9 + 4.6 * torch.rand(Hv, generator=gen)
     return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, do=do, dht=dht, cu_seqlens=cu,
-                scale=K ** -0.5, qk_l2norm=prob.qk_l2norm)
+                scale=K ** -0.5, qk_l2norm=prob.qk_l2norm, A_log=A_log, dt_bias=dt_bias)
 
 
 # The five workloads.  Sizes are those of the pages' API example

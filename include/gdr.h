@@ -22,7 +22,8 @@
  * Tensor layouts (row-major, contiguous, tokens of all sequences flattened):
  *   q, k          [B, T, Hq, K]           in_dtype
  *   v, o, do, dv  [B, T, Hv, V]           in_dtype
- *   g, dg         [B, T, Hv]              g_dtype (natural-log decay)
+ *   g, dg         [B, T, Hv]              g_dtype (natural-log decay, or the
+ *                                         gate's raw input with use_gate)
  *   beta, dbeta   [B, T, Hv]              in_dtype
  *   g_cum         [B, T, Hv]              fp32: chunk-local inclusive cumsum of g
  *   A             [B, T, Hv, 64]          in_dtype: row r of a chunk's inverse
@@ -112,6 +113,18 @@ typedef struct {
                                      negative eigenvalue; dbeta is with respect
                                      to the input (the PR page's
                                      allow_neg_eigval) */
+  int32_t use_gate;               /* 1: g holds the gate's raw input x and the
+                                     recurrence's log decay is, per token and
+                                     value head h, computed in fp32:
+                                       -exp(gate_A_log[h]) * softplus(x + gate_dt_bias[h])
+                                     (the Mamba-2 discretisation that Gated
+                                     DeltaNet layers use for their decay; the PR
+                                     page's use_gate_in_kernel).  g_cum is the
+                                     cumsum of that log decay; the backward
+                                     then goes through gdr_chunk_bwd_gate. */
+  const float* gate_A_log;        /* device [Hv] fp32: required iff use_gate */
+  const float* gate_dt_bias;      /* device [Hv] fp32, or NULL for a zero bias;
+                                     NULL unless use_gate */
 } gdr_problem;
 
 /* Status name ("GDR_ERR_SHAPE", ...). */
@@ -153,12 +166,29 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
  *   out: dq, dk (in_dtype, [B,T,Hq,K]); dv; dbeta; dg (g_dtype, gradient with
  *        respect to the raw g); dh0 (fp32, written iff initial_state != NULL,
  *        may be NULL otherwise)
+ *   Problems with use_gate are rejected (GDR_ERR_ARG): see gdr_chunk_bwd_gate.
  *   workspace: device buffer of gdr_chunk_bwd_workspace_size(p) bytes. */
 gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                          const float* g_cum, const void* beta, const void* A, const void* do_,
                          const float* dht, const float* initial_state, void* dq, void* dk,
                          void* dv, void* dbeta, void* dg, float* dh0, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Backward with the in-kernel gate (problem->use_gate == 1; gdr_chunk_bwd
+ * rejects such problems).  The arguments of gdr_chunk_bwd, plus:
+ *   in : g, the gate's raw input x the forward took (g_dtype [B,T,Hv])
+ *   out: dg is the gradient with respect to x (g_dtype);
+ *        dA_log, ddt_bias (fp32 [Hv], each nullable = not written): the
+ *        gradients of gate_A_log and gate_dt_bias, sums over every token of
+ *        every sequence, in a fixed order (deterministic)
+ * The workspace (gdr_chunk_bwd_workspace_size) includes 8 bytes per chunk
+ * and value head for the per-chunk partial sums of those two gradients. */
+gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k, const void* v,
+                              const float* g_cum, const void* g, const void* beta, const void* A,
+                              const void* do_, const float* dht, const float* initial_state,
+                              void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
+                              float* dA_log, float* ddt_bias, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Token-by-token forward for short inputs: decode steps, a few speculative
  * tokens, or a prefill continued from a cached state (the "state-cached
@@ -174,7 +204,8 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
  *        initial_state, nullable.  final_state may be the same buffer as
  *        initial_state (the state is updated in place); no other argument
  *        may alias another.
- * Honours cu_seqlens, state_v_first, scale and use_qk_l2norm.  Needs no
+ * Honours cu_seqlens, state_v_first, scale, use_qk_l2norm, the beta options
+ * and use_gate (g is then the gate's raw input).  Needs no
  * workspace.  Costs grow linearly with T; past a few chunks gdr_chunk_fwd is
  * faster.  Errors as gdr_chunk_fwd (validation on the host first). */
 gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,

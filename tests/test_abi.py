@@ -37,6 +37,9 @@ def test_status_strings():
         assert lib.gdr_status_string(code).decode() == name
 
 
+FAKE_DEV = 0x1000  # never dereferenced: validation happens on the host copy
+
+
 def good(**kw):
     base = dict(B=2, T=200, Hq=2, Hv=4, K=128, V=128, N=2, cu_seqlens_dev=None,
                 cu_seqlens_host=None, in_dtype=GDR_BF16, g_dtype=GDR_BF16, scale=0.088,
@@ -56,13 +59,14 @@ def test_acceptance_path():
     assert check(good()) == ("GDR_OK", "")
     assert check(good(in_dtype=GDR_FP16, g_dtype=GDR_FP32))[0] == "GDR_OK"
     assert check(good(use_qk_l2norm=1))[0] == "GDR_OK"
+    assert check(good(use_gate=1, gate_A_log=FAKE_DEV))[0] == "GDR_OK"
+    assert check(good(use_gate=1, gate_A_log=FAKE_DEV, gate_dt_bias=FAKE_DEV))[0] == "GDR_OK"
 
 
 HOST_CU = (ctypes.c_int32 * 4)(0, 70, 70, 200)
 HOST_CU_BAD0 = (ctypes.c_int32 * 4)(1, 70, 70, 200)
 HOST_CU_DEC = (ctypes.c_int32 * 4)(0, 70, 60, 200)
 HOST_CU_END = (ctypes.c_int32 * 4)(0, 70, 70, 199)
-FAKE_DEV = 0x1000  # never dereferenced: validation happens on the host copy
 
 
 def varlen(cu, **kw):
@@ -86,6 +90,9 @@ REJECT = [
     ("qk_l2norm", good(use_qk_l2norm=2), "GDR_ERR_ARG", "use_qk_l2norm"),
     ("beta_sigmoid", good(beta_sigmoid=2), "GDR_ERR_ARG", "beta_sigmoid"),
     ("neg_eigval", good(neg_eigval=-1), "GDR_ERR_ARG", "neg_eigval"),
+    ("use_gate", good(use_gate=2, gate_A_log=FAKE_DEV), "GDR_ERR_ARG", "use_gate"),
+    ("gate without A_log", good(use_gate=1, gate_dt_bias=FAKE_DEV), "GDR_ERR_NULL", "gate_A_log"),
+    ("gate params, gate off", good(gate_dt_bias=FAKE_DEV), "GDR_ERR_ARG", "use_gate is 0"),
 ]
 
 
@@ -120,6 +127,11 @@ def test_workspace_queries():
     assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(good(K=64))) == 0
     long = good(B=1, N=1, T=65536, Hq=32, Hv=32)
     assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(long)) > 0  # context-parallel buffers
+    # the gate adds the per-(chunk, head) parameter-gradient shares: 2 floats each
+    pg = good(use_gate=1, gate_A_log=FAKE_DEV)
+    extra = lib.gdr_chunk_bwd_workspace_size(ctypes.byref(pg)) - \
+        lib.gdr_chunk_bwd_workspace_size(ctypes.byref(p))
+    assert 2 * 4 * 4 * 8 <= extra < 2 * 4 * 4 * 8 + 256   # B=2 x 4 chunks, Hv=4
 
 
 def plan(p, backward):
@@ -164,6 +176,21 @@ def test_null_and_workspace_errors_before_any_device_work():
     st = lib.gdr_recurrent_fwd(ctypes.byref(good(K=64)), P(16), P(16), P(16), P(16), P(16), None,
                                P(16), None, None)
     assert _lib.STATUS[st] == "GDR_ERR_HEAD_DIM"
+    # the gate: the plain backward refuses it, the gated backward needs it and g
+    pg = good(use_gate=1, gate_A_log=FAKE_DEV)
+    args = [P(16)] * 16
+    st = lib.gdr_chunk_bwd(ctypes.byref(pg), *args[:7], None, *args[7:14], P(16), 1 << 40, None)
+    assert _lib.STATUS[st] == "GDR_ERR_ARG" and "gdr_chunk_bwd_gate" in lib.gdr_last_error().decode()
+    gate_args = [P(16)] * 19  # q .. ddt_bias, workspace
+    st = lib.gdr_chunk_bwd_gate(ctypes.byref(p), *gate_args, 1 << 40, None)
+    assert _lib.STATUS[st] == "GDR_ERR_ARG" and "use_gate" in lib.gdr_last_error().decode()
+    gate_args[4] = None  # the gate input g
+    st = lib.gdr_chunk_bwd_gate(ctypes.byref(pg), *gate_args, 1 << 40, None)
+    assert _lib.STATUS[st] == "GDR_ERR_NULL"
+    gate_args[4] = P(16)
+    gate_args[16] = gate_args[17] = None  # the parameter gradients are optional
+    st = lib.gdr_chunk_bwd_gate(ctypes.byref(pg), *gate_args, 1, None)
+    assert _lib.STATUS[st] == "GDR_ERR_WORKSPACE"
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="exercises the no-device path")
@@ -183,6 +210,8 @@ def test_python_rejects_verifier_options():
     import gated_delta_rule_66_amd as gdr
     x = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
     g = torch.zeros(1, 4, 1, dtype=torch.bfloat16)
-    for opt in ("use_gate_in_kernel", "transpose_state_layout"):
-        with pytest.raises(NotImplementedError):
-            gdr.chunk_gated_delta_rule(x, x, x, g, g, **{opt: True})
+    with pytest.raises(NotImplementedError):
+        gdr.chunk_gated_delta_rule(x, x, x, g, g, transpose_state_layout=True)
+    # the gate is supported, but needs its decay parameters
+    with pytest.raises(gdr.GdrError):
+        gdr.chunk_gated_delta_rule(x, x, x, g, g, use_gate_in_kernel=True)

@@ -1,0 +1,87 @@
+"""The workspace needs no initialisation: every kernel reads only workspace
+memory that an earlier kernel of the same call wrote (needs an MI355X).
+
+Each case runs the forward and the backward on a caller workspace filled with
+0xFF bytes (NaN as fp32 and bf16, -1 as int32), so any read of memory the call
+did not write shows up as NaN or a wrong value.  The plans include context
+parallelism with one-chunk segments, where the transition pass of an inner
+segment must start its value columns from zero rather than from the (not yet
+chained) segment start state."""
+import pytest
+import torch
+
+import gdr_synth
+import oracle
+from _util import TOL, np64, ratio, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dbeta", "dg", "dh0")
+WS_BYTES = 256 << 20
+
+
+def P(name, **kw):
+    kw.setdefault("init_state", True)
+    kw.setdefault("backward", True)
+    kw.setdefault("dht", True)
+    return gdr_synth.Problem(name, **kw)
+
+
+# (problem, cp_segments, wave_tiles)
+CASES = {
+    "one_chunk_segments_3": (P("s3", B=1, T=0, Hq=2, Hv=2, lens=[129]), 3, 1),
+    "one_chunk_segments_4": (P("s4", B=1, T=0, Hq=2, Hv=2, lens=[250]), 4, 1),
+    "mixed_varlen_cp3": (P("mix", B=1, T=0, Hq=2, Hv=2, lens=[70, 1, 64, 129, 250]), 3, 1),
+    "dense_cp4_vt2": (P("d4", B=2, T=600, Hq=2, Hv=2, g_shift=2.0), 4, 2),
+    "gva_fp16_cp2": (P("gva", B=1, T=333, Hq=1, Hv=4, dtype="fp16"), 2, 1),
+    "gate_gva_cp3": (P("gate", B=1, T=0, Hq=1, Hv=2, lens=[129, 200], gate=True), 3, 1),
+    "no_cp": (P("plain", B=2, T=200, Hq=2, Hv=4), 1, 1),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_poisoned_workspace(name):
+    import gated_delta_rule_66_amd as gdr
+    prob, cp, vt = CASES[name]
+    d = gdr_synth.make(prob)
+    print("case", name, "cp", cp, "vt", vt, flush=True)
+    dd = to_dev(d)
+    cu_cpu = d["cu_seqlens"]
+    gate = d["A_log"] is not None
+    kw = dict(use_gate_in_kernel=True, A_log=dd["A_log"], dt_bias=dd["dt_bias"]) if gate else {}
+    ws = torch.empty(WS_BYTES, dtype=torch.uint8, device="cuda")
+    outs = []
+    for rep in range(2):  # the second call finds the first call's leftovers
+        if rep == 0:
+            ws.fill_(0xFF)
+        g_cum, A, o, _, ht = gdr.chunk_gated_delta_rule_fwd(
+            dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
+            initial_state=dd["h0"], output_final_state=True, cu_seqlens=dd["cu_seqlens"],
+            cp_segments=cp, wave_tiles=vt, cu_seqlens_cpu=cu_cpu, workspace=ws, **kw)
+        if rep == 0:
+            ws.fill_(0xFF)
+        bkw = dict(kw, g_input=dd["g"]) if gate else {}
+        grads = gdr.chunk_gated_delta_rule_bwd(
+            dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dd["dht"],
+            scale=dd["scale"], initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
+            cp_segments=cp, wave_tiles=vt, cu_seqlens_cpu=cu_cpu, workspace=ws, **bkw)
+        torch.cuda.synchronize()
+        outs.append((o, ht) + tuple(grads))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)  # and deterministic
+    cu = None if cu_cpu is None else cu_cpu.numpy()
+    args = (np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]), d["scale"])
+    okw = dict(gate=(np64(d["A_log"]), np64(d["dt_bias"]))) if gate else {}
+    o_r, ht_r = oracle.fwd(*args, initial_state=np64(d["h0"]), cu_seqlens=cu, **okw)
+    ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]),
+                     cu_seqlens=cu, **okw)
+    o, ht = outs[0][:2]
+    grads = outs[0][2:]
+    res = {"o": ratio(np64(o), o_r), "final_state": ratio(np64(ht), ht_r)}
+    for nm, x, r in zip(NAMES, grads, ref):
+        res[nm] = ratio(np64(x), r)
+    print({k: round(v, 5) for k, v in res.items()}, flush=True)
+    for t in outs[0]:
+        assert bool(torch.isfinite(t).all())
+    for k, v in res.items():
+        assert v <= TOL, (k, v)
