@@ -118,7 +118,7 @@ def measured_traffic(kernel, workload, launches_bytes):
     return (k["fetch_kib"] * t["fetch_factor"] + k["write_kib"] * t["write_factor"]) * 1024.0
 
 
-def cpu_baseline(d, prob, nthreads_cap=16, max_units=32, qk_norm=False):
+def cpu_baseline(d, prob, nthreads_cap=16, max_units=32, qk_norm=False, gate=False):
     """The fp64 oracle, as it stands, on a bounded sample of the workload."""
     import numpy as np
     import oracle
@@ -151,10 +151,13 @@ def cpu_baseline(d, prob, nthreads_cap=16, max_units=32, qk_norm=False):
     units = nh * nseq
     threads = max(1, min(nthreads_cap, avail, units))
     t0 = time.perf_counter()
+    gkw = {}
+    if gate:
+        gkw["gate"] = (d["A_log"][:nh].double().numpy(), d["dt_bias"][:nh].double().numpy())
     oracle.fwd(q, k, v, g, beta, d["scale"], initial_state=h0, cu_seqlens=cun, nthreads=threads,
-               use_qk_l2norm=qk_norm)
+               use_qk_l2norm=qk_norm, **gkw)
     oracle.bwd(q, k, v, g, beta, d["scale"], do, initial_state=h0, dht=dht, cu_seqlens=cun,
-               nthreads=threads, use_qk_l2norm=qk_norm)
+               nthreads=threads, use_qk_l2norm=qk_norm, **gkw)
     dt = time.perf_counter() - t0
     total_units = (B if cu is None else nseq) * Hv
     frac = units / float(total_units)
@@ -182,6 +185,9 @@ def main():
                     help="16-column state tiles per wave in the scans (0 = the library's plan)")
     ap.add_argument("--qk-l2norm", action="store_true",
                     help="raw q / k rows, normalised inside the kernels (use_qk_l2norm_in_kernel)")
+    ap.add_argument("--gate", action="store_true",
+                    help="g is the raw gate input, activated inside the kernels "
+                         "(use_gate_in_kernel: -exp(A_log) softplus(g + dt_bias))")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path runs on a single MI355X and this build "
@@ -196,13 +202,16 @@ def main():
         return bench_decode(args)
     B, T, Hq, Hv, dt, g_shift, varlen = WORKLOADS[args.workload]
     prob = gdr_synth.Problem(args.workload, B=B, T=T, Hq=Hq, Hv=Hv, dtype=dt, init_state=True,
-                             backward=True, dht=True, g_shift=g_shift, qk_l2norm=args.qk_l2norm)
+                             backward=True, dht=True, g_shift=g_shift, qk_l2norm=args.qk_l2norm,
+                             gate=args.gate)
     qkn = args.qk_l2norm
     d = gdr_synth.make(prob, lengths_from=varlen)
     B, T = prob.B, prob.T
     dev = torch.device("cuda", 0)
     dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
     cu_cpu = d["cu_seqlens"]
+    gkw = dict(use_gate_in_kernel=True, A_log=dd["A_log"], dt_bias=dd["dt_bias"]) \
+        if args.gate else {}
     plans = {d_: gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
                                cu_seqlens_cpu=cu_cpu, cp_segments=args.cp, wave_tiles=args.vt,
                                backward=(d_ == "bwd"))
@@ -214,7 +223,7 @@ def main():
                                               output_final_state=True,
                                               cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=cu_cpu,
                                               cp_segments=args.cp, wave_tiles=args.vt,
-                                              use_qk_l2norm_in_kernel=qkn)
+                                              use_qk_l2norm_in_kernel=qkn, **gkw)
 
     def bwd(g_cum, A):
         return gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
@@ -222,7 +231,8 @@ def main():
                                               initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
                                               dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu,
                                               cp_segments=args.cp, wave_tiles=args.vt,
-                                              use_qk_l2norm_in_kernel=qkn)
+                                              use_qk_l2norm_in_kernel=qkn,
+                                              **(dict(gkw, g_input=dd["g"]) if args.gate else {}))
 
     def step():
         g_cum, A, o, _, ht = fwd()
@@ -287,8 +297,8 @@ def main():
     achieved = nbytes / avg_s / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, args.workload + ("+qk_l2norm" if qkn else ""),
-                                            nbytes),
+                "traffic": measured_traffic(dom, args.workload + ("+qk_l2norm" if qkn else "")
+                                            + ("+gate" if args.gate else ""), nbytes),
                 "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2)}
 
     out = {
@@ -303,14 +313,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dt,
-        "data": ("synthetic (seeded; raw N(0,1) q,k normalised in-kernel, g=logsigmoid, "
-                 "beta=sigmoid)" if qkn else
-                 "synthetic (seeded; q,k L2-normalised, g=logsigmoid, beta=sigmoid)"),
+        "data": "synthetic (seeded; %s, %s, beta=sigmoid)" % (
+            "raw N(0,1) q,k normalised in-kernel" if qkn else "q,k L2-normalised",
+            "g = raw gate input N(0,1), activated in-kernel" if args.gate else "g=logsigmoid"),
         "config": {"workload": args.workload, "B": B, "T": T, "Hq": Hq, "Hv": Hv, "K": 128,
                    "V": 128, "chunk": 64, "tokens": tokens,
                    "cp_segments": {k_: v_[0] for k_, v_ in plans.items()},
                    "wave_tiles": {k_: v_[1] for k_, v_ in plans.items()},
-                   "qk_l2norm_in_kernel": qkn, "parallelism": "single GPU"},
+                   "qk_l2norm_in_kernel": qkn, "gate_in_kernel": bool(args.gate),
+                   "parallelism": "single GPU"},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "tflops": round(tflops, 3),
@@ -320,7 +331,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(d, (B, T, Hq, Hv), qk_norm=qkn)
+        out["cpu_baseline"] = cpu_baseline(d, (B, T, Hq, Hv), qk_norm=qkn, gate=args.gate)
     print(json.dumps(out), flush=True)
 
 

@@ -734,6 +734,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   __shared__ float rowq[64];         // dgamma row terms of the dq side
   __shared__ float dbf[64];          // d beta / d (beta input) per row
   __shared__ float xinv[2][64];      // 1 / |q|, 1 / |k| per row (q / k normalisation)
+  __shared__ float gsl[2][64];       // the gate's slope and log decay per row (gate on)
 
   const int c = blockIdx.x, h = blockIdx.y;
   int n, j;
@@ -776,7 +777,12 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     tile_store<T, 64, 512>(Vs, L7, rv);
     tile_store<T, 64, 512>(Os, L7, ro);
   };
-  // every load of the first phase is issued before the first LDS store
+  // every load of the first phase is issued before the first LDS store, the
+  // per-row values (gamma, beta, the gate input) right after the tiles, so
+  // that their latency overlaps the tiles' instead of following it
+  float p_gr = 0.f, p_gl = 0.f;
+  T p_b = from_f<T>(0.f);
+  uint32_t p_x = 0;
   {
     TileRegs<128, 512> rq, rk;
     TileRegs<64, 512> ra;
@@ -787,6 +793,15 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     tile_load<T, 64, 512>(ra, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
                           (int64_t)a.Hv * kChunk, Cc);
     load_half(0);
+    if (tid < 64) {
+      const int64_t row = (t0 + min(tid, Cc - 1)) * a.Hv + h;
+      p_gr = a.gcum[row];
+      p_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
+      p_b = reinterpret_cast<const T*>(a.beta)[row];
+      if (a.gate_A_log)  // raw bits: converted after the tile stores
+        p_x = a.g_dtype == 2 ? reinterpret_cast<const uint32_t*>(a.graw)[row]
+                             : (uint32_t)reinterpret_cast<const uint16_t*>(a.graw)[row];
+    }
     if (QKN) {
       l2norm_rows<T, 512>(rq, xinv[0]);
       l2norm_rows<T, 512>(rk, xinv[1]);
@@ -797,9 +812,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     store_half();
   }
   if (tid < 64) {
-    const float gr = a.gcum[(t0 + min(tid, Cc - 1)) * a.Hv + h];
-    const float gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
-    const float bx = to_f(reinterpret_cast<const T*>(a.beta)[(t0 + min(tid, Cc - 1)) * a.Hv + h]);
+    const float gr = p_gr, gl = p_gl, bx = to_f(p_b);
     const float bt = (tid < Cc) ? beta_used(bx, a.beta_mode) : 0.f;
     const float e = __expf(gr);
     gam[tid] = gr;
@@ -809,6 +822,14 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     bex[tid] = bt * e;
     dl[tid] = __expf(gl - gr);
     dgam[tid] = 0.f;
+    if (a.gate_A_log) {
+      const float ga = a.gate_A_log[h], gb = a.gate_dt_bias ? a.gate_dt_bias[h] : 0.f;
+      const float xin = a.g_dtype == 2 ? __builtin_bit_cast(float, p_x)
+                        : a.g_dtype == 0 ? __builtin_bit_cast(float, p_x << 16)
+                                         : (float)__builtin_bit_cast(_Float16, (uint16_t)p_x);
+      gsl[0][tid] = tid < Cc ? gate_log_decay_grad(xin, ga, gb) : 0.f;
+      gsl[1][tid] = tid < Cc ? gate_log_decay(xin, ga, gb) : 0.f;
+    }
   }
   __syncthreads();
   const float gL = gam[63];
@@ -1212,11 +1233,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     if (a.gate_A_log) {
       // x is the gradient of the row's log decay; the gate input's gradient is
       // x times the gate's slope, and the chunk's shares of d A_log and
-      // d dt_bias are the sums of x * logdecay and of that gradient
-      const float ga = a.gate_A_log[h], gb = a.gate_dt_bias ? a.gate_dt_bias[h] : 0.f;
-      const float xin = r < Cc ? load_scalar(a.graw, (t0 + r) * a.Hv + h, a.g_dtype) : 0.f;
-      const float pa = r < Cc ? x * gate_log_decay(xin, ga, gb) : 0.f;
-      x = r < Cc ? x * gate_log_decay_grad(xin, ga, gb) : 0.f;
+      // d dt_bias are the sums of x * logdecay and of that gradient (rows
+      // past the chunk's end hold zero slope and log decay)
+      const float pa = x * gsl[1][r];
+      x *= gsl[0][r];
       const float sa = sum4g(sum16(pa)), sb = sum4g(sum16(x));
       if (l == 0) {
         a.gpart[((int64_t)c * a.Hv + h) * 2] = sa;
