@@ -85,3 +85,57 @@ def test_poisoned_workspace(name):
         assert bool(torch.isfinite(t).all())
     for k, v in res.items():
         assert v <= TOL, (k, v)
+
+
+_SWEEP = {}
+
+
+def _sweep_reference():
+    """Inputs and fp64 results for the plan sweep, computed once."""
+    if not _SWEEP:
+        d = gdr_synth.make(P("sweep", B=1, T=0, Hq=1, Hv=2,
+                             lens=[1, 63, 64, 65, 129, 200, 400, 0, 130]))
+        cu = d["cu_seqlens"].numpy()
+        args = (np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]),
+                d["scale"])
+        o_r, ht_r = oracle.fwd(*args, initial_state=np64(d["h0"]), cu_seqlens=cu)
+        ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]),
+                         cu_seqlens=cu)
+        _SWEEP.update(d=d, ref=(o_r, ht_r) + tuple(ref))
+    return _SWEEP["d"], _SWEEP["ref"]
+
+
+@pytest.mark.parametrize("vt", [1, 2])
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 5, 7, 8])
+def test_every_plan_on_a_poisoned_workspace(cp, vt):
+    """Every segment count and tile width on one packed batch whose sequences
+    split into empty, one-chunk and ragged segments: each plan matches the
+    oracle on a workspace filled with NaN bytes."""
+    import gated_delta_rule_66_amd as gdr
+    d, ref = _sweep_reference()
+    print("sweep cp", cp, "vt", vt, flush=True)
+    dd = to_dev(d)
+    cu_cpu = d["cu_seqlens"]
+    for bwd in (False, True):  # the plan asked for is the plan that runs (7 chunks at most)
+        assert gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=cu_cpu,
+                             cp_segments=cp, wave_tiles=vt, backward=bwd) == (min(cp, 7), vt)
+    ws = torch.full((WS_BYTES // 4,), 0xFF, dtype=torch.uint8, device="cuda")
+    g_cum, A, o, _, ht = gdr.chunk_gated_delta_rule_fwd(
+        dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
+        initial_state=dd["h0"], output_final_state=True, cu_seqlens=dd["cu_seqlens"],
+        cp_segments=cp, wave_tiles=vt, cu_seqlens_cpu=cu_cpu, workspace=ws)
+    ws.fill_(0xFF)
+    grads = gdr.chunk_gated_delta_rule_bwd(
+        dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dd["dht"],
+        scale=dd["scale"], initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"], cp_segments=cp,
+        wave_tiles=vt, cu_seqlens_cpu=cu_cpu, workspace=ws)
+    torch.cuda.synchronize()
+    res = {}
+    for nm, x, r in zip(("o", "final_state") + NAMES, (o, ht) + tuple(grads), ref):
+        res[nm] = ratio(np64(x), r)
+    print({k: round(v, 5) for k, v in res.items()}, flush=True)
+    for k, v in res.items():
+        assert v <= TOL, (k, v)
+    # the empty sequence keeps its state; its state gradient passes through
+    assert torch.equal(ht[7].cpu(), d["h0"][7])
+    assert torch.equal(grads[5][7].cpu(), d["dht"][7])
