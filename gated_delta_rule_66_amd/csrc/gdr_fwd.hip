@@ -55,9 +55,19 @@ template <typename T>
 __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   constexpr int LDK = 136;
   constexpr int LDM = 68;
-  __shared__ __align__(16) T Ks[64 * LDK];
-  __shared__ float Mf[64 * LDM];
-  __shared__ float Ai[64 * LDM];
+  static_assert(64 * LDK * sizeof(T) == 64 * LDM * sizeof(float), "Ks and Ai share storage");
+  // the k tile is dead once M is formed (a barrier follows), so the inverse
+  // reuses its storage: 35 KB per workgroup, four workgroups per CU
+  __shared__ __align__(16) float KsAi[64 * LDM];
+  T* const Ks = reinterpret_cast<T*>(KsAi);
+  float* const Ai = KsAi;
+  // M keeps only its ten lower 16 x 16 blocks (the only ones written or
+  // read), block (bi, bj), bj <= bi, at slot bi (bi + 1) / 2 + bj, rows 20
+  // floats apart: 31 KB per workgroup in all, five workgroups per CU
+  constexpr int MB = 20;
+  __shared__ float Mf[10 * 16 * MB];
+  auto mf = [](int r, int c) { return ((r >> 4) * ((r >> 4) + 1) / 2 + (c >> 4)) * 16 * MB +
+                                      (r & 15) * MB + (c & 15); };
   __shared__ float gam[64], bet[64];
 
   const int c = blockIdx.x, h = blockIdx.y;
@@ -97,18 +107,18 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
 
   // M, rows 16w .. 16w+15 (only the blocks on or below the diagonal are nonzero)
   for (int cb = 0; cb < 4; ++cb) {
-    f32x4 acc = zero4();
     if (cb <= w) {
+      f32x4 acc = zero4();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         acc = mfma16(frag_row(Ks + 16 * w * LDK + 32 * kk, LDK),
                      frag_row(Ks + 16 * cb * LDK + 32 * kk, LDK), acc);
-    }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
-      // masked entries take exp(-inf) = 0 (an unconditional exponential)
-      Mf[r * LDM + i] = bet[r] * __expf(i < r ? gam[r] - gam[i] : -INFINITY) * acc[e];
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
+        // masked entries take exp(-inf) = 0 (an unconditional exponential)
+        Mf[mf(r, i)] = bet[r] * __expf(i < r ? gam[r] - gam[i] : -INFINITY) * acc[e];
+      }
     }
   }
   // (the blocks of the inverse above the diagonal are never read)
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       float acc = (r == l) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc -= Mf[(b0 + r) * LDM + b0 + i] * x[i];
+      for (int i = 0; i < r; ++i) acc -= Mf[mf(b0 + r, b0 + i)] * x[i];
       x[r] = acc;
     }
 #pragma unroll
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
       for (int m = bj; m < bi; ++m) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          const float av = Mf[(16 * bi + col) * LDM + 16 * m + 4 * st + grp];
+          const float av = Mf[mf(16 * bi + col, 16 * m + 4 * st + grp)];
           const float bv = Ai[(16 * m + 4 * st + grp) * LDM + 16 * bj + col];
           t = mfma16f32(av, bv, t);
         }
