@@ -777,9 +777,9 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     tile_store<T, 64, 512>(Vs, L7, rv);
     tile_store<T, 64, 512>(Os, L7, ro);
   };
-  // every load of the first phase is issued before the first LDS store, the
-  // per-row values (gamma, beta, the gate input) right after the tiles, so
-  // that their latency overlaps the tiles' instead of following it
+  // q, k, A and the per-row values (gamma, beta, the gate input) are loaded
+  // and stored first; value half 0's tiles (S^T, dSn^T, V, dO) are issued
+  // next and stored only after the P / N phase, which overlaps their latency
   float p_gr = 0.f, p_gl = 0.f;
   T p_b = from_f<T>(0.f);
   uint32_t p_x = 0;
@@ -792,7 +792,6 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
                            (int64_t)a.Hq * kDim, Cc);
     tile_load<T, 64, 512>(ra, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
                           (int64_t)a.Hv * kChunk, Cc);
-    load_half(0);
     if (tid < 64) {
       const int64_t row = (t0 + min(tid, Cc - 1)) * a.Hv + h;
       p_gr = a.gcum[row];
@@ -802,6 +801,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
         p_x = a.g_dtype == 2 ? reinterpret_cast<const uint32_t*>(a.graw)[row]
                              : (uint32_t)reinterpret_cast<const uint16_t*>(a.graw)[row];
     }
+    load_half(0);
     if (QKN) {
       l2norm_rows<T, 512>(rq, xinv[0]);
       l2norm_rows<T, 512>(rk, xinv[1]);
@@ -809,7 +809,6 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     tile_store_q<T, 512>(Qs, rq);
     tile_store_q<T, 512>(Ks, rk);
     tile_store<T, 64, 512>(As, L7, ra);
-    store_half();
   }
   if (tid < 64) {
     const float gr = p_gr, gl = p_gl, bx = to_f(p_b);
@@ -856,6 +855,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       if (!hi) Ps[r * L7 + i] = from_f<T>(pn[cb][e]);
     }
   }
+
+  // half 0's tiles; the barrier also publishes Ps, which side 1 reads below
+  store_half();
+  __syncthreads();
 
   // accumulators over the value halves: side 0 accA = dA, accB = dP,
   // acc1 = dQ1; side 1 acc1 = dX, acc2 = dKs
