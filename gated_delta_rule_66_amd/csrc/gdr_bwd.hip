@@ -342,25 +342,31 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
   }
 }
 
-// B2 output pass (one 64-column block, 8 waves): waves 4-7 issue every
-// chunk load and tile store, waves 0-3 run the chain of dh_body unchanged, so
-// the vector-memory issue is off the chain.
+// B2 output pass (one 64-column block, 8 waves).  Waves 0-3 run the chain;
+// waves 4-7 issue every chunk load and tile store.  The q / k tiles and the
+// per-row values of two chunks are kept (slot = chunk & 1).  In the
+// iteration of chunk c, before the middle barrier, the helpers store chunk
+// c's dO and A tiles, chunk c-1's q / k slot and chunk c+1's dSn, while the
+// chain waves form K dSn and, each a quarter of its tiles, P of chunk c;
+// after it the chain finishes chunk c and the helpers issue the loads of the
+// next chunks.
 template <typename T, int OPT>
 __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
-  constexpr int VB = 1, MODE = MODE_OUT;
   typedef typename VT<T>::x8 x8;
-  constexpr int CW = 64 * VB;
+  constexpr int CW = 64;
   constexpr int LD = 136;
   constexpr int LDV = CW + 8;
   constexpr int LDA = 72;
-  __shared__ __align__(16) T Qs[64 * LD];
-  __shared__ __align__(16) T Ks[64 * LD];
+  __shared__ __align__(16) T Qs[2][64 * LD];
+  __shared__ __align__(16) T Ks[2][64 * LD];
   __shared__ __align__(16) T Ds[64 * LDV];
+  __shared__ __align__(16) T Es[64 * LDV];  // scale diag(e^gamma) dO
   __shared__ __align__(16) T As[64 * LDA];
-  __shared__ __align__(16) float gam[64], eg[64], bex[64], dl[64];
-  // dSn of the chain's chunk as bf16 operand registers ([buf][column block]
-  // [k block][lane]); the helpers store it one iteration later
-  __shared__ __align__(16) x8 Hx[2][4][4][64];
+  __shared__ __align__(16) T Ps[64 * LDA];
+  __shared__ __align__(16) float gam[2][64], eg[2][64], bex[2][64], dl[2][64];
+  // dSn of the chain's chunk as bf16 operand registers ([column block][k
+  // block][lane]), stored by the helpers in the next iteration
+  __shared__ __align__(16) x8 Hx[4][4][64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const bool helper = w >= 4;
@@ -373,15 +379,8 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   const SeqInfo s = seq_info(a.cu, n, a.T);
   const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
   const SegRange sr = seg_range(nch, a.P, p);
+  if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;
   const int cb0 = vs * CW;
-  const bool isT = (MODE == MODE_AUG) && cb0 < kDim;
-  if (MODE == MODE_AUG) {
-    if (p == 0 || p > sr.p_last) return;       // segment 0 needs no transition
-    if (p == sr.p_last && isT) return;         // the last segment starts from dht
-  } else {
-    if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;
-  }
-  const int vcol0 = (MODE == MODE_AUG) ? (isT ? 0 : cb0 - kDim) : cb0;
   const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
   const int64_t KV = (int64_t)kDim * kDim;
   const T* q = reinterpret_cast<const T*>(a.q);
@@ -389,36 +388,24 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   const T* dO = reinterpret_cast<const T*>(a.dO);
   const T* Ag = reinterpret_cast<const T*>(a.A);
   const T* beta = reinterpret_cast<const T*>(a.beta);
-  const int cw0 = 16 * VB * (w & 3);
+  const int cw0 = 16 * (w & 3);
 
-  // gradient entering the segment's end: dht (last segment) or the chained
-  // value; every load is issued before the first is used (null reads zeros)
-  f32x4 Gs[8][VB];
-  if (MODE == MODE_AUG && isT) {
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          Gs[kb][vb][e] = (16 * kb + 4 * grp + e == cb0 + cw0 + 16 * vb + col) ? 1.f : 0.f;
-  } else {
-    // the value columns of an inner segment's transition start from zero
-    // (their end state is b_seg); the gradient entering it comes from pass 2
+  // gradient entering the segment's end: dht (last segment) or the value
+  // chained by pass 2; every load is issued before the first is used (null
+  // reads zeros)
+  f32x4 Gs[8];
+  {
     const float* src = (p == sr.p_last) ? (a.dht ? a.dht + unit * KV : nullptr)
-                       : (MODE == MODE_AUG) ? nullptr
-                                            : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+                                        : a.seg_start + ((int64_t)unit * a.P + p) * KV;
     const bool vf = (p == sr.p_last) && a.svf;
     const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
-          Gs[kb][vb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
+        Gs[kb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
+      }
   }
 
   TileRegs<128, 256> rq, rk;
@@ -427,19 +414,42 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   float r_g = 0.f, r_gl = 0.f;
   T r_b = from_f<T>(0.f);
   bool r_ok = false;  // the row is inside the chunk
-  auto prefetch = [&](int c) {
+  auto chunk_rows = [&](int c) { return (int)min((int64_t)kChunk, s.end - s.start - (int64_t)kChunk * c); };
+  // q, k tiles and per-row values of chunk c
+  auto load_qk = [&](int c) {
     const int64_t t0 = s.start + (int64_t)kChunk * c;
-    const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+    const int Cc = chunk_rows(c);
     tile_load<T, 128, 256>(rq, q + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
     tile_load<T, 128, 256>(rk, k + (t0 * a.Hq + hq) * kDim, (int64_t)a.Hq * kDim, Cc, otid);
-    tile_load<T, CW, 256>(rd, dO + (t0 * a.Hv + h) * kDim + vcol0, (int64_t)a.Hv * kDim, Cc, otid);
-    tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc, otid);
     if (otid < 64) {
       r_g = a.gcum[(t0 + min(otid, Cc - 1)) * a.Hv + h];
       r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
       r_b = (otid < Cc) ? beta[(t0 + otid) * a.Hv + h] : from_f<T>(0.f);
       r_ok = otid < Cc;
     }
+  };
+  auto store_qk = [&](int c) {
+    const int b = c & 1;
+    if (OPT & 1) {
+      l2norm_rows<T, 256>(rq, nullptr, otid);
+      l2norm_rows<T, 256>(rk, nullptr, otid);
+    }
+    tile_store<T, 128, 256>(Qs[b], LD, rq, otid);
+    tile_store<T, 128, 256>(Ks[b], LD, rk, otid);
+    if (otid < 64) {
+      const float e = __expf(r_g);
+      gam[b][otid] = r_g;
+      eg[b][otid] = a.scale * e;
+      bex[b][otid] = ((OPT & 2) ? (r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f) : to_f(r_b)) * e;
+      dl[b][otid] = __expf(r_gl - r_g);
+    }
+  };
+  // dO and A tiles of chunk c
+  auto load_da = [&](int c) {
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int Cc = chunk_rows(c);
+    tile_load<T, CW, 256>(rd, dO + (t0 * a.Hv + h) * kDim + cb0, (int64_t)a.Hv * kDim, Cc, otid);
+    tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc, otid);
   };
 
   // gradient of chunk cc's end state out, value-major ([V][K]), from the
@@ -453,171 +463,206 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
     const int vc = cb0 + 16 * wq + col;
 #pragma unroll
     for (int kb2 = 0; kb2 < 4; ++kb2) {
-      const x8 g = Hx[cc & 1][wq][kb2][l];
+      const x8 g = Hx[wq][kb2][l];
       const u32x4 u = __builtin_bit_cast(u32x4, g);
       buf_store8(hrs, (vc * kDim + 32 * kb2 + 4 * grp) * (int)sizeof(T), u32x2{u[0], u[1]});
       buf_store8(hrs, (vc * kDim + 32 * kb2 + 16 + 4 * grp) * (int)sizeof(T), u32x2{u[2], u[3]});
     }
   };
 
-  // the initial state has arrived before the loop (else the loop-entry merge
-  // makes the first use of Gs wait for the prefetch as well)
+  // the initial gradient has arrived before the loop (else the loop-entry
+  // merge makes its first use wait for the helpers' loads as well)
   __builtin_amdgcn_s_waitcnt(0);
-  if (helper && sr.c0 < sr.c1) prefetch(sr.c1 - 1);
+  // the two tiles above the diagonal that P^T's products read stay zero
+  p_zero_tiles<T>(Ps, LDA);
+  if (helper && sr.c0 < sr.c1) {
+    const int cf = sr.c1 - 1;
+    load_da(cf);
+    load_qk(cf);
+    store_qk(cf);
+    if (cf - 1 >= sr.c0) load_qk(cf - 1);
+  }
+  // this chain wave's P tiles (as in p_tiles): 3, 3, 2, 2 per wave, (row
+  // block, column block) 4 bits each
+  constexpr uint64_t pcode = 0x0000ull | (0x8ull << 4) | (0xFull << 8) |
+                             ((0x4ull | (0x5ull << 4) | (0xCull << 8)) << 16) |
+                             ((0x9ull | (0xAull << 4)) << 32) |
+                             ((0xDull | (0xEull << 4)) << 48);
+  const int wu = __builtin_amdgcn_readfirstlane(w & 3);
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
-    __syncthreads();
+    const int b = c & 1;
+    __syncthreads();  // chunk c's slot is ready; every wave is done with chunk c+1
+    f32x4 dd[4];
     if (helper) {
-      if (OPT & 1) {
-        l2norm_rows<T, 256>(rq, nullptr, otid);
-        l2norm_rows<T, 256>(rk, nullptr, otid);
-      }
-      tile_store<T, 128, 256>(Qs, LD, rq, otid);
-      tile_store<T, 128, 256>(Ks, LD, rk, otid);
       tile_store<T, CW, 256>(Ds, LDV, rd, otid);
       tile_store<T, 64, 256>(As, LDA, ra, otid);
-      if (otid < 64) {
-        const float e = __expf(r_g);
-        gam[otid] = r_g;
-        eg[otid] = a.scale * e;
-        bex[otid] = ((OPT & 2) ? (r_ok ? beta_used(to_f(r_b), a.beta_mode) : 0.f) : to_f(r_b)) * e;
-        dl[otid] = __expf(r_gl - r_g);
+      // the dO tile scaled by scale e^gamma of its row (chunk c's per-row
+      // values were stored one iteration earlier), the B operand of Q^T
+#pragma unroll
+      for (int i = 0; i < TileRegs<CW, 256>::N; ++i) {
+        constexpr int PR = TileRegs<CW, 256>::PER_ROW;
+        const int x = otid + i * 256, r = x / PR, c8 = (x % PR) * 8;
+        const float f = eg[b][r];
+        x8 v = __builtin_bit_cast(x8, rd.r[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = from_f<T>(to_f(v[e]) * f);
+        *reinterpret_cast<x8*>(Es + r * LDV + c8) = v;
       }
-    }
-    __syncthreads();
-    if (helper) {
-      if (c - 1 >= sr.c0) prefetch(c - 1);
+      if (c - 1 >= sr.c0) store_qk(c - 1);
+      // last: a later wait on this wave's vector memory counter would also
+      // wait for these stores
       if (c + 1 < sr.c1) store_dh(c + 1);
-      continue;
-    }
-    const float eL = __expf(gam[63]);
-
-    // One pass over the key dimension forms K dSn and the lower tiles of
-    // P = Q K^T (tile (rb, ib), ib <= rb: rows r = 16 rb + 4 grp + e, column
-    // i = 16 ib + col) from the same K fragments.
-    x8 Gb[4][VB];
+    } else {
+      // K dSn and this wave's tiles of P = lower_incl(Q K^T o Gamma) of
+      // chunk c (published by the middle barrier), in four rounds over the
+      // key dimension; every fragment of a round is read before it
+      // multiplies.  P contracts over the keys, so the split k order of the
+      // K dSn fragments serves it too.
+      x8 Gb[4];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 4; ++kb2) {
-      Gb[kb2][0] = pack_split<T>(Gs[2 * kb2][0], Gs[2 * kb2 + 1][0]);
-      Hx[c & 1][w][kb2][l] = Gb[kb2][0];  // this chunk's dSn, stored by the helpers
-    }
-    f32x4 dd[4][VB], pt[10];
+      for (int kb2 = 0; kb2 < 4; ++kb2) Gb[kb2] = pack_split<T>(Gs[2 * kb2], Gs[2 * kb2 + 1]);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb) dd[tb] = zero4();
+      const int nt = wu < 2 ? 3 : 2;
+      int prb[3], pcb[3];
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = zero4();
+      for (int t = 0; t < 3; ++t) {
+        const int x = (int)((pcode >> (16 * wu + 4 * t)) & 15);
+        prb[t] = x >> 2;
+        pcb[t] = x & 3;
+      }
+      f32x4 pacc[3] = {zero4(), zero4(), zero4()};
 #pragma unroll
-    for (int x = 0; x < 10; ++x) pt[x] = zero4();
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        x8 fk[4], fq[3];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 4; ++kb2) {
-      x8 fk[4], fq[4];
+        for (int tb = 0; tb < 4; ++tb) fk[tb] = frag_row_split(Ks[b] + 16 * tb * LD + 32 * kb2, LD);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) fk[tb] = frag_row_split(Ks + 16 * tb * LD + 32 * kb2, LD);
-      if (!isT) {
+        for (int t = 0; t < 3; ++t)
+          if (t < nt) fq[t] = frag_row_split(Qs[b] + 16 * prb[t] * LD + 32 * kb2, LD);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) fq[tb] = frag_row_split(Qs + 16 * tb * LD + 32 * kb2, LD);
+        for (int tb = 0; tb < 4; ++tb) dd[tb] = mfma16(fk[tb], Gb[kb2], dd[tb]);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          if (t < nt) {
+            // the K fragment of column block pcb[t] (wave-uniform) is one of fk
+            const int cb = pcb[t];
+            const x8 kf = cb == 0 ? fk[0] : cb == 1 ? fk[1] : cb == 2 ? fk[2] : fk[3];
+            pacc[t] = mfma16(fq[t], kf, pacc[t]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int vb = 0; vb < VB; ++vb) dd[tb][vb] = mfma16(fk[tb], Gb[kb2][vb], dd[tb][vb]);
-      if (!isT) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-          for (int ib = 0; ib <= rb; ++ib) pt[tri_idx(ib, rb)] = mfma16(fq[rb], fk[ib], pt[tri_idx(ib, rb)]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO.  Two stacked D tiles
-    // of P (rows r) form the A operand of P^T with k = r.
-    if (!isT) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * rb + 4 * grp);
-#pragma unroll
-        for (int ib = 0; ib <= rb; ++ib) {
-          const float gi = gam[16 * ib + col];
+      for (int t = 0; t < 3; ++t) {
+        if (t < nt) {
+          const int rb = prb[t], cb = pcb[t];
+          const f32x4 gr = *reinterpret_cast<const f32x4*>(gam[b] + 16 * rb + 4 * grp);
+          const float gi = gam[b][16 * cb + col];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            // masked entries take exp(-inf) = 0 (unconditional exponential)
-            const bool keep = (ib < rb) || (col <= 4 * grp + e);
-            pt[tri_idx(ib, rb)][e] *= __expf(keep ? gr[e] - gi : -INFINITY);
+            const int r = 16 * rb + 4 * grp + e, i = 16 * cb + col;
+            // masked entries take exp(-inf) = 0 (an unconditional exponential)
+            const float pv = pacc[t][e] * __expf((rb != cb || i <= r) ? gr[e] - gi : -INFINITY);
+            Ps[r * LDA + i] = from_f<T>(pv);
           }
         }
       }
     }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      x8 pa[2];
-#pragma unroll
-      for (int kt = tb / 2; kt < 2; ++kt)
-        pa[kt] = pack_split<T>((2 * kt >= tb) ? pt[tri_idx(tb, 2 * kt < 4 ? 2 * kt : 3)] : zero4(),
-                               pt[tri_idx(tb, 2 * kt + 1)]);
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        f32x4 acc = zero4();
-        if (!isT) {
-#pragma unroll
-          for (int kt = tb / 2; kt < 2; ++kt)
-            acc = mfma16(pa[kt], frag_tr_split(Ds + 32 * kt * LDV + cw0 + 16 * vb, LDV), acc);
-        }
-        const f32x4 dlr = *reinterpret_cast<const f32x4*>(dl + 16 * tb + 4 * grp);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dd[tb][vb][e] = dlr[e] * dd[tb][vb][e] + a.scale * acc[e];
+    __syncthreads();  // P, dO and A of chunk c and chunk c-1's slot are in LDS; Hx is free
+    if (helper) {
+      if (c - 1 >= sr.c0) {
+        load_da(c - 1);
+        if (c - 2 >= sr.c0) load_qk(c - 2);
       }
+      continue;
     }
-    // Z = -diag(beta e^gamma) A^T dDelta
-    f32x4 zz[4][VB];
+    // chunk c's dSn for the helpers (packed again rather than kept live
+    // across the barrier)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) Hx[w][kb2][l] = pack_split<T>(Gs[2 * kb2], Gs[2 * kb2 + 1]);
+    const float eL = __expf(gam[b][63]);
+
+    // The products below run in rounds of independent accumulators whose
+    // LDS fragments are issued before the round multiplies; the scheduling
+    // fences keep the compiler from sinking every read to its product, which
+    // would put one LDS latency per MFMA on the chain.
+    // Fragment (tb, kt) of P^T or A^T (k = rows 32 kt ..) for kt >= tb / 2.
+    auto tk = [](int tb, int kt) { return tb < 2 ? 2 * tb + kt : 2 + tb; };
+    x8 fdo[2], fp[6], fa[6], fr[8];
+    f32x4 dlv[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) fdo[kt] = frag_tr_split(Ds + 32 * kt * LDV + cw0, LDV);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        f32x4 acc = zero4();
+      for (int kt = tb / 2; kt < 2; ++kt)
+        fp[tk(tb, kt)] = frag_tr_split(Ps + 32 * kt * LDA + 16 * tb, LDA);
 #pragma unroll
-        for (int kt = tb / 2; kt < 2; ++kt)
-          acc = mfma16(frag_tr_split(As + 32 * kt * LDA + 16 * tb, LDA),
-                       pack_split<T>(dd[2 * kt][vb], dd[2 * kt + 1][vb]), acc);
-        const f32x4 bx = *reinterpret_cast<const f32x4*>(bex + 16 * tb + 4 * grp);
+    for (int tb = 0; tb < 4; ++tb) dlv[tb] = *reinterpret_cast<const f32x4*>(dl[b] + 16 * tb + 4 * grp);
+    __builtin_amdgcn_sched_barrier(0);
+    // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
+    f32x4 pd[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] *= -bx[e];
-        zz[tb][vb] = acc;
-      }
-    // dS = e^{gL} dSn + K^T Z + Q^T (scale diag(e^gamma) dO)
-    x8 Zb[2][VB], Ob[2][VB];
+    for (int tb = 0; tb < 4; ++tb) pd[tb] = zero4();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        Zb[kt][vb] = pack_split<T>(zz[2 * kt][vb], zz[2 * kt + 1][vb]);
-        if (!isT) {
-          x8 f = frag_tr_split(Ds + 32 * kt * LDV + cw0 + 16 * vb, LDV);
+      for (int tb = 0; tb < 4; ++tb)
+        if (kt >= tb / 2) pd[tb] = mfma16(fp[tk(tb, kt)], fdo[kt], pd[tb]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 32 * kt + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-            f[e] = from_f<T>(to_f(f[e]) * eg[r]);
-          }
-          Ob[kt][vb] = f;
-        }
-      }
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      x8 fk[2], fq[2];
+      for (int kt = tb / 2; kt < 2; ++kt)
+        fa[tk(tb, kt)] = frag_tr_split(As + 32 * kt * LDA + 16 * tb, LDA);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        fk[kt] = frag_tr_split(Ks + 32 * kt * LD + 16 * kb, LD);
-        if (!isT) fq[kt] = frag_tr_split(Qs + 32 * kt * LD + 16 * kb, LD);
-      }
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        f32x4 acc = Gs[kb][vb] * eL;
+      for (int e = 0; e < 4; ++e) dd[tb][e] = dlv[tb][e] * dd[tb][e] + a.scale * pd[tb][e];
+    const x8 Db[2] = {pack_split<T>(dd[0], dd[1]), pack_split<T>(dd[2], dd[3])};
+    __builtin_amdgcn_sched_barrier(0);
+    x8 Ob[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          acc = mfma16(fk[kt], Zb[kt][vb], acc);
-          if (!isT) acc = mfma16(fq[kt], Ob[kt][vb], acc);
-        }
-        Gs[kb][vb] = acc;
-      }
+    for (int kt = 0; kt < 2; ++kt) Ob[kt] = frag_tr_split(Es + 32 * kt * LDV + cw0, LDV);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split(Qs[b] + 16 * kb, LD);
+    __builtin_amdgcn_sched_barrier(0);
+    // Z = -diag(beta e^gamma) A^T dDelta
+    f32x4 zz[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) zz[tb] = zero4();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        if (kt >= tb / 2) zz[tb] = mfma16(fa[tk(tb, kt)], Db[kt], zz[tb]);
+    // dS = e^{gL} dSn + Q^T (scale diag(e^gamma) dO) + K^T Z
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[0], Gs[kb] * eL);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split(Qs[b] + 32 * LD + 16 * kb, LD);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const f32x4 bx = *reinterpret_cast<const f32x4*>(bex[b] + 16 * tb + 4 * grp);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zz[tb][e] *= -bx[e];
+    }
+    const x8 Zb[2] = {pack_split<T>(zz[0], zz[1]), pack_split<T>(zz[2], zz[3])};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[1], Gs[kb]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split(Ks[b] + 32 * kt * LD + 16 * kb, LD);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Zb[kt], Gs[kb]);
     }
   }
 
@@ -627,25 +672,14 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
     if (sr.c0 < sr.c1) store_dh(sr.c0);
     return;
   }
-  if (MODE == MODE_AUG) {
-    float* so = a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
+  if (p == 0 && a.dh0) {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          so[(16 * kb + 4 * grp + e) * (2 * kDim) + cb0 + cw0 + 16 * vb + col] = Gs[kb][vb][e];
-  } else if (p == 0 && a.dh0) {
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = 16 * kb + 4 * grp + e, vc = vcol0 + cw0 + 16 * vb + col;
-          a.dh0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = Gs[kb][vb][e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
+        a.dh0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = Gs[kb][e];
+      }
   }
 }
 
