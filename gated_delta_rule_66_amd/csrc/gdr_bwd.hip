@@ -907,6 +907,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     acc1[x] = zero4();
     acc2[x] = zero4();
   }
+  // unrolled: a shared body would give half 1's prefetched tiles the
+  // registers of half 0's products, so half 0 would wait for the prefetch
+  // to land and copy it aside first
+#pragma unroll
   for (int hv = 0; hv < 2; ++hv) {
     const int v0 = 64 * hv;
     if (hv > 0) {
