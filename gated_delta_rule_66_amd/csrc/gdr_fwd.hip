@@ -85,24 +85,39 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   const int G = a.Hv / a.Hq, hq = h / G;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
 
-  // the k tile's loads are issued first; the gate loads and scan overlap them
+  // The row's g and beta are loaded as raw bits from a clamped row by every
+  // wave, with no branch around the loads (a load inside a branch ends with
+  // a wait for every load issued before it): two 16-bit loads give the bits
+  // of an fp32 g, or a 16-bit g in the low half (the other half is unused,
+  // or past the range and zero).  The k tile follows; g and beta are
+  // converted after the tile is stored.
+  const int gsz = a.g_dtype == 2 ? 4 : 2;
+  const int ld_g = a.Hv * gsz, rr = min(l, Cc - 1);
+  const __amdgpu_buffer_rsrc_t grs =
+      buf_rsrc(reinterpret_cast<const char*>(a.g) + (t0 * a.Hv + h) * (int64_t)gsz, (int64_t)Cc * ld_g);
+  const __amdgpu_buffer_rsrc_t brs =
+      buf_rsrc(reinterpret_cast<const T*>(a.beta) + (t0 * a.Hv + h), (int64_t)Cc * a.Hv * (int64_t)sizeof(T));
+  const uint32_t glo = __builtin_amdgcn_raw_buffer_load_b16(grs, rr * ld_g, 0, 0);
+  const uint32_t ghi = __builtin_amdgcn_raw_buffer_load_b16(grs, rr * ld_g + 2, 0, 0);
+  const uint16_t braw = __builtin_amdgcn_raw_buffer_load_b16(brs, rr * a.Hv * (int)sizeof(T), 0, 0);
   TileRegs<128, 256> rk;
   tile_load<T, 128, 256>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
                          (int64_t)a.Hq * kDim, Cc);
+  if (a.qk_norm) l2norm_rows<T, 256>(rk, nullptr);
+  tile_store<T, 128, 256>(Ks, LDK, rk);
   if (w == 0) {
-    float gv = (l < Cc) ? load_scalar(a.g, (t0 + l) * a.Hv + h, a.g_dtype) : 0.f;
-    if (a.gate_A_log && l < Cc)
+    float gv = a.g_dtype == 2 ? __builtin_bit_cast(float, glo | (ghi << 16))
+               : a.g_dtype == 0 ? __builtin_bit_cast(float, glo << 16)
+                                : (float)__builtin_bit_cast(_Float16, (uint16_t)glo);
+    if (a.gate_A_log)
       gv = gate_log_decay(gv, a.gate_A_log[h], a.gate_dt_bias ? a.gate_dt_bias[h] : 0.f);
-    const float bv =
-        (l < Cc) ? beta_used(to_f(reinterpret_cast<const T*>(a.beta)[(t0 + l) * a.Hv + h]), a.beta_mode)
-                 : 0.f;
+    if (l >= Cc) gv = 0.f;
+    const float bv = (l < Cc) ? beta_used(to_f(__builtin_bit_cast(T, braw)), a.beta_mode) : 0.f;
     const float gc = wave_inclusive_scan(gv);
     gam[l] = gc;
     bet[l] = bv;
     if (l < Cc) a.gcum[(t0 + l) * a.Hv + h] = gc;
   }
-  if (a.qk_norm) l2norm_rows<T, 256>(rk, nullptr);
-  tile_store<T, 128, 256>(Ks, LDK, rk);
   __syncthreads();
 
   // M, rows 16w .. 16w+15 (only the blocks on or below the diagonal are nonzero)
