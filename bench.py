@@ -166,8 +166,9 @@ def cpu_baseline(d, prob, nthreads_cap=16, max_units=32, qk_norm=False, gate=Fal
     return {"value": round(tokens * frac / dt / 1e6, 6), "unit": "Mtokens/s", "cores": threads,
             "kind": "oracle",
             "sample": "fp64 token recurrence fwd+bwd on %s, value heads 0..%d (%d of %d "
-                      "(sequence, head) units); %.1f s wall on %d threads; value scaled to the "
-                      "whole workload" % (where, nh - 1, units, total_units, dt, threads)}
+                      "(sequence, head) units); %.1f s wall on %d threads (about %.0f "
+                      "thread-seconds); value scaled to the whole workload"
+                      % (where, nh - 1, units, total_units, dt, threads, dt * threads)}
 
 
 def main():
@@ -190,7 +191,7 @@ def main():
                          "(use_gate_in_kernel: -exp(A_log) softplus(g + dt_bias))")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the path runs on a single MI355X and this build "
+        print("bench.py measures one GPU: the path runs on a single MI355X and the library "
               "has no multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
