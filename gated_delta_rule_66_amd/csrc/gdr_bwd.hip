@@ -769,6 +769,9 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   __shared__ float dbf[64];          // d beta / d (beta input) per row
   __shared__ float xinv[2][64];      // 1 / |q|, 1 / |k| per row (q / k normalisation)
   __shared__ float gsl[2][64];       // the gate's slope and log decay per row (gate on)
+  // side 1's row terms of the last step (rowacc, k . dX, F, dbeta part), in
+  // the P tile's storage (dead once the value halves are done)
+  float* const rowv = reinterpret_cast<float*>(Ps);
 
   const int c = blockIdx.x, h = blockIdx.y;
   int n, j;
@@ -865,7 +868,6 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     }
   }
   __syncthreads();
-  const float gL = gam[63];
 
   // rows 16 wr .. 16 wr + 15 of P = lower_incl(Q K^T o Gamma) (side 0, also
   // written to Ps) or N = strict_lower(K K^T o Gamma) (side 1), fp32
@@ -1219,7 +1221,18 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       rs2[e] = (r < Cc) ? rs2[e] * dl[r] : 0.f;  // F_r
       Fsum_part += rs2[e];
     }
-    if (col == 0) fsum[wr][grp] = Fsum_part;
+    if (col == 0) {
+      fsum[wr][grp] = Fsum_part;
+      // the row terms of this side for the dgamma / dbeta rows below
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wr + 4 * grp + e;
+        rowv[r] = rowacc[e];
+        rowv[64 + r] = rs1[e];
+        rowv[128 + r] = rs2[e];
+        rowv[192 + r] = dbacc[e];
+      }
+    }
   }
   // dq (side 0) / dk (side 1) rows: fp32 partials straight from registers, or
   // staged row-major in the free S / dSn tiles for 16-byte stores
@@ -1242,23 +1255,21 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       for (int e = 0; e < 4; ++e)
         stage[(16 * wr + 4 * grp + e) * LD + 16 * kb + col] = from_f<T>(dxv[kb][e]);
   }
-  if (hi && col == 0) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * wr + 4 * grp + e;
-      float dgv = rowq[r] + rowacc[e] + bex[r] * rs1[e] - rs2[e];
-      if (r == Cc - 1) {
-        float Fs = 0.f;
-        for (int ww = 0; ww < 4; ++ww)
-          for (int gg = 0; gg < 4; ++gg) Fs += fsum[ww][gg];
-        const float ss = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
-        dgv += Fs + __expf(gL) * ss;
-      }
-      dgam[r] += dgv;
-      const float db = dbv[0][r] + dbv[1][r] + dbv[2][r] + dbv[3][r] + dbv[4][r] + dbv[5][r] +
-                       dbv[6][r] + dbv[7][r] + eg[r] * rs1[e] + dbacc[e];
-      if (r < Cc) reinterpret_cast<T*>(a.dbeta)[(t0 + r) * a.Hv + h] = from_f<T>(db * dbf[r]);
-    }
+  // dgamma and dbeta rows, row l on lane l of wave 4: every read of a row
+  // issues at once (four rows per lane on a quarter of the lanes would chain
+  // their LDS round trips)
+  if (w == 4) {
+    const int r = l;
+    float Fs = 0.f;
+    for (int ww = 0; ww < 4; ++ww)
+      for (int gg = 0; gg < 4; ++gg) Fs += fsum[ww][gg];
+    const float ss = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+    float dgv = rowq[r] + rowv[r] + bex[r] * rowv[64 + r] - rowv[128 + r];
+    if (r == Cc - 1) dgv += Fs + __expf(gam[63]) * ss;
+    dgam[r] += dgv;
+    const float db = dbv[0][r] + dbv[1][r] + dbv[2][r] + dbv[3][r] + dbv[4][r] + dbv[5][r] +
+                     dbv[6][r] + dbv[7][r] + eg[r] * rowv[64 + r] + rowv[192 + r];
+    if (r < Cc) reinterpret_cast<T*>(a.dbeta)[(t0 + r) * a.Hv + h] = from_f<T>(db * dbf[r]);
   }
   __syncthreads();
   if (!a.partial) {
