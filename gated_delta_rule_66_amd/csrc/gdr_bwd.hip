@@ -1014,16 +1014,37 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
             accB[ib] = mfma16(fdo, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), accB[ib]);
           }
         }
+        // two rounds of four key blocks, fragments read before the products
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-          acc1[kb] = mfma16(fdo, frag_tr_split_q(Ss, 32 * vk, 16 * kb), acc1[kb]);
+        for (int kh = 0; kh < 2; ++kh) {
+          x8 fs4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fs4[i] = frag_tr_split_q(Ss, 32 * vk, 16 * (4 * kh + i));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc1[4 * kh + i] = mfma16(fdo, fs4[i], acc1[4 * kh + i]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       } else {
         const x8 fdr = frag_tr_split(DRs + 32 * vk * L7 + 16 * wr, L7);
         const x8 fdl = frag_tr_split(Dls + 32 * vk * L7 + 16 * wr, L7);
+        // four rounds of two key blocks, each round's fragments read before
+        // its four independent products issue
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-          acc1[kb] = mfma16(fdr, frag_tr_split_q(Ss, 32 * vk, 16 * kb), acc1[kb]);
-          acc2[kb] = mfma16(fdl, frag_tr_split_q(Gs_, 32 * vk, 16 * kb), acc2[kb]);
+        for (int kh = 0; kh < 4; ++kh) {
+          x8 fs2[2], fg2[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            fs2[i] = frag_tr_split_q(Ss, 32 * vk, 16 * (2 * kh + i));
+            fg2[i] = frag_tr_split_q(Gs_, 32 * vk, 16 * (2 * kh + i));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            acc1[2 * kh + i] = mfma16(fdr, fs2[i], acc1[2 * kh + i]);
+            acc2[2 * kh + i] = mfma16(fdl, fg2[i], acc2[2 * kh + i]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
