@@ -48,6 +48,10 @@ CASES = {
     "dense_state_dht": P("dense", B=2, T=200, Hq=2, Hv=2, init_state=True, dht=True),
     "no_state": P("nostate", B=1, T=130, Hq=2, Hv=2),
     "fp16_gva": P("fp16_gva", B=1, T=333, Hq=1, Hv=2, dtype="fp16", init_state=True, dht=True),
+    # groups of three and four value heads per q/k head (odd group size; two
+    # q/k heads of four value heads each)
+    "gva_group3": P("gva3", B=2, T=150, Hq=1, Hv=3, init_state=True, dht=True),
+    "gva_group4": P("gva4", B=1, T=200, Hq=2, Hv=8, init_state=True, dht=True),
     "varlen": P("varlen", B=1, T=0, Hq=2, Hv=2, init_state=True, dht=True,
                 lens=[70, 1, 64, 129, 250]),
     "varlen_empty_seq": P("varlen_empty", B=1, T=0, Hq=1, Hv=1, init_state=True, dht=True,
