@@ -346,10 +346,11 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
 // waves 4-7 issue every chunk load and tile store.  The q / k tiles and the
 // per-row values of two chunks are kept (slot = chunk & 1).  In the
 // iteration of chunk c, before the middle barrier, the helpers store chunk
-// c's dO and A tiles, chunk c-1's q / k slot and chunk c+1's dSn, while the
-// chain waves form K dSn and, each a quarter of its tiles, P of chunk c;
-// after it the chain finishes chunk c and the helpers issue the loads of the
-// next chunks.
+// c's dO and A tiles (dO also scaled by scale e^gamma, the operand of Q^T),
+// chunk c-1's q / k slot and chunk c+1's dSn, while the chain waves form
+// K dSn and, each a quarter of its tiles, P of chunk c; after it the chain
+// finishes chunk c in rounds of independent products and the helpers issue
+// the loads of the next chunks.
 template <typename T, int OPT>
 __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
   typedef typename VT<T>::x8 x8;
