@@ -118,6 +118,22 @@ def measured_traffic(kernel, workload, launches_bytes):
     return (k["fetch_kib"] * t["fetch_factor"] + k["write_kib"] * t["write_factor"]) * 1024.0
 
 
+def measured_mfma(kernel, workload):
+    """The kernel's MFMA-busy fraction from the committed rocprofv3 counter
+    summary (SQ_VALU_MFMA_BUSY_CYCLES over the active cycles of all SIMDs),
+    or None when absent or taken from different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest() or t.get("workload") != workload:
+        return None
+    k = t.get("mfma", {}).get(kernel)
+    return None if not k else k.get("busy_frac")
+
+
 def cpu_baseline(d, prob, nthreads_cap=16, max_units=32, qk_norm=False, gate=False):
     """The fp64 oracle, as it stands, on a bounded sample of the workload."""
     import numpy as np
@@ -300,7 +316,9 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom, args.workload + ("+qk_l2norm" if qkn else "")
                                             + ("+gate" if args.gate else ""), nbytes),
-                "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2)}
+                "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2),
+                "mfma_busy_frac": measured_mfma(dom, args.workload + ("+qk_l2norm" if qkn else "")
+                                                + ("+gate" if args.gate else ""))}
 
     out = {
         "metric": "GDN chunk fwd+bwd Mtokens/s at H=32,K=V=128 bf16 (and % of bf16 MFMA peak)",
