@@ -1066,10 +1066,13 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   float dbacc[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta row terms (side 1)
   if (!hi) {
     const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * wr + 4 * grp);
+    float gis[4];  // gamma of each column block's column, read at once
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) gis[cb] = gam[16 * cb + col];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       float cs = 0.f;
-      const float gi = gam[16 * cb + col];
+      const float gi = gis[cb];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * wr + 4 * grp + e, i = 16 * cb + col;
@@ -1125,6 +1128,9 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   if (hi) {
     const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * wr + 4 * grp);
     const f32x4 br = *reinterpret_cast<const f32x4*>(bet + 16 * wr + 4 * grp);
+    float gis[4];  // gamma of each column block's column, read at once
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) gis[ib] = gam[16 * ib + col];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
       f32x4 acc = zero4();
@@ -1133,7 +1139,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
         acc = mfma16(frag_row_split(T1s + 16 * wr * L7 + 32 * mk, L7),
                      frag_row_split(As + 16 * ib * L7 + 32 * mk, L7), acc);
       float cs = 0.f;
-      const float gi = gam[16 * ib + col];
+      const float gi = gis[ib];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * wr + 4 * grp + e, i = 16 * ib + col;
