@@ -888,7 +888,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * wr + 4 * grp + e, i = 16 * cb + col;
       const bool keep = hi ? (i < r) : (i <= r);
-      pn[cb][e] = acc[e] * __expf(keep ? gr[e] - gi : -INFINITY);
+      // masked by a select, not a zero factor: for cb > wr, acc is defined
+      // only if the compiler branches around the products above (an MFMA
+      // does not honour the EXEC mask)
+      pn[cb][e] = keep ? acc[e] * __expf(gr[e] - gi) : 0.f;
       if (!hi) Ps[r * L7 + i] = from_f<T>(pn[cb][e]);
     }
   }
