@@ -50,6 +50,9 @@ class _Call:
     def __init__(self, q, v, g_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first,
                  cp_segments, wave_tiles=0, use_qk_l2norm=False, beta_sigmoid=False,
                  neg_eigval=False, gate=None):
+        if q.dim() != 4 or v.dim() != 4:
+            raise GdrError(2, "q and v must be 4-D ([B, T, H, dim]), got %s and %s"
+                           % (tuple(q.shape), tuple(v.shape)))
         B, T, Hq, K = q.shape
         Hv, V = v.shape[2], v.shape[3]
         # gate = (A_log, dt_bias or None): fp32 [Hv] device copies the problem points to
@@ -69,6 +72,8 @@ class _Call:
         if cu_seqlens is not None:
             self.cu_dev = cu_seqlens.to(device=q.device, dtype=torch.int32).contiguous()
             if cu_seqlens_cpu is None:
+                # launch planning needs the lengths on the host: one blocking
+                # device-to-host copy (pass cu_seqlens_cpu to avoid it)
                 cu_seqlens_cpu = cu_seqlens.detach().to("cpu")
             self.cu_host = cu_seqlens_cpu.to(torch.int32).contiguous()
             N = self.cu_host.numel() - 1
@@ -110,6 +115,45 @@ def _contig(*ts):
     return [None if t is None else t.contiguous() for t in ts]
 
 
+def _expect(name, t, shape, dtypes, device):
+    """Rejects a tensor whose shape, dtype or device does not match what the
+    kernels read through its pointer (None passes: optional arguments)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise GdrError(2, "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if dtypes is not None and t.dtype not in dtypes:
+        raise GdrError(4, "%s must be %s, got %s"
+                       % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if t.device != device:
+        raise GdrError(8, "%s is on %s but q is on %s" % (name, t.device, device))
+
+
+_FLOATS = (torch.float32, torch.bfloat16, torch.float16)
+
+
+def _check_inputs(c, q, k, v, g, beta, state_v_first, initial_state=None, A=None, do=None,
+                  dht=None, g_cum=None, g_input=None):
+    """Every tensor the C call receives as a raw pointer against the problem
+    the descriptor states: token tensors [B, T, heads, ..] in q's dtype,
+    g_cum fp32, states [N, Hv, K, V] (or [N, Hv, V, K]) with one row per
+    sequence, all on q's device."""
+    B, T, Hq, K = q.shape
+    dev, dt = q.device, (q.dtype,)
+    Hv, V = c.Hv, c.V
+    _expect("k", k, (B, T, Hq, K), dt, dev)
+    _expect("v", v, (B, T, Hv, V), dt, dev)
+    _expect("g", g, (B, T, Hv), (q.dtype, torch.float32), dev)
+    _expect("beta", beta, (B, T, Hv), dt, dev)
+    _expect("A", A, (B, T, Hv, CHUNK), dt, dev)
+    _expect("do", do, (B, T, Hv, V), dt, dev)
+    _expect("g_cum", g_cum, (B, T, Hv), (torch.float32,), dev)
+    _expect("g_input", g_input, (B, T, Hv), (q.dtype, torch.float32), dev)
+    st = c.state_shape(state_v_first)
+    _expect("initial_state", initial_state, st, _FLOATS, dev)
+    _expect("dht", dht, st, _FLOATS, dev)
+
+
 def _workspace(nbytes, dev, workspace):
     """The caller's workspace (a device uint8 tensor of at least nbytes), or a
     new one."""
@@ -147,6 +191,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
               wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
               (A_log, dt_bias) if use_gate_in_kernel else None)
+    _check_inputs(c, q, k, v, g, beta, state_v_first, initial_state=initial_state)
     dev = q.device
     B, T = q.shape[0], q.shape[1]
     g_cum = torch.empty(B, T, c.Hv, dtype=torch.float32, device=dev)
@@ -199,6 +244,8 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     c = _Call(q, v, dg_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
               wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
               (A_log, dt_bias) if use_gate_in_kernel else None)
+    _check_inputs(c, q, k, v, None, beta, state_v_first, initial_state=initial_state, A=A,
+                  do=do, dht=dht, g_cum=g, g_input=g_input)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -233,6 +280,9 @@ class _GatedDeltaRule(torch.autograd.Function):
     def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
                 state_v_first, cp_segments, cu_seqlens_cpu, use_qk_l2norm, beta_sigmoid,
                 neg_eigval, use_gate, A_log, dt_bias):
+        if cu_seqlens is not None and cu_seqlens_cpu is None:
+            # the one device-to-host copy of the lengths, shared by the backward
+            cu_seqlens_cpu = cu_seqlens.detach().to("cpu")
         g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
             q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
             state_v_first, False, cp_segments, cu_seqlens_cpu,
@@ -309,6 +359,7 @@ def fused_recurrent_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, 1, 0,
               use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
               (A_log, dt_bias) if use_gate_in_kernel else None)
+    _check_inputs(c, q, k, v, g, beta, state_v_first, initial_state=initial_state)
     dev = q.device
     B, T = q.shape[0], q.shape[1]
     o = torch.empty(B, T, c.Hv, c.V, dtype=q.dtype, device=dev)

@@ -1471,7 +1471,7 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t
     const unsigned n1 = units * pl.cp * s1.nvs;
     GDR_LAUNCH("bwd_scan_aug", (bwd_scans_kernel<T, VB, MODE_AUG, MODE_AUG>), dim3(2 * n1),
                dim3(256), st, s1, d1, (int)n1);
-    GDR_LAUNCH("cp_combine", cp_combine_kernel, dim3(units * 8), dim3(256), st, s1);
+    GDR_LAUNCH("cp_combine_bwd", cp_combine_kernel, dim3(units * 8), dim3(256), st, s1);
     ScanArgs r;
     memset(&r, 0, sizeof(r));
     r.cu = da.cu;
@@ -1481,7 +1481,7 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t
     r.seg_out = da.seg_out;
     r.seg_start = da.seg_start;
     r.reverse = 1;
-    GDR_LAUNCH("cp_combine", cp_combine_kernel, dim3(units * 8), dim3(256), st, r);
+    GDR_LAUNCH("cp_combine_bwd", cp_combine_kernel, dim3(units * 8), dim3(256), st, r);
   }
   sa.P = da.P = pl.cp;
   sa.nvs = da.nvs = 2 / VB;

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   constexpr int LDM = 68;
   static_assert(64 * LDK * sizeof(T) == 64 * LDM * sizeof(float), "Ks and Ai share storage");
   // the k tile is dead once M is formed (a barrier follows), so the inverse
-  // reuses its storage: 35 KB per workgroup, four workgroups per CU
+  // reuses its storage (17 KB for both)
   __shared__ __align__(16) float KsAi[64 * LDM];
   T* const Ks = reinterpret_cast<T*>(KsAi);
   float* const Ai = KsAi;
@@ -224,7 +224,7 @@ static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st)
     a1.nvs = 4 / VB;
     GDR_LAUNCH("scan_aug", (scan_kernel<T, VB, MODE_AUG>), dim3(units * pl.cp * a1.nvs), dim3(256),
                st, a1);
-    GDR_LAUNCH("cp_combine", cp_combine_kernel, dim3(units * 8), dim3(256), st, a1);
+    GDR_LAUNCH("cp_combine_fwd", cp_combine_kernel, dim3(units * 8), dim3(256), st, a1);
   }
   a.P = pl.cp;
   a.nvs = 2 / VB;

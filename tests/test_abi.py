@@ -215,3 +215,70 @@ def test_python_rejects_verifier_options():
     # the gate is supported, but needs its decay parameters
     with pytest.raises(gdr.GdrError):
         gdr.chunk_gated_delta_rule(x, x, x, g, g, use_gate_in_kernel=True)
+
+
+def _inputs(B=1, T=100, Hq=2, Hv=4, dt=torch.bfloat16):
+    q = torch.zeros(B, T, Hq, 128, dtype=dt)
+    return dict(q=q, k=q.clone(), v=torch.zeros(B, T, Hv, 128, dtype=dt),
+                g=torch.zeros(B, T, Hv, dtype=dt), beta=torch.zeros(B, T, Hv, dtype=dt))
+
+
+BINDING_REJECT = [
+    # (name, fwd or bwd, override, error name, message part)
+    ("short k", "fwd", dict(k=torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16)), "GDR_ERR_SHAPE",
+     "k must have shape"),
+    ("fp16 k", "fwd", dict(k=torch.zeros(1, 100, 2, 128, dtype=torch.float16)), "GDR_ERR_DTYPE",
+     "k must be"),
+    ("fp32 beta", "fwd", dict(beta=torch.zeros(1, 100, 4)), "GDR_ERR_DTYPE", "beta must be"),
+    ("beta per q head", "fwd", dict(beta=torch.zeros(1, 100, 2, dtype=torch.bfloat16)),
+     "GDR_ERR_SHAPE", "beta must have shape"),
+    ("v of another length", "fwd", dict(v=torch.zeros(1, 99, 4, 128, dtype=torch.bfloat16)),
+     "GDR_ERR_SHAPE", "v must have shape"),
+    ("one-row h0 for two sequences", "fwd",
+     dict(initial_state=torch.zeros(1, 4, 128, 128), cu_seqlens=torch.tensor([0, 40, 100])),
+     "GDR_ERR_SHAPE", "initial_state must have shape"),
+    ("transposed h0 without state_v_first", "fwd",
+     dict(initial_state=torch.zeros(1, 4, 128, 64)), "GDR_ERR_SHAPE", "initial_state"),
+    ("A with 32 columns", "bwd", dict(A=torch.zeros(1, 100, 4, 32, dtype=torch.bfloat16)),
+     "GDR_ERR_SHAPE", "A must have shape"),
+    ("bf16 g_cum", "bwd", dict(g=torch.zeros(1, 100, 4, dtype=torch.bfloat16)),
+     "GDR_ERR_DTYPE", "fp32 g_cum"),
+    ("do per q head", "bwd", dict(do=torch.zeros(1, 100, 2, 128, dtype=torch.bfloat16)),
+     "GDR_ERR_SHAPE", "do must have shape"),
+    ("dht with three rows", "bwd", dict(dht=torch.zeros(3, 4, 128, 128)), "GDR_ERR_SHAPE",
+     "dht must have shape"),
+]
+
+
+@pytest.mark.parametrize("name,which,over,status,msg", BINDING_REJECT,
+                         ids=[r[0] for r in BINDING_REJECT])
+def test_binding_checks_every_tensor_before_the_call(name, which, over, status, msg):
+    """A tensor whose shape, dtype or device disagrees with the problem would
+    be read out of bounds (or reinterpreted) by the kernels through its raw
+    pointer: the binding rejects it on the host first."""
+    import gated_delta_rule_66_amd as gdr
+    x = _inputs()
+    if which == "fwd":
+        x.update(over)
+        with pytest.raises(gdr.GdrError) as e:
+            gdr.chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                           initial_state=x.get("initial_state"),
+                                           cu_seqlens=x.get("cu_seqlens"))
+    else:
+        b = dict(g=torch.zeros(1, 100, 4), A=torch.zeros(1, 100, 4, 64, dtype=torch.bfloat16),
+                 do=torch.zeros(1, 100, 4, 128, dtype=torch.bfloat16), dht=None)
+        b.update(over)
+        with pytest.raises(gdr.GdrError) as e:
+            gdr.chunk_gated_delta_rule_bwd(x["q"], x["k"], x["v"], b["g"], x["beta"], b["A"],
+                                           b["do"], dht=b["dht"])
+    assert e.value.name == status
+    assert msg in str(e.value)
+
+
+def test_binding_rejects_a_tensor_on_another_device():
+    import gated_delta_rule_66_amd as gdr
+    x = _inputs()
+    meta_v = torch.empty(1, 100, 4, 128, dtype=torch.bfloat16, device="meta")
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.chunk_gated_delta_rule_fwd(x["q"], x["k"], meta_v, x["g"], x["beta"])
+    assert e.value.name == "GDR_ERR_DEVICE"

@@ -82,3 +82,40 @@ def test_cpu_baseline_record():
     assert out["value"] > 0
     assert 1 <= out["cores"] <= 2
     assert "thread-seconds" in out["sample"]
+
+
+def test_pass_minimum_bytes_per_token_and_head():
+    # 16-bit inputs: 1160 / 904 B forward and 1930 / 1418 B backward per
+    # (token, value head) at Hq = Hv and Hq = Hv / 2
+    assert bench.alg_bytes_per_unit("fwd", 1.0) == 1160
+    assert bench.alg_bytes_per_unit("fwd", 0.5) == 904
+    assert bench.alg_bytes_per_unit("bwd", 1.0) == 1930
+    assert bench.alg_bytes_per_unit("bwd", 0.5) == 1418
+    # an fp32 g adds two bytes on each side (g read forward, dg written backward)
+    assert bench.alg_bytes_per_unit("fwd", 1.0, gsz=4) == 1162
+    assert bench.alg_bytes_per_unit("bwd", 1.0, gsz=4) == 1932
+
+
+def test_pass_bytes_add_the_fp32_states():
+    # B=2 T=4096 H=32: 262144 (token, head) units and 64 (sequence, head) units
+    fwd = bench.pass_bytes("fwd", 8192, 32, 32, 2, n_states=2)
+    assert fwd == 262144 * 1160 + 64 * 2 * 65536
+    bwd = bench.pass_bytes("bwd", 8192, 32, 32, 2, n_states=3)
+    assert bwd == 262144 * 1930 + 64 * 3 * 65536
+
+
+def test_fractions_take_the_larger_bound():
+    # 8 GB in 2 ms is 0.5 of 8 TB/s; 1 TFLOP in 2 ms is 500 TFLOP/s, 0.199 of
+    # the bf16 MFMA peak
+    f = bench.fractions(2e-3, 1e12, 8e9)
+    assert f["hbm"] == 0.5 and f["bound"] == "hbm" and f["roofline"] == 0.5
+    assert abs(f["mfma"] - 500.0 / bench.MFMA_BF16_PEAK_TFLOPS) < 1e-4
+    g = bench.fractions(2e-3, 4e12, 1e9)
+    assert g["bound"] == "mfma" and g["roofline"] == g["mfma"]
+
+
+def test_every_library_kernel_has_a_direction():
+    for k in ("fwd_prep", "scan_out", "scan_aug", "cp_combine_fwd"):
+        assert bench.kernel_direction(k) == "fwd"
+    for k in ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "grad", "gva_reduce"):
+        assert bench.kernel_direction(k) == "bwd"

@@ -7,7 +7,7 @@ import torch
 
 import gdr_synth
 import oracle
-from _util import TOL, np64, ratio, to_dev
+from _util import TOL, check, np64, ratio, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -57,11 +57,11 @@ def test_beta_options_fwd_bwd(name, sig, neg):
     kw = dict(beta_sigmoid=sig, neg_eigval=neg)
     _, A_r, o_r, _, ht_r = oracle.chunked_fwd(*args, chunk=64, initial_state=np64(d["h0"]),
                                               cu_seqlens=cu, **kw)
-    res = {"o": ratio(np64(o), o_r), "final_state": ratio(np64(ht), ht_r), "A": ratio(np64(A), A_r)}
+    res = {"o": check("o", o, o_r, "tok", d["cu_seqlens"]), "final_state": check("final_state", ht, ht_r, "state"), "A": check("A", A, A_r, "tok", d["cu_seqlens"])}
     ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]),
                      cu_seqlens=cu, **kw)
     for nm, x, r in zip(NAMES, grads, ref):
-        res[nm] = ratio(np64(x), r)
+        res[nm] = check(nm, x, r, "state" if nm in ("dh0", "final_state") else "tok", d["cu_seqlens"])
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for k, v in res.items():
         assert v <= TOL, (k, v)
@@ -78,8 +78,8 @@ def test_beta_options_recurrent(sig, neg):
     torch.cuda.synchronize()
     o_r, ht_r = oracle.fwd(np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]),
                            d["scale"], initial_state=np64(d["h0"]), beta_sigmoid=sig, neg_eigval=neg)
-    assert ratio(np64(o), o_r) <= TOL
-    assert ratio(np64(ht), ht_r) <= TOL
+    check("o", o, o_r, "tok", d["cu_seqlens"])
+    check("final_state", ht, ht_r, "state")
 
 
 def test_autograd_passes_the_options():
@@ -98,4 +98,4 @@ def test_autograd_passes_the_options():
     ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), use_qk_l2norm=True,
                      beta_sigmoid=True, neg_eigval=True)
     for n, i in (("q", 0), ("k", 1), ("v", 2), ("beta", 3), ("g", 4)):
-        assert ratio(np64(leaves[n].grad), ref[i]) <= TOL, n
+        check(n, leaves[n].grad, ref[i], "tok", d["cu_seqlens"])

@@ -8,7 +8,7 @@ import torch
 
 import gdr_synth
 import oracle
-from _util import TOL, np64, ratio, to_dev
+from _util import TOL, check, np64, ratio, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -82,9 +82,9 @@ def test_degenerate_fwd_bwd(name):
     o_r, ht_r = oracle.fwd(*args, initial_state=np64(d["h0"]), cu_seqlens=cu)
     ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]),
                      cu_seqlens=cu)
-    res = {"o": ratio(np64(o), o_r), "final_state": ratio(np64(ht), ht_r)}
+    res = {"o": check("o", o, o_r, "tok", d["cu_seqlens"]), "final_state": check("final_state", ht, ht_r, "state")}
     for nm, x, r in zip(NAMES, grads, ref):
-        res[nm] = ratio(np64(x), r)
+        res[nm] = check(nm, x, r, "state" if nm in ("dh0", "final_state") else "tok", d["cu_seqlens"])
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for k, v in res.items():
         assert v <= TOL, (k, v)
@@ -104,6 +104,6 @@ def test_tiny_sequences_token_by_token():
     o_r, ht_r = oracle.fwd(np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]),
                            d["scale"], initial_state=np64(d["h0"]),
                            cu_seqlens=d["cu_seqlens"].numpy())
-    assert ratio(np64(o), o_r) <= TOL
-    assert ratio(np64(ht), ht_r) <= TOL
+    check("o", o, o_r, "tok", d["cu_seqlens"])
+    check("final_state", ht, ht_r, "state")
     assert torch.equal(ht[37].cpu(), d["h0"][37])  # the empty sequence keeps its state

@@ -8,7 +8,7 @@ import torch
 
 import gdr_synth
 import oracle
-from _util import TOL, ratio
+from _util import TOL, check, ratio
 
 pytestmark = pytest.mark.gpu
 
@@ -66,8 +66,8 @@ def run_full(i, heads, svf_check=False):
             f64(sel(d["beta"], vh)), d["scale"])
     h0s = f64(sel(d["h0"], vh, 1))
     o_ref, ht_ref = oracle.fwd(*args, initial_state=h0s, cu_seqlens=cu, nthreads=16)
-    res = {"o": ratio(f64(sel(o.cpu(), vh)), o_ref),
-           "final_state": ratio(f64(sel(ht.cpu(), vh, 1)), ht_ref)}
+    res = {"o": check("o", f64(sel(o.cpu(), vh)), o_ref, "tok", cu),
+           "final_state": check("final_state", f64(sel(ht.cpu(), vh, 1)), ht_ref, "state")}
     if prob.backward:
         g_ref = oracle.bwd(*args[:5], d["scale"], f64(sel(d["do"], vh)), initial_state=h0s,
                            dht=f64(sel(d["dht"], vh, 1)), cu_seqlens=cu, nthreads=16)
@@ -75,10 +75,8 @@ def run_full(i, heads, svf_check=False):
                sel(grads[3].cpu(), vh), sel(grads[4].cpu(), vh),
                None if grads[5] is None else sel(grads[5].cpu(), vh, 1)]
         for name, x, r in zip(("dq", "dk", "dv", "dbeta", "dg", "dh0"), got, g_ref):
-            if r is None:
-                assert x is None
-                continue
-            res[name] = ratio(f64(x), r)
+            res[name] = check(name, None if x is None else f64(x), r,
+                              "state" if name == "dh0" else "tok", cu)
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for k, v in res.items():
         assert v <= TOL, (k, v)

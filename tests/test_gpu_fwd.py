@@ -5,7 +5,7 @@ import torch
 
 import gdr_synth
 import oracle
-from _util import TOL, np64, ratio, to_dev
+from _util import TOL, check, np64, ratio, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -51,17 +51,18 @@ def test_forward_matches_oracle(name):
     print("case", name, prob, flush=True)
     g_cum, A, o, h, ht = run_gpu_fwd(d)
     gc_r, A_r, o_r, h_r, ht_r = oracle_chunked(d)
-    assert ratio(np64(o), o_r) <= TOL
-    assert ratio(np64(ht), ht_r) <= TOL
-    assert ratio(np64(g_cum), gc_r) <= 1e-5
-    assert ratio(np64(A), A_r) <= TOL
-    assert ratio(np64(h), h_r) <= TOL
+    cu = d["cu_seqlens"]
+    check("o", o, o_r, "tok", cu)
+    check("final_state", ht, ht_r, "state")
+    check("g_cum", g_cum, gc_r, "tok", cu, tol=1e-5)
+    check("A", A, A_r, "tok", cu)
+    check("h", h, h_r, "state")
     # the token recurrence gives the same outputs
     o2, ht2 = oracle.fwd(np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]),
                          d["scale"], initial_state=np64(d["h0"]),
                          cu_seqlens=None if d["cu_seqlens"] is None else d["cu_seqlens"].numpy())
-    assert ratio(np64(o), o2) <= TOL
-    assert ratio(np64(ht), ht2) <= TOL
+    check("o (recurrence)", o, o2, "tok", cu)
+    check("final_state (recurrence)", ht, ht2, "state")
 
 
 def test_state_v_first_is_bit_exact():
@@ -99,9 +100,10 @@ def test_context_parallel_forward_matches_oracle(name, cp):
     print("case", name, "cp", cp, flush=True)
     g_cum, A, o, h, ht = run_gpu_fwd(d, cp=cp)
     gc_r, A_r, o_r, h_r, ht_r = oracle_chunked(d)
-    assert ratio(np64(o), o_r) <= TOL
-    assert ratio(np64(ht), ht_r) <= TOL
-    assert ratio(np64(h), h_r) <= TOL
+    cu = d["cu_seqlens"]
+    check("o", o, o_r, "tok", cu)
+    check("final_state", ht, ht_r, "state")
+    check("h", h, h_r, "state")
     # the same problem without CP agrees closely
     ref = run_gpu_fwd(d, cp=1)
     assert ratio(np64(o), np64(ref[2])) <= TOL
@@ -123,9 +125,10 @@ def test_forward_scan_variants(name, output_h, vt, cp):
     print("case", name, "output_h", output_h, "wave_tiles", vt, "cp", cp, flush=True)
     g_cum, A, o, h, ht = run_gpu_fwd(d, output_h=output_h, cp=cp, vt=vt)
     gc_r, A_r, o_r, h_r, ht_r = oracle_chunked(d)
-    assert ratio(np64(o), o_r) <= TOL
-    assert ratio(np64(ht), ht_r) <= TOL
+    cu = d["cu_seqlens"]
+    check("o", o, o_r, "tok", cu)
+    check("final_state", ht, ht_r, "state")
     if output_h:
-        assert ratio(np64(h), h_r) <= TOL
+        check("h", h, h_r, "state")
     else:
         assert h is None

@@ -9,7 +9,7 @@ import torch
 
 import gdr_synth
 import oracle
-from _util import TOL, np64, ratio, to_dev
+from _util import TOL, check, np64, ratio, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -70,10 +70,10 @@ def test_l2norm_matches_oracle(name, cp, vt, output_h):
     args = (np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]), d["scale"])
     gc_r, A_r, o_r, h_r, ht_r = oracle.chunked_fwd(*args, chunk=64, initial_state=np64(d["h0"]),
                                                    cu_seqlens=cu, use_qk_l2norm=True)
-    res = {"o": ratio(np64(o), o_r), "final_state": ratio(np64(ht), ht_r),
-           "A": ratio(np64(A), A_r)}
+    res = {"o": check("o", o, o_r, "tok", d["cu_seqlens"]), "final_state": check("final_state", ht, ht_r, "state"),
+           "A": check("A", A, A_r, "tok", d["cu_seqlens"])}
     if output_h:
-        res["h"] = ratio(np64(h), h_r)
+        res["h"] = check("h", h, h_r, "state")
     if grads is not None:
         ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]),
                          cu_seqlens=cu, use_qk_l2norm=True)
@@ -81,7 +81,7 @@ def test_l2norm_matches_oracle(name, cp, vt, output_h):
             if r is None:
                 assert x is None
                 continue
-            res[nm] = ratio(np64(x), r)
+            res[nm] = check(nm, x, r, "state" if nm in ("dh0", "final_state") else "tok", d["cu_seqlens"])
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for k, v in res.items():
         assert v <= TOL, (k, v)
@@ -123,11 +123,12 @@ def test_l2norm_full_B2_T4096_H32_fwd_bwd():
     o_r, ht_r = oracle.fwd(*args, initial_state=h0, nthreads=16, use_qk_l2norm=True)
     ref = oracle.bwd(*args, f(sel(d["do"])), initial_state=h0, dht=f(sel(d["dht"], 1)),
                      nthreads=16, use_qk_l2norm=True)
-    res = {"o": ratio(f(sel(o.cpu())), o_r), "final_state": ratio(f(sel(ht.cpu(), 1)), ht_r)}
+    res = {"o": check("o", f(sel(o.cpu())), o_r, "tok"),
+           "final_state": check("final_state", f(sel(ht.cpu(), 1)), ht_r, "state")}
     got = [sel(grads[0].cpu()), sel(grads[1].cpu()), sel(grads[2].cpu()), sel(grads[3].cpu()),
            sel(grads[4].cpu()), sel(grads[5].cpu(), 1)]
     for nm, x, r in zip(NAMES, got, ref):
-        res[nm] = ratio(f(x), r)
+        res[nm] = check(nm, f(x), r, "state" if nm == "dh0" else "tok")
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for k, v in res.items():
         assert v <= TOL, (k, v)

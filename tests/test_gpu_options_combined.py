@@ -9,7 +9,7 @@ import torch
 
 import gdr_synth
 import oracle
-from _util import TOL, np64, ratio, to_dev
+from _util import TOL, check, np64, ratio, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -62,10 +62,10 @@ def test_all_options_chunked(name):
     ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]),
                      cu_seqlens=cu, **opts(d))
     back = (lambda t: t.transpose(-1, -2)) if svf else (lambda t: t)
-    res = {"o": ratio(np64(o), o_r), "final_state": ratio(np64(back(ht)), ht_r)}
+    res = {"o": check("o", o, o_r, "tok", d["cu_seqlens"]), "final_state": check("final_state", back(ht), ht_r, "state")}
     got = list(grads[:5]) + [back(grads[5])]
     for nm, x, r in zip(NAMES, got, ref):
-        res[nm] = ratio(np64(x), r)
+        res[nm] = check(nm, x, r, "state" if nm in ("dh0", "final_state") else "tok", d["cu_seqlens"])
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for k, v in res.items():
         assert v <= TOL, (k, v)
@@ -84,5 +84,5 @@ def test_all_options_token_by_token():
     o_r, ht_r = oracle.fwd(np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]),
                            np64(d["beta"]), d["scale"], initial_state=np64(d["h0"]),
                            cu_seqlens=d["cu_seqlens"].numpy(), **opts(d))
-    assert ratio(np64(o), o_r) <= TOL
-    assert ratio(np64(ht), ht_r) <= TOL
+    check("o", o, o_r, "tok", d["cu_seqlens"])
+    check("final_state", ht, ht_r, "state")

@@ -12,7 +12,7 @@ import torch
 
 import gdr_synth
 import oracle
-from _util import TOL, np64, ratio, to_dev
+from _util import TOL, check, np64, ratio, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -77,9 +77,9 @@ def test_poisoned_workspace(name):
                      cu_seqlens=cu, **okw)
     o, ht = outs[0][:2]
     grads = outs[0][2:]
-    res = {"o": ratio(np64(o), o_r), "final_state": ratio(np64(ht), ht_r)}
+    res = {"o": check("o", o, o_r, "tok", d["cu_seqlens"]), "final_state": check("final_state", ht, ht_r, "state")}
     for nm, x, r in zip(NAMES, grads, ref):
-        res[nm] = ratio(np64(x), r)
+        res[nm] = check(nm, x, r, "state" if nm in ("dh0", "final_state") else "tok", d["cu_seqlens"])
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for t in outs[0]:
         assert bool(torch.isfinite(t).all())
@@ -132,7 +132,7 @@ def test_every_plan_on_a_poisoned_workspace(cp, vt):
     torch.cuda.synchronize()
     res = {}
     for nm, x, r in zip(("o", "final_state") + NAMES, (o, ht) + tuple(grads), ref):
-        res[nm] = ratio(np64(x), r)
+        res[nm] = check(nm, x, r, "state" if nm in ("dh0", "final_state") else "tok", d["cu_seqlens"])
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for k, v in res.items():
         assert v <= TOL, (k, v)
