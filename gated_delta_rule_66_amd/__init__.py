@@ -172,7 +172,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                wave_tiles=0, use_qk_l2norm_in_kernel=False,
                                use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False,
                                use_gate_in_kernel=False, A_log=None, dt_bias=None,
-                               workspace=None):
+                               workspace=None, no_alloc=False):
     """Forward.  Returns ``(g_cum, A, o, h, final_state)``: the chunk-local
     cumsum of g (fp32), the per-chunk inverse A ``[B,T,Hv,64]``, the output,
     the chunk-start states (``None`` unless ``output_h``) and the fp32 final
@@ -186,7 +186,10 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     dt_bias may be None); g_cum is the cumsum of that log decay.  ``workspace``
     (optional): a device uint8 tensor of at least
     ``gdr_chunk_fwd_workspace_size`` bytes to use instead of a new one; its
-    contents need no initialisation."""
+    contents need no initialisation.  ``no_alloc``: call
+    ``gdr_chunk_fwd_noalloc``, which takes no workspace (the library's static
+    64 MiB device array instead; larger problems raise).  The outputs are
+    still new tensors unless the caller hands them in through the C ABI."""
     q, k, v, g, beta, initial_state = _contig(q, k, v, g, beta, initial_state)
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
               wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
@@ -205,6 +208,13 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
         if output_final_state else None
     if initial_state is not None:
         initial_state = initial_state.to(torch.float32).contiguous()
+    if no_alloc:
+        if workspace is not None:
+            raise GdrError(10, "no_alloc takes no workspace")
+        check(lib.gdr_chunk_fwd_noalloc(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(initial_state), _ptr(g_cum), _ptr(A), _ptr(o),
+                                        _ptr(h), _ptr(ht), _stream(dev)))
+        return g_cum, A, o, h, ht
     ws_bytes = lib.gdr_chunk_fwd_workspace_size(c.ref)
     ws = _workspace(ws_bytes, dev, workspace)
     check(lib.gdr_chunk_fwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),

@@ -46,7 +46,7 @@ EXPORTS = [
     "gdr_prepare_chunk_indices_i32", "gdr_prepare_chunk_indices_i64",
     "gdr_prepare_chunk_offsets_i32", "gdr_prepare_chunk_offsets_i64",
     "gdr_prepare_chunk_token_starts_i64", "gdr_profile_enable", "gdr_profile_read",
-    "gdr_plan_info", "gdr_recurrent_fwd", "gdr_chunk_bwd_gate",
+    "gdr_plan_info", "gdr_recurrent_fwd", "gdr_chunk_bwd_gate", "gdr_chunk_fwd_noalloc",
 ]
 
 
@@ -77,6 +77,8 @@ def _declare(lib):
     lib.gdr_chunk_bwd_workspace_size.restype = S
     lib.gdr_chunk_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_chunk_fwd.restype = st
+    lib.gdr_chunk_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gdr_chunk_fwd_noalloc.restype = st
     lib.gdr_chunk_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_chunk_bwd.restype = st
     lib.gdr_chunk_bwd_gate.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,

@@ -390,6 +390,32 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
                     workspace, (hipStream_t)stream);
 }
 
+static_assert(GDR_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "header and library agree");
+
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void* k,
+                                 const void* v, const void* g, const void* beta,
+                                 const float* initial_state, float* g_cum, void* A, void* o,
+                                 void* h, float* final_state, void* stream) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  if (!q || !k || !v || !g || !beta || !g_cum || !A || !o)
+    return fail(GDR_ERR_NULL, nullptr, 0, "a required forward pointer is NULL");
+  const Plan pl = make_plan(p, false);
+  const size_t need = fwd_workspace_bytes(p, pl);
+  if (need > kNoAllocScratchBytes)
+    return fail(GDR_ERR_WORKSPACE, nullptr, 0,
+                "the forward needs %zu bytes of workspace; the no-allocation forward holds at "
+                "most %zu (call gdr_chunk_fwd with a workspace)",
+                need, kNoAllocScratchBytes);
+  s = check_device_cached();
+  if (s != GDR_OK) return s;
+  void* ws = nullptr;
+  s = noalloc_scratch(&ws);
+  if (s != GDR_OK) return s;
+  return launch_fwd(p, pl, q, k, v, g, beta, initial_state, g_cum, A, o, h, final_state, ws,
+                    (hipStream_t)stream);
+}
+
 static gdr_status chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                             const float* g_cum, const void* graw, const void* beta, const void* A,
                             const void* do_, const float* dht, const float* initial_state,

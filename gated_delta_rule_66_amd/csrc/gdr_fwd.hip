@@ -24,6 +24,8 @@
 #include "gdr_internal.h"
 #include "gdr_scan.h"
 
+#include <mutex>
+
 namespace gdr {
 
 struct FwdArgs {
@@ -199,6 +201,46 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   }
 }
 
+
+// ---- scratch of the no-allocation forward ---------------------------------
+// A file-scope device array that stands in for the caller's workspace in
+// gdr_chunk_fwd_noalloc.  Each GPU the library runs on holds its own copy from
+// module load until the process ends.  In host code `scratch` only names the
+// symbol: its device address on the current device comes from
+// hipGetSymbolAddress, resolved once per device and kept.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+gdr_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    set_error("no HIP device is available");
+    return GDR_ERR_DEVICE;
+  }
+  if (dev >= kMaxDevices) {
+    set_error("device %d is past the %d devices the scratch table tracks", dev, kMaxDevices);
+    return GDR_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      set_error("hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(e));
+      (void)hipGetLastError();
+      return GDR_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDR_OK;
+}
 
 size_t cp_workspace_bytes(const Plan& pl, int Hv) {
   if (pl.cp <= 1) return 0;

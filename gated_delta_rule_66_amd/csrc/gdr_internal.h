@@ -28,6 +28,13 @@ Plan make_plan(const gdr_problem* p, bool bwd);
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t fwd_workspace_bytes(const gdr_problem* p, const Plan& pl);
+
+// The no-allocation forward: its workspace is a file-scope device array of
+// kNoAllocScratchBytes (gdr_fwd.hip); noalloc_scratch gives its address on the
+// current device (resolved once per device with hipGetSymbolAddress).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+gdr_status noalloc_scratch(void** out);
 size_t cp_workspace_bytes(const Plan& pl, int Hv);
 size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl);
 

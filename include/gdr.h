@@ -158,6 +158,26 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
                          float* g_cum, void* A, void* o, void* h, float* final_state,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward without allocation, for callers that cannot call hipMalloc or take
+ * a caller-owned workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, results and
+ * errors as gdr_chunk_fwd (bit-identical outputs: same plan, same kernels),
+ * with no workspace: the library uses a static device array of 64 MiB per
+ * GPU (GDR_NOALLOC_SCRATCH_BYTES), allocated when the library's code object
+ * loads on that GPU and held until the process ends.  Problems whose
+ * gdr_chunk_fwd_workspace_size exceeds it are rejected with
+ * GDR_ERR_WORKSPACE before any device work (a single 65,536-token sequence
+ * with 32 value heads needs 48 MiB; short and dense problems need none).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from several threads) race and must not be
+ * issued.  Nothing in the array needs to start at zero: each call writes
+ * every byte it later reads. */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void* k,
+                                 const void* v, const void* g, const void* beta,
+                                 const float* initial_state, float* g_cum, void* A, void* o,
+                                 void* h, float* final_state, void* stream);
+
 /* Backward ("FlashQLA Documentation", backward pass: takes q, k, v, the g
  * returned by the forward, beta, A, do, dht, scale, initial_state, cu_seqlens
  * and returns dq, dk, dv, db, dg, dh0).

@@ -282,3 +282,27 @@ def test_binding_rejects_a_tensor_on_another_device():
     with pytest.raises(gdr.GdrError) as e:
         gdr.chunk_gated_delta_rule_fwd(x["q"], x["k"], meta_v, x["g"], x["beta"])
     assert e.value.name == "GDR_ERR_DEVICE"
+
+
+def test_no_alloc_forward_rejects_problems_past_its_scratch_before_device_work():
+    P = ctypes.c_void_p
+    assert _lib.lib.gdr_chunk_fwd_noalloc is not None
+    # four 65,536-token sequences of 32 heads split in segments need 192 MiB
+    # of context-parallel buffers: more than the 64 MiB static array
+    big = good(B=4, N=4, T=65536, Hq=32, Hv=32, cp_segments=8)
+    need = lib.gdr_chunk_fwd_workspace_size(ctypes.byref(big))
+    assert need > (64 << 20)
+    st = lib.gdr_chunk_fwd_noalloc(ctypes.byref(big), *[P(16)] * 5, None, P(16), P(16), P(16),
+                                   None, None, None)
+    assert _lib.STATUS[st] == "GDR_ERR_WORKSPACE"
+    assert "no-allocation forward holds at most 67108864" in lib.gdr_last_error().decode()
+    # the same validation as gdr_chunk_fwd comes first
+    st = lib.gdr_chunk_fwd_noalloc(ctypes.byref(good(K=64)), *[P(16)] * 5, None, P(16), P(16),
+                                   P(16), None, None, None)
+    assert _lib.STATUS[st] == "GDR_ERR_HEAD_DIM"
+    st = lib.gdr_chunk_fwd_noalloc(ctypes.byref(good()), *[P(16)] * 5, None, None, P(16), P(16),
+                                   None, None, None)
+    assert _lib.STATUS[st] == "GDR_ERR_NULL"
+    # one long sequence fits (48 MiB of segment buffers)
+    one = good(B=1, N=1, T=65536, Hq=32, Hv=32, cp_segments=8)
+    assert 0 < lib.gdr_chunk_fwd_workspace_size(ctypes.byref(one)) <= (64 << 20)
