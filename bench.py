@@ -257,7 +257,7 @@ class Case:
     for its forward, its backward (on the forward's g_cum and A) and a step."""
 
     def __init__(self, gdr, torch, gdr_synth, B, T, Hq, Hv, dt, g_shift, varlen, h0, dht, svf,
-                 cp=0, vt=0, qk_norm=False, gate=False, name="case"):
+                 cp=0, vt=0, qk_norm=False, gate=False, name="case", recompute=False):
         prob = gdr_synth.Problem(name, B=B, T=T, Hq=Hq, Hv=Hv, dtype=dt, init_state=h0,
                                  backward=True, dht=dht, g_shift=g_shift, qk_l2norm=qk_norm,
                                  gate=gate)
@@ -281,27 +281,30 @@ class Case:
         gkw = dict(use_gate_in_kernel=True, A_log=dd["A_log"], dt_bias=dd["dt_bias"]) if gate else {}
         self.plans = {d_: gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
                                         cu_seqlens_cpu=cu_cpu, cp_segments=cp, wave_tiles=vt,
-                                        backward=(d_ == "bwd"))
+                                        backward=(d_ == "bwd"), h_packed=not recompute)
                       for d_ in ("fwd", "bwd")}
 
+        # the autograd op's calls: the forward keeps its chunk-start states
+        # (value-major) and the backward takes them instead of recomputing
         def fwd():
             return gdr.chunk_gated_delta_rule_fwd(
                 dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
                 initial_state=dd["h0"], output_final_state=True, cu_seqlens=dd["cu_seqlens"],
                 cu_seqlens_cpu=cu_cpu, state_v_first=svf, cp_segments=cp, wave_tiles=vt,
-                use_qk_l2norm_in_kernel=qk_norm, **gkw)
+                use_qk_l2norm_in_kernel=qk_norm, output_h=not recompute, h_packed=True,
+                **gkw)
 
-        def bwd(g_cum, A):
+        def bwd(g_cum, A, h):
             return gdr.chunk_gated_delta_rule_bwd(
                 dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dd["dht"],
                 scale=dd["scale"], initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
                 state_v_first=svf, dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu,
-                cp_segments=cp, wave_tiles=vt, use_qk_l2norm_in_kernel=qk_norm,
+                cp_segments=cp, wave_tiles=vt, use_qk_l2norm_in_kernel=qk_norm, h=h,
                 **(dict(gkw, g_input=dd["g"]) if gate else {}))
 
         def step():
-            g_cum, A, o, _, ht = fwd()
-            return bwd(g_cum, A)
+            g_cum, A, o, h, ht = fwd()
+            return bwd(g_cum, A, h)
 
         self.fwd, self.bwd, self.step = fwd, bwd, step
 
@@ -385,9 +388,9 @@ def measure_case(gdr, torch, timer, case, direction, steps, warmup, n_cold):
         flop, nbytes = fwd_flop, fwd_bytes
         kt = kernel_times(gdr, torch, case.fwd, steps)
     else:
-        g_cum, A, _, _, _ = case.fwd()
-        bwd_ms = timer.mean_ms(lambda: case.bwd(g_cum, A), steps)
-        bwd_cold = timer.cold_ms(lambda: case.bwd(g_cum, A), n_cold)
+        g_cum, A, _, h, _ = case.fwd()
+        bwd_ms = timer.mean_ms(lambda: case.bwd(g_cum, A, h), steps)
+        bwd_cold = timer.cold_ms(lambda: case.bwd(g_cum, A, h), n_cold)
         rec["bwd_ms"], rec["bwd_cold_ms"] = round(bwd_ms, 4), round(bwd_cold, 4)
         rec["bwd_frac"] = fractions(bwd_ms * 1e-3, bwd_flop, bwd_bytes)
         ms = timer.mean_ms(case.step, steps)
@@ -424,6 +427,9 @@ def main():
     ap.add_argument("--gate", action="store_true",
                     help="g is the raw gate input, activated inside the kernels "
                          "(use_gate_in_kernel: -exp(A_log) softplus(g + dt_bias))")
+    ap.add_argument("--recompute-states", action="store_true",
+                    help="the backward recomputes the chunk-start states instead of taking the "
+                         "forward's (autograd's recompute_states=True)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path runs on a single MI355X and the library "
@@ -439,7 +445,8 @@ def main():
     B, T, Hq, Hv, dt, g_shift, varlen = WORKLOADS[args.workload]
     qkn = args.qk_l2norm
     case = Case(gdr, torch, gdr_synth, B, T, Hq, Hv, dt, g_shift, varlen, True, True, False,
-                cp=args.cp, vt=args.vt, qk_norm=qkn, gate=args.gate, name=args.workload)
+                cp=args.cp, vt=args.vt, qk_norm=qkn, gate=args.gate, name=args.workload,
+                recompute=args.recompute_states)
     B, T = case.B, case.T
     dev = torch.device("cuda", 0)
     timer = Timer(torch)
@@ -459,13 +466,13 @@ def main():
     ms = timer.mean_ms(case.step, args.steps)
 
     # the forward and the backward alone, cold runs, then per-kernel times
-    g_cum, A, o, _, ht = case.fwd()
+    g_cum, A, o, h, ht = case.fwd()
     n_sub = max(3, args.steps // 2)
     fwd_ms = timer.mean_ms(case.fwd, n_sub)
-    bwd_ms = timer.mean_ms(lambda: case.bwd(g_cum, A), n_sub)
+    bwd_ms = timer.mean_ms(lambda: case.bwd(g_cum, A, h), n_sub)
     cold_ms = timer.cold_ms(case.step, args.cold)
     fwd_cold = timer.cold_ms(case.fwd, args.cold)
-    bwd_cold = timer.cold_ms(lambda: case.bwd(g_cum, A), args.cold)
+    bwd_cold = timer.cold_ms(lambda: case.bwd(g_cum, A, h), args.cold)
     kernels = kernel_times(gdr, torch, case.step, args.steps)
 
     tokens = case.tokens
@@ -535,6 +542,8 @@ def main():
                    "cp_segments": {k_: v_[0] for k_, v_ in case.plans.items()},
                    "wave_tiles": {k_: v_[1] for k_, v_ in case.plans.items()},
                    "qk_l2norm_in_kernel": qkn, "gate_in_kernel": bool(args.gate),
+                   "backward_states": "recomputed" if args.recompute_states else
+                   "kept by the forward (autograd default)",
                    "parallelism": "single GPU"},
         "cold_ms_per_step": round(cold_ms, 4),
         "fwd_ms": round(fwd_ms, 4),
@@ -550,7 +559,7 @@ def main():
         "configs": None,
         "cpu_baseline": None,
     }
-    del g_cum, A, o, ht
+    del g_cum, A, o, h, ht
     host = case.host
     if not args.no_configs and args.workload == DEFAULT and not qkn and not args.gate:
         del case

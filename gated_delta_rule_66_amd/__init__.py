@@ -23,7 +23,7 @@ from ._lib import (GDR_BF16, GDR_FP16, GDR_FP32, GdrError, Problem, check, lib)
 __all__ = [
     "chunk_gated_delta_rule", "chunk_gated_delta_rule_fwd", "chunk_gated_delta_rule_bwd",
     "fused_recurrent_gated_delta_rule", "prepare_lens", "prepare_chunk_indices",
-    "prepare_chunk_offsets", "GdrError",
+    "prepare_chunk_offsets", "unpack_states", "GdrError",
 ]
 
 CHUNK = 64
@@ -49,7 +49,7 @@ class _Call:
 
     def __init__(self, q, v, g_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first,
                  cp_segments, wave_tiles=0, use_qk_l2norm=False, beta_sigmoid=False,
-                 neg_eigval=False, gate=None):
+                 neg_eigval=False, gate=None, h_packed=False):
         if q.dim() != 4 or v.dim() != 4:
             raise GdrError(2, "q and v must be 4-D ([B, T, H, dim]), got %s and %s"
                            % (tuple(q.shape), tuple(v.shape)))
@@ -92,7 +92,8 @@ class _Call:
                          use_gate=0 if self.gate is None else 1,
                          gate_A_log=None if self.gate is None else self.gate[0].data_ptr(),
                          gate_dt_bias=None if self.gate is None or self.gate[1] is None
-                         else self.gate[1].data_ptr())
+                         else self.gate[1].data_ptr(),
+                         h_packed=1 if h_packed else 0)
         self.N, self.Hv, self.K, self.V = N, Hv, K, V
         self.ref = ctypes.byref(self.p)
         reason = ctypes.create_string_buffer(256)
@@ -100,6 +101,13 @@ class _Call:
 
     def state_shape(self, state_v_first):
         return (self.N, self.Hv, self.V, self.K) if state_v_first else (self.N, self.Hv, self.K, self.V)
+
+    def h_shape(self, state_v_first, h_packed=False):
+        """Shape of the chunk-start states h: [NC, Hv, K, V] ([NC, Hv, V, K]
+        with state_v_first), or [NC, Hv, 128 * 128] packed (h_packed)."""
+        if h_packed:
+            return (self.num_chunks(), self.Hv, self.K * self.V)
+        return (self.num_chunks(), self.Hv) + self.state_shape(state_v_first)[2:]
 
     def num_chunks(self):
         if self.cu_host is None:
@@ -172,7 +180,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
                                wave_tiles=0, use_qk_l2norm_in_kernel=False,
                                use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False,
                                use_gate_in_kernel=False, A_log=None, dt_bias=None,
-                               workspace=None, no_alloc=False):
+                               workspace=None, no_alloc=False, h_packed=False):
     """Forward.  Returns ``(g_cum, A, o, h, final_state)``: the chunk-local
     cumsum of g (fp32), the per-chunk inverse A ``[B,T,Hv,64]``, the output,
     the chunk-start states (``None`` unless ``output_h``) and the fp32 final
@@ -189,11 +197,16 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     contents need no initialisation.  ``no_alloc``: call
     ``gdr_chunk_fwd_noalloc``, which takes no workspace (the library's static
     64 MiB device array instead; larger problems raise).  The outputs are
-    still new tensors unless the caller hands them in through the C ABI."""
+    still new tensors unless the caller hands them in through the C ABI.
+    ``h_packed``: with ``output_h``, h is ``[NC, Hv, 16384]`` in the packed
+    layout ``chunk_gated_delta_rule_bwd`` takes as its ``h`` (the states are
+    then not recomputed): element ``((vb*4 + kb)*64 + 16*g + c)*8 + e`` is the
+    state at value ``16*vb + c`` and key ``32*kb + 16*(e >= 4) + 4*g + e % 4``
+    (:func:`unpack_states` gives ``[NC, Hv, K, V]``)."""
     q, k, v, g, beta, initial_state = _contig(q, k, v, g, beta, initial_state)
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
               wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
-              (A_log, dt_bias) if use_gate_in_kernel else None)
+              (A_log, dt_bias) if use_gate_in_kernel else None, h_packed=h_packed)
     _check_inputs(c, q, k, v, g, beta, state_v_first, initial_state=initial_state)
     dev = q.device
     B, T = q.shape[0], q.shape[1]
@@ -202,8 +215,7 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     o = torch.empty(B, T, c.Hv, c.V, dtype=q.dtype, device=dev)
     h = None
     if output_h:
-        nc = c.num_chunks()
-        h = torch.empty((nc, c.Hv) + c.state_shape(state_v_first)[2:], dtype=q.dtype, device=dev)
+        h = torch.empty(c.h_shape(state_v_first, h_packed), dtype=q.dtype, device=dev)
     ht = torch.empty(c.state_shape(state_v_first), dtype=torch.float32, device=dev) \
         if output_final_state else None
     if initial_state is not None:
@@ -228,7 +240,7 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
                                cp_segments=0, cu_seqlens_cpu=None, wave_tiles=0,
                                use_qk_l2norm_in_kernel=False, use_beta_sigmoid_in_kernel=False,
                                allow_neg_eigval=False, use_gate_in_kernel=False, A_log=None,
-                               dt_bias=None, g_input=None, workspace=None):
+                               dt_bias=None, g_input=None, workspace=None, h=None):
     """Backward.  ``g`` is the forward's fp32 ``g_cum`` output.  Returns
     ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is the gradient with respect to
     the raw log-decay g (dtype ``dg_dtype``, default the input dtype) and
@@ -240,9 +252,12 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     ``dg`` is with respect to it (dtype ``dg_dtype``, default g_input's) and
     two more entries follow: the fp32 gradients of ``A_log`` and ``dt_bias``
     (``[Hv]``).  ``workspace`` as in the forward, of at least
-    ``gdr_chunk_bwd_workspace_size`` bytes."""
-    q, k, v, g, beta, A, do, dht, initial_state, g_input = _contig(
-        q, k, v, g, beta, A, do, dht, initial_state, g_input)
+    ``gdr_chunk_bwd_workspace_size`` bytes (``..._states_workspace_size`` with
+    ``h``).  ``h``: the packed chunk-start states the forward returned for the
+    same inputs with ``output_h=True, h_packed=True``; the backward then
+    skips recomputing them (``gdr_chunk_bwd_states``)."""
+    q, k, v, g, beta, A, do, dht, initial_state, g_input, h = _contig(
+        q, k, v, g, beta, A, do, dht, initial_state, g_input, h)
     if g.dtype != torch.float32:
         raise GdrError(4, "the backward takes the forward's fp32 g_cum as g")
     if use_gate_in_kernel and g_input is None:
@@ -256,6 +271,7 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
               (A_log, dt_bias) if use_gate_in_kernel else None)
     _check_inputs(c, q, k, v, None, beta, state_v_first, initial_state=initial_state, A=A,
                   do=do, dht=dht, g_cum=g, g_input=g_input)
+    _expect("h", h, c.h_shape(state_v_first, True), (q.dtype,), q.device)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -268,6 +284,22 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
         dh0 = torch.empty(c.state_shape(state_v_first), dtype=torch.float32, device=dev)
     if dht is not None:
         dht = dht.to(torch.float32).contiguous()
+    if h is not None:
+        ws_bytes = lib.gdr_chunk_bwd_states_workspace_size(c.ref)
+        ws = _workspace(ws_bytes, dev, workspace)
+        dA_log = ddt_bias = None
+        if use_gate_in_kernel:
+            dA_log = torch.empty(c.Hv, dtype=torch.float32, device=dev)
+            ddt_bias = torch.empty(c.Hv, dtype=torch.float32, device=dev)
+        check(lib.gdr_chunk_bwd_states(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(g_input if use_gate_in_kernel else None), _ptr(beta),
+                                       _ptr(A), _ptr(do), _ptr(dht), _ptr(initial_state), _ptr(h),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0),
+                                       _ptr(dA_log), _ptr(ddt_bias), _ptr(ws), ws_bytes,
+                                       _stream(dev)))
+        if use_gate_in_kernel:
+            return dq, dk, dv, db, dg, dh0, dA_log, ddt_bias
+        return dq, dk, dv, db, dg, dh0
     ws_bytes = lib.gdr_chunk_bwd_workspace_size(c.ref)
     ws = _workspace(ws_bytes, dev, workspace)
     if use_gate_in_kernel:
@@ -289,18 +321,18 @@ class _GatedDeltaRule(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
                 state_v_first, cp_segments, cu_seqlens_cpu, use_qk_l2norm, beta_sigmoid,
-                neg_eigval, use_gate, A_log, dt_bias):
+                neg_eigval, use_gate, A_log, dt_bias, recompute_states):
         if cu_seqlens is not None and cu_seqlens_cpu is None:
             # the one device-to-host copy of the lengths, shared by the backward
             cu_seqlens_cpu = cu_seqlens.detach().to("cpu")
-        g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
+        g_cum, A, o, h, ht = chunk_gated_delta_rule_fwd(
             q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
-            state_v_first, False, cp_segments, cu_seqlens_cpu,
+            state_v_first, not recompute_states, cp_segments, cu_seqlens_cpu,
             use_qk_l2norm_in_kernel=use_qk_l2norm, use_beta_sigmoid_in_kernel=beta_sigmoid,
             allow_neg_eigval=neg_eigval, use_gate_in_kernel=use_gate, A_log=A_log,
-            dt_bias=dt_bias)
+            dt_bias=dt_bias, h_packed=True)
         ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, cu_seqlens_cpu,
-                              g if use_gate else None, A_log, dt_bias)
+                              g if use_gate else None, A_log, dt_bias, h)
         ctx.scale, ctx.svf, ctx.cp, ctx.g_dtype = scale, state_v_first, cp_segments, g.dtype
         ctx.qk_norm, ctx.beta_sigmoid, ctx.neg_eigval = use_qk_l2norm, beta_sigmoid, neg_eigval
         ctx.use_gate = use_gate
@@ -308,19 +340,19 @@ class _GatedDeltaRule(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, do, dht):
-        q, k, v, g_cum, beta, A, h0, cu, cu_cpu, g_in, A_log, dt_bias = ctx.saved_tensors
+        q, k, v, g_cum, beta, A, h0, cu, cu_cpu, g_in, A_log, dt_bias, h = ctx.saved_tensors
         grads = chunk_gated_delta_rule_bwd(
             q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu, ctx.svf, ctx.g_dtype, ctx.cp,
             cu_cpu, use_qk_l2norm_in_kernel=ctx.qk_norm,
             use_beta_sigmoid_in_kernel=ctx.beta_sigmoid, allow_neg_eigval=ctx.neg_eigval,
-            use_gate_in_kernel=ctx.use_gate, A_log=A_log, dt_bias=dt_bias, g_input=g_in)
+            use_gate_in_kernel=ctx.use_gate, A_log=A_log, dt_bias=dt_bias, g_input=g_in, h=h)
         dq, dk, dv, db, dg, dh0 = grads[:6]
         dA = ddt = None
         if ctx.use_gate:
             dA = grads[6].to(A_log.dtype)
             ddt = None if dt_bias is None else grads[7].to(dt_bias.dtype)
         return (dq, dk, dv, dg, db, None, dh0, None, None, None, None, None, None, None, None,
-                None, dA, ddt)
+                None, dA, ddt, None)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
@@ -328,8 +360,13 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                            state_v_first=False, cu_seqlens=None, cp_segments=0,
                            cu_seqlens_cpu=None, use_beta_sigmoid_in_kernel=False,
                            allow_neg_eigval=False, use_gate_in_kernel=False, A_log=None,
-                           dt_bias=None, **unsupported):
+                           dt_bias=None, recompute_states=False, **unsupported):
     """High-level op with autograd: returns ``(o, final_state)``.
+
+    The forward keeps its chunk-start states (``[NC, Hv, V, K]`` in the input
+    dtype, 32 KiB per chunk and value head) for the backward, which then does
+    not recompute them; ``recompute_states=True`` keeps only the inputs and
+    recomputes the states in the backward instead.
 
     ``use_qk_l2norm_in_kernel`` scales q and k per (token, head) to unit
     length inside the kernels (and carries the gradient back to the raw q, k);
@@ -349,7 +386,7 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                                  bool(use_qk_l2norm_in_kernel), bool(use_beta_sigmoid_in_kernel),
                                  bool(allow_neg_eigval), bool(use_gate_in_kernel),
                                  A_log if use_gate_in_kernel else None,
-                                 dt_bias if use_gate_in_kernel else None)
+                                 dt_bias if use_gate_in_kernel else None, bool(recompute_states))
 
 
 def fused_recurrent_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
@@ -388,6 +425,14 @@ def fused_recurrent_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state
     check(lib.gdr_recurrent_fwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(initial_state), _ptr(o), _ptr(ht), _stream(dev)))
     return o, ht
+
+
+def unpack_states(h):
+    """``[NC, Hv, K, V]`` from packed chunk-start states ``[NC, Hv, 16384]``
+    (``h_packed``): a view change and a permutation, no arithmetic."""
+    nc, hv = h.shape[0], h.shape[1]
+    x = h.reshape(nc, hv, 8, 4, 4, 16, 2, 4)   # vb, kb, g, c, half, e
+    return x.permute(0, 1, 3, 6, 4, 7, 2, 5).reshape(nc, hv, 128, 128)
 
 
 # ---- variable-length helpers ------------------------------------------------
@@ -434,11 +479,12 @@ def prepare_chunk_offsets(cu_seqlens: torch.Tensor, chunk_size: int):
 # ---- diagnostics --------------------------------------------------------------
 
 def plan_info(q, v, g_dtype=None, cu_seqlens=None, cu_seqlens_cpu=None, cp_segments=0,
-              wave_tiles=0, backward=False):
+              wave_tiles=0, backward=False, h_packed=False):
     """``(cp_segments, wave_tiles)`` the library plans for these shapes, for the
-    forward pass or (``backward=True``) the backward pass."""
+    forward pass or (``backward=True``) the backward pass; ``h_packed`` as in
+    the forward (a forward that keeps packed states plans one tile per wave)."""
     c = _Call(q, v, q.dtype if g_dtype is None else g_dtype, None, cu_seqlens, cu_seqlens_cpu,
-              False, cp_segments, wave_tiles)
+              False, cp_segments, wave_tiles, h_packed=h_packed)
     cp = ctypes.c_int32(0)
     vt = ctypes.c_int32(0)
     check(lib.gdr_plan_info(c.ref, 1 if backward else 0, ctypes.byref(cp), ctypes.byref(vt)))

@@ -35,6 +35,7 @@ class Problem(ctypes.Structure):
         ("use_gate", ctypes.c_int32),
         ("gate_A_log", ctypes.c_void_p),
         ("gate_dt_bias", ctypes.c_void_p),
+        ("h_packed", ctypes.c_int32),
     ]
 
 
@@ -47,6 +48,7 @@ EXPORTS = [
     "gdr_prepare_chunk_offsets_i32", "gdr_prepare_chunk_offsets_i64",
     "gdr_prepare_chunk_token_starts_i64", "gdr_profile_enable", "gdr_profile_read",
     "gdr_plan_info", "gdr_recurrent_fwd", "gdr_chunk_bwd_gate", "gdr_chunk_fwd_noalloc",
+    "gdr_chunk_bwd_states", "gdr_chunk_bwd_states_workspace_size",
 ]
 
 
@@ -77,6 +79,10 @@ def _declare(lib):
     lib.gdr_chunk_bwd_workspace_size.restype = S
     lib.gdr_chunk_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_chunk_fwd.restype = st
+    lib.gdr_chunk_bwd_states_workspace_size.argtypes = [PP]
+    lib.gdr_chunk_bwd_states_workspace_size.restype = S
+    lib.gdr_chunk_bwd_states.argtypes = [PP] + [P] * 20 + [S, P]
+    lib.gdr_chunk_bwd_states.restype = st
     lib.gdr_chunk_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_chunk_fwd_noalloc.restype = st
     lib.gdr_chunk_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, S, P]

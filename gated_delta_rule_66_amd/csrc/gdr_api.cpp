@@ -143,6 +143,10 @@ Plan make_plan(const gdr_problem* p, bool bwd) {
     if (fixed == 0 && P > 1 && maxch < 8 * P) continue;
     for (int VB = 1; VB <= 2; ++VB) {
       if (p->wave_tiles > 0 && VB != p->wave_tiles) continue;
+      // a forward that keeps packed states writes them from the one-tile
+      // pass's output waves; the two-tile pass would store them from its
+      // state chain (measured 681 -> 964 us for one T=65536 sequence)
+      if (!bwd && p->h_packed && p->wave_tiles == 0 && VB == 2) continue;
       // a split must win clearly: the model is coarse and splitting adds work
       const double c = plan_cost(units, maxch, P, VB, bwd) * ((P > 1 && fixed == 0) ? 1.1 : 1.0);
       if (c < best) {
@@ -192,6 +196,8 @@ static gdr_status validate(const gdr_problem* p, char* reason, size_t len) {
     return fail(GDR_ERR_ARG, reason, len, "beta_sigmoid must be 0 or 1");
   if (p->neg_eigval != 0 && p->neg_eigval != 1)
     return fail(GDR_ERR_ARG, reason, len, "neg_eigval must be 0 or 1");
+  if (p->h_packed != 0 && p->h_packed != 1)
+    return fail(GDR_ERR_ARG, reason, len, "h_packed must be 0 or 1");
   if (p->use_gate != 0 && p->use_gate != 1)
     return fail(GDR_ERR_ARG, reason, len, "use_gate must be 0 or 1");
   if (p->use_gate && !p->gate_A_log)
@@ -368,7 +374,12 @@ size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
 
 size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p) {
   if (validate(p, nullptr, 0) != GDR_OK) return 0;
-  return bwd_workspace_bytes(p, make_plan(p, true));
+  return bwd_workspace_bytes(p, make_plan(p, true), false);
+}
+
+size_t gdr_chunk_bwd_states_workspace_size(const gdr_problem* p) {
+  if (validate(p, nullptr, 0) != GDR_OK) return 0;
+  return bwd_workspace_bytes(p, make_plan(p, true), true);
 }
 
 gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -419,23 +430,23 @@ gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void
 static gdr_status chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                             const float* g_cum, const void* graw, const void* beta, const void* A,
                             const void* do_, const float* dht, const float* initial_state,
-                            void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
-                            float* dA_log, float* ddt_bias, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const void* hstates, void* dq, void* dk, void* dv, void* dbeta,
+                            void* dg, float* dh0, float* dA_log, float* ddt_bias,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !g_cum || !beta || !A || !do_ || !dq || !dk || !dv || !dbeta || !dg)
     return fail(GDR_ERR_NULL, nullptr, 0, "a required backward pointer is NULL");
   if (initial_state && !dh0)
     return fail(GDR_ERR_NULL, nullptr, 0, "dh0 is required when initial_state is given");
   const Plan pl = make_plan(p, true);
-  const size_t need = bwd_workspace_bytes(p, pl);
+  const size_t need = bwd_workspace_bytes(p, pl, hstates != nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDR_ERR_WORKSPACE, nullptr, 0, "backward workspace needs %zu bytes, got %zu",
                 need, workspace ? workspace_bytes : (size_t)0);
   const gdr_status s = check_device_cached();
   if (s != GDR_OK) return s;
-  return launch_bwd(p, pl, q, k, v, g_cum, graw, beta, A, do_, dht, initial_state, dq, dk, dv,
-                    dbeta, dg, initial_state ? dh0 : nullptr, dA_log, ddt_bias, workspace,
-                    (hipStream_t)stream);
+  return launch_bwd(p, pl, q, k, v, g_cum, graw, beta, A, do_, dht, initial_state, hstates, dq,
+                    dk, dv, dbeta, dg, initial_state ? dh0 : nullptr, dA_log, ddt_bias,
+                    workspace, (hipStream_t)stream);
 }
 
 gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -448,8 +459,8 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   if (p->use_gate)
     return fail(GDR_ERR_ARG, nullptr, 0,
                 "use_gate needs the gate input: call gdr_chunk_bwd_gate");
-  return chunk_bwd(p, q, k, v, g_cum, nullptr, beta, A, do_, dht, initial_state, dq, dk, dv,
-                   dbeta, dg, dh0, nullptr, nullptr, workspace, workspace_bytes, stream);
+  return chunk_bwd(p, q, k, v, g_cum, nullptr, beta, A, do_, dht, initial_state, nullptr, dq, dk,
+                   dv, dbeta, dg, dh0, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -463,8 +474,26 @@ gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k
   if (!p->use_gate)
     return fail(GDR_ERR_ARG, nullptr, 0, "gdr_chunk_bwd_gate needs use_gate == 1");
   if (!g) return fail(GDR_ERR_NULL, nullptr, 0, "the gate input g is NULL");
-  return chunk_bwd(p, q, k, v, g_cum, g, beta, A, do_, dht, initial_state, dq, dk, dv, dbeta,
-                   dg, dh0, dA_log, ddt_bias, workspace, workspace_bytes, stream);
+  return chunk_bwd(p, q, k, v, g_cum, g, beta, A, do_, dht, initial_state, nullptr, dq, dk, dv,
+                   dbeta, dg, dh0, dA_log, ddt_bias, workspace, workspace_bytes, stream);
+}
+
+gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void* k,
+                                const void* v, const float* g_cum, const void* g,
+                                const void* beta, const void* A, const void* do_,
+                                const float* dht, const float* initial_state, const void* h,
+                                void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
+                                float* dA_log, float* ddt_bias, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  if (!h) return fail(GDR_ERR_NULL, nullptr, 0, "the forward's chunk-start states h are NULL");
+  if (p->use_gate && !g) return fail(GDR_ERR_NULL, nullptr, 0, "the gate input g is NULL");
+  if (!p->use_gate && (g || dA_log || ddt_bias))
+    return fail(GDR_ERR_ARG, nullptr, 0, "g, dA_log and ddt_bias are for use_gate problems only");
+  return chunk_bwd(p, q, k, v, g_cum, p->use_gate ? g : nullptr, beta, A, do_, dht,
+                   initial_state, h, dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, workspace,
+                   workspace_bytes, stream);
 }
 
 gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,

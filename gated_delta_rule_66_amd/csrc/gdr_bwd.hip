@@ -44,7 +44,7 @@ struct DhArgs {
   const float* gcum;
   const void* A;
   const float* dht;    // [N, Hv, K, V] (svf aware), nullable
-  void* dh;            // [NC, Hv, V, K] in_dtype (value-major): gradient of each chunk's end state
+  void* dh;            // [NC, Hv] packed (packed_off), in_dtype: gradient of each chunk's end state
   float* dh0;          // nullable (svf aware)
   const float* seg_start;  // [units, P, K, V]: gradient entering each segment's end
   float* seg_out;          // [units, P, K, 2V]: augmented pass-1 results
@@ -174,19 +174,17 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
     __syncthreads();
     const float eL = __expf(gam[63]);
 
-    // gradient of this chunk's end state out, value-major ([V][K]): a lane's
-    // four consecutive keys of one value column are 8 contiguous bytes
+    // gradient of this chunk's end state out, packed (packed_off)
     if (OUT) {
       const __amdgpu_buffer_rsrc_t hrs =
           buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
+      for (int kb2 = 0; kb2 < 4; ++kb2)
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) {
-          const int vc = cb0 + cw0 + 16 * vb + col;
-          const typename VT<T>::x4 hv{from_f<T>(Gs[kb][vb][0]), from_f<T>(Gs[kb][vb][1]),
-                                      from_f<T>(Gs[kb][vb][2]), from_f<T>(Gs[kb][vb][3])};
-          buf_store8(hrs, (vc * kDim + 16 * kb + 4 * grp) * (int)sizeof(T), __builtin_bit_cast(u32x2, hv));
+          const x8 f = pack_split<T>(Gs[2 * kb2][vb], Gs[2 * kb2 + 1][vb]);
+          buf_store16(hrs, packed_off((cb0 + cw0) / 16 + vb, kb2, l) * (int)sizeof(T),
+                      __builtin_bit_cast(uint4, f));
         }
     }
 
@@ -453,22 +451,16 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
     tile_load<T, 64, 256>(ra, Ag + (t0 * a.Hv + h) * kChunk, (int64_t)a.Hv * kChunk, Cc, otid);
   };
 
-  // gradient of chunk cc's end state out, value-major ([V][K]), from the
-  // operand copy the chain left in Hx: element e < 4 of k block kb2 is key
-  // 32 kb2 + 4 grp + e, element e >= 4 key 32 kb2 + 16 + 4 grp + e - 4, so
-  // each half is 8 contiguous bytes of one value column
+  // gradient of chunk cc's end state out, packed (packed_off), from the
+  // operand copy the chain left in Hx
   auto store_dh = [&](int cc) {
     const int wq = w & 3;
     const __amdgpu_buffer_rsrc_t hrs =
         buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + cc) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
-    const int vc = cb0 + 16 * wq + col;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 4; ++kb2) {
-      const x8 g = Hx[wq][kb2][l];
-      const u32x4 u = __builtin_bit_cast(u32x4, g);
-      buf_store8(hrs, (vc * kDim + 32 * kb2 + 4 * grp) * (int)sizeof(T), u32x2{u[0], u[1]});
-      buf_store8(hrs, (vc * kDim + 32 * kb2 + 16 + 4 * grp) * (int)sizeof(T), u32x2{u[2], u[3]});
-    }
+    for (int kb2 = 0; kb2 < 4; ++kb2)
+      buf_store16(hrs, packed_off(cb0 / 16 + wq, kb2, l) * (int)sizeof(T),
+                  __builtin_bit_cast(uint4, Hx[wq][kb2][l]));
   };
 
   // the initial gradient has arrived before the loop (else the loop-entry
@@ -713,8 +705,8 @@ struct GradArgs {
   const void* beta;
   const float* gcum;
   const void* A;
-  const void* h;   // [NC, Hv, V, K] chunk-start states (value-major)
-  const void* dh;  // [NC, Hv, V, K] end-state gradients (value-major)
+  const void* h;   // [NC, Hv] packed chunk-start states (packed_off)
+  const void* dh;  // [NC, Hv] packed end-state gradients
   void* dq;        // in_dtype [T, Hq, K], or fp32 [T, Hv, K] partials when partial
   void* dk;
   void* dv;
@@ -796,7 +788,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   const T* vv = reinterpret_cast<const T*>(a.v);
   const T* dOg = reinterpret_cast<const T*>(a.dO);
 
-  // the value-half tiles: S^T, dSn^T (value-major rows v0 .. v0+63) and
+  // the value-half tiles: S^T, dSn^T (value-major LDS rows v0 .. v0+63) and
   // V, dO (columns v0 .. v0+63); half 1 is prefetched while half 0 computes
   TileRegs<128, 512> rs, rg;
   TileRegs<64, 512> rv, ro;
@@ -806,12 +798,14 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     tile_load<T, 64, 512>(rv, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
     tile_load<T, 64, 512>(ro, dOg + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
   };
+  // (the states are packed: the half's 16 KiB load in storage order and
+  // scatter into value-major LDS rows)
   float sds = 0.f;
   auto store_half = [&]() {
 #pragma unroll
     for (int i = 0; i < TileRegs<128, 512>::N; ++i) sds += dot8<T>(rs.r[i], rg.r[i]);
-    tile_store_q<T, 512>(Ss, rs);
-    tile_store_q<T, 512>(Gs_, rg);
+    tile_store_packed_q<T, 512>(Ss, rs);
+    tile_store_packed_q<T, 512>(Gs_, rg);
     tile_store<T, 64, 512>(Vs, L7, rv);
     tile_store<T, 64, 512>(Os, L7, ro);
   };
@@ -1426,7 +1420,7 @@ struct BwdLayout {
   size_t offs, cp, cp2, h, dh, pq, pk, gpart, total;
 };
 
-static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
+static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_given) {
   BwdLayout L;
   size_t o = 0;
   L.offs = o;
@@ -1438,7 +1432,7 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
   o += cp_workspace_bytes(pl, p->Hv);
   const size_t st = (size_t)pl.total_chunks * p->Hv * kDim * kDim * 2;  // bf16/fp16
   L.h = o;
-  o += align256(st);
+  if (!states_given) o += align256(st);
   L.dh = o;
   o += align256(st);
   L.pq = L.pk = o;
@@ -1455,23 +1449,31 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl) {
   return L;
 }
 
-size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl) { return bwd_layout(p, pl).total; }
+size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl, bool states_given) {
+  return bwd_layout(p, pl, states_given).total;
+}
 
 // B1 and B2 together: with CP, both augmented passes in one launch, the two
 // chains (forward for B1, reverse for B2), then both output passes in one
 // launch.
+// With the forward's chunk states given (states_given), only the
+// state-gradient scan runs: the launches keep their layout with no blocks for
+// the state scan.
 template <typename T, int VB>
-static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t st) {
+static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, bool states_given,
+                             hipStream_t st) {
   const unsigned units = (unsigned)(pl.N * sa.Hv);
   if (pl.cp > 1) {
     ScanArgs s1 = sa;
     DhArgs d1 = da;
     s1.P = d1.P = pl.cp;
     s1.nvs = d1.nvs = 4 / VB;
-    const unsigned n1 = units * pl.cp * s1.nvs;
-    GDR_LAUNCH("bwd_scan_aug", (bwd_scans_kernel<T, VB, MODE_AUG, MODE_AUG>), dim3(2 * n1),
+    const unsigned n2 = units * pl.cp * s1.nvs;
+    const unsigned n1 = states_given ? 0u : n2;
+    GDR_LAUNCH("bwd_scan_aug", (bwd_scans_kernel<T, VB, MODE_AUG, MODE_AUG>), dim3(n1 + n2),
                dim3(256), st, s1, d1, (int)n1);
-    GDR_LAUNCH("cp_combine_bwd", cp_combine_kernel, dim3(units * 8), dim3(256), st, s1);
+    if (!states_given)
+      GDR_LAUNCH("cp_combine_bwd", cp_combine_kernel, dim3(units * 8), dim3(256), st, s1);
     ScanArgs r;
     memset(&r, 0, sizeof(r));
     r.cu = da.cu;
@@ -1485,34 +1487,37 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, hipStream_t
   }
   sa.P = da.P = pl.cp;
   sa.nvs = da.nvs = 2 / VB;
-  const unsigned n1 = units * pl.cp * sa.nvs;
+  const unsigned n2 = units * pl.cp * sa.nvs;
+  const unsigned n1 = states_given ? 0u : n2;
+  const dim3 grid(n1 + n2);
   if (VB == 1)
     switch ((sa.qk_norm ? 1 : 0) | (sa.beta_mode ? 2 : 0)) {
       case 0:
-        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 0>), dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 0>), grid, dim3(512), st, sa, da, (int)n1);
         break;
       case 1:
-        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 1>), dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 1>), grid, dim3(512), st, sa, da, (int)n1);
         break;
       case 2:
-        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 2>), dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 2>), grid, dim3(512), st, sa, da, (int)n1);
         break;
       default:
-        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 3>), dim3(2 * n1), dim3(512), st, sa, da, (int)n1);
+        GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 3>), grid, dim3(512), st, sa, da, (int)n1);
     }
   else
-    GDR_LAUNCH("bwd_scans", (bwd_scans_kernel<T, VB, MODE_STATE, MODE_OUT>), dim3(2 * n1),
-               dim3(256), st, sa, da, (int)n1);
+    GDR_LAUNCH("bwd_scans", (bwd_scans_kernel<T, VB, MODE_STATE, MODE_OUT>), grid, dim3(256), st,
+               sa, da, (int)n1);
 }
 
 template <typename T>
 static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                                const void* v, const float* gcum, const void* graw,
                                const void* beta, const void* A, const void* dO, const float* dht,
-                               const float* h0, void* dq, void* dk, void* dv, void* dbeta,
-                               void* dg, float* dh0, float* dA_log, float* ddt_bias, char* ws,
-                               hipStream_t st) {
-  const BwdLayout L = bwd_layout(p, pl);
+                               const float* h0, const void* hstates, void* dq, void* dk,
+                               void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
+                               float* ddt_bias, char* ws, hipStream_t st) {
+  const bool states_given = hstates != nullptr;
+  const BwdLayout L = bwd_layout(p, pl, states_given);
   const int32_t* offs = nullptr;
   if (p->cu_seqlens_dev) {
     int32_t* o32 = reinterpret_cast<int32_t*>(ws + L.offs);
@@ -1532,9 +1537,9 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
     cp2_out = reinterpret_cast<float*>(ws + L.cp2);
     cp2_start = reinterpret_cast<float*>(ws + L.cp2 + so);
   }
-  void* hbuf = ws + L.h;
+  void* hbuf = states_given ? const_cast<void*>(hstates) : (void*)(ws + L.h);
   void* dhbuf = ws + L.dh;
-  // B1: chunk-start states (value-major)
+  // B1: chunk-start states (packed)
   ScanArgs sa;
   memset(&sa, 0, sizeof(sa));
   sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
@@ -1545,7 +1550,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   sa.qk_norm = p->use_qk_l2norm ? 1 : 0;
   sa.beta_mode = (p->beta_sigmoid ? 1 : 0) | (p->neg_eigval ? 2 : 0);
   sa.seg_out = cp_out; sa.seg_start = cp_start; sa.reverse = 0;
-  // B2: state gradients (value-major)
+  // B2: state gradients (packed)
   DhArgs da;
   da.q = q; da.k = k; da.dO = dO; da.beta = beta; da.gcum = gcum; da.A = A; da.dht = dht;
   da.dh = dhbuf; da.dh0 = dh0; da.seg_start = cp2_start; da.seg_out = cp2_out;
@@ -1553,8 +1558,8 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   da.N = pl.N; da.T = p->T; da.Hq = p->Hq; da.Hv = p->Hv; da.nc_dense = pl.nc_dense;
   da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf; da.qk_norm = sa.qk_norm;
   da.beta_mode = sa.beta_mode;
-  if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, st);
-  else launch_bwd_scans<T, 1>(pl, sa, da, st);
+  if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, states_given, st);
+  else launch_bwd_scans<T, 1>(pl, sa, da, states_given, st);
   // B3-B5
   const bool partial = p->Hq != p->Hv;
   GradArgs ga;
@@ -1603,15 +1608,15 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
 
 gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const float* gcum, const void* graw, const void* beta,
-                      const void* A, const void* dO, const float* dht, const float* h0, void* dq,
-                      void* dk, void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
-                      float* ddt_bias, void* ws, hipStream_t st) {
+                      const void* A, const void* dO, const float* dht, const float* h0,
+                      const void* hstates, void* dq, void* dk, void* dv, void* dbeta, void* dg,
+                      float* dh0, float* dA_log, float* ddt_bias, void* ws, hipStream_t st) {
   char* w = reinterpret_cast<char*>(ws);
   if (p->in_dtype == GDR_BF16)
-    return launch_bwd_t<__bf16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, dq, dk, dv,
-                                dbeta, dg, dh0, dA_log, ddt_bias, w, st);
-  return launch_bwd_t<_Float16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, dq, dk, dv,
-                                dbeta, dg, dh0, dA_log, ddt_bias, w, st);
+    return launch_bwd_t<__bf16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, hstates, dq,
+                                dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st);
+  return launch_bwd_t<_Float16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, hstates, dq,
+                                dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st);
 }
 
 }  // namespace gdr

@@ -240,6 +240,21 @@ __device__ __forceinline__ f32x4 frag_d4_q(const T* X, int row0, int col0) {
   return f32x4{to_f(v[0]), to_f(v[1]), to_f(v[2]), to_f(v[3])};
 }
 
+// ---- packed states ------------------------------------------------------------
+// The chunk-start states the forward keeps for the backward, the backward's
+// recomputed states and its chunk end-state gradients are stored the way the
+// scans hold them: per (chunk, value head) the 128 x 128 values as
+// [V/16][K/32][64 lanes][8], where lane (grp, col) of block (vb, kb2) holds
+// value column 16 vb + col at keys 32 kb2 + 4 grp + e (e < 4) and
+// 32 kb2 + 16 + 4 grp + e - 4 (e >= 4): the split-order MFMA operand of the
+// 32 x 16 block.  A wave stores a block as 64 x 16 contiguous bytes (with
+// 8-byte pieces of value-major rows, the same bytes cost several times more).
+// The 64-column half starting at value v0 is then the 16 KiB starting at
+// element v0 * 128, as in a value-major layout.
+__device__ __forceinline__ int packed_off(int vb, int kb2, int lane) {
+  return ((vb * 4 + kb2) * 64 + lane) * 8;
+}
+
 // Register-staged tile copies, split in two so that the global loads of the
 // next chunk can be in flight while the current chunk computes.  A 64-row
 // tile of COLS elements is NT-thread cooperative; thread t holds 16-byte
@@ -318,6 +333,22 @@ __device__ __forceinline__ void tile_store_q(T* lds, const TileRegs<128, NT>& t,
   for (int i = 0; i < TileRegs<128, NT>::N; ++i) {
     const int x = t0 + i * NT;
     *reinterpret_cast<uint4*>(lds + qk_row(x >> 4) + 8 * (x & 15)) = t.r[i];
+  }
+}
+
+// Store 64 value columns of a packed state (64 x 128, loaded 16 bytes per
+// piece in storage order, piece x = t0 + i * NT) into a staggered LDS tile of
+// value-major rows (row = value column, qk_row).
+template <typename T, int NT>
+__device__ __forceinline__ void tile_store_packed_q(T* lds, const TileRegs<128, NT>& t,
+                                                    int t0 = threadIdx.x) {
+#pragma unroll
+  for (int i = 0; i < TileRegs<128, NT>::N; ++i) {
+    const int x = t0 + i * NT;
+    const int ln = x & 63, kb2 = (x >> 6) & 3, vbl = x >> 8;
+    T* p = lds + qk_row(16 * vbl + (ln & 15)) + 32 * kb2 + 4 * (ln >> 4);
+    *reinterpret_cast<uint2*>(p) = make_uint2(t.r[i].x, t.r[i].y);
+    *reinterpret_cast<uint2*>(p + 16) = make_uint2(t.r[i].z, t.r[i].w);
   }
 }
 

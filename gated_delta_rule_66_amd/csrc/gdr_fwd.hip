@@ -275,7 +275,9 @@ static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st)
   // output pass splits the value columns in four (two state waves each), so
   // the idle CUs take half of every workgroup's output work.
   const bool narrow = units * pl.cp * 2 <= 128;
-  if (mode == MODE_OUT && a.h)
+  // packed h is stored by the output waves of the wave-specialized pass from
+  // the state waves' operand copies; the user layouts by the 4-wave pass
+  if (mode == MODE_OUT && a.h && (VB == 2 || !a.h_vm))
     GDR_LAUNCH("scan_out", (scan_kernel<T, VB, MODE_OUT_H>), grid, dim3(256), st, a);
   else if (mode == MODE_OUT && VB == 1 && narrow) {
     a.nvs = 4;
@@ -337,7 +339,9 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   sa.cu = p->cu_seqlens_dev; sa.offs = offs;
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1;
-  sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf; sa.qk_norm = fa.qk_norm;
+  sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf;
+  sa.h_vm = p->h_packed ? 1 : 0;
+  sa.qk_norm = fa.qk_norm;
   sa.beta_mode = fa.beta_mode;
   sa.seg_out = nullptr; sa.seg_start = nullptr;
   sa.reverse = 0;

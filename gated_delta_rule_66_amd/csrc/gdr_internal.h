@@ -36,7 +36,8 @@ constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 constexpr int kMaxDevices = 64;
 gdr_status noalloc_scratch(void** out);
 size_t cp_workspace_bytes(const Plan& pl, int Hv);
-size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl);
+// states_given: the forward's chunk-start states are an input (no state scan)
+size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl, bool states_given);
 
 gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const void* g, const void* beta, const float* h0,
@@ -44,11 +45,13 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
                       hipStream_t st);
 
 // graw: the gate input (use_gate only, else NULL); dA_log, ddt_bias nullable.
+// hstates: the forward's chunk-start states in the packed layout, or
+// NULL to recompute them.
 gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const float* gcum, const void* graw, const void* beta,
-                      const void* A, const void* dO, const float* dht, const float* h0, void* dq,
-                      void* dk, void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
-                      float* ddt_bias, void* ws, hipStream_t st);
+                      const void* A, const void* dO, const float* dht, const float* h0,
+                      const void* hstates, void* dq, void* dk, void* dv, void* dbeta, void* dg,
+                      float* dh0, float* dA_log, float* ddt_bias, void* ws, hipStream_t st);
 
 // Token-by-token recurrence (decode and other short inputs), no workspace.
 gdr_status launch_recurrent(const gdr_problem* p, const void* q, const void* k, const void* v,

@@ -69,6 +69,10 @@ struct ScanArgs {
   float scale;
   int svf;     // layout of h0 / ht / user h
   int h_svf;   // layout of h: the user's h follows svf; MODE_STATE always writes [V][K]
+  int h_vm;    // h in the packed layout (packed_off) whatever svf says: the
+               // states the forward keeps for the backward.  The output pass's
+               // launch choice follows this, never svf, so both state layouts
+               // run the same kernel.
   int reverse; // cp_combine_kernel: chain segments backwards (state gradients)
   int qk_norm; // q, k rows scaled to unit length before use
   int beta_mode; // bit 0 sigmoid of a beta logit, bit 1 twice beta
@@ -223,7 +227,19 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
     // keys of one value column are 8 contiguous bytes, stored straight from
     // registers.  Key-major ([K][V]): staged in LDS for 16-byte row stores.
     if (HOUT) {
-      if (MODE == MODE_STATE || a.h_svf) {
+      if (MODE == MODE_STATE || a.h_vm) {
+        // packed: one 16-byte operand fragment per lane and block
+        const __amdgpu_buffer_rsrc_t hrs =
+            buf_rsrc(reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb) {
+            const typename VT<T>::x8 f = pack_split<T>(S[2 * kb2][vb], S[2 * kb2 + 1][vb]);
+            buf_store16(hrs, packed_off((cb0 + cw0) / 16 + vb, kb2, l) * (int)sizeof(T),
+                        __builtin_bit_cast(uint4, f));
+          }
+      } else if (a.h_svf) {
         const __amdgpu_buffer_rsrc_t hrs =
             buf_rsrc(reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
 #pragma unroll
@@ -453,7 +469,8 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
 //
 // MODE_STATE (the backward's chunk-start states) uses the same split with
 // waves 4-7 only loading and storing the chunk tiles, and the state waves
-// writing h (value-major) straight from registers.  OPT (template flags, so
+// writing h (packed) straight from registers; the output pass writes packed h
+// from the operand copies when asked for it.  OPT (template flags, so
 // the default path carries none of their code): bit 0 normalises the q / k
 // rows after their loads, bit 1 maps beta through the runtime beta options.
 template <typename T, int MODE, int OPT, int NCW = 4>
@@ -575,6 +592,23 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
       }
     }
     __syncthreads();
+    if (OUT && outw && a.h != nullptr && it > sr.c0) {
+      // chunk-start state of chunk it-1 out, packed (the output pass writes
+      // h only in that layout), from the state waves' operand copy.  Issued
+      // before the prefetch, so the wait for the prefetched tiles does not
+      // also wait for these stores.
+      const int c = it - 1, bo = c & 1;
+      constexpr int KPW = 4 * NCW / 4;  // k blocks per output wave
+      const int cbk = wq % NCW;
+      const __amdgpu_buffer_rsrc_t hrs = buf_rsrc(
+          reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
+#pragma unroll
+      for (int j = 0; j < KPW; ++j) {
+        const int kb2 = (wq / NCW) * KPW + j;
+        buf_store16(hrs, packed_off(cb0 / 16 + cbk, kb2, l) * (int)sizeof(T),
+                    __builtin_bit_cast(uint4, Xs[bo][cbk][kb2][l]));
+      }
+    }
     if (outw && it + 1 < sr.c1) prefetch(it + 1);
 
     if (!outw) {
@@ -587,17 +621,13 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
           if (OUT) Xs[b][wq][kb2][l] = Sb[kb2];
         }
         if (MODE == MODE_STATE) {
-          // chunk-start state out, value-major: a lane's four consecutive keys
-          // of one value column are 8 contiguous bytes
+          // chunk-start state out, packed: the operand fragments just formed
           const __amdgpu_buffer_rsrc_t hrs = buf_rsrc(
               reinterpret_cast<T*>(a.h) + ((choff + it) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
-          const int vc = cb0 + cw0 + col;
 #pragma unroll
-          for (int kb = 0; kb < 8; ++kb) {
-            const typename VT<T>::x4 hv{from_f<T>(S[kb][0]), from_f<T>(S[kb][1]), from_f<T>(S[kb][2]),
-                                        from_f<T>(S[kb][3])};
-            buf_store8(hrs, (vc * kDim + 16 * kb + 4 * grp) * (int)sizeof(T), __builtin_bit_cast(u32x2, hv));
-          }
+          for (int kb2 = 0; kb2 < 4; ++kb2)
+            buf_store16(hrs, packed_off((cb0 + cw0) / 16, kb2, l) * (int)sizeof(T),
+                        __builtin_bit_cast(uint4, Sb[kb2]));
         }
         // K S
         f32x4 ks[4];

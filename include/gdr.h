@@ -125,6 +125,12 @@ typedef struct {
   const float* gate_A_log;        /* device [Hv] fp32: required iff use_gate */
   const float* gate_dt_bias;      /* device [Hv] fp32, or NULL for a zero bias;
                                      NULL unless use_gate */
+  int32_t h_packed;               /* 1: gdr_chunk_fwd writes the chunk-start
+                                     states h in the packed layout that
+                                     gdr_chunk_bwd_states reads (below),
+                                     whatever state_v_first says; 0: h is
+                                     [NC, Hv, K, V] (or [NC, Hv, V, K] with
+                                     state_v_first) */
 } gdr_problem;
 
 /* Status name ("GDR_ERR_SHAPE", ...). */
@@ -142,10 +148,12 @@ gdr_status gdr_check_supported(const gdr_problem* p, char* reason, size_t reason
 /* Device check: the current HIP device is a gfx950.  GDR_ERR_DEVICE if not. */
 gdr_status gdr_check_device(void);
 
-/* Bytes of device workspace gdr_chunk_fwd / gdr_chunk_bwd need for `p`
- * (0 if `p` is invalid).  Depends only on the problem's shapes. */
+/* Bytes of device workspace gdr_chunk_fwd / gdr_chunk_bwd (and
+ * gdr_chunk_bwd_gate) / gdr_chunk_bwd_states need for `p` (0 if `p` is
+ * invalid).  Depends only on the problem's shapes. */
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p);
 size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p);
+size_t gdr_chunk_bwd_states_workspace_size(const gdr_problem* p);
 
 /* Forward ("flashqla-linear-attention", Low-Level API; "FlashQLA
  * Documentation", forward pass returning g, A, o, h, final_state).
@@ -209,6 +217,32 @@ gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k
                               void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
                               float* dA_log, float* ddt_bias, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* Backward given the forward's chunk-start states: the backward the pages'
+ * autograd integration ("flashqla-linear-attention", Integration with
+ * PyTorch Autograd) runs after a forward that kept its states.  The
+ * arguments and results of gdr_chunk_bwd (gdr_chunk_bwd_gate when
+ * p->use_gate), plus:
+ *   in : h, the chunk-start states gdr_chunk_fwd computed for the same
+ *        problem and inputs with h_packed = 1: per chunk row and value head
+ *        the 128 x 128 state in in_dtype as [V/16][K/32][64][8]: element
+ *        ((vb * 4 + kb) * 64 + 16 * g + c) * 8 + e holds the state at value
+ *        16 vb + c and key 32 kb + 4 g + e (e < 4), 32 kb + 16 + 4 g + e - 4
+ *        (e >= 4) -- the order the kernels hold it in, so that it is written
+ *        and read in 1 KiB contiguous pieces
+ *        g, the gate's raw input (use_gate only; NULL otherwise, and so are
+ *        dA_log, ddt_bias)
+ * The states are not recomputed: only the reverse state-gradient scan runs
+ * before the per-chunk gradients, and the workspace
+ * (gdr_chunk_bwd_states_workspace_size) holds no state buffer.  States from
+ * another problem or other inputs give meaningless gradients. */
+gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void* k,
+                                const void* v, const float* g_cum, const void* g,
+                                const void* beta, const void* A, const void* do_,
+                                const float* dht, const float* initial_state, const void* h,
+                                void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
+                                float* dA_log, float* ddt_bias, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Token-by-token forward for short inputs: decode steps, a few speculative
  * tokens, or a prefill continued from a cached state (the "state-cached

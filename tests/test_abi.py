@@ -306,3 +306,22 @@ def test_no_alloc_forward_rejects_problems_past_its_scratch_before_device_work()
     # one long sequence fits (48 MiB of segment buffers)
     one = good(B=1, N=1, T=65536, Hq=32, Hv=32, cp_segments=8)
     assert 0 < lib.gdr_chunk_fwd_workspace_size(ctypes.byref(one)) <= (64 << 20)
+
+
+def test_unpack_states_follows_the_packed_layout():
+    """unpack_states against the packed layout the header states, element by
+    element: ((vb * 4 + kb) * 64 + 16 g + c) * 8 + e holds value 16 vb + c at
+    key 32 kb + 4 g + e (e < 4) or 32 kb + 16 + 4 g + e - 4 (e >= 4)."""
+    import gated_delta_rule_66_amd as gdr
+    kv = torch.arange(128 * 128, dtype=torch.float64).reshape(128, 128)  # [key][value]
+    packed = torch.empty(128 * 128, dtype=torch.float64)
+    for vb in range(8):
+        for kb in range(4):
+            for g in range(4):
+                for c in range(16):
+                    for e in range(8):
+                        key = 32 * kb + 4 * g + e if e < 4 else 32 * kb + 16 + 4 * g + e - 4
+                        packed[((vb * 4 + kb) * 64 + 16 * g + c) * 8 + e] = kv[key, 16 * vb + c]
+    out = gdr.unpack_states(packed.reshape(1, 1, -1).repeat(2, 3, 1))
+    assert out.shape == (2, 3, 128, 128)
+    assert torch.equal(out[1, 2], kv)

@@ -129,3 +129,56 @@ def test_backward_scan_variants(name, vt, cp):
     ref = oracle_grads(d)
     for n, kind, x, r in zip(NAMES, KINDS, g, ref):
         check(n, x, r, kind, d["cu_seqlens"])
+
+
+def gpu_fwd_bwd_states(d, cp=0):
+    """The autograd path: the forward keeps its chunk-start states
+    (value-major) and the backward takes them instead of recomputing."""
+    import gated_delta_rule_66_amd as gdr
+    dd = to_dev(d)
+    cu_cpu = d["cu_seqlens"]
+    g_cum, A, o, h, ht = gdr.chunk_gated_delta_rule_fwd(
+        dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
+        initial_state=dd["h0"], output_final_state=True, cu_seqlens=dd["cu_seqlens"],
+        cp_segments=cp, cu_seqlens_cpu=cu_cpu, output_h=True, h_packed=True)
+    grads = gdr.chunk_gated_delta_rule_bwd(
+        dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dd["dht"],
+        scale=dd["scale"], initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
+        dg_dtype=dd["g"].dtype, cp_segments=cp, cu_seqlens_cpu=cu_cpu, h=h)
+    torch.cuda.synchronize()
+    return h, grads
+
+
+@pytest.mark.parametrize("name,cp", [("dense_state_dht", 1), ("varlen", 1), ("fp16_gva", 1),
+                                     ("varlen_empty_seq", 1), ("gva_group3", 1),
+                                     ("long_slow_decay", 4), ("varlen", 3)])
+def test_backward_from_the_forward_states(name, cp):
+    d = gdr_synth.make(CASES[name])
+    print("case", name, "cp", cp, flush=True)
+    h, g = gpu_fwd_bwd_states(d, cp=cp)
+    ref = oracle_grads(d)
+    for nm, kind, x, r in zip(NAMES, KINDS, g, ref):
+        check(nm, x, r, kind, d["cu_seqlens"])
+    # the same scans produce the same states: with one plan for both passes
+    # the gradients are those of the recomputing backward, bit for bit
+    if cp == 1:
+        _, _, g2 = gpu_fwd_bwd(d, cp=1)
+        for nm, x, y in zip(NAMES, g, g2):
+            assert (x is None and y is None) or torch.equal(x, y), nm
+
+
+def test_packed_h_holds_the_default_states():
+    import gated_delta_rule_66_amd as gdr
+    d = gdr_synth.make(CASES["varlen"])
+    dd = to_dev(d)
+    kw = dict(scale=dd["scale"], initial_state=dd["h0"], output_final_state=True,
+              cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=d["cu_seqlens"], output_h=True)
+    a = gdr.chunk_gated_delta_rule_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], **kw)
+    b = gdr.chunk_gated_delta_rule_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"],
+                                       h_packed=True, **kw)
+    torch.cuda.synchronize()
+    # the same states, rounded the same way, in another order
+    assert torch.equal(gdr.unpack_states(b[3]), a[3])
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    check("o", b[2], np64(a[2]), "tok", d["cu_seqlens"])
+    assert torch.equal(a[4], b[4])
