@@ -76,7 +76,8 @@ static gdr_status fail(gdr_status s, char* reason, size_t len, const char* fmt, 
 //   backward output pass (state and state-gradient scans in one launch):
 //     state scan 2.4 / 5.5 and state-gradient scan 3.3 / 5.5; the launch
 //     takes the longer of its total work spread over the CUs and one
-//     state-gradient chain,
+//     state-gradient chain (no state scan when the forward's states are
+//     given),
 //   backward transition pass 4.5 / 4.2,
 // one combine step 10 per scan, and 16 for the two extra launches of a split.
 static double rounds(int64_t wgs, int64_t slots) {
@@ -84,14 +85,15 @@ static double rounds(int64_t wgs, int64_t slots) {
   return r < 1 ? 1.0 : (double)r;
 }
 
-static double bwd_out_cost(int64_t wgs_per_scan, int64_t chunks, int VB) {
-  const double c1 = VB == 1 ? 2.4 : 5.5, c2 = VB == 1 ? 3.3 : 5.5;
+static double bwd_out_cost(int64_t wgs_per_scan, int64_t chunks, int VB, bool states_given) {
+  // with the forward's states given only the state-gradient scan runs
+  const double c1 = states_given ? 0.0 : (VB == 1 ? 2.4 : 5.5), c2 = VB == 1 ? 3.3 : 5.5;
   const double spread = (double)wgs_per_scan * (double)chunks * (c1 + c2) / 256.0;
   const double chain = (double)chunks * c2;
   return spread > chain ? spread : chain;
 }
 
-static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd) {
+static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd, bool states_given) {
   const int64_t nvs0 = 2 / VB, nvs1 = 4 / VB;
   if (!bwd) {
     const bool narrow = VB == 1 && units * P * 2 <= 128;
@@ -104,18 +106,18 @@ static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd) {
     return (double)sc * aug * rounds(wg_aug, VB == 1 ? 512 : 256) + 10.0 * (double)(P - 1) + 16.0 +
            (double)sc * out * rounds(units * P * nvs0, 256);
   }
-  if (P == 1) return bwd_out_cost(units * nvs0, maxch, VB);
+  if (P == 1) return bwd_out_cost(units * nvs0, maxch, VB, states_given);
   const int64_t sc = (maxch + P - 1) / P;
-  const int64_t wg_aug = 2 * units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
+  const int64_t wg_aug = (states_given ? 1 : 2) * units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
   const double aug = VB == 1 ? 4.5 : 4.2;
-  return (double)sc * aug * rounds(wg_aug, 256) + 20.0 * (double)(P - 1) + 16.0 +
-         bwd_out_cost(units * P * nvs0, sc, VB);
+  return (double)sc * aug * rounds(wg_aug, 256) + (states_given ? 10.0 : 20.0) * (double)(P - 1) +
+         16.0 + bwd_out_cost(units * P * nvs0, sc, VB, states_given);
 }
 
 // Context-parallel plan along T for one direction: it depends only on shapes
 // (never on data), so every run of a problem, in either state layout, takes
 // the same path.
-Plan make_plan(const gdr_problem* p, bool bwd) {
+Plan make_plan(const gdr_problem* p, bool bwd, bool states_given) {
   Plan pl;
   pl.N = p->N;
   pl.total_chunks = 0;
@@ -148,7 +150,8 @@ Plan make_plan(const gdr_problem* p, bool bwd) {
       // state chain (measured 681 -> 964 us for one T=65536 sequence)
       if (!bwd && p->h_packed && p->wave_tiles == 0 && VB == 2) continue;
       // a split must win clearly: the model is coarse and splitting adds work
-      const double c = plan_cost(units, maxch, P, VB, bwd) * ((P > 1 && fixed == 0) ? 1.1 : 1.0);
+      const double c = plan_cost(units, maxch, P, VB, bwd, states_given) *
+                       ((P > 1 && fixed == 0) ? 1.1 : 1.0);
       if (c < best) {
         best = c;
         pl.cp = P;
@@ -379,7 +382,7 @@ size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p) {
 
 size_t gdr_chunk_bwd_states_workspace_size(const gdr_problem* p) {
   if (validate(p, nullptr, 0) != GDR_OK) return 0;
-  return bwd_workspace_bytes(p, make_plan(p, true), true);
+  return bwd_workspace_bytes(p, make_plan(p, true, true), true);
 }
 
 gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -437,7 +440,7 @@ static gdr_status chunk_bwd(const gdr_problem* p, const void* q, const void* k, 
     return fail(GDR_ERR_NULL, nullptr, 0, "a required backward pointer is NULL");
   if (initial_state && !dh0)
     return fail(GDR_ERR_NULL, nullptr, 0, "dh0 is required when initial_state is given");
-  const Plan pl = make_plan(p, true);
+  const Plan pl = make_plan(p, true, hstates != nullptr);
   const size_t need = bwd_workspace_bytes(p, pl, hstates != nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDR_ERR_WORKSPACE, nullptr, 0, "backward workspace needs %zu bytes, got %zu",
@@ -512,7 +515,9 @@ gdr_status gdr_plan_info(const gdr_problem* p, int backward, int32_t* cp_segment
                          int32_t* wave_tiles) {
   gdr_status s = validate(p, nullptr, 0);
   if (s != GDR_OK) return s;
-  const Plan pl = make_plan(p, backward != 0);
+  // the backward of a forward that kept packed states takes them (no
+  // recompute), which changes its plan
+  const Plan pl = make_plan(p, backward != 0, backward != 0 && p->h_packed != 0);
   if (cp_segments) *cp_segments = pl.cp;
   if (wave_tiles) *wave_tiles = pl.vb;
   return GDR_OK;

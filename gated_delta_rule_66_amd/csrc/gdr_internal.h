@@ -22,7 +22,8 @@ struct Plan {
   int vb;             // 16-column MFMA tiles per wave in the scans (1 or 2)
 };
 
-Plan make_plan(const gdr_problem* p, bool bwd);
+// states_given: the backward takes the forward's chunk states (no state scan)
+Plan make_plan(const gdr_problem* p, bool bwd, bool states_given = false);
 
 // Workspace layout helpers: every region is 256-byte aligned.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -300,7 +300,8 @@ gdr_status gdr_prepare_chunk_token_starts_i64(const int64_t* cu, int64_t n_plus_
                                               int64_t* num_chunks);
 
 /* The launch plan the library picks for `p` in one direction (backward != 0:
- * gdr_chunk_bwd, else gdr_chunk_fwd); it depends only on shapes:
+ * gdr_chunk_bwd, or gdr_chunk_bwd_states when p->h_packed; else
+ * gdr_chunk_fwd); it depends only on shapes and those flags:
  * *cp_segments = T-segments per sequence (1 = no context parallelism),
  * *wave_tiles = 16-column state tiles per wave in the scans (1 or 2).
  * A nonzero cp_segments / wave_tiles in `p` fixes that choice for both. */
