@@ -23,7 +23,8 @@
 //       dg = reverse chunk-local cumsum of dgamma (times the gate's slope when
 //       g is a gate input, with per-chunk shares of the gate parameters'
 //       gradients, summed per head by gate_param_grad_kernel).
-//   B6  gva_reduce: dq, dk summed over the Hv/Hq value heads of a group.
+//   B6  with GVA the gradient kernel's workgroup takes the Hv/Hq value heads of
+//       a q/k head in turn and sums their dq, dk in registers (head order).
 #include "gdr_device.h"
 #include "gdr_internal.h"
 #include "gdr_scan.h"
@@ -707,7 +708,7 @@ struct GradArgs {
   const void* A;
   const void* h;   // [NC, Hv] packed chunk-start states (packed_off)
   const void* dh;  // [NC, Hv] packed end-state gradients
-  void* dq;        // in_dtype [T, Hq, K], or fp32 [T, Hv, K] partials when partial
+  void* dq;        // in_dtype [T, Hq, K]
   void* dk;
   void* dv;
   void* dbeta;
@@ -716,7 +717,8 @@ struct GradArgs {
   const int32_t* offs;
   int N, T, Hq, Hv, nc_dense, g_dtype;
   float scale;
-  int partial;
+  float* gacc;    // GVA: [G - 1 heads][NC, Hq, 8 waves, 8, 64 lanes, 4] fp32 dq / dk rows
+  int gva_final;  // GVA: 0 the launch of heads 0 .. G-2, 1 the launch of head G-1
   int qk_norm;    // q, k rows scaled to unit length before use
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
   // the gate (use_gate): g is the gate input graw, dg is with respect to it,
@@ -734,7 +736,12 @@ struct GradArgs {
 // (K dSn, dDelta, dR, dX = -dR S^T, dKs = Delta dSn^T, dM and everything of
 // dk).  The two sides of a phase are independent, so two waves share each
 // SIMD and hide each other's latencies.
-template <typename T, bool QKN>
+// A workgroup takes one (chunk, value head).  With GVA (Hq < Hv) the kernel
+// runs twice: the first launch takes value heads 0 .. G-2 of every group and
+// leaves each head's dq, dk contribution in its fp32 workspace slot; the
+// second takes head G-1, adds the slots in head order to its own
+// contribution and stores dq, dk (the kernel boundary orders the two).
+template <typename T, bool QKN, bool GVA>
 __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   typedef typename VT<T>::x8 x8;
   constexpr int LD = 136;  // row stride of the dq / dk staging in Ss / Gs_
@@ -766,7 +773,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   // the P tile's storage (dead once the value halves are done)
   float* const rowv = reinterpret_cast<float*>(Ps);
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int c = blockIdx.x;
   int n, j;
   if (a.cu) {
     n = find_seq(a.offs, a.N, c);
@@ -778,13 +785,17 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   const SeqInfo s = seq_info(a.cu, n, a.T);
   const int64_t t0 = s.start + (int64_t)kChunk * j;
   const int Cc = (int)min((int64_t)kChunk, s.end - t0);
-  const int G = a.Hv / a.Hq, hq = h / G;
+  const int G = a.Hv / a.Hq;
+  // GVA: the first launch has (G - 1) x Hq rows of workgroups (head r of
+  // group hq at row hq * (G - 1) + r), the second (gva_final) Hq rows
+  const int hq = !GVA ? (int)blockIdx.y / G : a.gva_final ? (int)blockIdx.y : (int)blockIdx.y / (G - 1);
+  const int gr = !GVA ? 0 : a.gva_final ? G - 1 : (int)blockIdx.y % (G - 1);
+  const int h = GVA ? hq * G + gr : (int)blockIdx.y;
+  const bool store_dqk = !GVA || a.gva_final;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const int wr = w & 3;
   const bool hi = w >= 4;
   const int64_t KV = (int64_t)kDim * kDim;
-  const T* hS = reinterpret_cast<const T*>(a.h) + ((int64_t)c * a.Hv + h) * KV;
-  const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)c * a.Hv + h) * KV;
   const T* vv = reinterpret_cast<const T*>(a.v);
   const T* dOg = reinterpret_cast<const T*>(a.dO);
 
@@ -793,6 +804,8 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   TileRegs<128, 512> rs, rg;
   TileRegs<64, 512> rv, ro;
   auto load_half = [&](int v0) {
+    const T* hS = reinterpret_cast<const T*>(a.h) + ((int64_t)c * a.Hv + h) * KV;
+    const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)c * a.Hv + h) * KV;
     tile_load<T, 128, 512>(rs, hS + v0 * kDim, kDim, 64);
     tile_load<T, 128, 512>(rg, hG + v0 * kDim, kDim, 64);
     tile_load<T, 64, 512>(rv, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
@@ -1200,11 +1213,31 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       }
     }
   }
+  // GVA: the group sum over the value heads, in head order.  Each head but
+  // the last leaves its rows in its fp32 workspace slot (register order:
+  // element kb of lane l at float4 kb * 64 + l, so each store is 1 KiB
+  // contiguous); the last adds the slots, head 0 first, to its own rows.
+  if (GVA) {
+    const int64_t slot = (int64_t)gridDim.x * a.Hq * 8 * 512;  // float4s per head slot
+    f32x4* acc = reinterpret_cast<f32x4*>(a.gacc) + (((int64_t)c * a.Hq + hq) * 8 + w) * 512 + l;
+    if (a.gva_final) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        f32x4 sum = acc[kb * 64];
+        for (int rr = 1; rr < G - 1; ++rr) sum += acc[rr * slot + kb * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dxv[kb][e] = sum[e] + dxv[kb][e];
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        acc[gr * slot + kb * 64] = f32x4{dxv[kb][0], dxv[kb][1], dxv[kb][2], dxv[kb][3]};
+    }
+  }
   // With q / k normalisation dxv is the gradient with respect to the unit
   // rows x^ (q^ on side 0, k^ on side 1); the raw rows' gradient is
-  // (dxv - x^ (x^ . dxv)) / |x|.  With value-head partials (Hq < Hv) the
-  // group sum comes first, so that step runs in gva_reduce_kernel.
-  if (QKN && !a.partial) {
+  // (dxv - x^ (x^ . dxv)) / |x| (on the group sum: the map is linear).
+  if (QKN && store_dqk) {
     const T* X = hi ? Ks : Qs;
     float dot[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1259,20 +1292,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       }
     }
   }
-  // dq (side 0) / dk (side 1) rows: fp32 partials straight from registers, or
-  // staged row-major in the free S / dSn tiles for 16-byte stores
-  if (a.partial) {
-    float* dst = reinterpret_cast<float*>(hi ? a.dk : a.dq);
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * wr + 4 * grp + e, key = 16 * kb + col;
-        if (r < Cc) dst[((t0 + r) * a.Hv + h) * kDim + key] = dxv[kb][e];
-      }
-  }
   __syncthreads();  // every wave is done with DMs, T1s, dAs; rowq and fsum are in
-  if (!a.partial) {
+  // dq (side 0) / dk (side 1) rows, once the group sum is whole: staged
+  // row-major in the free S / dSn tiles for 16-byte stores
+  if (store_dqk) {
     T* stage = hi ? Gs_ : Ss;
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
@@ -1297,7 +1320,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
     if (r < Cc) reinterpret_cast<T*>(a.dbeta)[(t0 + r) * a.Hv + h] = from_f<T>(db * dbf[r]);
   }
   __syncthreads();
-  if (!a.partial) {
+  if (store_dqk) {
     tile_from_lds<T, 128, 512>(reinterpret_cast<T*>(a.dq) + (t0 * a.Hq + hq) * kDim,
                                (int64_t)a.Hq * kDim, Ss, LD, Cc);
     tile_from_lds<T, 128, 512>(reinterpret_cast<T*>(a.dk) + (t0 * a.Hq + hq) * kDim,
@@ -1353,71 +1376,11 @@ __global__ __launch_bounds__(256) void gate_param_grad_kernel(const float* gpart
   }
 }
 
-// B6: dq[t, hq] = sum over the group's value heads, in head order, and the
-// same for dk.  Sixteen consecutive lanes take one (token, q head) row, eight
-// keys each.  With q / k normalisation the sum is the gradient with respect
-// to the unit row x^ = x / |x| (|x| = sqrt(sum x^2 + eps), recomputed from the
-// raw row in fp32) and the raw row's gradient is (d - x^ (x^ . d)) / |x|.
-template <typename T>
-__device__ __forceinline__ void gva_row_out(const float* part, const T* x, T* out, int64_t t,
-                                            int hq, int Hq, int Hv, int key0, int qk_norm) {
-  const int G = Hv / Hq;
-  float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < G; ++r) {
-    const float* src = part + (t * Hv + (int64_t)hq * G + r) * kDim + key0;
-    const float4 lo = *reinterpret_cast<const float4*>(src);
-    const float4 hi = *reinterpret_cast<const float4*>(src + 4);
-    d[0] += lo.x; d[1] += lo.y; d[2] += lo.z; d[3] += lo.w;
-    d[4] += hi.x; d[5] += hi.y; d[6] += hi.z; d[7] += hi.w;
-  }
-  const int64_t row = (t * Hq + hq) * kDim + key0;
-  if (qk_norm) {
-    const typename VT<T>::x8 xv = *reinterpret_cast<const typename VT<T>::x8*>(x + row);
-    float f[8], ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      f[e] = to_f(xv[e]);
-      ss += f[e] * f[e];
-    }
-    const float ri = rsqrtf(sum16(ss) + kQKNormEps);
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      f[e] *= ri;
-      dot += f[e] * d[e];
-    }
-    dot = sum16(dot);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = ri * (d[e] - f[e] * dot);
-  }
-  typename VT<T>::x8 o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = from_f<T>(d[e]);
-  *reinterpret_cast<typename VT<T>::x8*>(out + row) = o;
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void gva_reduce_kernel(const float* pq, const float* pk,
-                                                         const T* q, const T* k, T* dq, T* dk,
-                                                         int64_t Ttot, int Hq, int Hv,
-                                                         int qk_norm) {
-  const int64_t rows = Ttot * Hq;
-  const int key0 = 8 * (threadIdx.x & 15);
-  // the 16 lanes of a row share the loop bounds, so the row sums stay whole
-  for (int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4; row < rows;
-       row += ((int64_t)gridDim.x * blockDim.x) >> 4) {
-    const int hq = (int)(row % Hq);
-    const int64_t t = row / Hq;
-    gva_row_out<T>(pq, q, dq, t, hq, Hq, Hv, key0, qk_norm);
-    gva_row_out<T>(pk, k, dk, t, hq, Hq, Hv, key0, qk_norm);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-  size_t offs, cp, cp2, h, dh, pq, pk, gpart, total;
+  size_t offs, cp, cp2, h, dh, gacc, gpart, total;
 };
 
 static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_given) {
@@ -1435,14 +1398,10 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_gi
   if (!states_given) o += align256(st);
   L.dh = o;
   o += align256(st);
-  L.pq = L.pk = o;
-  if (p->Hq != p->Hv) {
-    const size_t part = (size_t)p->B * p->T * p->Hv * kDim * sizeof(float);
-    L.pq = o;
-    o += align256(part);
-    L.pk = o;
-    o += align256(part);
-  }
+  L.gacc = o;
+  if (p->Hq != p->Hv)
+    o += align256((size_t)(p->Hv / p->Hq - 1) * pl.total_chunks * p->Hq * 8 * 8 * 64 * 4 *
+                  sizeof(float));
   L.gpart = o;
   if (p->use_gate) o += align256((size_t)pl.total_chunks * p->Hv * 2 * sizeof(float));
   L.total = o;
@@ -1560,17 +1519,18 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   da.beta_mode = sa.beta_mode;
   if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, states_given, st);
   else launch_bwd_scans<T, 1>(pl, sa, da, states_given, st);
-  // B3-B5
-  const bool partial = p->Hq != p->Hv;
+  // B3-B6
+  const bool gva = p->Hq != p->Hv;
   GradArgs ga;
   ga.q = q; ga.k = k; ga.v = v; ga.dO = dO; ga.beta = beta; ga.gcum = gcum; ga.A = A;
   ga.h = hbuf; ga.dh = dhbuf;
-  ga.dq = partial ? (void*)(ws + L.pq) : dq;
-  ga.dk = partial ? (void*)(ws + L.pk) : dk;
+  ga.dq = dq;
+  ga.dk = dk;
+  ga.gacc = gva ? reinterpret_cast<float*>(ws + L.gacc) : nullptr;
   ga.dv = dv; ga.dbeta = dbeta; ga.dg = dg;
   ga.cu = p->cu_seqlens_dev; ga.offs = offs;
   ga.N = pl.N; ga.T = p->T; ga.Hq = p->Hq; ga.Hv = p->Hv; ga.nc_dense = pl.nc_dense;
-  ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale; ga.partial = partial ? 1 : 0;
+  ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale;
   ga.qk_norm = sa.qk_norm;
   ga.beta_mode = sa.beta_mode;
   const bool gate = p->use_gate != 0;
@@ -1578,26 +1538,25 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   ga.gate_A_log = gate ? p->gate_A_log : nullptr;
   ga.gate_dt_bias = gate ? p->gate_dt_bias : nullptr;
   ga.gpart = gate ? reinterpret_cast<float*>(ws + L.gpart) : nullptr;
-  if (pl.total_chunks > 0 && ga.qk_norm)
-    GDR_LAUNCH("grad", (grad_kernel<T, true>), dim3((unsigned)pl.total_chunks, p->Hv), dim3(512),
-               st, ga);
-  else if (pl.total_chunks > 0)
-    GDR_LAUNCH("grad", (grad_kernel<T, false>), dim3((unsigned)pl.total_chunks, p->Hv), dim3(512),
-               st, ga);
+  // one workgroup per (chunk, value head); with GVA the heads 0 .. G-2 of
+  // every group first, then the group's last head, which sums dq and dk
+  const unsigned nc = (unsigned)pl.total_chunks;
+  const int G = p->Hv / p->Hq;
+  ga.gva_final = 0;
+  if (pl.total_chunks > 0 && !gva) {
+    if (ga.qk_norm) GDR_LAUNCH("grad", (grad_kernel<T, true, false>), dim3(nc, p->Hv), dim3(512), st, ga);
+    else GDR_LAUNCH("grad", (grad_kernel<T, false, false>), dim3(nc, p->Hv), dim3(512), st, ga);
+  } else if (pl.total_chunks > 0) {
+    for (int fin = 0; fin < 2; ++fin) {
+      ga.gva_final = fin;
+      const dim3 gg(nc, fin ? p->Hq : p->Hq * (G - 1));
+      if (ga.qk_norm) GDR_LAUNCH("grad", (grad_kernel<T, true, true>), gg, dim3(512), st, ga);
+      else GDR_LAUNCH("grad", (grad_kernel<T, false, true>), gg, dim3(512), st, ga);
+    }
+  }
   if (gate && (dA_log || ddt_bias))
     GDR_LAUNCH("gate_param_grad", gate_param_grad_kernel, dim3((unsigned)p->Hv), dim3(256), st,
                ga.gpart, (int64_t)pl.total_chunks, p->Hv, dA_log, ddt_bias);
-  // B6
-  if (partial) {
-    const int64_t Ttot = (int64_t)p->B * p->T;
-    const int64_t threads = Ttot * p->Hq * 16;  // 16 lanes per (token, q head) row
-    const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 8192);
-    GDR_LAUNCH("gva_reduce", gva_reduce_kernel<T>, dim3(blocks), dim3(256), st,
-               reinterpret_cast<const float*>(ws + L.pq), reinterpret_cast<const float*>(ws + L.pk),
-               reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k),
-               reinterpret_cast<T*>(dq), reinterpret_cast<T*>(dk), Ttot, p->Hq, p->Hv,
-               ga.qk_norm);
-  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("backward launch failed: %s", hipGetErrorString(e));
