@@ -754,14 +754,13 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   __shared__ __align__(16) T Gs_[QK_TILE];   // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma, dk
   __shared__ __align__(16) T Vs[64 * L7];
   __shared__ __align__(16) T Os[64 * L7];    // dO[:, half]
-  __shared__ __align__(16) T Rs[64 * L7];    // R, transposed: [v][r]
   __shared__ __align__(16) T Dls[64 * L7];   // Delta, transposed
-  __shared__ __align__(16) T DDs[64 * L7];   // dDelta, transposed
   __shared__ __align__(16) T DRs[64 * L7];   // dR, transposed
   __shared__ __align__(16) T DVs[64 * L7];   // dv of the half, row-major
   __shared__ float gam[64], bet[64], eg[64], bex[64], dl[64];
   __shared__ float dbv[8][64];       // v . dR partials per (half, column block)
-  __shared__ float colE[4][64];      // column sums of dP o P and dM o M per row block
+  __shared__ float colE[4][64];      // column sums of dP o P per row block
+  __shared__ float colE2[4][64];     // column sums of dM o M per row block
   __shared__ float red[8];           // <S, dSn> per wave
   __shared__ float dgam[64];
   __shared__ float fsum[4][4];       // F partials per (row block, lane group)
@@ -907,12 +906,15 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   store_half();
   __syncthreads();
 
-  // accumulators over the value halves: side 0 accA = dA, accB = dP,
-  // acc1 = dQ1; side 1 acc1 = dX, acc2 = dKs
-  f32x4 accA[4], accB[4], acc1[8], acc2[8];
+  // accumulators over the value halves: side 0 accB = dP, acc1 = dQ1;
+  // side 1 accM = dR Delta^T, acc1 = dX, acc2 = dKs.  dR Delta^T is
+  // A^T dA A^T: with Delta = A R and dA = dDelta R^T,
+  // A^T dDelta R^T A^T = (A^T dDelta)(A R)^T = dR Delta^T, so
+  // dM = strict_lower(-dR Delta^T) needs neither dA nor R.
+  f32x4 accM[4], accB[4], acc1[8], acc2[8];
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    accA[x] = zero4();
+    accM[x] = zero4();
     accB[x] = zero4();
   }
 #pragma unroll
@@ -962,7 +964,6 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       for (int tb = 0; tb < 4; ++tb) {
         f32x4 acc = mfma16(frag_row_split(As + 16 * tb * L7, L7), Rb0, zero4());
         if (tb >= 2) acc = mfma16(frag_row_split(As + 16 * tb * L7 + 32, L7), Rb1, acc);
-        store_d4_t<T>(Rs, L7, 16 * tb, cc, R[tb]);
         store_d4_t<T>(Dls, L7, 16 * tb, cc, acc);
       }
     } else {
@@ -1004,7 +1005,6 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
           if (col == 0) dbv[4 * hv + wr][r] = pdot;
           DVs[r * L7 + cc + col] = from_f<T>(bt[e] * dR[e]);
         }
-        store_d4_t<T>(DDs, L7, 16 * tb, cc, dD[tb]);
         store_d4_t<T>(DRs, L7, 16 * tb, cc, dR);
       }
     }
@@ -1016,15 +1016,13 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
 #pragma unroll
     for (int vk = 0; vk < 2; ++vk) {
       if (!hi) {
-        const x8 fdd = frag_tr_split(DDs + 32 * vk * L7 + 16 * wr, L7);
         const x8 fdo = frag_row_split(Os + 16 * wr * L7 + 32 * vk, L7);
+        // all four column blocks: the blocks above the diagonal are masked
+        // by selects later (an MFMA alone under a per-wave condition would
+        // run regardless of EXEC, on operands never loaded)
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-          if (ib <= wr) {
-            accA[ib] = mfma16(fdd, frag_tr_split(Rs + 32 * vk * L7 + 16 * ib, L7), accA[ib]);
-            accB[ib] = mfma16(fdo, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), accB[ib]);
-          }
-        }
+        for (int ib = 0; ib < 4; ++ib)
+          accB[ib] = mfma16(fdo, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), accB[ib]);
         // two rounds of four key blocks, fragments read before the products
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
@@ -1039,6 +1037,10 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       } else {
         const x8 fdr = frag_tr_split(DRs + 32 * vk * L7 + 16 * wr, L7);
         const x8 fdl = frag_tr_split(Dls + 32 * vk * L7 + 16 * wr, L7);
+        // dR Delta^T, all four column blocks (masked by selects later)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+          accM[ib] = mfma16(fdr, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), accM[ib]);
         // four rounds of two key blocks, each round's fragments read before
         // its four independent products issue
 #pragma unroll
@@ -1068,14 +1070,17 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   __syncthreads();
 
   // ---- C x C terms, rows r = 16 wr + 4 grp + e ----
-  T* dAs = Ss;              // bf16 dA (64 x 64)
-  T* T1s = Ss + 64 * L7;    // bf16 A^T dA
+  // side 0: dP (masked, scaled) -> dP o Gamma and the E = dP o P row / column
+  // sums; side 1: dM = strict_lower(-dR Delta^T) -> dM o beta Gamma, the
+  // E2 = dM o M row / column sums and the dbeta row terms (M = beta_r N,
+  // N = (k_r . k_i) Gamma_ri, the side's pn)
   T* dPG = Gs_;             // bf16 dP o Gamma
   T* DMs = Gs_ + 64 * L7;   // bf16 dM o beta Gamma
   float rowacc[4] = {0.f, 0.f, 0.f, 0.f};  // dgamma row terms (E on side 0, E2 on side 1)
   float dbacc[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta row terms (side 1)
-  if (!hi) {
+  {
     const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * wr + 4 * grp);
+    const f32x4 br = *reinterpret_cast<const f32x4*>(bet + 16 * wr + 4 * grp);
     float gis[4];  // gamma of each column block's column, read at once
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) gis[cb] = gam[16 * cb + col];
@@ -1086,37 +1091,37 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * wr + 4 * grp + e, i = 16 * cb + col;
-        const bool keep = i <= r;
-        const float dpv = keep ? a.scale * accB[cb][e] : 0.f;
-        const float E = dpv * pn[cb][e];
-        rowacc[e] += E;
-        cs += E;
-        dPG[r * L7 + i] = from_f<T>(dpv * __expf(keep ? gr[e] - gi : -INFINITY));
-        dAs[r * L7 + i] = from_f<T>(keep ? accA[cb][e] : 0.f);
+        if (!hi) {
+          const bool keep = i <= r;
+          const float dpv = keep ? a.scale * accB[cb][e] : 0.f;
+          const float E = dpv * pn[cb][e];
+          rowacc[e] += E;
+          cs += E;
+          dPG[r * L7 + i] = from_f<T>(dpv * __expf(keep ? gr[e] - gi : -INFINITY));
+        } else {
+          const bool keep = i < r;
+          const float dm = keep ? -accM[cb][e] : 0.f;
+          dbacc[e] += dm * pn[cb][e];
+          const float E2 = dm * br[e] * pn[cb][e];
+          rowacc[e] += E2;
+          cs += E2;
+          DMs[r * L7 + i] = from_f<T>(dm * br[e] * __expf(keep ? gr[e] - gi : -INFINITY));
+        }
       }
       cs = sum4g(cs);
-      if (grp == 0) colE[wr][16 * cb + col] = cs;
+      if (grp == 0) (hi ? colE2 : colE)[wr][16 * cb + col] = cs;
     }
   }
   __syncthreads();
-  // dgamma -= column sums of dP o P (fixed order over row blocks)
-  if (tid < 64) dgam[tid] -= colE[0][tid] + colE[1][tid] + colE[2][tid] + colE[3][tid];
-  // side 0: T1 = A^T dA (rows 16 wr) and dQ2 = (dP o Gamma) K;
-  // side 1: dK2 = (dP o Gamma)^T Q
+  // dgamma -= column sums of dP o P and of dM o M (fixed order over row blocks)
+  if (tid < 64)
+    dgam[tid] -= (colE[0][tid] + colE[1][tid] + colE[2][tid] + colE[3][tid]) +
+                 (colE2[0][tid] + colE2[1][tid] + colE2[2][tid] + colE2[3][tid]);
+  // side 0: dQ2 = (dP o Gamma) K; side 1: dK2 = (dP o Gamma)^T Q (dK3 below)
   f32x4 acc3[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) acc3[x] = zero4();
   if (!hi) {
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int mk = 0; mk < 2; ++mk)
-        acc = mfma16(frag_tr_split(As + 32 * mk * L7 + 16 * wr, L7),
-                     frag_tr_split(dAs + 32 * mk * L7 + 16 * ib, L7), acc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) T1s[(16 * wr + 4 * grp + e) * L7 + 16 * ib + col] = from_f<T>(acc[e]);
-    }
 #pragma unroll
     for (int ik = 0; ik < 2; ++ik) {
       const x8 fa = frag_row_split(dPG + 16 * wr * L7 + 32 * ik, L7);
@@ -1133,41 +1138,6 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
         acc3[kb] = mfma16(fb, frag_tr_split_q(Qs, 32 * ik, 16 * kb), acc3[kb]);
     }
   }
-  __syncthreads();
-  // side 1: dM = strict_lower(-T1 A^T), rows 16 wr
-  if (hi) {
-    const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + 16 * wr + 4 * grp);
-    const f32x4 br = *reinterpret_cast<const f32x4*>(bet + 16 * wr + 4 * grp);
-    float gis[4];  // gamma of each column block's column, read at once
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) gis[ib] = gam[16 * ib + col];
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int mk = 0; mk < 2; ++mk)
-        acc = mfma16(frag_row_split(T1s + 16 * wr * L7 + 32 * mk, L7),
-                     frag_row_split(As + 16 * ib * L7 + 32 * mk, L7), acc);
-      float cs = 0.f;
-      const float gi = gis[ib];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * wr + 4 * grp + e, i = 16 * ib + col;
-        const bool keep = i < r;
-        const float dm = keep ? -acc[e] : 0.f;
-        // M = beta_r N, N = (k_r . k_i) Gamma_ri
-        dbacc[e] += dm * pn[ib][e];
-        const float E2 = dm * br[e] * pn[ib][e];
-        rowacc[e] += E2;
-        cs += E2;
-        DMs[r * L7 + i] = from_f<T>(dm * br[e] * __expf(keep ? gr[e] - gi : -INFINITY));
-      }
-      cs = sum4g(cs);
-      if (grp == 0) colE[wr][16 * ib + col] = cs;
-    }
-  }
-  __syncthreads();
-  if (tid < 64) dgam[tid] -= colE[0][tid] + colE[1][tid] + colE[2][tid] + colE[3][tid];
 
   // ---- final rows ----
   float rs1[4] = {0.f, 0.f, 0.f, 0.f}, rs2[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1292,7 +1262,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
       }
     }
   }
-  __syncthreads();  // every wave is done with DMs, T1s, dAs; rowq and fsum are in
+  __syncthreads();  // every wave is done with dPG and DMs; rowq and fsum are in
   // dq (side 0) / dk (side 1) rows, once the group sum is whole: staged
   // row-major in the free S / dSn tiles for 16-byte stores
   if (store_dqk) {
