@@ -3,8 +3,9 @@
 
 One step = one pass of the whole hot path over one batch: forward (gate cumsum,
 WY inverse, state scan with output, intra-GPU context parallelism when the plan
-uses it) and backward (state recompute, reverse state-gradient scan, per-chunk
-gradients).  The default workload is B=2, T=4096, Hq=Hv=32, K=V=128, bf16 with
+uses it; the chunk-start states are kept) and backward (reverse
+state-gradient scan and per-chunk gradients from the forward's states; with
+``--recompute-states`` the backward recomputes them instead).  The default workload is B=2, T=4096, Hq=Hv=32, K=V=128, bf16 with
 an initial state and a final-state gradient (the shape of the FlashQLA API
 example), synthetic seeded inputs resident in HBM before timing starts.
 
@@ -34,7 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 FWD_FLOP = 140629               # algorithmic flop per (token, value head), forward
-BWD_FLOP = 393216               # backward incl. the state recompute
+BWD_FLOP = 393216               # backward, counted with the state recompute
 
 # The workloads the path is specified on, each timed in the same run (the
 # "configs" block of the JSON line).  The B=1 T=256 H=2 forward is a parity case
@@ -53,8 +54,7 @@ CONFIGS = {
 STATE_BYTES = 128 * 128 * 4     # one fp32 state, per (sequence, value head)
 FLUSH_BYTES = 512 << 20         # written before each cold run: more than the 256 MiB MALL
 FWD_KERNELS = ("fwd_prep", "scan_out", "scan_aug", "scan_state", "cp_combine_fwd")
-BWD_KERNELS = ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "grad", "gva_reduce",
-               "gate_param_grad")
+BWD_KERNELS = ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "grad", "gate_param_grad")
 
 
 def alg_bytes_per_unit(direction, r, isz=2, gsz=2):
@@ -107,11 +107,12 @@ DECODE_WORKLOADS = {"decode_B256_H32_bf16": (256, 32, 1, "bf16")}
 
 
 def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True, with_dht=True,
-                 qk_norm=False):
+                 qk_norm=False, states=True):
     """Operand bytes of one launch of a library kernel: every operand it
     touches read once and every result it writes written once, workspace
-    intermediates (the backward's chunk states and state gradients, the GVA
-    partials) included.  A per-kernel diagnostic: the roofline fractions use
+    intermediates (the chunk states and state gradients) included.  With
+    ``states`` the forward scan writes the chunk-start states and the
+    backward's scan launch runs the state-gradient scan alone.  A per-kernel diagnostic: the roofline fractions use
     the pass minimum of pass_bytes instead.  Per (token, value head) terms with r = Hq / Hv:
     q, k 256 r each, v / o / do / dv 256, A 128, g_cum 4, beta 2, g 2;
     chunk states 32 KiB (bf16) per (chunk, head); fp32 states 64 KiB per
@@ -126,7 +127,8 @@ def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True,
     if name == "fwd_prep":
         return TH * (256 * r + gsz + isz + 4 + 128)
     if name == "scan_out":
-        return TH * (512 * r + 256 + 128 + 4 + isz + 256) + U * st * (int(with_h0) + 1)
+        return (TH * (512 * r + 256 + 128 + 4 + isz + 256) + U * st * (int(with_h0) + 1) +
+                NCH * ch * int(states))
     if name == "scan_state":
         return TH * (256 * r + 256 + 128 + 4 + isz) + NCH * ch + U * st * int(with_h0)
     if name == "scan_aug":
@@ -135,8 +137,9 @@ def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True,
         return TH * (512 * r + 256 + 128 + 4 + isz) + NCH * ch + U * st * (int(with_dht) + int(with_h0))
     if name == "dh_scan_aug":
         return frac * TH * (512 * r + 256 + 128 + 4 + isz) + U * (cp - 1) * 2 * st
-    if name == "bwd_scans":  # the state scan and the state-gradient scan in one launch
-        return (kernel_bytes("scan_state", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht) +
+    if name == "bwd_scans":  # the state scan (unless given) and the state-gradient scan
+        return (kernel_bytes("scan_state", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht)
+                * int(not states) +
                 kernel_bytes("dh_scan_out", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht))
     if name == "bwd_scan_aug":
         return (kernel_bytes("scan_aug", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht) +
@@ -146,10 +149,6 @@ def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True,
     if name == "grad":
         dqk = 512 * r if Hq == Hv else 1024
         return TH * (512 * r + 256 + 256 + 128 + 4 + isz + dqk + 256 + isz + gsz) + NCH * 2 * ch
-    if name == "gva_reduce":
-        G = Hv // Hq
-        # fp32 partials in, dq / dk out; with q / k normalisation the raw rows too
-        return B * T * Hq * 128 * (2 * 4 * G + 2 * isz + (2 * isz if qk_norm else 0))
     if name == "chunk_offsets":
         return 8 * (N + 1)
     return None
@@ -499,7 +498,8 @@ def main():
     alg = fwd_bytes if ddir == "fwd" else bwd_bytes
     dom_cp = case.plans[ddir][0]
     wl_key = args.workload + ("+qk_l2norm" if qkn else "") + ("+gate" if args.gate else "")
-    operand = kernel_bytes(dom, B, T, Hq, Hv, case.nchunks, case.N, dom_cp, qk_norm=qkn)
+    operand = kernel_bytes(dom, B, T, Hq, Hv, case.nchunks, case.N, dom_cp, qk_norm=qkn,
+                           states=not args.recompute_states)
     traffic = measured_traffic(dom, wl_key, operand)
     achieved = alg / avg_s / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),

@@ -68,8 +68,14 @@ def test_algorithmic_bytes_of_fwd_prep_by_hand():
 
 def test_fused_scan_bytes_are_the_sum_of_both_scans():
     args = (2, 4096, 32, 32, 128, 2, 1)
-    assert bench.kernel_bytes("bwd_scans", *args) == (bench.kernel_bytes("scan_state", *args) +
-                                                      bench.kernel_bytes("dh_scan_out", *args))
+    kb = bench.kernel_bytes
+    assert kb("bwd_scans", *args, states=False) == (kb("scan_state", *args) +
+                                                    kb("dh_scan_out", *args))
+    # given the forward's chunk states the launch runs the state-gradient scan
+    # alone, and the forward scan writes those states (one bf16 128 x 128
+    # tile per chunk and head)
+    assert kb("bwd_scans", *args) == kb("dh_scan_out", *args)
+    assert kb("scan_out", *args) - kb("scan_out", *args, states=False) == 128 * 32 * 128 * 128 * 2
 
 
 def test_cpu_baseline_record():
@@ -117,5 +123,5 @@ def test_fractions_take_the_larger_bound():
 def test_every_library_kernel_has_a_direction():
     for k in ("fwd_prep", "scan_out", "scan_aug", "cp_combine_fwd"):
         assert bench.kernel_direction(k) == "fwd"
-    for k in ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "grad", "gva_reduce"):
+    for k in ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "grad"):
         assert bench.kernel_direction(k) == "bwd"
