@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -154,13 +155,23 @@ def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True,
     return None
 
 
-def source_digest():
+def code_text(src):
+    """C/C++ source without its comments and blank space, so that an edit of
+    comments alone leaves the kernels' digest unchanged."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(" ".join(ln.split()) for ln in src.splitlines() if ln.strip())
+
+
+def source_digest(csrc=None):
+    """Digest of the kernel sources' code, which the committed counter
+    summaries carry: their figures apply only while it matches."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gated_delta_rule_66_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "gated_delta_rule_66_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, fn), "rb") as f:
+        with open(os.path.join(csrc, fn), encoding="utf-8") as f:
             h.update(fn.encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -14,8 +14,9 @@
 //       state construction as the forward).
 //   B3-5 grad_kernel, one workgroup per (chunk, value head), from S and dSn:
 //       R = diag(beta) V - diag(beta e^gamma) K S, Delta = A R,
-//       dDelta (as above), dR = A^T dDelta, dA = dDelta R^T,
-//       dM = strict_lower(-A^T dA A^T), dP = scale lower_incl(dO Delta^T),
+//       dDelta (as above), dR = A^T dDelta, dM = strict_lower(-dR Delta^T)
+//       (the gradient of A = (I + M)^-1 is -A^T dA A^T with dA = dDelta R^T,
+//       and A^T dDelta R^T A^T = dR Delta^T), dP = scale lower_incl(dO Delta^T),
 //       dq = scale diag(e^gamma) dO S^T + (dP o Gamma) K
 //       dk = (dP o Gamma)^T Q + diag(e^{gL-gamma}) Delta dSn^T
 //            - diag(beta e^gamma) dR S^T + (dM o beta Gamma) K + (..)^T K
@@ -23,8 +24,9 @@
 //       dg = reverse chunk-local cumsum of dgamma (times the gate's slope when
 //       g is a gate input, with per-chunk shares of the gate parameters'
 //       gradients, summed per head by gate_param_grad_kernel).
-//   B6  with GVA the gradient kernel's workgroup takes the Hv/Hq value heads of
-//       a q/k head in turn and sums their dq, dk in registers (head order).
+//   B6  with GVA the gradient kernel runs twice: value heads 0 .. G-2 of each
+//       group leave fp32 dq, dk rows in workspace slots, head G-1 adds them in
+//       head order to its own and stores dq, dk once.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 #include "gdr_scan.h"
@@ -732,9 +734,9 @@ struct GradArgs {
 
 // Eight waves: wave w works on row / column block wr = w % 4 and takes one
 // side of every phase (hi = w / 4): hi = 0 the forward-side chain (K S, R,
-// Delta, dA, dP, dQ1 = dO S^T and everything of dq), hi = 1 the gradient side
-// (K dSn, dDelta, dR, dX = -dR S^T, dKs = Delta dSn^T, dM and everything of
-// dk).  The two sides of a phase are independent, so two waves share each
+// Delta, dP, dQ1 = dO S^T and everything of dq), hi = 1 the gradient side
+// (K dSn, dDelta, dR, dX = -dR S^T, dKs = Delta dSn^T, dM = -dR Delta^T and
+// everything of dk).  The two sides of a phase are independent, so two waves share each
 // SIMD and hide each other's latencies.
 // A workgroup takes one (chunk, value head).  With GVA (Hq < Hv) the kernel
 // runs twice: the first launch takes value heads 0 .. G-2 of every group and
@@ -750,7 +752,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   __shared__ __align__(16) T Ks[QK_TILE];
   __shared__ __align__(16) T As[64 * L7];
   __shared__ __align__(16) T Ps[64 * L7];
-  __shared__ __align__(16) T Ss[QK_TILE];    // S[:, half]^T ([v][k]); later dA, T1, dq (ld LD)
+  __shared__ __align__(16) T Ss[QK_TILE];    // S[:, half]^T ([v][k]); later dq (ld LD)
   __shared__ __align__(16) T Gs_[QK_TILE];   // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma, dk
   __shared__ __align__(16) T Vs[64 * L7];
   __shared__ __align__(16) T Os[64 * L7];    // dO[:, half]

@@ -125,3 +125,11 @@ def test_every_library_kernel_has_a_direction():
         assert bench.kernel_direction(k) == "fwd"
     for k in ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "grad"):
         assert bench.kernel_direction(k) == "bwd"
+
+
+def test_source_digest_ignores_comments_only():
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* no\n overflow */\n}\n"
+    b = "int f(int x) {\n\n  return 2 * x;\n}  // edited comment\n"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
