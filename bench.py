@@ -267,7 +267,8 @@ class Case:
     for its forward, its backward (on the forward's g_cum and A) and a step."""
 
     def __init__(self, gdr, torch, gdr_synth, B, T, Hq, Hv, dt, g_shift, varlen, h0, dht, svf,
-                 cp=0, vt=0, qk_norm=False, gate=False, name="case", recompute=False):
+                 cp=0, vt=0, qk_norm=False, gate=False, name="case", recompute=False,
+                 fwd_only=False):
         prob = gdr_synth.Problem(name, B=B, T=T, Hq=Hq, Hv=Hv, dtype=dt, init_state=h0,
                                  backward=True, dht=dht, g_shift=g_shift, qk_l2norm=qk_norm,
                                  gate=gate)
@@ -289,32 +290,40 @@ class Case:
         self.dd = dd
         cu_cpu = d["cu_seqlens"]
         gkw = dict(use_gate_in_kernel=True, A_log=dd["A_log"], dt_bias=dd["dt_bias"]) if gate else {}
+        # a forward run for a backward keeps what that backward takes; an
+        # inference forward keeps nothing
+        keep = not (recompute or fwd_only)
         self.plans = {d_: gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
                                         cu_seqlens_cpu=cu_cpu, cp_segments=cp, wave_tiles=vt,
-                                        backward=(d_ == "bwd"), h_packed=not recompute)
+                                        backward=(d_ == "bwd"), h_packed=keep)
                       for d_ in ("fwd", "bwd")}
 
         # the autograd op's calls: the forward keeps its chunk-start states
-        # (value-major) and the backward takes them instead of recomputing
-        def fwd():
-            return gdr.chunk_gated_delta_rule_fwd(
-                dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
-                initial_state=dd["h0"], output_final_state=True, cu_seqlens=dd["cu_seqlens"],
-                cu_seqlens_cpu=cu_cpu, state_v_first=svf, cp_segments=cp, wave_tiles=vt,
-                use_qk_l2norm_in_kernel=qk_norm, output_h=not recompute, h_packed=True,
-                **gkw)
+        # (packed) and the segment transitions of a split plan, and the
+        # backward takes them instead of recomputing
+        fkw = dict(scale=dd["scale"], initial_state=dd["h0"], output_final_state=True,
+                   cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=cu_cpu, state_v_first=svf,
+                   cp_segments=cp, wave_tiles=vt, use_qk_l2norm_in_kernel=qk_norm, **gkw)
 
-        def bwd(g_cum, A, h):
+        def fwd():
+            if not keep:
+                g_cum, A, o, _, ht = gdr.chunk_gated_delta_rule_fwd(
+                    dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], **fkw)
+                return g_cum, A, o, None, None, ht
+            return gdr.chunk_gated_delta_rule_fwd_states(
+                dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], **fkw)
+
+        def bwd(g_cum, A, h, trans):
             return gdr.chunk_gated_delta_rule_bwd(
                 dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dd["dht"],
                 scale=dd["scale"], initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
                 state_v_first=svf, dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu,
                 cp_segments=cp, wave_tiles=vt, use_qk_l2norm_in_kernel=qk_norm, h=h,
-                **(dict(gkw, g_input=dd["g"]) if gate else {}))
+                trans=trans, **(dict(gkw, g_input=dd["g"]) if gate else {}))
 
         def step():
-            g_cum, A, o, h, ht = fwd()
-            return bwd(g_cum, A, h)
+            g_cum, A, o, h, trans, ht = fwd()
+            return bwd(g_cum, A, h, trans)
 
         self.fwd, self.bwd, self.step = fwd, bwd, step
 
@@ -398,9 +407,9 @@ def measure_case(gdr, torch, timer, case, direction, steps, warmup, n_cold):
         flop, nbytes = fwd_flop, fwd_bytes
         kt = kernel_times(gdr, torch, case.fwd, steps)
     else:
-        g_cum, A, _, h, _ = case.fwd()
-        bwd_ms = timer.mean_ms(lambda: case.bwd(g_cum, A, h), steps)
-        bwd_cold = timer.cold_ms(lambda: case.bwd(g_cum, A, h), n_cold)
+        g_cum, A, _, h, trans, _ = case.fwd()
+        bwd_ms = timer.mean_ms(lambda: case.bwd(g_cum, A, h, trans), steps)
+        bwd_cold = timer.cold_ms(lambda: case.bwd(g_cum, A, h, trans), n_cold)
         rec["bwd_ms"], rec["bwd_cold_ms"] = round(bwd_ms, 4), round(bwd_cold, 4)
         rec["bwd_frac"] = fractions(bwd_ms * 1e-3, bwd_flop, bwd_bytes)
         ms = timer.mean_ms(case.step, steps)
@@ -476,13 +485,13 @@ def main():
     ms = timer.mean_ms(case.step, args.steps)
 
     # the forward and the backward alone, cold runs, then per-kernel times
-    g_cum, A, o, h, ht = case.fwd()
+    g_cum, A, o, h, trans, ht = case.fwd()
     n_sub = max(3, args.steps // 2)
     fwd_ms = timer.mean_ms(case.fwd, n_sub)
-    bwd_ms = timer.mean_ms(lambda: case.bwd(g_cum, A, h), n_sub)
+    bwd_ms = timer.mean_ms(lambda: case.bwd(g_cum, A, h, trans), n_sub)
     cold_ms = timer.cold_ms(case.step, args.cold)
     fwd_cold = timer.cold_ms(case.fwd, args.cold)
-    bwd_cold = timer.cold_ms(lambda: case.bwd(g_cum, A, h), args.cold)
+    bwd_cold = timer.cold_ms(lambda: case.bwd(g_cum, A, h, trans), args.cold)
     kernels = kernel_times(gdr, torch, case.step, args.steps)
 
     tokens = case.tokens
@@ -570,7 +579,7 @@ def main():
         "configs": None,
         "cpu_baseline": None,
     }
-    del g_cum, A, o, h, ht
+    del g_cum, A, o, h, trans, ht
     host = case.host
     if not args.no_configs and args.workload == DEFAULT and not qkn and not args.gate:
         del case
@@ -578,7 +587,7 @@ def main():
         cfgs = {}
         for name, (direc, cB, cT, cHq, cHv, cdt, gsh, vl, ch0, cdht, svf) in CONFIGS.items():
             c = Case(gdr, torch, gdr_synth, cB, cT, cHq, cHv, cdt, gsh, vl, ch0, cdht, svf,
-                     name=name)
+                     name=name, fwd_only=(direc == "fwd"))
             cfgs[name], _ = measure_case(gdr, torch, timer, c, direc, steps=10, warmup=3,
                                          n_cold=args.cold)
             cfgs[name].update({"B": c.B, "T": c.T, "Hq": cHq, "Hv": cHv, "dtype": cdt,

@@ -21,7 +21,8 @@ import torch
 from ._lib import (GDR_BF16, GDR_FP16, GDR_FP32, GdrError, Problem, check, lib)
 
 __all__ = [
-    "chunk_gated_delta_rule", "chunk_gated_delta_rule_fwd", "chunk_gated_delta_rule_bwd",
+    "chunk_gated_delta_rule", "chunk_gated_delta_rule_fwd", "chunk_gated_delta_rule_fwd_states",
+    "chunk_gated_delta_rule_bwd",
     "fused_recurrent_gated_delta_rule", "prepare_lens", "prepare_chunk_indices",
     "prepare_chunk_offsets", "unpack_states", "GdrError",
 ]
@@ -203,6 +204,35 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
     then not recomputed): element ``((vb*4 + kb)*64 + 16*g + c)*8 + e`` is the
     state at value ``16*vb + c`` and key ``32*kb + 16*(e >= 4) + 4*g + e % 4``
     (:func:`unpack_states` gives ``[NC, Hv, K, V]``)."""
+    return _fwd(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                state_v_first, output_h, cp_segments, cu_seqlens_cpu, wave_tiles,
+                use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
+                use_gate_in_kernel, A_log, dt_bias, workspace, no_alloc, h_packed, False)
+
+
+def chunk_gated_delta_rule_fwd_states(q, k, v, g, beta, scale=None, initial_state=None,
+                                      output_final_state=True, cu_seqlens=None,
+                                      state_v_first=False, cp_segments=0, cu_seqlens_cpu=None,
+                                      wave_tiles=0, use_qk_l2norm_in_kernel=False,
+                                      use_beta_sigmoid_in_kernel=False, allow_neg_eigval=False,
+                                      use_gate_in_kernel=False, A_log=None, dt_bias=None,
+                                      workspace=None):
+    """The forward the autograd op runs (``gdr_chunk_fwd_states``):
+    :func:`chunk_gated_delta_rule_fwd` with ``output_h=True, h_packed=True``
+    that also keeps, when the plan splits sequences into T-segments, each
+    segment's fp32 state transition for the backward.  Returns ``(g_cum, A,
+    o, h, trans, final_state)``; ``trans`` is ``None`` when nothing is split.
+    Hand ``h`` and ``trans`` to :func:`chunk_gated_delta_rule_bwd`."""
+    return _fwd(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                state_v_first, True, cp_segments, cu_seqlens_cpu, wave_tiles,
+                use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
+                use_gate_in_kernel, A_log, dt_bias, workspace, False, True, True)
+
+
+def _fwd(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens, state_v_first,
+         output_h, cp_segments, cu_seqlens_cpu, wave_tiles, use_qk_l2norm_in_kernel,
+         use_beta_sigmoid_in_kernel, allow_neg_eigval, use_gate_in_kernel, A_log, dt_bias,
+         workspace, no_alloc, h_packed, keep):
     q, k, v, g, beta, initial_state = _contig(q, k, v, g, beta, initial_state)
     c = _Call(q, v, g.dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
               wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
@@ -229,6 +259,15 @@ def chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=None, initial_state=None,
         return g_cum, A, o, h, ht
     ws_bytes = lib.gdr_chunk_fwd_workspace_size(c.ref)
     ws = _workspace(ws_bytes, dev, workspace)
+    if keep:
+        tr_bytes = lib.gdr_chunk_trans_size(c.ref)
+        trans = (torch.empty(tr_bytes // 4, dtype=torch.float32, device=dev)
+                 if tr_bytes else None)
+        check(lib.gdr_chunk_fwd_states(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(initial_state), _ptr(g_cum), _ptr(A), _ptr(o),
+                                       _ptr(h), _ptr(trans), _ptr(ht), _ptr(ws), ws_bytes,
+                                       _stream(dev)))
+        return g_cum, A, o, h, trans, ht
     check(lib.gdr_chunk_fwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             _ptr(initial_state), _ptr(g_cum), _ptr(A), _ptr(o), _ptr(h), _ptr(ht),
                             _ptr(ws), ws_bytes, _stream(dev)))
@@ -240,7 +279,8 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
                                cp_segments=0, cu_seqlens_cpu=None, wave_tiles=0,
                                use_qk_l2norm_in_kernel=False, use_beta_sigmoid_in_kernel=False,
                                allow_neg_eigval=False, use_gate_in_kernel=False, A_log=None,
-                               dt_bias=None, g_input=None, workspace=None, h=None):
+                               dt_bias=None, g_input=None, workspace=None, h=None,
+                               trans=None):
     """Backward.  ``g`` is the forward's fp32 ``g_cum`` output.  Returns
     ``(dq, dk, dv, dbeta, dg, dh0)``; ``dg`` is the gradient with respect to
     the raw log-decay g (dtype ``dg_dtype``, default the input dtype) and
@@ -255,9 +295,14 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
     ``gdr_chunk_bwd_workspace_size`` bytes (``..._states_workspace_size`` with
     ``h``).  ``h``: the packed chunk-start states the forward returned for the
     same inputs with ``output_h=True, h_packed=True``; the backward then
-    skips recomputing them (``gdr_chunk_bwd_states``)."""
-    q, k, v, g, beta, A, do, dht, initial_state, g_input, h = _contig(
-        q, k, v, g, beta, A, do, dht, initial_state, g_input, h)
+    skips recomputing them (``gdr_chunk_bwd_states``).  ``trans`` (with
+    ``h``): the segment transitions :func:`chunk_gated_delta_rule_fwd_states`
+    returned for the same inputs; a split backward then applies them instead
+    of forming its own."""
+    q, k, v, g, beta, A, do, dht, initial_state, g_input, h, trans = _contig(
+        q, k, v, g, beta, A, do, dht, initial_state, g_input, h, trans)
+    if trans is not None and h is None:
+        raise GdrError(1, "trans comes with the forward's states h")
     if g.dtype != torch.float32:
         raise GdrError(4, "the backward takes the forward's fp32 g_cum as g")
     if use_gate_in_kernel and g_input is None:
@@ -268,10 +313,13 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
         g_input = g_input.to(dg_dtype).contiguous()
     c = _Call(q, v, dg_dtype, scale, cu_seqlens, cu_seqlens_cpu, state_v_first, cp_segments,
               wave_tiles, use_qk_l2norm_in_kernel, use_beta_sigmoid_in_kernel, allow_neg_eigval,
-              (A_log, dt_bias) if use_gate_in_kernel else None)
+              (A_log, dt_bias) if use_gate_in_kernel else None, h_packed=h is not None)
     _check_inputs(c, q, k, v, None, beta, state_v_first, initial_state=initial_state, A=A,
                   do=do, dht=dht, g_cum=g, g_input=g_input)
     _expect("h", h, c.h_shape(state_v_first, True), (q.dtype,), q.device)
+    if trans is not None:
+        n_tr = lib.gdr_chunk_trans_size(c.ref) // 4
+        _expect("trans", trans, (n_tr,), (torch.float32,), q.device)
     dev = q.device
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -294,7 +342,7 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
         check(lib.gdr_chunk_bwd_states(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                        _ptr(g_input if use_gate_in_kernel else None), _ptr(beta),
                                        _ptr(A), _ptr(do), _ptr(dht), _ptr(initial_state), _ptr(h),
-                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0),
+                                       _ptr(trans), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0),
                                        _ptr(dA_log), _ptr(ddt_bias), _ptr(ws), ws_bytes,
                                        _stream(dev)))
         if use_gate_in_kernel:
@@ -325,14 +373,20 @@ class _GatedDeltaRule(torch.autograd.Function):
         if cu_seqlens is not None and cu_seqlens_cpu is None:
             # the one device-to-host copy of the lengths, shared by the backward
             cu_seqlens_cpu = cu_seqlens.detach().to("cpu")
-        g_cum, A, o, h, ht = chunk_gated_delta_rule_fwd(
-            q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
-            state_v_first, not recompute_states, cp_segments, cu_seqlens_cpu,
-            use_qk_l2norm_in_kernel=use_qk_l2norm, use_beta_sigmoid_in_kernel=beta_sigmoid,
-            allow_neg_eigval=neg_eigval, use_gate_in_kernel=use_gate, A_log=A_log,
-            dt_bias=dt_bias, h_packed=True)
+        kw = dict(use_qk_l2norm_in_kernel=use_qk_l2norm, use_beta_sigmoid_in_kernel=beta_sigmoid,
+                  allow_neg_eigval=neg_eigval, use_gate_in_kernel=use_gate, A_log=A_log,
+                  dt_bias=dt_bias)
+        h = trans = None
+        if recompute_states:
+            g_cum, A, o, _, ht = chunk_gated_delta_rule_fwd(
+                q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                state_v_first, False, cp_segments, cu_seqlens_cpu, **kw)
+        else:
+            g_cum, A, o, h, trans, ht = chunk_gated_delta_rule_fwd_states(
+                q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                state_v_first, cp_segments, cu_seqlens_cpu, **kw)
         ctx.save_for_backward(q, k, v, g_cum, beta, A, initial_state, cu_seqlens, cu_seqlens_cpu,
-                              g if use_gate else None, A_log, dt_bias, h)
+                              g if use_gate else None, A_log, dt_bias, h, trans)
         ctx.scale, ctx.svf, ctx.cp, ctx.g_dtype = scale, state_v_first, cp_segments, g.dtype
         ctx.qk_norm, ctx.beta_sigmoid, ctx.neg_eigval = use_qk_l2norm, beta_sigmoid, neg_eigval
         ctx.use_gate = use_gate
@@ -340,12 +394,13 @@ class _GatedDeltaRule(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, do, dht):
-        q, k, v, g_cum, beta, A, h0, cu, cu_cpu, g_in, A_log, dt_bias, h = ctx.saved_tensors
+        q, k, v, g_cum, beta, A, h0, cu, cu_cpu, g_in, A_log, dt_bias, h, trans = ctx.saved_tensors
         grads = chunk_gated_delta_rule_bwd(
             q, k, v, g_cum, beta, A, do, dht, ctx.scale, h0, cu, ctx.svf, ctx.g_dtype, ctx.cp,
             cu_cpu, use_qk_l2norm_in_kernel=ctx.qk_norm,
             use_beta_sigmoid_in_kernel=ctx.beta_sigmoid, allow_neg_eigval=ctx.neg_eigval,
-            use_gate_in_kernel=ctx.use_gate, A_log=A_log, dt_bias=dt_bias, g_input=g_in, h=h)
+            use_gate_in_kernel=ctx.use_gate, A_log=A_log, dt_bias=dt_bias, g_input=g_in, h=h,
+            trans=trans)
         dq, dk, dv, db, dg, dh0 = grads[:6]
         dA = ddt = None
         if ctx.use_gate:
@@ -363,10 +418,12 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                            dt_bias=None, recompute_states=False, **unsupported):
     """High-level op with autograd: returns ``(o, final_state)``.
 
-    The forward keeps its chunk-start states (``[NC, Hv, V, K]`` in the input
-    dtype, 32 KiB per chunk and value head) for the backward, which then does
-    not recompute them; ``recompute_states=True`` keeps only the inputs and
-    recomputes the states in the backward instead.
+    The forward keeps its chunk-start states (packed, in the input dtype, 32
+    KiB per chunk and value head) and, when its plan splits sequences into
+    T-segments, each segment's fp32 state transition (64 KiB per segment and
+    value head) for the backward, which then neither recomputes the states
+    nor forms its own transitions; ``recompute_states=True`` keeps only the
+    inputs and recomputes the states in the backward instead.
 
     ``use_qk_l2norm_in_kernel`` scales q and k per (token, head) to unit
     length inside the kernels (and carries the gradient back to the raw q, k);

@@ -48,7 +48,8 @@ EXPORTS = [
     "gdr_prepare_chunk_offsets_i32", "gdr_prepare_chunk_offsets_i64",
     "gdr_prepare_chunk_token_starts_i64", "gdr_profile_enable", "gdr_profile_read",
     "gdr_plan_info", "gdr_recurrent_fwd", "gdr_chunk_bwd_gate", "gdr_chunk_fwd_noalloc",
-    "gdr_chunk_bwd_states", "gdr_chunk_bwd_states_workspace_size",
+    "gdr_chunk_bwd_states", "gdr_chunk_bwd_states_workspace_size", "gdr_chunk_fwd_states",
+    "gdr_chunk_trans_size",
 ]
 
 
@@ -81,7 +82,11 @@ def _declare(lib):
     lib.gdr_chunk_fwd.restype = st
     lib.gdr_chunk_bwd_states_workspace_size.argtypes = [PP]
     lib.gdr_chunk_bwd_states_workspace_size.restype = S
-    lib.gdr_chunk_bwd_states.argtypes = [PP] + [P] * 20 + [S, P]
+    lib.gdr_chunk_bwd_states.argtypes = [PP] + [P] * 21 + [S, P]
+    lib.gdr_chunk_trans_size.argtypes = [PP]
+    lib.gdr_chunk_trans_size.restype = S
+    lib.gdr_chunk_fwd_states.argtypes = [PP] + [P] * 13 + [S, P]
+    lib.gdr_chunk_fwd_states.restype = st
     lib.gdr_chunk_bwd_states.restype = st
     lib.gdr_chunk_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_chunk_fwd_noalloc.restype = st

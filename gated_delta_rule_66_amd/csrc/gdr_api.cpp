@@ -93,7 +93,11 @@ static double bwd_out_cost(int64_t wgs_per_scan, int64_t chunks, int VB, bool st
   return spread > chain ? spread : chain;
 }
 
-static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd, bool states_given) {
+// trans_given: the backward applies the forward's kept segment transitions,
+// so its transition pass runs the value columns of every segment but the
+// first, in a launch that fits two workgroups per CU at VB = 1.
+static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd, bool states_given,
+                        bool trans_given = false) {
   const int64_t nvs0 = 2 / VB, nvs1 = 4 / VB;
   if (!bwd) {
     const bool narrow = VB == 1 && units * P * 2 <= 128;
@@ -108,16 +112,24 @@ static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd, b
   }
   if (P == 1) return bwd_out_cost(units * nvs0, maxch, VB, states_given);
   const int64_t sc = (maxch + P - 1) / P;
-  const int64_t wg_aug = (states_given ? 1 : 2) * units * (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
+  const int64_t wg_aug = trans_given ? units * (int64_t)(P - 1) * (nvs1 / 2)
+                                     : (states_given ? 1 : 2) * units *
+                                           (nvs1 / 2 + (int64_t)(P - 2) * nvs1);
   const double aug = VB == 1 ? 4.5 : 4.2;
-  return (double)sc * aug * rounds(wg_aug, 256) + (states_given ? 10.0 : 20.0) * (double)(P - 1) +
-         16.0 + bwd_out_cost(units * P * nvs0, sc, VB, states_given);
+  const int64_t slots = (trans_given && VB == 1) ? 512 : 256;
+  return (double)sc * aug * rounds(wg_aug, slots) +
+         (states_given ? 10.0 : 20.0) * (double)(P - 1) + 16.0 +
+         bwd_out_cost(units * P * nvs0, sc, VB, states_given);
 }
 
-// Context-parallel plan along T for one direction: it depends only on shapes
-// (never on data), so every run of a problem, in either state layout, takes
-// the same path.
+// Context-parallel plan along T: it depends only on shapes and flags (never
+// on data), so every run of a problem, in either state layout, takes the same
+// path.  One direction on its own, or, on the states path (a forward that
+// keeps its packed chunk-start states, and the backward that takes them), one
+// segment count for both directions, chosen for their sum: the backward then
+// applies the forward's segment transitions instead of forming its own.
 Plan make_plan(const gdr_problem* p, bool bwd, bool states_given) {
+  const bool joint = bwd ? states_given : (p->h_packed != 0);
   Plan pl;
   pl.N = p->N;
   pl.total_chunks = 0;
@@ -140,18 +152,34 @@ Plan make_plan(const gdr_problem* p, bool bwd, bool states_given) {
   pl.vb = 2;
   double best = 1e300;
   const int fixed = p->cp_segments;
+  // the forward's tile count on the states path: a forward that keeps packed
+  // states writes them from the one-tile pass's output waves; the two-tile
+  // pass would store them from its state chain (measured 681 -> 964 us for
+  // one T=65536 sequence)
+  const int vb_keep = p->wave_tiles > 0 ? p->wave_tiles : 1;
   for (int P = 1; P <= 16; P *= 2) {
     if (fixed > 0 && P != fixed) continue;
     if (fixed == 0 && P > 1 && maxch < 8 * P) continue;
     for (int VB = 1; VB <= 2; ++VB) {
       if (p->wave_tiles > 0 && VB != p->wave_tiles) continue;
-      // a forward that keeps packed states writes them from the one-tile
-      // pass's output waves; the two-tile pass would store them from its
-      // state chain (measured 681 -> 964 us for one T=65536 sequence)
-      if (!bwd && p->h_packed && p->wave_tiles == 0 && VB == 2) continue;
+      double c;
+      if (!joint) {
+        c = plan_cost(units, maxch, P, VB, bwd, states_given);
+      } else if (bwd) {  // VB is the backward's; the forward's is vb_keep
+        c = plan_cost(units, maxch, P, vb_keep, false, false) +
+            plan_cost(units, maxch, P, VB, true, true, true);
+      } else {           // VB is the forward's; the backward takes its best
+        if (VB != vb_keep) continue;
+        double cb = 1e300;
+        for (int VBb = 1; VBb <= 2; ++VBb) {
+          if (p->wave_tiles > 0 && VBb != p->wave_tiles) continue;
+          const double x = plan_cost(units, maxch, P, VBb, true, true, true);
+          if (x < cb) cb = x;
+        }
+        c = plan_cost(units, maxch, P, VB, false, false) + cb;
+      }
       // a split must win clearly: the model is coarse and splitting adds work
-      const double c = plan_cost(units, maxch, P, VB, bwd, states_given) *
-                       ((P > 1 && fixed == 0) ? 1.1 : 1.0);
+      c *= (P > 1 && fixed == 0) ? 1.1 : 1.0;
       if (c < best) {
         best = c;
         pl.cp = P;
@@ -385,12 +413,11 @@ size_t gdr_chunk_bwd_states_workspace_size(const gdr_problem* p) {
   return bwd_workspace_bytes(p, make_plan(p, true, true), true);
 }
 
-gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
-                         const void* g, const void* beta, const float* initial_state,
-                         float* g_cum, void* A, void* o, void* h, float* final_state,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  gdr_status s = validate(p, nullptr, 0);
-  if (s != GDR_OK) return s;
+static gdr_status chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                            const void* g, const void* beta, const float* initial_state,
+                            float* g_cum, void* A, void* o, void* h, float* trans,
+                            float* final_state, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   if (!q || !k || !v || !g || !beta || !g_cum || !A || !o)
     return fail(GDR_ERR_NULL, nullptr, 0, "a required forward pointer is NULL");
   const Plan pl = make_plan(p, false);
@@ -398,10 +425,44 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDR_ERR_WORKSPACE, nullptr, 0, "forward workspace needs %zu bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
-  s = check_device_cached();
+  const gdr_status s = check_device_cached();
   if (s != GDR_OK) return s;
-  return launch_fwd(p, pl, q, k, v, g, beta, initial_state, g_cum, A, o, h, final_state,
-                    workspace, (hipStream_t)stream);
+  return launch_fwd(p, pl, q, k, v, g, beta, initial_state, g_cum, A, o, h,
+                    pl.cp > 1 ? trans : nullptr, final_state, workspace, (hipStream_t)stream);
+}
+
+gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, const float* initial_state,
+                         float* g_cum, void* A, void* o, void* h, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  return chunk_fwd(p, q, k, v, g, beta, initial_state, g_cum, A, o, h, nullptr, final_state,
+                   workspace, workspace_bytes, stream);
+}
+
+size_t gdr_chunk_trans_size(const gdr_problem* p) {
+  if (validate(p, nullptr, 0) != GDR_OK || !p->h_packed) return 0;
+  const Plan pl = make_plan(p, false);
+  if (pl.cp <= 1) return 0;
+  return (size_t)pl.N * p->Hv * pl.cp * kDim * kDim * sizeof(float);
+}
+
+gdr_status gdr_chunk_fwd_states(const gdr_problem* p, const void* q, const void* k,
+                                const void* v, const void* g, const void* beta,
+                                const float* initial_state, float* g_cum, void* A, void* o,
+                                void* h, float* trans, float* final_state, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  const gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  if (!p->h_packed)
+    return fail(GDR_ERR_ARG, nullptr, 0, "gdr_chunk_fwd_states keeps packed states: h_packed = 1");
+  if (!h) return fail(GDR_ERR_NULL, nullptr, 0, "gdr_chunk_fwd_states needs h");
+  if (!trans && gdr_chunk_trans_size(p) > 0)
+    return fail(GDR_ERR_NULL, nullptr, 0,
+                "the plan splits sequences: trans needs gdr_chunk_trans_size bytes");
+  return chunk_fwd(p, q, k, v, g, beta, initial_state, g_cum, A, o, h, trans, final_state,
+                   workspace, workspace_bytes, stream);
 }
 
 static_assert(GDR_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "header and library agree");
@@ -426,16 +487,17 @@ gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void
   void* ws = nullptr;
   s = noalloc_scratch(&ws);
   if (s != GDR_OK) return s;
-  return launch_fwd(p, pl, q, k, v, g, beta, initial_state, g_cum, A, o, h, final_state, ws,
-                    (hipStream_t)stream);
+  return launch_fwd(p, pl, q, k, v, g, beta, initial_state, g_cum, A, o, h, nullptr, final_state,
+                    ws, (hipStream_t)stream);
 }
 
 static gdr_status chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                             const float* g_cum, const void* graw, const void* beta, const void* A,
                             const void* do_, const float* dht, const float* initial_state,
-                            const void* hstates, void* dq, void* dk, void* dv, void* dbeta,
-                            void* dg, float* dh0, float* dA_log, float* ddt_bias,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            const void* hstates, const float* trans, void* dq, void* dk,
+                            void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
+                            float* ddt_bias, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   if (!q || !k || !v || !g_cum || !beta || !A || !do_ || !dq || !dk || !dv || !dbeta || !dg)
     return fail(GDR_ERR_NULL, nullptr, 0, "a required backward pointer is NULL");
   if (initial_state && !dh0)
@@ -447,9 +509,10 @@ static gdr_status chunk_bwd(const gdr_problem* p, const void* q, const void* k, 
                 need, workspace ? workspace_bytes : (size_t)0);
   const gdr_status s = check_device_cached();
   if (s != GDR_OK) return s;
-  return launch_bwd(p, pl, q, k, v, g_cum, graw, beta, A, do_, dht, initial_state, hstates, dq,
-                    dk, dv, dbeta, dg, initial_state ? dh0 : nullptr, dA_log, ddt_bias,
-                    workspace, (hipStream_t)stream);
+  return launch_bwd(p, pl, q, k, v, g_cum, graw, beta, A, do_, dht, initial_state, hstates,
+                    pl.cp > 1 ? trans : nullptr, dq, dk, dv, dbeta, dg,
+                    initial_state ? dh0 : nullptr, dA_log, ddt_bias, workspace,
+                    (hipStream_t)stream);
 }
 
 gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -462,8 +525,9 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   if (p->use_gate)
     return fail(GDR_ERR_ARG, nullptr, 0,
                 "use_gate needs the gate input: call gdr_chunk_bwd_gate");
-  return chunk_bwd(p, q, k, v, g_cum, nullptr, beta, A, do_, dht, initial_state, nullptr, dq, dk,
-                   dv, dbeta, dg, dh0, nullptr, nullptr, workspace, workspace_bytes, stream);
+  return chunk_bwd(p, q, k, v, g_cum, nullptr, beta, A, do_, dht, initial_state, nullptr, nullptr,
+                   dq, dk, dv, dbeta, dg, dh0, nullptr, nullptr, workspace, workspace_bytes,
+                   stream);
 }
 
 gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -477,17 +541,17 @@ gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k
   if (!p->use_gate)
     return fail(GDR_ERR_ARG, nullptr, 0, "gdr_chunk_bwd_gate needs use_gate == 1");
   if (!g) return fail(GDR_ERR_NULL, nullptr, 0, "the gate input g is NULL");
-  return chunk_bwd(p, q, k, v, g_cum, g, beta, A, do_, dht, initial_state, nullptr, dq, dk, dv,
-                   dbeta, dg, dh0, dA_log, ddt_bias, workspace, workspace_bytes, stream);
+  return chunk_bwd(p, q, k, v, g_cum, g, beta, A, do_, dht, initial_state, nullptr, nullptr, dq,
+                   dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, workspace, workspace_bytes, stream);
 }
 
 gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void* k,
                                 const void* v, const float* g_cum, const void* g,
                                 const void* beta, const void* A, const void* do_,
                                 const float* dht, const float* initial_state, const void* h,
-                                void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
-                                float* dA_log, float* ddt_bias, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                const float* trans, void* dq, void* dk, void* dv, void* dbeta,
+                                void* dg, float* dh0, float* dA_log, float* ddt_bias,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   gdr_status s = validate(p, nullptr, 0);
   if (s != GDR_OK) return s;
   if (!h) return fail(GDR_ERR_NULL, nullptr, 0, "the forward's chunk-start states h are NULL");
@@ -495,8 +559,8 @@ gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void*
   if (!p->use_gate && (g || dA_log || ddt_bias))
     return fail(GDR_ERR_ARG, nullptr, 0, "g, dA_log and ddt_bias are for use_gate problems only");
   return chunk_bwd(p, q, k, v, g_cum, p->use_gate ? g : nullptr, beta, A, do_, dht,
-                   initial_state, h, dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, workspace,
-                   workspace_bytes, stream);
+                   initial_state, h, trans, dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias,
+                   workspace, workspace_bytes, stream);
 }
 
 gdr_status gdr_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,

@@ -59,6 +59,8 @@ struct DhArgs {
   int svf;
   int qk_norm;    // q, k rows scaled to unit length before use
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
+  int v_only;     // pass 1 runs the value columns only: the transitions are
+                  // the forward's, kept (ScanArgs::trans)
 };
 
 template <typename T, int VB, int MODE>
@@ -84,7 +86,7 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
   const SeqInfo s = seq_info(a.cu, n, a.T);
   const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
   const SegRange sr = seg_range(nch, a.P, p);
-  const int cb0 = vs * CW;
+  const int cb0 = vs * CW + ((MODE == MODE_AUG && a.v_only) ? kDim : 0);
   const bool isT = (MODE == MODE_AUG) && cb0 < kDim;
   if (MODE == MODE_AUG) {
     if (p == 0 || p > sr.p_last) return;       // segment 0 needs no transition
@@ -685,6 +687,13 @@ template <typename T, int OPT>
 __global__ __launch_bounds__(512) void bwd_scans_lh_kernel(ScanArgs sa, DhArgs da, int n1) {
   if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE, OPT>(sa, xcd_block(blockIdx.x, n1));
   else dh_lh_body<T, OPT>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
+}
+
+// Pass 1 of the state-gradient scan alone (the forward's states given): with
+// no state-scan LDS beside it two workgroups fit a CU at VB = 1.
+template <typename T, int VB>
+__global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_aug_kernel(DhArgs da) {
+  dh_body<T, VB, MODE_AUG>(da, xcd_block(blockIdx.x, gridDim.x));
 }
 
 // The state scan (B1) and the state-gradient scan (B2) are independent (B2
@@ -1390,19 +1399,27 @@ size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl, bool states_giv
 // With the forward's chunk states given (states_given), only the
 // state-gradient scan runs: the launches keep their layout with no blocks for
 // the state scan.
+// With the forward's segment transitions given as well (trans), the
+// state-gradient pass 1 runs only its value columns and pass 2 applies the
+// forward's transitions transposed.
 template <typename T, int VB>
 static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, bool states_given,
-                             hipStream_t st) {
+                             const float* trans, hipStream_t st) {
   const unsigned units = (unsigned)(pl.N * sa.Hv);
   if (pl.cp > 1) {
     ScanArgs s1 = sa;
     DhArgs d1 = da;
     s1.P = d1.P = pl.cp;
-    s1.nvs = d1.nvs = 4 / VB;
-    const unsigned n2 = units * pl.cp * s1.nvs;
-    const unsigned n1 = states_given ? 0u : n2;
-    GDR_LAUNCH("bwd_scan_aug", (bwd_scans_kernel<T, VB, MODE_AUG, MODE_AUG>), dim3(n1 + n2),
-               dim3(256), st, s1, d1, (int)n1);
+    s1.nvs = 4 / VB;
+    d1.nvs = trans ? 2 / VB : 4 / VB;
+    d1.v_only = trans ? 1 : 0;
+    const unsigned n2 = units * pl.cp * d1.nvs;
+    const unsigned n1 = states_given ? 0u : units * pl.cp * s1.nvs;
+    if (states_given)
+      GDR_LAUNCH("bwd_scan_aug", (dh_aug_kernel<T, VB>), dim3(n2), dim3(256), st, d1);
+    else
+      GDR_LAUNCH("bwd_scan_aug", (bwd_scans_kernel<T, VB, MODE_AUG, MODE_AUG>), dim3(n1 + n2),
+                 dim3(256), st, s1, d1, (int)n1);
     if (!states_given)
       GDR_LAUNCH("cp_combine_bwd", cp_combine_kernel, dim3(units * 8), dim3(256), st, s1);
     ScanArgs r;
@@ -1413,6 +1430,7 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, bool states
     r.P = pl.cp;
     r.seg_out = da.seg_out;
     r.seg_start = da.seg_start;
+    r.trans = const_cast<float*>(trans);
     r.reverse = 1;
     GDR_LAUNCH("cp_combine_bwd", cp_combine_kernel, dim3(units * 8), dim3(256), st, r);
   }
@@ -1444,9 +1462,9 @@ template <typename T>
 static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                                const void* v, const float* gcum, const void* graw,
                                const void* beta, const void* A, const void* dO, const float* dht,
-                               const float* h0, const void* hstates, void* dq, void* dk,
-                               void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
-                               float* ddt_bias, char* ws, hipStream_t st) {
+                               const float* h0, const void* hstates, const float* trans,
+                               void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
+                               float* dA_log, float* ddt_bias, char* ws, hipStream_t st) {
   const bool states_given = hstates != nullptr;
   const BwdLayout L = bwd_layout(p, pl, states_given);
   const int32_t* offs = nullptr;
@@ -1483,14 +1501,15 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   sa.seg_out = cp_out; sa.seg_start = cp_start; sa.reverse = 0;
   // B2: state gradients (packed)
   DhArgs da;
+  memset(&da, 0, sizeof(da));
   da.q = q; da.k = k; da.dO = dO; da.beta = beta; da.gcum = gcum; da.A = A; da.dht = dht;
   da.dh = dhbuf; da.dh0 = dh0; da.seg_start = cp2_start; da.seg_out = cp2_out;
   da.cu = p->cu_seqlens_dev; da.offs = offs;
   da.N = pl.N; da.T = p->T; da.Hq = p->Hq; da.Hv = p->Hv; da.nc_dense = pl.nc_dense;
   da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf; da.qk_norm = sa.qk_norm;
   da.beta_mode = sa.beta_mode;
-  if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, states_given, st);
-  else launch_bwd_scans<T, 1>(pl, sa, da, states_given, st);
+  if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, states_given, trans, st);
+  else launch_bwd_scans<T, 1>(pl, sa, da, states_given, trans, st);
   // B3-B6
   const bool gva = p->Hq != p->Hv;
   GradArgs ga;
@@ -1540,14 +1559,19 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
 gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const float* gcum, const void* graw, const void* beta,
                       const void* A, const void* dO, const float* dht, const float* h0,
-                      const void* hstates, void* dq, void* dk, void* dv, void* dbeta, void* dg,
-                      float* dh0, float* dA_log, float* ddt_bias, void* ws, hipStream_t st) {
+                      const void* hstates, const float* trans, void* dq, void* dk, void* dv,
+                      void* dbeta, void* dg, float* dh0, float* dA_log, float* ddt_bias, void* ws,
+                      hipStream_t st) {
   char* w = reinterpret_cast<char*>(ws);
+  if (trans && !hstates) {
+    set_error("segment transitions come with the forward's states");
+    return GDR_ERR_ARG;
+  }
   if (p->in_dtype == GDR_BF16)
-    return launch_bwd_t<__bf16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, hstates, dq,
-                                dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st);
-  return launch_bwd_t<_Float16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, hstates, dq,
-                                dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st);
+    return launch_bwd_t<__bf16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, hstates, trans,
+                                dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st);
+  return launch_bwd_t<_Float16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, hstates, trans,
+                                dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st);
 }
 
 }  // namespace gdr

@@ -24,6 +24,7 @@
 #include "gdr_internal.h"
 #include "gdr_scan.h"
 
+#include <cstring>
 #include <mutex>
 
 namespace gdr {
@@ -311,7 +312,7 @@ template void launch_scan<_Float16>(const Plan&, ScanArgs, int, hipStream_t);
 
 gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const void* g, const void* beta, const float* h0,
-                      float* gcum, void* A, void* o, void* h, float* ht, void* ws,
+                      float* gcum, void* A, void* o, void* h, float* trans, float* ht, void* ws,
                       hipStream_t st) {
   char* wp = reinterpret_cast<char*>(ws);
   const int32_t* offs = nullptr;
@@ -334,8 +335,9 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   fa.gate_dt_bias = p->use_gate ? p->gate_dt_bias : nullptr;
 
   ScanArgs sa;
+  memset(&sa, 0, sizeof(sa));
   sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
-  sa.o = o; sa.h = h; sa.ht = ht;
+  sa.o = o; sa.h = h; sa.ht = ht; sa.trans = trans;
   sa.cu = p->cu_seqlens_dev; sa.offs = offs;
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1;

@@ -22,7 +22,10 @@ struct Plan {
   int vb;             // 16-column MFMA tiles per wave in the scans (1 or 2)
 };
 
-// states_given: the backward takes the forward's chunk states (no state scan)
+// states_given: the backward takes the forward's chunk states (no state
+// scan).  A forward with p->h_packed and a backward with states_given plan
+// jointly (one segment count for both, so that the backward can apply the
+// forward's segment transitions).
 Plan make_plan(const gdr_problem* p, bool bwd, bool states_given = false);
 
 // Workspace layout helpers: every region is 256-byte aligned.
@@ -40,19 +43,23 @@ size_t cp_workspace_bytes(const Plan& pl, int Hv);
 // states_given: the forward's chunk-start states are an input (no state scan)
 size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl, bool states_given);
 
+// trans: [N * Hv, cp, K, K] fp32, where the transition pass leaves every
+// segment transition T_seg for the backward (NULL: kept in the workspace).
 gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const void* g, const void* beta, const float* h0,
-                      float* gcum, void* A, void* o, void* h, float* ht, void* ws,
+                      float* gcum, void* A, void* o, void* h, float* trans, float* ht, void* ws,
                       hipStream_t st);
 
 // graw: the gate input (use_gate only, else NULL); dA_log, ddt_bias nullable.
 // hstates: the forward's chunk-start states in the packed layout, or
-// NULL to recompute them.
+// NULL to recompute them.  trans (with hstates, nullable): the forward's
+// segment transitions for the same plan.
 gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const float* gcum, const void* graw, const void* beta,
                       const void* A, const void* dO, const float* dht, const float* h0,
-                      const void* hstates, void* dq, void* dk, void* dv, void* dbeta, void* dg,
-                      float* dh0, float* dA_log, float* ddt_bias, void* ws, hipStream_t st);
+                      const void* hstates, const float* trans, void* dq, void* dk, void* dv,
+                      void* dbeta, void* dg, float* dh0, float* dA_log, float* ddt_bias, void* ws,
+                      hipStream_t st);
 
 // Token-by-token recurrence (decode and other short inputs), no workspace.
 gdr_status launch_recurrent(const gdr_problem* p, const void* q, const void* k, const void* v,

@@ -60,6 +60,11 @@ struct ScanArgs {
   float* ht;              // final state, nullable
   const float* seg_start; // [units, P, K, V] fp32 segment start states (P > 1)
   float* seg_out;         // [units, P, K, 2V] fp32 augmented end states (pass 1)
+  // [units, P, K, K] fp32 segment transitions T_seg kept for the backward
+  // (nullable).  Forward: pass 1 writes T_seg here instead of into seg_out
+  // and pass 2 reads it back.  Backward (reverse): pass 2 applies the
+  // forward's T_seg transposed, which is the state gradient's transition.
+  float* trans;
   const int32_t* cu;
   const int32_t* offs;
   int N, T, Hq, Hv;
@@ -310,7 +315,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (OUT && c + 1 < sr.c1) prefetch(c + 1);
-    if (HST && !a.h_svf) {
+    if (HST && !a.h_vm && !a.h_svf) {
       __syncthreads();  // every wave's part of the staged state is in Hs
       T* hp = reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV;
       constexpr int PR = CW / 8;
@@ -429,7 +434,11 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
   }
 
   if (MODE == MODE_AUG) {
-    float* so = a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
+    // T_seg to the kept transitions when there are any, else beside B_seg
+    const bool kept = isT && a.trans;
+    float* so = kept ? a.trans + ((int64_t)unit * a.P + p) * KV
+                     : a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
+    const int ld = kept ? kDim : 2 * kDim;
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
@@ -437,7 +446,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = 16 * kb + 4 * grp + e, lc = cw0 + 16 * vb + col;
-          so[key * (2 * kDim) + cb0 + lc] = S[kb][vb][e];
+          so[key * ld + cb0 + lc] = S[kb][vb][e];
         }
   } else if (a.ht && p == sr.p_last) {
 #pragma unroll
@@ -756,6 +765,13 @@ static __global__ __launch_bounds__(256) void cp_combine_kernel(ScanArgs a) {
     const int src = a.reverse ? p + 1 : p - 1;
     const float* prev = a.seg_out + ((int64_t)unit * a.P + src) * (2 * KV);
     float* dst = const_cast<float*>(a.seg_start) + ((int64_t)unit * a.P + p) * KV;
+    // the matrix applied to the chained value, element (r, s) at
+    // tm[r * trs + s * tcs]: the transition beside B_seg in seg_out (the
+    // backward's own pass 1 leaves the transposed one there), or the kept
+    // forward transition, transposed for the backward
+    const float* tm = a.trans ? a.trans + ((int64_t)unit * a.P + src) * KV : prev;
+    const int trs = a.trans ? (a.reverse ? 1 : kDim) : 2 * kDim;
+    const int tcs = (a.trans && a.reverse) ? kDim : 1;
     f32x4 acc[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -765,7 +781,7 @@ static __global__ __launch_bounds__(256) void cp_combine_kernel(ScanArgs a) {
         acc[rt][e] = prev[(r0 + 4 * grp + e) * (2 * kDim) + kDim + c0 + col];
       if (jstep > 1) {
         for (int st = 0; st < 32; ++st) {
-          const float av = prev[(r0 + col) * (2 * kDim) + 4 * st + grp];
+          const float av = tm[(r0 + col) * trs + (4 * st + grp) * tcs];
           const float bv = Sp[(4 * st + grp) * 17 + col];
           acc[rt] = mfma16f32(av, bv, acc[rt]);
         }

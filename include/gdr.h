@@ -166,6 +166,30 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
                          float* g_cum, void* A, void* o, void* h, float* final_state,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward that keeps what the backward needs (the pages' autograd
+ * integration, "flashqla-linear-attention", Integration with PyTorch
+ * Autograd: the forward saves what its backward takes).  gdr_chunk_fwd with
+ * p->h_packed = 1, plus:
+ *   out: h (required), the packed chunk-start states gdr_chunk_bwd_states
+ *        reads
+ *        trans: when the plan splits sequences into T-segments, each
+ *        segment's state transition T_seg (S_end = T_seg S_start + B_seg),
+ *        fp32 [N * Hv][cp_segments][K][K], gdr_chunk_trans_size(p) bytes;
+ *        required when that size is nonzero, ignored (may be NULL) when it
+ *        is zero.  Entries of the first and last segment of each sequence
+ *        are never written or read.
+ * A forward with h_packed = 1 and the backward that takes its states plan
+ * together (one segment count for both, gdr_plan_info), so that the
+ * backward applies the transposed T_seg instead of forming its own
+ * transitions.  Errors: GDR_ERR_ARG when h_packed != 1, GDR_ERR_NULL for a
+ * missing h or trans, else as gdr_chunk_fwd. */
+size_t gdr_chunk_trans_size(const gdr_problem* p);
+gdr_status gdr_chunk_fwd_states(const gdr_problem* p, const void* q, const void* k,
+                                const void* v, const void* g, const void* beta,
+                                const float* initial_state, float* g_cum, void* A, void* o,
+                                void* h, float* trans, float* final_state, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Forward without allocation, for callers that cannot call hipMalloc or take
  * a caller-owned workspace: code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation.  Same arguments, results and
@@ -230,19 +254,26 @@ gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k
  *        16 vb + c and key 32 kb + 4 g + e (e < 4), 32 kb + 16 + 4 g + e - 4
  *        (e >= 4) -- the order the kernels hold it in, so that it is written
  *        and read in 1 KiB contiguous pieces
+ *        trans (nullable), the segment transitions gdr_chunk_fwd_states
+ *        kept for the same problem and inputs; when the plan splits
+ *        sequences the state-gradient scan then applies them transposed
+ *        (the gradient's transition over a segment is T_seg^T) instead of
+ *        forming its own, which halves its transition pass; NULL: it forms
+ *        them (ignored when the plan splits nothing)
  *        g, the gate's raw input (use_gate only; NULL otherwise, and so are
  *        dA_log, ddt_bias)
  * The states are not recomputed: only the reverse state-gradient scan runs
  * before the per-chunk gradients, and the workspace
- * (gdr_chunk_bwd_states_workspace_size) holds no state buffer.  States from
- * another problem or other inputs give meaningless gradients. */
+ * (gdr_chunk_bwd_states_workspace_size) holds no state buffer.  States or
+ * transitions from another problem or other inputs give meaningless
+ * gradients. */
 gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void* k,
                                 const void* v, const float* g_cum, const void* g,
                                 const void* beta, const void* A, const void* do_,
                                 const float* dht, const float* initial_state, const void* h,
-                                void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
-                                float* dA_log, float* ddt_bias, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                const float* trans, void* dq, void* dk, void* dv, void* dbeta,
+                                void* dg, float* dh0, float* dA_log, float* ddt_bias,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Token-by-token forward for short inputs: decode steps, a few speculative
  * tokens, or a prefill continued from a cached state (the "state-cached
@@ -301,7 +332,8 @@ gdr_status gdr_prepare_chunk_token_starts_i64(const int64_t* cu, int64_t n_plus_
 
 /* The launch plan the library picks for `p` in one direction (backward != 0:
  * gdr_chunk_bwd, or gdr_chunk_bwd_states when p->h_packed; else
- * gdr_chunk_fwd); it depends only on shapes and those flags:
+ * gdr_chunk_fwd / gdr_chunk_fwd_states); it depends only on shapes and those
+ * flags.  With p->h_packed both directions share one segment count:
  * *cp_segments = T-segments per sequence (1 = no context parallelism),
  * *wave_tiles = 16-column state tiles per wave in the scans (1 or 2).
  * A nonzero cp_segments / wave_tiles in `p` fixes that choice for both. */

@@ -155,6 +155,38 @@ def test_plan_depends_only_on_shapes():
     assert plan(good(B=2, N=2, T=256, Hq=32, Hv=32), 0)[0] == 1
 
 
+def test_states_path_plans_both_directions_together():
+    # a forward that keeps packed states and the backward that takes them
+    # split sequences the same way, so that the backward can apply the
+    # forward's segment transitions
+    shapes = [dict(B=1, N=1, T=65536, Hq=32, Hv=32), dict(B=1, N=1, T=16384, Hq=16, Hv=32),
+              dict(B=4, N=4, T=8192, Hq=16, Hv=32), dict(B=2, N=2, T=4096, Hq=32, Hv=32),
+              dict(B=1, N=1, T=32768, Hq=4, Hv=8)]
+    for kw in shapes:
+        f = plan(good(h_packed=1, **kw), 0)
+        b = plan(good(h_packed=1, **kw), 1)
+        assert f[0] == b[0], (kw, f, b)
+    assert plan(good(h_packed=1, B=1, N=1, T=65536, Hq=32, Hv=32), 0)[0] > 1
+    for cp in (2, 3, 5):
+        kw = dict(B=1, N=1, T=4096, Hq=2, Hv=4, cp_segments=cp)
+        assert plan(good(h_packed=1, **kw), 0)[0] == plan(good(h_packed=1, **kw), 1)[0] == cp
+
+
+def test_transition_buffer_size():
+    P = lambda **kw: ctypes.byref(good(**kw))
+    # one fp32 K x K matrix per (sequence, value head, segment) of a split plan
+    assert lib.gdr_chunk_trans_size(P(h_packed=1, B=1, N=1, T=4096, Hq=2, Hv=4,
+                                      cp_segments=3)) == 1 * 4 * 3 * 128 * 128 * 4
+    assert lib.gdr_chunk_trans_size(P(h_packed=1, B=1, N=1, T=4096, Hq=2, Hv=4,
+                                      cp_segments=1)) == 0
+    # nothing is kept without the states path
+    assert lib.gdr_chunk_trans_size(P(h_packed=0, B=1, N=1, T=4096, Hq=2, Hv=4,
+                                      cp_segments=3)) == 0
+    cp, _ = plan(good(h_packed=1, B=1, N=1, T=65536, Hq=32, Hv=32), 0)
+    assert lib.gdr_chunk_trans_size(P(h_packed=1, B=1, N=1, T=65536, Hq=32, Hv=32)) == \
+        32 * cp * 128 * 128 * 4
+
+
 def test_null_and_workspace_errors_before_any_device_work():
     p = good()
     P = ctypes.c_void_p
@@ -191,6 +223,22 @@ def test_null_and_workspace_errors_before_any_device_work():
     gate_args[16] = gate_args[17] = None  # the parameter gradients are optional
     st = lib.gdr_chunk_bwd_gate(ctypes.byref(pg), *gate_args, 1, None)
     assert _lib.STATUS[st] == "GDR_ERR_WORKSPACE"
+
+
+def test_states_forward_rejections():
+    P = ctypes.c_void_p
+    req = [P(16)] * 10   # q, k, v, g, beta, initial_state, g_cum, A, o, h
+
+    def call(p, h=P(16), trans=None):
+        a = list(req)
+        a[9] = h
+        return _lib.STATUS[lib.gdr_chunk_fwd_states(ctypes.byref(p), *a, trans, None, None, 0,
+                                                    None)]
+    assert call(good()) == "GDR_ERR_ARG"                   # h_packed = 0
+    assert call(good(h_packed=1), h=None) == "GDR_ERR_NULL"
+    split = good(h_packed=1, B=1, N=1, T=4096, cp_segments=3)
+    assert call(split) == "GDR_ERR_NULL"                   # a split plan needs trans
+    assert "gdr_chunk_trans_size" in lib.gdr_last_error().decode()
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="exercises the no-device path")

@@ -131,31 +131,37 @@ def test_backward_scan_variants(name, vt, cp):
         check(n, x, r, kind, d["cu_seqlens"])
 
 
-def gpu_fwd_bwd_states(d, cp=0):
-    """The autograd path: the forward keeps its chunk-start states
-    (value-major) and the backward takes them instead of recomputing."""
+def gpu_fwd_bwd_states(d, cp=0, use_trans=True, vt=0):
+    """The autograd path: the forward keeps its chunk-start states (packed)
+    and, for a split plan, its segment transitions; the backward takes them
+    instead of recomputing (use_trans=False: it forms its own transitions)."""
     import gated_delta_rule_66_amd as gdr
     dd = to_dev(d)
     cu_cpu = d["cu_seqlens"]
-    g_cum, A, o, h, ht = gdr.chunk_gated_delta_rule_fwd(
+    g_cum, A, o, h, trans, ht = gdr.chunk_gated_delta_rule_fwd_states(
         dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
         initial_state=dd["h0"], output_final_state=True, cu_seqlens=dd["cu_seqlens"],
-        cp_segments=cp, cu_seqlens_cpu=cu_cpu, output_h=True, h_packed=True)
+        cp_segments=cp, cu_seqlens_cpu=cu_cpu, wave_tiles=vt)
     grads = gdr.chunk_gated_delta_rule_bwd(
         dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dd["dht"],
         scale=dd["scale"], initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
-        dg_dtype=dd["g"].dtype, cp_segments=cp, cu_seqlens_cpu=cu_cpu, h=h)
+        dg_dtype=dd["g"].dtype, cp_segments=cp, cu_seqlens_cpu=cu_cpu, h=h,
+        trans=trans if use_trans else None, wave_tiles=vt)
     torch.cuda.synchronize()
     return h, grads
 
 
-@pytest.mark.parametrize("name,cp", [("dense_state_dht", 1), ("varlen", 1), ("fp16_gva", 1),
-                                     ("varlen_empty_seq", 1), ("gva_group3", 1),
-                                     ("long_slow_decay", 4), ("varlen", 3)])
-def test_backward_from_the_forward_states(name, cp):
+@pytest.mark.parametrize("name,cp,use_trans,vt", [
+    ("dense_state_dht", 1, True, 0), ("varlen", 1, True, 0), ("fp16_gva", 1, True, 0),
+    ("varlen_empty_seq", 1, True, 0), ("gva_group3", 1, True, 0),
+    ("long_slow_decay", 4, True, 1), ("long_slow_decay", 4, True, 2),
+    ("long_slow_decay", 4, False, 1), ("varlen", 3, True, 0), ("varlen", 3, False, 0),
+    ("dense_state_dht", 2, True, 2), ("fp16_gva", 3, True, 1), ("gva_group4", 2, True, 0),
+    ("varlen_empty_seq", 2, True, 0)])
+def test_backward_from_the_forward_states(name, cp, use_trans, vt):
     d = gdr_synth.make(CASES[name])
-    print("case", name, "cp", cp, flush=True)
-    h, g = gpu_fwd_bwd_states(d, cp=cp)
+    print("case", name, "cp", cp, "trans", use_trans, "wave_tiles", vt, flush=True)
+    h, g = gpu_fwd_bwd_states(d, cp=cp, use_trans=use_trans, vt=vt)
     ref = oracle_grads(d)
     for nm, kind, x, r in zip(NAMES, KINDS, g, ref):
         check(nm, x, r, kind, d["cu_seqlens"])
@@ -182,3 +188,33 @@ def test_packed_h_holds_the_default_states():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     check("o", b[2], np64(a[2]), "tok", d["cu_seqlens"])
     assert torch.equal(a[4], b[4])
+
+
+def test_kept_transitions_are_the_segment_maps():
+    """Each kept T_seg is the linear part of the segment's state map: for any
+    start state S0, the oracle's end state from S0 minus its end state from
+    zero is T_seg S0 (the recurrence is affine in the state)."""
+    import gated_delta_rule_66_amd as gdr
+    d = gdr_synth.make(P("trans", B=2, T=700, Hq=1, Hv=2, init_state=True))
+    dd = to_dev(d)
+    P_ = 4   # 11 chunks per sequence: segments of chunks [0,3) [3,6) [6,9) [9,11)
+    out = gdr.chunk_gated_delta_rule_fwd_states(
+        dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
+        initial_state=dd["h0"], cp_segments=P_)
+    torch.cuda.synchronize()
+    trans = out[4].cpu().double().view(2 * 2, P_, 128, 128)
+    rng = np.random.default_rng(11)
+    for n in range(2):
+        for p in (1, 2):   # the segments that are neither first nor last
+            t0, t1 = 64 * 3 * p, 64 * 3 * (p + 1)
+            sl = lambda x: np64(x[n:n + 1, t0:t1])
+            args = (sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(d["beta"]), d["scale"])
+            s0 = rng.standard_normal((1, 2, 128, 128)) * 0.1
+            _, e1 = oracle.fwd(*args, initial_state=s0)
+            _, e0 = oracle.fwd(*args, initial_state=np.zeros_like(s0))
+            for h in range(2):
+                want = e1[0, h] - e0[0, h]
+                got = trans[n * 2 + h, p].numpy() @ s0[0, h]
+                r = ratio(got, want)
+                print("sequence", n, "segment", p, "head", h, "ratio", r, flush=True)
+                assert r <= TOL, (n, p, h, r)
