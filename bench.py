@@ -55,7 +55,8 @@ CONFIGS = {
 STATE_BYTES = 128 * 128 * 4     # one fp32 state, per (sequence, value head)
 FLUSH_BYTES = 512 << 20         # written before each cold run: more than the 256 MiB MALL
 FWD_KERNELS = ("fwd_prep", "scan_out", "scan_aug", "scan_state", "cp_combine_fwd")
-BWD_KERNELS = ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "grad", "gate_param_grad")
+BWD_KERNELS = ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "bwd_pipe", "grad",
+               "gate_param_grad")
 
 
 def alg_bytes_per_unit(direction, r, isz=2, gsz=2):
@@ -297,6 +298,10 @@ class Case:
                                         cu_seqlens_cpu=cu_cpu, cp_segments=cp, wave_tiles=vt,
                                         backward=(d_ == "bwd"), h_packed=keep)
                       for d_ in ("fwd", "bwd")}
+        # the backward's pipeline on the states path: (slices, chunk bounds)
+        self.pipe = (gdr.pipeline_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
+                                       cu_seqlens_cpu=cu_cpu, cp_segments=cp, wave_tiles=vt)
+                     if keep else (0, []))
 
         # the autograd op's calls: the forward keeps its chunk-start states
         # (packed) and the segment transitions of a split plan, and the
@@ -516,10 +521,21 @@ def main():
     avg_s = kernels[dom][0] / kernels[dom][1] * 1e-3
     ddir = kernel_direction(dom)
     alg = fwd_bytes if ddir == "fwd" else bwd_bytes
+    alg_desc = ("minimum bytes of the %s pass (%s B per (token, value head) + fp32 states)"
+                % (ddir, round(alg_bytes_per_unit(ddir, Hq / Hv), 1)))
     dom_cp = case.plans[ddir][0]
     wl_key = args.workload + ("+qk_l2norm" if qkn else "") + ("+gate" if args.gate else "")
     operand = kernel_bytes(dom, B, T, Hq, Hv, case.nchunks, case.N, dom_cp, qk_norm=qkn,
                            states=not args.recompute_states)
+    if dom == "grad" and case.pipe[0] > 0:
+        # pipelined: the gradient launch covers chunks bounds[0] .. bounds[1]
+        # of every sequence (the other chunks' gradients run beside the scan)
+        covered = case.N * min(64 * case.pipe[1][1], T)
+        alg = pass_bytes("bwd", covered, Hq, Hv, case.N, 0)
+        alg_desc = ("minimum bytes of the backward for the tokens the launch covers (%d of %d; "
+                    "%s B per (token, value head))"
+                    % (covered, case.tokens, round(alg_bytes_per_unit("bwd", Hq / Hv), 1)))
+        operand = None if operand is None else operand * covered / case.tokens
     traffic = measured_traffic(dom, wl_key, operand)
     achieved = alg / avg_s / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
@@ -527,9 +543,7 @@ def main():
                 "traffic": traffic,
                 "traffic_over_alg": None if traffic is None else round(traffic / alg, 3),
                 "algorithmic_bytes_per_launch": int(alg),
-                "algorithmic_bytes": "minimum bytes of the %s pass (%s B per (token, value head)"
-                                     " + fp32 states)" % (ddir, round(alg_bytes_per_unit(
-                                         ddir, Hq / Hv), 1)),
+                "algorithmic_bytes": alg_desc,
                 "avg_launch_us": round(avg_s * 1e6, 2),
                 "operand_bytes_per_launch": None if operand is None else int(operand),
                 "operand_frac": None if operand is None else
@@ -538,7 +552,10 @@ def main():
     # counter traffic of whole passes over their minimum, where every kernel
     # of the pass has a committed counter figure
     for d_, kset, nb in (("fwd", FWD_KERNELS, fwd_bytes), ("bwd", BWD_KERNELS, bwd_bytes)):
-        tr = [measured_traffic(k_, wl_key, 0) for k_ in kernels if k_ in kset]
+        # per step: each kernel's bytes per launch times its launches per step
+        tr = [None if measured_traffic(k_, wl_key, 0) is None else
+              measured_traffic(k_, wl_key, 0) * kernels[k_][1] / args.steps
+              for k_ in kernels if k_ in kset]
         roofline["%s_traffic_over_alg" % d_] = (round(sum(tr) / nb, 3)
                                                  if tr and all(x is not None for x in tr) else None)
 

@@ -538,14 +538,31 @@ def prepare_chunk_offsets(cu_seqlens: torch.Tensor, chunk_size: int):
 def plan_info(q, v, g_dtype=None, cu_seqlens=None, cu_seqlens_cpu=None, cp_segments=0,
               wave_tiles=0, backward=False, h_packed=False):
     """``(cp_segments, wave_tiles)`` the library plans for these shapes, for the
-    forward pass or (``backward=True``) the backward pass; ``h_packed`` as in
-    the forward (a forward that keeps packed states plans one tile per wave)."""
+    forward pass or (``backward=True``) the backward pass; ``h_packed``: the
+    states path (a forward that keeps packed states, and the backward that
+    takes them), which plans one tile per wave for the forward and one
+    segment count for both directions."""
     c = _Call(q, v, q.dtype if g_dtype is None else g_dtype, None, cu_seqlens, cu_seqlens_cpu,
               False, cp_segments, wave_tiles, h_packed=h_packed)
     cp = ctypes.c_int32(0)
     vt = ctypes.c_int32(0)
     check(lib.gdr_plan_info(c.ref, 1 if backward else 0, ctypes.byref(cp), ctypes.byref(vt)))
     return int(cp.value), int(vt.value)
+
+
+def pipeline_info(q, v, cu_seqlens=None, cu_seqlens_cpu=None, cp_segments=0, wave_tiles=0):
+    """The backward's pipeline for these shapes on the states path (the
+    autograd op's backward): ``(slices, bounds)``; with ``slices > 0`` the
+    state-gradient scan runs in ranges of chunks ``bounds[i] .. bounds[i+1]``
+    and the last launch runs the gradients of chunks ``bounds[0] ..
+    bounds[1]`` alone; ``(0, [])``: one scan launch, then one gradient
+    launch."""
+    c = _Call(q, v, q.dtype, None, cu_seqlens, cu_seqlens_cpu, False, cp_segments, wave_tiles,
+              h_packed=True)
+    n = ctypes.c_int32(0)
+    b = (ctypes.c_int32 * 9)()
+    check(lib.gdr_bwd_pipeline_info(c.ref, ctypes.byref(n), b, 9))
+    return int(n.value), [int(x) for x in b[:n.value + 1]] if n.value else []
 
 
 class KernelTimer:

@@ -49,7 +49,7 @@ EXPORTS = [
     "gdr_prepare_chunk_token_starts_i64", "gdr_profile_enable", "gdr_profile_read",
     "gdr_plan_info", "gdr_recurrent_fwd", "gdr_chunk_bwd_gate", "gdr_chunk_fwd_noalloc",
     "gdr_chunk_bwd_states", "gdr_chunk_bwd_states_workspace_size", "gdr_chunk_fwd_states",
-    "gdr_chunk_trans_size",
+    "gdr_chunk_trans_size", "gdr_bwd_pipeline_info",
 ]
 
 
@@ -83,6 +83,9 @@ def _declare(lib):
     lib.gdr_chunk_bwd_states_workspace_size.argtypes = [PP]
     lib.gdr_chunk_bwd_states_workspace_size.restype = S
     lib.gdr_chunk_bwd_states.argtypes = [PP] + [P] * 21 + [S, P]
+    lib.gdr_bwd_pipeline_info.argtypes = [PP, ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
+    lib.gdr_bwd_pipeline_info.restype = st
     lib.gdr_chunk_trans_size.argtypes = [PP]
     lib.gdr_chunk_trans_size.restype = S
     lib.gdr_chunk_fwd_states.argtypes = [PP] + [P] * 13 + [S, P]

@@ -587,6 +587,17 @@ gdr_status gdr_plan_info(const gdr_problem* p, int backward, int32_t* cp_segment
   return GDR_OK;
 }
 
+gdr_status gdr_bwd_pipeline_info(const gdr_problem* p, int32_t* slices, int32_t* bounds,
+                                 int32_t max_bounds) {
+  gdr_status s = validate(p, nullptr, 0);
+  if (s != GDR_OK) return s;
+  int lo[9];
+  const int S = bwd_pipe_bounds(p, make_plan(p, true, true), true, lo);
+  if (slices) *slices = S;
+  for (int i = 0; bounds && S > 0 && i <= S && i < max_bounds; ++i) bounds[i] = lo[i];
+  return GDR_OK;
+}
+
 gdr_status gdr_profile_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (auto& r : g_prof) {

@@ -61,6 +61,13 @@ struct DhArgs {
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
   int v_only;     // pass 1 runs the value columns only: the transitions are
                   // the forward's, kept (ScanArgs::trans)
+  // Pipelined output pass (sliced != 0): one launch runs segment slice_p of
+  // every (sequence, head), the segments walked one launch after another
+  // from the last; a segment starts from the gradient the launch before
+  // left in seg_start and leaves its own start gradient in seg_next for
+  // segment slice_p - 1 (both [units, P, K, V] fp32, one buffer).
+  int sliced, slice_p, sl_c0, sl_c1;  // sliced: the slice's chunks [sl_c0, sl_c1)
+  float* seg_next;
 };
 
 template <typename T, int VB, int MODE>
@@ -354,35 +361,61 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
 // K dSn and, each a quarter of its tiles, P of chunk c; after it the chain
 // finishes chunk c in rounds of independent products and the helpers issue
 // the loads of the next chunks.
-template <typename T, int OPT>
-__device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
-  typedef typename VT<T>::x8 x8;
-  constexpr int CW = 64;
-  constexpr int LD = 136;
-  constexpr int LDV = CW + 8;
-  constexpr int LDA = 72;
-  __shared__ __align__(16) T Qs[2][64 * LD];
-  __shared__ __align__(16) T Ks[2][64 * LD];
-  __shared__ __align__(16) T Ds[64 * LDV];
-  __shared__ __align__(16) T Es[64 * LDV];  // scale diag(e^gamma) dO
-  __shared__ __align__(16) T As[64 * LDA];
-  __shared__ __align__(16) T Ps[64 * LDA];
-  __shared__ __align__(16) float gam[2][64], eg[2][64], bex[2][64], dl[2][64];
+// LDS of one B2 output-pass workgroup (dh_lh_body), a struct so that a
+// launch can share its LDS with another pass's workgroups.
+template <typename T>
+struct DhLhLds {
+  static constexpr int CW = 64, LD = 136, LDV = CW + 8, LDA = 72;
+  alignas(16) T Qs[2][64 * LD];
+  alignas(16) T Ks[2][64 * LD];
+  alignas(16) T Ds[64 * LDV];
+  alignas(16) T Es[64 * LDV];  // scale diag(e^gamma) dO
+  alignas(16) T As[64 * LDA];
+  alignas(16) T Ps[64 * LDA];
+  alignas(16) float gam[2][64];
+  alignas(16) float eg[2][64];
+  alignas(16) float bex[2][64];
+  alignas(16) float dl[2][64];
   // dSn of the chain's chunk as bf16 operand registers ([column block][k
   // block][lane]), stored by the helpers in the next iteration
-  __shared__ __align__(16) x8 Hx[4][4][64];
+  alignas(16) typename VT<T>::x8 Hx[4][4][64];
+};
+
+template <typename T, int OPT>
+__device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid, DhLhLds<T>& L) {
+  typedef typename VT<T>::x8 x8;
+  constexpr int CW = DhLhLds<T>::CW;
+  constexpr int LD = DhLhLds<T>::LD;
+  constexpr int LDV = DhLhLds<T>::LDV;
+  constexpr int LDA = DhLhLds<T>::LDA;
+  auto& Qs = L.Qs;
+  auto& Ks = L.Ks;
+  auto& Ds = L.Ds;
+  auto& Es = L.Es;
+  auto& As = L.As;
+  auto& Ps = L.Ps;
+  auto& gam = L.gam;
+  auto& eg = L.eg;
+  auto& bex = L.bex;
+  auto& dl = L.dl;
+  auto& Hx = L.Hx;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const bool helper = w >= 4;
   const int otid = tid - 256;  // index among the helper threads
   const int vs = bid % a.nvs;
   const int up = bid / a.nvs;
-  const int p = up % a.P, unit = up / a.P;
+  const int p = a.sliced ? a.slice_p : up % a.P, unit = a.sliced ? up : up / a.P;
   const int n = unit / a.Hv, h = unit % a.Hv;
   const int G = a.Hv / a.Hq, hq = h / G;
   const SeqInfo s = seq_info(a.cu, n, a.T);
   const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
-  const SegRange sr = seg_range(nch, a.P, p);
+  SegRange sr = seg_range(nch, a.P, p);
+  if (a.sliced) {  // a dense batch: every sequence has the same slices
+    sr.c0 = a.sl_c0;
+    sr.c1 = a.sl_c1;
+    sr.p_last = a.P - 1;
+  }
   if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;
   const int cb0 = vs * CW;
   const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
@@ -678,6 +711,14 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
         const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
         a.dh0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = Gs[kb][e];
       }
+  } else if (a.sliced && p > 0) {
+    // the gradient entering the previous segment's end, for the next launch
+    float* dst = a.seg_next + ((int64_t)unit * a.P + p - 1) * KV;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dst[(16 * kb + 4 * grp + e) * kDim + cb0 + cw0 + col] = Gs[kb][e];
   }
 }
 
@@ -685,8 +726,9 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid) {
 // launch of 8-wave workgroups: blocks [0, n1) take B1.
 template <typename T, int OPT>
 __global__ __launch_bounds__(512) void bwd_scans_lh_kernel(ScanArgs sa, DhArgs da, int n1) {
+  __shared__ DhLhLds<T> lds;
   if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE, OPT>(sa, xcd_block(blockIdx.x, n1));
-  else dh_lh_body<T, OPT>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
+  else dh_lh_body<T, OPT>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1), lds);
 }
 
 // Pass 1 of the state-gradient scan alone (the forward's states given): with
@@ -730,6 +772,9 @@ struct GradArgs {
   float scale;
   float* gacc;    // GVA: [G - 1 heads][NC, Hq, 8 waves, 8, 64 lanes, 4] fp32 dq / dk rows
   int gva_final;  // GVA: 0 the launch of heads 0 .. G-2, 1 the launch of head G-1
+  // a pipelined slice of a dense batch (sl_len > 0): workgroup row x takes
+  // chunk sl_c0 + x % sl_len of sequence x / sl_len
+  int sl_c0, sl_len;
   int qk_norm;    // q, k rows scaled to unit length before use
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
   // the gate (use_gate): g is the gate input graw, dg is with respect to it,
@@ -752,38 +797,78 @@ struct GradArgs {
 // leaves each head's dq, dk contribution in its fp32 workspace slot; the
 // second takes head G-1, adds the slots in head order to its own
 // contribution and stores dq, dk (the kernel boundary orders the two).
+// LDS of one gradient workgroup (grad_body), a struct so that a launch can
+// share its LDS with another pass's workgroups.
+template <typename T>
+struct GradLds {
+  static constexpr int L7 = 72;   // every 64-wide tile
+  alignas(16) T Qs[QK_TILE];  // q, k, S^T, dSn^T: staggered rows (qk_row)
+  alignas(16) T Ks[QK_TILE];
+  alignas(16) T As[64 * L7];
+  alignas(16) T Ps[64 * L7];
+  alignas(16) T Ss[QK_TILE];    // S[:, half]^T ([v][k]); later dq (ld LD)
+  alignas(16) T Gs_[QK_TILE];   // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma, dk
+  alignas(16) T Vs[64 * L7];
+  alignas(16) T Os[64 * L7];    // dO[:, half]
+  alignas(16) T Dls[64 * L7];   // Delta, transposed
+  alignas(16) T DRs[64 * L7];   // dR, transposed
+  alignas(16) T DVs[64 * L7];   // dv of the half, row-major
+  alignas(16) float gam[64];
+  alignas(16) float bet[64];
+  alignas(16) float eg[64];
+  alignas(16) float bex[64];
+  alignas(16) float dl[64];
+  alignas(16) float dbv[8][64];     // v . dR partials per (half, column block)
+  alignas(16) float colE[4][64];    // column sums of dP o P per row block
+  alignas(16) float colE2[4][64];   // column sums of dM o M per row block
+  alignas(16) float red[8];         // <S, dSn> per wave
+  alignas(16) float dgam[64];
+  alignas(16) float fsum[4][4];     // F partials per (row block, lane group)
+  alignas(16) float rowq[64];       // dgamma row terms of the dq side
+  alignas(16) float dbf[64];        // d beta / d (beta input) per row
+  alignas(16) float xinv[2][64];    // 1 / |q|, 1 / |k| per row (q / k normalisation)
+  alignas(16) float gsl[2][64];     // the gate's slope and log decay per row (gate on)
+};
+
+// One (chunk row c, workgroup row by) of the gradient pass; nbx is the
+// number of chunk rows of the launch (the GVA slots' stride).
 template <typename T, bool QKN, bool GVA>
-__global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
+__device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int nbx,
+                                          GradLds<T>& L) {
+  if (a.sl_len > 0) c = (c / a.sl_len) * a.nc_dense + a.sl_c0 + c % a.sl_len;
   typedef typename VT<T>::x8 x8;
   constexpr int LD = 136;  // row stride of the dq / dk staging in Ss / Gs_
-  constexpr int L7 = 72;   // every 64-wide tile
-  __shared__ __align__(16) T Qs[QK_TILE];  // q, k, S^T, dSn^T: staggered rows (qk_row)
-  __shared__ __align__(16) T Ks[QK_TILE];
-  __shared__ __align__(16) T As[64 * L7];
-  __shared__ __align__(16) T Ps[64 * L7];
-  __shared__ __align__(16) T Ss[QK_TILE];    // S[:, half]^T ([v][k]); later dq (ld LD)
-  __shared__ __align__(16) T Gs_[QK_TILE];   // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma, dk
-  __shared__ __align__(16) T Vs[64 * L7];
-  __shared__ __align__(16) T Os[64 * L7];    // dO[:, half]
-  __shared__ __align__(16) T Dls[64 * L7];   // Delta, transposed
-  __shared__ __align__(16) T DRs[64 * L7];   // dR, transposed
-  __shared__ __align__(16) T DVs[64 * L7];   // dv of the half, row-major
-  __shared__ float gam[64], bet[64], eg[64], bex[64], dl[64];
-  __shared__ float dbv[8][64];       // v . dR partials per (half, column block)
-  __shared__ float colE[4][64];      // column sums of dP o P per row block
-  __shared__ float colE2[4][64];     // column sums of dM o M per row block
-  __shared__ float red[8];           // <S, dSn> per wave
-  __shared__ float dgam[64];
-  __shared__ float fsum[4][4];       // F partials per (row block, lane group)
-  __shared__ float rowq[64];         // dgamma row terms of the dq side
-  __shared__ float dbf[64];          // d beta / d (beta input) per row
-  __shared__ float xinv[2][64];      // 1 / |q|, 1 / |k| per row (q / k normalisation)
-  __shared__ float gsl[2][64];       // the gate's slope and log decay per row (gate on)
+  constexpr int L7 = GradLds<T>::L7;
+  auto& Qs = L.Qs;
+  auto& Ks = L.Ks;
+  auto& As = L.As;
+  auto& Ps = L.Ps;
+  auto& Ss = L.Ss;
+  auto& Gs_ = L.Gs_;
+  auto& Vs = L.Vs;
+  auto& Os = L.Os;
+  auto& Dls = L.Dls;
+  auto& DRs = L.DRs;
+  auto& DVs = L.DVs;
+  auto& gam = L.gam;
+  auto& bet = L.bet;
+  auto& eg = L.eg;
+  auto& bex = L.bex;
+  auto& dl = L.dl;
+  auto& dbv = L.dbv;
+  auto& colE = L.colE;
+  auto& colE2 = L.colE2;
+  auto& red = L.red;
+  auto& dgam = L.dgam;
+  auto& fsum = L.fsum;
+  auto& rowq = L.rowq;
+  auto& dbf = L.dbf;
+  auto& xinv = L.xinv;
+  auto& gsl = L.gsl;
   // side 1's row terms of the last step (rowacc, k . dX, F, dbeta part), in
   // the P tile's storage (dead once the value halves are done)
   float* const rowv = reinterpret_cast<float*>(Ps);
 
-  const int c = blockIdx.x;
   int n, j;
   if (a.cu) {
     n = find_seq(a.offs, a.N, c);
@@ -798,9 +883,9 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   const int G = a.Hv / a.Hq;
   // GVA: the first launch has (G - 1) x Hq rows of workgroups (head r of
   // group hq at row hq * (G - 1) + r), the second (gva_final) Hq rows
-  const int hq = !GVA ? (int)blockIdx.y / G : a.gva_final ? (int)blockIdx.y : (int)blockIdx.y / (G - 1);
-  const int gr = !GVA ? 0 : a.gva_final ? G - 1 : (int)blockIdx.y % (G - 1);
-  const int h = GVA ? hq * G + gr : (int)blockIdx.y;
+  const int hq = !GVA ? by / G : a.gva_final ? by : by / (G - 1);
+  const int gr = !GVA ? 0 : a.gva_final ? G - 1 : by % (G - 1);
+  const int h = GVA ? hq * G + gr : by;
   const bool store_dqk = !GVA || a.gva_final;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const int wr = w & 3;
@@ -1199,7 +1284,7 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   // element kb of lane l at float4 kb * 64 + l, so each store is 1 KiB
   // contiguous); the last adds the slots, head 0 first, to its own rows.
   if (GVA) {
-    const int64_t slot = (int64_t)gridDim.x * a.Hq * 8 * 512;  // float4s per head slot
+    const int64_t slot = (int64_t)nbx * a.Hq * 8 * 512;  // float4s per head slot
     f32x4* acc = reinterpret_cast<f32x4*>(a.gacc) + (((int64_t)c * a.Hq + hq) * 8 + w) * 512 + l;
     if (a.gva_final) {
 #pragma unroll
@@ -1328,6 +1413,33 @@ __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   }
 }
 
+template <typename T, bool QKN, bool GVA>
+__global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
+  __shared__ GradLds<T> lds;
+  grad_body<T, QKN, GVA>(a, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x, lds);
+}
+
+// Pipelined backward (dense batches, one segment per sequence): the
+// state-gradient scan runs in slices of chunks, last slice first, and each
+// launch after the first also runs the gradient workgroups of the slice the
+// launch before finished.  Blocks [0, nb2) take the scan slice (one 64-column
+// block each, dispatched first, so they start on free CUs); the rest take
+// gradient workgroups, ngx chunk rows per head, on the CUs the scan leaves
+// idle and then on all of them.  The kernel boundary between launches orders
+// a slice's state gradients before their gradient workgroups read them.
+template <typename T, int OPT>
+__global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, int nb2, int ngx) {
+  constexpr size_t B = sizeof(DhLhLds<T>), G = sizeof(GradLds<T>);
+  __shared__ __align__(16) char lds[B > G ? B : G];
+  if ((int)blockIdx.x < nb2) {
+    dh_lh_body<T, OPT>(da, xcd_block(blockIdx.x, nb2), *reinterpret_cast<DhLhLds<T>*>(lds));
+  } else {
+    const int g = (int)blockIdx.x - nb2;
+    grad_body<T, (OPT & 1) != 0, false>(ga, g % ngx, g / ngx, ngx,
+                                        *reinterpret_cast<GradLds<T>*>(lds));
+  }
+}
+
 // d A_log[h] and d dt_bias[h]: the per-chunk shares summed over every chunk of
 // every sequence.  One workgroup per head; thread t adds chunks t, t + 256,
 // ... in order, then a fixed pairwise tree combines the 256 partial sums.
@@ -1360,8 +1472,47 @@ __global__ __launch_bounds__(256) void gate_param_grad_kernel(const float* gpart
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Slices of the pipelined backward (bwd_pipe_kernel), 0 when it does not
+// apply: the forward's states given, a dense batch, no grouped heads, no
+// split along T, the one-tile scan, at least 16 chunks per sequence, and few
+// enough (sequence, head) units that the scan leaves at least half the CUs
+// idle (its 64-column workgroups are then at most 128).
+static int pipe_slices(const gdr_problem* p, const Plan& pl, bool states_given) {
+  if (!states_given || p->cu_seqlens_dev || p->Hq != p->Hv || pl.cp != 1 || pl.vb != 1) return 0;
+  if (pl.nc_dense < 16 || (int64_t)pl.N * p->Hv * 2 > 128) return 0;
+  return 2;  // measured at B=2 T=4096 H=32: 2 slices 449 us, 3 slices 455, 4 slices 498,
+             // one pass 489
+}
+
+// Slice boundaries (chunks [lo[p], lo[p + 1]) form slice p; the scan walks
+// slice S-1 first).  A launch runs one slice of the scan beside the gradient
+// workgroups of the slice after it, so each slice is sized for those to fit
+// on the CUs the scan leaves idle: r = (gradient work of one chunk index) /
+// (idle CUs x scan time of one chunk), about 19 us per gradient workgroup and
+// 2.9 us per scan chunk, and slice p is r times slice p + 1.
+static void pipe_bounds(const gdr_problem* p, const Plan& pl, int S, int* lo) {
+  const double units = (double)pl.N * p->Hv;
+  const double r = units * 19.0 / ((256.0 - 2.0 * units) * 2.9);
+  double w[8], sum = 0.0, x = 1.0;
+  for (int q = S - 1; q >= 0; --q, x *= r) sum += (w[q] = x);
+  const int nch = pl.nc_dense;
+  lo[S] = nch;
+  for (int q = S - 1; q >= 1; --q) {
+    int m = (int)(w[q] / sum * nch + 0.5);
+    if (m < 1) m = 1;
+    lo[q] = lo[q + 1] - m;
+    if (lo[q] < q) lo[q] = q;  // every slice keeps at least one chunk
+  }
+  // the last launch runs slice 0's gradients alone on the whole chip: a
+  // whole number of rounds of 256 workgroups where the sizes allow it
+  int gq = 256;
+  for (int u = (int)units; gq > 1 && u % 2 == 0; u /= 2) gq /= 2;  // 256 / gcd(256, units)
+  if (gq <= lo[1] / 2 && lo[1] - lo[1] % gq >= 1) lo[1] -= lo[1] % gq;
+  lo[0] = 0;
+}
+
 struct BwdLayout {
-  size_t offs, cp, cp2, h, dh, gacc, gpart, total;
+  size_t offs, cp, cp2, h, dh, gacc, gpart, pipe, total;
 };
 
 static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_given) {
@@ -1385,12 +1536,21 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_gi
                   sizeof(float));
   L.gpart = o;
   if (p->use_gate) o += align256((size_t)pl.total_chunks * p->Hv * 2 * sizeof(float));
+  L.pipe = o;  // the pipelined scan's gradients between slices
+  const int S = pipe_slices(p, pl, states_given);
+  if (S) o += align256((size_t)pl.N * p->Hv * S * kDim * kDim * sizeof(float));
   L.total = o;
   return L;
 }
 
 size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl, bool states_given) {
   return bwd_layout(p, pl, states_given).total;
+}
+
+int bwd_pipe_bounds(const gdr_problem* p, const Plan& pl, bool states_given, int* lo) {
+  const int S = pipe_slices(p, pl, states_given);
+  if (S > 0) pipe_bounds(p, pl, S, lo);
+  return S;
 }
 
 // B1 and B2 together: with CP, both augmented passes in one launch, the two
@@ -1508,11 +1668,15 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   da.N = pl.N; da.T = p->T; da.Hq = p->Hq; da.Hv = p->Hv; da.nc_dense = pl.nc_dense;
   da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf; da.qk_norm = sa.qk_norm;
   da.beta_mode = sa.beta_mode;
-  if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, states_given, trans, st);
-  else launch_bwd_scans<T, 1>(pl, sa, da, states_given, trans, st);
+  const int S = pipe_slices(p, pl, states_given);
+  if (S == 0) {
+    if (pl.vb == 2) launch_bwd_scans<T, 2>(pl, sa, da, states_given, trans, st);
+    else launch_bwd_scans<T, 1>(pl, sa, da, states_given, trans, st);
+  }
   // B3-B6
   const bool gva = p->Hq != p->Hv;
   GradArgs ga;
+  memset(&ga, 0, sizeof(ga));
   ga.q = q; ga.k = k; ga.v = v; ga.dO = dO; ga.beta = beta; ga.gcum = gcum; ga.A = A;
   ga.h = hbuf; ga.dh = dhbuf;
   ga.dq = dq;
@@ -1534,7 +1698,48 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   const unsigned nc = (unsigned)pl.total_chunks;
   const int G = p->Hv / p->Hq;
   ga.gva_final = 0;
-  if (pl.total_chunks > 0 && !gva) {
+  if (S > 0) {
+    // launch k runs scan slice S-1-k (while k < S) and the gradient
+    // workgroups of slice S-k (once k > 0)
+    DhArgs d = da;
+    d.P = S;
+    d.nvs = 2;
+    d.sliced = 1;
+    d.seg_start = d.seg_next = reinterpret_cast<float*>(ws + L.pipe);
+    const int nb2 = pl.N * p->Hv * 2;
+    int lo[9];
+    bwd_pipe_bounds(p, pl, states_given, lo);
+    const int opt = (sa.qk_norm ? 1 : 0) | (sa.beta_mode ? 2 : 0);
+    for (int k = 0; k <= S; ++k) {
+      const int pb = S - 1 - k, pg = S - k;
+      GradArgs g2 = ga;
+      int ngx = 0;
+      if (pg < S) {
+        g2.sl_c0 = lo[pg];
+        g2.sl_len = lo[pg + 1] - lo[pg];
+        ngx = pl.N * g2.sl_len;
+      }
+      d.slice_p = pb >= 0 ? pb : 0;
+      d.sl_c0 = pb >= 0 ? lo[pb] : 0;
+      d.sl_c1 = pb >= 0 ? lo[pb + 1] : 0;
+      const int b2 = pb >= 0 ? nb2 : 0;
+      const unsigned blocks = (unsigned)(b2 + ngx * p->Hv);
+      if (blocks == 0) continue;
+      if (b2 == 0) {  // the last slice's gradients alone: the gradient kernel itself
+        if (ga.qk_norm)
+          GDR_LAUNCH("grad", (grad_kernel<T, true, false>), dim3(ngx, p->Hv), dim3(512), st, g2);
+        else
+          GDR_LAUNCH("grad", (grad_kernel<T, false, false>), dim3(ngx, p->Hv), dim3(512), st, g2);
+        continue;
+      }
+      switch (opt) {
+        case 0: GDR_LAUNCH("bwd_pipe", (bwd_pipe_kernel<T, 0>), dim3(blocks), dim3(512), st, d, g2, b2, ngx); break;
+        case 1: GDR_LAUNCH("bwd_pipe", (bwd_pipe_kernel<T, 1>), dim3(blocks), dim3(512), st, d, g2, b2, ngx); break;
+        case 2: GDR_LAUNCH("bwd_pipe", (bwd_pipe_kernel<T, 2>), dim3(blocks), dim3(512), st, d, g2, b2, ngx); break;
+        default: GDR_LAUNCH("bwd_pipe", (bwd_pipe_kernel<T, 3>), dim3(blocks), dim3(512), st, d, g2, b2, ngx);
+      }
+    }
+  } else if (pl.total_chunks > 0 && !gva) {
     if (ga.qk_norm) GDR_LAUNCH("grad", (grad_kernel<T, true, false>), dim3(nc, p->Hv), dim3(512), st, ga);
     else GDR_LAUNCH("grad", (grad_kernel<T, false, false>), dim3(nc, p->Hv), dim3(512), st, ga);
   } else if (pl.total_chunks > 0) {

@@ -42,6 +42,10 @@ gdr_status noalloc_scratch(void** out);
 size_t cp_workspace_bytes(const Plan& pl, int Hv);
 // states_given: the forward's chunk-start states are an input (no state scan)
 size_t bwd_workspace_bytes(const gdr_problem* p, const Plan& pl, bool states_given);
+// The backward's pipeline: the number of slices S (0: one pass) and, in
+// lo[0 .. S], the chunk each slice starts at (lo[S] = chunks per sequence);
+// lo holds at least 9 entries.
+int bwd_pipe_bounds(const gdr_problem* p, const Plan& pl, bool states_given, int* lo);
 
 // trans: [N * Hv, cp, K, K] fp32, where the transition pass leaves every
 // segment transition T_seg for the backward (NULL: kept in the workspace).

@@ -172,6 +172,29 @@ def test_states_path_plans_both_directions_together():
         assert plan(good(h_packed=1, **kw), 0)[0] == plan(good(h_packed=1, **kw), 1)[0] == cp
 
 
+def test_backward_pipeline_plan():
+    n = ctypes.c_int32()
+    b = (ctypes.c_int32 * 9)()
+
+    def info(p):
+        assert lib.gdr_bwd_pipeline_info(ctypes.byref(p), ctypes.byref(n), b, 9) == 0
+        return n.value, (list(b[:n.value + 1]) if n.value else [])
+    # B=2 T=4096 H=32: two slices; the last launch's gradients cover 48 of the
+    # 64 chunks, 3072 workgroups, twelve whole rounds of the 256 CUs
+    assert info(good(B=2, N=2, T=4096, Hq=32, Hv=32)) == (2, [0, 48, 64])
+    # one pass: grouped heads, packed sequences, a scan that fills the chip,
+    # short sequences, a split along T
+    assert info(good(B=2, N=2, T=4096, Hq=16, Hv=32))[0] == 0
+    assert info(varlen(HOST_CU, T=200))[0] == 0
+    assert info(good(B=4, N=4, T=4096, Hq=32, Hv=32))[0] == 0
+    assert info(good(B=2, N=2, T=512, Hq=32, Hv=32))[0] == 0
+    assert info(good(B=1, N=1, T=65536, Hq=32, Hv=32))[0] == 0
+    # fewer units leave more CUs idle beside the scan, which then hide the
+    # gradients of a longer first slice: the slice walked first grows
+    s, bnd = info(good(B=1, N=1, T=1024, Hq=8, Hv=8))
+    assert s == 2 and bnd[0] == 0 and bnd[2] == 16 and 0 < bnd[1] < 8
+
+
 def test_transition_buffer_size():
     P = lambda **kw: ctypes.byref(good(**kw))
     # one fp32 K x K matrix per (sequence, value head, segment) of a split plan

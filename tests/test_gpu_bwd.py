@@ -59,6 +59,11 @@ CASES = {
                           lens=[70, 0, 65]),
     "one_token": P("one", B=1, T=1, Hq=1, Hv=1, init_state=True, dht=True),
     "long_slow_decay": P("long", B=1, T=1500, Hq=2, Hv=2, init_state=True, dht=True, g_shift=2.0),
+    # dense, few heads, 16+ chunks: the states-path backward runs pipelined
+    # (the scan in slices, the gradient workgroups of a slice beside the
+    # next slice's scan); ragged last chunk
+    "pipe": P("pipe", B=2, T=1100, Hq=2, Hv=2, init_state=True, dht=True),
+    "pipe_no_state": P("pipe0", B=1, T=1030, Hq=3, Hv=3),
 }
 
 
@@ -157,7 +162,7 @@ def gpu_fwd_bwd_states(d, cp=0, use_trans=True, vt=0):
     ("long_slow_decay", 4, True, 1), ("long_slow_decay", 4, True, 2),
     ("long_slow_decay", 4, False, 1), ("varlen", 3, True, 0), ("varlen", 3, False, 0),
     ("dense_state_dht", 2, True, 2), ("fp16_gva", 3, True, 1), ("gva_group4", 2, True, 0),
-    ("varlen_empty_seq", 2, True, 0)])
+    ("varlen_empty_seq", 2, True, 0), ("pipe", 1, True, 1), ("pipe_no_state", 1, True, 1)])
 def test_backward_from_the_forward_states(name, cp, use_trans, vt):
     d = gdr_synth.make(CASES[name])
     print("case", name, "cp", cp, "trans", use_trans, "wave_tiles", vt, flush=True)
@@ -218,3 +223,42 @@ def test_kept_transitions_are_the_segment_maps():
                 r = ratio(got, want)
                 print("sequence", n, "segment", p, "head", h, "ratio", r, flush=True)
                 assert r <= TOL, (n, p, h, r)
+
+
+PIPE_OPTS = {"plain": {}, "qk_norm": dict(use_qk_l2norm_in_kernel=True),
+             "beta_logit_neg": dict(use_beta_sigmoid_in_kernel=True, allow_neg_eigval=True),
+             "qk_norm_beta_logit": dict(use_qk_l2norm_in_kernel=True,
+                                        use_beta_sigmoid_in_kernel=True),
+             "gate": "gate"}
+
+
+@pytest.mark.parametrize("name", list(PIPE_OPTS))
+def test_pipelined_backward_equals_the_one_pass_backward(name):
+    """The pipelined backward hands the fp32 state gradient from slice to
+    slice unrounded and runs the same per-chunk work, so its results are the
+    one-pass (recomputing) backward's, bit for bit, under every option."""
+    import gated_delta_rule_66_amd as gdr
+    opts = PIPE_OPTS[name]
+    d = gdr_synth.make(CASES["pipe"])
+    dd = to_dev(d)
+    print("case pipe", name, flush=True)
+    kw = dict(scale=dd["scale"], initial_state=dd["h0"], cp_segments=1, wave_tiles=1)
+    g = dd["g"]
+    if opts == "gate":
+        gen = torch.Generator().manual_seed(3)
+        A_log = (torch.rand(2, generator=gen) * 2 - 1).to(g.device)
+        dt_bias = (torch.rand(2, generator=gen) - 0.5).to(g.device)
+        opts = dict(use_gate_in_kernel=True, A_log=A_log, dt_bias=dt_bias)
+    g_cum, A, o, h, trans, ht = gdr.chunk_gated_delta_rule_fwd_states(
+        dd["q"], dd["k"], dd["v"], g, dd["beta"], **kw, **opts)
+    assert trans is None
+    bkw = dict(kw, dht=dd["dht"], dg_dtype=g.dtype, **opts)
+    if "A_log" in opts:
+        bkw["g_input"] = g
+    piped = gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
+                                           dd["do"], h=h, **bkw)
+    plain = gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
+                                           dd["do"], **bkw)
+    torch.cuda.synchronize()
+    for i, (x, y) in enumerate(zip(piped, plain)):
+        assert (x is None and y is None) or torch.equal(x, y), i

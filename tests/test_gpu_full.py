@@ -17,15 +17,25 @@ def f64(t):
     return None if t is None else t.float().numpy().astype(np.float64)
 
 
-def run_full(i, heads, svf_check=False):
+def run_full(i, heads, svf_check=False, states=False):
+    """states: the launch configuration bench.py times (the autograd op's):
+    the forward keeps its chunk-start states and segment transitions and the
+    backward takes them."""
     import gated_delta_rule_66_amd as gdr
-    prob, d = gdr_synth.make_workload(i)
-    print("workload", i, prob.name, "T", prob.T, "heads", heads, flush=True)
+    if i == "headline":
+        prob = gdr_synth.Problem("fwd_bwd_B2_T4096_H32", B=2, T=4096, Hq=32, Hv=32,
+                                 init_state=True, backward=True, dht=True)
+        d = gdr_synth.make(prob)
+    else:
+        prob, d = gdr_synth.make_workload(i)
+    print("workload", i, prob.name, "T", prob.T, "heads", heads, "states", states, flush=True)
     dev = torch.device("cuda", 0)
     dd = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
     cu_cpu = d["cu_seqlens"]
-    cp, vt = gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"], cu_seqlens_cpu=cu_cpu)
-    print("plan cp", cp, "wave_tiles", vt, flush=True)
+    for bwd in (False, True):
+        cp, vt = gdr.plan_info(dd["q"], dd["v"], cu_seqlens=dd["cu_seqlens"],
+                               cu_seqlens_cpu=cu_cpu, backward=bwd, h_packed=states)
+        print("plan", "bwd" if bwd else "fwd", "cp", cp, "wave_tiles", vt, flush=True)
 
     def fwd_bwd(svf):
         h0 = dd["h0"]
@@ -33,16 +43,22 @@ def run_full(i, heads, svf_check=False):
         if svf:
             h0 = None if h0 is None else h0.transpose(-1, -2).contiguous()
             dht = None if dht is None else dht.transpose(-1, -2).contiguous()
-        g_cum, A, o, _, ht = gdr.chunk_gated_delta_rule_fwd(
-            dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"], initial_state=h0,
-            output_final_state=True, cu_seqlens=dd["cu_seqlens"], state_v_first=svf,
-            cu_seqlens_cpu=cu_cpu)
+        fkw = dict(scale=dd["scale"], initial_state=h0, output_final_state=True,
+                   cu_seqlens=dd["cu_seqlens"], state_v_first=svf, cu_seqlens_cpu=cu_cpu)
+        h = trans = None
+        if states:
+            g_cum, A, o, h, trans, ht = gdr.chunk_gated_delta_rule_fwd_states(
+                dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], **fkw)
+        else:
+            g_cum, A, o, _, ht = gdr.chunk_gated_delta_rule_fwd(
+                dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], **fkw)
         grads = None
         if prob.backward:
             grads = gdr.chunk_gated_delta_rule_bwd(
                 dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dht,
                 scale=dd["scale"], initial_state=h0, cu_seqlens=dd["cu_seqlens"],
-                state_v_first=svf, dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu)
+                state_v_first=svf, dg_dtype=dd["g"].dtype, cu_seqlens_cpu=cu_cpu, h=h,
+                trans=trans)
         torch.cuda.synchronize()
         return o, ht, grads
 
@@ -96,3 +112,22 @@ def test_full_gva_B4_T8192_fp16_fwd_bwd_both_state_layouts():
 
 def test_full_long_T65536_H32_fwd_bwd_context_parallel():
     run_full(4, heads=[5])
+
+
+# the launch configuration bench.py times: the states path
+
+
+def test_full_headline_fwd_bwd_B2_T4096_H32_states():
+    run_full("headline", heads=[0, 13, 31], states=True)
+
+
+def test_full_varlen8_H32_fwd_bwd_states():
+    run_full(2, heads=[7], states=True)
+
+
+def test_full_gva_B4_T8192_fp16_fwd_bwd_states_both_layouts():
+    run_full(3, heads=[5], svf_check=True, states=True)
+
+
+def test_full_long_T65536_H32_fwd_bwd_states_context_parallel():
+    run_full(4, heads=[21], states=True)
