@@ -265,8 +265,8 @@ def _fwd(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
                  if tr_bytes else None)
         check(lib.gdr_chunk_fwd_states(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                        _ptr(initial_state), _ptr(g_cum), _ptr(A), _ptr(o),
-                                       _ptr(h), _ptr(trans), _ptr(ht), _ptr(ws), ws_bytes,
-                                       _stream(dev)))
+                                       _ptr(h), _ptr(trans), tr_bytes, _ptr(ht), _ptr(ws),
+                                       ws_bytes, _stream(dev)))
         return g_cum, A, o, h, trans, ht
     check(lib.gdr_chunk_fwd(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             _ptr(initial_state), _ptr(g_cum), _ptr(A), _ptr(o), _ptr(h), _ptr(ht),
@@ -342,7 +342,9 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
         check(lib.gdr_chunk_bwd_states(c.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                        _ptr(g_input if use_gate_in_kernel else None), _ptr(beta),
                                        _ptr(A), _ptr(do), _ptr(dht), _ptr(initial_state), _ptr(h),
-                                       _ptr(trans), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0),
+                                       _ptr(trans),
+                                       0 if trans is None else trans.numel() * 4,
+                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(dg), _ptr(dh0),
                                        _ptr(dA_log), _ptr(ddt_bias), _ptr(ws), ws_bytes,
                                        _stream(dev)))
         if use_gate_in_kernel:

@@ -82,13 +82,13 @@ def _declare(lib):
     lib.gdr_chunk_fwd.restype = st
     lib.gdr_chunk_bwd_states_workspace_size.argtypes = [PP]
     lib.gdr_chunk_bwd_states_workspace_size.restype = S
-    lib.gdr_chunk_bwd_states.argtypes = [PP] + [P] * 21 + [S, P]
+    lib.gdr_chunk_bwd_states.argtypes = [PP] + [P] * 12 + [S] + [P] * 9 + [S, P]
     lib.gdr_bwd_pipeline_info.argtypes = [PP, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
     lib.gdr_bwd_pipeline_info.restype = st
     lib.gdr_chunk_trans_size.argtypes = [PP]
     lib.gdr_chunk_trans_size.restype = S
-    lib.gdr_chunk_fwd_states.argtypes = [PP] + [P] * 13 + [S, P]
+    lib.gdr_chunk_fwd_states.argtypes = [PP] + [P] * 11 + [S] + [P] * 2 + [S, P]
     lib.gdr_chunk_fwd_states.restype = st
     lib.gdr_chunk_bwd_states.restype = st
     lib.gdr_chunk_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P]

@@ -451,16 +451,20 @@ size_t gdr_chunk_trans_size(const gdr_problem* p) {
 gdr_status gdr_chunk_fwd_states(const gdr_problem* p, const void* q, const void* k,
                                 const void* v, const void* g, const void* beta,
                                 const float* initial_state, float* g_cum, void* A, void* o,
-                                void* h, float* trans, float* final_state, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                void* h, float* trans, size_t trans_bytes, float* final_state,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   const gdr_status s = validate(p, nullptr, 0);
   if (s != GDR_OK) return s;
   if (!p->h_packed)
     return fail(GDR_ERR_ARG, nullptr, 0, "gdr_chunk_fwd_states keeps packed states: h_packed = 1");
   if (!h) return fail(GDR_ERR_NULL, nullptr, 0, "gdr_chunk_fwd_states needs h");
-  if (!trans && gdr_chunk_trans_size(p) > 0)
+  const size_t tneed = gdr_chunk_trans_size(p);
+  if (!trans && tneed > 0)
     return fail(GDR_ERR_NULL, nullptr, 0,
                 "the plan splits sequences: trans needs gdr_chunk_trans_size bytes");
+  if (trans && trans_bytes < tneed)
+    return fail(GDR_ERR_WORKSPACE, nullptr, 0, "trans needs %zu bytes, got %zu", tneed,
+                trans_bytes);
   return chunk_fwd(p, q, k, v, g, beta, initial_state, g_cum, A, o, h, trans, final_state,
                    workspace, workspace_bytes, stream);
 }
@@ -549,11 +553,21 @@ gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void*
                                 const void* v, const float* g_cum, const void* g,
                                 const void* beta, const void* A, const void* do_,
                                 const float* dht, const float* initial_state, const void* h,
-                                const float* trans, void* dq, void* dk, void* dv, void* dbeta,
-                                void* dg, float* dh0, float* dA_log, float* ddt_bias,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                const float* trans, size_t trans_bytes, void* dq, void* dk,
+                                void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
+                                float* ddt_bias, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   gdr_status s = validate(p, nullptr, 0);
   if (s != GDR_OK) return s;
+  if (trans) {
+    // the transitions of the states path's plan, which the backward shares
+    gdr_problem pk = *p;
+    pk.h_packed = 1;
+    const size_t tneed = gdr_chunk_trans_size(&pk);
+    if (trans_bytes < tneed)
+      return fail(GDR_ERR_WORKSPACE, nullptr, 0, "trans needs %zu bytes, got %zu", tneed,
+                  trans_bytes);
+  }
   if (!h) return fail(GDR_ERR_NULL, nullptr, 0, "the forward's chunk-start states h are NULL");
   if (p->use_gate && !g) return fail(GDR_ERR_NULL, nullptr, 0, "the gate input g is NULL");
   if (!p->use_gate && (g || dA_log || ddt_bias))

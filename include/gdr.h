@@ -176,8 +176,9 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
  *        segment's state transition T_seg (S_end = T_seg S_start + B_seg),
  *        fp32 [N * Hv][cp_segments][K][K], gdr_chunk_trans_size(p) bytes;
  *        required when that size is nonzero, ignored (may be NULL) when it
- *        is zero.  Entries of the first and last segment of each sequence
- *        are never written or read.
+ *        is zero; trans_bytes is its size (GDR_ERR_WORKSPACE when smaller).
+ *        Entries of the first and last segment of each sequence are never
+ *        written or read.
  * A forward with h_packed = 1 and the backward that takes its states plan
  * together (one segment count for both, gdr_plan_info), so that the
  * backward applies the transposed T_seg instead of forming its own
@@ -187,8 +188,8 @@ size_t gdr_chunk_trans_size(const gdr_problem* p);
 gdr_status gdr_chunk_fwd_states(const gdr_problem* p, const void* q, const void* k,
                                 const void* v, const void* g, const void* beta,
                                 const float* initial_state, float* g_cum, void* A, void* o,
-                                void* h, float* trans, float* final_state, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                void* h, float* trans, size_t trans_bytes, float* final_state,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Forward without allocation, for callers that cannot call hipMalloc or take
  * a caller-owned workspace: code under HIP graph capture, tight serving
@@ -255,11 +256,12 @@ gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k
  *        (e >= 4) -- the order the kernels hold it in, so that it is written
  *        and read in 1 KiB contiguous pieces
  *        trans (nullable), the segment transitions gdr_chunk_fwd_states
- *        kept for the same problem and inputs; when the plan splits
- *        sequences the state-gradient scan then applies them transposed
- *        (the gradient's transition over a segment is T_seg^T) instead of
- *        forming its own, which halves its transition pass; NULL: it forms
- *        them (ignored when the plan splits nothing)
+ *        kept for the same problem and inputs, trans_bytes its size
+ *        (GDR_ERR_WORKSPACE when below gdr_chunk_trans_size); when the plan
+ *        splits sequences the state-gradient scan then applies them
+ *        transposed (the gradient's transition over a segment is T_seg^T)
+ *        instead of forming its own, which halves its transition pass;
+ *        NULL: it forms them (ignored when the plan splits nothing)
  *        g, the gate's raw input (use_gate only; NULL otherwise, and so are
  *        dA_log, ddt_bias)
  * The states are not recomputed: only the reverse state-gradient scan runs
@@ -271,9 +273,10 @@ gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void*
                                 const void* v, const float* g_cum, const void* g,
                                 const void* beta, const void* A, const void* do_,
                                 const float* dht, const float* initial_state, const void* h,
-                                const float* trans, void* dq, void* dk, void* dv, void* dbeta,
-                                void* dg, float* dh0, float* dA_log, float* ddt_bias,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                const float* trans, size_t trans_bytes, void* dq, void* dk,
+                                void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
+                                float* ddt_bias, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Token-by-token forward for short inputs: decode steps, a few speculative
  * tokens, or a prefill continued from a cached state (the "state-cached

@@ -252,16 +252,23 @@ def test_states_forward_rejections():
     P = ctypes.c_void_p
     req = [P(16)] * 10   # q, k, v, g, beta, initial_state, g_cum, A, o, h
 
-    def call(p, h=P(16), trans=None):
+    def call(p, h=P(16), trans=None, trans_bytes=0):
         a = list(req)
         a[9] = h
-        return _lib.STATUS[lib.gdr_chunk_fwd_states(ctypes.byref(p), *a, trans, None, None, 0,
-                                                    None)]
+        return _lib.STATUS[lib.gdr_chunk_fwd_states(ctypes.byref(p), *a, trans, trans_bytes,
+                                                    None, None, 0, None)]
     assert call(good()) == "GDR_ERR_ARG"                   # h_packed = 0
     assert call(good(h_packed=1), h=None) == "GDR_ERR_NULL"
     split = good(h_packed=1, B=1, N=1, T=4096, cp_segments=3)
     assert call(split) == "GDR_ERR_NULL"                   # a split plan needs trans
     assert "gdr_chunk_trans_size" in lib.gdr_last_error().decode()
+    need = lib.gdr_chunk_trans_size(ctypes.byref(split))
+    assert call(split, trans=P(16), trans_bytes=need - 4) == "GDR_ERR_WORKSPACE"
+    # the backward checks the size of the transitions it is handed too
+    args = [P(16)] * 10 + [P(16), P(16)]  # q .. initial_state, h, trans
+    st = lib.gdr_chunk_bwd_states(ctypes.byref(split), *args, need - 4, *([P(16)] * 9),
+                                  1 << 40, None)
+    assert _lib.STATUS[st] == "GDR_ERR_WORKSPACE" and "trans" in lib.gdr_last_error().decode()
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="exercises the no-device path")
