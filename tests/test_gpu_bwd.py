@@ -262,3 +262,27 @@ def test_pipelined_backward_equals_the_one_pass_backward(name):
     torch.cuda.synchronize()
     for i, (x, y) in enumerate(zip(piped, plain)):
         assert (x is None and y is None) or torch.equal(x, y), i
+
+
+def test_pipelined_backward_in_both_state_layouts():
+    """The pipelined backward hands its fp32 gradient between slices in the
+    key-major layout whatever the caller's state layout: value-first states
+    give the same results, bit for bit, with dh0 transposed."""
+    import gated_delta_rule_66_amd as gdr
+    d = gdr_synth.make(CASES["pipe"])
+    dd = to_dev(d)
+    out = []
+    for svf in (False, True):
+        h0, dht = dd["h0"], dd["dht"]
+        if svf:
+            h0, dht = h0.transpose(-1, -2).contiguous(), dht.transpose(-1, -2).contiguous()
+        kw = dict(scale=dd["scale"], initial_state=h0, state_v_first=svf, cp_segments=1)
+        g_cum, A, o, h, trans, ht = gdr.chunk_gated_delta_rule_fwd_states(
+            dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], **kw)
+        out.append(gdr.chunk_gated_delta_rule_bwd(
+            dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dht,
+            dg_dtype=dd["g"].dtype, h=h, **kw))
+    torch.cuda.synchronize()
+    for x, y in zip(out[0][:5], out[1][:5]):
+        assert torch.equal(x, y)
+    assert torch.equal(out[0][5].transpose(-1, -2), out[1][5])
