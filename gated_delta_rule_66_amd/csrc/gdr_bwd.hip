@@ -830,12 +830,100 @@ struct GradLds {
   alignas(16) float gsl[2][64];     // the gate's slope and log decay per row (gate on)
 };
 
+// What a gradient workgroup loads first: the q, k and A tiles, the per-row
+// values and value half 0's tiles (the half's registers serve half 1 after).
+template <typename T>
+struct GradFirst {
+  TileRegs<128, 512> rq, rk, rs, rg;
+  TileRegs<64, 512> ra, rv, ro;
+  float gr = 0.f, gl = 0.f;
+  T b = from_f<T>(0.f);
+  uint32_t x = 0;  // raw bits of the gate input
+};
+
+// An item's place: global chunk row c, its sequence n and first token t0,
+// its valid rows Cc, the q / k head hq and the value head h (gr: h's index
+// in its group).
+struct GradItem {
+  int c, n;
+  int64_t t0;
+  int Cc, hq, gr, h;
+};
+
+template <bool GVA>
+__device__ __forceinline__ GradItem grad_item(const GradArgs& a, int c, int by) {
+  GradItem it;
+  if (a.sl_len > 0) c = (c / a.sl_len) * a.nc_dense + a.sl_c0 + c % a.sl_len;
+  int j;
+  if (a.cu) {
+    it.n = find_seq(a.offs, a.N, c);
+    j = c - a.offs[it.n];
+  } else {
+    it.n = c / a.nc_dense;
+    j = c % a.nc_dense;
+  }
+  const SeqInfo s = seq_info(a.cu, it.n, a.T);
+  it.c = c;
+  it.t0 = s.start + (int64_t)kChunk * j;
+  it.Cc = (int)min((int64_t)kChunk, s.end - it.t0);
+  const int G = a.Hv / a.Hq;
+  // GVA: the first launch has (G - 1) x Hq rows of workgroups (head r of
+  // group hq at row hq * (G - 1) + r), the second (gva_final) Hq rows
+  it.hq = !GVA ? by / G : a.gva_final ? by : by / (G - 1);
+  it.gr = !GVA ? 0 : a.gva_final ? G - 1 : by % (G - 1);
+  it.h = GVA ? it.hq * G + it.gr : by;
+  return it;
+}
+
+// The loads of a value half's tiles: S^T, dSn^T (packed, 16 KiB each) and
+// the half's V and dO columns.
+template <typename T>
+__device__ __forceinline__ void grad_half_loads(const GradArgs& a, const GradItem& it, int v0,
+                                                TileRegs<128, 512>& rs, TileRegs<128, 512>& rg,
+                                                TileRegs<64, 512>& rv, TileRegs<64, 512>& ro) {
+  const int64_t KV = (int64_t)kDim * kDim;
+  const T* hS = reinterpret_cast<const T*>(a.h) + ((int64_t)it.c * a.Hv + it.h) * KV;
+  const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)it.c * a.Hv + it.h) * KV;
+  tile_load<T, 128, 512>(rs, hS + v0 * kDim, kDim, 64);
+  tile_load<T, 128, 512>(rg, hG + v0 * kDim, kDim, 64);
+  tile_load<T, 64, 512>(rv, reinterpret_cast<const T*>(a.v) + (it.t0 * a.Hv + it.h) * kDim + v0,
+                        (int64_t)a.Hv * kDim, it.Cc);
+  tile_load<T, 64, 512>(ro, reinterpret_cast<const T*>(a.dO) + (it.t0 * a.Hv + it.h) * kDim + v0,
+                        (int64_t)a.Hv * kDim, it.Cc);
+}
+
+// The first loads of an item: q, k, A, the per-row values (threads 0..63),
+// then value half 0.
+template <typename T>
+__device__ __forceinline__ void grad_first_loads(const GradArgs& a, const GradItem& it,
+                                                 GradFirst<T>& f) {
+  const int tid = threadIdx.x;
+  tile_load<T, 128, 512>(f.rq, reinterpret_cast<const T*>(a.q) + (it.t0 * a.Hq + it.hq) * kDim,
+                         (int64_t)a.Hq * kDim, it.Cc);
+  tile_load<T, 128, 512>(f.rk, reinterpret_cast<const T*>(a.k) + (it.t0 * a.Hq + it.hq) * kDim,
+                         (int64_t)a.Hq * kDim, it.Cc);
+  tile_load<T, 64, 512>(f.ra, reinterpret_cast<const T*>(a.A) + (it.t0 * a.Hv + it.h) * kChunk,
+                        (int64_t)a.Hv * kChunk, it.Cc);
+  if (tid < 64) {
+    const int64_t row = (it.t0 + min(tid, it.Cc - 1)) * a.Hv + it.h;
+    f.gr = a.gcum[row];
+    f.gl = a.gcum[(it.t0 + it.Cc - 1) * a.Hv + it.h];
+    f.b = reinterpret_cast<const T*>(a.beta)[row];
+    if (a.gate_A_log)  // raw bits: converted after the tile stores
+      f.x = a.g_dtype == 2 ? reinterpret_cast<const uint32_t*>(a.graw)[row]
+                           : (uint32_t)reinterpret_cast<const uint16_t*>(a.graw)[row];
+  }
+  grad_half_loads<T>(a, it, 0, f.rs, f.rg, f.rv, f.ro);
+}
+
 // One (chunk row c, workgroup row by) of the gradient pass; nbx is the
-// number of chunk rows of the launch (the GVA slots' stride).
+// number of chunk rows of the launch (the GVA slots' stride).  f holds the
+// item's first loads (grad_first_loads), issued by the caller.
 template <typename T, bool QKN, bool GVA>
 __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int nbx,
-                                          GradLds<T>& L) {
-  if (a.sl_len > 0) c = (c / a.sl_len) * a.nc_dense + a.sl_c0 + c % a.sl_len;
+                                          GradLds<T>& L, GradFirst<T>& f) {
+  const GradItem item = grad_item<GVA>(a, c, by);
+  c = item.c;
   typedef typename VT<T>::x8 x8;
   constexpr int LD = 136;  // row stride of the dq / dk staging in Ss / Gs_
   constexpr int L7 = GradLds<T>::L7;
@@ -869,43 +957,22 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
   // the P tile's storage (dead once the value halves are done)
   float* const rowv = reinterpret_cast<float*>(Ps);
 
-  int n, j;
-  if (a.cu) {
-    n = find_seq(a.offs, a.N, c);
-    j = c - a.offs[n];
-  } else {
-    n = c / a.nc_dense;
-    j = c % a.nc_dense;
-  }
-  const SeqInfo s = seq_info(a.cu, n, a.T);
-  const int64_t t0 = s.start + (int64_t)kChunk * j;
-  const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+  const int64_t t0 = item.t0;
+  const int Cc = item.Cc;
   const int G = a.Hv / a.Hq;
-  // GVA: the first launch has (G - 1) x Hq rows of workgroups (head r of
-  // group hq at row hq * (G - 1) + r), the second (gva_final) Hq rows
-  const int hq = !GVA ? by / G : a.gva_final ? by : by / (G - 1);
-  const int gr = !GVA ? 0 : a.gva_final ? G - 1 : by % (G - 1);
-  const int h = GVA ? hq * G + gr : by;
+  const int hq = item.hq, gr = item.gr, h = item.h;
   const bool store_dqk = !GVA || a.gva_final;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const int wr = w & 3;
   const bool hi = w >= 4;
-  const int64_t KV = (int64_t)kDim * kDim;
-  const T* vv = reinterpret_cast<const T*>(a.v);
-  const T* dOg = reinterpret_cast<const T*>(a.dO);
 
   // the value-half tiles: S^T, dSn^T (value-major LDS rows v0 .. v0+63) and
   // V, dO (columns v0 .. v0+63); half 1 is prefetched while half 0 computes
-  TileRegs<128, 512> rs, rg;
-  TileRegs<64, 512> rv, ro;
-  auto load_half = [&](int v0) {
-    const T* hS = reinterpret_cast<const T*>(a.h) + ((int64_t)c * a.Hv + h) * KV;
-    const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)c * a.Hv + h) * KV;
-    tile_load<T, 128, 512>(rs, hS + v0 * kDim, kDim, 64);
-    tile_load<T, 128, 512>(rg, hG + v0 * kDim, kDim, 64);
-    tile_load<T, 64, 512>(rv, vv + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
-    tile_load<T, 64, 512>(ro, dOg + (t0 * a.Hv + h) * kDim + v0, (int64_t)a.Hv * kDim, Cc);
-  };
+  TileRegs<128, 512>& rs = f.rs;
+  TileRegs<128, 512>& rg = f.rg;
+  TileRegs<64, 512>& rv = f.rv;
+  TileRegs<64, 512>& ro = f.ro;
+  auto load_half = [&](int v0) { grad_half_loads<T>(a, item, v0, rs, rg, rv, ro); };
   // (the states are packed: the half's 16 KiB load in storage order and
   // scatter into value-major LDS rows)
   float sds = 0.f;
@@ -920,38 +987,19 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
   // q, k, A and the per-row values (gamma, beta, the gate input) are loaded
   // and stored first; value half 0's tiles (S^T, dSn^T, V, dO) are issued
   // next and stored only after the P / N phase, which overlaps their latency
-  float p_gr = 0.f, p_gl = 0.f;
-  T p_b = from_f<T>(0.f);
-  uint32_t p_x = 0;
+  grad_first_loads<T>(a, item, f);
   {
-    TileRegs<128, 512> rq, rk;
-    TileRegs<64, 512> ra;
-    tile_load<T, 128, 512>(rq, reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim,
-                           (int64_t)a.Hq * kDim, Cc);
-    tile_load<T, 128, 512>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
-                           (int64_t)a.Hq * kDim, Cc);
-    tile_load<T, 64, 512>(ra, reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
-                          (int64_t)a.Hv * kChunk, Cc);
-    if (tid < 64) {
-      const int64_t row = (t0 + min(tid, Cc - 1)) * a.Hv + h;
-      p_gr = a.gcum[row];
-      p_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
-      p_b = reinterpret_cast<const T*>(a.beta)[row];
-      if (a.gate_A_log)  // raw bits: converted after the tile stores
-        p_x = a.g_dtype == 2 ? reinterpret_cast<const uint32_t*>(a.graw)[row]
-                             : (uint32_t)reinterpret_cast<const uint16_t*>(a.graw)[row];
-    }
-    load_half(0);
     if (QKN) {
-      l2norm_rows<T, 512>(rq, xinv[0]);
-      l2norm_rows<T, 512>(rk, xinv[1]);
+      l2norm_rows<T, 512>(f.rq, xinv[0]);
+      l2norm_rows<T, 512>(f.rk, xinv[1]);
     }
-    tile_store_q<T, 512>(Qs, rq);
-    tile_store_q<T, 512>(Ks, rk);
-    tile_store<T, 64, 512>(As, L7, ra);
+    tile_store_q<T, 512>(Qs, f.rq);
+    tile_store_q<T, 512>(Ks, f.rk);
+    tile_store<T, 64, 512>(As, L7, f.ra);
   }
+  const uint32_t p_x = f.x;
   if (tid < 64) {
-    const float gr = p_gr, gl = p_gl, bx = to_f(p_b);
+    const float gr = f.gr, gl = f.gl, bx = to_f(f.b);
     const float bt = (tid < Cc) ? beta_used(bx, a.beta_mode) : 0.f;
     const float e = __expf(gr);
     gam[tid] = gr;
@@ -1369,6 +1417,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
       for (int e = 0; e < 4; ++e)
         stage[(16 * wr + 4 * grp + e) * LD + 16 * kb + col] = from_f<T>(dxv[kb][e]);
   }
+
   // dgamma and dbeta rows, row l on lane l of wave 4: every read of a row
   // issues at once (four rows per lane on a quarter of the lanes would chain
   // their LDS round trips)
@@ -1416,7 +1465,19 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
 template <typename T, bool QKN, bool GVA>
 __global__ __launch_bounds__(512) void grad_kernel(GradArgs a) {
   __shared__ GradLds<T> lds;
-  grad_body<T, QKN, GVA>(a, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x, lds);
+  GradFirst<T> f;
+  grad_body<T, QKN, GVA>(a, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x, lds, f);
+}
+
+// The gradient pass over ngx chunk rows x rows workgroup rows, one
+// workgroup per item.
+template <typename T, bool GVA>
+static void launch_grad(const GradArgs& ga, int ngx, int rows, hipStream_t st) {
+  if (ngx <= 0 || rows <= 0) return;
+  if (ga.qk_norm)
+    GDR_LAUNCH("grad", (grad_kernel<T, true, GVA>), dim3(ngx, rows), dim3(512), st, ga);
+  else
+    GDR_LAUNCH("grad", (grad_kernel<T, false, GVA>), dim3(ngx, rows), dim3(512), st, ga);
 }
 
 // Pipelined backward (dense batches, one segment per sequence): the
@@ -1435,8 +1496,9 @@ __global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, i
     dh_lh_body<T, OPT>(da, xcd_block(blockIdx.x, nb2), *reinterpret_cast<DhLhLds<T>*>(lds));
   } else {
     const int g = (int)blockIdx.x - nb2;
+    GradFirst<T> f;
     grad_body<T, (OPT & 1) != 0, false>(ga, g % ngx, g / ngx, ngx,
-                                        *reinterpret_cast<GradLds<T>*>(lds));
+                                        *reinterpret_cast<GradLds<T>*>(lds), f);
   }
 }
 
@@ -1726,10 +1788,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
       const unsigned blocks = (unsigned)(b2 + ngx * p->Hv);
       if (blocks == 0) continue;
       if (b2 == 0) {  // the last slice's gradients alone: the gradient kernel itself
-        if (ga.qk_norm)
-          GDR_LAUNCH("grad", (grad_kernel<T, true, false>), dim3(ngx, p->Hv), dim3(512), st, g2);
-        else
-          GDR_LAUNCH("grad", (grad_kernel<T, false, false>), dim3(ngx, p->Hv), dim3(512), st, g2);
+        launch_grad<T, false>(g2, ngx, p->Hv, st);
         continue;
       }
       switch (opt) {
@@ -1740,14 +1799,11 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
       }
     }
   } else if (pl.total_chunks > 0 && !gva) {
-    if (ga.qk_norm) GDR_LAUNCH("grad", (grad_kernel<T, true, false>), dim3(nc, p->Hv), dim3(512), st, ga);
-    else GDR_LAUNCH("grad", (grad_kernel<T, false, false>), dim3(nc, p->Hv), dim3(512), st, ga);
+    launch_grad<T, false>(ga, (int)nc, p->Hv, st);
   } else if (pl.total_chunks > 0) {
     for (int fin = 0; fin < 2; ++fin) {
       ga.gva_final = fin;
-      const dim3 gg(nc, fin ? p->Hq : p->Hq * (G - 1));
-      if (ga.qk_norm) GDR_LAUNCH("grad", (grad_kernel<T, true, true>), gg, dim3(512), st, ga);
-      else GDR_LAUNCH("grad", (grad_kernel<T, false, true>), gg, dim3(512), st, ga);
+      launch_grad<T, true>(ga, (int)nc, fin ? p->Hq : p->Hq * (G - 1), st);
     }
   }
   if (gate && (dA_log || ddt_bias))
