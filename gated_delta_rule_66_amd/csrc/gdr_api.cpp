@@ -85,10 +85,14 @@ static double rounds(int64_t wgs, int64_t slots) {
   return r < 1 ? 1.0 : (double)r;
 }
 
-static double bwd_out_cost(int64_t wgs_per_scan, int64_t chunks, int VB, bool states_given) {
+// fill: the mean chain over the longest (packed sequences whose scan blocks
+// start the longest chains first, block_pos), else 1: the total work is
+// spread over the CUs, never shorter than the longest chain.
+static double bwd_out_cost(int64_t wgs_per_scan, int64_t chunks, int VB, bool states_given,
+                           double fill) {
   // with the forward's states given only the state-gradient scan runs
   const double c1 = states_given ? 0.0 : (VB == 1 ? 2.4 : 5.5), c2 = VB == 1 ? 3.3 : 5.5;
-  const double spread = (double)wgs_per_scan * (double)chunks * (c1 + c2) / 256.0;
+  const double spread = (double)wgs_per_scan * (double)chunks * fill * (c1 + c2) / 256.0;
   const double chain = (double)chunks * c2;
   return spread > chain ? spread : chain;
 }
@@ -97,11 +101,16 @@ static double bwd_out_cost(int64_t wgs_per_scan, int64_t chunks, int VB, bool st
 // so its transition pass runs the value columns of every segment but the
 // first, in a launch that fits two workgroups per CU at VB = 1.
 static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd, bool states_given,
-                        bool trans_given = false) {
+                        bool trans_given, double fill) {
   const int64_t nvs0 = 2 / VB, nvs1 = 4 / VB;
   if (!bwd) {
     const bool narrow = VB == 1 && units * P * 2 <= 128;
     const double out = VB == 1 ? (narrow ? 2.55 : 3.1) : 5.0;
+    if (P == 1 && fill < 1.0) {
+      const double spread = (double)(units * nvs0) * (double)maxch * fill * out / 256.0;
+      const double chain = (double)maxch * out;
+      return spread > chain ? spread : chain;
+    }
     if (P == 1) return (double)maxch * out * rounds(units * nvs0, 256);
     const int64_t sc = (maxch + P - 1) / P;
     // one end segment needs only its value columns, the inner ones everything
@@ -110,7 +119,7 @@ static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd, b
     return (double)sc * aug * rounds(wg_aug, VB == 1 ? 512 : 256) + 10.0 * (double)(P - 1) + 16.0 +
            (double)sc * out * rounds(units * P * nvs0, 256);
   }
-  if (P == 1) return bwd_out_cost(units * nvs0, maxch, VB, states_given);
+  if (P == 1) return bwd_out_cost(units * nvs0, maxch, VB, states_given, fill);
   const int64_t sc = (maxch + P - 1) / P;
   const int64_t wg_aug = trans_given ? units * (int64_t)(P - 1) * (nvs1 / 2)
                                      : (states_given ? 1 : 2) * units *
@@ -119,7 +128,7 @@ static double plan_cost(int64_t units, int64_t maxch, int P, int VB, bool bwd, b
   const int64_t slots = (trans_given && VB == 1) ? 512 : 256;
   return (double)sc * aug * rounds(wg_aug, slots) +
          (states_given ? 10.0 : 20.0) * (double)(P - 1) + 16.0 +
-         bwd_out_cost(units * P * nvs0, sc, VB, states_given);
+         bwd_out_cost(units * P * nvs0, sc, VB, states_given, fill);
 }
 
 // Context-parallel plan along T: it depends only on shapes and flags (never
@@ -148,6 +157,10 @@ Plan make_plan(const gdr_problem* p, bool bwd, bool states_given) {
   }
   const int64_t units = (int64_t)p->N * p->Hv;
   const int64_t maxch = (pl.max_len + kChunk - 1) / kChunk;
+  // packed sequences with rank-ordered scan blocks (units a multiple of 8)
+  const double fill = (p->cu_seqlens_host && units % 8 == 0 && maxch > 0)
+                          ? (double)pl.total_chunks / ((double)p->N * (double)maxch)
+                          : 1.0;
   pl.cp = 1;
   pl.vb = 2;
   double best = 1e300;
@@ -164,19 +177,19 @@ Plan make_plan(const gdr_problem* p, bool bwd, bool states_given) {
       if (p->wave_tiles > 0 && VB != p->wave_tiles) continue;
       double c;
       if (!joint) {
-        c = plan_cost(units, maxch, P, VB, bwd, states_given);
+        c = plan_cost(units, maxch, P, VB, bwd, states_given, false, fill);
       } else if (bwd) {  // VB is the backward's; the forward's is vb_keep
-        c = plan_cost(units, maxch, P, vb_keep, false, false) +
-            plan_cost(units, maxch, P, VB, true, true, true);
+        c = plan_cost(units, maxch, P, vb_keep, false, false, false, fill) +
+            plan_cost(units, maxch, P, VB, true, true, true, fill);
       } else {           // VB is the forward's; the backward takes its best
         if (VB != vb_keep) continue;
         double cb = 1e300;
         for (int VBb = 1; VBb <= 2; ++VBb) {
           if (p->wave_tiles > 0 && VBb != p->wave_tiles) continue;
-          const double x = plan_cost(units, maxch, P, VBb, true, true, true);
+          const double x = plan_cost(units, maxch, P, VBb, true, true, true, fill);
           if (x < cb) cb = x;
         }
-        c = plan_cost(units, maxch, P, VB, false, false) + cb;
+        c = plan_cost(units, maxch, P, VB, false, false, false, fill) + cb;
       }
       // a split must win clearly: the model is coarse and splitting adds work
       c *= (P > 1 && fixed == 0) ? 1.1 : 1.0;

@@ -53,6 +53,7 @@ struct DhArgs {
   float* seg_out;          // [units, P, K, 2V]: augmented pass-1 results
   const int32_t* cu;
   const int32_t* offs;
+  const int32_t* order;  // packed input: sequences by chunk count, longest first (block_pos)
   int N, T, Hq, Hv, nc_dense;
   int P, nvs;
   float scale;
@@ -71,7 +72,7 @@ struct DhArgs {
 };
 
 template <typename T, int VB, int MODE>
-__device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
+__device__ __forceinline__ void dh_body(const DhArgs& a, int b, int nb) {
   typedef typename VT<T>::x8 x8;
   constexpr int CW = 64 * VB;
   constexpr int LD = 136;
@@ -85,9 +86,9 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid) {
   __shared__ __align__(16) float gam[64], eg[64], bex[64], dl[64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
-  const int vs = bid % a.nvs;
-  const int up = bid / a.nvs;
-  const int p = up % a.P, unit = up / a.P;
+  const BlockPos bp = block_pos(a.order, b, nb, a.P * a.nvs, a.Hv);
+  const int vs = bp.sub % a.nvs;
+  const int p = bp.sub / a.nvs, unit = bp.unit;
   const int n = unit / a.Hv, h = unit % a.Hv;
   const int G = a.Hv / a.Hq, hq = h / G;
   const SeqInfo s = seq_info(a.cu, n, a.T);
@@ -382,7 +383,7 @@ struct DhLhLds {
 };
 
 template <typename T, int OPT>
-__device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid, DhLhLds<T>& L) {
+__device__ __forceinline__ void dh_lh_body(const DhArgs& a, int b, int nb, DhLhLds<T>& L) {
   typedef typename VT<T>::x8 x8;
   constexpr int CW = DhLhLds<T>::CW;
   constexpr int LD = DhLhLds<T>::LD;
@@ -403,9 +404,10 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid, DhLhLds<T>&
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const bool helper = w >= 4;
   const int otid = tid - 256;  // index among the helper threads
-  const int vs = bid % a.nvs;
-  const int up = bid / a.nvs;
-  const int p = a.sliced ? a.slice_p : up % a.P, unit = a.sliced ? up : up / a.P;
+  // a pipelined slice runs one segment of every unit
+  const BlockPos bp = block_pos(a.order, b, nb, a.sliced ? a.nvs : a.P * a.nvs, a.Hv);
+  const int vs = bp.sub % a.nvs;
+  const int p = a.sliced ? a.slice_p : bp.sub / a.nvs, unit = bp.unit;
   const int n = unit / a.Hv, h = unit % a.Hv;
   const int G = a.Hv / a.Hq, hq = h / G;
   const SeqInfo s = seq_info(a.cu, n, a.T);
@@ -727,15 +729,15 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int bid, DhLhLds<T>&
 template <typename T, int OPT>
 __global__ __launch_bounds__(512) void bwd_scans_lh_kernel(ScanArgs sa, DhArgs da, int n1) {
   __shared__ DhLhLds<T> lds;
-  if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE, OPT>(sa, xcd_block(blockIdx.x, n1));
-  else dh_lh_body<T, OPT>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1), lds);
+  if ((int)blockIdx.x < n1) scan_spec_body<T, MODE_STATE, OPT>(sa, (int)blockIdx.x, n1);
+  else dh_lh_body<T, OPT>(da, (int)blockIdx.x - n1, (int)gridDim.x - n1, lds);
 }
 
 // Pass 1 of the state-gradient scan alone (the forward's states given): with
 // no state-scan LDS beside it two workgroups fit a CU at VB = 1.
 template <typename T, int VB>
 __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_aug_kernel(DhArgs da) {
-  dh_body<T, VB, MODE_AUG>(da, xcd_block(blockIdx.x, gridDim.x));
+  dh_body<T, VB, MODE_AUG>(da, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // The state scan (B1) and the state-gradient scan (B2) are independent (B2
@@ -744,8 +746,8 @@ __global__ __launch_bounds__(256, VB == 1 ? 2 : 1) void dh_aug_kernel(DhArgs da)
 // few (sequence, head) units.
 template <typename T, int VB, int MS, int MD>
 __global__ __launch_bounds__(256, 1) void bwd_scans_kernel(ScanArgs sa, DhArgs da, int n1) {
-  if ((int)blockIdx.x < n1) scan_body<T, VB, MS>(sa, xcd_block(blockIdx.x, n1));
-  else dh_body<T, VB, MD>(da, xcd_block(blockIdx.x - n1, gridDim.x - n1));
+  if ((int)blockIdx.x < n1) scan_body<T, VB, MS>(sa, (int)blockIdx.x, n1);
+  else dh_body<T, VB, MD>(da, (int)blockIdx.x - n1, (int)gridDim.x - n1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1493,7 +1495,7 @@ __global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, i
   constexpr size_t B = sizeof(DhLhLds<T>), G = sizeof(GradLds<T>);
   __shared__ __align__(16) char lds[B > G ? B : G];
   if ((int)blockIdx.x < nb2) {
-    dh_lh_body<T, OPT>(da, xcd_block(blockIdx.x, nb2), *reinterpret_cast<DhLhLds<T>*>(lds));
+    dh_lh_body<T, OPT>(da, (int)blockIdx.x, nb2, *reinterpret_cast<DhLhLds<T>*>(lds));
   } else {
     const int g = (int)blockIdx.x - nb2;
     GradFirst<T> f;
@@ -1580,8 +1582,9 @@ struct BwdLayout {
 static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_given) {
   BwdLayout L;
   size_t o = 0;
-  L.offs = o;
-  if (p->cu_seqlens_dev) o += align256(sizeof(int32_t) * (size_t)(pl.N + 1));
+  L.offs = o;  // chunk offsets, then the sequences' length order
+  if (p->cu_seqlens_dev)
+    o += align256(sizeof(int32_t) * (size_t)(pl.N + 1)) + align256(sizeof(int32_t) * (size_t)pl.N);
   // the two scans run in one launch: each has its own CP buffers
   L.cp = o;
   o += cp_workspace_bytes(pl, p->Hv);
@@ -1690,11 +1693,15 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   const bool states_given = hstates != nullptr;
   const BwdLayout L = bwd_layout(p, pl, states_given);
   const int32_t* offs = nullptr;
+  const int32_t* order = nullptr;
   if (p->cu_seqlens_dev) {
     int32_t* o32 = reinterpret_cast<int32_t*>(ws + L.offs);
-    GDR_LAUNCH("chunk_offsets", chunk_offsets_kernel, dim3(1), dim3(64), st, p->cu_seqlens_dev,
-               pl.N, o32);
+    int32_t* r32 = reinterpret_cast<int32_t*>(ws + L.offs +
+                                              align256(sizeof(int32_t) * (size_t)(pl.N + 1)));
+    GDR_LAUNCH("chunk_offsets", chunk_offsets_kernel, dim3(1), dim3(256), st, p->cu_seqlens_dev,
+               pl.N, o32, r32);
     offs = o32;
+    order = r32;
   }
   float* cp_out = nullptr;
   float* cp_start = nullptr;
@@ -1715,7 +1722,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   memset(&sa, 0, sizeof(sa));
   sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
   sa.h = hbuf;
-  sa.cu = p->cu_seqlens_dev; sa.offs = offs;
+  sa.cu = p->cu_seqlens_dev; sa.offs = offs; sa.order = order;
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1; sa.scale = p->scale; sa.svf = p->state_v_first ? 1 : 0; sa.h_svf = 1;
   sa.qk_norm = p->use_qk_l2norm ? 1 : 0;
@@ -1726,7 +1733,7 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   memset(&da, 0, sizeof(da));
   da.q = q; da.k = k; da.dO = dO; da.beta = beta; da.gcum = gcum; da.A = A; da.dht = dht;
   da.dh = dhbuf; da.dh0 = dh0; da.seg_start = cp2_start; da.seg_out = cp2_out;
-  da.cu = p->cu_seqlens_dev; da.offs = offs;
+  da.cu = p->cu_seqlens_dev; da.offs = offs; da.order = order;
   da.N = pl.N; da.T = p->T; da.Hq = p->Hq; da.Hv = p->Hv; da.nc_dense = pl.nc_dense;
   da.P = 1; da.nvs = 1; da.scale = p->scale; da.svf = sa.svf; da.qk_norm = sa.qk_norm;
   da.beta_mode = sa.beta_mode;

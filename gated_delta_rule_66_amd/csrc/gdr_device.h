@@ -556,6 +556,33 @@ __device__ __forceinline__ int xcd_block(int b, int nblocks) {
   return (b & 7) * (nblocks >> 3) + (b >> 3);
 }
 
+// The (sequence, head) unit of hardware block b of a scan launch with nb
+// blocks, per_unit of them per unit (its segments and column blocks), and
+// the block's index sub within the unit.  The blocks of one unit run on one
+// XCD (xcd_block).  Packed sequences of unequal length (order: the sequences
+// by chunk count, longest first) also start the longest chains first: the
+// XCDs take the units in rank order, rank k on XCD k % 8, so that when there
+// are more blocks than CUs the short chains, not the long ones, wait for a
+// free CU.
+struct BlockPos {
+  int unit, sub;
+};
+__device__ __forceinline__ BlockPos block_pos(const int32_t* order, int b, int nb, int per_unit,
+                                              int Hv) {
+  BlockPos r;
+  if (order && nb % (8 * per_unit) == 0) {
+    const int x = b & 7, y = b >> 3;
+    const int k = (y / per_unit) * 8 + x;
+    r.unit = order[k / Hv] * Hv + k % Hv;
+    r.sub = y % per_unit;
+  } else {
+    const int L = xcd_block(b, nb);
+    r.unit = L / per_unit;
+    r.sub = L % per_unit;
+  }
+  return r;
+}
+
 // Where a (sequence, chunk) pair starts.  Dense batches: sequence n spans
 // tokens [n*T, n*T + T).  Packed input: cu_seqlens.
 struct SeqInfo {

@@ -253,7 +253,8 @@ size_t cp_workspace_bytes(const Plan& pl, int Hv) {
 
 size_t fwd_workspace_bytes(const gdr_problem* p, const Plan& pl) {
   size_t b = 0;
-  if (p->cu_seqlens_dev) b += align256(sizeof(int32_t) * (size_t)(pl.N + 1));
+  if (p->cu_seqlens_dev)  // chunk offsets and the sequences' length order
+    b += align256(sizeof(int32_t) * (size_t)(pl.N + 1)) + align256(sizeof(int32_t) * (size_t)pl.N);
   b += cp_workspace_bytes(pl, p->Hv);
   return b;
 }
@@ -316,12 +317,16 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
                       hipStream_t st) {
   char* wp = reinterpret_cast<char*>(ws);
   const int32_t* offs = nullptr;
+  const int32_t* order = nullptr;
   if (p->cu_seqlens_dev) {
     int32_t* o32 = reinterpret_cast<int32_t*>(wp);
-    GDR_LAUNCH("chunk_offsets", chunk_offsets_kernel, dim3(1), dim3(64), st, p->cu_seqlens_dev, pl.N,
-               o32);
-    offs = o32;
     wp += align256(sizeof(int32_t) * (size_t)(pl.N + 1));
+    int32_t* r32 = reinterpret_cast<int32_t*>(wp);
+    wp += align256(sizeof(int32_t) * (size_t)pl.N);
+    GDR_LAUNCH("chunk_offsets", chunk_offsets_kernel, dim3(1), dim3(256), st, p->cu_seqlens_dev,
+               pl.N, o32, r32);
+    offs = o32;
+    order = r32;
   }
   FwdArgs fa;
   fa.q = q; fa.k = k; fa.v = v; fa.g = g; fa.beta = beta; fa.h0 = h0; fa.gcum = gcum;
@@ -338,7 +343,7 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   memset(&sa, 0, sizeof(sa));
   sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
   sa.o = o; sa.h = h; sa.ht = ht; sa.trans = trans;
-  sa.cu = p->cu_seqlens_dev; sa.offs = offs;
+  sa.cu = p->cu_seqlens_dev; sa.offs = offs; sa.order = order;
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1;
   sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf;

@@ -35,15 +35,27 @@ enum ScanMode { MODE_OUT = 0, MODE_AUG = 1, MODE_STATE = 2, MODE_OUT_H = 3 };
 
 // Chunk offsets of packed sequences, computed on the device so that no
 // device-to-host copy is needed: offs[0] = 0, offs[n+1] = offs[n] +
-// ceil(len_n / 64).
-static __global__ void chunk_offsets_kernel(const int32_t* cu, int N, int32_t* offs) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+// ceil(len_n / 64); and order[k] = the sequence of rank k by chunk count,
+// longest first (ties by index), each thread ranking its sequences against
+// all others.
+static __global__ void chunk_offsets_kernel(const int32_t* cu, int N, int32_t* offs,
+                                            int32_t* order) {
+  if (threadIdx.x == 0) {
     int32_t acc = 0;
     offs[0] = 0;
     for (int n = 0; n < N; ++n) {
       acc += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
       offs[n + 1] = acc;
     }
+  }
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    const int32_t cn = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+      const int32_t cm = (cu[m + 1] - cu[m] + kChunk - 1) / kChunk;
+      rank += (cm > cn || (cm == cn && m < n)) ? 1 : 0;
+    }
+    order[rank] = n;
   }
 }
 
@@ -67,6 +79,7 @@ struct ScanArgs {
   float* trans;
   const int32_t* cu;
   const int32_t* offs;
+  const int32_t* order;  // packed input: sequences by chunk count, longest first (block_pos)
   int N, T, Hq, Hv;
   int nc_dense;
   int P;    // segments per sequence
@@ -101,11 +114,11 @@ __device__ __forceinline__ SegRange seg_range(int nch, int P, int p) {
 // list of ten tiles.
 __host__ __device__ constexpr int tri_idx(int ib, int rb) { return rb * (rb + 1) / 2 + ib; }
 
-// One workgroup's share of a scan pass; bid is the (XCD-renumbered) block
-// index within the pass.  A device function so that two independent passes
-// can share one launch (the backward's state and state-gradient scans).
+// One workgroup's share of a scan pass: block b of the pass's nb (block_pos
+// gives its unit).  A device function so that two independent passes can
+// share one launch (the backward's state and state-gradient scans).
 template <typename T, int VB, int MODE>
-__device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
+__device__ __forceinline__ void scan_body(const ScanArgs& a, int b, int nb) {
   typedef typename VT<T>::x8 x8;
   constexpr int CW = 64 * VB;          // columns per workgroup
   constexpr int LD = 136;              // q / k tile leading dimension
@@ -122,9 +135,9 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
   __shared__ __align__(16) float gam[64], bet[64], eg[64], bex[64], dl[64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
-  const int vs = bid % a.nvs;
-  const int up = bid / a.nvs;
-  const int p = up % a.P, unit = up / a.P;
+  const BlockPos bp = block_pos(a.order, b, nb, a.P * a.nvs, a.Hv);
+  const int vs = bp.sub % a.nvs;
+  const int p = bp.sub / a.nvs, unit = bp.unit;
   const int n = unit / a.Hv, h = unit % a.Hv;
   const int G = a.Hv / a.Hq, hq = h / G;
   const SeqInfo s = seq_info(a.cu, n, a.T);
@@ -463,7 +476,7 @@ __device__ __forceinline__ void scan_body(const ScanArgs& a, int bid) {
 
 template <typename T, int VB, int MODE>
 __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_STATE)) ? 2 : 1) void scan_kernel(ScanArgs a) {
-  scan_body<T, VB, MODE>(a, xcd_block(blockIdx.x, gridDim.x));
+  scan_body<T, VB, MODE>(a, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Forward output pass with specialized waves (one 64-column block per
@@ -483,7 +496,7 @@ __global__ __launch_bounds__(256, (VB == 1 && (MODE == MODE_AUG || MODE == MODE_
 // the default path carries none of their code): bit 0 normalises the q / k
 // rows after their loads, bit 1 maps beta through the runtime beta options.
 template <typename T, int MODE, int OPT, int NCW = 4>
-__device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
+__device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int b, int nb) {
   typedef typename VT<T>::x8 x8;
   constexpr bool OUT = (MODE == MODE_OUT);
   static_assert(NCW == 4 || (NCW == 2 && OUT), "two state waves only for the output pass");
@@ -505,9 +518,9 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
   const bool outw = w >= NCW;
   // state waves: their 16-column block; output waves: their index 0..3
   const int wq = NCW == 4 ? (w & 3) : (outw ? w - NCW : w);
-  const int vs = bid % NVS;
-  const int up = bid / NVS;
-  const int p = up % a.P, unit = up / a.P;
+  const BlockPos bp = block_pos(a.order, b, nb, a.P * NVS, a.Hv);
+  const int vs = bp.sub % NVS;
+  const int p = bp.sub / NVS, unit = bp.unit;
   const int n = unit / a.Hv, h = unit % a.Hv;
   const int G = a.Hv / a.Hq, hq = h / G;
   const SeqInfo s = seq_info(a.cu, n, a.T);
@@ -740,7 +753,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int bid) {
 
 template <typename T, int OPT, int NCW>
 __global__ __launch_bounds__(64 * (NCW + 4)) void scan_out_kernel(ScanArgs a) {
-  scan_spec_body<T, MODE_OUT, OPT, NCW>(a, xcd_block(blockIdx.x, gridDim.x));
+  scan_spec_body<T, MODE_OUT, OPT, NCW>(a, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Pass 2: chain the segment start states of one (unit, 16-column block).

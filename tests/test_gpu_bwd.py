@@ -64,6 +64,9 @@ CASES = {
     # next slice's scan); ragged last chunk
     "pipe": P("pipe", B=2, T=1100, Hq=2, Hv=2, init_state=True, dht=True),
     "pipe_no_state": P("pipe0", B=1, T=1030, Hq=3, Hv=3),
+    # (sequence, head) units a multiple of 8: rank-ordered scan blocks
+    "varlen_ranked": P("varlen_ranked", B=1, T=0, Hq=2, Hv=2, init_state=True, dht=True,
+                       lens=[300, 1000, 64, 700]),
 }
 
 
@@ -124,7 +127,8 @@ def test_autograd_end_to_end():
         check(nm, leaves[key].grad, ref[NAMES.index(nm)], kind)
 
 
-@pytest.mark.parametrize("name", ["dense_state_dht", "fp16_gva", "varlen_empty_seq"])
+@pytest.mark.parametrize("name", ["dense_state_dht", "fp16_gva", "varlen_empty_seq",
+                                  "varlen_ranked"])
 @pytest.mark.parametrize("vt,cp", [(1, 1), (2, 1), (1, 3), (2, 3)])
 def test_backward_scan_variants(name, vt, cp):
     """One and two 16-column tiles per wave, unsplit and in three segments."""
@@ -162,7 +166,8 @@ def gpu_fwd_bwd_states(d, cp=0, use_trans=True, vt=0):
     ("long_slow_decay", 4, True, 1), ("long_slow_decay", 4, True, 2),
     ("long_slow_decay", 4, False, 1), ("varlen", 3, True, 0), ("varlen", 3, False, 0),
     ("dense_state_dht", 2, True, 2), ("fp16_gva", 3, True, 1), ("gva_group4", 2, True, 0),
-    ("varlen_empty_seq", 2, True, 0), ("pipe", 1, True, 1), ("pipe_no_state", 1, True, 1)])
+    ("varlen_empty_seq", 2, True, 0), ("pipe", 1, True, 1), ("pipe_no_state", 1, True, 1),
+    ("varlen_ranked", 1, True, 0), ("varlen_ranked", 3, True, 1)])
 def test_backward_from_the_forward_states(name, cp, use_trans, vt):
     d = gdr_synth.make(CASES[name])
     print("case", name, "cp", cp, "trans", use_trans, "wave_tiles", vt, flush=True)

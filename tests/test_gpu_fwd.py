@@ -39,6 +39,10 @@ CASES = {
     "varlen": gdr_synth.Problem("varlen", B=1, T=0, Hq=2, Hv=2, init_state=True,
                                 lens=[70, 1, 64, 129, 250]),
     "fp32_gates": gdr_synth.Problem("fp32_gates", B=1, T=130, Hq=2, Hv=2, init_state=True),
+    # (sequence, head) units a multiple of 8: the scans start the longest
+    # sequences' chains first (rank-ordered blocks)
+    "varlen_ranked": gdr_synth.Problem("varlen_ranked", B=1, T=0, Hq=2, Hv=2, init_state=True,
+                                       lens=[300, 1000, 64, 700]),
 }
 
 
@@ -85,6 +89,7 @@ def test_forward_is_deterministic():
 
 CP_CASES = [
     ("dense_ragged_state", 2), ("dense_ragged_state", 3), ("varlen", 2), ("varlen", 4),
+    ("varlen_ranked", 3),
     ("long", 4), ("long", 7), ("long_gva_fp16", 8),
 ]
 CASES["long"] = gdr_synth.Problem("long", B=1, T=2500, Hq=2, Hv=2, init_state=True, g_shift=2.0)
@@ -118,7 +123,7 @@ def test_context_parallel_forward_matches_oracle(name, cp):
 VARIANTS = [(oh, vt, cp) for oh in (False, True) for vt in (1, 2) for cp in (1, 3)]
 
 
-@pytest.mark.parametrize("name", ["dense_ragged_state", "fp16_gva", "varlen"])
+@pytest.mark.parametrize("name", ["dense_ragged_state", "fp16_gva", "varlen", "varlen_ranked"])
 @pytest.mark.parametrize("output_h,vt,cp", VARIANTS)
 def test_forward_scan_variants(name, output_h, vt, cp):
     d = gdr_synth.make(CASES[name])
