@@ -240,6 +240,96 @@ __device__ __forceinline__ f32x4 frag_d4_q(const T* X, int row0, int col0) {
   return f32x4{to_f(v[0]), to_f(v[1]), to_f(v[2]), to_f(v[3])};
 }
 
+// ---- swizzled tiles, filled by LDS-direct loads -------------------------------
+// A 16-byte buffer load to LDS (gfx950) writes the pieces fetched by a
+// wave's 64 lanes to 1 KiB of consecutive LDS, lane by lane, so a tile
+// filled that way has unpadded rows.  Bank conflicts are avoided instead by
+// permuting the 16-byte pieces of each row: piece j of row r sits at
+// position j ^ sw_piece(r).
+//   64 x 128 (q, k; 256-byte rows): sw(r) = 2 (r % 8) + (r / 8) % 2.  It
+//     takes every value over 16 aligned rows (a row operand reads one piece
+//     of each of 16 rows) and sw / 2 every value over 8 aligned rows (a
+//     transposing read takes two adjacent pieces, 32 bytes, of 8 rows).
+//   64 x 64 (A; 128-byte rows): sw(r) = (r / 2) % 8.  Rows 2i and 2i + 1
+//     share 256 bytes, so 16 aligned rows fill all 16 positions.
+//   64 x 32 (32 value columns; 64-byte rows): sw(r) = 2 ((r / 4) % 2).  The
+//     transposing reads take 32 bytes of 8 aligned rows; rows 4..7 land in the
+//     other half of their 64 bytes.
+template <int COLS>
+__device__ __forceinline__ int sw_piece(int r) {
+  static_assert(COLS == 128 || COLS == 64 || COLS == 32, "swizzled tile width");
+  if (COLS == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  if (COLS == 64) return (r >> 1) & 7;
+  return ((r >> 2) & 1) << 1;
+}
+
+// element offset of (r, c) in a swizzled tile of COLS 16-bit columns
+template <int COLS>
+__device__ __forceinline__ int sw_off(int r, int c) {
+  return COLS * r + 8 * ((c >> 3) ^ sw_piece<COLS>(r)) + (c & 7);
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Operand rows r0 + (lane % 16) (r0 a multiple of 16), split k order.
+template <typename T, int COLS>
+__device__ __forceinline__ typename VT<T>::x8 frag_row_split_w(const T* X, int r0, int k0) {
+  const int l = lane_id(), r = r0 + (l & 15), c = k0 + 4 * (l >> 4);
+  typedef typename VT<T>::x4 x4;
+  const x4 lo = *reinterpret_cast<const x4*>(X + sw_off<COLS>(r, c));
+  const x4 hi = *reinterpret_cast<const x4*>(X + sw_off<COLS>(r, c + 16));
+  return typename VT<T>::x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Operand rows r0 + (lane % 16), contiguous k order.
+template <typename T, int COLS>
+__device__ __forceinline__ typename VT<T>::x8 frag_row_w(const T* X, int r0, int k0) {
+  const int l = lane_id();
+  return *reinterpret_cast<const typename VT<T>::x8*>(
+      X + sw_off<COLS>(r0 + (l & 15), k0 + 8 * (l >> 4)));
+}
+
+// Transposed operand, split k order: k runs down rows k0 .. k0 + 31, the
+// operand's columns are m0 .. m0 + 15 (as frag_tr_split).
+template <typename T, int COLS>
+__device__ __forceinline__ typename VT<T>::x8 frag_tr_split_w(const T* X, int k0, int m0) {
+  const int l = lane_id(), j = l & 15;
+  const int r = k0 + 4 * (l >> 4) + (j >> 2), c = m0 + 4 * (j & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + sw_off<COLS>(r, c)));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + sw_off<COLS>(r + 16, c)));
+  return __builtin_bit_cast(typename VT<T>::x8,
+                            i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+// frag_d4 on a swizzled tile (row0 a multiple of 16).
+template <typename T, int COLS>
+__device__ __forceinline__ f32x4 frag_d4_w(const T* X, int row0, int col0) {
+  const int l = lane_id(), grp = l >> 4, j = l & 15;
+  const int r = row0 + 4 * grp + (j >> 2), c = col0 + 4 * (j & 3);
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + sw_off<COLS>(r, c)));
+  const typename VT<T>::x4 v = __builtin_bit_cast(typename VT<T>::x4, x);
+  return f32x4{to_f(v[0]), to_f(v[1]), to_f(v[2]), to_f(v[3])};
+}
+
+// One wave copies a 64-row tile of COLS 16-bit columns into a swizzled LDS
+// tile, one 16-byte LDS-direct buffer load per 1 KiB.  Row r of the tile is
+// at byte r * gs of the range rs; pieces past the range's end read as zero.
+// Completion is counted by the wave's vector-memory counter: the wave waits
+// for it (s_waitcnt vmcnt) before a barrier hands the tile to other waves.
+template <int COLS>
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, int gs, void* lds) {
+  constexpr int PR = COLS / 8;  // pieces per row, = instructions per tile
+  const int l = lane_id();
+#pragma unroll
+  for (int m = 0; m < PR; ++m) {
+    const int s = 64 * m + l, r = s / PR, j = (s % PR) ^ sw_piece<COLS>(s / PR);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)((char*)lds + 1024 * m), 16, r * gs + 16 * j,
+        0, 0, 0);
+  }
+}
+
 // ---- packed states ------------------------------------------------------------
 // The chunk-start states the forward keeps for the backward, the backward's
 // recomputed states and its chunk end-state gradients are stored the way the
@@ -385,9 +475,11 @@ __device__ __forceinline__ void store_scalar(void* p, int64_t idx, int dtype, fl
 // written to LDS in the input dtype.  The ten 16x16 tiles on or below the
 // diagonal are spread over the four waves (3, 3, 2, 2); the two tiles above
 // the diagonal that the triangular products read, (0,1) and (2,3), are zeroed
-// once by p_zero_tiles and never written again.  With STAG the q and k
-// tiles are staggered (qk_row) and ldq is not used.
-template <typename T, bool STAG = false>
+// once by p_zero_tiles and never written again.  LAY gives the layout of the
+// q and k tiles: 0 rows ldq apart, 1 staggered (qk_row), 2 swizzled (sw_off);
+// ldq is used by the first only.
+enum { LAY_PLAIN = 0, LAY_STAG = 1, LAY_SWZ = 2 };
+template <typename T, int LAY = LAY_PLAIN>
 __device__ __forceinline__ void p_tiles(const T* Qs, const T* Ks, int ldq, T* Ps, int ldp,
                                         const float* gam, int w) {
   const int l = lane_id(), grp = l >> 4, col = l & 15;
@@ -408,8 +500,11 @@ __device__ __forceinline__ void p_tiles(const T* Qs, const T* Ks, int ldq, T* Ps
     f32x4 acc = zero4();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (STAG)
+      if (LAY == LAY_STAG)
         acc = mfma16(frag_row_q(Qs, 16 * rb, 32 * kk), frag_row_q(Ks, 16 * cb, 32 * kk), acc);
+      else if (LAY == LAY_SWZ)
+        acc = mfma16(frag_row_w<T, 128>(Qs, 16 * rb, 32 * kk),
+                     frag_row_w<T, 128>(Ks, 16 * cb, 32 * kk), acc);
       else
         acc = mfma16(frag_row(Qs + 16 * rb * ldq + 32 * kk, ldq),
                      frag_row(Ks + 16 * cb * ldq + 32 * kk, ldq), acc);

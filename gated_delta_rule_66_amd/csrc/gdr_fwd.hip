@@ -285,9 +285,9 @@ static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st)
     a.nvs = 4;
     const dim3 g4(units * pl.cp * 4);
     switch ((a.qk_norm ? 1 : 0) | (a.beta_mode ? 2 : 0)) {
-      case 0: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 0, 2>), g4, dim3(384), st, a); break;
+      case 0: GDR_LAUNCH("scan_out", (scan_out_ld_kernel<T, 0>), g4, dim3(512), st, a); break;
       case 1: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 1, 2>), g4, dim3(384), st, a); break;
-      case 2: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 2, 2>), g4, dim3(384), st, a); break;
+      case 2: GDR_LAUNCH("scan_out", (scan_out_ld_kernel<T, 2>), g4, dim3(512), st, a); break;
       default: GDR_LAUNCH("scan_out", (scan_out_kernel<T, 3, 2>), g4, dim3(384), st, a);
     }
   } else if (mode == MODE_OUT && VB == 1) {

@@ -736,7 +736,7 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int b, int nb)
       }
       }
       // P of chunk it for the next iteration (tiles spread over the four waves)
-      if (it < sr.c1) p_tiles<T, true>(Qs[b], Ks[b], 128, Ps[b], LDA, gam, wq);
+      if (it < sr.c1) p_tiles<T, LAY_STAG>(Qs[b], Ks[b], 128, Ps[b], LDA, gam, wq);
     }
   }
 
@@ -754,6 +754,242 @@ __device__ __forceinline__ void scan_spec_body(const ScanArgs& a, int b, int nb)
 template <typename T, int OPT, int NCW>
 __global__ __launch_bounds__(64 * (NCW + 4)) void scan_out_kernel(ScanArgs a) {
   scan_spec_body<T, MODE_OUT, OPT, NCW>(a, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// The 32-column output pass with a loader wave (8 waves).  Waves 0-1 run the
+// state chain of chunk it (16 value columns each); waves 2, 3, 6, 7 write the
+// chunk-start state and the output of chunk it-1 and form the P tiles of
+// chunk it; wave 4 copies the tiles of chunk it+1 from HBM into LDS with
+// LDS-direct loads (no registers, no LDS stores by the compute waves), waits
+// for them and publishes the chunk's per-row values, all before the one
+// barrier per chunk, so the copies have a whole chunk's time to land.  Wave 5
+// has no work: waves are dealt to the SIMDs in turn (w % 4), and with it the
+// state chains share their SIMDs with the loader and an idle wave only while
+// the output waves pair up on the other two (7 waves, one state chain
+// sharing with an output wave: 165 instead of 160 us at B=2 T=4096 H=32;
+// wave 5 storing h: 168).  Buffers: q three-deep (the output of it-1 and the
+// P tiles of it read two chunks while it+1 arrives), k, v, A and the row
+// values two-deep, e^gamma three-deep.  OPT bit 1 maps beta through the
+// runtime beta options; q / k normalisation keeps scan_spec_body.
+template <typename T, int OPT>
+__device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int nb) {
+  typedef typename VT<T>::x8 x8;
+  static_assert((OPT & 1) == 0, "q / k normalisation runs in scan_spec_body");
+  constexpr int CW = 32, NVS = 4, LDA = 72;
+  __shared__ __align__(16) T Qs[3][64 * 128];  // swizzled (sw_off)
+  __shared__ __align__(16) T Ks[2][64 * 128];
+  __shared__ __align__(16) T Vs[2][64 * CW];
+  __shared__ __align__(16) T As[2][64 * 64];
+  __shared__ __align__(16) T Ps[2][64 * LDA];
+  __shared__ __align__(16) x8 Xs[2][2][4][64];  // S_c operands: [buf][column block][k block][lane]
+  __shared__ __align__(16) x8 Xd[2][2][2][64];  // Delta_c operands
+  __shared__ __align__(16) float gam[2][64], bet[2][64], bex[2][64], dl[2][64], eg[3][64];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  const BlockPos bp = block_pos(a.order, b, nb, a.P * NVS, a.Hv);
+  const int vs = bp.sub % NVS;
+  const int p = bp.sub / NVS, unit = bp.unit;
+  const int n = unit / a.Hv, h = unit % a.Hv;
+  const int G = a.Hv / a.Hq, hq = h / G;
+  const SeqInfo s = seq_info(a.cu, n, a.T);
+  const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
+  const SegRange sr = seg_range(nch, a.P, p);
+  if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;  // empty segment
+  const int cb0 = CW * vs;
+  const int64_t KV = (int64_t)kDim * kDim;
+  const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
+
+  // the chunk's tiles into buffers c % 3 (q, e^gamma) and c % 2 (the rest)
+  auto load_chunk = [&](int c) {
+    const int bq = c % 3, bk = c & 1;
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+    const int gq = a.Hq * kDim * (int)sizeof(T), gv = a.Hv * kDim * (int)sizeof(T),
+              ga = a.Hv * kChunk * (int)sizeof(T);
+    const float gr = a.gcum[(t0 + min(l, Cc - 1)) * a.Hv + h];
+    const float gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
+    const float br = to_f(reinterpret_cast<const T*>(a.beta)[(t0 + min(l, Cc - 1)) * a.Hv + h]);
+    tile_dma<128>(buf_rsrc(reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gq),
+                  gq, Qs[bq]);
+    tile_dma<128>(buf_rsrc(reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gq),
+                  gq, Ks[bk]);
+    tile_dma<CW>(buf_rsrc(reinterpret_cast<const T*>(a.v) + (t0 * a.Hv + h) * kDim + cb0,
+                          (int64_t)Cc * gv),
+                 gv, Vs[bk]);
+    tile_dma<64>(buf_rsrc(reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
+                          (int64_t)Cc * ga),
+                 ga, As[bk]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every copy has landed in LDS
+    if (Cc < kChunk) {
+      // rows past the chunk's end are zero whatever the copies left there
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      for (int x = 16 * l; x < (kChunk - Cc) * 256; x += 1024) {
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Qs[bq]) + Cc * 256 + x) = z;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Ks[bk]) + Cc * 256 + x) = z;
+      }
+      for (int x = 16 * l; x < (kChunk - Cc) * 2 * CW; x += 1024)
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Vs[bk]) + Cc * 2 * CW + x) = z;
+      for (int x = 16 * l; x < (kChunk - Cc) * 128; x += 1024)
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(As[bk]) + Cc * 128 + x) = z;
+    }
+    const bool ok = l < Cc;
+    const float bv = ok ? ((OPT & 2) ? beta_used(br, a.beta_mode) : br) : 0.f;
+    const float e = __expf(gr);
+    gam[bk][l] = gr;
+    bet[bk][l] = bv;
+    bex[bk][l] = bv * e;
+    dl[bk][l] = __expf(gl - gr);
+    eg[bq][l] = e;
+  };
+
+  f32x4 S[8];
+  if (w < 2) {
+    const float* src = (p == 0) ? (a.h0 ? a.h0 + unit * KV : nullptr)
+                                : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+    const bool vf = (p == 0) && a.svf;
+    const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, vc = cb0 + 16 * w + col;
+        S[kb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
+      }
+  } else if (w == 4 && sr.c0 < sr.c1) {
+    load_chunk(sr.c0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  p_zero_tiles<T>(Ps[0], LDA);
+  p_zero_tiles<T>(Ps[1], LDA);
+
+  // iteration it: state chain of chunk it (it < c1), output of chunk it-1
+  // (it > c0), copies of chunk it+1; the last iteration only drains the output
+  for (int it = sr.c0; it <= sr.c1; ++it) {
+    __syncthreads();  // chunk it is in LDS; iteration it-1 is done with what it+1 overwrites
+    const int b = it & 1, bq = it % 3;
+    if (w == 4) {
+      if (it + 1 < sr.c1) load_chunk(it + 1);
+    } else if (w < 2) {
+      if (it < sr.c1) {
+        const int cw0 = 16 * w;
+        const float eLc = __expf(gam[b][63]);
+        x8 Sb[4];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2) {
+          Sb[kb2] = pack_split<T>(S[2 * kb2], S[2 * kb2 + 1]);
+          Xs[b][w][kb2][l] = Sb[kb2];
+        }
+        // K S
+        f32x4 ks[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) ks[tb] = zero4();
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+            ks[tb] = mfma16(frag_row_split_w<T, 128>(Ks[b], 16 * tb, 32 * kb2), Sb[kb2], ks[tb]);
+        // R = diag(beta) V - diag(beta e^gamma) K S
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(bet[b] + 16 * tb + 4 * grp);
+          const f32x4 bx = *reinterpret_cast<const f32x4*>(bex[b] + 16 * tb + 4 * grp);
+          const f32x4 vd = frag_d4_w<T, CW>(Vs[b], 16 * tb, cw0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ks[tb][e] = bt[e] * vd[e] - bx[e] * ks[tb][e];
+        }
+        // Delta = A R
+        const x8 Rb0 = pack_split<T>(ks[0], ks[1]), Rb1 = pack_split<T>(ks[2], ks[3]);
+        f32x4 dd[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          f32x4 acc = mfma16(frag_row_split_w<T, 64>(As[b], 16 * tb, 0), Rb0, zero4());
+          if (tb >= 2) acc = mfma16(frag_row_split_w<T, 64>(As[b], 16 * tb, 32), Rb1, acc);
+          dd[tb] = acc;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Xd[b][w][kb][l] = pack_split<T>(dd[2 * kb], dd[2 * kb + 1]);
+        // S <- e^{gamma_L} S + K^T diag(e^{gamma_L - gamma}) Delta
+        x8 Eb[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(dl[b] + 32 * kt + 4 * grp);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(dl[b] + 32 * kt + 16 + 4 * grp);
+          Eb[kt] = pack_split<T>(dd[2 * kt] * d0, dd[2 * kt + 1] * d1);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          f32x4 acc = S[kb] * eLc;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            acc = mfma16(frag_tr_split_w<T, 128>(Ks[b], 32 * kt, 16 * kb), Eb[kt], acc);
+          S[kb] = acc;
+        }
+      }
+    } else if (w != 5) {
+      // waves 2, 3, 6, 7 -> 0..3
+      const int wq = (w & 1) | ((w >> 1) & 2), cbk = wq & 1, rb0 = (wq >> 1) * 2;
+      if (it > sr.c0) {
+        const int c = it - 1, bo = c & 1, bqo = (bq + 2) % 3;
+        if (a.h != nullptr) {
+          // chunk-start state of chunk c out, packed, from the operand copy
+          const __amdgpu_buffer_rsrc_t hrs = buf_rsrc(
+              reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int kb2 = (wq >> 1) * 2 + j;
+            buf_store16(hrs, packed_off(cb0 / 16 + cbk, kb2, l) * (int)sizeof(T),
+                        __builtin_bit_cast(uint4, Xs[bo][cbk][kb2][l]));
+          }
+        }
+        // O^T = (Q S)^T diag(e^gamma) + Delta^T P^T, times scale, for column
+        // block cbk and row blocks rb0, rb0 + 1
+        const int64_t t0 = s.start + (int64_t)kChunk * c;
+        const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+        f32x4 qsT[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2) {
+          const x8 sb = Xs[bo][cbk][kb2][l];
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            qsT[i] = mfma16(sb, frag_row_split_w<T, 128>(Qs[bqo], 16 * (rb0 + i), 32 * kb2), qsT[i]);
+        }
+        const x8 Db0 = Xd[bo][cbk][0][l], Db1 = Xd[bo][cbk][1][l];
+        const int ld_o = a.Hv * kDim * (int)sizeof(T);
+        const __amdgpu_buffer_rsrc_t ors =
+            buf_rsrc(reinterpret_cast<T*>(a.o) + (t0 * a.Hv + h) * kDim + cb0, (int64_t)Cc * ld_o);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int rb = rb0 + i;
+          f32x4 acc = qsT[i] * eg[bqo][16 * rb + col];
+          acc = mfma16(Db0, frag_row_split(Ps[bo] + 16 * rb * LDA, LDA), acc);
+          if (rb >= 2) acc = mfma16(Db1, frag_row_split(Ps[bo] + 16 * rb * LDA + 32, LDA), acc);
+          acc *= a.scale;
+          const typename VT<T>::x4 ov{from_f<T>(acc[0]), from_f<T>(acc[1]), from_f<T>(acc[2]),
+                                      from_f<T>(acc[3])};
+          // rows past the chunk's end fall outside the buffer range: dropped
+          buf_store8(ors, (16 * rb + col) * ld_o + (16 * cbk + 4 * grp) * (int)sizeof(T),
+                     __builtin_bit_cast(u32x2, ov));
+        }
+      }
+      // P of chunk it for the next iteration (tiles spread over the four waves)
+      if (it < sr.c1) p_tiles<T, LAY_SWZ>(Qs[bq], Ks[b], 128, Ps[b], LDA, gam[b], wq);
+    }
+  }
+
+  if (w < 2 && a.ht && p == sr.p_last) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, vc = cb0 + 16 * w + col;
+        a.ht[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = S[kb][e];
+      }
+  }
+}
+
+template <typename T, int OPT>
+__global__ __launch_bounds__(512) void scan_out_ld_kernel(ScanArgs a) {
+  scan_out_ld_body<T, OPT>(a, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Pass 2: chain the segment start states of one (unit, 16-column block).
