@@ -758,32 +758,33 @@ __global__ __launch_bounds__(64 * (NCW + 4)) void scan_out_kernel(ScanArgs a) {
 
 // The 32-column output pass with a loader wave (8 waves).  Waves 0-1 run the
 // state chain of chunk it (16 value columns each); waves 2, 3, 6, 7 write the
-// chunk-start state and the output of chunk it-1 and form the P tiles of
-// chunk it; wave 4 copies the tiles of chunk it+1 from HBM into LDS with
-// LDS-direct loads (no registers, no LDS stores by the compute waves), waits
-// for them and publishes the chunk's per-row values, all before the one
-// barrier per chunk, so the copies have a whole chunk's time to land.  Wave 5
-// has no work: waves are dealt to the SIMDs in turn (w % 4), and with it the
-// state chains share their SIMDs with the loader and an idle wave only while
-// the output waves pair up on the other two (7 waves, one state chain
-// sharing with an output wave: 165 instead of 160 us at B=2 T=4096 H=32;
-// wave 5 storing h: 168).  Buffers: q three-deep (the output of it-1 and the
-// P tiles of it read two chunks while it+1 arrives), k, v, A and the row
-// values two-deep, e^gamma three-deep.  OPT bit 1 maps beta through the
-// runtime beta options; q / k normalisation keeps scan_spec_body.
+// chunk-start state and the output of chunk it-1, P included (each forms the
+// P tiles of its own rows in registers, from the q fragments its (Q S)^T
+// product reads anyway); wave 4 copies the tiles of chunk it+1 from HBM into
+// LDS with LDS-direct loads (no registers, no LDS stores by the compute
+// waves), waits for them and publishes the chunk's per-row values, all before
+// the one barrier per chunk, so the copies have a whole chunk's time to land.
+// Wave 5 has no work: waves are dealt to the SIMDs in turn (w % 4), and with
+// it the state chains share their SIMDs with the loader and an idle wave
+// only while the output waves pair up on the other two (7 waves, one state
+// chain sharing with an output wave, was 5 us slower at B=2 T=4096 H=32;
+// wave 5 storing h, 8 us).  Buffers: q, k, gamma and e^gamma three-deep (the
+// output of it-1 and the state chain of it read two chunks while it+1
+// arrives), v, A and the other row values two-deep.  OPT bit 1 maps beta
+// through the runtime beta options; q / k normalisation keeps
+// scan_spec_body.
 template <typename T, int OPT>
 __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int nb) {
   typedef typename VT<T>::x8 x8;
   static_assert((OPT & 1) == 0, "q / k normalisation runs in scan_spec_body");
-  constexpr int CW = 32, NVS = 4, LDA = 72;
+  constexpr int CW = 32, NVS = 4;
   __shared__ __align__(16) T Qs[3][64 * 128];  // swizzled (sw_off)
-  __shared__ __align__(16) T Ks[2][64 * 128];
+  __shared__ __align__(16) T Ks[3][64 * 128];
   __shared__ __align__(16) T Vs[2][64 * CW];
   __shared__ __align__(16) T As[2][64 * 64];
-  __shared__ __align__(16) T Ps[2][64 * LDA];
   __shared__ __align__(16) x8 Xs[2][2][4][64];  // S_c operands: [buf][column block][k block][lane]
   __shared__ __align__(16) x8 Xd[2][2][2][64];  // Delta_c operands
-  __shared__ __align__(16) float gam[2][64], bet[2][64], bex[2][64], dl[2][64], eg[3][64];
+  __shared__ __align__(16) float gam[3][64], eg[3][64], bet[2][64], bex[2][64], dl[2][64];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   const BlockPos bp = block_pos(a.order, b, nb, a.P * NVS, a.Hv);
@@ -799,7 +800,7 @@ __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int n
   const int64_t KV = (int64_t)kDim * kDim;
   const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
 
-  // the chunk's tiles into buffers c % 3 (q, e^gamma) and c % 2 (the rest)
+  // the chunk's tiles into buffers c % 3 (q, k, gamma, e^gamma) and c % 2 (the rest)
   auto load_chunk = [&](int c) {
     const int bq = c % 3, bk = c & 1;
     const int64_t t0 = s.start + (int64_t)kChunk * c;
@@ -812,7 +813,7 @@ __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int n
     tile_dma<128>(buf_rsrc(reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gq),
                   gq, Qs[bq]);
     tile_dma<128>(buf_rsrc(reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gq),
-                  gq, Ks[bk]);
+                  gq, Ks[bq]);
     tile_dma<CW>(buf_rsrc(reinterpret_cast<const T*>(a.v) + (t0 * a.Hv + h) * kDim + cb0,
                           (int64_t)Cc * gv),
                  gv, Vs[bk]);
@@ -825,7 +826,7 @@ __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int n
       const uint4 z = make_uint4(0, 0, 0, 0);
       for (int x = 16 * l; x < (kChunk - Cc) * 256; x += 1024) {
         *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Qs[bq]) + Cc * 256 + x) = z;
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Ks[bk]) + Cc * 256 + x) = z;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Ks[bq]) + Cc * 256 + x) = z;
       }
       for (int x = 16 * l; x < (kChunk - Cc) * 2 * CW; x += 1024)
         *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Vs[bk]) + Cc * 2 * CW + x) = z;
@@ -835,7 +836,7 @@ __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int n
     const bool ok = l < Cc;
     const float bv = ok ? ((OPT & 2) ? beta_used(br, a.beta_mode) : br) : 0.f;
     const float e = __expf(gr);
-    gam[bk][l] = gr;
+    gam[bq][l] = gr;
     bet[bk][l] = bv;
     bex[bk][l] = bv * e;
     dl[bk][l] = __expf(gl - gr);
@@ -859,8 +860,6 @@ __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int n
     load_chunk(sr.c0);
   }
   __builtin_amdgcn_s_waitcnt(0);
-  p_zero_tiles<T>(Ps[0], LDA);
-  p_zero_tiles<T>(Ps[1], LDA);
 
   // iteration it: state chain of chunk it (it < c1), output of chunk it-1
   // (it > c0), copies of chunk it+1; the last iteration only drains the output
@@ -872,7 +871,7 @@ __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int n
     } else if (w < 2) {
       if (it < sr.c1) {
         const int cw0 = 16 * w;
-        const float eLc = __expf(gam[b][63]);
+        const float eLc = __expf(gam[bq][63]);
         x8 Sb[4];
 #pragma unroll
         for (int kb2 = 0; kb2 < 4; ++kb2) {
@@ -887,7 +886,7 @@ __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int n
         for (int kb2 = 0; kb2 < 4; ++kb2)
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb)
-            ks[tb] = mfma16(frag_row_split_w<T, 128>(Ks[b], 16 * tb, 32 * kb2), Sb[kb2], ks[tb]);
+            ks[tb] = mfma16(frag_row_split_w<T, 128>(Ks[bq], 16 * tb, 32 * kb2), Sb[kb2], ks[tb]);
         // R = diag(beta) V - diag(beta e^gamma) K S
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -921,58 +920,99 @@ __device__ __forceinline__ void scan_out_ld_body(const ScanArgs& a, int b, int n
           f32x4 acc = S[kb] * eLc;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
-            acc = mfma16(frag_tr_split_w<T, 128>(Ks[b], 32 * kt, 16 * kb), Eb[kt], acc);
+            acc = mfma16(frag_tr_split_w<T, 128>(Ks[bq], 32 * kt, 16 * kb), Eb[kt], acc);
           S[kb] = acc;
         }
       }
-    } else if (w != 5) {
-      // waves 2, 3, 6, 7 -> 0..3
-      const int wq = (w & 1) | ((w >> 1) & 2), cbk = wq & 1, rb0 = (wq >> 1) * 2;
-      if (it > sr.c0) {
-        const int c = it - 1, bo = c & 1, bqo = (bq + 2) % 3;
-        if (a.h != nullptr) {
-          // chunk-start state of chunk c out, packed, from the operand copy
-          const __amdgpu_buffer_rsrc_t hrs = buf_rsrc(
-              reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
+    } else if (w != 5 && it > sr.c0) {
+      // waves 2, 3, 6, 7 -> 0..3: value column block cbk, row blocks
+      // {rA, rB} = {0, 3} or {1, 2} (equal shares of the triangular P)
+      const int wq = (w & 1) | ((w >> 1) & 2), cbk = wq & 1;
+      const int rA = wq >> 1, rB = 3 - rA;
+      const int c = it - 1, bo = c & 1, bqo = (bq + 2) % 3;
+      if (a.h != nullptr) {
+        // chunk-start state of chunk c out, packed, from the operand copy
+        const __amdgpu_buffer_rsrc_t hrs = buf_rsrc(
+            reinterpret_cast<T*>(a.h) + ((choff + c) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int kb2 = (wq >> 1) * 2 + j;
-            buf_store16(hrs, packed_off(cb0 / 16 + cbk, kb2, l) * (int)sizeof(T),
-                        __builtin_bit_cast(uint4, Xs[bo][cbk][kb2][l]));
-          }
-        }
-        // O^T = (Q S)^T diag(e^gamma) + Delta^T P^T, times scale, for column
-        // block cbk and row blocks rb0, rb0 + 1
-        const int64_t t0 = s.start + (int64_t)kChunk * c;
-        const int Cc = (int)min((int64_t)kChunk, s.end - t0);
-        f32x4 qsT[2] = {zero4(), zero4()};
-#pragma unroll
-        for (int kb2 = 0; kb2 < 4; ++kb2) {
-          const x8 sb = Xs[bo][cbk][kb2][l];
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            qsT[i] = mfma16(sb, frag_row_split_w<T, 128>(Qs[bqo], 16 * (rb0 + i), 32 * kb2), qsT[i]);
-        }
-        const x8 Db0 = Xd[bo][cbk][0][l], Db1 = Xd[bo][cbk][1][l];
-        const int ld_o = a.Hv * kDim * (int)sizeof(T);
-        const __amdgpu_buffer_rsrc_t ors =
-            buf_rsrc(reinterpret_cast<T*>(a.o) + (t0 * a.Hv + h) * kDim + cb0, (int64_t)Cc * ld_o);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int rb = rb0 + i;
-          f32x4 acc = qsT[i] * eg[bqo][16 * rb + col];
-          acc = mfma16(Db0, frag_row_split(Ps[bo] + 16 * rb * LDA, LDA), acc);
-          if (rb >= 2) acc = mfma16(Db1, frag_row_split(Ps[bo] + 16 * rb * LDA + 32, LDA), acc);
-          acc *= a.scale;
-          const typename VT<T>::x4 ov{from_f<T>(acc[0]), from_f<T>(acc[1]), from_f<T>(acc[2]),
-                                      from_f<T>(acc[3])};
-          // rows past the chunk's end fall outside the buffer range: dropped
-          buf_store8(ors, (16 * rb + col) * ld_o + (16 * cbk + 4 * grp) * (int)sizeof(T),
-                     __builtin_bit_cast(u32x2, ov));
+        for (int j = 0; j < 2; ++j) {
+          const int kb2 = (wq >> 1) * 2 + j;
+          buf_store16(hrs, packed_off(cb0 / 16 + cbk, kb2, l) * (int)sizeof(T),
+                      __builtin_bit_cast(uint4, Xs[bo][cbk][kb2][l]));
         }
       }
-      // P of chunk it for the next iteration (tiles spread over the four waves)
-      if (it < sr.c1) p_tiles<T, LAY_SWZ>(Qs[bq], Ks[b], 128, Ps[b], LDA, gam[b], wq);
+      // O^T = (Q S)^T diag(e^gamma) + Delta^T P^T, times scale, rows rA and rB.
+      // The q fragments of both row blocks serve (Q S)^T and P^T = K Q^T, the
+      // latter kept in registers: tiles (cb, rA) for cb < 2 and (cb, rB) for
+      // all cb (those above the diagonal come out zero), each gated by
+      // e^{gamma_t - gamma_i} on and below it.
+      const T* Qc = Qs[bqo];
+      const T* Kc = Ks[bqo];
+      const float* gc = gam[bqo];
+      x8 fq[2][4];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        fq[0][kb2] = frag_row_split_w<T, 128>(Qc, 16 * rA, 32 * kb2);
+        fq[1][kb2] = frag_row_split_w<T, 128>(Qc, 16 * rB, 32 * kb2);
+      }
+      f32x4 qsT[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        const x8 sb = Xs[bo][cbk][kb2][l];
+        qsT[0] = mfma16(sb, fq[0][kb2], qsT[0]);
+        qsT[1] = mfma16(sb, fq[1][kb2], qsT[1]);
+      }
+      f32x4 pa[2], pb[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        x8 fk[4];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2) fk[kb2] = frag_row_split_w<T, 128>(Kc, 16 * cb, 32 * kb2);
+        f32x4 accb = zero4();
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2) accb = mfma16(fk[kb2], fq[1][kb2], accb);
+        pb[cb] = accb;
+        if (cb < 2) {
+          f32x4 acca = zero4();
+#pragma unroll
+          for (int kb2 = 0; kb2 < 4; ++kb2) acca = mfma16(fk[kb2], fq[0][kb2], acca);
+          pa[cb] = acca;
+        }
+      }
+      // gate and mask: lane (grp, col) of tile (cb, r) holds P[t][i] with
+      // t = 16 r + col, i = 16 cb + 4 grp + e; masked entries take exp(-inf)
+      const float gtA = gc[16 * rA + col], gtB = gc[16 * rB + col];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(gc + 16 * cb + 4 * grp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * cb + 4 * grp + e;
+          pb[cb][e] *= __expf(i <= 16 * rB + col ? gtB - gi[e] : -INFINITY);
+          if (cb < 2) pa[cb][e] *= __expf(i <= 16 * rA + col ? gtA - gi[e] : -INFINITY);
+        }
+      }
+      const x8 Db0 = Xd[bo][cbk][0][l], Db1 = Xd[bo][cbk][1][l];
+      const int64_t t0 = s.start + (int64_t)kChunk * c;
+      const int Cc = (int)min((int64_t)kChunk, s.end - t0);
+      const int ld_o = a.Hv * kDim * (int)sizeof(T);
+      const __amdgpu_buffer_rsrc_t ors =
+          buf_rsrc(reinterpret_cast<T*>(a.o) + (t0 * a.Hv + h) * kDim + cb0, (int64_t)Cc * ld_o);
+      f32x4 oA = qsT[0] * eg[bqo][16 * rA + col];
+      oA = mfma16(Db0, pack_split<T>(pa[0], pa[1]), oA);  // rA < 2: keys 0..31 only
+      f32x4 oB = qsT[1] * eg[bqo][16 * rB + col];
+      oB = mfma16(Db0, pack_split<T>(pb[0], pb[1]), oB);
+      oB = mfma16(Db1, pack_split<T>(pb[2], pb[3]), oB);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int rb = i ? rB : rA;
+        const f32x4 acc = (i ? oB : oA) * a.scale;
+        const typename VT<T>::x4 ov{from_f<T>(acc[0]), from_f<T>(acc[1]), from_f<T>(acc[2]),
+                                    from_f<T>(acc[3])};
+        // rows past the chunk's end fall outside the buffer range: dropped
+        buf_store8(ors, (16 * rb + col) * ld_o + (16 * cbk + 4 * grp) * (int)sizeof(T),
+                   __builtin_bit_cast(u32x2, ov));
+      }
     }
   }
 
