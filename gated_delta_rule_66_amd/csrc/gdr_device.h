@@ -386,6 +386,16 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t rs, int off, u
   __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
 }
 
+// Non-temporal stores (cache policy bit 1, nt): data the kernel writes and
+// never reads back, so that it does not displace lines that other
+// workgroups are about to read.
+__device__ __forceinline__ void buf_store16_nt(__amdgpu_buffer_rsrc_t rs, int off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, rs, off, 0, 2);
+}
+__device__ __forceinline__ void buf_store8_nt(__amdgpu_buffer_rsrc_t rs, int off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 2);
+}
+
 // Rows [0, rows) of the tile load; rows past that read as zero.  Row r of the
 // tile starts r * gstride elements after g (gstride >= COLS).
 // `t0` is the calling thread's index among the NT cooperating threads.
