@@ -492,14 +492,15 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int b, int nb, DhLhL
   };
 
   // gradient of chunk cc's end state out, packed (packed_off), from the
-  // operand copy the chain left in Hx
+  // operand copy the chain left in Hx; non-temporal, as this pass never
+  // reads it back
   auto store_dh = [&](int cc) {
     const int wq = w & 3;
     const __amdgpu_buffer_rsrc_t hrs =
         buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + cc) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
 #pragma unroll
     for (int kb2 = 0; kb2 < 4; ++kb2)
-      buf_store16(hrs, packed_off(cb0 / 16 + wq, kb2, l) * (int)sizeof(T),
+      buf_store16_nt(hrs, packed_off(cb0 / 16 + wq, kb2, l) * (int)sizeof(T),
                   __builtin_bit_cast(uint4, Hx[wq][kb2][l]));
   };
 
@@ -1155,7 +1156,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
       }
     }
     __syncthreads();
-    tile_from_lds<T, 64, 512>(reinterpret_cast<T*>(a.dv) + (t0 * a.Hv + h) * kDim + v0,
+    tile_from_lds<T, 64, 512, true>(reinterpret_cast<T*>(a.dv) + (t0 * a.Hv + h) * kDim + v0,
                               (int64_t)a.Hv * kDim, DVs, L7, Cc);
 
     // ---- rows 16 wr .. 16 wr + 15, contractions over this half's v ----
@@ -1438,9 +1439,9 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
   }
   __syncthreads();
   if (store_dqk) {
-    tile_from_lds<T, 128, 512>(reinterpret_cast<T*>(a.dq) + (t0 * a.Hq + hq) * kDim,
+    tile_from_lds<T, 128, 512, true>(reinterpret_cast<T*>(a.dq) + (t0 * a.Hq + hq) * kDim,
                                (int64_t)a.Hq * kDim, Ss, LD, Cc);
-    tile_from_lds<T, 128, 512>(reinterpret_cast<T*>(a.dk) + (t0 * a.Hq + hq) * kDim,
+    tile_from_lds<T, 128, 512, true>(reinterpret_cast<T*>(a.dk) + (t0 * a.Hq + hq) * kDim,
                                (int64_t)a.Hq * kDim, Gs_, LD, Cc);
   }
   // dg = reverse cumsum of dgamma over the valid rows: lane l scans row 63 - l

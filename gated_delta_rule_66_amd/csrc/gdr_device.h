@@ -453,8 +453,8 @@ __device__ __forceinline__ void tile_store_packed_q(T* lds, const TileRegs<128, 
 }
 
 // LDS tile rows [0, rows) -> global, 16 bytes per store (stores of rows past
-// `rows` fall outside the buffer range and are dropped).
-template <typename T, int COLS, int NT>
+// `rows` fall outside the buffer range and are dropped); NTS: non-temporal.
+template <typename T, int COLS, int NT, bool NTS = false>
 __device__ __forceinline__ void tile_from_lds(T* g, int64_t gstride, const T* lds, int ld,
                                               int rows) {
   constexpr int PR = COLS / 8;
@@ -464,7 +464,9 @@ __device__ __forceinline__ void tile_from_lds(T* g, int64_t gstride, const T* ld
   for (int i = 0; i < (64 * PR) / NT; ++i) {
     const int x = threadIdx.x + i * NT;
     const int r = x / PR, c8 = (x % PR) * 8;
-    buf_store16(rs, r * gs + c8 * (int)sizeof(T), *reinterpret_cast<const uint4*>(lds + r * ld + c8));
+    const uint4 val = *reinterpret_cast<const uint4*>(lds + r * ld + c8);
+    if (NTS) buf_store16_nt(rs, r * gs + c8 * (int)sizeof(T), val);
+    else buf_store16(rs, r * gs + c8 * (int)sizeof(T), val);
   }
 }
 
