@@ -32,6 +32,7 @@
 #include "gdr_scan.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <cstring>
 
 namespace gdr {
@@ -706,6 +707,399 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int b, int nb, DhLhL
     if (sr.c0 < sr.c1) store_dh(sr.c0);
     return;
   }
+  if (p == 0 && a.dh0) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
+        a.dh0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = Gs[kb][e];
+      }
+  } else if (a.sliced && p > 0) {
+    // the gradient entering the previous segment's end, for the next launch
+    float* dst = a.seg_next + ((int64_t)unit * a.P + p - 1) * KV;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dst[(16 * kb + 4 * grp + e) * kDim + cb0 + cw0 + col] = Gs[kb][e];
+  }
+}
+
+// B2 output pass with a loader wave (one 64-column block, 8 waves): the
+// form used unless q / k are normalised in the kernel.  Waves 0-3 run the
+// chain as in dh_lh_body; wave 4 copies the tiles from HBM into LDS with
+// LDS-direct loads (no registers, no tile stores): in the iteration of chunk
+// c, chunk c-1's dO and A tiles and per-row values before the middle
+// barrier, and chunk c-2's q and k tiles after it, so that each copy has
+// about a chunk's time to land.  Its waits name how many of its
+// newest copies may still be in flight (the vector memory counter retires
+// loads in order).  Waves 5-7 form the P tiles of the chunk while the chain
+// forms K dSn, wave 5 after storing the state gradients from the chain's
+// operand copies.  The tiles are swizzled (sw_off),
+// q / k three-deep (slot c % 3), the rest two-deep (slot c & 1); the chain
+// scales the dO fragments of Q^T (scale diag(e^gamma) dO) itself.
+template <typename T>
+struct DhLdLds {
+  static constexpr int CW = 64, LDA = 72;
+  alignas(16) T Qs[3][64 * 128];
+  alignas(16) T Ks[3][64 * 128];
+  alignas(16) T Ds[2][64 * CW];
+  alignas(16) T As[2][64 * 64];
+  alignas(16) T Ps[64 * LDA];
+  alignas(16) float gam[2][64];
+  alignas(16) float eg[2][64];
+  alignas(16) float bex[2][64];
+  alignas(16) float dl[2][64];
+  // dSn of the chain's chunk as bf16 operand registers ([column block][k
+  // block][lane]), stored by wave 5 in the next iteration
+  alignas(16) typename VT<T>::x8 Hx[4][4][64];
+};
+
+template <typename T, int OPT>
+__device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdLds<T>& L) {
+  typedef typename VT<T>::x8 x8;
+  static_assert((OPT & 1) == 0, "q / k normalisation runs in dh_lh_body");
+  constexpr int CW = DhLdLds<T>::CW;
+  constexpr int LDA = DhLdLds<T>::LDA;
+  auto& Qs = L.Qs;
+  auto& Ks = L.Ks;
+  auto& Ds = L.Ds;
+  auto& As = L.As;
+  auto& Ps = L.Ps;
+  auto& gam = L.gam;
+  auto& eg = L.eg;
+  auto& bex = L.bex;
+  auto& dl = L.dl;
+  auto& Hx = L.Hx;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
+  // a pipelined slice runs one segment of every unit
+  const BlockPos bp = block_pos(a.order, b, nb, a.sliced ? a.nvs : a.P * a.nvs, a.Hv);
+  const int vs = bp.sub % a.nvs;
+  const int p = a.sliced ? a.slice_p : bp.sub / a.nvs, unit = bp.unit;
+  const int n = unit / a.Hv, h = unit % a.Hv;
+  const int G = a.Hv / a.Hq, hq = h / G;
+  const SeqInfo s = seq_info(a.cu, n, a.T);
+  const int nch = (int)((s.end - s.start + kChunk - 1) / kChunk);
+  SegRange sr = seg_range(nch, a.P, p);
+  if (a.sliced) {  // a dense batch: every sequence has the same slices
+    sr.c0 = a.sl_c0;
+    sr.c1 = a.sl_c1;
+    sr.p_last = a.P - 1;
+  }
+  if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;
+  const int cb0 = vs * CW;
+  const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
+  const int64_t KV = (int64_t)kDim * kDim;
+  const int cw0 = 16 * (w & 3);
+
+  // gradient entering the segment's end: dht (last segment) or the value
+  // chained by pass 2; every load is issued before the first is used (null
+  // reads zeros)
+  f32x4 Gs[8];
+  if (w < 4) {
+    const float* src = (p == sr.p_last) ? (a.dht ? a.dht + unit * KV : nullptr)
+                                        : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+    const bool vf = (p == sr.p_last) && a.svf;
+    const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
+        Gs[kb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
+      }
+  }
+
+  // wave 4's copies: per-row values and dO / A of chunk c (3 + 16 loads, in
+  // that order), q / k of chunk c (32 loads)
+  float r_g = 0.f, r_gl = 0.f;
+  T r_bt = from_f<T>(0.f);  // raw: converted where it is used, not where it lands
+  auto chunk_rows = [&](int c) { return (int)min((int64_t)kChunk, s.end - s.start - (int64_t)kChunk * c); };
+  auto issue_da = [&](int c) {
+    const int bs = c & 1, Cc = chunk_rows(c);
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int gv = a.Hv * kDim * (int)sizeof(T), ga = a.Hv * kChunk * (int)sizeof(T);
+    r_g = a.gcum[(t0 + min(l, Cc - 1)) * a.Hv + h];
+    r_gl = a.gcum[(t0 + Cc - 1) * a.Hv + h];
+    r_bt = reinterpret_cast<const T*>(a.beta)[(t0 + min(l, Cc - 1)) * a.Hv + h];
+    __builtin_amdgcn_sched_barrier(0);  // the three loads first, as the waits count
+    tile_dma<CW>(buf_rsrc(reinterpret_cast<const T*>(a.dO) + (t0 * a.Hv + h) * kDim + cb0,
+                          (int64_t)Cc * gv),
+                 gv, Ds[bs]);
+    tile_dma<64>(buf_rsrc(reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
+                          (int64_t)Cc * ga),
+                 ga, As[bs]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto issue_qk = [&](int c) {
+    const int bs = c % 3, Cc = chunk_rows(c);
+    const int64_t t0 = s.start + (int64_t)kChunk * c;
+    const int gq = a.Hq * kDim * (int)sizeof(T);
+    tile_dma<128>(buf_rsrc(reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gq),
+                  gq, Qs[bs]);
+    tile_dma<128>(buf_rsrc(reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gq),
+                  gq, Ks[bs]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // rows past the chunk's end are zero whatever the copies left there
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  auto zero_da = [&](int c) {
+    const int bs = c & 1, Cc = chunk_rows(c);
+    for (int x = 16 * l; x < (kChunk - Cc) * 128; x += 1024) {
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Ds[bs]) + Cc * 128 + x) = z4;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(As[bs]) + Cc * 128 + x) = z4;
+    }
+  };
+  auto zero_qk = [&](int c) {
+    const int bs = c % 3, Cc = chunk_rows(c);
+    for (int x = 16 * l; x < (kChunk - Cc) * 256; x += 1024) {
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Qs[bs]) + Cc * 256 + x) = z4;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Ks[bs]) + Cc * 256 + x) = z4;
+    }
+  };
+  auto put_rows = [&](int c) {  // the per-row values loaded by issue_da(c)
+    const int bs = c & 1;
+    const bool ok = l < chunk_rows(c);
+    const float e = __expf(r_g), r_b = to_f(r_bt);
+    gam[bs][l] = r_g;
+    eg[bs][l] = a.scale * e;
+    bex[bs][l] = (ok ? ((OPT & 2) ? beta_used(r_b, a.beta_mode) : r_b) : 0.f) * e;
+    dl[bs][l] = __expf(r_gl - r_g);
+  };
+
+  // gradient of chunk cc's end state out, packed (packed_off), from the
+  // operand copies the chain left in Hx; non-temporal, as this pass never
+  // reads it back
+  auto store_dh = [&](int cc) {
+    const __amdgpu_buffer_rsrc_t hrs =
+        buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + cc) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
+#pragma unroll
+    for (int wq = 0; wq < 4; ++wq)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2)
+        buf_store16_nt(hrs, packed_off(cb0 / 16 + wq, kb2, l) * (int)sizeof(T),
+                       __builtin_bit_cast(uint4, Hx[wq][kb2][l]));
+  };
+
+  // before chunk c's first barrier: its q / k and per-row values are in LDS;
+  // its dO / A copies may still be in flight, followed by chunk c-1's q / k
+  if (w == 4 && sr.c0 < sr.c1) {
+    const int cf = sr.c1 - 1;
+    issue_da(cf);
+    issue_qk(cf);
+    if (cf - 1 >= sr.c0) {
+      issue_qk(cf - 1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(32));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    zero_qk(cf);
+    put_rows(cf);
+  }
+  // the initial gradient has arrived before the loop (else the loop-entry
+  // merge makes its first use wait for later loads as well)
+  __builtin_amdgcn_s_waitcnt(0);
+  // the two tiles above the diagonal that P^T's products read stay zero
+  p_zero_tiles<T>(Ps, LDA);
+  // the P tiles of waves 5, 6, 7 (3, 3, 4), (row block, column block) 4 bits
+  // each: (0,0) (1,0) (1,1); (2,0) (2,1) (2,2); (3,0) (3,1) (3,2) (3,3)
+  constexpr uint64_t pcode = 0x0ull | (0x4ull << 4) | (0x5ull << 8) |
+                             ((0x8ull | (0x9ull << 4) | (0xAull << 8)) << 16) |
+                             ((0xCull | (0xDull << 4) | (0xEull << 8) | (0xFull << 12)) << 32);
+  // Wave 4 meets the barriers without __syncthreads' fences: they would wait
+  // for every copy in flight (the LDS-direct loads count as its LDS writes).
+  // Its own waits are explicit: the copies the next phase reads (above) and
+  // its LDS stores (here); the wavefront-scope fences only keep the compiler
+  // from moving its memory operations across the barrier.
+  auto barrier = [&]() {
+    if (w == 4) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      __syncthreads();
+    }
+  };
+  for (int c = sr.c1 - 1; c >= sr.c0; --c) {
+    const int b = c & 1, bq = c % 3;
+    barrier();  // chunk c's slots are ready; every wave is done with chunk c+1
+    f32x4 dd[4];
+    if (w == 4) {
+      // chunk c's dO / A have landed once at most the 32 copies of chunk
+      // c-1's q / k are outstanding
+      if (c - 1 >= sr.c0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(32));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      zero_da(c);
+      if (c - 1 >= sr.c0) issue_da(c - 1);
+    } else if (w < 4) {
+      // K dSn of chunk c in four rounds over the key dimension; every
+      // fragment of a round is read before it multiplies
+      x8 Gb[4];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) Gb[kb2] = pack_split<T>(Gs[2 * kb2], Gs[2 * kb2 + 1]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) dd[tb] = zero4();
+#pragma unroll
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        x8 fk[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) fk[tb] = frag_row_split_w<T, 128>(Ks[bq], 16 * tb, 32 * kb2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) dd[tb] = mfma16(fk[tb], Gb[kb2], dd[tb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // waves 5-7: this wave's tiles of P = lower_incl(Q K^T o Gamma) of
+      // chunk c, published by the middle barrier; wave 5 first stores the
+      // state gradient of chunk c+1 (last in this wave's vector memory
+      // queue: a later wait would also wait for these stores)
+      if (w == 5 && c + 1 < sr.c1) store_dh(c + 1);
+      const int sl = __builtin_amdgcn_readfirstlane(w - 5);  // wave-uniform
+      const int nt = sl == 2 ? 4 : 3;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < nt) {
+          const int x = (int)((pcode >> (16 * sl + 4 * t)) & 15), rb = x >> 2, cb = x & 3;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)  // split k order, as dh_lh_body's chain
+            acc = mfma16(frag_row_split_w<T, 128>(Qs[bq], 16 * rb, 32 * kk),
+                         frag_row_split_w<T, 128>(Ks[bq], 16 * cb, 32 * kk), acc);
+          const f32x4 gr = *reinterpret_cast<const f32x4*>(gam[b] + 16 * rb + 4 * grp);
+          const float gi = gam[b][16 * cb + col];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * grp + e, i = 16 * cb + col;
+            // masked entries take exp(-inf) = 0 (an unconditional exponential)
+            const float pv = acc[e] * __expf((rb != cb || i <= r) ? gr[e] - gi : -INFINITY);
+            Ps[r * LDA + i] = from_f<T>(pv);
+          }
+        }
+      }
+    }
+    barrier();  // P of chunk c is in LDS; Hx is free
+    if (w == 4) {
+      // chunk c-2's q / k (issued here, in the chain's long phase), then
+      // chunk c-1's q / k and per-row values land before the next first
+      // barrier; newer: its dO / A (16) and chunk c-2's q / k (32)
+      if (c - 2 >= sr.c0) issue_qk(c - 2);
+      if (c - 1 >= sr.c0) {
+        if (c - 2 >= sr.c0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(48));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+        zero_qk(c - 1);
+        put_rows(c - 1);
+      }
+      continue;
+    }
+    if (w >= 4) continue;
+    // chunk c's dSn for the store wave (packed again rather than kept live
+    // across the barrier)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) Hx[w][kb2][l] = pack_split<T>(Gs[2 * kb2], Gs[2 * kb2 + 1]);
+    const float eL = __expf(gam[b][63]);
+
+    // The products below run in rounds of independent accumulators whose
+    // LDS fragments are issued before the round multiplies; the scheduling
+    // fences keep the compiler from sinking every read to its product, which
+    // would put one LDS latency per MFMA on the chain.
+    // Fragment (tb, kt) of P^T or A^T (k = rows 32 kt ..) for kt >= tb / 2.
+    auto tk = [](int tb, int kt) { return tb < 2 ? 2 * tb + kt : 2 + tb; };
+    x8 fdo[2], fp[6], fa[6], fr[8];
+    f32x4 dlv[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) fdo[kt] = frag_tr_split_w<T, CW>(Ds[b], 32 * kt, cw0);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int kt = tb / 2; kt < 2; ++kt)
+        fp[tk(tb, kt)] = frag_tr_split(Ps + 32 * kt * LDA + 16 * tb, LDA);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) dlv[tb] = *reinterpret_cast<const f32x4*>(dl[b] + 16 * tb + 4 * grp);
+    __builtin_amdgcn_sched_barrier(0);
+    // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
+    f32x4 pd[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) pd[tb] = zero4();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        if (kt >= tb / 2) pd[tb] = mfma16(fp[tk(tb, kt)], fdo[kt], pd[tb]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int kt = tb / 2; kt < 2; ++kt)
+        fa[tk(tb, kt)] = frag_tr_split_w<T, 64>(As[b], 32 * kt, 16 * tb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dd[tb][e] = dlv[tb][e] * dd[tb][e] + a.scale * pd[tb][e];
+    const x8 Db[2] = {pack_split<T>(dd[0], dd[1]), pack_split<T>(dd[2], dd[3])};
+    // Q^T's operand scale diag(e^gamma) dO: the dO fragments, each row
+    // scaled (row 32 kt + k(grp, e) of the split order)
+    x8 Ob[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 4 * grp);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 16 + 4 * grp);
+      x8 f = fdo[kt];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = from_f<T>(to_f(f[e]) * e0[e]);
+        f[e + 4] = from_f<T>(to_f(f[e + 4]) * e1[e]);
+      }
+      Ob[kt] = f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 0, 16 * kb);
+    __builtin_amdgcn_sched_barrier(0);
+    // Z = -diag(beta e^gamma) A^T dDelta
+    f32x4 zz[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) zz[tb] = zero4();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        if (kt >= tb / 2) zz[tb] = mfma16(fa[tk(tb, kt)], Db[kt], zz[tb]);
+    // dS = e^{gL} dSn + Q^T (scale diag(e^gamma) dO) + K^T Z
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[0], Gs[kb] * eL);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 32, 16 * kb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const f32x4 bx = *reinterpret_cast<const f32x4*>(bex[b] + 16 * tb + 4 * grp);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zz[tb][e] *= -bx[e];
+    }
+    const x8 Zb[2] = {pack_split<T>(zz[0], zz[1]), pack_split<T>(zz[2], zz[3])};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[1], Gs[kb]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Ks[bq], 32 * kt, 16 * kb);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Zb[kt], Gs[kb]);
+    }
+  }
+
+  // the dSn of the last chunk walked (c0)
+  __syncthreads();
+  if (w == 5 && sr.c0 < sr.c1) store_dh(sr.c0);
+  if (w >= 4) return;
   if (p == 0 && a.dh0) {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
@@ -1493,10 +1887,14 @@ static void launch_grad(const GradArgs& ga, int ngx, int rows, hipStream_t st) {
 // a slice's state gradients before their gradient workgroups read them.
 template <typename T, int OPT>
 __global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, int nb2, int ngx) {
-  constexpr size_t B = sizeof(DhLhLds<T>), G = sizeof(GradLds<T>);
+  typedef typename std::conditional<(OPT & 1) != 0, DhLhLds<T>, DhLdLds<T>>::type L2;
+  constexpr size_t B = sizeof(L2), G = sizeof(GradLds<T>);
   __shared__ __align__(16) char lds[B > G ? B : G];
   if ((int)blockIdx.x < nb2) {
-    dh_lh_body<T, OPT>(da, (int)blockIdx.x, nb2, *reinterpret_cast<DhLhLds<T>*>(lds));
+    if constexpr ((OPT & 1) != 0)
+      dh_lh_body<T, OPT>(da, (int)blockIdx.x, nb2, *reinterpret_cast<L2*>(lds));
+    else
+      dh_ld_body<T, OPT>(da, (int)blockIdx.x, nb2, *reinterpret_cast<L2*>(lds));
   } else {
     const int g = (int)blockIdx.x - nb2;
     GradFirst<T> f;

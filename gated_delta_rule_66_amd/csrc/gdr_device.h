@@ -250,8 +250,10 @@ __device__ __forceinline__ f32x4 frag_d4_q(const T* X, int row0, int col0) {
 //     takes every value over 16 aligned rows (a row operand reads one piece
 //     of each of 16 rows) and sw / 2 every value over 8 aligned rows (a
 //     transposing read takes two adjacent pieces, 32 bytes, of 8 rows).
-//   64 x 64 (A; 128-byte rows): sw(r) = (r / 2) % 8.  Rows 2i and 2i + 1
-//     share 256 bytes, so 16 aligned rows fill all 16 positions.
+//   64 x 64 (A, dO; 128-byte rows, two to 256 bytes): sw(r) =
+//     2 ((r / 2) % 4) + (r / 8) % 2.  Over 16 aligned rows (r % 2, sw) takes
+//     every value (row operands), and (r % 2, sw / 2) over 8 aligned rows
+//     (transposing reads).
 //   64 x 32 (32 value columns; 64-byte rows): sw(r) = 2 ((r / 4) % 2).  The
 //     transposing reads take 32 bytes of 8 aligned rows; rows 4..7 land in the
 //     other half of their 64 bytes.
@@ -259,7 +261,7 @@ template <int COLS>
 __device__ __forceinline__ int sw_piece(int r) {
   static_assert(COLS == 128 || COLS == 64 || COLS == 32, "swizzled tile width");
   if (COLS == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  if (COLS == 64) return (r >> 1) & 7;
+  if (COLS == 64) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
   return ((r >> 2) & 1) << 1;
 }
 
@@ -270,6 +272,13 @@ __device__ __forceinline__ int sw_off(int r, int c) {
 }
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// s_waitcnt immediate that waits until at most n (< 64) vector memory
+// operations of the wave are outstanding (the export and LDS counters are
+// left alone)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt immediate that waits for the wave's LDS operations only
+constexpr int lgkmcnt0_imm() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 
 // Operand rows r0 + (lane % 16) (r0 a multiple of 16), split k order.
 template <typename T, int COLS>
