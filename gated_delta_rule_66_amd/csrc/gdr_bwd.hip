@@ -1128,6 +1128,14 @@ __global__ __launch_bounds__(512) void bwd_scans_lh_kernel(ScanArgs sa, DhArgs d
   else dh_lh_body<T, OPT>(da, (int)blockIdx.x - n1, (int)gridDim.x - n1, lds);
 }
 
+// The state-gradient scan's output pass alone (the forward's states given,
+// q / k not normalised in the kernel): the loader-wave form.
+template <typename T, int OPT>
+__global__ __launch_bounds__(512) void dh_ld_kernel(DhArgs da) {
+  __shared__ DhLdLds<T> lds;
+  dh_ld_body<T, OPT>(da, (int)blockIdx.x, (int)gridDim.x, lds);
+}
+
 // Pass 1 of the state-gradient scan alone (the forward's states given): with
 // no state-scan LDS beside it two workgroups fit a CU at VB = 1.
 template <typename T, int VB>
@@ -2063,7 +2071,10 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, bool states
   const unsigned n2 = units * pl.cp * sa.nvs;
   const unsigned n1 = states_given ? 0u : n2;
   const dim3 grid(n1 + n2);
-  if (VB == 1)
+  if (VB == 1 && n1 == 0 && !sa.qk_norm) {
+    if (sa.beta_mode) GDR_LAUNCH("bwd_scans", (dh_ld_kernel<T, 2>), grid, dim3(512), st, da);
+    else GDR_LAUNCH("bwd_scans", (dh_ld_kernel<T, 0>), grid, dim3(512), st, da);
+  } else if (VB == 1)
     switch ((sa.qk_norm ? 1 : 0) | (sa.beta_mode ? 2 : 0)) {
       case 0:
         GDR_LAUNCH("bwd_scans", (bwd_scans_lh_kernel<T, 0>), grid, dim3(512), st, sa, da, (int)n1);
