@@ -731,12 +731,12 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int b, int nb, DhLhL
 // chain as in dh_lh_body; wave 4 copies the tiles from HBM into LDS with
 // LDS-direct loads (no registers, no tile stores): in the iteration of chunk
 // c, chunk c-1's dO and A tiles and per-row values before the middle
-// barrier, and chunk c-2's q and k tiles after it, so that each copy has
-// about a chunk's time to land.  Its waits name how many of its
+// barrier, and chunk c-2's q and k tiles after it, so that each copy has a
+// chunk's time or more to land.  Its waits name how many of its
 // newest copies may still be in flight (the vector memory counter retires
 // loads in order).  Waves 5-7 form the P tiles of the chunk while the chain
-// forms K dSn, wave 5 after storing the state gradients from the chain's
-// operand copies.  The tiles are swizzled (sw_off),
+// forms K dSn and e^{gL} dSn + Q^T (scale diag(e^gamma) dO), which need no P;
+// wave 5 first stores the state gradients from the chain's operand copies.  The tiles are swizzled (sw_off),
 // q / k three-deep (slot c % 3), the rest two-deep (slot c & 1); the chain
 // scales the dO fragments of Q^T (scale diag(e^gamma) dO) itself.
 template <typename T>
@@ -883,8 +883,8 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
                        __builtin_bit_cast(uint4, Hx[wq][kb2][l]));
   };
 
-  // before chunk c's first barrier: its q / k and per-row values are in LDS;
-  // its dO / A copies may still be in flight, followed by chunk c-1's q / k
+  // before chunk c's first barrier: its q / k, dO / A and per-row values are
+  // in LDS; chunk c-1's q / k copies may still be in flight
   if (w == 4 && sr.c0 < sr.c1) {
     const int cf = sr.c1 - 1;
     issue_da(cf);
@@ -896,6 +896,7 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     zero_qk(cf);
+    zero_da(cf);
     put_rows(cf);
   }
   // the initial gradient has arrived before the loop (else the loop-entry
@@ -927,17 +928,12 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
     const int b = c & 1, bq = c % 3;
     barrier();  // chunk c's slots are ready; every wave is done with chunk c+1
     f32x4 dd[4];
+    x8 Gb[4], fdo[2];
     if (w == 4) {
-      // chunk c's dO / A have landed once at most the 32 copies of chunk
-      // c-1's q / k are outstanding
-      if (c - 1 >= sr.c0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(32));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      zero_da(c);
       if (c - 1 >= sr.c0) issue_da(c - 1);
     } else if (w < 4) {
       // K dSn of chunk c in four rounds over the key dimension; every
       // fragment of a round is read before it multiplies
-      x8 Gb[4];
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) Gb[kb2] = pack_split<T>(Gs[2 * kb2], Gs[2 * kb2 + 1]);
 #pragma unroll
@@ -952,6 +948,35 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
         for (int tb = 0; tb < 4; ++tb) dd[tb] = mfma16(fk[tb], Gb[kb2], dd[tb]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // dS so far = e^{gL} dSn + Q^T (scale diag(e^gamma) dO): its dO
+      // fragments, each row scaled (row 32 kt + k(grp, e) of the split order)
+      const float eL = __expf(gam[b][63]);
+      x8 Ob[2], fr[8];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) fdo[kt] = frag_tr_split_w<T, CW>(Ds[b], 32 * kt, cw0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 0, 16 * kb);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 4 * grp);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 16 + 4 * grp);
+        x8 f = fdo[kt];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] = from_f<T>(to_f(f[e]) * e0[e]);
+          f[e + 4] = from_f<T>(to_f(f[e + 4]) * e1[e]);
+        }
+        Ob[kt] = f;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[0], Gs[kb] * eL);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 32, 16 * kb);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[1], Gs[kb]);
     } else {
       // waves 5-7: this wave's tiles of P = lower_incl(Q K^T o Gamma) of
       // chunk c, published by the middle barrier; wave 5 first stores the
@@ -984,23 +1009,22 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
     barrier();  // P of chunk c is in LDS; Hx is free
     if (w == 4) {
       // chunk c-2's q / k (issued here, in the chain's long phase), then
-      // chunk c-1's q / k and per-row values land before the next first
-      // barrier; newer: its dO / A (16) and chunk c-2's q / k (32)
+      // chunk c-1's q / k, dO / A and per-row values land before the next
+      // first barrier; newer: chunk c-2's q / k (32)
       if (c - 2 >= sr.c0) issue_qk(c - 2);
       if (c - 1 >= sr.c0) {
-        if (c - 2 >= sr.c0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(48));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+        if (c - 2 >= sr.c0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(32));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         zero_qk(c - 1);
+        zero_da(c - 1);
         put_rows(c - 1);
       }
       continue;
     }
     if (w >= 4) continue;
-    // chunk c's dSn for the store wave (packed again rather than kept live
-    // across the barrier)
+    // chunk c's dSn for the store wave
 #pragma unroll
-    for (int kb2 = 0; kb2 < 4; ++kb2) Hx[w][kb2][l] = pack_split<T>(Gs[2 * kb2], Gs[2 * kb2 + 1]);
-    const float eL = __expf(gam[b][63]);
+    for (int kb2 = 0; kb2 < 4; ++kb2) Hx[w][kb2][l] = Gb[kb2];
 
     // The products below run in rounds of independent accumulators whose
     // LDS fragments are issued before the round multiplies; the scheduling
@@ -1008,10 +1032,8 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
     // would put one LDS latency per MFMA on the chain.
     // Fragment (tb, kt) of P^T or A^T (k = rows 32 kt ..) for kt >= tb / 2.
     auto tk = [](int tb, int kt) { return tb < 2 ? 2 * tb + kt : 2 + tb; };
-    x8 fdo[2], fp[6], fa[6], fr[8];
+    x8 fp[6], fa[6], fr[8];
     f32x4 dlv[4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) fdo[kt] = frag_tr_split_w<T, CW>(Ds[b], 32 * kt, cw0);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -1041,25 +1063,6 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
 #pragma unroll
       for (int e = 0; e < 4; ++e) dd[tb][e] = dlv[tb][e] * dd[tb][e] + a.scale * pd[tb][e];
     const x8 Db[2] = {pack_split<T>(dd[0], dd[1]), pack_split<T>(dd[2], dd[3])};
-    // Q^T's operand scale diag(e^gamma) dO: the dO fragments, each row
-    // scaled (row 32 kt + k(grp, e) of the split order)
-    x8 Ob[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const f32x4 e0 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 4 * grp);
-      const f32x4 e1 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 16 + 4 * grp);
-      x8 f = fdo[kt];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[e] = from_f<T>(to_f(f[e]) * e0[e]);
-        f[e + 4] = from_f<T>(to_f(f[e + 4]) * e1[e]);
-      }
-      Ob[kt] = f;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 0, 16 * kb);
-    __builtin_amdgcn_sched_barrier(0);
     // Z = -diag(beta e^gamma) A^T dDelta
     f32x4 zz[4];
 #pragma unroll
@@ -1069,13 +1072,7 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
         if (kt >= tb / 2) zz[tb] = mfma16(fa[tk(tb, kt)], Db[kt], zz[tb]);
-    // dS = e^{gL} dSn + Q^T (scale diag(e^gamma) dO) + K^T Z
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[0], Gs[kb] * eL);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 32, 16 * kb);
-    __builtin_amdgcn_sched_barrier(0);
+    // dS += K^T Z
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const f32x4 bx = *reinterpret_cast<const f32x4*>(bex[b] + 16 * tb + 4 * grp);
@@ -1083,8 +1080,6 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
       for (int e = 0; e < 4; ++e) zz[tb][e] *= -bx[e];
     }
     const x8 Zb[2] = {pack_split<T>(zz[0], zz[1]), pack_split<T>(zz[2], zz[3])};
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[1], Gs[kb]);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
