@@ -55,8 +55,8 @@ CONFIGS = {
 STATE_BYTES = 128 * 128 * 4     # one fp32 state, per (sequence, value head)
 FLUSH_BYTES = 512 << 20         # written before each cold run: more than the 256 MiB MALL
 FWD_KERNELS = ("fwd_prep", "scan_out", "scan_aug", "scan_state", "cp_combine_fwd")
-BWD_KERNELS = ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "bwd_pipe", "grad",
-               "gate_param_grad")
+BWD_KERNELS = ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "bwd_pipe", "bwd_dyn",
+               "bwd_flags", "grad", "gate_param_grad")
 
 
 def alg_bytes_per_unit(direction, r, isz=2, gsz=2):
@@ -151,6 +151,9 @@ def kernel_bytes(name, B, T, Hq, Hv, nchunks, N, cp, isz=2, gsz=2, with_h0=True,
     if name == "grad":
         dqk = 512 * r if Hq == Hv else 1024
         return TH * (512 * r + 256 + 256 + 128 + 4 + isz + dqk + 256 + isz + gsz) + NCH * 2 * ch
+    if name == "bwd_dyn":  # the state-gradient scan and every chunk's gradients, one launch
+        return (kernel_bytes("dh_scan_out", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht) +
+                kernel_bytes("grad", B, T, Hq, Hv, nchunks, N, cp, isz, gsz, with_h0, with_dht))
     if name == "chunk_offsets":
         return 8 * (N + 1)
     return None

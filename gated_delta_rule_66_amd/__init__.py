@@ -554,10 +554,13 @@ def plan_info(q, v, g_dtype=None, cu_seqlens=None, cu_seqlens_cpu=None, cp_segme
 
 def pipeline_info(q, v, cu_seqlens=None, cu_seqlens_cpu=None, cp_segments=0, wave_tiles=0):
     """The backward's pipeline for these shapes on the states path (the
-    autograd op's backward): ``(slices, bounds)``; with ``slices > 0`` the
-    state-gradient scan runs in ranges of chunks ``bounds[i] .. bounds[i+1]``
+    autograd op's backward): ``(slices, bounds)``.  ``slices == 1``: one
+    launch runs the state-gradient scan and every chunk's gradient
+    workgroups, each starting once its chunk's state gradient is stored
+    (``bounds == [0, chunks]``).  ``slices >= 2`` (q / k normalised in the
+    kernel): the scan runs in ranges of chunks ``bounds[i] .. bounds[i+1]``
     and the last launch runs the gradients of chunks ``bounds[0] ..
-    bounds[1]`` alone; ``(0, [])``: one scan launch, then one gradient
+    bounds[1]`` alone.  ``(0, [])``: one scan launch, then one gradient
     launch."""
     c = _Call(q, v, q.dtype, None, cu_seqlens, cu_seqlens_cpu, False, cp_segments, wave_tiles,
               h_packed=True)

@@ -70,6 +70,11 @@ struct DhArgs {
   // segment slice_p - 1 (both [units, P, K, V] fp32, one buffer).
   int sliced, slice_p, sl_c0, sl_c1;  // sliced: the slice's chunks [sl_c0, sl_c1)
   float* seg_next;
+  // Gradient workgroups in the same launch (bwd_dyn_kernel, loader-wave form
+  // only): per (unit, column block) the number of chunks, counted from the
+  // sequence's end, whose state gradient is stored; the stores and the count
+  // are coherent across the XCDs (sc1).  Null otherwise.
+  unsigned* flags;
 };
 
 template <typename T, int VB, int MODE>
@@ -878,9 +883,20 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
 #pragma unroll
     for (int wq = 0; wq < 4; ++wq)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2)
-        buf_store16_nt(hrs, packed_off(cb0 / 16 + wq, kb2, l) * (int)sizeof(T),
-                       __builtin_bit_cast(uint4, Hx[wq][kb2][l]));
+      for (int kb2 = 0; kb2 < 4; ++kb2) {
+        const int off = packed_off(cb0 / 16 + wq, kb2, l) * (int)sizeof(T);
+        const uint4 x = __builtin_bit_cast(uint4, Hx[wq][kb2][l]);
+        if (a.flags) buf_store16_sc1(hrs, off, x);
+        else buf_store16_nt(hrs, off, x);
+      }
+  };
+  // with gradient workgroups in the launch: chunk cc's state gradient (this
+  // wave's stores, all issued) is complete; count it
+  auto publish = [&](int cc) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (l == 0)
+      buf_store_u32_sc1(buf_rsrc(a.flags, (int64_t)(unit * a.nvs + vs + 1) * 4),
+                        (unit * a.nvs + vs) * 4, (unsigned)(nch - cc));
   };
 
   // before chunk c's first barrier: its q / k, dO / A and per-row values are
@@ -982,7 +998,10 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
       // chunk c, published by the middle barrier; wave 5 first stores the
       // state gradient of chunk c+1 (last in this wave's vector memory
       // queue: a later wait would also wait for these stores)
-      if (w == 5 && c + 1 < sr.c1) store_dh(c + 1);
+      if (w == 5) {
+        if (a.flags && c + 2 < sr.c1) publish(c + 2);  // stored an iteration ago
+        if (c + 1 < sr.c1) store_dh(c + 1);
+      }
       const int sl = __builtin_amdgcn_readfirstlane(w - 5);  // wave-uniform
       const int nt = sl == 2 ? 4 : 3;
 #pragma unroll
@@ -1093,7 +1112,11 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
 
   // the dSn of the last chunk walked (c0)
   __syncthreads();
-  if (w == 5 && sr.c0 < sr.c1) store_dh(sr.c0);
+  if (w == 5 && sr.c0 < sr.c1) {
+    if (a.flags && sr.c0 + 1 < sr.c1) publish(sr.c0 + 1);
+    store_dh(sr.c0);
+    if (a.flags) publish(sr.c0);
+  }
   if (w >= 4) return;
   if (p == 0 && a.dh0) {
 #pragma unroll
@@ -1184,6 +1207,9 @@ struct GradArgs {
   const float* gate_A_log;  // non-null iff the gate is on
   const float* gate_dt_bias;
   float* gpart;
+  // the state gradients are being written in the same launch (bwd_dyn_kernel):
+  // load them coherently (sc1); the progress counts a workgroup waits for
+  const unsigned* flags;
 };
 
 // Eight waves: wave w works on row / column block wr = w % 4 and takes one
@@ -1285,7 +1311,8 @@ __device__ __forceinline__ void grad_half_loads(const GradArgs& a, const GradIte
   const T* hS = reinterpret_cast<const T*>(a.h) + ((int64_t)it.c * a.Hv + it.h) * KV;
   const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)it.c * a.Hv + it.h) * KV;
   tile_load<T, 128, 512>(rs, hS + v0 * kDim, kDim, 64);
-  tile_load<T, 128, 512>(rg, hG + v0 * kDim, kDim, 64);
+  if (a.flags) tile_load<T, 128, 512, 16>(rg, hG + v0 * kDim, kDim, 64);
+  else tile_load<T, 128, 512>(rg, hG + v0 * kDim, kDim, 64);
   tile_load<T, 64, 512>(rv, reinterpret_cast<const T*>(a.v) + (it.t0 * a.Hv + it.h) * kDim + v0,
                         (int64_t)a.Hv * kDim, it.Cc);
   tile_load<T, 64, 512>(ro, reinterpret_cast<const T*>(a.dO) + (it.t0 * a.Hv + it.h) * kDim + v0,
@@ -1906,6 +1933,45 @@ __global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, i
   }
 }
 
+// The backward of a dense batch with few heads in one launch, scheduled by
+// data: blocks [0, nb2) run the state-gradient scan over every chunk
+// (loader-wave form), the rest are the gradient workgroups, the last chunk's
+// first (row g: chunk nch - 1 - g / units of unit g % units).  Blocks are
+// dispatched in order, so the scan's workgroups are resident before any
+// gradient workgroup waits for them; a gradient workgroup waits (bounded)
+// until both column blocks of its unit count its chunk's state gradient as
+// stored, then runs on whatever CU it was given: the chip's idle CUs during
+// the scan, every CU after it.
+constexpr int kDynSpinLimit = 1 << 20;  // about 0.25 s of s_sleep: never reached in a healthy run
+template <typename T, int OPT>
+__global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, int nb2) {
+  static_assert((OPT & 1) == 0, "q / k normalisation runs the sliced pipeline");
+  constexpr size_t B = sizeof(DhLdLds<T>), G = sizeof(GradLds<T>);
+  __shared__ __align__(16) char lds[B > G ? B : G];
+  if ((int)blockIdx.x < nb2) {
+    dh_ld_body<T, OPT>(da, (int)blockIdx.x, nb2, *reinterpret_cast<DhLdLds<T>*>(lds));
+    return;
+  }
+  const int g = (int)blockIdx.x - nb2, units = ga.N * ga.Hv, nch = ga.nc_dense;
+  const int j = nch - 1 - g / units, u = g % units, n = u / ga.Hv, h = u % ga.Hv;
+  if (threadIdx.x == 0) {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ga.flags, (int64_t)units * 2 * 4);
+    const unsigned need = (unsigned)(nch - j);
+    for (int it = 0; it < kDynSpinLimit; ++it) {
+      const unsigned f0 = buf_load_u32_sc1(rs, (2 * u) * 4), f1 = buf_load_u32_sc1(rs, (2 * u + 1) * 4);
+      if (f0 >= need && f1 >= need) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __syncthreads();
+  GradFirst<T> f;
+  grad_body<T, false, false>(ga, n * nch + j, h, ga.N * nch, *reinterpret_cast<GradLds<T>*>(lds), f);
+}
+
+static __global__ void zero_u32_kernel(unsigned* p, int n) {
+  for (int i = (int)threadIdx.x; i < n; i += (int)blockDim.x) p[i] = 0u;
+}
+
 // d A_log[h] and d dt_bias[h]: the per-chunk shares summed over every chunk of
 // every sequence.  One workgroup per head; thread t adds chunks t, t + 256,
 // ... in order, then a fixed pairwise tree combines the 256 partial sums.
@@ -1943,9 +2009,13 @@ __global__ __launch_bounds__(256) void gate_param_grad_kernel(const float* gpart
 // split along T, the one-tile scan, at least 16 chunks per sequence, and few
 // enough (sequence, head) units that the scan leaves at least half the CUs
 // idle (its 64-column workgroups are then at most 128).
+// 0: no pipeline; 1: one launch scheduled by data (bwd_dyn_kernel); S >= 2:
+// S slices (q / k normalised in the kernel, whose scan form has no progress
+// counts).
 static int pipe_slices(const gdr_problem* p, const Plan& pl, bool states_given) {
   if (!states_given || p->cu_seqlens_dev || p->Hq != p->Hv || pl.cp != 1 || pl.vb != 1) return 0;
   if (pl.nc_dense < 16 || (int64_t)pl.N * p->Hv * 2 > 128) return 0;
+  if (!p->use_qk_l2norm) return 1;
   return 2;  // measured at B=2 T=4096 H=32: 2 slices 449 us, 3 slices 455, 4 slices 498,
              // one pass 489
 }
@@ -1957,6 +2027,11 @@ static int pipe_slices(const gdr_problem* p, const Plan& pl, bool states_given) 
 // (idle CUs x scan time of one chunk), about 19 us per gradient workgroup and
 // 2.9 us per scan chunk, and slice p is r times slice p + 1.
 static void pipe_bounds(const gdr_problem* p, const Plan& pl, int S, int* lo) {
+  if (S == 1) {  // one launch over every chunk
+    lo[0] = 0;
+    lo[1] = pl.nc_dense;
+    return;
+  }
   const double units = (double)pl.N * p->Hv;
   const double r = units * 19.0 / ((256.0 - 2.0 * units) * 2.9);
   double w[8], sum = 0.0, x = 1.0;
@@ -1978,7 +2053,7 @@ static void pipe_bounds(const gdr_problem* p, const Plan& pl, int S, int* lo) {
 }
 
 struct BwdLayout {
-  size_t offs, cp, cp2, h, dh, gacc, gpart, pipe, total;
+  size_t offs, cp, cp2, h, dh, gacc, gpart, pipe, flags, total;
 };
 
 static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_given) {
@@ -2005,7 +2080,9 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_gi
   if (p->use_gate) o += align256((size_t)pl.total_chunks * p->Hv * 2 * sizeof(float));
   L.pipe = o;  // the pipelined scan's gradients between slices
   const int S = pipe_slices(p, pl, states_given);
-  if (S) o += align256((size_t)pl.N * p->Hv * S * kDim * kDim * sizeof(float));
+  if (S >= 2) o += align256((size_t)pl.N * p->Hv * S * kDim * kDim * sizeof(float));
+  L.flags = o;  // the data-scheduled launch's progress counts, per (unit, column block)
+  if (S == 1) o += align256((size_t)pl.N * p->Hv * 2 * sizeof(unsigned));
   L.total = o;
   return L;
 }
@@ -2172,7 +2249,26 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   const unsigned nc = (unsigned)pl.total_chunks;
   const int G = p->Hv / p->Hq;
   ga.gva_final = 0;
-  if (S > 0) {
+  if (S == 1) {
+    // one launch: the scan's 2 x units workgroups, then the gradient
+    // workgroups of every chunk, last chunk first, each waiting for its
+    // chunk's state gradient (progress counts zeroed by a kernel, so that a
+    // captured graph replays correctly)
+    const int units = pl.N * p->Hv, nb2 = units * 2;
+    unsigned* flags = reinterpret_cast<unsigned*>(ws + L.flags);
+    GDR_LAUNCH("bwd_flags", zero_u32_kernel, dim3(1), dim3(256), st, flags, nb2);
+    DhArgs d = da;
+    d.P = 1;
+    d.nvs = 2;
+    d.flags = flags;
+    GradArgs g2 = ga;
+    g2.flags = flags;
+    const unsigned blocks = (unsigned)(nb2 + units * pl.nc_dense);
+    if (sa.beta_mode)
+      GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 2>), dim3(blocks), dim3(512), st, d, g2, nb2);
+    else
+      GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 0>), dim3(blocks), dim3(512), st, d, g2, nb2);
+  } else if (S > 0) {
     // launch k runs scan slice S-1-k (while k < S) and the gradient
     // workgroups of slice S-k (once k > 0)
     DhArgs d = da;

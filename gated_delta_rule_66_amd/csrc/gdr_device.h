@@ -405,10 +405,25 @@ __device__ __forceinline__ void buf_store8_nt(__amdgpu_buffer_rsrc_t rs, int off
   __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 2);
 }
 
+// Stores and loads with cache policy sc1: coherent at device scope across
+// the XCDs' L2s (a store is complete, for the wave's vector memory counter,
+// once it is visible to such loads from any CU).  For data handed from one
+// workgroup to another inside a launch.
+__device__ __forceinline__ void buf_store16_sc1(__amdgpu_buffer_rsrc_t rs, int off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, rs, off, 0, 16);
+}
+__device__ __forceinline__ void buf_store_u32_sc1(__amdgpu_buffer_rsrc_t rs, int off, unsigned v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, rs, off, 0, 16);
+}
+__device__ __forceinline__ unsigned buf_load_u32_sc1(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 16);
+}
+
 // Rows [0, rows) of the tile load; rows past that read as zero.  Row r of the
 // tile starts r * gstride elements after g (gstride >= COLS).
-// `t0` is the calling thread's index among the NT cooperating threads.
-template <typename T, int COLS, int NT>
+// `t0` is the calling thread's index among the NT cooperating threads; AUX
+// is the loads' cache policy (16: sc1, coherent across the XCDs' L2s).
+template <typename T, int COLS, int NT, int AUX = 0>
 __device__ __forceinline__ void tile_load(TileRegs<COLS, NT>& t, const T* g, int64_t gstride,
                                           int rows, int t0 = threadIdx.x) {
   constexpr int PR = TileRegs<COLS, NT>::PER_ROW;
@@ -418,7 +433,8 @@ __device__ __forceinline__ void tile_load(TileRegs<COLS, NT>& t, const T* g, int
   for (int i = 0; i < TileRegs<COLS, NT>::N; ++i) {
     const int x = t0 + i * NT;
     const int r = x / PR, c8 = (x % PR) * 8;
-    t.r[i] = buf_load16(rs, r * gs + c8 * (int)sizeof(T));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, r * gs + c8 * (int)sizeof(T), 0, AUX);
+    t.r[i] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 }
 

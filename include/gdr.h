@@ -344,14 +344,17 @@ gdr_status gdr_plan_info(const gdr_problem* p, int backward, int32_t* cp_segment
                          int32_t* wave_tiles);
 
 /* The pipelined backward gdr_chunk_bwd_states runs for `p` (a diagnostic;
- * shapes only).  On a dense batch with few (sequence, head) units the
- * state-gradient scan runs in *slices ranges of chunks, the last range
- * first, each launch pairing one range's scan with the per-chunk gradients
- * of the range the launch before finished; the last launch runs the
- * gradients of chunks [bounds[0], bounds[1]) of every sequence alone.
- * *slices = 0: one scan launch, then one gradient launch.  bounds (nullable)
- * receives up to max_bounds of the *slices + 1 range starts (bounds[*slices]
- * = chunks per sequence). */
+ * shapes only).  On a dense batch with few (sequence, head) units:
+ * *slices = 1: one launch holds the state-gradient scan and the gradient
+ * workgroups of every chunk, the last chunk's first, each starting once
+ * the scan has stored its chunk's state gradient (bounds = 0, chunks per
+ * sequence).  With use_qk_l2norm, *slices >= 2: the scan runs in ranges of
+ * chunks, the last range first, each launch pairing one range's scan with
+ * the per-chunk gradients of the range the launch before finished; the last
+ * launch runs the gradients of chunks [bounds[0], bounds[1]) of every
+ * sequence alone.  *slices = 0: one scan launch, then one gradient launch.
+ * bounds (nullable) receives up to max_bounds of the *slices + 1 range
+ * starts (bounds[*slices] = chunks per sequence). */
 gdr_status gdr_bwd_pipeline_info(const gdr_problem* p, int32_t* slices, int32_t* bounds,
                                  int32_t max_bounds);
 

@@ -179,9 +179,13 @@ def test_backward_pipeline_plan():
     def info(p):
         assert lib.gdr_bwd_pipeline_info(ctypes.byref(p), ctypes.byref(n), b, 9) == 0
         return n.value, (list(b[:n.value + 1]) if n.value else [])
-    # B=2 T=4096 H=32: two slices; the last launch's gradients cover 48 of the
-    # 64 chunks, 3072 workgroups, twelve whole rounds of the 256 CUs
-    assert info(good(B=2, N=2, T=4096, Hq=32, Hv=32)) == (2, [0, 48, 64])
+    # B=2 T=4096 H=32: one launch scheduled by data (the scan and every
+    # chunk's gradient workgroups)
+    assert info(good(B=2, N=2, T=4096, Hq=32, Hv=32)) == (1, [0, 64])
+    # with q / k normalised in the kernel, two slices; the last launch's
+    # gradients cover 48 of the 64 chunks, 3072 workgroups, twelve whole
+    # rounds of the 256 CUs
+    assert info(good(B=2, N=2, T=4096, Hq=32, Hv=32, use_qk_l2norm=1)) == (2, [0, 48, 64])
     # one pass: grouped heads, packed sequences, a scan that fills the chip,
     # short sequences, a split along T
     assert info(good(B=2, N=2, T=4096, Hq=16, Hv=32))[0] == 0
@@ -191,7 +195,8 @@ def test_backward_pipeline_plan():
     assert info(good(B=1, N=1, T=65536, Hq=32, Hv=32))[0] == 0
     # fewer units leave more CUs idle beside the scan, which then hide the
     # gradients of a longer first slice: the slice walked first grows
-    s, bnd = info(good(B=1, N=1, T=1024, Hq=8, Hv=8))
+    assert info(good(B=1, N=1, T=1024, Hq=8, Hv=8)) == (1, [0, 16])
+    s, bnd = info(good(B=1, N=1, T=1024, Hq=8, Hv=8, use_qk_l2norm=1))
     assert s == 2 and bnd[0] == 0 and bnd[2] == 16 and 0 < bnd[1] < 8
 
 

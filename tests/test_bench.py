@@ -123,7 +123,8 @@ def test_fractions_take_the_larger_bound():
 def test_every_library_kernel_has_a_direction():
     for k in ("fwd_prep", "scan_out", "scan_aug", "cp_combine_fwd"):
         assert bench.kernel_direction(k) == "fwd"
-    for k in ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "grad"):
+    for k in ("bwd_scans", "bwd_scan_aug", "cp_combine_bwd", "bwd_pipe", "bwd_dyn", "bwd_flags",
+              "grad"):
         assert bench.kernel_direction(k) == "bwd"
 
 
