@@ -744,9 +744,19 @@ __device__ __forceinline__ void dh_lh_body(const DhArgs& a, int b, int nb, DhLhL
 // wave 5 first stores the state gradients from the chain's operand copies.  The tiles are swizzled (sw_off),
 // q / k three-deep (slot c % 3), the rest two-deep (slot c & 1); the chain
 // scales the dO fragments of Q^T (scale diag(e^gamma) dO) itself.
+// dSn of the chain's chunk as bf16 operand registers ([column block][k
+// block][lane]), stored by wave 5 in the next iteration (64-column form only)
+template <typename T, bool HAS>
+struct DhLdHx {
+  alignas(16) typename VT<T>::x8 Hx[4][4][64];
+};
 template <typename T>
-struct DhLdLds {
-  static constexpr int CW = 64, LDA = 72;
+struct DhLdHx<T, false> {};
+
+// NB: 16-column blocks per chain wave (the workgroup's columns: 64 NB)
+template <typename T, int NB = 1>
+struct DhLdLds : DhLdHx<T, NB == 1> {
+  static constexpr int CW = 64 * NB, LDA = 72;
   alignas(16) T Qs[3][64 * 128];
   alignas(16) T Ks[3][64 * 128];
   alignas(16) T Ds[2][64 * CW];
@@ -756,17 +766,15 @@ struct DhLdLds {
   alignas(16) float eg[2][64];
   alignas(16) float bex[2][64];
   alignas(16) float dl[2][64];
-  // dSn of the chain's chunk as bf16 operand registers ([column block][k
-  // block][lane]), stored by wave 5 in the next iteration
-  alignas(16) typename VT<T>::x8 Hx[4][4][64];
 };
 
-template <typename T, int OPT>
-__device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdLds<T>& L) {
+template <typename T, int OPT, int NB = 1>
+__device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdLds<T, NB>& L) {
   typedef typename VT<T>::x8 x8;
   static_assert((OPT & 1) == 0, "q / k normalisation runs in dh_lh_body");
-  constexpr int CW = DhLdLds<T>::CW;
-  constexpr int LDA = DhLdLds<T>::LDA;
+  static_assert(NB == 1 || NB == 2, "one or two column blocks per chain wave");
+  constexpr int CW = DhLdLds<T, NB>::CW;
+  constexpr int LDA = DhLdLds<T, NB>::LDA;
   auto& Qs = L.Qs;
   auto& Ks = L.Ks;
   auto& Ds = L.Ds;
@@ -776,7 +784,6 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
   auto& eg = L.eg;
   auto& bex = L.bex;
   auto& dl = L.dl;
-  auto& Hx = L.Hx;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, grp = l >> 4, col = l & 15;
   // a pipelined slice runs one segment of every unit
@@ -797,32 +804,46 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
   const int cb0 = vs * CW;
   const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
   const int64_t KV = (int64_t)kDim * kDim;
-  const int cw0 = 16 * (w & 3);
+  // chain wave w's 16-column blocks: w, w + 4 (columns cb0 + cw(j) ..)
+  auto cw = [&](int j) { return 16 * ((w & 3) + 4 * j); };
+  // The lane index the chain's fragment addresses derive from: in the
+  // 128-column form an opaque copy per phase, so that the compiler computes
+  // the swizzled addresses where they are used instead of hoisting every one
+  // of them out of the loop (they would hold the registers the wider chain
+  // needs and spill)
+  auto fresh_lane = [&]() {
+    int x = l;
+    if constexpr (NB == 2) asm volatile("" : "+v"(x));
+    return x;
+  };
 
   // gradient entering the segment's end: dht (last segment) or the value
   // chained by pass 2; every load is issued before the first is used (null
-  // reads zeros)
-  f32x4 Gs[8];
+  // reads zeros).  Gs[8 j + kb]: column block j, keys 16 kb ..
+  f32x4 Gs[8 * NB];
   if (w < 4) {
     const float* src = (p == sr.p_last) ? (a.dht ? a.dht + unit * KV : nullptr)
                                         : a.seg_start + ((int64_t)unit * a.P + p) * KV;
     const bool vf = (p == sr.p_last) && a.svf;
     const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
-        Gs[kb][e] = buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
-      }
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw(j) + col;
+          Gs[8 * j + kb][e] =
+              buf_load_f32(srs, (vf ? vc * kDim + key : key * kDim + vc) * (int)sizeof(float));
+        }
   }
 
-  // wave 4's copies: per-row values and dO / A of chunk c (3 + 16 loads, in
-  // that order), q / k of chunk c (32 loads)
+  // wave 4's copies: per-row values and dO / A of chunk c (3 + 8 NB + 8
+  // loads, in that order), q / k of chunk c (32 loads)
   float r_g = 0.f, r_gl = 0.f;
   T r_bt = from_f<T>(0.f);  // raw: converted where it is used, not where it lands
   auto chunk_rows = [&](int c) { return (int)min((int64_t)kChunk, s.end - s.start - (int64_t)kChunk * c); };
-  auto issue_da = [&](int c) {
+  auto issue_da = [&](int c, int lq) {
     const int bs = c & 1, Cc = chunk_rows(c);
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int gv = a.Hv * kDim * (int)sizeof(T), ga = a.Hv * kChunk * (int)sizeof(T);
@@ -832,39 +853,40 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
     __builtin_amdgcn_sched_barrier(0);  // the three loads first, as the waits count
     tile_dma<CW>(buf_rsrc(reinterpret_cast<const T*>(a.dO) + (t0 * a.Hv + h) * kDim + cb0,
                           (int64_t)Cc * gv),
-                 gv, Ds[bs]);
+                 gv, Ds[bs], lq);
     tile_dma<64>(buf_rsrc(reinterpret_cast<const T*>(a.A) + (t0 * a.Hv + h) * kChunk,
                           (int64_t)Cc * ga),
-                 ga, As[bs]);
+                 ga, As[bs], lq);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto issue_qk = [&](int c) {
+  auto issue_qk = [&](int c, int lq) {
     const int bs = c % 3, Cc = chunk_rows(c);
     const int64_t t0 = s.start + (int64_t)kChunk * c;
     const int gq = a.Hq * kDim * (int)sizeof(T);
     tile_dma<128>(buf_rsrc(reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gq),
-                  gq, Qs[bs]);
+                  gq, Qs[bs], lq);
     tile_dma<128>(buf_rsrc(reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gq),
-                  gq, Ks[bs]);
+                  gq, Ks[bs], lq);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // rows past the chunk's end are zero whatever the copies left there
+  // rows past the chunk's end are zero whatever the copies left there (a
+  // tile row r is bytes [r, r + 1) x its row size, swizzled within the row)
   const uint4 z4 = make_uint4(0, 0, 0, 0);
-  auto zero_da = [&](int c) {
+  auto zero_da = [&](int c, int l) {
     const int bs = c & 1, Cc = chunk_rows(c);
-    for (int x = 16 * l; x < (kChunk - Cc) * 128; x += 1024) {
-      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Ds[bs]) + Cc * 128 + x) = z4;
+    for (int x = 16 * l; x < (kChunk - Cc) * 2 * CW; x += 1024)
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Ds[bs]) + Cc * 2 * CW + x) = z4;
+    for (int x = 16 * l; x < (kChunk - Cc) * 128; x += 1024)
       *reinterpret_cast<uint4*>(reinterpret_cast<char*>(As[bs]) + Cc * 128 + x) = z4;
-    }
   };
-  auto zero_qk = [&](int c) {
+  auto zero_qk = [&](int c, int l) {
     const int bs = c % 3, Cc = chunk_rows(c);
     for (int x = 16 * l; x < (kChunk - Cc) * 256; x += 1024) {
       *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Qs[bs]) + Cc * 256 + x) = z4;
       *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Ks[bs]) + Cc * 256 + x) = z4;
     }
   };
-  auto put_rows = [&](int c) {  // the per-row values loaded by issue_da(c)
+  auto put_rows = [&](int c, int l) {  // the per-row values loaded by issue_da(c)
     const int bs = c & 1;
     const bool ok = l < chunk_rows(c);
     const float e = __expf(r_g), r_b = to_f(r_bt);
@@ -874,26 +896,33 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
     dl[bs][l] = __expf(r_gl - r_g);
   };
 
-  // gradient of chunk cc's end state out, packed (packed_off), from the
-  // operand copies the chain left in Hx; non-temporal, as this pass never
-  // reads it back
-  auto store_dh = [&](int cc) {
-    const __amdgpu_buffer_rsrc_t hrs =
-        buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + cc) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
-#pragma unroll
-    for (int wq = 0; wq < 4; ++wq)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2) {
-        const int off = packed_off(cb0 / 16 + wq, kb2, l) * (int)sizeof(T);
-        const uint4 x = __builtin_bit_cast(uint4, Hx[wq][kb2][l]);
-        if (a.flags) buf_store16_sc1(hrs, off, x);
-        else buf_store16_nt(hrs, off, x);
-      }
+  // gradient of chunk cc's end state out, packed (packed_off)
+  auto dh_rsrc = [&](int cc) {
+    return buf_rsrc(reinterpret_cast<T*>(a.dh) + ((choff + cc) * a.Hv + h) * KV, KV * (int64_t)sizeof(T));
   };
-  // with gradient workgroups in the launch: chunk cc's state gradient (this
-  // wave's stores, all issued) is complete; count it
+  // 64-column form: wave 5 stores it from the operand copies the chain left
+  // in Hx; non-temporal, as this pass never reads it back (coherent, sc1,
+  // when gradient workgroups in the same launch read it)
+  auto store_dh = [&](int cc) {
+    if constexpr (NB == 1) {
+      const __amdgpu_buffer_rsrc_t hrs = dh_rsrc(cc);
+#pragma unroll
+      for (int wq = 0; wq < 4; ++wq)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2) {
+          const int off = packed_off(cb0 / 16 + wq, kb2, l) * (int)sizeof(T);
+          const uint4 x = __builtin_bit_cast(uint4, L.Hx[wq][kb2][l]);
+          if (a.flags) buf_store16_sc1(hrs, off, x);
+          else buf_store16_nt(hrs, off, x);
+        }
+    }
+  };
+  // with gradient workgroups in the launch: chunk cc's state gradient is
+  // complete (64-column form: this wave's stores, all issued; 128-column
+  // form: the chain waves waited for theirs before the barrier this follows);
+  // count it
   auto publish = [&](int cc) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if constexpr (NB == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     if (l == 0)
       buf_store_u32_sc1(buf_rsrc(a.flags, (int64_t)(unit * a.nvs + vs + 1) * 4),
                         (unit * a.nvs + vs) * 4, (unsigned)(nch - cc));
@@ -903,17 +932,17 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
   // in LDS; chunk c-1's q / k copies may still be in flight
   if (w == 4 && sr.c0 < sr.c1) {
     const int cf = sr.c1 - 1;
-    issue_da(cf);
-    issue_qk(cf);
+    issue_da(cf, l);
+    issue_qk(cf, l);
     if (cf - 1 >= sr.c0) {
-      issue_qk(cf - 1);
+      issue_qk(cf - 1, l);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(32));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    zero_qk(cf);
-    zero_da(cf);
-    put_rows(cf);
+    zero_qk(cf, l);
+    zero_da(cf, l);
+    put_rows(cf, l);
   }
   // the initial gradient has arrived before the loop (else the loop-entry
   // merge makes its first use wait for later loads as well)
@@ -925,13 +954,15 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
   constexpr uint64_t pcode = 0x0ull | (0x4ull << 4) | (0x5ull << 8) |
                              ((0x8ull | (0x9ull << 4) | (0xAull << 8)) << 16) |
                              ((0xCull | (0xDull << 4) | (0xEull << 8) | (0xFull << 12)) << 32);
-  // Wave 4 meets the barriers without __syncthreads' fences: they would wait
-  // for every copy in flight (the LDS-direct loads count as its LDS writes).
-  // Its own waits are explicit: the copies the next phase reads (above) and
-  // its LDS stores (here); the wavefront-scope fences only keep the compiler
-  // from moving its memory operations across the barrier.
+  // Wave 4 (and, in the 128-column form, the chain waves, whose state
+  // gradient stores are in flight) meet the barriers without
+  // __syncthreads' fences: they would wait for every copy or store in flight
+  // (the LDS-direct loads count as LDS writes).  Their own waits are
+  // explicit: the copies the next phase reads and the LDS stores (here); the
+  // wavefront-scope fences only keep the compiler from moving memory
+  // operations across the barrier.
   auto barrier = [&]() {
-    if (w == 4) {
+    if (w == 4 || (NB == 2 && w < 4)) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
       __builtin_amdgcn_s_barrier();
@@ -943,67 +974,98 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
   for (int c = sr.c1 - 1; c >= sr.c0; --c) {
     const int b = c & 1, bq = c % 3;
     barrier();  // chunk c's slots are ready; every wave is done with chunk c+1
-    f32x4 dd[4];
-    x8 Gb[4], fdo[2];
+    f32x4 dd[NB][4];
+    x8 Gb[NB][4], fdo[NB][2];
     if (w == 4) {
-      if (c - 1 >= sr.c0) issue_da(c - 1);
+      if (c - 1 >= sr.c0) issue_da(c - 1, fresh_lane());
     } else if (w < 4) {
+      const int lq = fresh_lane();
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2)
+          Gb[j][kb2] = pack_split<T>(Gs[8 * j + 2 * kb2], Gs[8 * j + 2 * kb2 + 1]);
+      if constexpr (NB == 2) {
+        // chunk c+1's stores (issued an iteration ago) are complete before
+        // the middle barrier, after which wave 5 counts them; then chunk c's
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        const __amdgpu_buffer_rsrc_t hrs = dh_rsrc(c);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int kb2 = 0; kb2 < 4; ++kb2)
+            buf_store16_sc1(hrs, packed_off((cb0 + cw(j)) / 16, kb2, lq) * (int)sizeof(T),
+                            __builtin_bit_cast(uint4, Gb[j][kb2]));
+      }
       // K dSn of chunk c in four rounds over the key dimension; every
       // fragment of a round is read before it multiplies
 #pragma unroll
-      for (int kb2 = 0; kb2 < 4; ++kb2) Gb[kb2] = pack_split<T>(Gs[2 * kb2], Gs[2 * kb2 + 1]);
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) dd[tb] = zero4();
+        for (int tb = 0; tb < 4; ++tb) dd[j][tb] = zero4();
 #pragma unroll
       for (int kb2 = 0; kb2 < 4; ++kb2) {
         x8 fk[4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) fk[tb] = frag_row_split_w<T, 128>(Ks[bq], 16 * tb, 32 * kb2);
+        for (int tb = 0; tb < 4; ++tb) fk[tb] = frag_row_split_w<T, 128>(Ks[bq], 16 * tb, 32 * kb2, lq);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) dd[tb] = mfma16(fk[tb], Gb[kb2], dd[tb]);
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) dd[j][tb] = mfma16(fk[tb], Gb[j][kb2], dd[j][tb]);
         __builtin_amdgcn_sched_barrier(0);
       }
       // dS so far = e^{gL} dSn + Q^T (scale diag(e^gamma) dO): its dO
       // fragments, each row scaled (row 32 kt + k(grp, e) of the split order)
       const float eL = __expf(gam[b][63]);
-      x8 Ob[2], fr[8];
+      x8 Ob[NB][2], fr[8];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) fdo[kt] = frag_tr_split_w<T, CW>(Ds[b], 32 * kt, cw0);
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 0, 16 * kb);
+        for (int kt = 0; kt < 2; ++kt) fdo[j][kt] = frag_tr_split_w<T, CW>(Ds[b], 32 * kt, cw(j), lq);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 0, 16 * kb, lq);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const f32x4 e0 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 4 * grp);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 16 + 4 * grp);
-        x8 f = fdo[kt];
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 4 * (lq >> 4));
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(eg[b] + 32 * kt + 16 + 4 * (lq >> 4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[e] = from_f<T>(to_f(f[e]) * e0[e]);
-          f[e + 4] = from_f<T>(to_f(f[e + 4]) * e1[e]);
+        for (int j = 0; j < NB; ++j) {
+          x8 f = fdo[j][kt];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f[e] = from_f<T>(to_f(f[e]) * e0[e]);
+            f[e + 4] = from_f<T>(to_f(f[e + 4]) * e1[e]);
+          }
+          Ob[j][kt] = f;
         }
-        Ob[kt] = f;
       }
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[0], Gs[kb] * eL);
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) Gs[8 * j + kb] = mfma16(fr[kb], Ob[j][0], Gs[8 * j + kb] * eL);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 32, 16 * kb);
+      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Qs[bq], 32, 16 * kb, lq);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Ob[1], Gs[kb]);
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) Gs[8 * j + kb] = mfma16(fr[kb], Ob[j][1], Gs[8 * j + kb]);
     } else {
       // waves 5-7: this wave's tiles of P = lower_incl(Q K^T o Gamma) of
-      // chunk c, published by the middle barrier; wave 5 first stores the
-      // state gradient of chunk c+1 (last in this wave's vector memory
-      // queue: a later wait would also wait for these stores)
-      if (w == 5) {
+      // chunk c, published by the middle barrier; in the 64-column form
+      // wave 5 first stores the state gradient of chunk c+1 (last in this
+      // wave's vector memory queue: a later wait would also wait for these
+      // stores)
+      if (NB == 1 && w == 5) {
         if (a.flags && c + 2 < sr.c1) publish(c + 2);  // stored an iteration ago
         if (c + 1 < sr.c1) store_dh(c + 1);
       }
       const int sl = __builtin_amdgcn_readfirstlane(w - 5);  // wave-uniform
       const int nt = sl == 2 ? 4 : 3;
+      const int lp = fresh_lane(), pgrp = lp >> 4, pcol = lp & 15;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if (t < nt) {
@@ -1011,13 +1073,13 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
           f32x4 acc = zero4();
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)  // split k order, as dh_lh_body's chain
-            acc = mfma16(frag_row_split_w<T, 128>(Qs[bq], 16 * rb, 32 * kk),
-                         frag_row_split_w<T, 128>(Ks[bq], 16 * cb, 32 * kk), acc);
-          const f32x4 gr = *reinterpret_cast<const f32x4*>(gam[b] + 16 * rb + 4 * grp);
-          const float gi = gam[b][16 * cb + col];
+            acc = mfma16(frag_row_split_w<T, 128>(Qs[bq], 16 * rb, 32 * kk, lp),
+                         frag_row_split_w<T, 128>(Ks[bq], 16 * cb, 32 * kk, lp), acc);
+          const f32x4 gr = *reinterpret_cast<const f32x4*>(gam[b] + 16 * rb + 4 * pgrp);
+          const float gi = gam[b][16 * cb + pcol];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rb + 4 * grp + e, i = 16 * cb + col;
+            const int r = 16 * rb + 4 * pgrp + e, i = 16 * cb + pcol;
             // masked entries take exp(-inf) = 0 (an unconditional exponential)
             const float pv = acc[e] * __expf((rb != cb || i <= r) ? gr[e] - gi : -INFINITY);
             Ps[r * LDA + i] = from_f<T>(pv);
@@ -1030,20 +1092,24 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
       // chunk c-2's q / k (issued here, in the chain's long phase), then
       // chunk c-1's q / k, dO / A and per-row values land before the next
       // first barrier; newer: chunk c-2's q / k (32)
-      if (c - 2 >= sr.c0) issue_qk(c - 2);
+      const int lq = fresh_lane();
+      if (c - 2 >= sr.c0) issue_qk(c - 2, lq);
       if (c - 1 >= sr.c0) {
         if (c - 2 >= sr.c0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(32));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        zero_qk(c - 1);
-        zero_da(c - 1);
-        put_rows(c - 1);
+        zero_qk(c - 1, lq);
+        zero_da(c - 1, lq);
+        put_rows(c - 1, lq);
       }
       continue;
     }
+    if (NB == 2 && w == 5 && a.flags && c + 1 < sr.c1) publish(c + 1);
     if (w >= 4) continue;
     // chunk c's dSn for the store wave
+    if constexpr (NB == 1) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 4; ++kb2) Hx[w][kb2][l] = Gb[kb2];
+      for (int kb2 = 0; kb2 < 4; ++kb2) L.Hx[w][kb2][l] = Gb[0][kb2];
+    }
 
     // The products below run in rounds of independent accumulators whose
     // LDS fragments are issued before the round multiplies; the scheduling
@@ -1051,6 +1117,7 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
     // would put one LDS latency per MFMA on the chain.
     // Fragment (tb, kt) of P^T or A^T (k = rows 32 kt ..) for kt >= tb / 2.
     auto tk = [](int tb, int kt) { return tb < 2 ? 2 * tb + kt : 2 + tb; };
+    const int lq = fresh_lane();
     x8 fp[6], fa[6], fr[8];
     f32x4 dlv[4];
 #pragma unroll
@@ -1059,81 +1126,143 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
       for (int kt = tb / 2; kt < 2; ++kt)
         fp[tk(tb, kt)] = frag_tr_split(Ps + 32 * kt * LDA + 16 * tb, LDA);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) dlv[tb] = *reinterpret_cast<const f32x4*>(dl[b] + 16 * tb + 4 * grp);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int tb = 0; tb < 4; ++tb) dlv[tb] = *reinterpret_cast<const f32x4*>(dl[b] + 16 * tb + 4 * (lq >> 4));
     // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO
-    f32x4 pd[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) pd[tb] = zero4();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    x8 Db[NB][2];
+    auto delta = [&](int j, const f32x4 (&pd)[4]) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
-        if (kt >= tb / 2) pd[tb] = mfma16(fp[tk(tb, kt)], fdo[kt], pd[tb]);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+        for (int e = 0; e < 4; ++e) dd[j][tb][e] = dlv[tb][e] * dd[j][tb][e] + a.scale * pd[tb][e];
+      Db[j][0] = pack_split<T>(dd[j][0], dd[j][1]);
+      Db[j][1] = pack_split<T>(dd[j][2], dd[j][3]);
+    };
+    if constexpr (NB == 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 pd[4];
 #pragma unroll
-      for (int kt = tb / 2; kt < 2; ++kt)
-        fa[tk(tb, kt)] = frag_tr_split_w<T, 64>(As[b], 32 * kt, 16 * tb);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int tb = 0; tb < 4; ++tb) pd[tb] = zero4();
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dd[tb][e] = dlv[tb][e] * dd[tb][e] + a.scale * pd[tb][e];
-    const x8 Db[2] = {pack_split<T>(dd[0], dd[1]), pack_split<T>(dd[2], dd[3])};
+        for (int tb = 0; tb < 4; ++tb)
+          if (kt >= tb / 2) pd[tb] = mfma16(fp[tk(tb, kt)], fdo[0][kt], pd[tb]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kt = tb / 2; kt < 2; ++kt)
+          fa[tk(tb, kt)] = frag_tr_split_w<T, 64>(As[b], 32 * kt, 16 * tb, lq);
+      __builtin_amdgcn_sched_barrier(0);
+      delta(0, pd);
+    } else {
+      // 128-column form: one column block at a time, its dO fragments read
+      // again (chunk c's slot is unchanged until the next iteration's
+      // copies) rather than held across the barrier
+      x8 fo[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) fo[0][kt] = frag_tr_split_w<T, CW>(Ds[b], 32 * kt, cw(0), lq);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) fo[1][kt] = frag_tr_split_w<T, CW>(Ds[b], 32 * kt, cw(1), lq);
+      f32x4 pd[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) pd[tb] = zero4();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          if (kt >= tb / 2) pd[tb] = mfma16(fp[tk(tb, kt)], fo[0][kt], pd[tb]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kt = tb / 2; kt < 2; ++kt)
+          fa[tk(tb, kt)] = frag_tr_split_w<T, 64>(As[b], 32 * kt, 16 * tb, lq);
+      delta(0, pd);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) pd[tb] = zero4();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          if (kt >= tb / 2) pd[tb] = mfma16(fp[tk(tb, kt)], fo[1][kt], pd[tb]);
+      __builtin_amdgcn_sched_barrier(0);
+      delta(1, pd);
+    }
     // Z = -diag(beta e^gamma) A^T dDelta
-    f32x4 zz[4];
+    f32x4 zz[NB][4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) zz[tb] = zero4();
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) zz[j][tb] = zero4();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        if (kt >= tb / 2) zz[tb] = mfma16(fa[tk(tb, kt)], Db[kt], zz[tb]);
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          if (kt >= tb / 2) zz[j][tb] = mfma16(fa[tk(tb, kt)], Db[j][kt], zz[j][tb]);
     // dS += K^T Z
+    x8 Zb[NB][2];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const f32x4 bx = *reinterpret_cast<const f32x4*>(bex[b] + 16 * tb + 4 * grp);
+      const f32x4 bx = *reinterpret_cast<const f32x4*>(bex[b] + 16 * tb + 4 * (lq >> 4));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zz[tb][e] *= -bx[e];
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zz[j][tb][e] *= -bx[e];
     }
-    const x8 Zb[2] = {pack_split<T>(zz[0], zz[1]), pack_split<T>(zz[2], zz[3])};
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      Zb[j][0] = pack_split<T>(zz[j][0], zz[j][1]);
+      Zb[j][1] = pack_split<T>(zz[j][2], zz[j][3]);
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Ks[bq], 32 * kt, 16 * kb);
+      for (int kb = 0; kb < 8; ++kb) fr[kb] = frag_tr_split_w<T, 128>(Ks[bq], 32 * kt, 16 * kb, lq);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) Gs[kb] = mfma16(fr[kb], Zb[kt], Gs[kb]);
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) Gs[8 * j + kb] = mfma16(fr[kb], Zb[j][kt], Gs[8 * j + kb]);
     }
   }
 
-  // the dSn of the last chunk walked (c0)
+  // the dSn of the last chunk walked (c0): 64-column form, wave 5 stores it;
+  // 128-column form, the chain's own stores are complete before the barrier
+  if (NB == 2 && w < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   if (w == 5 && sr.c0 < sr.c1) {
-    if (a.flags && sr.c0 + 1 < sr.c1) publish(sr.c0 + 1);
-    store_dh(sr.c0);
+    if (NB == 1) {
+      if (a.flags && sr.c0 + 1 < sr.c1) publish(sr.c0 + 1);
+      store_dh(sr.c0);
+    }
     if (a.flags) publish(sr.c0);
   }
   if (w >= 4) return;
   if (p == 0 && a.dh0) {
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw0 + col;
-        a.dh0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = Gs[kb][e];
-      }
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 16 * kb + 4 * grp + e, vc = cb0 + cw(j) + col;
+          a.dh0[unit * KV + (a.svf ? vc * kDim + key : key * kDim + vc)] = Gs[8 * j + kb][e];
+        }
   } else if (a.sliced && p > 0) {
     // the gradient entering the previous segment's end, for the next launch
     float* dst = a.seg_next + ((int64_t)unit * a.P + p - 1) * KV;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dst[(16 * kb + 4 * grp + e) * kDim + cb0 + cw0 + col] = Gs[kb][e];
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[(16 * kb + 4 * grp + e) * kDim + cb0 + cw(j) + col] = Gs[8 * j + kb][e];
   }
 }
 
@@ -1935,31 +2064,30 @@ __global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, i
 
 // The backward of a dense batch with few heads in one launch, scheduled by
 // data: blocks [0, nb2) run the state-gradient scan over every chunk
-// (loader-wave form), the rest are the gradient workgroups, the last chunk's
-// first (row g: chunk nch - 1 - g / units of unit g % units).  Blocks are
-// dispatched in order, so the scan's workgroups are resident before any
-// gradient workgroup waits for them; a gradient workgroup waits (bounded)
-// until both column blocks of its unit count its chunk's state gradient as
-// stored, then runs on whatever CU it was given: the chip's idle CUs during
-// the scan, every CU after it.
+// (loader-wave form, one 128-column workgroup per unit), the rest are the
+// gradient workgroups, the last chunk's first (row g: chunk nch - 1 - g /
+// units of unit g % units).  Blocks are dispatched in order, so the scan's
+// workgroups are resident before any gradient workgroup waits for them; a
+// gradient workgroup waits (bounded) until its unit's count covers its
+// chunk's state gradient, then runs on whatever CU it was given: the chip's
+// idle CUs during the scan, every CU after it.
 constexpr int kDynSpinLimit = 1 << 20;  // about 0.25 s of s_sleep: never reached in a healthy run
 template <typename T, int OPT>
 __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, int nb2) {
   static_assert((OPT & 1) == 0, "q / k normalisation runs the sliced pipeline");
-  constexpr size_t B = sizeof(DhLdLds<T>), G = sizeof(GradLds<T>);
+  constexpr size_t B = sizeof(DhLdLds<T, 2>), G = sizeof(GradLds<T>);
   __shared__ __align__(16) char lds[B > G ? B : G];
   if ((int)blockIdx.x < nb2) {
-    dh_ld_body<T, OPT>(da, (int)blockIdx.x, nb2, *reinterpret_cast<DhLdLds<T>*>(lds));
+    dh_ld_body<T, OPT, 2>(da, (int)blockIdx.x, nb2, *reinterpret_cast<DhLdLds<T, 2>*>(lds));
     return;
   }
   const int g = (int)blockIdx.x - nb2, units = ga.N * ga.Hv, nch = ga.nc_dense;
   const int j = nch - 1 - g / units, u = g % units, n = u / ga.Hv, h = u % ga.Hv;
   if (threadIdx.x == 0) {
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ga.flags, (int64_t)units * 2 * 4);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ga.flags, (int64_t)units * 4);
     const unsigned need = (unsigned)(nch - j);
     for (int it = 0; it < kDynSpinLimit; ++it) {
-      const unsigned f0 = buf_load_u32_sc1(rs, (2 * u) * 4), f1 = buf_load_u32_sc1(rs, (2 * u + 1) * 4);
-      if (f0 >= need && f1 >= need) break;
+      if (buf_load_u32_sc1(rs, u * 4) >= need) break;
       __builtin_amdgcn_s_sleep(8);
     }
   }
@@ -2081,8 +2209,8 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_gi
   L.pipe = o;  // the pipelined scan's gradients between slices
   const int S = pipe_slices(p, pl, states_given);
   if (S >= 2) o += align256((size_t)pl.N * p->Hv * S * kDim * kDim * sizeof(float));
-  L.flags = o;  // the data-scheduled launch's progress counts, per (unit, column block)
-  if (S == 1) o += align256((size_t)pl.N * p->Hv * 2 * sizeof(unsigned));
+  L.flags = o;  // the data-scheduled launch's progress counts, one per unit
+  if (S == 1) o += align256((size_t)pl.N * p->Hv * sizeof(unsigned));
   L.total = o;
   return L;
 }
@@ -2250,16 +2378,16 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   const int G = p->Hv / p->Hq;
   ga.gva_final = 0;
   if (S == 1) {
-    // one launch: the scan's 2 x units workgroups, then the gradient
+    // one launch: the scan's units workgroups (128 columns each), then the gradient
     // workgroups of every chunk, last chunk first, each waiting for its
     // chunk's state gradient (progress counts zeroed by a kernel, so that a
     // captured graph replays correctly)
-    const int units = pl.N * p->Hv, nb2 = units * 2;
+    const int units = pl.N * p->Hv, nb2 = units;
     unsigned* flags = reinterpret_cast<unsigned*>(ws + L.flags);
-    GDR_LAUNCH("bwd_flags", zero_u32_kernel, dim3(1), dim3(256), st, flags, nb2);
+    GDR_LAUNCH("bwd_flags", zero_u32_kernel, dim3(1), dim3(256), st, flags, units);
     DhArgs d = da;
     d.P = 1;
-    d.nvs = 2;
+    d.nvs = 1;
     d.flags = flags;
     GradArgs g2 = ga;
     g2.flags = flags;

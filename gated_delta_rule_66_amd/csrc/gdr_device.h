@@ -282,8 +282,9 @@ constexpr int lgkmcnt0_imm() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 
 // Operand rows r0 + (lane % 16) (r0 a multiple of 16), split k order.
 template <typename T, int COLS>
-__device__ __forceinline__ typename VT<T>::x8 frag_row_split_w(const T* X, int r0, int k0) {
-  const int l = lane_id(), r = r0 + (l & 15), c = k0 + 4 * (l >> 4);
+__device__ __forceinline__ typename VT<T>::x8 frag_row_split_w(const T* X, int r0, int k0,
+                                                                int l = lane_id()) {
+  const int r = r0 + (l & 15), c = k0 + 4 * (l >> 4);
   typedef typename VT<T>::x4 x4;
   const x4 lo = *reinterpret_cast<const x4*>(X + sw_off<COLS>(r, c));
   const x4 hi = *reinterpret_cast<const x4*>(X + sw_off<COLS>(r, c + 16));
@@ -301,8 +302,9 @@ __device__ __forceinline__ typename VT<T>::x8 frag_row_w(const T* X, int r0, int
 // Transposed operand, split k order: k runs down rows k0 .. k0 + 31, the
 // operand's columns are m0 .. m0 + 15 (as frag_tr_split).
 template <typename T, int COLS>
-__device__ __forceinline__ typename VT<T>::x8 frag_tr_split_w(const T* X, int k0, int m0) {
-  const int l = lane_id(), j = l & 15;
+__device__ __forceinline__ typename VT<T>::x8 frag_tr_split_w(const T* X, int k0, int m0,
+                                                               int l = lane_id()) {
+  const int j = l & 15;
   const int r = k0 + 4 * (l >> 4) + (j >> 2), c = m0 + 4 * (j & 3);
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + sw_off<COLS>(r, c)));
   const i16x4 hi =
@@ -327,9 +329,9 @@ __device__ __forceinline__ f32x4 frag_d4_w(const T* X, int row0, int col0) {
 // Completion is counted by the wave's vector-memory counter: the wave waits
 // for it (s_waitcnt vmcnt) before a barrier hands the tile to other waves.
 template <int COLS>
-__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, int gs, void* lds) {
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, int gs, void* lds,
+                                         int l = lane_id()) {
   constexpr int PR = COLS / 8;  // pieces per row, = instructions per tile
-  const int l = lane_id();
 #pragma unroll
   for (int m = 0; m < PR; ++m) {
     const int s = 64 * m + l, r = s / PR, j = (s % PR) ^ sw_piece<COLS>(s / PR);
