@@ -1356,17 +1356,23 @@ struct GradArgs {
 // share its LDS with another pass's workgroups.
 template <typename T>
 struct GradLds {
-  static constexpr int L7 = 72;   // every 64-wide tile
+  // 64-wide tiles: row stride 72 elements (36 banks) for the tiles read as
+  // row operands as often as transposed, 80 (40 banks) for those read
+  // mostly by the transposing loads (P, V, dO, Delta, dR).  A transposing
+  // load takes 32 bytes of four consecutive rows per 16 lanes; at 40 banks
+  // per row those land on distinct banks (at 36 they overlap two ways).
+  static constexpr int L7 = 72;
+  static constexpr int LT = 80;
   alignas(16) T Qs[QK_TILE];  // q, k, S^T, dSn^T: staggered rows (qk_row)
   alignas(16) T Ks[QK_TILE];
   alignas(16) T As[64 * L7];
-  alignas(16) T Ps[64 * L7];
+  alignas(16) T Ps[64 * LT];
   alignas(16) T Ss[QK_TILE];    // S[:, half]^T ([v][k]); later dq (ld LD)
   alignas(16) T Gs_[QK_TILE];   // dSn[:, half]^T; later dP o Gamma, dM o beta Gamma, dk
-  alignas(16) T Vs[64 * L7];
-  alignas(16) T Os[64 * L7];    // dO[:, half]
-  alignas(16) T Dls[64 * L7];   // Delta, transposed
-  alignas(16) T DRs[64 * L7];   // dR, transposed
+  alignas(16) T Vs[64 * LT];
+  alignas(16) T Os[64 * LT];    // dO[:, half]
+  alignas(16) T Dls[64 * LT];   // Delta, transposed
+  alignas(16) T DRs[64 * LT];   // dR, transposed
   alignas(16) T DVs[64 * L7];   // dv of the half, row-major
   alignas(16) float gam[64];
   alignas(16) float bet[64];
@@ -1432,16 +1438,27 @@ __device__ __forceinline__ GradItem grad_item(const GradArgs& a, int c, int by) 
 
 // The loads of a value half's tiles: S^T, dSn^T (packed, 16 KiB each) and
 // the half's V and dO columns.
+// The state gradient's half (dSn^T, packed): coherent loads (sc1) when the
+// state gradients are written in the same launch.
+template <typename T>
+__device__ __forceinline__ void grad_dsn_load(const GradArgs& a, const GradItem& it, int v0,
+                                              TileRegs<128, 512>& rg) {
+  const int64_t KV = (int64_t)kDim * kDim;
+  const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)it.c * a.Hv + it.h) * KV;
+  if (a.flags) tile_load<T, 128, 512, 16>(rg, hG + v0 * kDim, kDim, 64);
+  else tile_load<T, 128, 512>(rg, hG + v0 * kDim, kDim, 64);
+}
+
+// with_dsn false: every tile of the half but the state gradient's
 template <typename T>
 __device__ __forceinline__ void grad_half_loads(const GradArgs& a, const GradItem& it, int v0,
                                                 TileRegs<128, 512>& rs, TileRegs<128, 512>& rg,
-                                                TileRegs<64, 512>& rv, TileRegs<64, 512>& ro) {
+                                                TileRegs<64, 512>& rv, TileRegs<64, 512>& ro,
+                                                bool with_dsn = true) {
   const int64_t KV = (int64_t)kDim * kDim;
   const T* hS = reinterpret_cast<const T*>(a.h) + ((int64_t)it.c * a.Hv + it.h) * KV;
-  const T* hG = reinterpret_cast<const T*>(a.dh) + ((int64_t)it.c * a.Hv + it.h) * KV;
   tile_load<T, 128, 512>(rs, hS + v0 * kDim, kDim, 64);
-  if (a.flags) tile_load<T, 128, 512, 16>(rg, hG + v0 * kDim, kDim, 64);
-  else tile_load<T, 128, 512>(rg, hG + v0 * kDim, kDim, 64);
+  if (with_dsn) grad_dsn_load<T>(a, it, v0, rg);
   tile_load<T, 64, 512>(rv, reinterpret_cast<const T*>(a.v) + (it.t0 * a.Hv + it.h) * kDim + v0,
                         (int64_t)a.Hv * kDim, it.Cc);
   tile_load<T, 64, 512>(ro, reinterpret_cast<const T*>(a.dO) + (it.t0 * a.Hv + it.h) * kDim + v0,
@@ -1449,10 +1466,10 @@ __device__ __forceinline__ void grad_half_loads(const GradArgs& a, const GradIte
 }
 
 // The first loads of an item: q, k, A, the per-row values (threads 0..63),
-// then value half 0.
+// then value half 0 (with_dsn false: without its state gradient).
 template <typename T>
 __device__ __forceinline__ void grad_first_loads(const GradArgs& a, const GradItem& it,
-                                                 GradFirst<T>& f) {
+                                                 GradFirst<T>& f, bool with_dsn = true) {
   const int tid = threadIdx.x;
   tile_load<T, 128, 512>(f.rq, reinterpret_cast<const T*>(a.q) + (it.t0 * a.Hq + it.hq) * kDim,
                          (int64_t)a.Hq * kDim, it.Cc);
@@ -1469,20 +1486,20 @@ __device__ __forceinline__ void grad_first_loads(const GradArgs& a, const GradIt
       f.x = a.g_dtype == 2 ? reinterpret_cast<const uint32_t*>(a.graw)[row]
                            : (uint32_t)reinterpret_cast<const uint16_t*>(a.graw)[row];
   }
-  grad_half_loads<T>(a, it, 0, f.rs, f.rg, f.rv, f.ro);
+  grad_half_loads<T>(a, it, 0, f.rs, f.rg, f.rv, f.ro, with_dsn);
 }
 
 // One (chunk row c, workgroup row by) of the gradient pass; nbx is the
-// number of chunk rows of the launch (the GVA slots' stride).  f holds the
-// item's first loads (grad_first_loads), issued by the caller.
-template <typename T, bool QKN, bool GVA>
+// number of chunk rows of the launch (the GVA slots' stride).  f receives the
+// item's first loads (grad_first_loads); PRE: the caller has issued them.
+template <typename T, bool QKN, bool GVA, bool PRE = false>
 __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int nbx,
                                           GradLds<T>& L, GradFirst<T>& f) {
   const GradItem item = grad_item<GVA>(a, c, by);
   c = item.c;
   typedef typename VT<T>::x8 x8;
   constexpr int LD = 136;  // row stride of the dq / dk staging in Ss / Gs_
-  constexpr int L7 = GradLds<T>::L7;
+  constexpr int L7 = GradLds<T>::L7, LT = GradLds<T>::LT;
   auto& Qs = L.Qs;
   auto& Ks = L.Ks;
   auto& As = L.As;
@@ -1537,13 +1554,13 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
     for (int i = 0; i < TileRegs<128, 512>::N; ++i) sds += dot8<T>(rs.r[i], rg.r[i]);
     tile_store_packed_q<T, 512>(Ss, rs);
     tile_store_packed_q<T, 512>(Gs_, rg);
-    tile_store<T, 64, 512>(Vs, L7, rv);
-    tile_store<T, 64, 512>(Os, L7, ro);
+    tile_store<T, 64, 512>(Vs, LT, rv);
+    tile_store<T, 64, 512>(Os, LT, ro);
   };
   // q, k, A and the per-row values (gamma, beta, the gate input) are loaded
   // and stored first; value half 0's tiles (S^T, dSn^T, V, dO) are issued
   // next and stored only after the P / N phase, which overlaps their latency
-  grad_first_loads<T>(a, item, f);
+  if (!PRE) grad_first_loads<T>(a, item, f);
   {
     if (QKN) {
       l2norm_rows<T, 512>(f.rq, xinv[0]);
@@ -1598,7 +1615,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
       // only if the compiler branches around the products above (an MFMA
       // does not honour the EXEC mask)
       pn[cb][e] = keep ? acc[e] * __expf(gr[e] - gi) : 0.f;
-      if (!hi) Ps[r * L7 + i] = from_f<T>(pn[cb][e]);
+      if (!hi) Ps[r * LT + i] = from_f<T>(pn[cb][e]);
     }
   }
 
@@ -1653,7 +1670,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
       f32x4 R[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const f32x4 vd = frag_d4(Vs, L7, 16 * tb, cc);
+        const f32x4 vd = frag_d4(Vs, LT, 16 * tb, cc);
         const f32x4 bt = *reinterpret_cast<const f32x4*>(bet + 16 * tb + 4 * grp);
         const f32x4 bx = *reinterpret_cast<const f32x4*>(bex + 16 * tb + 4 * grp);
 #pragma unroll
@@ -1664,7 +1681,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
       for (int tb = 0; tb < 4; ++tb) {
         f32x4 acc = mfma16(frag_row_split(As + 16 * tb * L7, L7), Rb0, zero4());
         if (tb >= 2) acc = mfma16(frag_row_split(As + 16 * tb * L7 + 32, L7), Rb1, acc);
-        store_d4_t<T>(Dls, L7, 16 * tb, cc, acc);
+        store_d4_t<T>(Dls, LT, 16 * tb, cc, acc);
       }
     } else {
       // dDelta = diag(e^{gL-gamma}) K dSn + scale P^T dO ; dR = A^T dDelta
@@ -1684,8 +1701,8 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
         f32x4 pt = zero4();
 #pragma unroll
         for (int kt = tb / 2; kt < 2; ++kt)
-          pt = mfma16(frag_tr_split(Ps + 32 * kt * L7 + 16 * tb, L7),
-                      frag_tr_split(Os + 32 * kt * L7 + cc, L7), pt);
+          pt = mfma16(frag_tr_split(Ps + 32 * kt * LT + 16 * tb, LT),
+                      frag_tr_split(Os + 32 * kt * LT + cc, LT), pt);
         const f32x4 dlr = *reinterpret_cast<const f32x4*>(dl + 16 * tb + 4 * grp);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dD[tb][e] = dlr[e] * kg[tb][e] + a.scale * pt[e];
@@ -1696,7 +1713,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
         f32x4 dR = mfma16(frag_tr_split(As + 32 * L7 + 16 * tb, L7), Db1, zero4());
         if (tb < 2) dR = mfma16(frag_tr_split(As + 16 * tb, L7), Db0, dR);
         // the v . dR part of dbeta, and dv = diag(beta) dR
-        const f32x4 vd = frag_d4(Vs, L7, 16 * tb, cc);
+        const f32x4 vd = frag_d4(Vs, LT, 16 * tb, cc);
         const f32x4 bt = *reinterpret_cast<const f32x4*>(bet + 16 * tb + 4 * grp);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1705,7 +1722,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
           if (col == 0) dbv[4 * hv + wr][r] = pdot;
           DVs[r * L7 + cc + col] = from_f<T>(bt[e] * dR[e]);
         }
-        store_d4_t<T>(DRs, L7, 16 * tb, cc, dR);
+        store_d4_t<T>(DRs, LT, 16 * tb, cc, dR);
       }
     }
     __syncthreads();
@@ -1716,13 +1733,13 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
 #pragma unroll
     for (int vk = 0; vk < 2; ++vk) {
       if (!hi) {
-        const x8 fdo = frag_row_split(Os + 16 * wr * L7 + 32 * vk, L7);
+        const x8 fdo = frag_row_split(Os + 16 * wr * LT + 32 * vk, LT);
         // all four column blocks: the blocks above the diagonal are masked
         // by selects later (an MFMA alone under a per-wave condition would
         // run regardless of EXEC, on operands never loaded)
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
-          accB[ib] = mfma16(fdo, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), accB[ib]);
+          accB[ib] = mfma16(fdo, frag_tr_split(Dls + 32 * vk * LT + 16 * ib, LT), accB[ib]);
         // two rounds of four key blocks, fragments read before the products
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
@@ -1735,12 +1752,12 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        const x8 fdr = frag_tr_split(DRs + 32 * vk * L7 + 16 * wr, L7);
-        const x8 fdl = frag_tr_split(Dls + 32 * vk * L7 + 16 * wr, L7);
+        const x8 fdr = frag_tr_split(DRs + 32 * vk * LT + 16 * wr, LT);
+        const x8 fdl = frag_tr_split(Dls + 32 * vk * LT + 16 * wr, LT);
         // dR Delta^T, all four column blocks (masked by selects later)
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
-          accM[ib] = mfma16(fdr, frag_tr_split(Dls + 32 * vk * L7 + 16 * ib, L7), accM[ib]);
+          accM[ib] = mfma16(fdr, frag_tr_split(Dls + 32 * vk * LT + 16 * ib, LT), accM[ib]);
         // four rounds of two key blocks, each round's fragments read before
         // its four independent products issue
 #pragma unroll
@@ -2083,6 +2100,11 @@ __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, in
   }
   const int g = (int)blockIdx.x - nb2, units = ga.N * ga.Hv, nch = ga.nc_dense;
   const int j = nch - 1 - g / units, u = g % units, n = u / ga.Hv, h = u % ga.Hv;
+  // every tile but the state gradient is an input of the launch: the loads
+  // are issued before the wait, so their latency overlaps it
+  GradFirst<T> f;
+  const GradItem item = grad_item<false>(ga, n * nch + j, h);
+  grad_first_loads<T>(ga, item, f, false);
   if (threadIdx.x == 0) {
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ga.flags, (int64_t)units * 4);
     const unsigned need = (unsigned)(nch - j);
@@ -2091,9 +2113,15 @@ __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, in
       __builtin_amdgcn_s_sleep(8);
     }
   }
-  __syncthreads();
-  GradFirst<T> f;
-  grad_body<T, false, false>(ga, n * nch + j, h, ga.N * nch, *reinterpret_cast<GradLds<T>*>(lds), f);
+  // the workgroup barrier without __syncthreads' fence, which would wait for
+  // the loads just issued; the acquire fence keeps the state gradient's loads
+  // below it
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  grad_dsn_load<T>(ga, item, 0, f.rg);
+  grad_body<T, false, false, true>(ga, n * nch + j, h, ga.N * nch,
+                                   *reinterpret_cast<GradLds<T>*>(lds), f);
 }
 
 static __global__ void zero_u32_kernel(unsigned* p, int n) {
