@@ -768,7 +768,10 @@ struct DhLdLds : DhLdHx<T, NB == 1> {
   alignas(16) float dl[2][64];
 };
 
-template <typename T, int OPT, int NB = 1>
+// INST only separates the instantiations of the kernels that run the body
+// (each then has one caller: with two, the compiler's inlining order changes
+// and the kernel spilled 11 more registers, 7 us at B=2 T=4096 H=32)
+template <typename T, int OPT, int NB = 1, int INST = 0>
 __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdLds<T, NB>& L) {
   typedef typename VT<T>::x8 x8;
   static_assert((OPT & 1) == 0, "q / k normalisation runs in dh_lh_body");
@@ -2083,27 +2086,43 @@ __global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, i
 // data: blocks [0, nb2) run the state-gradient scan over every chunk
 // (loader-wave form, one 128-column workgroup per unit), the rest are the
 // gradient workgroups, the last chunk's first (row g: chunk nch - 1 - g /
-// units of unit g % units).  Blocks are dispatched in order, so the scan's
-// workgroups are resident before any gradient workgroup waits for them; a
-// gradient workgroup waits (bounded) until its unit's count covers its
-// chunk's state gradient, then runs on whatever CU it was given: the chip's
-// idle CUs during the scan, every CU after it.
+// rows of workgroup row g % rows, rows per chunk; with GVA the rows of value
+// heads 0 .. G-2 of every group, whose group sums the gradient kernel
+// completes in a launch of its own).  Blocks are dispatched in order, so the
+// scan's workgroups are resident before any gradient workgroup waits for
+// them; a gradient workgroup waits (bounded) until its unit's count covers
+// its chunk's state gradient, then runs on whatever CU it was given: the
+// chip's idle CUs during the scan, every CU after it.
 constexpr int kDynSpinLimit = 1 << 20;  // about 0.25 s of s_sleep: never reached in a healthy run
-template <typename T, int OPT>
+template <typename T, int OPT, bool GVA>
 __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, int nb2) {
   static_assert((OPT & 1) == 0, "q / k normalisation runs the sliced pipeline");
   constexpr size_t B = sizeof(DhLdLds<T, 2>), G = sizeof(GradLds<T>);
   __shared__ __align__(16) char lds[B > G ? B : G];
   if ((int)blockIdx.x < nb2) {
-    dh_ld_body<T, OPT, 2>(da, (int)blockIdx.x, nb2, *reinterpret_cast<DhLdLds<T, 2>*>(lds));
+    dh_ld_body<T, OPT, 2, GVA ? 1 : 0>(da, (int)blockIdx.x, nb2,
+                                      *reinterpret_cast<DhLdLds<T, 2>*>(lds));
     return;
   }
   const int g = (int)blockIdx.x - nb2, units = ga.N * ga.Hv, nch = ga.nc_dense;
-  const int j = nch - 1 - g / units, u = g % units, n = u / ga.Hv, h = u % ga.Hv;
+  int j, n, by, u;
+  if constexpr (GVA) {
+    const int gs = ga.Hv / ga.Hq, hrow = ga.Hq * (gs - 1);  // workgroup rows per (sequence, chunk)
+    const int rows = ga.N * hrow, x = g % rows;
+    j = nch - 1 - g / rows;
+    n = x / hrow;
+    by = x % hrow;
+    u = n * ga.Hv + (by / (gs - 1)) * gs + by % (gs - 1);
+  } else {
+    j = nch - 1 - g / units;
+    u = g % units;
+    n = u / ga.Hv;
+    by = u % ga.Hv;
+  }
   // every tile but the state gradient is an input of the launch: the loads
   // are issued before the wait, so their latency overlaps it
   GradFirst<T> f;
-  const GradItem item = grad_item<false>(ga, n * nch + j, h);
+  const GradItem item = grad_item<GVA>(ga, n * nch + j, by);
   grad_first_loads<T>(ga, item, f, false);
   if (threadIdx.x == 0) {
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ga.flags, (int64_t)units * 4);
@@ -2120,8 +2139,8 @@ __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, in
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   grad_dsn_load<T>(ga, item, 0, f.rg);
-  grad_body<T, false, false, true>(ga, n * nch + j, h, ga.N * nch,
-                                   *reinterpret_cast<GradLds<T>*>(lds), f);
+  grad_body<T, false, GVA, true>(ga, n * nch + j, by, ga.N * nch,
+                                 *reinterpret_cast<GradLds<T>*>(lds), f);
 }
 
 static __global__ void zero_u32_kernel(unsigned* p, int n) {
@@ -2161,17 +2180,20 @@ __global__ __launch_bounds__(256) void gate_param_grad_kernel(const float* gpart
 // host side
 // ---------------------------------------------------------------------------
 // Slices of the pipelined backward (bwd_pipe_kernel), 0 when it does not
-// apply: the forward's states given, a dense batch, no grouped heads, no
-// split along T, the one-tile scan, at least 16 chunks per sequence, and few
-// enough (sequence, head) units that the scan leaves at least half the CUs
-// idle (its 64-column workgroups are then at most 128).
+// apply: the forward's states given, a dense batch, no split along T, the
+// one-tile scan, at least 16 chunks per sequence, and few enough (sequence,
+// head) units that the scan leaves at least half the CUs idle: at most 128
+// units for the data-scheduled launch (one 128-column workgroup each), at
+// most 64 and no grouped heads for the slices (two 64-column workgroups
+// each).
 // 0: no pipeline; 1: one launch scheduled by data (bwd_dyn_kernel); S >= 2:
 // S slices (q / k normalised in the kernel, whose scan form has no progress
 // counts).
 static int pipe_slices(const gdr_problem* p, const Plan& pl, bool states_given) {
-  if (!states_given || p->cu_seqlens_dev || p->Hq != p->Hv || pl.cp != 1 || pl.vb != 1) return 0;
-  if (pl.nc_dense < 16 || (int64_t)pl.N * p->Hv * 2 > 128) return 0;
+  if (!states_given || p->cu_seqlens_dev || pl.cp != 1 || pl.vb != 1) return 0;
+  if (pl.nc_dense < 16 || (int64_t)pl.N * p->Hv > 128) return 0;
   if (!p->use_qk_l2norm) return 1;
+  if (p->Hq != p->Hv || (int64_t)pl.N * p->Hv * 2 > 128) return 0;
   return 2;  // measured at B=2 T=4096 H=32: 2 slices 449 us, 3 slices 455, 4 slices 498,
              // one pass 489
 }
@@ -2419,11 +2441,20 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
     d.flags = flags;
     GradArgs g2 = ga;
     g2.flags = flags;
-    const unsigned blocks = (unsigned)(nb2 + units * pl.nc_dense);
-    if (sa.beta_mode)
-      GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 2>), dim3(blocks), dim3(512), st, d, g2, nb2);
-    else
-      GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 0>), dim3(blocks), dim3(512), st, d, g2, nb2);
+    // with GVA the launch takes value heads 0 .. G-2 of every group; the
+    // gradient kernel then runs the group's last head, which sums dq and dk
+    const int rows = gva ? pl.N * p->Hq * (G - 1) : units;
+    const unsigned blocks = (unsigned)(nb2 + rows * pl.nc_dense);
+    switch ((sa.beta_mode ? 2 : 0) | (gva ? 1 : 0)) {
+      case 0: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 0, false>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
+      case 1: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 0, true>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
+      case 2: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 2, false>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
+      default: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 2, true>), dim3(blocks), dim3(512), st, d, g2, nb2);
+    }
+    if (gva) {
+      ga.gva_final = 1;
+      launch_grad<T, true>(ga, (int)nc, p->Hq, st);
+    }
   } else if (S > 0) {
     // launch k runs scan slice S-1-k (while k < S) and the gradient
     // workgroups of slice S-k (once k > 0)

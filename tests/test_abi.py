@@ -186,11 +186,19 @@ def test_backward_pipeline_plan():
     # gradients cover 48 of the 64 chunks, 3072 workgroups, twelve whole
     # rounds of the 256 CUs
     assert info(good(B=2, N=2, T=4096, Hq=32, Hv=32, use_qk_l2norm=1)) == (2, [0, 48, 64])
-    # one pass: grouped heads, packed sequences, a scan that fills the chip,
-    # short sequences, a split along T
-    assert info(good(B=2, N=2, T=4096, Hq=16, Hv=32))[0] == 0
+    # grouped heads and up to 128 units (the scan on at most half the CUs)
+    # keep the data-scheduled launch
+    assert info(good(B=2, N=2, T=4096, Hq=16, Hv=32)) == (1, [0, 64])
+    assert info(good(B=4, N=4, T=8192, Hq=16, Hv=32)) == (1, [0, 128])
+    assert info(good(B=4, N=4, T=4096, Hq=32, Hv=32)) == (1, [0, 64])
+    # the slices keep two 64-column scan workgroups per unit: no grouped
+    # heads, at most 64 units
+    assert info(good(B=2, N=2, T=4096, Hq=16, Hv=32, use_qk_l2norm=1))[0] == 0
+    assert info(good(B=4, N=4, T=4096, Hq=32, Hv=32, use_qk_l2norm=1))[0] == 0
+    # one pass: packed sequences, a scan that fills the chip, short
+    # sequences, a split along T
     assert info(varlen(HOST_CU, T=200))[0] == 0
-    assert info(good(B=4, N=4, T=4096, Hq=32, Hv=32))[0] == 0
+    assert info(good(B=8, N=8, T=4096, Hq=32, Hv=32))[0] == 0
     assert info(good(B=2, N=2, T=512, Hq=32, Hv=32))[0] == 0
     assert info(good(B=1, N=1, T=65536, Hq=32, Hv=32))[0] == 0
     # fewer units leave more CUs idle beside the scan, which then hide the

@@ -59,11 +59,15 @@ CASES = {
                           lens=[70, 0, 65]),
     "one_token": P("one", B=1, T=1, Hq=1, Hv=1, init_state=True, dht=True),
     "long_slow_decay": P("long", B=1, T=1500, Hq=2, Hv=2, init_state=True, dht=True, g_shift=2.0),
-    # dense, few heads, 16+ chunks: the states-path backward runs pipelined
-    # (the scan in slices, the gradient workgroups of a slice beside the
-    # next slice's scan); ragged last chunk
+    # dense, few heads, 16+ chunks: the states-path backward runs in one
+    # launch scheduled by data (the gradient workgroups of a chunk start once
+    # the scan has stored its state gradient; with q / k normalised, in
+    # slices); ragged last chunk
     "pipe": P("pipe", B=2, T=1100, Hq=2, Hv=2, init_state=True, dht=True),
     "pipe_no_state": P("pipe0", B=1, T=1030, Hq=3, Hv=3),
+    # the same launch with grouped heads (groups of three value heads): it
+    # runs heads 0 .. G-2 of every group, the gradient kernel the last
+    "pipe_gva": P("pipe_gva", B=2, T=1030, Hq=2, Hv=6, init_state=True, dht=True),
     # (sequence, head) units a multiple of 8: rank-ordered scan blocks
     "varlen_ranked": P("varlen_ranked", B=1, T=0, Hq=2, Hv=2, init_state=True, dht=True,
                        lens=[300, 1000, 64, 700]),
@@ -167,6 +171,7 @@ def gpu_fwd_bwd_states(d, cp=0, use_trans=True, vt=0):
     ("long_slow_decay", 4, False, 1), ("varlen", 3, True, 0), ("varlen", 3, False, 0),
     ("dense_state_dht", 2, True, 2), ("fp16_gva", 3, True, 1), ("gva_group4", 2, True, 0),
     ("varlen_empty_seq", 2, True, 0), ("pipe", 1, True, 1), ("pipe_no_state", 1, True, 1),
+    ("pipe_gva", 1, True, 1),
     ("varlen_ranked", 1, True, 0), ("varlen_ranked", 3, True, 1)])
 def test_backward_from_the_forward_states(name, cp, use_trans, vt):
     d = gdr_synth.make(CASES[name])
