@@ -398,12 +398,21 @@ def kernel_direction(name):
     return "bwd" if name in BWD_KERNELS else "fwd"
 
 
-def measure_case(gdr, torch, timer, case, direction, steps, warmup, n_cold):
-    """Times one workload; returns the configs-block record."""
+def measure_case(gdr, torch, timer, case, direction, steps, warmup, n_cold, warm_ms=50.0):
+    """Times one workload; returns the configs-block record.  The warm-up
+    runs at least `warmup` times and at least `warm_ms` of wall time: after
+    the host has prepared a workload the GPU has idled, and its first
+    milliseconds of work run slower."""
     fwd_flop, fwd_bytes = case.alg("fwd")
     bwd_flop, bwd_bytes = case.alg("bwd")
-    for _ in range(warmup):
-        case.step() if direction == "fwd+bwd" else case.fwd()
+    fn = case.step if direction == "fwd+bwd" else case.fwd
+    t0, n = time.perf_counter(), 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     rec = {"direction": direction, "tokens": case.tokens,
            "plan": {k: {"cp_segments": v[0], "wave_tiles": v[1]} for k, v in case.plans.items()}}
     fwd_ms = timer.mean_ms(case.fwd, steps)
