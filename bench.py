@@ -97,11 +97,12 @@ def fractions(t_s, flop, nbytes):
 
 
 WORKLOADS = {
-    # name: (B, T, Hq, Hv, dtype, g_shift, varlen)
-    "fwd_bwd_B2_T4096_H32_bf16": (2, 4096, 32, 32, "bf16", 0.0, None),
-    "fwd_bwd_varlen8_H32_bf16": (1, 0, 32, 32, "bf16", 0.0, (8, 128, 4096)),
-    "fwd_bwd_B4_T8192_Hq16_Hv32_fp16": (4, 8192, 16, 32, "fp16", 0.0, None),
-    "fwd_bwd_B1_T65536_H32_bf16": (1, 65536, 32, 32, "bf16", 2.0, None),
+    # name: (B, T, Hq, Hv, dtype, g_shift, varlen, initial state, dht), the
+    # states as in the configs block
+    "fwd_bwd_B2_T4096_H32_bf16": (2, 4096, 32, 32, "bf16", 0.0, None, True, True),
+    "fwd_bwd_varlen8_H32_bf16": (1, 0, 32, 32, "bf16", 0.0, (8, 128, 4096), True, True),
+    "fwd_bwd_B4_T8192_Hq16_Hv32_fp16": (4, 8192, 16, 32, "fp16", 0.0, None, False, False),
+    "fwd_bwd_B1_T65536_H32_bf16": (1, 65536, 32, 32, "bf16", 2.0, None, True, True),
 }
 DEFAULT = "fwd_bwd_B2_T4096_H32_bf16"
 # token-by-token forward: (B sequences, Hv = Hq heads, tokens per step, dtype)
@@ -479,9 +480,9 @@ def main():
 
     if args.workload in DECODE_WORKLOADS:
         return bench_decode(args)
-    B, T, Hq, Hv, dt, g_shift, varlen = WORKLOADS[args.workload]
+    B, T, Hq, Hv, dt, g_shift, varlen, w_h0, w_dht = WORKLOADS[args.workload]
     qkn = args.qk_l2norm
-    case = Case(gdr, torch, gdr_synth, B, T, Hq, Hv, dt, g_shift, varlen, True, True, False,
+    case = Case(gdr, torch, gdr_synth, B, T, Hq, Hv, dt, g_shift, varlen, w_h0, w_dht, False,
                 cp=args.cp, vt=args.vt, qk_norm=qkn, gate=args.gate, name=args.workload,
                 recompute=args.recompute_states)
     B, T = case.B, case.T
@@ -588,7 +589,7 @@ def main():
             "raw N(0,1) q,k normalised in-kernel" if qkn else "q,k L2-normalised",
             "g = raw gate input N(0,1), activated in-kernel" if args.gate else "g=logsigmoid"),
         "config": {"workload": args.workload, "B": B, "T": T, "Hq": Hq, "Hv": Hv, "K": 128,
-                   "V": 128, "chunk": 64, "tokens": tokens, "initial_state": True, "dht": True,
+                   "V": 128, "chunk": 64, "tokens": tokens, "initial_state": w_h0, "dht": w_dht,
                    "cp_segments": {k_: v_[0] for k_, v_ in case.plans.items()},
                    "wave_tiles": {k_: v_[1] for k_, v_ in case.plans.items()},
                    "qk_l2norm_in_kernel": qkn, "gate_in_kernel": bool(args.gate),
