@@ -4,6 +4,7 @@
 // be exercised on a machine without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -413,7 +414,13 @@ gdr_status gdr_check_device(void) { return check_device_cached(); }
 
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
   if (validate(p, nullptr, 0) != GDR_OK) return 0;
-  return fwd_workspace_bytes(p, make_plan(p, false));
+  size_t b = fwd_workspace_bytes(p, make_plan(p, false));
+  if (p->use_qk_l2norm && p->h_packed) {  // the states path runs without the option
+    gdr_problem pn = *p;
+    pn.use_qk_l2norm = 0;
+    b = std::max(b, fwd_workspace_bytes(&pn, make_plan(&pn, false)));
+  }
+  return b;
 }
 
 size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p) {
@@ -421,9 +428,53 @@ size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p) {
   return bwd_workspace_bytes(p, make_plan(p, true), false);
 }
 
+// The states path with q / k normalised in the kernel normalises the rows
+// once, in the forward, and runs the rest as a problem without the option
+// (the forward's scans and the backward's launches then take their
+// loader-wave and data-scheduled forms); the rows and their norms are kept
+// after the segment transitions in the caller's trans buffer.
+static gdr_problem without_qk_norm(const gdr_problem* p) {
+  gdr_problem pn = *p;
+  pn.use_qk_l2norm = 0;
+  return pn;
+}
+
+// Byte offsets in the trans buffer: the segment transitions, then (q / k
+// normalised) the unit q and k rows and their fp32 1 / |x|.
+struct TransLayout {
+  size_t qn, kn, qinv, kinv, total;
+};
+
+static TransLayout trans_layout(const gdr_problem* p) {
+  TransLayout t{0, 0, 0, 0, 0};
+  if (!p->h_packed) return t;
+  const gdr_problem pn = without_qk_norm(p);
+  const Plan pl = make_plan(&pn, false);
+  size_t o = pl.cp > 1 ? (size_t)pl.N * p->Hv * pl.cp * kDim * kDim * sizeof(float) : 0;
+  if (p->use_qk_l2norm) {
+    const size_t rows = (size_t)p->B * p->T * p->Hq;
+    o = align256(o);
+    t.qn = o;
+    o += align256(rows * kDim * 2);
+    t.kn = o;
+    o += align256(rows * kDim * 2);
+    t.qinv = o;
+    o += align256(rows * sizeof(float));
+    t.kinv = o;
+    o += rows * sizeof(float);
+  }
+  t.total = o;
+  return t;
+}
+
 size_t gdr_chunk_bwd_states_workspace_size(const gdr_problem* p) {
   if (validate(p, nullptr, 0) != GDR_OK) return 0;
-  return bwd_workspace_bytes(p, make_plan(p, true, true), true);
+  size_t b = bwd_workspace_bytes(p, make_plan(p, true, true), true);
+  if (p->use_qk_l2norm) {  // with the forward's unit rows, or without them
+    const gdr_problem pn = without_qk_norm(p);
+    b = std::max(b, bwd_workspace_bytes(&pn, make_plan(&pn, true, true), true));
+  }
+  return b;
 }
 
 static gdr_status chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -456,9 +507,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
 
 size_t gdr_chunk_trans_size(const gdr_problem* p) {
   if (validate(p, nullptr, 0) != GDR_OK || !p->h_packed) return 0;
-  const Plan pl = make_plan(p, false);
-  if (pl.cp <= 1) return 0;
-  return (size_t)pl.N * p->Hv * pl.cp * kDim * kDim * sizeof(float);
+  return trans_layout(p).total;
 }
 
 gdr_status gdr_chunk_fwd_states(const gdr_problem* p, const void* q, const void* k,
@@ -474,12 +523,27 @@ gdr_status gdr_chunk_fwd_states(const gdr_problem* p, const void* q, const void*
   const size_t tneed = gdr_chunk_trans_size(p);
   if (!trans && tneed > 0)
     return fail(GDR_ERR_NULL, nullptr, 0,
-                "the plan splits sequences: trans needs gdr_chunk_trans_size bytes");
+                "the plan splits sequences or q / k are normalised in the kernel: trans needs "
+                "gdr_chunk_trans_size bytes");
   if (trans && trans_bytes < tneed)
     return fail(GDR_ERR_WORKSPACE, nullptr, 0, "trans needs %zu bytes, got %zu", tneed,
                 trans_bytes);
-  return chunk_fwd(p, q, k, v, g, beta, initial_state, g_cum, A, o, h, trans, final_state,
-                   workspace, workspace_bytes, stream);
+  if (!p->use_qk_l2norm)
+    return chunk_fwd(p, q, k, v, g, beta, initial_state, g_cum, A, o, h, trans, final_state,
+                     workspace, workspace_bytes, stream);
+  // normalise the rows once, keep them, and run the rest without the option
+  if (!q || !k) return fail(GDR_ERR_NULL, nullptr, 0, "a required forward pointer is NULL");
+  const gdr_status sd = check_device_cached();
+  if (sd != GDR_OK) return sd;
+  const TransLayout t = trans_layout(p);
+  char* tb = reinterpret_cast<char*>(trans);
+  const gdr_status sn = launch_qk_norm(p, q, k, tb + t.qn, tb + t.kn,
+                                       reinterpret_cast<float*>(tb + t.qinv),
+                                       reinterpret_cast<float*>(tb + t.kinv), (hipStream_t)stream);
+  if (sn != GDR_OK) return sn;
+  const gdr_problem pn = without_qk_norm(p);
+  return chunk_fwd(&pn, tb + t.qn, tb + t.kn, v, g, beta, initial_state, g_cum, A, o, h, trans,
+                   final_state, workspace, workspace_bytes, stream);
 }
 
 static_assert(GDR_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "header and library agree");
@@ -514,7 +578,8 @@ static gdr_status chunk_bwd(const gdr_problem* p, const void* q, const void* k, 
                             const void* hstates, const float* trans, void* dq, void* dk,
                             void* dv, void* dbeta, void* dg, float* dh0, float* dA_log,
                             float* ddt_bias, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            void* stream, const float* qinv = nullptr,
+                            const float* kinv = nullptr) {
   if (!q || !k || !v || !g_cum || !beta || !A || !do_ || !dq || !dk || !dv || !dbeta || !dg)
     return fail(GDR_ERR_NULL, nullptr, 0, "a required backward pointer is NULL");
   if (initial_state && !dh0)
@@ -529,7 +594,7 @@ static gdr_status chunk_bwd(const gdr_problem* p, const void* q, const void* k, 
   return launch_bwd(p, pl, q, k, v, g_cum, graw, beta, A, do_, dht, initial_state, hstates,
                     pl.cp > 1 ? trans : nullptr, dq, dk, dv, dbeta, dg,
                     initial_state ? dh0 : nullptr, dA_log, ddt_bias, workspace,
-                    (hipStream_t)stream);
+                    (hipStream_t)stream, qinv, kinv);
 }
 
 gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -572,10 +637,10 @@ gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void*
                                 void* stream) {
   gdr_status s = validate(p, nullptr, 0);
   if (s != GDR_OK) return s;
+  gdr_problem pk = *p;
+  pk.h_packed = 1;
   if (trans) {
     // the transitions of the states path's plan, which the backward shares
-    gdr_problem pk = *p;
-    pk.h_packed = 1;
     const size_t tneed = gdr_chunk_trans_size(&pk);
     if (trans_bytes < tneed)
       return fail(GDR_ERR_WORKSPACE, nullptr, 0, "trans needs %zu bytes, got %zu", tneed,
@@ -585,6 +650,18 @@ gdr_status gdr_chunk_bwd_states(const gdr_problem* p, const void* q, const void*
   if (p->use_gate && !g) return fail(GDR_ERR_NULL, nullptr, 0, "the gate input g is NULL");
   if (!p->use_gate && (g || dA_log || ddt_bias))
     return fail(GDR_ERR_ARG, nullptr, 0, "g, dA_log and ddt_bias are for use_gate problems only");
+  if (p->use_qk_l2norm && trans) {
+    // the forward's unit rows: the backward runs without the option and maps
+    // dq, dk back through the normalisation
+    const TransLayout t = trans_layout(&pk);
+    const char* tb = reinterpret_cast<const char*>(trans);
+    const gdr_problem pn = without_qk_norm(p);
+    return chunk_bwd(&pn, tb + t.qn, tb + t.kn, v, g_cum, p->use_gate ? g : nullptr, beta, A,
+                     do_, dht, initial_state, h, trans, dq, dk, dv, dbeta, dg, dh0, dA_log,
+                     ddt_bias, workspace, workspace_bytes, stream,
+                     reinterpret_cast<const float*>(tb + t.qinv),
+                     reinterpret_cast<const float*>(tb + t.kinv));
+  }
   return chunk_bwd(p, q, k, v, g_cum, p->use_gate ? g : nullptr, beta, A, do_, dht,
                    initial_state, h, trans, dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias,
                    workspace, workspace_bytes, stream);

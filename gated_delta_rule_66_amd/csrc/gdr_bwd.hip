@@ -60,6 +60,10 @@ struct DhArgs {
   float scale;
   int svf;
   int qk_norm;    // q, k rows scaled to unit length before use
+  // (qk_norm) the rows were normalised beforehand: q and k hold the unit
+  // rows, and these their 1 / |x| per (token, q head) row; else null
+  const float* qinv;
+  const float* kinv;
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
   int v_only;     // pass 1 runs the value columns only: the transitions are
                   // the forward's, kept (ScanArgs::trans)
@@ -1331,6 +1335,10 @@ struct GradArgs {
   // chunk sl_c0 + x % sl_len of sequence x / sl_len
   int sl_c0, sl_len;
   int qk_norm;    // q, k rows scaled to unit length before use
+  // (qk_norm) the rows were normalised beforehand: q and k hold the unit
+  // rows, and these their 1 / |x| per (token, q head) row; else null
+  const float* qinv;
+  const float* kinv;
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
   // the gate (use_gate): g is the gate input graw, dg is with respect to it,
   // and each workgroup leaves its chunk's shares of the parameter gradients
@@ -1566,8 +1574,16 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, int c, int by, int 
   if (!PRE) grad_first_loads<T>(a, item, f);
   {
     if (QKN) {
-      l2norm_rows<T, 512>(f.rq, xinv[0]);
-      l2norm_rows<T, 512>(f.rk, xinv[1]);
+      if (a.qinv) {  // unit rows given: their 1 / |x|
+        if (tid < 64) {
+          const int64_t row = (t0 + min(tid, Cc - 1)) * a.Hq + hq;
+          xinv[0][tid] = a.qinv[row];
+          xinv[1][tid] = a.kinv[row];
+        }
+      } else {
+        l2norm_rows<T, 512>(f.rq, xinv[0]);
+        l2norm_rows<T, 512>(f.rk, xinv[1]);
+      }
     }
     tile_store_q<T, 512>(Qs, f.rq);
     tile_store_q<T, 512>(Ks, f.rk);
@@ -2094,14 +2110,16 @@ __global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, i
 // its chunk's state gradient, then runs on whatever CU it was given: the
 // chip's idle CUs during the scan, every CU after it.
 constexpr int kDynSpinLimit = 1 << 20;  // about 0.25 s of s_sleep: never reached in a healthy run
+// OPT bit 0: q and k hold rows normalised beforehand (GradArgs::qinv), which
+// the scan reads as they are and the gradient workgroups map dq, dk back
+// through; bit 1: the beta options.
 template <typename T, int OPT, bool GVA>
 __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, int nb2) {
-  static_assert((OPT & 1) == 0, "q / k normalisation runs the sliced pipeline");
   constexpr size_t B = sizeof(DhLdLds<T, 2>), G = sizeof(GradLds<T>);
   __shared__ __align__(16) char lds[B > G ? B : G];
   if ((int)blockIdx.x < nb2) {
-    dh_ld_body<T, OPT, 2, GVA ? 1 : 0>(da, (int)blockIdx.x, nb2,
-                                      *reinterpret_cast<DhLdLds<T, 2>*>(lds));
+    dh_ld_body<T, OPT & 2, 2, (GVA ? 1 : 0) | (OPT & 1 ? 2 : 0)>(
+        da, (int)blockIdx.x, nb2, *reinterpret_cast<DhLdLds<T, 2>*>(lds));
     return;
   }
   const int g = (int)blockIdx.x - nb2, units = ga.N * ga.Hv, nch = ga.nc_dense;
@@ -2139,8 +2157,8 @@ __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, in
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   grad_dsn_load<T>(ga, item, 0, f.rg);
-  grad_body<T, false, GVA, true>(ga, n * nch + j, by, ga.N * nch,
-                                 *reinterpret_cast<GradLds<T>*>(lds), f);
+  grad_body<T, (OPT & 1) != 0, GVA, true>(ga, n * nch + j, by, ga.N * nch,
+                                          *reinterpret_cast<GradLds<T>*>(lds), f);
 }
 
 static __global__ void zero_u32_kernel(unsigned* p, int n) {
@@ -2349,7 +2367,8 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
                                const void* beta, const void* A, const void* dO, const float* dht,
                                const float* h0, const void* hstates, const float* trans,
                                void* dq, void* dk, void* dv, void* dbeta, void* dg, float* dh0,
-                               float* dA_log, float* ddt_bias, char* ws, hipStream_t st) {
+                               float* dA_log, float* ddt_bias, char* ws, hipStream_t st,
+                               const float* qinv, const float* kinv) {
   const bool states_given = hstates != nullptr;
   const BwdLayout L = bwd_layout(p, pl, states_given);
   const int32_t* offs = nullptr;
@@ -2415,7 +2434,9 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
   ga.cu = p->cu_seqlens_dev; ga.offs = offs;
   ga.N = pl.N; ga.T = p->T; ga.Hq = p->Hq; ga.Hv = p->Hv; ga.nc_dense = pl.nc_dense;
   ga.g_dtype = (int)p->g_dtype; ga.scale = p->scale;
-  ga.qk_norm = sa.qk_norm;
+  ga.qk_norm = sa.qk_norm || qinv ? 1 : 0;  // unit rows given: the map of dq, dk only
+  ga.qinv = qinv;
+  ga.kinv = kinv;
   ga.beta_mode = sa.beta_mode;
   const bool gate = p->use_gate != 0;
   ga.graw = gate ? graw : nullptr;
@@ -2445,11 +2466,15 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
     // gradient kernel then runs the group's last head, which sums dq and dk
     const int rows = gva ? pl.N * p->Hq * (G - 1) : units;
     const unsigned blocks = (unsigned)(nb2 + rows * pl.nc_dense);
-    switch ((sa.beta_mode ? 2 : 0) | (gva ? 1 : 0)) {
+    switch ((qinv ? 4 : 0) | (sa.beta_mode ? 2 : 0) | (gva ? 1 : 0)) {
       case 0: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 0, false>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
       case 1: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 0, true>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
       case 2: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 2, false>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
-      default: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 2, true>), dim3(blocks), dim3(512), st, d, g2, nb2);
+      case 3: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 2, true>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
+      case 4: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 1, false>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
+      case 5: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 1, true>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
+      case 6: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 3, false>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
+      default: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 3, true>), dim3(blocks), dim3(512), st, d, g2, nb2);
     }
     if (gva) {
       ga.gva_final = 1;
@@ -2517,17 +2542,21 @@ gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const
                       const void* A, const void* dO, const float* dht, const float* h0,
                       const void* hstates, const float* trans, void* dq, void* dk, void* dv,
                       void* dbeta, void* dg, float* dh0, float* dA_log, float* ddt_bias, void* ws,
-                      hipStream_t st) {
+                      hipStream_t st, const float* qinv, const float* kinv) {
   char* w = reinterpret_cast<char*>(ws);
   if (trans && !hstates) {
     set_error("segment transitions come with the forward's states");
     return GDR_ERR_ARG;
   }
+  if ((qinv != nullptr) != (kinv != nullptr) || (qinv && p->use_qk_l2norm)) {
+    set_error("normalised rows come with both norms, on a problem that does not normalise");
+    return GDR_ERR_ARG;
+  }
   if (p->in_dtype == GDR_BF16)
     return launch_bwd_t<__bf16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, hstates, trans,
-                                dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st);
+                                dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st, qinv, kinv);
   return launch_bwd_t<_Float16>(p, pl, q, k, v, gcum, graw, beta, A, dO, dht, h0, hstates, trans,
-                                dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st);
+                                dq, dk, dv, dbeta, dg, dh0, dA_log, ddt_bias, w, st, qinv, kinv);
 }
 
 }  // namespace gdr

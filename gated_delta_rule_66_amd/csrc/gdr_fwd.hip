@@ -259,6 +259,64 @@ size_t fwd_workspace_bytes(const gdr_problem* p, const Plan& pl) {
   return b;
 }
 
+// q and k rows scaled to unit length (the states path with q / k
+// normalisation in the kernel normalises once, here, and keeps the rows for
+// the backward): one workgroup per 64 tokens of one q head; l2norm_rows does
+// the same arithmetic as the scans' and gradient kernel's in-register
+// normalisation, so the rows and 1 / |x| are the same bits.
+template <typename T>
+__global__ __launch_bounds__(256) void qk_norm_kernel(const T* q, const T* k, T* qn, T* kn,
+                                                      float* qinv, float* kinv, int64_t rows,
+                                                      int Hq) {
+  __shared__ float ri[2][64];
+  const int hq = blockIdx.y, tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int nr = (int)min((int64_t)64, rows - r0);
+  const int64_t base = (r0 * Hq + hq) * kDim;
+  const int gs = Hq * kDim * (int)sizeof(T);
+#pragma unroll
+  for (int side = 0; side < 2; ++side) {
+    TileRegs<128, 256> t;
+    tile_load<T, 128, 256>(t, (side ? k : q) + base, (int64_t)Hq * kDim, nr);
+    l2norm_rows<T, 256>(t, ri[side]);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc((side ? kn : qn) + base, (int64_t)nr * gs);
+#pragma unroll
+    for (int i = 0; i < TileRegs<128, 256>::N; ++i) {
+      const int x = tid + i * 256;
+      buf_store16(rs, (x >> 4) * gs + (x & 15) * 16, t.r[i]);
+    }
+  }
+  __syncthreads();
+  if (tid < nr) {
+    qinv[(r0 + tid) * Hq + hq] = ri[0][tid];
+    kinv[(r0 + tid) * Hq + hq] = ri[1][tid];
+  }
+}
+
+gdr_status launch_qk_norm(const gdr_problem* p, const void* q, const void* k, void* qn, void* kn,
+                          float* qinv, float* kinv, hipStream_t st) {
+  const int64_t rows = (int64_t)p->B * p->T;
+  if (rows > 0) {
+    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)p->Hq);
+    if (p->in_dtype == GDR_BF16)
+      GDR_LAUNCH("qk_norm", qk_norm_kernel<__bf16>, grid, dim3(256), st,
+                 reinterpret_cast<const __bf16*>(q), reinterpret_cast<const __bf16*>(k),
+                 reinterpret_cast<__bf16*>(qn), reinterpret_cast<__bf16*>(kn), qinv, kinv, rows,
+                 p->Hq);
+    else
+      GDR_LAUNCH("qk_norm", qk_norm_kernel<_Float16>, grid, dim3(256), st,
+                 reinterpret_cast<const _Float16*>(q), reinterpret_cast<const _Float16*>(k),
+                 reinterpret_cast<_Float16*>(qn), reinterpret_cast<_Float16*>(kn), qinv, kinv,
+                 rows, p->Hq);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("q / k normalisation launch failed: %s", hipGetErrorString(e));
+    return GDR_ERR_HIP;
+  }
+  return GDR_OK;
+}
+
 template <typename T, int VB>
 static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st) {
   const unsigned units = (unsigned)(pl.N * a.Hv);

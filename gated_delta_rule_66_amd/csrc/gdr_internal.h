@@ -58,12 +58,21 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
 // hstates: the forward's chunk-start states in the packed layout, or
 // NULL to recompute them.  trans (with hstates, nullable): the forward's
 // segment transitions for the same plan.
+// qinv, kinv (nullable): q and k were normalised beforehand (qk_norm_rows)
+// and p has use_qk_l2norm off; the gradient kernel maps dq, dk back through
+// the normalisation with these per-(token, q head) 1 / |x|.
 gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const float* gcum, const void* graw, const void* beta,
                       const void* A, const void* dO, const float* dht, const float* h0,
                       const void* hstates, const float* trans, void* dq, void* dk, void* dv,
                       void* dbeta, void* dg, float* dh0, float* dA_log, float* ddt_bias, void* ws,
-                      hipStream_t st);
+                      hipStream_t st, const float* qinv = nullptr, const float* kinv = nullptr);
+
+// Every (token, q head) row of q and k scaled to unit length as the kernels
+// normalise them in registers (same rounding): qn, kn in the input dtype and
+// layout, qinv, kinv the fp32 1 / |x| per row ([rows, Hq], rows = B * T).
+gdr_status launch_qk_norm(const gdr_problem* p, const void* q, const void* k, void* qn, void* kn,
+                          float* qinv, float* kinv, hipStream_t st);
 
 // Token-by-token recurrence (decode and other short inputs), no workspace.
 gdr_status launch_recurrent(const gdr_problem* p, const void* q, const void* k, const void* v,

@@ -178,7 +178,14 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
  *        required when that size is nonzero, ignored (may be NULL) when it
  *        is zero; trans_bytes is its size (GDR_ERR_WORKSPACE when smaller).
  *        Entries of the first and last segment of each sequence are never
- *        written or read.
+ *        written or read.  With p->use_qk_l2norm the buffer also keeps,
+ *        after the transitions (256-byte aligned), the q and k rows scaled
+ *        to unit length (in_dtype, q's layout) and their fp32 1 / |x| per
+ *        (token, q head): the forward normalises the rows once, runs the
+ *        rest as a problem without the option, and gdr_chunk_bwd_states
+ *        given the buffer does the same, mapping dq, dk back through the
+ *        normalisation; gdr_chunk_trans_size is then nonzero whatever the
+ *        plan.
  * A forward with h_packed = 1 and the backward that takes its states plan
  * together (one segment count for both, gdr_plan_info), so that the
  * backward applies the transposed T_seg instead of forming its own
@@ -261,7 +268,10 @@ gdr_status gdr_chunk_bwd_gate(const gdr_problem* p, const void* q, const void* k
  *        splits sequences the state-gradient scan then applies them
  *        transposed (the gradient's transition over a segment is T_seg^T)
  *        instead of forming its own, which halves its transition pass;
- *        NULL: it forms them (ignored when the plan splits nothing)
+ *        NULL: it forms them (ignored when the plan splits nothing).
+ *        With p->use_qk_l2norm the buffer's unit rows are used instead of
+ *        normalising q and k again (q and k are then not read); NULL: the
+ *        backward normalises them itself
  *        g, the gate's raw input (use_gate only; NULL otherwise, and so are
  *        dA_log, ddt_bias)
  * The states are not recomputed: only the reverse state-gradient scan runs

@@ -221,6 +221,19 @@ def test_transition_buffer_size():
     cp, _ = plan(good(h_packed=1, B=1, N=1, T=65536, Hq=32, Hv=32), 0)
     assert lib.gdr_chunk_trans_size(P(h_packed=1, B=1, N=1, T=65536, Hq=32, Hv=32)) == \
         32 * cp * 128 * 128 * 4
+    # q / k normalised in the kernel: the unit q and k rows (bf16) and their
+    # fp32 norms follow the transitions, 256-byte aligned, whatever the plan
+    a256 = lambda n: (n + 255) // 256 * 256
+    rows = 2 * 4096 * 16
+    assert lib.gdr_chunk_trans_size(P(h_packed=1, B=2, N=2, T=4096, Hq=16, Hv=32,
+                                      use_qk_l2norm=1)) == \
+        2 * a256(rows * 128 * 2) + a256(rows * 4) + rows * 4
+    rows = 4096 * 2
+    assert lib.gdr_chunk_trans_size(P(h_packed=1, B=1, N=1, T=4096, Hq=2, Hv=4, cp_segments=3,
+                                      use_qk_l2norm=1)) == \
+        a256(4 * 3 * 128 * 128 * 4) + 2 * a256(rows * 128 * 2) + a256(rows * 4) + rows * 4
+    assert lib.gdr_chunk_trans_size(P(h_packed=0, B=1, N=1, T=4096, Hq=2, Hv=4,
+                                      use_qk_l2norm=1)) == 0
 
 
 def test_null_and_workspace_errors_before_any_device_work():

@@ -261,17 +261,24 @@ def test_pipelined_backward_equals_the_one_pass_backward(name):
         opts = dict(use_gate_in_kernel=True, A_log=A_log, dt_bias=dt_bias)
     g_cum, A, o, h, trans, ht = gdr.chunk_gated_delta_rule_fwd_states(
         dd["q"], dd["k"], dd["v"], g, dd["beta"], **kw, **opts)
-    assert trans is None
+    # nothing is split; with q / k normalised the forward keeps the unit rows
+    qkn = bool(opts.get("use_qk_l2norm_in_kernel"))
+    assert (trans is not None) == qkn
     bkw = dict(kw, dht=dd["dht"], dg_dtype=g.dtype, **opts)
     if "A_log" in opts:
         bkw["g_input"] = g
     piped = gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
-                                           dd["do"], h=h, **bkw)
+                                           dd["do"], h=h, trans=trans, **bkw)
     plain = gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
                                            dd["do"], **bkw)
+    runs = [piped]
+    if qkn:  # the states without the unit rows: the backward normalises q, k itself
+        runs.append(gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum,
+                                                   dd["beta"], A, dd["do"], h=h, **bkw))
     torch.cuda.synchronize()
-    for i, (x, y) in enumerate(zip(piped, plain)):
-        assert (x is None and y is None) or torch.equal(x, y), i
+    for run in runs:
+        for i, (x, y) in enumerate(zip(run, plain)):
+            assert (x is None and y is None) or torch.equal(x, y), i
 
 
 def test_pipelined_backward_in_both_state_layouts():

@@ -31,6 +31,10 @@ CASES = {
                 lens=[70, 1, 64, 129, 250]),
     "long_slow_decay": P("long", B=1, T=1500, Hq=2, Hv=2, init_state=True, backward=True,
                          dht=True, g_shift=2.0),
+    # grouped heads, 16+ chunks: the states path's backward takes the
+    # data-scheduled launch
+    "gva_long": P("gva_long", B=2, T=1100, Hq=1, Hv=2, init_state=True, backward=True,
+                  dht=True),
 }
 
 # (case, cp_segments, wave_tiles, output_h): the scan variants the plans pick
@@ -82,6 +86,48 @@ def test_l2norm_matches_oracle(name, cp, vt, output_h):
                 assert x is None
                 continue
             res[nm] = check(nm, x, r, "state" if nm in ("dh0", "final_state") else "tok", d["cu_seqlens"])
+    print({k: round(v, 5) for k, v in res.items()}, flush=True)
+    for k, v in res.items():
+        assert v <= TOL, (k, v)
+
+
+# (case, cp_segments): the states path (the autograd op's): the forward
+# normalises the rows once and keeps them with its states, the backward takes
+# both (data-scheduled for the dense cases with 16+ chunks, one pass for the
+# short, packed and grouped-head ones, the unit rows after the segment
+# transitions under a split)
+STATES_VARIANTS = [("dense_state_dht", 1), ("fp16_gva", 1), ("varlen", 1),
+                   ("long_slow_decay", 1), ("long_slow_decay", 3), ("gva_long", 1)]
+
+
+@pytest.mark.parametrize("name,cp", STATES_VARIANTS)
+def test_l2norm_states_path_matches_oracle(name, cp):
+    import gated_delta_rule_66_amd as gdr
+    d = gdr_synth.make(CASES[name])
+    print("case", name, "cp", cp, "states", flush=True)
+    dd = to_dev(d)
+    cu_cpu = d["cu_seqlens"]
+    kw = dict(scale=dd["scale"], initial_state=dd["h0"], cu_seqlens=dd["cu_seqlens"],
+              cu_seqlens_cpu=cu_cpu, cp_segments=cp, use_qk_l2norm_in_kernel=True)
+    g_cum, A, o, h, trans, ht = gdr.chunk_gated_delta_rule_fwd_states(
+        dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], output_final_state=True, **kw)
+    assert trans is not None
+    grads = gdr.chunk_gated_delta_rule_bwd(dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A,
+                                           dd["do"], dht=dd["dht"], dg_dtype=dd["g"].dtype,
+                                           h=h, trans=trans, **kw)
+    torch.cuda.synchronize()
+    cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].numpy()
+    args = (np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]), d["scale"])
+    o_r, ht_r = oracle.fwd(*args, initial_state=np64(d["h0"]), cu_seqlens=cu, use_qk_l2norm=True)
+    res = {"o": check("o", o, o_r, "tok", d["cu_seqlens"]),
+           "final_state": check("final_state", ht, ht_r, "state")}
+    ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]),
+                     cu_seqlens=cu, use_qk_l2norm=True)
+    for nm, x, r in zip(NAMES, grads, ref):
+        if r is None:
+            assert x is None
+            continue
+        res[nm] = check(nm, x, r, "state" if nm == "dh0" else "tok", d["cu_seqlens"])
     print({k: round(v, 5) for k, v in res.items()}, flush=True)
     for k, v in res.items():
         assert v <= TOL, (k, v)
