@@ -221,7 +221,9 @@ def chunk_gated_delta_rule_fwd_states(q, k, v, g, beta, scale=None, initial_stat
     :func:`chunk_gated_delta_rule_fwd` with ``output_h=True, h_packed=True``
     that also keeps, when the plan splits sequences into T-segments, each
     segment's fp32 state transition for the backward.  Returns ``(g_cum, A,
-    o, h, trans, final_state)``; ``trans`` is ``None`` when nothing is split.
+    o, h, trans, final_state)``; ``trans`` also keeps, with
+    ``use_qk_l2norm_in_kernel``, the unit q and k rows and their norms, and is
+    ``None`` when nothing is split and q, k are not normalised.
     Hand ``h`` and ``trans`` to :func:`chunk_gated_delta_rule_bwd`."""
     return _fwd(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
                 state_v_first, True, cp_segments, cu_seqlens_cpu, wave_tiles,
