@@ -481,7 +481,8 @@ static gdr_status chunk_fwd(const gdr_problem* p, const void* q, const void* k, 
                             const void* g, const void* beta, const float* initial_state,
                             float* g_cum, void* A, void* o, void* h, float* trans,
                             float* final_state, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            void* stream, void* qn = nullptr, void* kn = nullptr,
+                            float* qinv = nullptr, float* kinv = nullptr) {
   if (!q || !k || !v || !g || !beta || !g_cum || !A || !o)
     return fail(GDR_ERR_NULL, nullptr, 0, "a required forward pointer is NULL");
   const Plan pl = make_plan(p, false);
@@ -492,7 +493,8 @@ static gdr_status chunk_fwd(const gdr_problem* p, const void* q, const void* k, 
   const gdr_status s = check_device_cached();
   if (s != GDR_OK) return s;
   return launch_fwd(p, pl, q, k, v, g, beta, initial_state, g_cum, A, o, h,
-                    pl.cp > 1 ? trans : nullptr, final_state, workspace, (hipStream_t)stream);
+                    pl.cp > 1 ? trans : nullptr, final_state, workspace, (hipStream_t)stream, qn,
+                    kn, qinv, kinv);
 }
 
 gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
@@ -531,19 +533,14 @@ gdr_status gdr_chunk_fwd_states(const gdr_problem* p, const void* q, const void*
   if (!p->use_qk_l2norm)
     return chunk_fwd(p, q, k, v, g, beta, initial_state, g_cum, A, o, h, trans, final_state,
                      workspace, workspace_bytes, stream);
-  // normalise the rows once, keep them, and run the rest without the option
-  if (!q || !k) return fail(GDR_ERR_NULL, nullptr, 0, "a required forward pointer is NULL");
-  const gdr_status sd = check_device_cached();
-  if (sd != GDR_OK) return sd;
+  // fwd_prep normalises the rows once and keeps them; the rest runs without
+  // the option
   const TransLayout t = trans_layout(p);
   char* tb = reinterpret_cast<char*>(trans);
-  const gdr_status sn = launch_qk_norm(p, q, k, tb + t.qn, tb + t.kn,
-                                       reinterpret_cast<float*>(tb + t.qinv),
-                                       reinterpret_cast<float*>(tb + t.kinv), (hipStream_t)stream);
-  if (sn != GDR_OK) return sn;
   const gdr_problem pn = without_qk_norm(p);
-  return chunk_fwd(&pn, tb + t.qn, tb + t.kn, v, g, beta, initial_state, g_cum, A, o, h, trans,
-                   final_state, workspace, workspace_bytes, stream);
+  return chunk_fwd(&pn, q, k, v, g, beta, initial_state, g_cum, A, o, h, trans, final_state,
+                   workspace, workspace_bytes, stream, tb + t.qn, tb + t.kn,
+                   reinterpret_cast<float*>(tb + t.qinv), reinterpret_cast<float*>(tb + t.kinv));
 }
 
 static_assert(GDR_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "header and library agree");

@@ -52,9 +52,18 @@ struct FwdArgs {
   int beta_mode;  // bit 0 sigmoid of a beta logit, bit 1 twice beta
   const float* gate_A_log;    // non-null: g is the gate input (gate_log_decay)
   const float* gate_dt_bias;  // nullable
+  // (qk_norm) non-null: the group's first value head also writes the unit q
+  // and k rows of its chunk (q's layout) and their fp32 1 / |x| per (token,
+  // q head), which the scans and the backward then read instead
+  void* qn;
+  void* kn;
+  float* qinv;
+  float* kinv;
 };
 
-template <typename T>
+// KEEP: a.qn is set (the states path with q / k normalised): the group's
+// first value head also keeps the unit rows and their norms.
+template <typename T, bool KEEP>
 __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   constexpr int LDK = 136;
   constexpr int LDM = 68;
@@ -103,10 +112,31 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   const uint32_t glo = __builtin_amdgcn_raw_buffer_load_b16(grs, rr * ld_g, 0, 0);
   const uint32_t ghi = __builtin_amdgcn_raw_buffer_load_b16(grs, rr * ld_g + 2, 0, 0);
   const uint16_t braw = __builtin_amdgcn_raw_buffer_load_b16(brs, rr * a.Hv * (int)sizeof(T), 0, 0);
-  TileRegs<128, 256> rk;
+  TileRegs<128, 256> rk, rq;
   tile_load<T, 128, 256>(rk, reinterpret_cast<const T*>(a.k) + (t0 * a.Hq + hq) * kDim,
                          (int64_t)a.Hq * kDim, Cc);
-  if (a.qk_norm) l2norm_rows<T, 256>(rk, nullptr);
+  // the unit q rows when this workgroup keeps them (a q load over no rows,
+  // zeros, for the group's other heads: no branch around the load)
+  const bool keep_qk = KEEP && h % G == 0;
+  if (KEEP)
+    tile_load<T, 128, 256>(rq, reinterpret_cast<const T*>(a.q) + (t0 * a.Hq + hq) * kDim,
+                           (int64_t)a.Hq * kDim, keep_qk ? Cc : 0);
+  __shared__ float rinv[2][KEEP ? 64 : 1];  // 1 / |x| of the kept rows: q, k
+  if (a.qk_norm) l2norm_rows<T, 256>(rk, keep_qk ? rinv[1] : nullptr);
+  if (keep_qk) {
+    l2norm_rows<T, 256>(rq, rinv[0]);
+    const int gs = a.Hq * kDim * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t qs =
+        buf_rsrc(reinterpret_cast<T*>(a.qn) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gs);
+    const __amdgpu_buffer_rsrc_t ks =
+        buf_rsrc(reinterpret_cast<T*>(a.kn) + (t0 * a.Hq + hq) * kDim, (int64_t)Cc * gs);
+#pragma unroll
+    for (int i = 0; i < TileRegs<128, 256>::N; ++i) {
+      const int x = tid + i * 256;
+      buf_store16(qs, (x >> 4) * gs + (x & 15) * 16, rq.r[i]);
+      buf_store16(ks, (x >> 4) * gs + (x & 15) * 16, rk.r[i]);
+    }
+  }
   tile_store<T, 128, 256>(Ks, LDK, rk);
   if (w == 0) {
     float gv = a.g_dtype == 2 ? __builtin_bit_cast(float, glo | (ghi << 16))
@@ -122,6 +152,10 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
     if (l < Cc) a.gcum[(t0 + l) * a.Hv + h] = gc;
   }
   __syncthreads();
+  if (keep_qk && tid < Cc) {
+    a.qinv[(t0 + tid) * a.Hq + hq] = rinv[0][tid];
+    a.kinv[(t0 + tid) * a.Hq + hq] = rinv[1][tid];
+  }
 
   // M, rows 16w .. 16w+15 (only the blocks on or below the diagonal are nonzero)
   for (int cb = 0; cb < 4; ++cb) {
@@ -259,64 +293,6 @@ size_t fwd_workspace_bytes(const gdr_problem* p, const Plan& pl) {
   return b;
 }
 
-// q and k rows scaled to unit length (the states path with q / k
-// normalisation in the kernel normalises once, here, and keeps the rows for
-// the backward): one workgroup per 64 tokens of one q head; l2norm_rows does
-// the same arithmetic as the scans' and gradient kernel's in-register
-// normalisation, so the rows and 1 / |x| are the same bits.
-template <typename T>
-__global__ __launch_bounds__(256) void qk_norm_kernel(const T* q, const T* k, T* qn, T* kn,
-                                                      float* qinv, float* kinv, int64_t rows,
-                                                      int Hq) {
-  __shared__ float ri[2][64];
-  const int hq = blockIdx.y, tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  const int nr = (int)min((int64_t)64, rows - r0);
-  const int64_t base = (r0 * Hq + hq) * kDim;
-  const int gs = Hq * kDim * (int)sizeof(T);
-#pragma unroll
-  for (int side = 0; side < 2; ++side) {
-    TileRegs<128, 256> t;
-    tile_load<T, 128, 256>(t, (side ? k : q) + base, (int64_t)Hq * kDim, nr);
-    l2norm_rows<T, 256>(t, ri[side]);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc((side ? kn : qn) + base, (int64_t)nr * gs);
-#pragma unroll
-    for (int i = 0; i < TileRegs<128, 256>::N; ++i) {
-      const int x = tid + i * 256;
-      buf_store16(rs, (x >> 4) * gs + (x & 15) * 16, t.r[i]);
-    }
-  }
-  __syncthreads();
-  if (tid < nr) {
-    qinv[(r0 + tid) * Hq + hq] = ri[0][tid];
-    kinv[(r0 + tid) * Hq + hq] = ri[1][tid];
-  }
-}
-
-gdr_status launch_qk_norm(const gdr_problem* p, const void* q, const void* k, void* qn, void* kn,
-                          float* qinv, float* kinv, hipStream_t st) {
-  const int64_t rows = (int64_t)p->B * p->T;
-  if (rows > 0) {
-    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)p->Hq);
-    if (p->in_dtype == GDR_BF16)
-      GDR_LAUNCH("qk_norm", qk_norm_kernel<__bf16>, grid, dim3(256), st,
-                 reinterpret_cast<const __bf16*>(q), reinterpret_cast<const __bf16*>(k),
-                 reinterpret_cast<__bf16*>(qn), reinterpret_cast<__bf16*>(kn), qinv, kinv, rows,
-                 p->Hq);
-    else
-      GDR_LAUNCH("qk_norm", qk_norm_kernel<_Float16>, grid, dim3(256), st,
-                 reinterpret_cast<const _Float16*>(q), reinterpret_cast<const _Float16*>(k),
-                 reinterpret_cast<_Float16*>(qn), reinterpret_cast<_Float16*>(kn), qinv, kinv,
-                 rows, p->Hq);
-  }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_error("q / k normalisation launch failed: %s", hipGetErrorString(e));
-    return GDR_ERR_HIP;
-  }
-  return GDR_OK;
-}
-
 template <typename T, int VB>
 static void launch_scan_vb(const Plan& pl, ScanArgs a, int mode, hipStream_t st) {
   const unsigned units = (unsigned)(pl.N * a.Hv);
@@ -372,7 +348,11 @@ template void launch_scan<_Float16>(const Plan&, ScanArgs, int, hipStream_t);
 gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const void* g, const void* beta, const float* h0,
                       float* gcum, void* A, void* o, void* h, float* trans, float* ht, void* ws,
-                      hipStream_t st) {
+                      hipStream_t st, void* qn, void* kn, float* qinv, float* kinv) {
+  if ((qn || kn || qinv || kinv) && (!qn || !kn || !qinv || !kinv || p->use_qk_l2norm)) {
+    set_error("unit rows are kept with both norms, on a problem that does not normalise");
+    return GDR_ERR_ARG;
+  }
   char* wp = reinterpret_cast<char*>(ws);
   const int32_t* offs = nullptr;
   const int32_t* order = nullptr;
@@ -396,17 +376,20 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
   fa.beta_mode = (p->beta_sigmoid ? 1 : 0) | (p->neg_eigval ? 2 : 0);
   fa.gate_A_log = p->use_gate ? p->gate_A_log : nullptr;
   fa.gate_dt_bias = p->use_gate ? p->gate_dt_bias : nullptr;
+  fa.qn = qn; fa.kn = kn; fa.qinv = qinv; fa.kinv = kinv;
+  if (qn) fa.qk_norm = 1;  // fwd_prep normalises and keeps the rows; the scans read them
 
   ScanArgs sa;
   memset(&sa, 0, sizeof(sa));
-  sa.q = q; sa.k = k; sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
+  sa.q = qn ? qn : q; sa.k = kn ? kn : k;
+  sa.v = v; sa.beta = beta; sa.gcum = gcum; sa.A = A; sa.h0 = h0;
   sa.o = o; sa.h = h; sa.ht = ht; sa.trans = trans;
   sa.cu = p->cu_seqlens_dev; sa.offs = offs; sa.order = order;
   sa.N = pl.N; sa.T = p->T; sa.Hq = p->Hq; sa.Hv = p->Hv; sa.nc_dense = pl.nc_dense;
   sa.P = 1; sa.nvs = 1;
   sa.scale = p->scale; sa.svf = fa.svf; sa.h_svf = fa.svf;
   sa.h_vm = p->h_packed ? 1 : 0;
-  sa.qk_norm = fa.qk_norm;
+  sa.qk_norm = p->use_qk_l2norm ? 1 : 0;
   sa.beta_mode = fa.beta_mode;
   sa.seg_out = nullptr; sa.seg_start = nullptr;
   sa.reverse = 0;
@@ -417,15 +400,18 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
     wp += align256(units * pl.cp * 2 * KV * sizeof(float));
     sa.seg_start = reinterpret_cast<float*>(wp);
   }
+  const dim3 gp((unsigned)pl.total_chunks, p->Hv);
   if (p->in_dtype == GDR_BF16) {
-    if (pl.total_chunks > 0)
-      GDR_LAUNCH("fwd_prep", fwd_prep_kernel<__bf16>, dim3((unsigned)pl.total_chunks, p->Hv),
-                 dim3(256), st, fa);
+    if (pl.total_chunks > 0 && qn)
+      GDR_LAUNCH("fwd_prep", (fwd_prep_kernel<__bf16, true>), gp, dim3(256), st, fa);
+    else if (pl.total_chunks > 0)
+      GDR_LAUNCH("fwd_prep", (fwd_prep_kernel<__bf16, false>), gp, dim3(256), st, fa);
     launch_scan<__bf16>(pl, sa, MODE_OUT, st);
   } else {
-    if (pl.total_chunks > 0)
-      GDR_LAUNCH("fwd_prep", fwd_prep_kernel<_Float16>, dim3((unsigned)pl.total_chunks, p->Hv),
-                 dim3(256), st, fa);
+    if (pl.total_chunks > 0 && qn)
+      GDR_LAUNCH("fwd_prep", (fwd_prep_kernel<_Float16, true>), gp, dim3(256), st, fa);
+    else if (pl.total_chunks > 0)
+      GDR_LAUNCH("fwd_prep", (fwd_prep_kernel<_Float16, false>), gp, dim3(256), st, fa);
     launch_scan<_Float16>(pl, sa, MODE_OUT, st);
   }
   hipError_t e = hipGetLastError();

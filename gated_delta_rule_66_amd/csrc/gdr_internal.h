@@ -49,10 +49,14 @@ int bwd_pipe_bounds(const gdr_problem* p, const Plan& pl, bool states_given, int
 
 // trans: [N * Hv, cp, K, K] fp32, where the transition pass leaves every
 // segment transition T_seg for the backward (NULL: kept in the workspace).
+// qn, kn, qinv, kinv (all or none; p without use_qk_l2norm): fwd_prep
+// normalises the q and k rows and keeps them there (the unit rows in q's
+// layout, fp32 1 / |x| per (token, q head)); the scans read the unit rows.
 gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const void* k,
                       const void* v, const void* g, const void* beta, const float* h0,
                       float* gcum, void* A, void* o, void* h, float* trans, float* ht, void* ws,
-                      hipStream_t st);
+                      hipStream_t st, void* qn = nullptr, void* kn = nullptr,
+                      float* qinv = nullptr, float* kinv = nullptr);
 
 // graw: the gate input (use_gate only, else NULL); dA_log, ddt_bias nullable.
 // hstates: the forward's chunk-start states in the packed layout, or
@@ -67,12 +71,6 @@ gdr_status launch_bwd(const gdr_problem* p, const Plan& pl, const void* q, const
                       const void* hstates, const float* trans, void* dq, void* dk, void* dv,
                       void* dbeta, void* dg, float* dh0, float* dA_log, float* ddt_bias, void* ws,
                       hipStream_t st, const float* qinv = nullptr, const float* kinv = nullptr);
-
-// Every (token, q head) row of q and k scaled to unit length as the kernels
-// normalise them in registers (same rounding): qn, kn in the input dtype and
-// layout, qinv, kinv the fp32 1 / |x| per row ([rows, Hq], rows = B * T).
-gdr_status launch_qk_norm(const gdr_problem* p, const void* q, const void* k, void* qn, void* kn,
-                          float* qinv, float* kinv, hipStream_t st);
 
 // Token-by-token recurrence (decode and other short inputs), no workspace.
 gdr_status launch_recurrent(const gdr_problem* p, const void* q, const void* k, const void* v,
