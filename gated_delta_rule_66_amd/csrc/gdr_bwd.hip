@@ -1350,6 +1350,9 @@ struct GradArgs {
   // the state gradients are being written in the same launch (bwd_dyn_kernel):
   // load them coherently (sc1); the progress counts a workgroup waits for
   const unsigned* flags;
+  // (bwd_dyn_kernel, packed sequences) the gradient items in launch order:
+  // (sequence, chunk) pairs (dyn_items_kernel)
+  const int32_t* items;
 };
 
 // Eight waves: wave w works on row / column block wr = w % 4 and takes one
@@ -2123,8 +2126,14 @@ __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, in
     return;
   }
   const int g = (int)blockIdx.x - nb2, units = ga.N * ga.Hv, nch = ga.nc_dense;
-  int j, n, by, u;
-  if constexpr (GVA) {
+  int j, n, by, u, nc = nch;
+  if (!GVA && ga.items) {  // packed sequences: the item table's order
+    n = ga.items[2 * (g / ga.Hv)];
+    j = ga.items[2 * (g / ga.Hv) + 1];
+    by = g % ga.Hv;
+    u = n * ga.Hv + by;
+    nc = ga.offs[n + 1] - ga.offs[n];
+  } else if constexpr (GVA) {
     const int gs = ga.Hv / ga.Hq, hrow = ga.Hq * (gs - 1);  // workgroup rows per (sequence, chunk)
     const int rows = ga.N * hrow, x = g % rows;
     j = nch - 1 - g / rows;
@@ -2140,11 +2149,12 @@ __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, in
   // every tile but the state gradient is an input of the launch: the loads
   // are issued before the wait, so their latency overlaps it
   GradFirst<T> f;
-  const GradItem item = grad_item<GVA>(ga, n * nch + j, by);
+  const int c = ga.items ? ga.offs[n] + j : n * nch + j;  // global chunk row
+  const GradItem item = grad_item<GVA>(ga, c, by);
   grad_first_loads<T>(ga, item, f, false);
   if (threadIdx.x == 0) {
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ga.flags, (int64_t)units * 4);
-    const unsigned need = (unsigned)(nch - j);
+    const unsigned need = (unsigned)(nc - j);
     for (int it = 0; it < kDynSpinLimit; ++it) {
       if (buf_load_u32_sc1(rs, u * 4) >= need) break;
       __builtin_amdgcn_s_sleep(8);
@@ -2157,8 +2167,71 @@ __global__ __launch_bounds__(512) void bwd_dyn_kernel(DhArgs da, GradArgs ga, in
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   grad_dsn_load<T>(ga, item, 0, f.rg);
-  grad_body<T, (OPT & 1) != 0, GVA, true>(ga, n * nch + j, by, ga.N * nch,
+  grad_body<T, (OPT & 1) != 0, GVA, true>(ga, c, by, ga.N * nch,
                                           *reinterpret_cast<GradLds<T>*>(lds), f);
+}
+
+// The data-scheduled backward's gradient items for packed sequences, in
+// launch order: by distance from the sequence's end (the order the scan
+// stores the state gradients in), within one distance the longest sequences
+// first.  Sequences longer than d chunks are ranks 0 .. cnt[d]-1 of order
+// (longest first), so item (sequence order[r], its chunk L-1-d) takes slot
+// base[d] + r, base the exclusive prefix sum of cnt.  Also zeroes the
+// progress counts.  One workgroup; maxc (the longest sequence's chunks) at
+// most kDynMaxChunks.
+constexpr int kDynMaxChunks = 4096;
+static __global__ __launch_bounds__(256) void dyn_items_kernel(const int32_t* offs,
+                                                               const int32_t* order, int N,
+                                                               int maxc, int32_t* items,
+                                                               int64_t nitems, unsigned* flags,
+                                                               int nflags) {
+  __shared__ int32_t base[kDynMaxChunks];
+  __shared__ int32_t part[256];
+  const int tid = (int)threadIdx.x;
+  for (int i = tid; i < nflags; i += 256) flags[i] = 0u;
+  for (int d = tid; d < maxc; d += 256) {  // cnt[d]: the first rank of at most d chunks
+    int lo = 0, hi = N;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1, m = order[mid];
+      if (offs[m + 1] - offs[m] > d) lo = mid + 1;
+      else hi = mid;
+    }
+    base[d] = lo;
+  }
+  __syncthreads();
+  const int per = (maxc + 255) / 256, d0 = min(maxc, tid * per), d1 = min(maxc, d0 + per);
+  int sum = 0;
+  for (int d = d0; d < d1; ++d) sum += base[d];
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int t = part[i];
+      part[i] = acc;
+      acc += t;
+    }
+  }
+  __syncthreads();
+  int acc = part[tid];
+  for (int d = d0; d < d1; ++d) {
+    const int t = base[d];
+    base[d] = acc;
+    acc += t;
+  }
+  __syncthreads();
+  // (the host's lengths bound every slot: a device cu_seqlens that disagrees
+  // with them cannot write past the table)
+  for (int r = tid; r < N; r += 256) {
+    const int n = order[r], L = min(offs[n + 1] - offs[n], maxc);
+    for (int d = 0; d < L; ++d) {
+      const int64_t slot = (int64_t)base[d] + r;
+      if (slot < nitems) {
+        items[2 * slot] = n;
+        items[2 * slot + 1] = L - 1 - d;
+      }
+    }
+  }
 }
 
 static __global__ void zero_u32_kernel(unsigned* p, int n) {
@@ -2208,7 +2281,17 @@ __global__ __launch_bounds__(256) void gate_param_grad_kernel(const float* gpart
 // S slices (q / k normalised in the kernel, whose scan form has no progress
 // counts).
 static int pipe_slices(const gdr_problem* p, const Plan& pl, bool states_given) {
-  if (!states_given || p->cu_seqlens_dev || pl.cp != 1 || pl.vb != 1) return 0;
+  if (!states_given || pl.cp != 1 || pl.vb != 1) return 0;
+  if (p->cu_seqlens_dev) {
+    // packed sequences (no grouped heads): the data-scheduled launch for up
+    // to 256 units, the scan's workgroups of short sequences handing their
+    // CUs to the gradient workgroups as they finish
+    const int64_t maxc = (pl.max_len + kChunk - 1) / kChunk;
+    if (p->Hq != p->Hv || p->use_qk_l2norm || (int64_t)pl.N * p->Hv > 256 || maxc < 16 ||
+        maxc > kDynMaxChunks)
+      return 0;
+    return 1;
+  }
   if (pl.nc_dense < 16 || (int64_t)pl.N * p->Hv > 128) return 0;
   if (!p->use_qk_l2norm) return 1;
   if (p->Hq != p->Hv || (int64_t)pl.N * p->Hv * 2 > 128) return 0;
@@ -2223,9 +2306,9 @@ static int pipe_slices(const gdr_problem* p, const Plan& pl, bool states_given) 
 // (idle CUs x scan time of one chunk), about 19 us per gradient workgroup and
 // 2.9 us per scan chunk, and slice p is r times slice p + 1.
 static void pipe_bounds(const gdr_problem* p, const Plan& pl, int S, int* lo) {
-  if (S == 1) {  // one launch over every chunk
+  if (S == 1) {  // one launch over every chunk (packed: the longest sequence's)
     lo[0] = 0;
-    lo[1] = pl.nc_dense;
+    lo[1] = p->cu_seqlens_dev ? (int)((pl.max_len + kChunk - 1) / kChunk) : pl.nc_dense;
     return;
   }
   const double units = (double)pl.N * p->Hv;
@@ -2249,7 +2332,7 @@ static void pipe_bounds(const gdr_problem* p, const Plan& pl, int S, int* lo) {
 }
 
 struct BwdLayout {
-  size_t offs, cp, cp2, h, dh, gacc, gpart, pipe, flags, total;
+  size_t offs, cp, cp2, h, dh, gacc, gpart, pipe, flags, items, total;
 };
 
 static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_given) {
@@ -2279,6 +2362,8 @@ static BwdLayout bwd_layout(const gdr_problem* p, const Plan& pl, bool states_gi
   if (S >= 2) o += align256((size_t)pl.N * p->Hv * S * kDim * kDim * sizeof(float));
   L.flags = o;  // the data-scheduled launch's progress counts, one per unit
   if (S == 1) o += align256((size_t)pl.N * p->Hv * sizeof(unsigned));
+  L.items = o;  // and its item table (packed sequences)
+  if (S == 1 && p->cu_seqlens_dev) o += align256((size_t)pl.total_chunks * 2 * sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -2455,17 +2540,27 @@ static gdr_status launch_bwd_t(const gdr_problem* p, const Plan& pl, const void*
     // captured graph replays correctly)
     const int units = pl.N * p->Hv, nb2 = units;
     unsigned* flags = reinterpret_cast<unsigned*>(ws + L.flags);
-    GDR_LAUNCH("bwd_flags", zero_u32_kernel, dim3(1), dim3(256), st, flags, units);
+    int32_t* items = nullptr;
+    if (p->cu_seqlens_dev) {
+      items = reinterpret_cast<int32_t*>(ws + L.items);
+      GDR_LAUNCH("bwd_flags", dyn_items_kernel, dim3(1), dim3(256), st, offs, order, pl.N,
+                 (int)((pl.max_len + kChunk - 1) / kChunk), items, (int64_t)pl.total_chunks,
+                 flags, units);
+    } else {
+      GDR_LAUNCH("bwd_flags", zero_u32_kernel, dim3(1), dim3(256), st, flags, units);
+    }
     DhArgs d = da;
     d.P = 1;
     d.nvs = 1;
     d.flags = flags;
     GradArgs g2 = ga;
     g2.flags = flags;
+    g2.items = items;
     // with GVA the launch takes value heads 0 .. G-2 of every group; the
     // gradient kernel then runs the group's last head, which sums dq and dk
     const int rows = gva ? pl.N * p->Hq * (G - 1) : units;
-    const unsigned blocks = (unsigned)(nb2 + rows * pl.nc_dense);
+    const unsigned blocks = (unsigned)(items ? nb2 + pl.total_chunks * p->Hv
+                                             : nb2 + (int64_t)rows * pl.nc_dense);
     switch ((qinv ? 4 : 0) | (sa.beta_mode ? 2 : 0) | (gva ? 1 : 0)) {
       case 0: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 0, false>), dim3(blocks), dim3(512), st, d, g2, nb2); break;
       case 1: GDR_LAUNCH("bwd_dyn", (bwd_dyn_kernel<T, 0, true>), dim3(blocks), dim3(512), st, d, g2, nb2); break;

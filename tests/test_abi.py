@@ -195,7 +195,14 @@ def test_backward_pipeline_plan():
     # heads, at most 64 units
     assert info(good(B=2, N=2, T=4096, Hq=16, Hv=32, use_qk_l2norm=1))[0] == 0
     assert info(good(B=4, N=4, T=4096, Hq=32, Hv=32, use_qk_l2norm=1))[0] == 0
-    # one pass: packed sequences, a scan that fills the chip, short
+    # packed sequences whose longest has 16+ chunks: the data-scheduled
+    # launch (bounds up to the longest sequence's chunks), not with grouped
+    # heads
+    long_cu = (ctypes.c_int32 * 4)(0, 70, 1100, 3100)
+    assert info(varlen(long_cu, T=3100, Hq=8, Hv=8)) == (1, [0, 32])
+    assert info(varlen(long_cu, T=3100, Hq=4, Hv=8))[0] == 0
+    assert info(varlen(long_cu, T=3100, Hq=8, Hv=8, use_qk_l2norm=1))[0] == 0
+    # one pass: short packed sequences, a scan that fills the chip, short
     # sequences, a split along T
     assert info(varlen(HOST_CU, T=200))[0] == 0
     assert info(good(B=8, N=8, T=4096, Hq=32, Hv=32))[0] == 0

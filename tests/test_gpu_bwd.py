@@ -68,6 +68,10 @@ CASES = {
     # the same launch with grouped heads (groups of three value heads): it
     # runs heads 0 .. G-2 of every group, the gradient kernel the last
     "pipe_gva": P("pipe_gva", B=2, T=1030, Hq=2, Hv=6, init_state=True, dht=True),
+    # packed sequences, the longest with 16+ chunks, an empty and a one-token
+    # one: the gradient workgroups in the item table's order
+    "pipe_varlen": P("pipe_varlen", B=1, T=0, Hq=2, Hv=2, init_state=True, dht=True,
+                     lens=[1100, 0, 70, 2000, 1, 640]),
     # (sequence, head) units a multiple of 8: rank-ordered scan blocks
     "varlen_ranked": P("varlen_ranked", B=1, T=0, Hq=2, Hv=2, init_state=True, dht=True,
                        lens=[300, 1000, 64, 700]),
@@ -171,7 +175,7 @@ def gpu_fwd_bwd_states(d, cp=0, use_trans=True, vt=0):
     ("long_slow_decay", 4, False, 1), ("varlen", 3, True, 0), ("varlen", 3, False, 0),
     ("dense_state_dht", 2, True, 2), ("fp16_gva", 3, True, 1), ("gva_group4", 2, True, 0),
     ("varlen_empty_seq", 2, True, 0), ("pipe", 1, True, 1), ("pipe_no_state", 1, True, 1),
-    ("pipe_gva", 1, True, 1),
+    ("pipe_gva", 1, True, 1), ("pipe_varlen", 1, True, 1),
     ("varlen_ranked", 1, True, 0), ("varlen_ranked", 3, True, 1)])
 def test_backward_from_the_forward_states(name, cp, use_trans, vt):
     d = gdr_synth.make(CASES[name])
