@@ -2101,13 +2101,14 @@ __global__ __launch_bounds__(512) void bwd_pipe_kernel(DhArgs da, GradArgs ga, i
   }
 }
 
-// The backward of a dense batch with few heads in one launch, scheduled by
-// data: blocks [0, nb2) run the state-gradient scan over every chunk
-// (loader-wave form, one 128-column workgroup per unit), the rest are the
-// gradient workgroups, the last chunk's first (row g: chunk nch - 1 - g /
-// rows of workgroup row g % rows, rows per chunk; with GVA the rows of value
-// heads 0 .. G-2 of every group, whose group sums the gradient kernel
-// completes in a launch of its own).  Blocks are dispatched in order, so the
+// The backward of a batch with few (sequence, head) units in one launch,
+// scheduled by data: blocks [0, nb2) run the state-gradient scan over every
+// chunk (loader-wave form, one 128-column workgroup per unit), the rest are
+// the gradient workgroups, the last chunk's first (dense: row g is chunk
+// nch - 1 - g / rows of workgroup row g % rows, rows per chunk; with GVA the
+// rows of value heads 0 .. G-2 of every group, whose group sums the gradient
+// kernel completes in a launch of its own; packed sequences: item g / Hv of
+// the item table, head g % Hv).  Blocks are dispatched in order, so the
 // scan's workgroups are resident before any gradient workgroup waits for
 // them; a gradient workgroup waits (bounded) until its unit's count covers
 // its chunk's state gradient, then runs on whatever CU it was given: the

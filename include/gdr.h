@@ -354,11 +354,15 @@ gdr_status gdr_plan_info(const gdr_problem* p, int backward, int32_t* cp_segment
                          int32_t* wave_tiles);
 
 /* The pipelined backward gdr_chunk_bwd_states runs for `p` (a diagnostic;
- * shapes only).  On a dense batch with few (sequence, head) units:
- * *slices = 1: one launch holds the state-gradient scan and the gradient
- * workgroups of every chunk, the last chunk's first, each starting once
- * the scan has stored its chunk's state gradient (bounds = 0, chunks per
- * sequence).  With use_qk_l2norm, *slices >= 2: the scan runs in ranges of
+ * shapes only).  With at most 128 (sequence, head) units of a dense batch,
+ * or 256 of packed sequences without grouped heads, and 16 or more chunks
+ * in the longest sequence: *slices = 1: one launch holds the state-gradient
+ * scan and the gradient workgroups of every chunk, the chunks nearest their
+ * sequence's end first, each starting once the scan has stored its chunk's
+ * state gradient (bounds = 0, chunks of the longest sequence).  With
+ * use_qk_l2norm (reported for the backward that normalises q and k itself;
+ * given the forward's unit rows it runs as without the option), at most 64
+ * units of a dense batch and no grouped heads, *slices >= 2: the scan runs in ranges of
  * chunks, the last range first, each launch pairing one range's scan with
  * the per-chunk gradients of the range the launch before finished; the last
  * launch runs the gradients of chunks [bounds[0], bounds[1]) of every
