@@ -35,6 +35,10 @@ CASES = {
     # data-scheduled launch
     "gva_long": P("gva_long", B=2, T=1100, Hq=1, Hv=2, init_state=True, backward=True,
                   dht=True),
+    # packed sequences, the longest with 16+ chunks: the data-scheduled launch
+    # in the item table's order
+    "varlen_long": P("varlen_long", B=1, T=0, Hq=2, Hv=2, init_state=True, backward=True,
+                     dht=True, lens=[1100, 0, 300, 2000]),
 }
 
 # (case, cp_segments, wave_tiles, output_h): the scan variants the plans pick
@@ -97,7 +101,8 @@ def test_l2norm_matches_oracle(name, cp, vt, output_h):
 # short, packed and grouped-head ones, the unit rows after the segment
 # transitions under a split)
 STATES_VARIANTS = [("dense_state_dht", 1), ("fp16_gva", 1), ("varlen", 1),
-                   ("long_slow_decay", 1), ("long_slow_decay", 3), ("gva_long", 1)]
+                   ("long_slow_decay", 1), ("long_slow_decay", 3), ("gva_long", 1),
+                   ("varlen_long", 1)]
 
 
 @pytest.mark.parametrize("name,cp", STATES_VARIANTS)
