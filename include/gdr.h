@@ -150,7 +150,10 @@ gdr_status gdr_check_device(void);
 
 /* Bytes of device workspace gdr_chunk_fwd / gdr_chunk_bwd (and
  * gdr_chunk_bwd_gate) / gdr_chunk_bwd_states need for `p` (0 if `p` is
- * invalid).  Depends only on the problem's shapes. */
+ * invalid).  Depends only on the problem's shapes.  With use_qk_l2norm the
+ * forward (h_packed = 1) and the states backward size for both of their
+ * forms: given the forward's unit rows they run as problems without the
+ * option, whose plans may differ. */
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p);
 size_t gdr_chunk_bwd_workspace_size(const gdr_problem* p);
 size_t gdr_chunk_bwd_states_workspace_size(const gdr_problem* p);
