@@ -412,14 +412,27 @@ gdr_status gdr_check_supported(const gdr_problem* p, char* reason, size_t reason
 
 gdr_status gdr_check_device(void) { return check_device_cached(); }
 
+// The unit q and k rows and their fp32 norms (q / k normalised in the
+// kernel): 520 bytes per (token, q head), each part 256-byte aligned.
+static size_t qk_rows_bytes(const gdr_problem* p) {
+  const size_t rows = (size_t)p->B * p->T * p->Hq;
+  return 2 * align256(rows * kDim * 2) + 2 * align256(rows * sizeof(float));
+}
+
+// gdr_chunk_fwd with q / k normalised and no user-layout h: the rows are
+// normalised once (fwd_prep) into the workspace's tail, after the workspace
+// of the problem without the option, which the rest then runs as
+static size_t fwd_rows_offset(const gdr_problem* p) {
+  gdr_problem pn = *p;
+  pn.use_qk_l2norm = 0;
+  return align256(fwd_workspace_bytes(&pn, make_plan(&pn, false)));
+}
+
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem* p) {
   if (validate(p, nullptr, 0) != GDR_OK) return 0;
   size_t b = fwd_workspace_bytes(p, make_plan(p, false));
-  if (p->use_qk_l2norm && p->h_packed) {  // the states path runs without the option
-    gdr_problem pn = *p;
-    pn.use_qk_l2norm = 0;
-    b = std::max(b, fwd_workspace_bytes(&pn, make_plan(&pn, false)));
-  }
+  if (p->use_qk_l2norm)  // the forms that run as a problem without the option
+    b = std::max(b, fwd_rows_offset(p) + qk_rows_bytes(p));
   return b;
 }
 
@@ -503,6 +516,23 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
                          void* workspace, size_t workspace_bytes, void* stream) {
   const gdr_status s = validate(p, nullptr, 0);
   if (s != GDR_OK) return s;
+  if (p->use_qk_l2norm && (!h || p->h_packed)) {
+    // normalise the rows once (fwd_prep) into the workspace's tail and run
+    // the rest without the option (the loader-wave output scan)
+    const size_t off = fwd_rows_offset(p), need = off + qk_rows_bytes(p);
+    if (!workspace || workspace_bytes < need)
+      return fail(GDR_ERR_WORKSPACE, nullptr, 0, "forward workspace needs %zu bytes, got %zu",
+                  need, workspace ? workspace_bytes : (size_t)0);
+    const size_t rows = (size_t)p->B * p->T * p->Hq;
+    char* t = reinterpret_cast<char*>(workspace) + off;
+    char* kn = t + align256(rows * kDim * 2);
+    char* qinv = kn + align256(rows * kDim * 2);
+    char* kinv = qinv + align256(rows * sizeof(float));
+    const gdr_problem pn = without_qk_norm(p);
+    return chunk_fwd(&pn, q, k, v, g, beta, initial_state, g_cum, A, o, h, nullptr, final_state,
+                     workspace, workspace_bytes, stream, t, kn, reinterpret_cast<float*>(qinv),
+                     reinterpret_cast<float*>(kinv));
+  }
   return chunk_fwd(p, q, k, v, g, beta, initial_state, g_cum, A, o, h, nullptr, final_state,
                    workspace, workspace_bytes, stream);
 }

@@ -163,7 +163,10 @@ size_t gdr_chunk_bwd_states_workspace_size(const gdr_problem* p);
  *   in : q, k, v, g, beta; initial_state (nullable, fp32 state layout)
  *   out: g_cum, A, o (required); h (nullable: chunk-start states);
  *        final_state (nullable: output_final_state == False)
- *   workspace: device buffer of gdr_chunk_fwd_workspace_size(p) bytes. */
+ *   workspace: device buffer of gdr_chunk_fwd_workspace_size(p) bytes.  With
+ *   use_qk_l2norm and h NULL or packed, its tail holds the q and k rows
+ *   normalised once (fwd_prep) for the rest of the forward, which then runs
+ *   as a problem without the option. */
 gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, const float* initial_state,
                          float* g_cum, void* A, void* o, void* h, float* final_state,
