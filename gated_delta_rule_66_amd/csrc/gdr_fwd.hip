@@ -64,25 +64,27 @@ struct FwdArgs {
 // KEEP: a.qn is set (the states path with q / k normalised): the group's
 // first value head also keeps the unit rows and their norms.
 template <typename T, bool KEEP>
-__global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
-  constexpr int LDK = 136;
-  constexpr int LDM = 68;
-  static_assert(64 * LDK * sizeof(T) == 64 * LDM * sizeof(float), "Ks and Ai share storage");
-  // the k tile is dead once M is formed (a barrier follows), so the inverse
-  // reuses its storage (17 KB for both)
-  __shared__ __align__(16) float KsAi[64 * LDM];
-  T* const Ks = reinterpret_cast<T*>(KsAi);
-  float* const Ai = KsAi;
-  // M keeps only its ten lower 16 x 16 blocks (the only ones written or
-  // read), block (bi, bj), bj <= bi, at slot bi (bi + 1) / 2 + bj, rows 20
-  // floats apart: 31 KB per workgroup in all, five workgroups per CU
-  constexpr int MB = 20;
-  __shared__ float Mf[10 * 16 * MB];
-  auto mf = [](int r, int c) { return ((r >> 4) * ((r >> 4) + 1) / 2 + (c >> 4)) * 16 * MB +
-                                      (r & 15) * MB + (c & 15); };
-  __shared__ float gam[64], bet[64];
+__device__ __forceinline__ void fwd_prep_item(const FwdArgs& a, const int c, const int h) {
+  // LDS, 26 KB per workgroup (six workgroups per CU): the k tile, swizzled
+  // (sw_off, 16 KB), and M.  Only the ten 16 x 16 blocks on or below the
+  // diagonal of M and of the inverse are ever written or read: block
+  // (bi, bj), bj <= bi, sits at slot bi (bi + 1) / 2 + bj.  The k tile is
+  // dead once M is formed (a barrier follows), so the inverse's blocks
+  // (rows 20 floats apart, 12.5 KB) take its storage.  M's rows are 16 floats
+  // with column c of row r at (c + 4 ((r / 4) % 4)) % 16: the inverse's
+  // products read 16 rows of one column group at once, and over rows
+  // 0 .. 15 of a block that rotation puts them on distinct banks.
+  __shared__ __align__(16) T Ks[64 * 128];
+  float* const Ai = reinterpret_cast<float*>(Ks);
+  __shared__ __align__(16) float Mf[10 * 16 * 16];
+  auto slot = [](int r, int c) { return (r >> 4) * ((r >> 4) + 1) / 2 + (c >> 4); };
+  auto ai = [&](int r, int c) { return (slot(r, c) * 16 + (r & 15)) * 20 + (c & 15); };
+  auto mf = [&](int r, int c) {
+    return (slot(r, c) * 16 + (r & 15)) * 16 + (((c & 15) + 4 * ((r >> 2) & 3)) & 15);
+  };
+  static_assert((9 * 16 + 15) * 20 + 16 <= 64 * 128 * (int)sizeof(T) / 4,
+                "the inverse's blocks fit in the k tile's storage");
 
-  const int c = blockIdx.x, h = blockIdx.y;
   int n, j;
   if (a.cu) {
     n = find_seq(a.offs, a.N, c);
@@ -137,20 +139,22 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
       buf_store16(ks, (x >> 4) * gs + (x & 15) * 16, rk.r[i]);
     }
   }
-  tile_store<T, 128, 256>(Ks, LDK, rk);
-  if (w == 0) {
-    float gv = a.g_dtype == 2 ? __builtin_bit_cast(float, glo | (ghi << 16))
-               : a.g_dtype == 0 ? __builtin_bit_cast(float, glo << 16)
-                                : (float)__builtin_bit_cast(_Float16, (uint16_t)glo);
-    if (a.gate_A_log)
-      gv = gate_log_decay(gv, a.gate_A_log[h], a.gate_dt_bias ? a.gate_dt_bias[h] : 0.f);
-    if (l >= Cc) gv = 0.f;
-    const float bv = (l < Cc) ? beta_used(to_f(__builtin_bit_cast(T, braw)), a.beta_mode) : 0.f;
-    const float gc = wave_inclusive_scan(gv);
-    gam[l] = gc;
-    bet[l] = bv;
-    if (l < Cc) a.gcum[(t0 + l) * a.Hv + h] = gc;
+#pragma unroll
+  for (int i = 0; i < TileRegs<128, 256>::N; ++i) {
+    const int x = tid + i * 256;  // 16-byte piece x % 16 of row x / 16
+    *reinterpret_cast<uint4*>(Ks + sw_off<128>(x >> 4, 8 * (x & 15))) = rk.r[i];
   }
+  // every wave forms the gate cumsum itself (lane l: row l) and takes the
+  // rows' values it needs by lane shuffles; wave 0 stores it
+  float gv = a.g_dtype == 2 ? __builtin_bit_cast(float, glo | (ghi << 16))
+             : a.g_dtype == 0 ? __builtin_bit_cast(float, glo << 16)
+                              : (float)__builtin_bit_cast(_Float16, (uint16_t)glo);
+  if (a.gate_A_log)
+    gv = gate_log_decay(gv, a.gate_A_log[h], a.gate_dt_bias ? a.gate_dt_bias[h] : 0.f);
+  if (l >= Cc) gv = 0.f;
+  const float bv = (l < Cc) ? beta_used(to_f(__builtin_bit_cast(T, braw)), a.beta_mode) : 0.f;
+  const float gc = wave_inclusive_scan(gv);
+  if (w == 0 && l < Cc) a.gcum[(t0 + l) * a.Hv + h] = gc;
   __syncthreads();
   if (keep_qk && tid < Cc) {
     a.qinv[(t0 + tid) * a.Hq + hq] = rinv[0][tid];
@@ -158,18 +162,25 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
   }
 
   // M, rows 16w .. 16w+15 (only the blocks on or below the diagonal are nonzero)
+  float gr[4], br[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    gr[e] = __shfl(gc, 16 * w + 4 * grp + e);
+    br[e] = __shfl(bv, 16 * w + 4 * grp + e);
+  }
   for (int cb = 0; cb < 4; ++cb) {
     if (cb <= w) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = mfma16(frag_row(Ks + 16 * w * LDK + 32 * kk, LDK),
-                     frag_row(Ks + 16 * cb * LDK + 32 * kk, LDK), acc);
+        acc = mfma16(frag_row_w<T, 128>(Ks, 16 * w, 32 * kk),
+                     frag_row_w<T, 128>(Ks, 16 * cb, 32 * kk), acc);
+      const float gi = __shfl(gc, 16 * cb + col);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * w + 4 * grp + e, i = 16 * cb + col;
         // masked entries take exp(-inf) = 0 (an unconditional exponential)
-        Mf[mf(r, i)] = bet[r] * __expf(i < r ? gam[r] - gam[i] : -INFINITY) * acc[e];
+        Mf[mf(r, i)] = br[e] * __expf(i < r ? gr[e] - gi : -INFINITY) * acc[e];
       }
     }
   }
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
       x[r] = acc;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Ai[(b0 + r) * LDM + b0 + l] = x[r];
+    for (int r = 0; r < 16; ++r) Ai[ai(b0 + r, b0 + l)] = x[r];
   }
   __syncthreads();
 
@@ -202,8 +213,8 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const float av = Mf[mf(16 * bi + col, 16 * m + 4 * st + grp)];
-          const float bv = Ai[(16 * m + 4 * st + grp) * LDM + 16 * bj + col];
-          t = mfma16f32(av, bv, t);
+          const float bv2 = Ai[ai(16 * m + 4 * st + grp, 16 * bj + col)];
+          t = mfma16f32(av, bv2, t);
         }
       }
       // t is a D tile: lane (grp, col) holds t[4 grp + e][col]; step e of the
@@ -211,11 +222,11 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
       f32x4 r = zero4();
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float av = Ai[(16 * bi + col) * LDM + 16 * bi + 4 * grp + e];
+        const float av = Ai[ai(16 * bi + col, 16 * bi + 4 * grp + e)];
         r = mfma16f32(av, t[e], r);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Ai[(16 * bi + 4 * grp + e) * LDM + 16 * bj + col] = -r[e];
+      for (int e = 0; e < 4; ++e) Ai[ai(16 * bi + 4 * grp + e, 16 * bj + col)] = -r[e];
     }
     __syncthreads();
   }
@@ -229,10 +240,27 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int cc = c8 + e;
-        vals[e] = from_f<T>(cc <= r ? Ai[r * LDM + cc] : 0.f);
+        vals[e] = from_f<T>(cc <= r ? Ai[ai(r, cc)] : 0.f);
       }
       *reinterpret_cast<typename VT<T>::x8*>(Aout + ((t0 + r) * a.Hv + h) * kChunk + c8) = vals;
     }
+  }
+}
+
+
+// Workgroups take (chunk row c, value head h) pairs in the order c * Hv + h,
+// each XCD a contiguous range of them (xcd_block), so the heads of a chunk run
+// together on one XCD: the workgroups in flight read whole token rows of k,
+// g and beta and write whole rows of A and g_cum, and the g, beta and g_cum
+// lines that the heads share stay in that XCD's L2.  Past 2^31 - 1 pairs the
+// grid is (chunk, head).
+template <typename T, bool KEEP>
+__global__ __launch_bounds__(256) void fwd_prep_kernel(FwdArgs a) {
+  if (gridDim.y > 1) {
+    fwd_prep_item<T, KEEP>(a, (int)blockIdx.x, (int)blockIdx.y);
+  } else {
+    const int L = xcd_block((int)blockIdx.x, (int)gridDim.x);
+    fwd_prep_item<T, KEEP>(a, L / a.Hv, L % a.Hv);
   }
 }
 
@@ -400,7 +428,9 @@ gdr_status launch_fwd(const gdr_problem* p, const Plan& pl, const void* q, const
     wp += align256(units * pl.cp * 2 * KV * sizeof(float));
     sa.seg_start = reinterpret_cast<float*>(wp);
   }
-  const dim3 gp((unsigned)pl.total_chunks, p->Hv);
+  const int64_t pairs = (int64_t)pl.total_chunks * p->Hv;
+  const dim3 gp = pairs <= INT32_MAX ? dim3((unsigned)pairs)
+                                     : dim3((unsigned)pl.total_chunks, (unsigned)p->Hv);
   if (p->in_dtype == GDR_BF16) {
     if (pl.total_chunks > 0 && qn)
       GDR_LAUNCH("fwd_prep", (fwd_prep_kernel<__bf16, true>), gp, dim3(256), st, fa);
