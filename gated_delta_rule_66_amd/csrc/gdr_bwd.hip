@@ -1290,6 +1290,15 @@ __global__ __launch_bounds__(512) void dh_ld_kernel(DhArgs da) {
   dh_ld_body<T, OPT>(da, (int)blockIdx.x, (int)gridDim.x, lds);
 }
 
+// The same at two tiles per wave: one 128-column workgroup per unit and
+// segment (the body of the data-scheduled launch's scan, without the
+// progress counts).
+template <typename T, int OPT>
+__global__ __launch_bounds__(512) void dh_ld2_kernel(DhArgs da) {
+  __shared__ DhLdLds<T, 2> lds;
+  dh_ld_body<T, OPT, 2, 4>(da, (int)blockIdx.x, (int)gridDim.x, lds);
+}
+
 // Pass 1 of the state-gradient scan alone (the forward's states given): with
 // no state-scan LDS beside it two workgroups fit a CU at VB = 1.
 template <typename T, int VB>
@@ -2428,6 +2437,9 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, bool states
   if (VB == 1 && n1 == 0 && !sa.qk_norm) {
     if (sa.beta_mode) GDR_LAUNCH("bwd_scans", (dh_ld_kernel<T, 2>), grid, dim3(512), st, da);
     else GDR_LAUNCH("bwd_scans", (dh_ld_kernel<T, 0>), grid, dim3(512), st, da);
+  } else if (VB == 2 && n1 == 0 && !sa.qk_norm) {
+    if (sa.beta_mode) GDR_LAUNCH("bwd_scans", (dh_ld2_kernel<T, 2>), grid, dim3(512), st, da);
+    else GDR_LAUNCH("bwd_scans", (dh_ld2_kernel<T, 0>), grid, dim3(512), st, da);
   } else if (VB == 1)
     switch ((sa.qk_norm ? 1 : 0) | (sa.beta_mode ? 2 : 0)) {
       case 0:

@@ -176,7 +176,8 @@ def gpu_fwd_bwd_states(d, cp=0, use_trans=True, vt=0):
     ("dense_state_dht", 2, True, 2), ("fp16_gva", 3, True, 1), ("gva_group4", 2, True, 0),
     ("varlen_empty_seq", 2, True, 0), ("pipe", 1, True, 1), ("pipe_no_state", 1, True, 1),
     ("pipe_gva", 1, True, 1), ("pipe_varlen", 1, True, 1),
-    ("varlen_ranked", 1, True, 0), ("varlen_ranked", 3, True, 1)])
+    ("varlen_ranked", 1, True, 0), ("varlen_ranked", 3, True, 1),
+    ("fp16_gva", 1, True, 2), ("varlen_ranked", 1, True, 2), ("varlen", 3, True, 2)])
 def test_backward_from_the_forward_states(name, cp, use_trans, vt):
     d = gdr_synth.make(CASES[name])
     print("case", name, "cp", cp, "trans", use_trans, "wave_tiles", vt, flush=True)
