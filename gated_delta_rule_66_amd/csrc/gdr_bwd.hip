@@ -780,6 +780,12 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
   typedef typename VT<T>::x8 x8;
   static_assert((OPT & 1) == 0, "q / k normalisation runs in dh_lh_body");
   static_assert(NB == 1 || NB == 2, "one or two column blocks per chain wave");
+  // OPT bit 2: pass 1 of a split backward given the forward's transitions.
+  // Segments 1 .. p_last walk their chunks from zero (the last from dht) and
+  // leave the gradient reaching their start in the value half of seg_out
+  // ([units, P, K, 2V]); no state gradient is stored.
+  constexpr bool P1 = (OPT & 4) != 0;
+  static_assert(!P1 || NB == 2, "pass 1 runs the 128-column form");
   constexpr int CW = DhLdLds<T, NB>::CW;
   constexpr int LDA = DhLdLds<T, NB>::LDA;
   auto& Qs = L.Qs;
@@ -807,6 +813,7 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
     sr.c1 = a.sl_c1;
     sr.p_last = a.P - 1;
   }
+  if (P1 && (p == 0 || p > sr.p_last)) return;  // segment 0 needs no pass 1
   if (sr.c0 >= sr.c1 && !(nch == 0 && p == 0)) return;
   const int cb0 = vs * CW;
   const int64_t choff = a.cu ? (int64_t)a.offs[n] : (int64_t)n * a.nc_dense;
@@ -830,7 +837,7 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
   f32x4 Gs[8 * NB];
   if (w < 4) {
     const float* src = (p == sr.p_last) ? (a.dht ? a.dht + unit * KV : nullptr)
-                                        : a.seg_start + ((int64_t)unit * a.P + p) * KV;
+                       : P1 ? nullptr : a.seg_start + ((int64_t)unit * a.P + p) * KV;
     const bool vf = (p == sr.p_last) && a.svf;
     const __amdgpu_buffer_rsrc_t srs = buf_rsrc(src, src ? KV * (int64_t)sizeof(float) : 0);
 #pragma unroll
@@ -911,7 +918,7 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
   // in Hx; non-temporal, as this pass never reads it back (coherent, sc1,
   // when gradient workgroups in the same launch read it)
   auto store_dh = [&](int cc) {
-    if constexpr (NB == 1) {
+    if constexpr (NB == 1 && !P1) {
       const __amdgpu_buffer_rsrc_t hrs = dh_rsrc(cc);
 #pragma unroll
       for (int wq = 0; wq < 4; ++wq)
@@ -992,7 +999,7 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
 #pragma unroll
         for (int kb2 = 0; kb2 < 4; ++kb2)
           Gb[j][kb2] = pack_split<T>(Gs[8 * j + 2 * kb2], Gs[8 * j + 2 * kb2 + 1]);
-      if constexpr (NB == 2) {
+      if constexpr (NB == 2 && !P1) {
         // chunk c+1's stores (issued an iteration ago) are complete before
         // the middle barrier, after which wave 5 counts them; then chunk c's
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1250,7 +1257,16 @@ __device__ __forceinline__ void dh_ld_body(const DhArgs& a, int b, int nb, DhLdL
     if (a.flags) publish(sr.c0);
   }
   if (w >= 4) return;
-  if (p == 0 && a.dh0) {
+  if (P1) {
+    float* so = a.seg_out + ((int64_t)unit * a.P + p) * (2 * KV);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          so[(16 * kb + 4 * grp + e) * (2 * kDim) + kDim + cb0 + cw(j) + col] = Gs[8 * j + kb][e];
+  } else if (p == 0 && a.dh0) {
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -1292,11 +1308,11 @@ __global__ __launch_bounds__(512) void dh_ld_kernel(DhArgs da) {
 
 // The same at two tiles per wave: one 128-column workgroup per unit and
 // segment (the body of the data-scheduled launch's scan, without the
-// progress counts).
+// progress counts); OPT bit 2 runs pass 1 of a split backward.
 template <typename T, int OPT>
 __global__ __launch_bounds__(512) void dh_ld2_kernel(DhArgs da) {
   __shared__ DhLdLds<T, 2> lds;
-  dh_ld_body<T, OPT, 2, 4>(da, (int)blockIdx.x, (int)gridDim.x, lds);
+  dh_ld_body<T, OPT, 2, (OPT & 4) ? 5 : 4>(da, (int)blockIdx.x, (int)gridDim.x, lds);
 }
 
 // Pass 1 of the state-gradient scan alone (the forward's states given): with
@@ -2410,7 +2426,12 @@ static void launch_bwd_scans(const Plan& pl, ScanArgs sa, DhArgs da, bool states
     d1.v_only = trans ? 1 : 0;
     const unsigned n2 = units * pl.cp * d1.nvs;
     const unsigned n1 = states_given ? 0u : units * pl.cp * s1.nvs;
-    if (states_given)
+    if (states_given && trans && VB == 2 && !sa.qk_norm) {
+      if (sa.beta_mode)
+        GDR_LAUNCH("bwd_scan_aug", (dh_ld2_kernel<T, 6>), dim3(n2), dim3(512), st, d1);
+      else
+        GDR_LAUNCH("bwd_scan_aug", (dh_ld2_kernel<T, 4>), dim3(n2), dim3(512), st, d1);
+    } else if (states_given)
       GDR_LAUNCH("bwd_scan_aug", (dh_aug_kernel<T, VB>), dim3(n2), dim3(256), st, d1);
     else
       GDR_LAUNCH("bwd_scan_aug", (bwd_scans_kernel<T, VB, MODE_AUG, MODE_AUG>), dim3(n1 + n2),

@@ -99,3 +99,34 @@ def test_autograd_passes_the_options():
                      beta_sigmoid=True, neg_eigval=True)
     for n, i in (("q", 0), ("k", 1), ("v", 2), ("beta", 3), ("g", 4)):
         check(n, leaves[n].grad, ref[i], "tok", d["cu_seqlens"])
+
+
+@pytest.mark.parametrize("vt", [1, 2])
+def test_beta_options_states_path_split(vt):
+    """The forward keeping its states and segment transitions, the backward
+    taking them, in three segments, with both beta options."""
+    import gated_delta_rule_66_amd as gdr
+    sig, neg = True, True
+    d = gdr_synth.make(shapes(sig)["long_cp"])
+    dd = to_dev(d)
+    print("case long_cp states path cp 3 wave_tiles", vt, flush=True)
+    g_cum, A, o, h, trans, ht = gdr.chunk_gated_delta_rule_fwd_states(
+        dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], scale=dd["scale"],
+        initial_state=dd["h0"], output_final_state=True, cp_segments=3, wave_tiles=vt,
+        **opts_kw(sig, neg))
+    assert trans is not None
+    grads = gdr.chunk_gated_delta_rule_bwd(
+        dd["q"], dd["k"], dd["v"], g_cum, dd["beta"], A, dd["do"], dht=dd["dht"],
+        scale=dd["scale"], initial_state=dd["h0"], dg_dtype=dd["g"].dtype, cp_segments=3,
+        wave_tiles=vt, h=h, trans=trans, **opts_kw(sig, neg))
+    torch.cuda.synchronize()
+    args = (np64(d["q"]), np64(d["k"]), np64(d["v"]), np64(d["g"]), np64(d["beta"]), d["scale"])
+    kw = dict(beta_sigmoid=sig, neg_eigval=neg)
+    o_r, ht_r = oracle.fwd(*args, initial_state=np64(d["h0"]), **kw)
+    ref = oracle.bwd(*args, np64(d["do"]), initial_state=np64(d["h0"]), dht=np64(d["dht"]), **kw)
+    res = {"o": check("o", o, o_r, "tok"), "final_state": check("final_state", ht, ht_r, "state")}
+    for nm, x, r in zip(NAMES, grads, ref):
+        res[nm] = check(nm, x, r, "state" if nm in ("dh0", "final_state") else "tok")
+    print({k: round(v, 5) for k, v in res.items()}, flush=True)
+    for k, v in res.items():
+        assert v <= TOL, (k, v)
